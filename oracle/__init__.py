@@ -1,0 +1,372 @@
+"""CPU oracle of the Sparsely-Gated MoE layer forward (double precision).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the package smoke check and the
+benchmark's CPU-baseline leg are the only users.  The product path never
+imports this package; it shares no code with the HIP implementation.
+
+The arithmetic lives in ``oracle.c`` (built into ``liboracle.so`` next to this
+file).  This module marshals numpy arrays and composes the stages in the order
+the pages give them:
+
+* gate: clean/noisy logits -> KeepTopK -> softmax (or the Switch router),
+* the Importance and Load vectors and the auxiliary losses,
+* dispatch into one merged batch per expert (with optional capacity),
+* expert FFNs, gate-weighted combine,
+* the two-level (hierarchical) composition.
+
+Citations use the page titles listed at the top of ``oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+GATE_TOPK_SOFTMAX = 0
+GATE_SWITCH_TOP1 = 1
+ACT_RELU = 0
+ACT_SWIGLU = 1
+NEAR_TIE_REL = 1e-4
+
+_dp = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
+_ip = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc (-O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.run(
+            ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-std=c11", "-Wall",
+             "-o", tmp, _SRC, "-lm"],
+            check=True,
+        )
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _opt(ptr_type):
+    """ctypes argtype accepting None for optional arrays."""
+
+    class _Opt:
+        @classmethod
+        def from_param(cls, obj):
+            if obj is None:
+                return None
+            return ptr_type.from_param(obj)
+
+    return _Opt
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build(force=True)
+        L = ctypes.CDLL(_LIB_PATH)
+        c_int, c_dbl, c_i64 = ctypes.c_int, ctypes.c_double, ctypes.c_int64
+        odp, oip = _opt(_dp), _opt(_ip)
+        L.oracle_softplus.argtypes = [c_dbl]
+        L.oracle_softplus.restype = c_dbl
+        L.oracle_phi.argtypes = [c_dbl]
+        L.oracle_phi.restype = c_dbl
+        L.oracle_bf16_round.argtypes = [c_dbl]
+        L.oracle_bf16_round.restype = c_dbl
+        L.oracle_bf16_round_array.argtypes = [c_i64, _dp, _dp]
+        L.oracle_gate_logits.argtypes = [c_int, c_int, c_int, _dp, _dp, odp, odp, odp, _dp, odp, _dp]
+        L.oracle_keep_topk.argtypes = [c_int, c_int, c_int, _dp, _ip, odp, odp]
+        L.oracle_gate_weights.argtypes = [c_int, c_int, c_int, c_int, _dp, _ip, _dp, odp]
+        L.oracle_importance.argtypes = [c_int, c_int, _dp, _dp]
+        L.oracle_load.argtypes = [c_int, c_int, c_int, _dp, _dp, _ip, _dp, _dp, odp, odp]
+        L.oracle_dispatch.argtypes = [c_int, c_int, c_int, c_dbl, _ip, _ip, _ip, _ip, _ip, _ip]
+        L.oracle_dispatch.restype = c_int
+        L.oracle_expert_ffn.argtypes = [c_int, c_int, c_int, c_int, c_int, _dp, _dp, odp, odp, _dp,
+                                        odp, _dp]
+        L.oracle_combine.argtypes = [c_int, c_int, c_int, _dp, _ip, _dp, _dp]
+        L.oracle_cv2.argtypes = [c_int, _dp]
+        L.oracle_cv2.restype = c_dbl
+        L.oracle_aux.argtypes = [c_int, c_int, c_int, _dp, odp, _ip, c_dbl, c_dbl, c_dbl, _dp]
+        L.oracle_hier_load.argtypes = [c_int, c_int, _dp, _dp, _ip, _dp]
+        _lib = L
+    return _lib
+
+
+def _d(a):
+    return None if a is None else np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _i(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+# --------------------------------------------------------------------------
+# scalar helpers
+# --------------------------------------------------------------------------
+
+def softplus(z: float) -> float:
+    return lib().oracle_softplus(float(z))
+
+
+def phi(z: float) -> float:
+    return lib().oracle_phi(float(z))
+
+
+def bf16_round(a) -> np.ndarray:
+    a = _d(a)
+    out = np.empty_like(a)
+    lib().oracle_bf16_round_array(a.size, a.reshape(-1), out.reshape(-1))
+    return out
+
+
+def cv2(v) -> float:
+    v = _d(v)
+    return lib().oracle_cv2(v.size, v)
+
+
+# --------------------------------------------------------------------------
+# stages
+# --------------------------------------------------------------------------
+
+def gate_logits(x, w_gate, b_gate=None, w_noise=None, noise=None):
+    """clean, sp (None if noiseless), H  -- all [T, n] float64."""
+    x, w_gate, b_gate, w_noise, noise = map(_d, (x, w_gate, b_gate, w_noise, noise))
+    T, d = x.shape
+    n = w_gate.shape[0]
+    clean = np.empty((T, n))
+    H = np.empty((T, n))
+    sp = np.empty((T, n)) if w_noise is not None else None
+    lib().oracle_gate_logits(T, d, n, x, w_gate, b_gate, w_noise, noise, clean, sp, H)
+    return clean, sp, H
+
+
+def keep_topk(H, k):
+    H = _d(H)
+    T, n = H.shape
+    idx = np.empty((T, k), np.int32)
+    hk = np.empty(T)
+    hk1 = np.empty(T)
+    lib().oracle_keep_topk(T, n, k, H, idx, hk, hk1)
+    return idx, hk, hk1
+
+
+def gate_weights(H, topk_idx, mode=GATE_TOPK_SOFTMAX):
+    H = _d(H)
+    topk_idx = _i(topk_idx)
+    T, n = H.shape
+    k = topk_idx.shape[1]
+    w = np.empty((T, k))
+    probs = np.empty((T, n))
+    lib().oracle_gate_weights(T, n, k, mode, H, topk_idx, w, probs)
+    return w, probs
+
+
+def importance(probs):
+    probs = _d(probs)
+    T, n = probs.shape
+    out = np.empty(n)
+    lib().oracle_importance(T, n, probs, out)
+    return out
+
+
+def load(clean, sp, topk_idx, hk, hk1):
+    clean, sp, hk, hk1 = map(_d, (clean, sp, hk, hk1))
+    topk_idx = _i(topk_idx)
+    T, n = clean.shape
+    k = topk_idx.shape[1]
+    P = np.empty((T, n))
+    out = np.empty(n)
+    lib().oracle_load(T, n, k, clean, sp, topk_idx, hk, hk1, P, out)
+    return out, P
+
+
+def dispatch(topk_idx, n, capacity_factor=0.0):
+    topk_idx = _i(topk_idx)
+    T, k = topk_idx.shape
+    counts_pre = np.empty(n, np.int32)
+    counts = np.empty(n, np.int32)
+    offsets = np.empty(n + 1, np.int32)
+    perm = np.zeros(max(T * k, 1), np.int32)
+    slot_pos = np.empty((T, k), np.int32)
+    rows = lib().oracle_dispatch(T, k, n, float(capacity_factor), topk_idx, counts_pre, counts,
+                                 offsets, perm, slot_pos)
+    return dict(counts_pre=counts_pre, counts=counts, offsets=offsets, perm=perm[:rows].copy(),
+                slot_pos=slot_pos, rows=rows)
+
+
+def expert_ffn(u, w1, w2, b1=None, w3=None, b2=None, act=ACT_RELU, bf16=False):
+    """One expert on its merged rows u [rows, d]; returns [rows, d]."""
+    u, w1, w2, b1, w3, b2 = map(_d, (u, w1, w2, b1, w3, b2))
+    rows, d = u.shape
+    h = w1.shape[0]
+    y = np.empty((rows, d))
+    if rows:
+        lib().oracle_expert_ffn(rows, d, h, act, int(bool(bf16)), u, w1, b1, w3, w2, b2, y)
+    return y
+
+
+def combine(y_perm, slot_pos, topk_w, d):
+    slot_pos = _i(slot_pos)
+    topk_w = _d(topk_w)
+    T, k = slot_pos.shape
+    yp = _d(y_perm) if y_perm is not None and len(y_perm) else np.zeros((1, d))
+    y = np.empty((T, d))
+    lib().oracle_combine(T, k, d, yp, slot_pos, topk_w, y)
+    return y
+
+
+def aux(T, k, importance_v, load_v, counts_pre, w_importance, w_load, alpha):
+    importance_v = _d(importance_v)
+    load_v = _d(load_v)
+    counts_pre = _i(counts_pre)
+    out = np.empty(3)
+    lib().oracle_aux(T, k, importance_v.size, importance_v, load_v, counts_pre,
+                     float(w_importance), float(w_load), float(alpha), out)
+    return out
+
+
+def hier_load(load_primary, load_secondary, group_tokens):
+    load_primary, load_secondary = _d(load_primary), _d(load_secondary)
+    a, b = load_secondary.shape
+    out = np.empty(a * b)
+    lib().oracle_hier_load(a, b, load_primary, load_secondary, _i(group_tokens), out)
+    return out
+
+
+def near_ties(hk, hk1):
+    """O5: tokens whose k-th and (k+1)-th largest H differ by less than
+    1e-4 * max(|a|, |b|) (never true when k == n)."""
+    hk = np.asarray(hk)
+    hk1 = np.asarray(hk1)
+    with np.errstate(invalid="ignore"):
+        return (hk - hk1) < NEAR_TIE_REL * np.maximum(np.abs(hk), np.abs(hk1))
+
+
+# --------------------------------------------------------------------------
+# compositions
+# --------------------------------------------------------------------------
+
+@dataclass
+class GateResult:
+    clean: np.ndarray
+    sp: np.ndarray | None
+    H: np.ndarray
+    topk_idx: np.ndarray
+    topk_w: np.ndarray
+    probs: np.ndarray
+    hk: np.ndarray
+    hk1: np.ndarray
+    importance: np.ndarray
+    load: np.ndarray | None
+    P: np.ndarray | None
+    near_tie: np.ndarray
+
+
+def gate(x, w_gate, k, b_gate=None, w_noise=None, noise=None, mode=GATE_TOPK_SOFTMAX):
+    """[PAPER] Noisy Top-K gating plus its Importance / Load vectors."""
+    clean, sp, H = gate_logits(x, w_gate, b_gate, w_noise, noise)
+    idx, hk, hk1 = keep_topk(H, k)
+    w, probs = gate_weights(H, idx, mode)
+    imp = importance(probs)
+    ld, P = (None, None)
+    if sp is not None:
+        ld, P = load(clean, sp, idx, hk, hk1)
+    return GateResult(clean, sp, H, idx, w, probs, hk, hk1, imp, ld, P, near_ties(hk, hk1))
+
+
+def experts_apply(x, perm, offsets, w1, w2, b1=None, w3=None, b2=None, act=ACT_RELU, bf16=False,
+                  experts=None):
+    """Run every (or the listed) expert on its merged rows; returns y_perm."""
+    x = np.asarray(x)
+    n = len(offsets) - 1
+    rows = int(offsets[n])
+    d = x.shape[1]
+    y_perm = np.zeros((rows, d))
+    for e in (range(n) if experts is None else experts):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        u = x[perm[lo:hi]]
+        y_perm[lo:hi] = expert_ffn(u, w1[e], w2[e], None if b1 is None else b1[e],
+                                   None if w3 is None else w3[e], None if b2 is None else b2[e],
+                                   act, bf16)
+    return y_perm
+
+
+def forward(x, w_gate, k, w1, w2, *, b_gate=None, w_noise=None, noise=None, b1=None, w3=None,
+            b2=None, mode=GATE_TOPK_SOFTMAX, act=ACT_RELU, bf16=False, capacity_factor=0.0,
+            w_importance=0.1, w_load=0.1, alpha=1.0):
+    """The whole flat layer: gate -> dispatch -> experts -> combine -> losses."""
+    T, d = np.asarray(x).shape
+    n = np.asarray(w_gate).shape[0]
+    g = gate(x, w_gate, k, b_gate, w_noise, noise, mode)
+    disp = dispatch(g.topk_idx, n, capacity_factor)
+    y_perm = experts_apply(x, disp["perm"], disp["offsets"], w1, w2, b1, w3, b2, act, bf16)
+    y = combine(y_perm, disp["slot_pos"], g.topk_w, d)
+    losses = aux(T, k, g.importance, g.load, disp["counts_pre"], w_importance, w_load, alpha)
+    return dict(gate=g, dispatch=disp, y_perm=y_perm, y=y, losses=losses)
+
+
+def gate_hier(x, w_gate, w_noise, noise, k1, w_gate2, w_noise2, noise2, k2, b_gate=None,
+              b_gate2=None):
+    """O10 gating.  [NOTES] "分层 MoE": a primary gate picks k1 of a groups; in
+    each chosen group a secondary gate (that group's own parameters) picks k2
+    of its b experts.  Slot s*k2 + s2 of a token is expert g_s*b + e with
+    weight w1_s * w2_{s,s2}.  Aux vectors: Importance over the product
+    weights; Load in the factorised form of ``hier_load``.
+    Shapes: w_gate2/w_noise2 [a, b, d], noise2 [T, k1, b]."""
+    x = _d(x)
+    T, d = x.shape
+    w_gate2 = _d(w_gate2)
+    a, b, _ = w_gate2.shape
+    pg = gate(x, w_gate, k1, b_gate, w_noise, noise)
+    idx = np.empty((T, k1 * k2), np.int32)
+    wts = np.empty((T, k1 * k2))
+    near = pg.near_tie.copy()
+    load_sec = np.zeros((a, b))
+    group_tokens = np.zeros(a, np.int32)
+    noise2 = _d(noise2) if noise2 is not None else None
+    w_noise2 = _d(w_noise2) if w_noise2 is not None else None
+    for g in range(a):
+        sel = np.nonzero(pg.topk_idx == g)  # (tokens ascending, slot)
+        toks, slots = sel
+        group_tokens[g] = len(toks)
+        if len(toks) == 0:
+            continue
+        z2 = noise2[toks, slots] if noise2 is not None else None
+        sg = gate(x[toks], w_gate2[g], k2, None if b_gate2 is None else b_gate2[g],
+                  None if w_noise2 is None else w_noise2[g], z2)
+        for r, (t, s) in enumerate(zip(toks, slots)):
+            idx[t, s * k2:(s + 1) * k2] = g * b + sg.topk_idx[r]
+            wts[t, s * k2:(s + 1) * k2] = pg.topk_w[t, s] * sg.topk_w[r]
+            near[t] |= sg.near_tie[r]
+        if sg.load is not None:
+            load_sec[g] = sg.load
+    n = a * b
+    dense = np.zeros((T, n))
+    for s in range(k1 * k2):
+        dense[np.arange(T), idx[:, s]] = wts[:, s]
+    imp = importance(dense)
+    ld = hier_load(pg.load, load_sec, group_tokens) if pg.load is not None else None
+    return dict(primary=pg, topk_idx=idx, topk_w=wts, importance=imp, load=ld,
+                load_secondary=load_sec, group_tokens=group_tokens, near_tie=near)
+
+
+def forward_hier(x, w_gate, w_noise, noise, k1, w_gate2, w_noise2, noise2, k2, w1, w2, *,
+                 b1=None, b2=None, bf16=False, w_importance=0.1, w_load=0.1, alpha=1.0):
+    T, d = np.asarray(x).shape
+    gh = gate_hier(x, w_gate, w_noise, noise, k1, w_gate2, w_noise2, noise2, k2)
+    n = np.asarray(w_gate2).shape[0] * np.asarray(w_gate2).shape[1]
+    disp = dispatch(gh["topk_idx"], n, 0.0)
+    y_perm = experts_apply(x, disp["perm"], disp["offsets"], w1, w2, b1, None, b2, ACT_RELU, bf16)
+    y = combine(y_perm, disp["slot_pos"], gh["topk_w"], d)
+    losses = aux(T, k1 * k2, gh["importance"], gh["load"], disp["counts_pre"], w_importance,
+                 w_load, alpha)
+    return dict(gate=gh, dispatch=disp, y_perm=y_perm, y=y, losses=losses)

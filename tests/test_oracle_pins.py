@@ -1,0 +1,521 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself.
+
+Each test checks the oracle against a closed form, an invariant, a
+brute-force enumeration, a library routine (scipy / numpy / torch CPU) or a
+hand-worked example under tests/golden/ -- never against a retyped copy of its
+own formula.  Citations name the page and section the fact comes from.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import ndtr
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------------------
+# Special values and library reductions (softplus, Phi, bf16)
+# ---------------------------------------------------------------------------
+
+def test_special_values():
+    # Softplus(0) = ln 2; Phi(0) = 1/2
+    assert oracle.softplus(0.0) == pytest.approx(math.log(2.0), rel=0, abs=1e-16)
+    assert oracle.phi(0.0) == 0.5
+
+
+def test_phi_matches_scipy_ndtr():
+    # Phi against scipy's ndtr from z = -37 (just above ndtr's underflow) to 8.
+    # Both sides evaluate erfc at a rounded -z/sqrt(2); the relative
+    # sensitivity of erfc(y) to its argument is about 2*y^2, so the bound is a
+    # few ulps times max(1, 2*y^2) per side.
+    z = np.concatenate([np.linspace(-37, 8, 6001), [-20.0, -5.0, -1.0, 0.0, 1.0, 5.0]])
+    ours = np.array([oracle.phi(v) for v in z])
+    ref = ndtr(z)
+    y = -z / np.sqrt(2.0)
+    tol = 4 * np.maximum(1.0, 2 * y ** 2) * np.finfo(float).eps
+    rel = np.abs(ours - ref) / ref
+    assert np.all(rel <= tol), float(np.max(rel / tol))
+
+
+def test_softplus_matches_logaddexp():
+    z = np.concatenate([np.linspace(-60, 60, 2401), [-745.0, 700.0, 1e-12, -1e-12]])
+    ours = np.array([oracle.softplus(v) for v in z])
+    ref = np.logaddexp(0.0, z)
+    np.testing.assert_allclose(ours, ref, rtol=1e-15, atol=1e-300)
+
+
+def test_bf16_round_matches_torch():
+    r = rng(0)
+    vals = np.concatenate([
+        r.standard_normal(20000).astype(np.float32),
+        (r.standard_normal(2000) * 1e-38).astype(np.float32),   # subnormal range
+        (r.standard_normal(2000) * 1e30).astype(np.float32),
+        np.array([0.0, -0.0, 1.0, -1.0, 3.0e38, -3.0e38], np.float32),
+    ])
+    # exact ties: low 16 bits == 0x8000, with both parities of bit 16
+    bits = r.integers(0, 2**31, 4000, dtype=np.int64).astype(np.uint32)
+    bits = (bits & np.uint32(0xFFFF0000)) | np.uint32(0x8000)
+    bits = bits & np.uint32(0x7F7FFFFF)  # keep finite
+    vals = np.concatenate([vals, bits.view(np.float32)])
+    ours = oracle.bf16_round(vals.astype(np.float64))
+    ref = torch.from_numpy(vals).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(ours, ref)
+
+
+# ---------------------------------------------------------------------------
+# Hand-worked golden example
+# ---------------------------------------------------------------------------
+
+def _golden():
+    with open(os.path.join(GOLDEN, "worked_layer.json")) as f:
+        g = json.load(f)
+    e = math.e
+    ns = {"a": e / (1 + e), "b": 1 / (1 + e), "L": math.log(2.0),
+          "Phi": lambda z: float(ndtr(z))}
+
+    def ev(v):
+        if isinstance(v, list):
+            return [ev(u) for u in v]
+        if isinstance(v, str):
+            return float(eval(v, {"__builtins__": {}}, ns))
+        return v
+    return g, ev
+
+
+def test_golden_worked_layer():
+    g, ev = _golden()
+    inp, exp = g["inputs"], g["expected"]
+    n, k, h = inp["n"], inp["k"], inp["h"]
+    x = np.array(inp["x"], float)
+    w_gate = np.array(inp["w_gate"])
+    b_gate = np.array(inp["b_gate"])
+    w_noise = np.array(inp["w_noise"], float)
+    noise = np.array(ev(inp["noise"]))
+    w1 = np.stack([(e + 1) * np.array(inp["w1_unit"], float) for e in range(n)])
+    w2 = np.stack([np.array(inp["w2"], float)] * n)
+    b1 = np.zeros((n, h))
+    b2 = np.stack([[0.0, 0.0, float(e)] for e in range(n)])
+
+    out = oracle.forward(x, w_gate, k, w1, w2, b_gate=b_gate, w_noise=w_noise, noise=noise,
+                         b1=b1, b2=b2, alpha=1.0)
+    gt = out["gate"]
+    np.testing.assert_allclose(gt.H, ev(exp["H"]), rtol=0, atol=1e-15)
+    np.testing.assert_array_equal(gt.topk_idx, exp["topk_idx"])
+    np.testing.assert_allclose(gt.topk_w, ev(exp["topk_w"]), rtol=1e-15)
+    np.testing.assert_allclose(gt.importance, ev(exp["importance"]), rtol=1e-15, atol=1e-300)
+    np.testing.assert_allclose(gt.load, ev(exp["load"]), rtol=1e-14)
+    d = out["dispatch"]
+    np.testing.assert_array_equal(d["counts"], exp["counts"])
+    np.testing.assert_array_equal(d["offsets"], exp["offsets"])
+    np.testing.assert_array_equal(d["perm"], exp["perm"])
+    np.testing.assert_array_equal(d["slot_pos"], exp["slot_pos"])
+    np.testing.assert_allclose(out["y"], ev(exp["y"]), rtol=1e-15, atol=1e-15)
+    assert out["losses"][2] == pytest.approx(ev(exp["switch_loss_alpha1"]), rel=1e-15)
+    imp = np.array(ev(exp["importance"]))
+    cv2 = np.mean((imp - imp.mean()) ** 2) / imp.mean() ** 2
+    assert out["losses"][0] == pytest.approx(0.1 * cv2, rel=1e-14)
+
+    cap = exp["capacity_1"]
+    out = oracle.forward(x, w_gate, k, w1, w2, b_gate=b_gate, w_noise=w_noise, noise=noise,
+                         b1=b1, b2=b2, capacity_factor=1.0)
+    d = out["dispatch"]
+    for key in ("counts_pre", "counts", "offsets", "perm", "slot_pos"):
+        np.testing.assert_array_equal(d[key], cap[key], err_msg=key)
+    np.testing.assert_allclose(out["y"], ev(cap["y"]), rtol=1e-15, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# Brute force on tiny inputs (selection, kth_excluding, dispatch)
+# ---------------------------------------------------------------------------
+
+def _tiny_H(r, T, n, quant):
+    H = r.standard_normal((T, n))
+    if quant:
+        H = np.round(H * 2) / 2  # many exact ties
+        H[H == 0] = np.where(r.random(np.sum(H == 0)) < 0.5, -0.0, 0.0)
+    return H
+
+
+@pytest.mark.parametrize("quant", [False, True])
+def test_keep_topk_brute_force(quant):
+    r = rng(1 + quant)
+    for n in range(1, 8):
+        for k in range(1, n + 1):
+            H = _tiny_H(r, 6, n, quant)
+            idx, hk, hk1 = oracle.keep_topk(H, k)
+            for t in range(H.shape[0]):
+                v = H[t]
+                valid = []
+                for S in itertools.combinations(range(n), k):
+                    rest = [j for j in range(n) if j not in S]
+                    if not rest or min(v[list(S)]) >= max(v[rest]):
+                        valid.append(S)
+                best = min(valid)  # lowest indices win ties
+                expect_order = sorted(best, key=lambda j: (-v[j], j))
+                assert list(idx[t]) == expect_order
+                # kth_excluding(H, k, i) by literally deleting i and sorting
+                for i in range(n):
+                    others = sorted(np.delete(v, i), reverse=True)
+                    kth_ex = others[k - 1] if k - 1 < len(others) else -np.inf
+                    thr = hk1[t] if i in best else hk[t]
+                    assert thr == kth_ex
+
+
+def test_load_against_deleted_kth():
+    r = rng(3)
+    T, d, n, k = 7, 5, 6, 2
+    x = r.standard_normal((T, d))
+    wg = r.standard_normal((n, d)) / math.sqrt(d)
+    wn = r.standard_normal((n, d)) / math.sqrt(d)
+    z = r.standard_normal((T, n))
+    g = oracle.gate(x, wg, k, None, wn, z)
+    raw = x @ wn.T
+    sp = np.logaddexp(0.0, raw)
+    clean = x @ wg.T
+    H = clean + z * sp
+    for t in range(T):
+        for i in range(n):
+            kth_ex = sorted(np.delete(H[t], i), reverse=True)[k - 1]
+            assert g.P[t, i] == pytest.approx(ndtr((clean[t, i] - kth_ex) / sp[t, i]),
+                                              rel=1e-12, abs=1e-15)
+    np.testing.assert_allclose(g.load, g.P.sum(0), rtol=1e-14)
+
+
+def _dispatch_brute(idx, n, cf):
+    T, k = idx.shape
+    cap = math.floor(cf * T * k / n) if cf > 0 else 10**9
+    lists = [[] for _ in range(n)]
+    dropped = set()
+    for t in range(T):
+        for s in range(k):
+            e = idx[t, s]
+            if len(lists[e]) < cap:
+                lists[e].append((t, s))
+            else:
+                dropped.add((t, s))
+    return lists, dropped, cap
+
+
+@pytest.mark.parametrize("cf", [0.0, 0.5, 1.0, 1.25, 3.0])
+def test_dispatch_brute_force(cf):
+    r = rng(4)
+    for (T, n, k) in [(1, 1, 1), (9, 4, 2), (33, 7, 3), (64, 5, 1), (40, 16, 4)]:
+        idx = np.stack([r.permutation(n)[:k] for _ in range(T)]).astype(np.int32)
+        if T > 3:
+            idx[: T // 2, 0] = 0  # a hot expert to force drops
+            for t in range(T // 2):
+                row = list(idx[t])
+                if row.count(0) > 1:
+                    idx[t] = [0] + [e for e in r.permutation(np.arange(1, n))[: k - 1]]
+        disp = oracle.dispatch(idx, n, cf)
+        lists, dropped, cap = _dispatch_brute(idx, n, cf)
+        counts = np.array([len(l) for l in lists])
+        pre = np.bincount(idx.reshape(-1), minlength=n)
+        np.testing.assert_array_equal(disp["counts_pre"], pre)
+        np.testing.assert_array_equal(disp["counts"], counts)
+        np.testing.assert_array_equal(disp["offsets"], np.concatenate([[0], np.cumsum(counts)]))
+        perm = [t for l in lists for (t, s) in l]
+        np.testing.assert_array_equal(disp["perm"], perm)
+        row = 0
+        expect_pos = -np.ones((T, k), np.int64)
+        for l in lists:
+            for (t, s) in l:
+                expect_pos[t, s] = row
+                row += 1
+        np.testing.assert_array_equal(disp["slot_pos"], expect_pos)
+
+
+def test_dispatch_invariants():
+    # perm is a permutation of the kept pairs, slot_pos is its inverse, offsets
+    # are monotone with offsets[n] = rows, tokens ascend inside each segment.
+    r = rng(5)
+    T, n, k = 500, 13, 3
+    idx = np.stack([r.choice(n, k, replace=False, p=np.linspace(1, 3, n) / np.linspace(1, 3, n).sum())
+                    for _ in range(T)]).astype(np.int32)
+    for cf in (0.0, 0.8, 1.1):
+        d = oracle.dispatch(idx, n, cf)
+        off, perm, pos = d["offsets"], d["perm"], d["slot_pos"]
+        assert np.all(np.diff(off) >= 0) and off[-1] == d["rows"] == d["counts"].sum()
+        kept = [(t, s) for t in range(T) for s in range(k) if pos[t, s] >= 0]
+        assert len(kept) == d["rows"]
+        assert sorted(pos[pos >= 0].tolist()) == list(range(d["rows"]))
+        for (t, s) in kept:
+            p = pos[t, s]
+            assert perm[p] == t
+            e = idx[t, s]
+            assert off[e] <= p < off[e + 1]
+        for e in range(n):
+            seg = perm[off[e]:off[e + 1]]
+            assert np.all(np.diff(seg) > 0)
+
+
+# ---------------------------------------------------------------------------
+# Closed forms
+# ---------------------------------------------------------------------------
+
+def _ffn_np(u, w1, w2, b1=None, b2=None):
+    hdn = u @ w1.T
+    if b1 is not None:
+        hdn = hdn + b1
+    hdn = np.maximum(hdn, 0.0)
+    y = hdn @ w2.T
+    if b2 is not None:
+        y = y + b2
+    return y
+
+
+def test_dense_softmax_mixture_when_k_equals_n():
+    # k = n and no noise: G = softmax(clean) and y = sum_i softmax_i E_i(x)
+    # ("soft routing", wiki article part 2), computed here with dense numpy.
+    r = rng(6)
+    T, d, n, h = 11, 6, 5, 7
+    x = r.standard_normal((T, d))
+    wg = r.standard_normal((n, d))
+    bg = r.standard_normal(n)
+    w1 = r.standard_normal((n, h, d))
+    w2 = r.standard_normal((n, d, h))
+    b1 = r.standard_normal((n, h))
+    b2 = r.standard_normal((n, d))
+    out = oracle.forward(x, wg, n, w1, w2, b_gate=bg, b1=b1, b2=b2)
+    logits = x @ wg.T + bg
+    sm = np.exp(logits - logits.max(1, keepdims=True))
+    sm /= sm.sum(1, keepdims=True)
+    dense = sum(sm[:, [i]] * _ffn_np(x, w1[i], w2[i], b1[i], b2[i]) for i in range(n))
+    np.testing.assert_allclose(out["y"], dense, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(out["gate"].probs, sm, rtol=1e-13)
+    np.testing.assert_allclose(out["gate"].importance, sm.sum(0), rtol=1e-13)
+
+
+def test_k_equals_n_load_and_counts():
+    # k = n: kth_excluding is -inf for every expert, P = 1, Load_i = T,
+    # CV^2(Load) = 0; every count is T and each segment is tokens 0..T-1.
+    r = rng(7)
+    T, d, n = 20, 4, 6
+    x = r.standard_normal((T, d))
+    g = oracle.gate(x, r.standard_normal((n, d)), n, None, r.standard_normal((n, d)),
+                    r.standard_normal((T, n)))
+    np.testing.assert_array_equal(g.load, np.full(n, float(T)))
+    assert oracle.cv2(g.load) == 0.0
+    d_ = oracle.dispatch(g.topk_idx, n)
+    np.testing.assert_array_equal(d_["counts"], np.full(n, T))
+    for e in range(n):
+        np.testing.assert_array_equal(d_["perm"][d_["offsets"][e]:d_["offsets"][e + 1]],
+                                      np.arange(T))
+
+
+@pytest.mark.parametrize("k", [1, 2, 3])
+def test_degenerate_all_equal_logits(k):
+    # All-zero gate weights and noise: every H is equal, so by the
+    # lowest-index rule every token takes experts 0..k-1 with weight 1/k.
+    T, d, n = 10, 3, 5
+    x = rng(8).standard_normal((T, d))
+    zero = np.zeros((n, d))
+    out = oracle.forward(x, zero, k, np.zeros((n, 2, d)), np.zeros((n, d, 2)), w_noise=zero,
+                         noise=np.zeros((T, n)))
+    g = out["gate"]
+    np.testing.assert_array_equal(g.topk_idx, np.tile(np.arange(k), (T, 1)))
+    np.testing.assert_allclose(g.topk_w, np.full((T, k), 1.0 / k), rtol=1e-15)
+    np.testing.assert_array_equal(out["dispatch"]["counts"], [T] * k + [0] * (n - k))
+    assert oracle.cv2(g.importance) == pytest.approx((n - k) / k, rel=1e-14)
+    np.testing.assert_allclose(g.load, np.full(n, T / 2.0), rtol=1e-15)  # Phi(0) = 1/2
+    assert out["losses"][1] == 0.0
+    # capacity: exactly tokens 0..C-1 are kept by each of experts 0..k-1
+    cf = 0.6
+    C = math.floor(cf * T * k / n)
+    dd = oracle.dispatch(g.topk_idx, n, cf)
+    for e in range(k):
+        np.testing.assert_array_equal(dd["perm"][dd["offsets"][e]:dd["offsets"][e + 1]],
+                                      np.arange(C))
+    assert np.all(dd["slot_pos"][C:] == -1)
+
+
+def test_switch_degenerate_and_bounds():
+    # Switch router with equal logits: p_i = 1/n, top-1 = expert 0, f_0 = 1,
+    # P_i = 1/n -> n * sum f P = 1 (tufusi survey 3.2, minimum at uniform).
+    T, d, n = 12, 3, 7
+    x = rng(9).standard_normal((T, d))
+    out = oracle.forward(x, np.zeros((n, d)), 1, np.zeros((n, 2, d)), np.zeros((n, d, 2)),
+                         mode=oracle.GATE_SWITCH_TOP1, alpha=1.0)
+    np.testing.assert_allclose(out["gate"].topk_w, 1.0 / n, rtol=1e-15)
+    assert out["losses"][2] == pytest.approx(1.0, rel=1e-14)
+    # random logits: the weight is the largest softmax probability, in [1/n, 1]
+    r = rng(10)
+    H = r.standard_normal((50, n)) * 3
+    idx, _, _ = oracle.keep_topk(H, 1)
+    w, p = oracle.gate_weights(H, idx, oracle.GATE_SWITCH_TOP1)
+    sm = np.exp(H - H.max(1, keepdims=True))
+    sm /= sm.sum(1, keepdims=True)
+    np.testing.assert_allclose(w[:, 0], sm.max(1), rtol=1e-14)
+    np.testing.assert_allclose(p, sm, rtol=1e-13)
+    assert np.all(w >= 1.0 / n - 1e-15) and np.all(w <= 1.0)
+
+
+def test_topk_weights_sum_to_one():
+    r = rng(11)
+    for k in (1, 2, 4, 8):
+        H = r.standard_normal((40, 16)) * 4
+        idx, _, _ = oracle.keep_topk(H, k)
+        w, probs = oracle.gate_weights(H, idx)
+        np.testing.assert_allclose(w.sum(1), 1.0, rtol=1e-14)
+        assert np.all(w > 0) and np.all(w <= 1)
+        assert np.all(np.diff(w, axis=1) <= 1e-15)  # slots in descending H
+        # renormalised top-k of the full softmax (wiki article part 2)
+        sm = np.exp(H - H.max(1, keepdims=True))
+        sm /= sm.sum(1, keepdims=True)
+        sel = np.take_along_axis(sm, idx, 1)
+        np.testing.assert_allclose(w, sel / sel.sum(1, keepdims=True), rtol=1e-13)
+        if k == 1:
+            np.testing.assert_array_equal(w, 1.0)
+
+
+def test_cv2_closed_forms():
+    n, T = 9, 100.0
+    assert oracle.cv2(np.full(n, T / n)) == pytest.approx(0.0, abs=1e-25)  # rounding of the mean only
+    collapsed = np.zeros(n)
+    collapsed[3] = T
+    assert oracle.cv2(collapsed) == pytest.approx(n - 1, rel=1e-14)
+    assert oracle.cv2(np.zeros(n)) == 0.0
+    v = np.array([1.0, 2.0, 3.0, 6.0])
+    assert oracle.cv2(v) == pytest.approx(np.var(v) / np.mean(v) ** 2, rel=1e-14)
+
+
+def test_switch_loss_closed_forms():
+    n, T = 8, 64
+    uni = np.full(n, T // n, np.int32)
+    l = oracle.aux(T, 1, np.full(n, T / n), None, uni, 0.1, 0.1, 1.0)
+    assert l[2] == pytest.approx(1.0, rel=1e-14)
+    col = np.zeros(n, np.int32)
+    col[0] = T
+    imp = np.zeros(n)
+    imp[0] = T
+    l = oracle.aux(T, 1, imp, None, col, 0.1, 0.1, 1.0)
+    assert l[2] == pytest.approx(float(n), rel=1e-14)
+    assert l[0] == pytest.approx(0.1 * (n - 1), rel=1e-14)
+
+
+def test_single_expert_reduces_to_dense_ffn_bf16():
+    # n = 1, k = 1: y = FFN(x), with bf16-rounded operands (torch's RNE
+    # conversion) and a float64 numpy FFN.
+    r = rng(12)
+    T, d, h = 37, 24, 40
+    x = r.standard_normal((T, d))
+    wg = r.standard_normal((1, d))
+
+    def bf(a):
+        return torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).double().numpy()
+    w1 = bf(r.standard_normal((1, h, d)) / math.sqrt(d))
+    w2 = bf(r.standard_normal((1, d, h)) / math.sqrt(h))
+    out = oracle.forward(x, wg, 1, w1, w2, bf16=True)
+    xb = bf(x)
+    hid = bf(np.maximum(xb @ w1[0].T, 0.0))
+    np.testing.assert_allclose(out["y"], hid @ w2[0].T, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(out["gate"].topk_w, 1.0)
+
+
+def test_swiglu_expert_against_numpy():
+    r = rng(13)
+    rows, d, h = 9, 8, 12
+    u = r.standard_normal((rows, d))
+    w1 = r.standard_normal((h, d))
+    w3 = r.standard_normal((h, d))
+    w2 = r.standard_normal((d, h))
+    y = oracle.expert_ffn(u, w1, w2, w3=w3, act=oracle.ACT_SWIGLU)
+    g = u @ w1.T
+    ref = ((g / (1.0 + np.exp(-g))) * (u @ w3.T)) @ w2.T
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Statistical semantics of P(x, i)  (Monte Carlo)
+# ---------------------------------------------------------------------------
+
+def test_load_probability_monte_carlo():
+    # P(x,i) is the probability that expert i stays in the top k when only its
+    # own noise z_i is redrawn: Pr[clean_i + z_i sp_i beats the k-th best of
+    # the others].  The selection here is a full top-k per draw.
+    r = rng(14)
+    d, n, k = 6, 8, 2
+    x = r.standard_normal((1, d))
+    wg = r.standard_normal((n, d)) / math.sqrt(d)
+    wn = r.standard_normal((n, d)) / math.sqrt(d)
+    z = r.standard_normal((1, n))
+    g = oracle.gate(x, wg, k, None, wn, z)
+    clean, sp, H = g.clean[0], g.sp[0], g.H[0]
+    draws = 1_000_000
+    mc_r = np.random.default_rng(15)
+    for i in range(n):
+        zi = mc_r.standard_normal(draws)
+        Hi = clean[i] + zi * sp[i]
+        others = np.delete(H, i)
+        beaten_by = (others[None, :] > Hi[:, None]).sum(1)
+        frac = np.mean(beaten_by < k)
+        assert abs(frac - g.P[0, i]) < 3e-3, (i, frac, g.P[0, i])
+
+
+# ---------------------------------------------------------------------------
+# Hierarchical composition
+# ---------------------------------------------------------------------------
+
+def test_hierarchical_one_group_reduces_to_flat():
+    # a = 1, k1 = 1: the primary gate is 1 with Load_primary = T and
+    # |X_0| = T, so the two-level layer is the flat layer over b experts.
+    r = rng(16)
+    T, d, b, k2, h = 25, 6, 7, 2, 5
+    x = r.standard_normal((T, d))
+    wg1 = r.standard_normal((1, d))
+    wn1 = r.standard_normal((1, d))
+    z1 = r.standard_normal((T, 1))
+    wg2 = r.standard_normal((1, b, d))
+    wn2 = r.standard_normal((1, b, d))
+    z2 = r.standard_normal((T, 1, b))
+    w1 = r.standard_normal((b, h, d))
+    w2 = r.standard_normal((b, d, h))
+    hier = oracle.forward_hier(x, wg1, wn1, z1, 1, wg2, wn2, z2, k2, w1, w2)
+    flat = oracle.forward(x, wg2[0], k2, w1, w2, w_noise=wn2[0], noise=z2[:, 0])
+    np.testing.assert_allclose(hier["y"], flat["y"], rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(hier["gate"]["importance"], flat["gate"].importance, rtol=1e-14)
+    np.testing.assert_allclose(hier["gate"]["load"], flat["gate"].load, rtol=1e-14)
+    np.testing.assert_array_equal(hier["gate"]["topk_idx"], flat["gate"].topk_idx)
+    np.testing.assert_allclose(hier["losses"], flat["losses"], rtol=1e-12, atol=1e-15)
+
+
+def test_hierarchical_matches_dense_two_level_sum():
+    # y = sum_g Gp(x)_g sum_e G_g(x)_e E_{g,e}(x), evaluated densely per token.
+    r = rng(17)
+    T, d, a, b, k1, k2, h = 9, 5, 3, 4, 2, 2, 6
+    x = r.standard_normal((T, d))
+    wg1, wn1 = r.standard_normal((a, d)), r.standard_normal((a, d))
+    z1 = r.standard_normal((T, a))
+    wg2, wn2 = r.standard_normal((a, b, d)), r.standard_normal((a, b, d))
+    z2 = r.standard_normal((T, k1, b))
+    w1 = r.standard_normal((a * b, h, d))
+    w2 = r.standard_normal((a * b, d, h))
+    out = oracle.forward_hier(x, wg1, wn1, z1, k1, wg2, wn2, z2, k2, w1, w2)
+    y = np.zeros((T, d))
+    imp = np.zeros(a * b)
+    for t in range(T):
+        Hp = x[t] @ wg1.T + z1[t] * np.logaddexp(0, x[t] @ wn1.T)
+        order = sorted(range(a), key=lambda j: (-Hp[j], j))[:k1]
+        wp = np.exp(Hp[order] - Hp[order[0]])
+        wp /= wp.sum()
+        for s, g in enumerate(order):
+            Hs = x[t] @ wg2[g].T + z2[t, s] * np.logaddexp(0, x[t] @ wn2[g].T)
+            o2 = sorted(range(b), key=lambda j: (-Hs[j], j))[:k2]
+            ws = np.exp(Hs[o2] - Hs[o2[0]])
+            ws /= ws.sum()
+            for e, w in zip(o2, ws):
+                y[t] += wp[s] * w * _ffn_np(x[t:t + 1], w1[g * b + e], w2[g * b + e])[0]
+                imp[g * b + e] += wp[s] * w
+    np.testing.assert_allclose(out["y"], y, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(out["gate"]["importance"], imp, rtol=1e-12, atol=1e-15)
