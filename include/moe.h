@@ -1,0 +1,251 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) Sparsely-Gated Mixture-of-Experts
+ * layer forward.
+ *
+ * The layer computes y = sum_i G(x)_i * E_i(x) over n experts, with the
+ * noisy top-k gate G(x) = Softmax(KeepTopK(H(x), k)),
+ *   H(x)_i = (x . W_g)_i + StandardNormal() * Softplus((x . W_noise)_i),
+ * and the importance / load auxiliary losses w * CV(.)^2.
+ *   Source: arXiv 1701.06538 summary page (xyznot.com), section
+ *   "Method and key formulas" (layer output, Noisy Top-K gating, load
+ *   balancing losses); reading notes on the same paper (chenshi221.pages.dev),
+ *   sections "Sparsely-Gated MoE layer architecture", "Noisy Top-K Gating",
+ *   "Balancing expert utilization", "Hierarchical MoE".
+ * Also supported: the Switch top-1 router with expert capacity and its
+ * n * sum f_i P_i loss (MoE survey, tufusi.com, sections 3.1 and 3.2), and
+ * renormalised top-k over a gated (SwiGLU) expert FFN (same survey, section
+ * 6.2, fine-grained routed experts).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Data pointers are DEVICE pointers (HIP device memory of the current
+ *    device), caller-owned.  The library never allocates, frees, copies to
+ *    the host or synchronises; scratch memory is the caller's workspace `ws`.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  All work is
+ *    enqueued on it; calls return after enqueueing.
+ *  - Validation is synchronous and complete before anything is enqueued:
+ *    a status other than MOE_OK means nothing was launched.  The detail of the
+ *    last failure on the calling thread is in moe_last_error().  Device faults
+ *    surface at the caller's next synchronisation.
+ *  - Required pointers must be non-NULL and 16-byte aligned.  Optional
+ *    pointers may be NULL, meaning "absent" (zero bias, noiseless gate, ...).
+ *  - All matrices are row-major and contiguous.  Weights are stored out-by-in
+ *    (like a PyTorch Linear): w_gate[i][c] multiplies x[t][c] for expert i.
+ *  - bf16 tensors are passed as raw 16-bit patterns (uint16_t storage).
+ *  - Results are bitwise deterministic for identical inputs on one device:
+ *    no floating-point atomics, fixed-order reductions.
+ *  - The calls are stateless and reentrant; concurrent calls need distinct
+ *    workspaces.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* NULL / misaligned pointer, bad size or enum */
+  MOE_ERR_UNSUPPORTED = 2, /* valid but outside what the kernels implement */
+  MOE_ERR_WORKSPACE = 3,   /* ws NULL or ws_bytes too small */
+  MOE_ERR_HIP = 4          /* a HIP launch failed */
+} moe_status;
+
+typedef enum {
+  MOE_GATE_TOPK_SOFTMAX = 0, /* G = Softmax(KeepTopK(H, k)); noisy iff w_noise != NULL */
+  MOE_GATE_SWITCH_TOP1 = 1   /* p = softmax(h) over all n; top-1 with weight p_argmax; k = 1 */
+} moe_gate_kind;
+
+typedef enum {
+  MOE_ACT_RELU = 0,  /* E(u) = max(0, u W1^T + b1) W2^T + b2 */
+  MOE_ACT_SWIGLU = 1 /* E(u) = (silu(u W1^T) * (u W3^T)) W2^T; bf16 experts only */
+} moe_act;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Layer shape and options.  All fields are 4 bytes. */
+typedef struct {
+  int32_t T;              /* tokens (all positions merged into one batch), >= 0 */
+  int32_t d_model;        /* d, multiple of 8 */
+  int32_t d_hidden;       /* expert hidden width h, multiple of 8 */
+  int32_t n_experts;      /* n (two-level layer: a*b) */
+  int32_t k;              /* experts per token, 1..min(n,64) (two-level: k1*k2) */
+  int32_t gate;           /* moe_gate_kind */
+  int32_t act;            /* moe_act */
+  int32_t expert_dtype;   /* moe_dtype of w1/w3/w2 and of x_perm */
+  int32_t n_groups;       /* two-level layer: a groups of b = n/a experts; 0 = flat */
+  int32_t k_groups;       /* two-level layer: k1 groups per token, k = k1*k2 */
+  float capacity_factor;  /* > 0: expert capacity floor(cf*T*k/n); <= 0: none */
+  float w_importance;     /* weight of CV(Importance)^2 */
+  float w_load;           /* weight of CV(Load)^2 */
+  float alpha_switch;     /* weight of n * sum_i f_i P_i */
+} moe_config;
+
+/* Weight pointers for moe_forward (a host struct holding device pointers). */
+typedef struct {
+  const float* w_gate;   /* [n_gate, d] fp32; n_gate = n (flat) or a (two-level) */
+  const float* b_gate;   /* [n_gate] fp32 per-expert logit bias, optional */
+  const float* w_noise;  /* [n_gate, d] fp32, optional (NULL = noiseless gate) */
+  const float* w_gate2;  /* two-level only: [a, b, d] secondary gates */
+  const float* w_noise2; /* two-level only: [a, b, d], optional */
+  const void* w1;        /* [n, h, d] expert_dtype */
+  const float* b1;       /* [n, h] fp32, optional (ReLU only) */
+  const void* w3;        /* [n, h, d] expert_dtype, SwiGLU only */
+  const void* w2;        /* [n, d, h] expert_dtype */
+  const float* b2;       /* [n, d] fp32, optional (ReLU only) */
+} moe_weights;
+
+/* Optional intermediate outputs of moe_forward; every field may be NULL
+ * (the forward then keeps that intermediate in the workspace). */
+typedef struct {
+  int32_t* topk_idx;   /* [T, k] */
+  float* topk_w;       /* [T, k] */
+  float* importance;   /* [n] */
+  float* load;         /* [n]; written only for a noisy gate */
+  int32_t* counts_pre; /* [n] */
+  int32_t* counts;     /* [n] */
+  int32_t* offsets;    /* [n+1] */
+  int32_t* perm;       /* [T*k] */
+  int32_t* slot_pos;   /* [T, k] */
+} moe_diag;
+
+/* Bytes of workspace that every call below accepts as sufficient (the
+ * forward's need; each stage needs at most this).  0 on an invalid config. */
+size_t moe_workspace_size(const moe_config* cfg);
+
+/* Flat gating network: logits, noise, KeepTopK, softmax, and the two
+ * auxiliary-loss vectors.
+ *   Definition: xyznot.com summary, "Method and key formulas", Noisy Top-K
+ *   gating (H, KeepTopK, G) and the Importance / P(x,i) / Load equations;
+ *   Switch router: tufusi.com survey, section 3.1.
+ * In:  x [T, d], w_gate [n, d], b_gate [n] (optional; added to the clean
+ *      logit), w_noise [n, d] (optional), noise [T, n] (the StandardNormal
+ *      draws; required iff w_noise != NULL), all fp32.
+ * Out: topk_idx [T, k] int32 -- slot s holds the expert of rank s: descending
+ *      H, lower index first on equal H (-0.0 == +0.0);
+ *      topk_w [T, k] fp32 -- softmax over the kept H (Switch: p_argmax);
+ *      importance [n] fp32 -- sum over tokens of the dense gate G (Switch:
+ *      of the full softmax p);
+ *      load [n] fp32 -- sum over tokens of P(x,i) = Phi((clean_i - thr_i) /
+ *      Softplus(raw_i)), thr_i = H_(k+1) if i is kept else H_(k); required iff
+ *      w_noise != NULL, ignored otherwise (may be NULL).
+ * Flat configs only (n_groups == 0); n <= 2048. */
+moe_status moe_gate(const moe_config* cfg, const float* x, const float* w_gate,
+                    const float* b_gate, const float* w_noise, const float* noise,
+                    int32_t* topk_idx, float* topk_w, float* importance, float* load, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/* Two-level gate: a primary gate picks k1 of a groups, then each chosen
+ * group's own secondary gate picks k2 of its b experts.
+ *   Definition: chenshi221.pages.dev notes, section "Hierarchical MoE"; the
+ *   xyznot.com summary's key-term entry on hierarchical mixtures of experts.
+ * In:  x [T, d]; w_gate/w_noise [a, d], b_gate [a] (optional), noise [T, a];
+ *      w_gate2/w_noise2 [a, b, d]; noise2 [T, k1, b] (draws of the secondary
+ *      gate for the token's primary slot s).  Noise pointers are required
+ *      iff the matching w_noise is given.
+ * Out: topk_idx [T, k1*k2]: slot s*k2+s2 = g_s*b + e (g_s primary slot s,
+ *      e the secondary slot s2); topk_w = w_primary[s] * w_secondary[s2];
+ *      importance [a*b] = sum of those products per expert;
+ *      load [a*b] = Load_primary[g] * Load_g[e] / |X_g| (0 when no token
+ *      reaches g), Load_g the secondary gate's load over the tokens X_g routed
+ *      to g; required iff w_noise != NULL (both levels must then be noisy).
+ * cfg->n_groups = a, cfg->k_groups = k1, cfg->k = k1*k2, n = a*b. */
+moe_status moe_gate_hier(const moe_config* cfg, const float* x, const float* w_gate,
+                         const float* b_gate, const float* w_noise, const float* noise,
+                         const float* w_gate2, const float* w_noise2, const float* noise2,
+                         int32_t* topk_idx, float* topk_w, float* importance, float* load,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* Merge every position routed to an expert into one contiguous batch.
+ *   Definition: chenshi221.pages.dev notes, "Engineering" (all time steps
+ *   merged into one batch); tufusi.com survey 3.2 (expert capacity C =
+ *   tokens/E * capacity factor; overflow passes through the residual).
+ * In:  topk_idx [T, k], x [T, d] fp32.
+ * Out: counts_pre [n] (slots routed to each expert), counts [n] =
+ *      min(counts_pre, C) with C = floor(cf*T*k/n) (no limit if cf <= 0),
+ *      offsets [n+1] = exclusive scan of counts (offsets[n] = kept rows),
+ *      perm [T*k] (row -> token; tokens ascend within each expert; rows >=
+ *      offsets[n] untouched), slot_pos [T, k] (row of each slot, -1 when the
+ *      slot was over capacity; over-capacity slots are dropped first come
+ *      first served in (token, slot) order),
+ *      x_perm [T*k, d] = x[perm[row]] converted to expert_dtype (bf16 round
+ *      to nearest even).
+ * topk_idx entries must lie in [0, n). */
+moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, const float* x,
+                        int32_t* counts_pre, int32_t* counts, int32_t* offsets, int32_t* perm,
+                        int32_t* slot_pos, void* x_perm, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/* All experts on their merged batches (one grouped launch per layer).
+ *   Definition: chenshi221.pages.dev notes, "Sparsely-Gated MoE layer
+ *   architecture" (identical one-hidden-layer ReLU FFNs, own parameters);
+ *   tufusi.com survey 6.2 (fine-grained routed experts, d_ff = 2048).
+ * In:  x_perm [T*k, d] expert_dtype; offsets [n+1] (rows of expert e are
+ *      offsets[e] .. offsets[e+1]-1); w1 [n, h, d], w3 [n, h, d] (SwiGLU),
+ *      w2 [n, d, h] in expert_dtype; b1 [n, h], b2 [n, d] fp32 optional
+ *      (ReLU only).  bf16 experts accumulate in fp32; the hidden activations
+ *      are rounded to bf16 before the second product.
+ * Out: y_perm [T*k, d] fp32 (rows >= offsets[n] untouched). */
+moe_status moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32_t* offsets,
+                          const void* w1, const float* b1, const void* w3, const void* w2,
+                          const float* b2, float* y_perm, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* y[t] = sum over the token's slots s (in slot order) of topk_w[t,s] *
+ * y_perm[slot_pos[t,s]]; slots with slot_pos < 0 add nothing.  A gather:
+ * every output row is written exactly once, no atomics.
+ *   Definition: xyznot.com summary, "Method and key formulas" (layer output).
+ * In: y_perm [*, d] fp32, slot_pos [T, k], topk_w [T, k].  Out: y [T, d] fp32. */
+moe_status moe_combine(const moe_config* cfg, const float* y_perm, const int32_t* slot_pos,
+                       const float* topk_w, float* y, void* stream);
+
+/* Auxiliary losses, losses[3] fp32 on the device:
+ *   losses[0] = w_importance * CV(importance)^2
+ *   losses[1] = w_load * CV(load)^2 (0 when load == NULL)
+ *   losses[2] = alpha_switch * n * sum_i f_i P_i, f_i = counts_pre[i]/(T*k),
+ *               P_i = importance[i]/T (0 when T == 0)
+ * CV uses the population variance; CV^2 = 0 when the mean is 0.
+ *   Definition: xyznot.com summary, "Method and key formulas" (L_importance,
+ *   L_load); tufusi.com survey 3.2 (Switch auxiliary loss). */
+moe_status moe_aux_loss(const moe_config* cfg, const float* importance, const float* load,
+                        const int32_t* counts_pre, float* losses, void* stream);
+
+/* The whole layer: gate (flat or two-level), dispatch, experts, combine,
+ * losses, all on `stream` with no host synchronisation.
+ * In:  weights (see moe_weights), x [T, d], noise [T, n_gate] (required iff
+ *      weights->w_noise), noise2 [T, k1, b] (two-level, iff w_noise2).
+ * Out: y [T, d] fp32 (no residual added), losses [3] fp32 (as moe_aux_loss),
+ *      diag: optional intermediates (may be NULL). */
+moe_status moe_forward(const moe_config* cfg, const moe_weights* weights, const float* x,
+                       const float* noise, const float* noise2, float* y, float* losses,
+                       const moe_diag* diag, void* ws, size_t ws_bytes, void* stream);
+
+/* Kernel timing, a tracing aid (off by default).  moe_profile_enable(1)
+ * clears earlier results and starts bracketing every kernel launch of the
+ * library with two HIP events recorded on that launch's stream;
+ * moe_profile_enable(0) stops recording.  moe_profile_collect() waits for the
+ * recorded events, folds them into per-kernel totals and returns the number
+ * of distinct kernels; moe_profile_entry(i, ...) copies kernel i's name
+ * (NUL-terminated, truncated to name_len), its total milliseconds and its
+ * launch count, or returns MOE_ERR_INVALID_ARG for a bad index or NULL
+ * output.  Process-wide state, safe to call from several threads. */
+moe_status moe_profile_enable(int on);
+int moe_profile_collect(void);
+moe_status moe_profile_entry(int i, char* name, size_t name_len, double* total_ms,
+                             long long* launches);
+
+/* Static text for a status code. */
+const char* moe_status_string(moe_status status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

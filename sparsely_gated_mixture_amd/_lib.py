@@ -1,0 +1,240 @@
+"""ctypes binding of libmoe.so (argument marshalling only).
+
+Each function has the name and argument order of the C entry point in
+include/moe.h.  Tensor arguments are torch tensors on the GPU (or None for an
+optional pointer; plain integers are passed through as raw addresses).  The
+stream defaults to torch's current HIP stream.  A non-OK status raises
+MoEError carrying the library's message.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = 1
+MOE_ERR_UNSUPPORTED = 2
+MOE_ERR_WORKSPACE = 3
+MOE_ERR_HIP = 4
+
+EXPORTS = ["moe_workspace_size", "moe_gate", "moe_gate_hier", "moe_dispatch", "moe_expert_ffn",
+           "moe_combine", "moe_aux_loss", "moe_forward", "moe_status_string", "moe_last_error",
+           "moe_profile_enable", "moe_profile_collect", "moe_profile_entry"]
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"status {status}: {msg}")
+        self.status = status
+
+
+class MoeConfig(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d_model", ctypes.c_int32), ("d_hidden", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("k", ctypes.c_int32), ("gate", ctypes.c_int32),
+                ("act", ctypes.c_int32), ("expert_dtype", ctypes.c_int32),
+                ("n_groups", ctypes.c_int32), ("k_groups", ctypes.c_int32),
+                ("capacity_factor", ctypes.c_float), ("w_importance", ctypes.c_float),
+                ("w_load", ctypes.c_float), ("alpha_switch", ctypes.c_float)]
+
+
+_vp = ctypes.c_void_p
+
+
+class MoeWeights(ctypes.Structure):
+    _fields_ = [("w_gate", _vp), ("b_gate", _vp), ("w_noise", _vp), ("w_gate2", _vp),
+                ("w_noise2", _vp), ("w1", _vp), ("b1", _vp), ("w3", _vp), ("w2", _vp),
+                ("b2", _vp)]
+
+
+class MoeDiag(ctypes.Structure):
+    _fields_ = [("topk_idx", _vp), ("topk_w", _vp), ("importance", _vp), ("load", _vp),
+                ("counts_pre", _vp), ("counts", _vp), ("offsets", _vp), ("perm", _vp),
+                ("slot_pos", _vp)]
+
+
+_lib = None
+
+
+def load_library():
+    """Load libmoe.so; fails loudly when the HIP library has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python sparsely_gated_mixture_amd/build.py`")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    S = ctypes.c_size_t
+    cfgp = ctypes.POINTER(MoeConfig)
+    L.moe_workspace_size.argtypes = [cfgp]
+    L.moe_workspace_size.restype = S
+    L.moe_gate.argtypes = [cfgp] + [P] * 9 + [P, S, P]
+    L.moe_gate_hier.argtypes = [cfgp] + [P] * 12 + [P, S, P]
+    L.moe_dispatch.argtypes = [cfgp] + [P] * 8 + [P, S, P]
+    L.moe_expert_ffn.argtypes = [cfgp] + [P] * 8 + [P, S, P]
+    L.moe_combine.argtypes = [cfgp] + [P] * 4 + [P]
+    L.moe_aux_loss.argtypes = [cfgp] + [P] * 4 + [P]
+    L.moe_forward.argtypes = [cfgp, ctypes.POINTER(MoeWeights)] + [P] * 5 + \
+        [ctypes.POINTER(MoeDiag), P, S, P]
+    L.moe_status_string.argtypes = [ctypes.c_int]
+    L.moe_status_string.restype = ctypes.c_char_p
+    L.moe_last_error.argtypes = []
+    L.moe_last_error.restype = ctypes.c_char_p
+    L.moe_profile_enable.argtypes = [ctypes.c_int]
+    L.moe_profile_enable.restype = ctypes.c_int
+    L.moe_profile_collect.argtypes = []
+    L.moe_profile_collect.restype = ctypes.c_int
+    L.moe_profile_entry.argtypes = [ctypes.c_int, ctypes.c_char_p, S,
+                                    ctypes.POINTER(ctypes.c_double),
+                                    ctypes.POINTER(ctypes.c_longlong)]
+    L.moe_profile_entry.restype = ctypes.c_int
+    for name in ("moe_gate", "moe_gate_hier", "moe_dispatch", "moe_expert_ffn", "moe_combine",
+                 "moe_aux_loss", "moe_forward"):
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def make_config(cfg) -> MoeConfig:
+    """MoeConfig from anything with the moe_config field names (e.g. a
+    workloads.MoEConfig)."""
+    if isinstance(cfg, MoeConfig):
+        return cfg
+    return MoeConfig(int(cfg.T), int(cfg.d_model), int(cfg.d_hidden), int(cfg.n_experts),
+                     int(cfg.k), int(cfg.gate), int(cfg.act), int(cfg.expert_dtype),
+                     int(cfg.n_groups), int(cfg.k_groups), float(cfg.capacity_factor),
+                     float(cfg.w_importance), float(cfg.w_load), float(cfg.alpha_switch))
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ws(ws):
+    if ws is None:
+        return None, 0
+    if isinstance(ws, tuple):
+        return ws
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
+def _check(status: int):
+    if status != MOE_OK:
+        L = load_library()
+        raise MoEError(status, (L.moe_last_error() or b"").decode())
+
+
+def moe_status_string(status: int) -> str:
+    return load_library().moe_status_string(status).decode()
+
+
+def moe_last_error() -> str:
+    return (load_library().moe_last_error() or b"").decode()
+
+
+def moe_workspace_size(cfg) -> int:
+    c = make_config(cfg)
+    return load_library().moe_workspace_size(ctypes.byref(c))
+
+
+def moe_gate(cfg, x, w_gate, b_gate, w_noise, noise, topk_idx, topk_w, importance, load, ws,
+             stream=None):
+    c = make_config(cfg)
+    wp, wb = _ws(ws)
+    _check(load_library().moe_gate(ctypes.byref(c), _ptr(x), _ptr(w_gate), _ptr(b_gate),
+                                   _ptr(w_noise), _ptr(noise), _ptr(topk_idx), _ptr(topk_w),
+                                   _ptr(importance), _ptr(load), wp, wb, _stream(stream)))
+
+
+def moe_gate_hier(cfg, x, w_gate, b_gate, w_noise, noise, w_gate2, w_noise2, noise2, topk_idx,
+                  topk_w, importance, load, ws, stream=None):
+    c = make_config(cfg)
+    wp, wb = _ws(ws)
+    _check(load_library().moe_gate_hier(
+        ctypes.byref(c), _ptr(x), _ptr(w_gate), _ptr(b_gate), _ptr(w_noise), _ptr(noise),
+        _ptr(w_gate2), _ptr(w_noise2), _ptr(noise2), _ptr(topk_idx), _ptr(topk_w),
+        _ptr(importance), _ptr(load), wp, wb, _stream(stream)))
+
+
+def moe_dispatch(cfg, topk_idx, x, counts_pre, counts, offsets, perm, slot_pos, x_perm, ws,
+                 stream=None):
+    c = make_config(cfg)
+    wp, wb = _ws(ws)
+    _check(load_library().moe_dispatch(ctypes.byref(c), _ptr(topk_idx), _ptr(x),
+                                       _ptr(counts_pre), _ptr(counts), _ptr(offsets),
+                                       _ptr(perm), _ptr(slot_pos), _ptr(x_perm), wp, wb,
+                                       _stream(stream)))
+
+
+def moe_expert_ffn(cfg, x_perm, offsets, w1, b1, w3, w2, b2, y_perm, ws, stream=None):
+    c = make_config(cfg)
+    wp, wb = _ws(ws)
+    _check(load_library().moe_expert_ffn(ctypes.byref(c), _ptr(x_perm), _ptr(offsets), _ptr(w1),
+                                         _ptr(b1), _ptr(w3), _ptr(w2), _ptr(b2), _ptr(y_perm),
+                                         wp, wb, _stream(stream)))
+
+
+def moe_combine(cfg, y_perm, slot_pos, topk_w, y, stream=None):
+    c = make_config(cfg)
+    _check(load_library().moe_combine(ctypes.byref(c), _ptr(y_perm), _ptr(slot_pos),
+                                      _ptr(topk_w), _ptr(y), _stream(stream)))
+
+
+def moe_aux_loss(cfg, importance, load, counts_pre, losses, stream=None):
+    c = make_config(cfg)
+    _check(load_library().moe_aux_loss(ctypes.byref(c), _ptr(importance), _ptr(load),
+                                       _ptr(counts_pre), _ptr(losses), _stream(stream)))
+
+
+def make_weights(w_gate, b_gate=None, w_noise=None, w_gate2=None, w_noise2=None, w1=None,
+                 b1=None, w3=None, w2=None, b2=None) -> MoeWeights:
+    return MoeWeights(_ptr(w_gate), _ptr(b_gate), _ptr(w_noise), _ptr(w_gate2), _ptr(w_noise2),
+                      _ptr(w1), _ptr(b1), _ptr(w3), _ptr(w2), _ptr(b2))
+
+
+def make_diag(**kw) -> MoeDiag:
+    return MoeDiag(*[_ptr(kw.get(f)) for f, _ in MoeDiag._fields_])
+
+
+def moe_forward(cfg, weights: MoeWeights, x, noise, noise2, y, losses, diag: MoeDiag | None, ws,
+                stream=None):
+    c = make_config(cfg)
+    wp, wb = _ws(ws)
+    _check(load_library().moe_forward(ctypes.byref(c), ctypes.byref(weights), _ptr(x),
+                                      _ptr(noise), _ptr(noise2), _ptr(y), _ptr(losses),
+                                      ctypes.byref(diag) if diag is not None else None, wp, wb,
+                                      _stream(stream)))
+
+
+def moe_profile_enable(on: bool) -> None:
+    _check(load_library().moe_profile_enable(1 if on else 0))
+
+
+def moe_profile_collect() -> int:
+    return load_library().moe_profile_collect()
+
+
+def moe_profile_entry(i: int):
+    """(kernel name, total milliseconds, launches) of collected entry i."""
+    buf = ctypes.create_string_buffer(128)
+    ms = ctypes.c_double()
+    n = ctypes.c_longlong()
+    _check(load_library().moe_profile_entry(i, buf, 128, ctypes.byref(ms), ctypes.byref(n)))
+    return buf.value.decode(), ms.value, n.value

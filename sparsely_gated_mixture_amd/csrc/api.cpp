@@ -1,0 +1,720 @@
+// C ABI of the MoE layer forward: argument validation, workspace layout and
+// the launch sequence of each stage.  Validation runs before any HIP call,
+// so a failing call enqueues nothing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/moe.h"
+#include "launch.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+#define HIP_TRY(expr)                                                              \
+  do {                                                                             \
+    hipError_t e_ = (expr);                                                        \
+    if (e_ != hipSuccess)                                                          \
+      return fail(MOE_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_));            \
+  } while (0)
+
+constexpr int kMaxGateN = 2048;     // experts per gate (64 lanes x 32 registers)
+constexpr int kMaxExperts = 16384;  // dispatch histogram in LDS
+constexpr int kMaxK = 64;           // one slot per lane
+constexpr int kSecondaryBM = 64;    // row tile of the two-level secondary gate
+constexpr int kF32ExpertBM = 64;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Required pointer.  A buffer that holds no element (empty == true, e.g. a
+// per-token array when T == 0) may be NULL.
+moe_status need(const void* p, const char* name, bool empty = false) {
+  if (!p && empty) return MOE_OK;
+  if (!p) return fail(MOE_ERR_INVALID_ARG, "%s must not be NULL", name);
+  if (!aligned16(p)) return fail(MOE_ERR_INVALID_ARG, "%s must be 16-byte aligned", name);
+  return MOE_OK;
+}
+moe_status optional(const void* p, const char* name) {
+  if (p && !aligned16(p)) return fail(MOE_ERR_INVALID_ARG, "%s must be 16-byte aligned", name);
+  return MOE_OK;
+}
+
+#define CHECK(expr)                     \
+  do {                                  \
+    moe_status s_ = (expr);             \
+    if (s_ != MOE_OK) return s_;        \
+  } while (0)
+
+moe_status validate(const moe_config* c) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "cfg must not be NULL");
+  if (c->T < 0) return fail(MOE_ERR_INVALID_ARG, "T must be >= 0 (got %d)", c->T);
+  if (c->d_model <= 0 || c->d_hidden <= 0)
+    return fail(MOE_ERR_INVALID_ARG, "d_model and d_hidden must be positive");
+  if (c->d_model % 8 || c->d_hidden % 8)
+    return fail(MOE_ERR_UNSUPPORTED, "d_model (%d) and d_hidden (%d) must be multiples of 8",
+                c->d_model, c->d_hidden);
+  if (c->n_experts < 1) return fail(MOE_ERR_INVALID_ARG, "n_experts must be >= 1");
+  if (c->k < 1 || c->k > c->n_experts)
+    return fail(MOE_ERR_INVALID_ARG, "k must be in [1, n_experts] (k=%d, n=%d)", c->k,
+                c->n_experts);
+  if (c->k > kMaxK) return fail(MOE_ERR_UNSUPPORTED, "k must be <= %d", kMaxK);
+  if (c->gate != MOE_GATE_TOPK_SOFTMAX && c->gate != MOE_GATE_SWITCH_TOP1)
+    return fail(MOE_ERR_INVALID_ARG, "unknown gate kind %d", c->gate);
+  if (c->act != MOE_ACT_RELU && c->act != MOE_ACT_SWIGLU)
+    return fail(MOE_ERR_INVALID_ARG, "unknown activation %d", c->act);
+  if (c->expert_dtype != MOE_F32 && c->expert_dtype != MOE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "unknown expert dtype %d", c->expert_dtype);
+  if (c->gate == MOE_GATE_SWITCH_TOP1 && c->k != 1)
+    return fail(MOE_ERR_INVALID_ARG, "the Switch router needs k = 1");
+  if (c->act == MOE_ACT_SWIGLU && c->expert_dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "SwiGLU experts are implemented for bf16 only");
+  if (!std::isfinite(c->capacity_factor))
+    return fail(MOE_ERR_INVALID_ARG, "capacity_factor must be finite");
+  if (c->n_experts > kMaxExperts)
+    return fail(MOE_ERR_UNSUPPORTED, "n_experts must be <= %d", kMaxExperts);
+  if ((long long)c->T * c->k > (1LL << 30))
+    return fail(MOE_ERR_UNSUPPORTED, "T*k must be <= 2^30");
+  if (c->n_groups < 0) return fail(MOE_ERR_INVALID_ARG, "n_groups must be >= 0");
+  if (c->n_groups > 0) {
+    const int a = c->n_groups;
+    if (c->n_experts % a)
+      return fail(MOE_ERR_INVALID_ARG, "n_experts (%d) must be a multiple of n_groups (%d)",
+                  c->n_experts, a);
+    if (c->gate != MOE_GATE_TOPK_SOFTMAX)
+      return fail(MOE_ERR_INVALID_ARG, "the two-level layer uses the top-k softmax gate");
+    if (c->k_groups < 1 || c->k_groups > a || c->k % c->k_groups)
+      return fail(MOE_ERR_INVALID_ARG, "k_groups must be in [1, n_groups] and divide k");
+    const int b = c->n_experts / a, k2 = c->k / c->k_groups;
+    if (k2 > b) return fail(MOE_ERR_INVALID_ARG, "k / k_groups must be <= experts per group");
+    if (a > kMaxGateN || b > kMaxGateN)
+      return fail(MOE_ERR_UNSUPPORTED, "gates are limited to %d experts", kMaxGateN);
+  } else if (c->n_experts > kMaxGateN) {
+    return fail(MOE_ERR_UNSUPPORTED, "a flat gate is limited to %d experts", kMaxGateN);
+  }
+  return MOE_OK;
+}
+
+long long capacity(const moe_config& c) {
+  if (!(c.capacity_factor > 0.f)) return (long long)1 << 62;
+  return (long long)std::floor((double)c.capacity_factor * (double)c.T * (double)c.k /
+                               (double)c.n_experts);
+}
+
+long long round_up(long long v, long long m) { return (v + m - 1) / m * m; }
+
+// ---------------------------------------------------------------------------
+// Workspace layout.  [stage scratch: max over gate / dispatch / ffn]
+// [forward intermediates].  Stage calls use only the first part.
+// ---------------------------------------------------------------------------
+struct Region {
+  size_t off = 0, bytes = 0;
+};
+
+struct Plan {
+  // gate (flat or primary)
+  int n_gate = 0, ldl = 0, gemm_bm = 128, rows_per_block = 16, nparts = 0;
+  Region logits, part_imp, part_load;
+  // two-level extras
+  int a = 0, b = 0, k1 = 0, k2 = 0, ldl2 = 0, max_tiles2 = 0;
+  Region prim_idx, prim_w, prim_imp, prim_load, g_counts_pre, g_counts, g_offsets, g_perm,
+      g_slot, g_chunk_hist, g_chunk_base, t2_expert, t2_row0, t2_count, part2_imp, part2_load;
+  // dispatch
+  int nchunks = 0;
+  Region chunk_hist, chunk_base;
+  // ffn
+  int ffn_bm = 128, max_mtiles = 0;
+  Region t_expert, t_row0, t_count, hidden;
+  size_t gate_bytes = 0, dispatch_bytes = 0, ffn_bytes = 0, stage_bytes = 0;
+  // forward intermediates
+  Region f_idx, f_w, f_imp, f_load, f_counts_pre, f_counts, f_offsets, f_perm, f_slot, f_xperm,
+      f_yperm;
+  size_t total = 0;
+};
+
+struct Cursor {
+  size_t at;
+  Region take(size_t bytes) {
+    Region r;
+    r.off = at;
+    r.bytes = bytes;
+    at += (size_t)round_up((long long)bytes, 256);
+    return r;
+  }
+};
+
+Plan make_plan(const moe_config& c) {
+  Plan p;
+  const long long T = c.T, d = c.d_model, h = c.d_hidden, n = c.n_experts, k = c.k;
+  const long long A = T * k;
+  const bool hier = c.n_groups > 0;
+  p.n_gate = hier ? c.n_groups : c.n_experts;
+  const int ncols = 2 * p.n_gate;  // clean | raw (the raw half is unused when noiseless)
+  p.ldl = (int)round_up(ncols, 4);
+  {
+    const long long t128 = ((T + 127) / 128) * ((ncols + 127) / 128);
+    p.gemm_bm = t128 >= 256 ? 128 : 64;
+  }
+  {
+    long long rpb = std::max(16LL, round_up((T + 1023) / 1024, 4));
+    p.rows_per_block = (int)rpb;
+    p.nparts = (int)((T + rpb - 1) / rpb);
+  }
+  // gate scratch
+  Cursor g{0};
+  if (hier) {
+    p.a = c.n_groups;
+    p.b = c.n_experts / c.n_groups;
+    p.k1 = c.k_groups;
+    p.k2 = c.k / c.k_groups;
+    p.ldl2 = (int)round_up(2 * p.b, 4);
+    p.max_tiles2 = (int)((T * p.k1 + kSecondaryBM - 1) / kSecondaryBM + p.a);
+    const long long logit_elems = std::max(T * p.ldl, T * p.k1 * p.ldl2);
+    p.logits = g.take(logit_elems * 4);
+    p.part_imp = g.take((size_t)p.nparts * p.a * 4);
+    p.part_load = g.take((size_t)p.nparts * p.a * 4);
+    p.prim_idx = g.take(T * p.k1 * 4);
+    p.prim_w = g.take(T * p.k1 * 4);
+    p.prim_imp = g.take(p.a * 4);
+    p.prim_load = g.take(p.a * 4);
+    p.g_counts_pre = g.take(p.a * 4);
+    p.g_counts = g.take(p.a * 4);
+    p.g_offsets = g.take((p.a + 1) * 4);
+    p.g_perm = g.take(std::max(1LL, T * p.k1) * 4);
+    p.g_slot = g.take(std::max(1LL, T * p.k1) * 4);
+    const long long gchunks = (T * p.k1 + kDispatchChunk - 1) / kDispatchChunk;
+    p.g_chunk_hist = g.take(std::max(1LL, gchunks) * p.a * 4);
+    p.g_chunk_base = g.take(std::max(1LL, gchunks) * p.a * 4);
+    p.t2_expert = g.take((size_t)p.max_tiles2 * 4);
+    p.t2_row0 = g.take((size_t)p.max_tiles2 * 4);
+    p.t2_count = g.take(4);
+    p.part2_imp = g.take((size_t)p.max_tiles2 * p.b * 4);
+    p.part2_load = g.take((size_t)p.max_tiles2 * p.b * 4);
+  } else {
+    p.logits = g.take(T * p.ldl * 4);
+    p.part_imp = g.take((size_t)p.nparts * n * 4);
+    p.part_load = g.take((size_t)p.nparts * n * 4);
+  }
+  p.gate_bytes = g.at;
+  // dispatch scratch
+  Cursor dsp{0};
+  p.nchunks = (int)((A + kDispatchChunk - 1) / kDispatchChunk);
+  p.chunk_hist = dsp.take(std::max(1LL, (long long)p.nchunks) * n * 4);
+  p.chunk_base = dsp.take(std::max(1LL, (long long)p.nchunks) * n * 4);
+  p.dispatch_bytes = dsp.at;
+  // ffn scratch
+  Cursor f{0};
+  p.ffn_bm = c.expert_dtype == MOE_BF16 ? kBf16BM : kF32ExpertBM;
+  p.max_mtiles = (int)((A + p.ffn_bm - 1) / p.ffn_bm + n);
+  p.t_expert = f.take((size_t)p.max_mtiles * 4);
+  p.t_row0 = f.take((size_t)p.max_mtiles * 4);
+  p.t_count = f.take(4);
+  p.hidden = f.take(std::max(1LL, A) * h * (c.expert_dtype == MOE_BF16 ? 2 : 4));
+  p.ffn_bytes = f.at;
+  p.stage_bytes = std::max(p.gate_bytes, std::max(p.dispatch_bytes, p.ffn_bytes));
+  // forward intermediates
+  Cursor w{p.stage_bytes};
+  const long long A1 = std::max(1LL, A);
+  p.f_idx = w.take(A1 * 4);
+  p.f_w = w.take(A1 * 4);
+  p.f_imp = w.take(n * 4);
+  p.f_load = w.take(n * 4);
+  p.f_counts_pre = w.take(n * 4);
+  p.f_counts = w.take(n * 4);
+  p.f_offsets = w.take((n + 1) * 4);
+  p.f_perm = w.take(A1 * 4);
+  p.f_slot = w.take(A1 * 4);
+  p.f_xperm = w.take(A1 * d * (c.expert_dtype == MOE_BF16 ? 2 : 4));
+  p.f_yperm = w.take(A1 * d * 4);
+  p.total = w.at;
+  return p;
+}
+
+template <typename Tp>
+Tp* at(void* ws, const Region& r) {
+  return (Tp*)((char*)ws + r.off);
+}
+
+moe_status check_ws(void* ws, size_t ws_bytes, size_t need_bytes, const char* what) {
+  if (need_bytes == 0) return MOE_OK;
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "%s: ws must not be NULL", what);
+  if (!aligned16(ws)) return fail(MOE_ERR_INVALID_ARG, "%s: ws must be 16-byte aligned", what);
+  if (ws_bytes < need_bytes)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes is too small (needs %zu)", what,
+                ws_bytes, need_bytes);
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Stages (arguments already validated).
+// ---------------------------------------------------------------------------
+moe_status run_gate(const moe_config& c, const Plan& p, const float* x, const float* w_gate,
+                    const float* b_gate, const float* w_noise, const float* noise,
+                    int32_t* topk_idx, float* topk_w, float* importance, float* load, void* ws,
+                    hipStream_t s) {
+  const int n = c.n_experts;
+  const bool noisy = w_noise != nullptr;
+  float* logits = at<float>(ws, p.logits);
+  if (c.T > 0) {
+    GemmF32Args g{};
+    g.A = x;
+    g.lda = c.d_model;
+    g.B1 = w_gate;
+    g.B2 = w_noise;
+    g.n1 = n;
+    g.N = noisy ? 2 * n : n;
+    g.K = c.d_model;
+    g.C = logits;
+    g.ldc = p.ldl;
+    g.M = c.T;
+    g.mtiles = (c.T + p.gemm_bm - 1) / p.gemm_bm;
+    g.max_mtiles = g.mtiles;
+    HIP_TRY(launch_gemm_f32(g, p.gemm_bm, s));
+  }
+  TopkArgs t{};
+  t.rows = c.T;
+  t.n = n;
+  t.k = c.k;
+  t.switch_mode = c.gate == MOE_GATE_SWITCH_TOP1;
+  t.noisy = noisy;
+  t.logits = logits;
+  t.ldl = p.ldl;
+  t.bias = b_gate;
+  t.noise = noise;
+  t.topk_idx = topk_idx;
+  t.topk_w = topk_w;
+  t.part_imp = at<float>(ws, p.part_imp);
+  t.part_load = noisy ? at<float>(ws, p.part_load) : nullptr;
+  t.rows_per_block = p.rows_per_block;
+  HIP_TRY(launch_topk(t, s));
+  HIP_TRY(launch_colsum(t.part_imp, p.nparts, n, importance, s));
+  if (noisy) HIP_TRY(launch_colsum(t.part_load, p.nparts, n, load, s));
+  return MOE_OK;
+}
+
+moe_status run_gate_hier(const moe_config& c, const Plan& p, const float* x, const float* w_gate,
+                         const float* b_gate, const float* w_noise, const float* noise,
+                         const float* w_gate2, const float* w_noise2, const float* noise2,
+                         int32_t* topk_idx, float* topk_w, float* importance, float* load,
+                         void* ws, hipStream_t s) {
+  const bool noisy = w_noise != nullptr;
+  const int a = p.a, b = p.b, k1 = p.k1;
+  float* logits = at<float>(ws, p.logits);
+  int32_t* prim_idx = at<int32_t>(ws, p.prim_idx);
+  float* prim_w = at<float>(ws, p.prim_w);
+  // 1. primary gate over the a groups
+  if (c.T > 0) {
+    GemmF32Args g{};
+    g.A = x;
+    g.lda = c.d_model;
+    g.B1 = w_gate;
+    g.B2 = w_noise;
+    g.n1 = a;
+    g.N = noisy ? 2 * a : a;
+    g.K = c.d_model;
+    g.C = logits;
+    g.ldc = p.ldl;
+    g.M = c.T;
+    g.mtiles = (c.T + p.gemm_bm - 1) / p.gemm_bm;
+    g.max_mtiles = g.mtiles;
+    HIP_TRY(launch_gemm_f32(g, p.gemm_bm, s));
+  }
+  TopkArgs t{};
+  t.rows = c.T;
+  t.n = a;
+  t.k = k1;
+  t.noisy = noisy;
+  t.logits = logits;
+  t.ldl = p.ldl;
+  t.bias = b_gate;
+  t.noise = noise;
+  t.topk_idx = prim_idx;
+  t.topk_w = prim_w;
+  t.part_imp = at<float>(ws, p.part_imp);
+  t.part_load = noisy ? at<float>(ws, p.part_load) : nullptr;
+  t.rows_per_block = p.rows_per_block;
+  HIP_TRY(launch_topk(t, s));
+  HIP_TRY(launch_colsum(t.part_imp, p.nparts, a, at<float>(ws, p.prim_imp), s));
+  if (noisy) HIP_TRY(launch_colsum(t.part_load, p.nparts, a, at<float>(ws, p.prim_load), s));
+  // 2. rows of each group (tokens ascending)
+  int32_t* g_counts_pre = at<int32_t>(ws, p.g_counts_pre);
+  int32_t* g_offsets = at<int32_t>(ws, p.g_offsets);
+  int32_t* g_perm = at<int32_t>(ws, p.g_perm);
+  HIP_TRY(launch_dispatch(prim_idx, c.T, k1, a, (long long)1 << 62, g_counts_pre,
+                          at<int32_t>(ws, p.g_counts), g_offsets, g_perm,
+                          at<int32_t>(ws, p.g_slot), at<int32_t>(ws, p.g_chunk_hist),
+                          at<int32_t>(ws, p.g_chunk_base), s));
+  int32_t* t2e = at<int32_t>(ws, p.t2_expert);
+  int32_t* t2r = at<int32_t>(ws, p.t2_row0);
+  int32_t* t2c = at<int32_t>(ws, p.t2_count);
+  HIP_TRY(launch_tilemap(g_offsets, a, kSecondaryBM, t2e, t2r, t2c, s));
+  // 3. secondary logits: each group's own gate over its rows
+  {
+    GemmF32Args g{};
+    g.A = x;
+    g.lda = c.d_model;
+    g.rowmap = g_perm;
+    g.B1 = w_gate2;
+    g.B2 = w_noise2;
+    g.strideB1 = (long long)b * c.d_model;
+    g.strideB2 = (long long)b * c.d_model;
+    g.n1 = b;
+    g.N = w_noise2 ? 2 * b : b;
+    g.K = c.d_model;
+    g.C = logits;
+    g.ldc = p.ldl2;
+    g.tile_expert = t2e;
+    g.tile_row0 = t2r;
+    g.offsets = g_offsets;
+    g.tile_count = t2c;
+    g.max_mtiles = p.max_tiles2;
+    HIP_TRY(launch_gemm_f32(g, kSecondaryBM, s));
+  }
+  // 4. secondary top-k per (token, primary slot) row
+  TopkArgs u{};
+  u.n = b;
+  u.k = p.k2;
+  u.noisy = w_noise2 != nullptr;
+  u.logits = logits;
+  u.ldl = p.ldl2;
+  u.noise = noise2;
+  u.topk_idx = topk_idx;
+  u.topk_w = topk_w;
+  u.part_imp = at<float>(ws, p.part2_imp);
+  u.part_load = u.noisy ? at<float>(ws, p.part2_load) : nullptr;
+  u.row_token = g_perm;
+  u.prim_idx = prim_idx;
+  u.prim_w = prim_w;
+  u.k1 = k1;
+  u.tile_expert = t2e;
+  u.tile_row0 = t2r;
+  u.offsets = g_offsets;
+  u.tile_count = t2c;
+  u.max_tiles = p.max_tiles2;
+  u.tile_rows = kSecondaryBM;
+  HIP_TRY(launch_topk(u, s));
+  // 5. two-level importance / load vectors
+  const bool both_noisy = noisy && w_noise2 != nullptr;
+  HIP_TRY(launch_hier_finalize(u.part_imp, both_noisy ? u.part_load : nullptr, t2e, t2c,
+                               g_counts_pre, at<float>(ws, p.prim_load), a, b, importance,
+                               both_noisy ? load : nullptr, s));
+  return MOE_OK;
+}
+
+moe_status run_dispatch(const moe_config& c, const Plan& p, const int32_t* topk_idx,
+                        const float* x, int32_t* counts_pre, int32_t* counts, int32_t* offsets,
+                        int32_t* perm, int32_t* slot_pos, void* x_perm, void* ws, hipStream_t s) {
+  HIP_TRY(launch_dispatch(topk_idx, c.T, c.k, c.n_experts, capacity(c), counts_pre, counts,
+                          offsets, perm, slot_pos, at<int32_t>(ws, p.chunk_hist),
+                          at<int32_t>(ws, p.chunk_base), s));
+  HIP_TRY(launch_gather(x, perm, offsets + c.n_experts, c.T * c.k, c.d_model,
+                        c.expert_dtype == MOE_BF16, x_perm, s));
+  return MOE_OK;
+}
+
+moe_status run_ffn(const moe_config& c, const Plan& p, const void* x_perm,
+                   const int32_t* offsets, const void* w1, const float* b1, const void* w3,
+                   const void* w2, const float* b2, float* y_perm, void* ws, hipStream_t s) {
+  const int n = c.n_experts, d = c.d_model, h = c.d_hidden;
+  int32_t* te = at<int32_t>(ws, p.t_expert);
+  int32_t* tr = at<int32_t>(ws, p.t_row0);
+  int32_t* tc = at<int32_t>(ws, p.t_count);
+  void* hidden = at<void>(ws, p.hidden);
+  HIP_TRY(launch_tilemap(offsets, n, p.ffn_bm, te, tr, tc, s));
+  if (c.expert_dtype == MOE_BF16) {
+    GemmBf16Args g{};
+    g.A = (const uint16_t*)x_perm;
+    g.lda = d;
+    g.B1 = (const uint16_t*)w1;
+    g.B3 = (const uint16_t*)w3;
+    g.strideB = (long long)h * d;
+    g.N = h;
+    g.K = d;
+    g.C = hidden;
+    g.ldc = h;
+    g.bias = b1;
+    g.tile_expert = te;
+    g.tile_row0 = tr;
+    g.offsets = offsets;
+    g.tile_count = tc;
+    g.max_mtiles = p.max_mtiles;
+    HIP_TRY(launch_gemm_bf16(g, c.act == MOE_ACT_SWIGLU ? EPI_SWIGLU_BF16 : EPI_RELU_BF16, s));
+    GemmBf16Args g2 = g;
+    g2.A = (const uint16_t*)hidden;
+    g2.lda = h;
+    g2.B1 = (const uint16_t*)w2;
+    g2.B3 = nullptr;
+    g2.strideB = (long long)d * h;
+    g2.N = d;
+    g2.K = h;
+    g2.C = y_perm;
+    g2.ldc = d;
+    g2.bias = b2;
+    HIP_TRY(launch_gemm_bf16(g2, EPI_IDENT_F32, s));
+  } else {
+    GemmF32Args g{};
+    g.A = (const float*)x_perm;
+    g.lda = d;
+    g.B1 = (const float*)w1;
+    g.strideB1 = (long long)h * d;
+    g.n1 = h;
+    g.N = h;
+    g.K = d;
+    g.C = (float*)hidden;
+    g.ldc = h;
+    g.bias = b1;
+    g.stride_bias = h;
+    g.relu = 1;
+    g.tile_expert = te;
+    g.tile_row0 = tr;
+    g.offsets = offsets;
+    g.tile_count = tc;
+    g.max_mtiles = p.max_mtiles;
+    HIP_TRY(launch_gemm_f32(g, kF32ExpertBM, s));
+    GemmF32Args g2 = g;
+    g2.A = (const float*)hidden;
+    g2.lda = h;
+    g2.B1 = (const float*)w2;
+    g2.strideB1 = (long long)d * h;
+    g2.n1 = d;
+    g2.N = d;
+    g2.K = h;
+    g2.C = y_perm;
+    g2.ldc = d;
+    g2.bias = b2;
+    g2.stride_bias = d;
+    g2.relu = 0;
+    HIP_TRY(launch_gemm_f32(g2, kF32ExpertBM, s));
+  }
+  return MOE_OK;
+}
+
+moe_status check_gate_ptrs(const moe_config& c, const float* x, const float* w_gate,
+                           const float* b_gate, const float* w_noise, const float* noise) {
+  CHECK(need(x, "x", c.T == 0));
+  CHECK(need(w_gate, "w_gate"));
+  CHECK(optional(b_gate, "b_gate"));
+  CHECK(optional(w_noise, "w_noise"));
+  if (w_noise) CHECK(need(noise, "noise (required with w_noise)", c.T == 0));
+  if (w_noise && c.gate == MOE_GATE_SWITCH_TOP1)
+    return fail(MOE_ERR_INVALID_ARG, "the Switch router is noiseless (w_noise must be NULL)");
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_size(const moe_config* cfg) {
+  if (validate(cfg) != MOE_OK) return 0;
+  return make_plan(*cfg).total;
+}
+
+moe_status moe_gate(const moe_config* cfg, const float* x, const float* w_gate,
+                    const float* b_gate, const float* w_noise, const float* noise,
+                    int32_t* topk_idx, float* topk_w, float* importance, float* load, void* ws,
+                    size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  CHECK(validate(cfg));
+  const moe_config& c = *cfg;
+  if (c.n_groups > 0) return fail(MOE_ERR_INVALID_ARG, "moe_gate is the flat gate; use moe_gate_hier");
+  CHECK(check_gate_ptrs(c, x, w_gate, b_gate, w_noise, noise));
+  CHECK(need(topk_idx, "topk_idx", c.T == 0));
+  CHECK(need(topk_w, "topk_w", c.T == 0));
+  CHECK(need(importance, "importance"));
+  if (w_noise) CHECK(need(load, "load (required for a noisy gate)"));
+  const Plan p = make_plan(c);
+  CHECK(check_ws(ws, ws_bytes, p.gate_bytes, "moe_gate"));
+  return run_gate(c, p, x, w_gate, b_gate, w_noise, noise, topk_idx, topk_w, importance, load, ws,
+                  (hipStream_t)stream);
+}
+
+moe_status moe_gate_hier(const moe_config* cfg, const float* x, const float* w_gate,
+                         const float* b_gate, const float* w_noise, const float* noise,
+                         const float* w_gate2, const float* w_noise2, const float* noise2,
+                         int32_t* topk_idx, float* topk_w, float* importance, float* load,
+                         void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  CHECK(validate(cfg));
+  const moe_config& c = *cfg;
+  if (c.n_groups <= 0) return fail(MOE_ERR_INVALID_ARG, "moe_gate_hier needs n_groups > 0");
+  CHECK(check_gate_ptrs(c, x, w_gate, b_gate, w_noise, noise));
+  CHECK(need(w_gate2, "w_gate2"));
+  CHECK(optional(w_noise2, "w_noise2"));
+  if (w_noise2) CHECK(need(noise2, "noise2 (required with w_noise2)", c.T == 0));
+  CHECK(need(topk_idx, "topk_idx", c.T == 0));
+  CHECK(need(topk_w, "topk_w", c.T == 0));
+  CHECK(need(importance, "importance"));
+  if (w_noise && w_noise2) CHECK(need(load, "load (required for noisy gates)"));
+  const Plan p = make_plan(c);
+  CHECK(check_ws(ws, ws_bytes, p.gate_bytes, "moe_gate_hier"));
+  return run_gate_hier(c, p, x, w_gate, b_gate, w_noise, noise, w_gate2, w_noise2, noise2,
+                       topk_idx, topk_w, importance, load, ws, (hipStream_t)stream);
+}
+
+moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, const float* x,
+                        int32_t* counts_pre, int32_t* counts, int32_t* offsets, int32_t* perm,
+                        int32_t* slot_pos, void* x_perm, void* ws, size_t ws_bytes,
+                        void* stream) {
+  g_err[0] = 0;
+  CHECK(validate(cfg));
+  const moe_config& c = *cfg;
+  CHECK(need(topk_idx, "topk_idx", c.T == 0));
+  CHECK(need(x, "x", c.T == 0));
+  CHECK(need(counts_pre, "counts_pre"));
+  CHECK(need(counts, "counts"));
+  CHECK(need(offsets, "offsets"));
+  CHECK(need(perm, "perm", c.T == 0));
+  CHECK(need(slot_pos, "slot_pos", c.T == 0));
+  CHECK(need(x_perm, "x_perm", c.T == 0));
+  const Plan p = make_plan(c);
+  CHECK(check_ws(ws, ws_bytes, p.dispatch_bytes, "moe_dispatch"));
+  return run_dispatch(c, p, topk_idx, x, counts_pre, counts, offsets, perm, slot_pos, x_perm, ws,
+                      (hipStream_t)stream);
+}
+
+moe_status moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32_t* offsets,
+                          const void* w1, const float* b1, const void* w3, const void* w2,
+                          const float* b2, float* y_perm, void* ws, size_t ws_bytes,
+                          void* stream) {
+  g_err[0] = 0;
+  CHECK(validate(cfg));
+  const moe_config& c = *cfg;
+  CHECK(need(x_perm, "x_perm", c.T == 0));
+  CHECK(need(offsets, "offsets"));
+  CHECK(need(w1, "w1"));
+  CHECK(need(w2, "w2"));
+  CHECK(need(y_perm, "y_perm", c.T == 0));
+  if (c.act == MOE_ACT_SWIGLU) {
+    CHECK(need(w3, "w3 (required for SwiGLU)"));
+    if (b1 || b2) return fail(MOE_ERR_UNSUPPORTED, "SwiGLU experts take no biases");
+  } else {
+    CHECK(optional(w3, "w3"));
+  }
+  CHECK(optional(b1, "b1"));
+  CHECK(optional(b2, "b2"));
+  const Plan p = make_plan(c);
+  CHECK(check_ws(ws, ws_bytes, p.ffn_bytes, "moe_expert_ffn"));
+  return run_ffn(c, p, x_perm, offsets, w1, b1, w3, w2, b2, y_perm, ws, (hipStream_t)stream);
+}
+
+moe_status moe_combine(const moe_config* cfg, const float* y_perm, const int32_t* slot_pos,
+                       const float* topk_w, float* y, void* stream) {
+  g_err[0] = 0;
+  CHECK(validate(cfg));
+  const moe_config& c = *cfg;
+  CHECK(need(y_perm, "y_perm", c.T == 0));
+  CHECK(need(slot_pos, "slot_pos", c.T == 0));
+  CHECK(need(topk_w, "topk_w", c.T == 0));
+  CHECK(need(y, "y", c.T == 0));
+  HIP_TRY(launch_combine(y_perm, slot_pos, topk_w, c.T, c.k, c.d_model, y, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+moe_status moe_aux_loss(const moe_config* cfg, const float* importance, const float* load,
+                        const int32_t* counts_pre, float* losses, void* stream) {
+  g_err[0] = 0;
+  CHECK(validate(cfg));
+  const moe_config& c = *cfg;
+  CHECK(need(importance, "importance"));
+  CHECK(optional(load, "load"));
+  CHECK(need(counts_pre, "counts_pre"));
+  CHECK(need(losses, "losses"));
+  HIP_TRY(launch_aux(importance, load, counts_pre, c.T, c.k, c.n_experts, c.w_importance,
+                     c.w_load, c.alpha_switch, losses, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const float* x,
+                       const float* noise, const float* noise2, float* y, float* losses,
+                       const moe_diag* diag, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  CHECK(validate(cfg));
+  const moe_config& c = *cfg;
+  if (!wt) return fail(MOE_ERR_INVALID_ARG, "weights must not be NULL");
+  const bool hier = c.n_groups > 0;
+  CHECK(check_gate_ptrs(c, x, wt->w_gate, wt->b_gate, wt->w_noise, noise));
+  if (hier) {
+    CHECK(need(wt->w_gate2, "weights->w_gate2"));
+    CHECK(optional(wt->w_noise2, "weights->w_noise2"));
+    if (wt->w_noise2) CHECK(need(noise2, "noise2 (required with w_noise2)", c.T == 0));
+  }
+  CHECK(need(wt->w1, "weights->w1"));
+  CHECK(need(wt->w2, "weights->w2"));
+  if (c.act == MOE_ACT_SWIGLU) {
+    CHECK(need(wt->w3, "weights->w3 (required for SwiGLU)"));
+    if (wt->b1 || wt->b2) return fail(MOE_ERR_UNSUPPORTED, "SwiGLU experts take no biases");
+  }
+  CHECK(optional(wt->b1, "weights->b1"));
+  CHECK(optional(wt->b2, "weights->b2"));
+  CHECK(need(y, "y", c.T == 0));
+  CHECK(need(losses, "losses"));
+  moe_diag dg{};
+  if (diag) {
+    dg = *diag;
+    CHECK(optional(dg.topk_idx, "diag->topk_idx"));
+    CHECK(optional(dg.topk_w, "diag->topk_w"));
+    CHECK(optional(dg.importance, "diag->importance"));
+    CHECK(optional(dg.load, "diag->load"));
+    CHECK(optional(dg.counts_pre, "diag->counts_pre"));
+    CHECK(optional(dg.counts, "diag->counts"));
+    CHECK(optional(dg.offsets, "diag->offsets"));
+    CHECK(optional(dg.perm, "diag->perm"));
+    CHECK(optional(dg.slot_pos, "diag->slot_pos"));
+  }
+  const Plan p = make_plan(c);
+  CHECK(check_ws(ws, ws_bytes, p.total, "moe_forward"));
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* idx = dg.topk_idx ? dg.topk_idx : at<int32_t>(ws, p.f_idx);
+  float* w = dg.topk_w ? dg.topk_w : at<float>(ws, p.f_w);
+  float* imp = dg.importance ? dg.importance : at<float>(ws, p.f_imp);
+  float* ld = dg.load ? dg.load : at<float>(ws, p.f_load);
+  int32_t* counts_pre = dg.counts_pre ? dg.counts_pre : at<int32_t>(ws, p.f_counts_pre);
+  int32_t* counts = dg.counts ? dg.counts : at<int32_t>(ws, p.f_counts);
+  int32_t* offsets = dg.offsets ? dg.offsets : at<int32_t>(ws, p.f_offsets);
+  int32_t* perm = dg.perm ? dg.perm : at<int32_t>(ws, p.f_perm);
+  int32_t* slot = dg.slot_pos ? dg.slot_pos : at<int32_t>(ws, p.f_slot);
+  void* xperm = at<void>(ws, p.f_xperm);
+  float* yperm = at<float>(ws, p.f_yperm);
+  const bool has_load = hier ? (wt->w_noise && wt->w_noise2) : (wt->w_noise != nullptr);
+  if (hier) {
+    CHECK(run_gate_hier(c, p, x, wt->w_gate, wt->b_gate, wt->w_noise, noise, wt->w_gate2,
+                        wt->w_noise2, noise2, idx, w, imp, ld, ws, s));
+  } else {
+    CHECK(run_gate(c, p, x, wt->w_gate, wt->b_gate, wt->w_noise, noise, idx, w, imp, ld, ws, s));
+  }
+  CHECK(run_dispatch(c, p, idx, x, counts_pre, counts, offsets, perm, slot, xperm, ws, s));
+  CHECK(run_ffn(c, p, xperm, offsets, wt->w1, wt->b1, wt->w3, wt->w2, wt->b2, yperm, ws, s));
+  HIP_TRY(launch_combine(yperm, slot, w, c.T, c.k, c.d_model, y, s));
+  HIP_TRY(launch_aux(imp, has_load ? ld : nullptr, counts_pre, c.T, c.k, c.n_experts,
+                     c.w_importance, c.w_load, c.alpha_switch, losses, s));
+  return MOE_OK;
+}
+
+const char* moe_status_string(moe_status status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP launch failure";
+  }
+  return "unknown status";
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+}  // extern "C"

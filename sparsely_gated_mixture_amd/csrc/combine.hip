@@ -1,0 +1,108 @@
+// Combine and auxiliary losses on gfx950.
+//
+// Combine (arXiv 1701.06538 summary, xyznot.com, "Method and key formulas":
+// y = sum_i G(x)_i E_i(x)): a gather -- one wavefront per token reads the
+// expert rows of its kept slots in slot order and writes its output row once.
+// No atomics, so the sum order is fixed.
+//
+// Aux losses (same page, load-balancing losses; MoE survey, tufusi.com 3.2):
+// one block computes, in double precision with fixed-order tree reductions,
+// w_imp*CV(Importance)^2, w_load*CV(Load)^2 (population variance, two passes)
+// and alpha*n*sum_i f_i P_i.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+namespace {
+
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_perm,
+                                                      const int32_t* __restrict__ slot_pos,
+                                                      const float* __restrict__ topk_w, int T,
+                                                      int k, int d, float* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int32_t* sp = slot_pos + (long long)t * k;
+  const float* w = topk_w + (long long)t * k;
+  for (int c = lane * 4; c < d; c += 64 * 4) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < k; ++s) {
+      const int pos = sp[s];
+      if (pos < 0) continue;
+      const float ws = w[s];
+      const f32x4 v = *(const f32x4*)(y_perm + (long long)pos * d + c);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = fmaf(ws, v[q], acc[q]);
+    }
+    *(f32x4*)(y + (long long)t * d + c) = acc;
+  }
+}
+
+// Fixed-shape tree sum over the 256 threads (same order every call).
+__device__ double block_sum(double v, double* sh) {
+  sh[threadIdx.x] = v;
+  __syncthreads();
+  for (int off = 128; off >= 1; off >>= 1) {
+    if ((int)threadIdx.x < off) sh[threadIdx.x] += sh[threadIdx.x + off];
+    __syncthreads();
+  }
+  const double r = sh[0];
+  __syncthreads();
+  return r;
+}
+
+__device__ double cv2_block(const float* v, int n, double* sh) {
+  double s = 0.0;
+  for (int i = threadIdx.x; i < n; i += 256) s += (double)v[i];
+  const double mean = block_sum(s, sh) / n;
+  if (mean == 0.0) return 0.0;
+  double q = 0.0;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const double dv = (double)v[i] - mean;
+    q += dv * dv;
+  }
+  const double var = block_sum(q, sh) / n;
+  return var / (mean * mean);
+}
+
+__global__ __launch_bounds__(256) void aux_kernel(const float* __restrict__ importance,
+                                                  const float* __restrict__ load,
+                                                  const int32_t* __restrict__ counts_pre, int T,
+                                                  int k, int n, float w_imp, float w_load,
+                                                  float alpha, float* __restrict__ losses) {
+  __shared__ double sh[256];
+  const double li = (double)w_imp * cv2_block(importance, n, sh);
+  const double ll = load ? (double)w_load * cv2_block(load, n, sh) : 0.0;
+  double fp = 0.0;
+  if (T > 0) {
+    for (int i = threadIdx.x; i < n; i += 256)
+      fp += ((double)counts_pre[i] / ((double)T * k)) * ((double)importance[i] / T);
+  }
+  const double sw = (double)alpha * n * block_sum(fp, sh);
+  if (threadIdx.x == 0) {
+    losses[0] = (float)li;
+    losses[1] = (float)ll;
+    losses[2] = (float)sw;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const float* y_perm, const int32_t* slot_pos, const float* topk_w,
+                          int T, int k, int d, float* y, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  ProfScope ps("combine", s);
+  combine_kernel<<<dim3((T + 3) / 4), dim3(256), 0, s>>>(y_perm, slot_pos, topk_w, T, k, d, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_aux(const float* importance, const float* load, const int32_t* counts_pre,
+                      int T, int k, int n, float w_imp, float w_load, float alpha,
+                      float* losses, hipStream_t s) {
+  ProfScope ps("aux_loss", s);
+  aux_kernel<<<dim3(1), dim3(256), 0, s>>>(importance, load, counts_pre, T, k, n, w_imp, w_load,
+                                           alpha, losses);
+  return hipGetLastError();
+}
+
+}  // namespace moe

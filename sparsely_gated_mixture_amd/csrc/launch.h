@@ -1,0 +1,146 @@
+// Host-side launchers of the gfx950 kernels (internal to libmoe).
+// Each returns the HIP error of its launch; none synchronises.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Brackets one kernel launch with HIP events while kernel timing is on
+// (moe_profile_enable); a no-op otherwise.
+struct ProfScope {
+  int slot;
+  hipStream_t stream;
+  ProfScope(const char* name, hipStream_t s);
+  ~ProfScope();
+  ProfScope(const ProfScope&) = delete;
+  ProfScope& operator=(const ProfScope&) = delete;
+};
+
+// ---------------------------------------------------------------------------
+// fp32 MFMA GEMM:  C[r, c] = epi(sum_k A[r, k] * B[c, k] + bias[c]).
+// Flat mode (tile_expert == nullptr): rows 0..M-1.  Grouped mode: M-tiles
+// come from a device tile map (expert / group e, first row), rows of tile
+// stop at offsets[e+1], and B / bias are offset by e * stride.
+// B rows [0, n1) come from B1, rows [n1, N) from B2 (gate: clean | noise).
+// A row r is A + (rowmap ? rowmap[r] : r) * lda.
+// ---------------------------------------------------------------------------
+struct GemmF32Args {
+  const float* A;
+  long long lda;
+  const int32_t* rowmap;
+  const float* B1;
+  const float* B2;
+  long long strideB1, strideB2;  // per-group element strides
+  int n1, N, K;
+  float* C;
+  long long ldc;
+  const float* bias;       // per-group bias rows of length N (may be null)
+  long long stride_bias;
+  int relu;                // 1: max(0, .)
+  int M;                   // flat mode rows
+  int mtiles;              // flat mode M-tiles (host-known)
+  const int32_t* tile_expert;
+  const int32_t* tile_row0;
+  const int32_t* offsets;
+  const int32_t* tile_count;  // device total of M-tiles (grouped mode)
+  int max_mtiles;             // upper bound of M-tiles (grid sizing)
+};
+// bm: 64 or 128 (BN = bm).
+hipError_t launch_gemm_f32(const GemmF32Args& a, int bm, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA grouped GEMM for the expert FFNs.
+// ---------------------------------------------------------------------------
+enum GemmEpi { EPI_RELU_BF16 = 0, EPI_SWIGLU_BF16 = 1, EPI_IDENT_F32 = 2 };
+struct GemmBf16Args {
+  const uint16_t* A;     // [rows, K] bf16, rows contiguous
+  long long lda;
+  const uint16_t* B1;    // [n, N, K] bf16
+  const uint16_t* B3;    // SwiGLU second matrix [n, N, K]
+  long long strideB;     // N * K
+  int N, K;
+  void* C;               // bf16 [rows, N] or f32 [rows, N]
+  long long ldc;
+  const float* bias;     // [n, N] or null
+  const int32_t* tile_expert;
+  const int32_t* tile_row0;
+  const int32_t* offsets;
+  const int32_t* tile_count;
+  int max_mtiles;
+};
+constexpr int kBf16BM = 128;
+hipError_t launch_gemm_bf16(const GemmBf16Args& a, int epi, hipStream_t s);
+
+// Tile map of a grouped GEMM: for every expert e with rows in
+// [offsets[e], offsets[e+1]), ceil(rows/bm) M-tiles in expert order.
+hipError_t launch_tilemap(const int32_t* offsets, int n, int bm, int32_t* tile_expert,
+                          int32_t* tile_row0, int32_t* tile_count, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Gate epilogue: noise, KeepTopK, softmax / Switch, importance/load partials.
+// Row r reads clean logits at logits[r*ldl + j] (j < n) and raw noise logits
+// at logits[r*ldl + n + j].
+// Flat mode: row r is token r; outputs at [r*k + s]; bias b[j]; noise[r*n+j].
+// Grouped (two-level secondary) mode: rows are the primary slots dispatched
+// by group (row_token[r] = token); tiles of rows never straddle a group; the
+// outputs go to the token's combined slots and multiply by the primary
+// weight; partial sums are per tile.
+// ---------------------------------------------------------------------------
+struct TopkArgs {
+  int rows, n, k, switch_mode, noisy;
+  const float* logits;
+  long long ldl;
+  const float* bias;
+  const float* noise;       // flat: [rows, n]; grouped: [T, k1, n] indexed by (token, slot)
+  int32_t* topk_idx;
+  float* topk_w;
+  float* part_imp;          // [nparts, n]
+  float* part_load;         // [nparts, n]
+  int rows_per_block;       // flat mode
+  // grouped mode
+  const int32_t* row_token;     // perm of the group dispatch
+  const int32_t* prim_idx;      // [T, k1] primary group per slot
+  const float* prim_w;          // [T, k1]
+  int k1;
+  const int32_t* tile_expert;   // group of each row tile
+  const int32_t* tile_row0;
+  const int32_t* offsets;       // group row offsets
+  const int32_t* tile_count;
+  int max_tiles;
+  int tile_rows;
+};
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+// out[j] = sum over parts p < nparts (ascending) of part[p*n + j]  (double sum)
+hipError_t launch_colsum(const float* part, int nparts, int n, float* out, hipStream_t s);
+// Two-level aux vectors: per-tile partials of the secondary gate are summed
+// per group (tiles of a group are consecutive), then combined with the
+// primary vectors: load[g*b+e] = load_p[g]*load_g[e]/|X_g|.
+hipError_t launch_hier_finalize(const float* part_imp, const float* part_load,
+                                const int32_t* tile_expert, const int32_t* tile_count,
+                                const int32_t* group_counts, const float* load_primary, int a,
+                                int b, float* importance, float* load, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Dispatch.
+// ---------------------------------------------------------------------------
+constexpr int kDispatchChunk = 1024;  // assignments per chunk
+hipError_t launch_dispatch(const int32_t* topk_idx, int T, int k, int n, long long cap,
+                           int32_t* counts_pre, int32_t* counts, int32_t* offsets,
+                           int32_t* perm, int32_t* slot_pos, int32_t* chunk_hist,
+                           int32_t* chunk_base, hipStream_t s);
+// x_perm[r] = convert(x[perm[r]]) for r < offsets[n].
+hipError_t launch_gather(const float* x, const int32_t* perm, const int32_t* rows_dev,
+                         int max_rows, int d, int bf16_out, void* x_perm, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Combine and aux.
+// ---------------------------------------------------------------------------
+hipError_t launch_combine(const float* y_perm, const int32_t* slot_pos, const float* topk_w,
+                          int T, int k, int d, float* y, hipStream_t s);
+hipError_t launch_aux(const float* importance, const float* load, const int32_t* counts_pre,
+                      int T, int k, int n, float w_imp, float w_load, float alpha,
+                      float* losses, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,138 @@
+"""The C ABI library loads, exports what include/moe.h declares, and rejects
+bad arguments synchronously -- before any HIP call, so these run without a GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import sparsely_gated_mixture_amd as moe
+from sparsely_gated_mixture_amd import _lib
+from sparsely_gated_mixture_amd.workloads import PRESETS, MoEConfig
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+FAKE = 0x10000  # an aligned non-null address; never dereferenced by these calls
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_calls():
+    decl = declared_functions()
+    for name in ["moe_gate", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_aux_loss",
+                 "moe_forward", "moe_workspace_size", "moe_status_string", "moe_last_error",
+                 "moe_gate_hier"]:
+        assert name in decl
+    assert sorted(_lib.EXPORTS) == decl
+
+
+def test_library_exports_every_declared_symbol():
+    L = moe.load_library()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in syms, name
+
+
+def test_status_strings():
+    for code in range(5):
+        assert moe.moe_status_string(code)
+    assert moe.moe_status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("name", list(PRESETS))
+def test_workspace_size_of_presets(name):
+    cfg = PRESETS[name]
+    size = moe.moe_workspace_size(cfg)
+    assert size > 0
+    # the forward keeps x_perm and y_perm for every routed slot
+    rows = cfg.T * cfg.k
+    per = 2 if cfg.expert_dtype == 1 else 4
+    assert size >= rows * cfg.d_model * (per + 4)
+
+
+def base_cfg(**kw):
+    c = MoEConfig("t", T=64, d_model=32, d_hidden=64, n_experts=8, k=2)
+    return c.replace(**kw)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), moe.MOE_ERR_INVALID_ARG),
+    (dict(k=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(k=9), moe.MOE_ERR_INVALID_ARG),
+    (dict(d_model=30), moe.MOE_ERR_UNSUPPORTED),
+    (dict(d_hidden=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(gate=7), moe.MOE_ERR_INVALID_ARG),
+    (dict(gate=1, k=2), moe.MOE_ERR_INVALID_ARG),
+    (dict(act=1, expert_dtype=0), moe.MOE_ERR_UNSUPPORTED),
+    (dict(expert_dtype=5), moe.MOE_ERR_INVALID_ARG),
+    (dict(n_experts=4096, k=2), moe.MOE_ERR_UNSUPPORTED),  # flat gate limit
+    (dict(n_groups=3), moe.MOE_ERR_INVALID_ARG),           # 8 % 3
+    (dict(n_groups=2, k_groups=3), moe.MOE_ERR_INVALID_ARG),
+    (dict(capacity_factor=float("nan")), moe.MOE_ERR_INVALID_ARG),
+])
+def test_invalid_configs(kw, status):
+    c = _lib.make_config(base_cfg(**kw))
+    L = moe.load_library()
+    assert L.moe_workspace_size(ctypes.byref(c)) == 0
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_combine(c, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert ei.value.status == status
+    assert moe.moe_last_error()
+
+
+def test_null_and_misaligned_pointers():
+    c = base_cfg()
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_combine(c, None, FAKE, FAKE, FAKE, stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG and "y_perm" in str(ei.value)
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_combine(c, FAKE + 4, FAKE, FAKE, FAKE, stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG and "aligned" in str(ei.value)
+    with pytest.raises(moe.MoEError) as ei:   # noisy gate without its noise tensor
+        moe.moe_gate(c, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, FAKE, (FAKE, 1 << 30),
+                     stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG and "noise" in str(ei.value)
+    with pytest.raises(moe.MoEError) as ei:   # Switch router is noiseless
+        moe.moe_gate(base_cfg(gate=1, k=1), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                     FAKE, (FAKE, 1 << 30), stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoEError) as ei:   # flat call on a two-level config
+        moe.moe_gate(base_cfg(n_groups=2, k_groups=1), FAKE, FAKE, None, None, None, FAKE, FAKE,
+                     FAKE, None, (FAKE, 1 << 30), stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+
+
+def test_workspace_too_small_rejected_before_launch():
+    c = base_cfg()
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_dispatch(c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, (FAKE, 16), stream=0)
+    assert ei.value.status == moe.MOE_ERR_WORKSPACE
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_expert_ffn(c, FAKE, FAKE, FAKE, None, None, FAKE, None, FAKE, None, stream=0)
+    assert ei.value.status == moe.MOE_ERR_WORKSPACE
+    w = moe.make_weights(FAKE, w1=FAKE, w2=FAKE)
+    size = moe.moe_workspace_size(c)
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_forward(c, w, FAKE, None, None, FAKE, FAKE, None, (FAKE, size - 256), stream=0)
+    assert ei.value.status == moe.MOE_ERR_WORKSPACE
+
+
+def test_swiglu_requires_w3_and_no_bias():
+    c = base_cfg(act=1)
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_expert_ffn(c, FAKE, FAKE, FAKE, None, None, FAKE, None, FAKE, (FAKE, 1 << 40),
+                           stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG and "w3" in str(ei.value)
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_expert_ffn(c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, (FAKE, 1 << 40),
+                           stream=0)
+    assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
