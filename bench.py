@@ -1,0 +1,246 @@
+"""Benchmark of the MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload lm_layer]
+
+One step is one moe_forward call over one batch: gate GEMM + gate epilogue
+(noise, top-k, softmax, importance/load), dispatch (histogram, scan,
+permutation, gather), the two grouped expert GEMMs, combine and the aux
+losses.  Inputs and weights are seeded synthetic tensors already resident in
+HBM.  Prints one JSON line:
+  value        tokens/s over K back-to-back steps (host clock around the
+               synchronised loop);
+  roofline     the dominant kernel's algorithmic bytes (or flops) per launch
+               over its average duration, measured with HIP events recorded
+               on the library's stream (moe_profile_*), against the MI355X
+               peak (HBM 8 TB/s, bf16 MFMA 2.5 PFLOP/s, fp32 157.3 TFLOP/s);
+  kernels      the same figures for every kernel of the step;
+  cpu_baseline the CPU oracle timed on a bounded sample of the same workload
+               (its first tokens) on this host's cores;
+  check        the GPU output on that sample against the oracle.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer fwd tokens/sec at 1 GPU; expert-GEMM % MFMA peak; routing % HBM BW"
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+# rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE of the dominant kernel, per launch
+# (KiB, scaled by the copy-kernel calibration); null until measured for the
+# current kernel.
+TRAFFIC_BYTES = None
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_work(name, cfg, rows, nonempty, T):
+    """(algorithmic bytes, flops, dtype) of one launch of kernel `name` for
+    this step's realised routing."""
+    d, h, n, k = cfg.d_model, cfg.d_hidden, cfg.n_experts, cfg.k
+    bf = cfg.expert_dtype == 1
+    wsz = 2 if bf else 4
+    noisy = cfg.noisy
+    ncols = 2 * n if noisy else n
+    if name == "ggemm_bf16_relu":
+        return (nonempty * h * d * 2 + rows * d * 2 + rows * h * 2, 2.0 * rows * h * d, "bf16")
+    if name == "ggemm_bf16_swiglu":
+        return (nonempty * 2 * h * d * 2 + rows * d * 2 + rows * h * 2, 4.0 * rows * h * d,
+                "bf16")
+    if name == "ggemm_bf16_out":
+        return (nonempty * d * h * 2 + rows * h * 2 + rows * d * 4, 2.0 * rows * d * h, "bf16")
+    if name.startswith("gemm_f32"):
+        return (T * d * 4 + ncols * d * 4 + T * ncols * 4, 2.0 * T * ncols * d, "f32")
+    if name == "gate_topk":
+        return (T * ncols * 4 + (T * n * 4 if noisy else 0) + T * k * 8, 0.0, "f32")
+    if name == "dispatch_gather":
+        return (T * d * 4 + rows * d * wsz + rows * 4, 0.0, "f32")
+    if name == "combine":
+        return (rows * d * 4 + T * d * 4 + T * k * 8, 0.0, "f32")
+    if name == "dispatch_permute":
+        return (T * k * 4 * 2 + rows * 4, 0.0, "i32")
+    if name == "dispatch_hist":
+        return (T * k * 4 + ((T * k + 1023) // 1024) * n * 4, 0.0, "i32")
+    rpb = max(16, -(-((T + 255) // 256) // 4) * 4)
+    nparts = (T + rpb - 1) // rpb
+    if name == "gate_colsum":
+        return (nparts * n * 4 + n * 4, 0.0, "f32")
+    if name == "dispatch_colscan":
+        return (((T * k + 1023) // 1024) * n * 8 + n * 4, 0.0, "i32")
+    if name in ("dispatch_offsets", "ffn_tilemap", "aux_loss"):
+        return (n * 12, 0.0, "i32")
+    return (0.0, 0.0, "")
+
+
+def roofline_entry(bytes_, flops, dtype, avg_s):
+    t_hbm = bytes_ / (PEAK_HBM_GBS * 1e9)
+    t_mfma = flops / (PEAK_TFLOPS.get(dtype, 1e30) * 1e12) if flops else 0.0
+    gbs = bytes_ / avg_s / 1e9 if avg_s > 0 else 0.0
+    tfs = flops / avg_s / 1e12 if avg_s > 0 else 0.0
+    if t_mfma > t_hbm:
+        return dict(bound="mfma", achieved=tfs, peak=PEAK_TFLOPS[dtype], unit="TFLOP/s",
+                    frac=tfs / PEAK_TFLOPS[dtype]), gbs, tfs
+    return dict(bound="hbm", achieved=gbs, peak=PEAK_HBM_GBS, unit="GB/s",
+                frac=gbs / PEAK_HBM_GBS), gbs, tfs
+
+
+def cpu_baseline(cfg, inp, y_gpu, idx_gpu, sample_tokens):
+    """Time the CPU oracle on the first `sample_tokens` tokens (their gate,
+    dispatch, experts, combine and losses) and check the GPU output there."""
+    import oracle
+    from sparsely_gated_mixture_amd.workloads import to_numpy64
+    S = min(sample_tokens, cfg.T)
+    x = to_numpy64(inp["x"][:S])
+    g = {k: to_numpy64(inp[k]) for k in ("w_gate", "b_gate", "w_noise")}
+    noise = to_numpy64(inp["noise"][:S]) if inp.get("noise") is not None else None
+    w1 = to_numpy64(inp["w1"])
+    w2 = to_numpy64(inp["w2"])
+    w3 = to_numpy64(inp["w3"]) if inp.get("w3") is not None else None
+    oracle.lib()
+    t0 = time.perf_counter()
+    ref = oracle.forward(x, g["w_gate"], cfg.k, w1, w2, b_gate=g["b_gate"], w_noise=g["w_noise"],
+                         noise=noise, w3=w3, mode=cfg.gate, act=cfg.act,
+                         bf16=cfg.expert_dtype == 1, capacity_factor=cfg.capacity_factor,
+                         w_importance=cfg.w_importance, w_load=cfg.w_load,
+                         alpha=cfg.alpha_switch)
+    dt = time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    same = np.all(idx_gpu[:S] == ref["gate"].topk_idx, axis=1)
+    scale = np.max(np.abs(ref["y"][same])) if same.any() else 1.0
+    err = float(np.max(np.abs(y_gpu[:S][same] - ref["y"][same])) / scale) if same.any() else None
+    base = {"value": S / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {S} of {cfg.T} tokens of the {cfg.name} workload "
+                      f"(gate, dispatch, experts, combine, losses in float64); {dt:.2f} s"}
+    check = {"tokens": S, "routing_match": float(same.mean()), "y_max_abs_norm_err": err,
+             "tolerance": 2e-2 if cfg.expert_dtype == 1 else 1e-4}
+    return base, check
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="lm_layer")
+    ap.add_argument("--profile-steps", type=int, default=20)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the layer is built and "
+              "measured on a single MI355X, with no collectives.", file=sys.stderr)
+        sys.exit(2)
+
+    import sparsely_gated_mixture_amd as moe
+    from sparsely_gated_mixture_amd.workloads import PRESETS, make_inputs
+
+    cfg = PRESETS[args.workload]
+    torch.cuda.set_device(0)
+    log(f"[bench] workload {cfg.name}: T={cfg.T} d={cfg.d_model} h={cfg.d_hidden} "
+        f"n={cfg.n_experts} k={cfg.k}")
+    inp = make_inputs(cfg, device="cuda")
+    torch.cuda.synchronize()
+    layer = moe.MoELayer(cfg, inp)
+    T, n, k = cfg.T, cfg.n_experts, cfg.k
+    i32 = dict(dtype=torch.int32, device="cuda")
+    diag = {"topk_idx": torch.empty((T, k), **i32), "counts": torch.empty(n, **i32),
+            "offsets": torch.empty(n + 1, **i32)}
+    y = torch.empty((T, cfg.d_model), dtype=torch.float32, device="cuda")
+    losses = torch.empty(3, dtype=torch.float32, device="cuda")
+
+    for _ in range(args.warmup):
+        layer.forward(inp["x"], inp.get("noise"), inp.get("noise2"), y=y, losses=losses)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps")
+
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        layer.forward(inp["x"], inp.get("noise"), inp.get("noise2"), y=y, losses=losses)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed / args.steps * 1e3
+    tokens_per_s = T * args.steps / elapsed
+    log(f"[bench] {ms_per_step * 1e3:.1f} us/step, {tokens_per_s / 1e6:.2f} M tokens/s")
+
+    # Per-kernel durations: HIP events recorded by the library on its stream.
+    moe.moe_profile_enable(True)
+    for _ in range(args.profile_steps):
+        layer.forward(inp["x"], inp.get("noise"), inp.get("noise2"), y=y, losses=losses)
+    torch.cuda.synchronize()
+    moe.moe_profile_enable(False)
+    nk = moe.moe_profile_collect()
+    stats = [moe.moe_profile_entry(i) for i in range(nk)]
+
+    # Realised routing of this batch (identical every step).
+    layer.forward(inp["x"], inp.get("noise"), inp.get("noise2"), y=y, losses=losses, diag=diag)
+    torch.cuda.synchronize()
+    counts = diag["counts"].cpu().numpy()
+    rows = int(counts.sum())
+    nonempty = int((counts > 0).sum())
+
+    kernels = {}
+    dominant = None
+    for name, total_ms, launches in stats:
+        avg_s = total_ms / launches / 1e3
+        b, f, dt = kernel_work(name, cfg, rows, nonempty, T)
+        entry = {"avg_us": avg_s * 1e6, "launches_per_step": launches / args.profile_steps}
+        if b:
+            rl, gbs, tfs = roofline_entry(b, f, dt, avg_s)
+            entry.update({"algo_bytes": b, "GB_s": gbs, "hbm_frac": gbs / PEAK_HBM_GBS})
+            if f:
+                entry.update({"flops": f, "TFLOP_s": tfs, "mfma_frac": tfs / PEAK_TFLOPS[dt]})
+            entry["roofline"] = rl
+        kernels[name] = entry
+        if dominant is None or total_ms > dominant[1]:
+            dominant = (name, total_ms)
+    for name, e in sorted(kernels.items(), key=lambda kv: -kv[1]["avg_us"] * kv[1]["launches_per_step"]):
+        log(f"[bench]   {name:22s} {e['avg_us']:9.1f} us x{e['launches_per_step']:.0f}"
+            + (f"  {e['GB_s']:8.1f} GB/s" if "GB_s" in e else "")
+            + (f"  {e['TFLOP_s']:7.1f} TFLOP/s" if "TFLOP_s" in e else ""))
+    dname = dominant[0]
+    dk = kernels[dname]
+    roofline = dict(dk["roofline"])
+    roofline["kernel"] = dname
+    roofline["traffic"] = TRAFFIC_BYTES
+    roofline["algo_bytes_per_launch"] = dk["algo_bytes"]
+    roofline["avg_us"] = dk["avg_us"]
+
+    result = {
+        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": T, "d_model": cfg.d_model,
+                   "d_hidden": cfg.d_hidden, "n_experts": n, "k": k,
+                   "gate": "noisy top-k softmax, fp32" if cfg.noisy else "top-k softmax, fp32",
+                   "experts": "bf16 ReLU FFN, fp32 accumulate" if cfg.expert_dtype == 1
+                   else "fp32 ReLU FFN",
+                   "rows": rows, "nonempty_experts": nonempty, "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle on the first {args.cpu_sample_tokens} tokens")
+        yh = y.cpu().double().numpy()
+        ih = diag["topk_idx"].cpu().numpy()
+        base, check = cpu_baseline(cfg, inp, yh, ih, args.cpu_sample_tokens)
+        result["cpu_baseline"] = base
+        result["check"] = check
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -169,7 +169,9 @@ Plan make_plan(const moe_config& c) {
     p.gemm_bm = t128 >= 256 ? 128 : 64;
   }
   {
-    long long rpb = std::max(16LL, round_up((T + 1023) / 1024, 4));
+    // one partial vector per block; at most 256 blocks (one per CU) once T
+    // is large, so the column sums stay short
+    long long rpb = std::max(16LL, round_up((T + 255) / 256, 4));
     p.rows_per_block = (int)rpb;
     p.nparts = (int)((T + rpb - 1) / rpb);
   }

@@ -45,6 +45,7 @@ __global__ __launch_bounds__(256) void column_scan_kernel(const int32_t* __restr
   const int e = blockIdx.x * 256 + threadIdx.x;
   if (e >= n) return;
   int run = 0;
+#pragma unroll 8
   for (int c = 0; c < nchunks; ++c) {
     const int h = chunk_hist[(long long)c * n + e];
     chunk_base[(long long)c * n + e] = run;
@@ -94,15 +95,23 @@ __global__ __launch_bounds__(64) void permute_kernel(const int32_t* __restrict__
                                                      int32_t* __restrict__ perm,
                                                      int32_t* __restrict__ slot_pos) {
   extern __shared__ int32_t fill[];
+  constexpr int G = kDispatchChunk / 64;
   const int lane = threadIdx.x;
   const long long c = blockIdx.x;
+  const long long a0 = c * kDispatchChunk;
+  int ev[G];  // the whole chunk's expert ids, loaded up front
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const long long a = a0 + g * 64 + lane;
+    ev[g] = a < A ? idx[a] : -1;
+  }
   for (int e = lane; e < n; e += 64) fill[e] = chunk_base[c * n + e];
   __syncthreads();
-  const long long a0 = c * kDispatchChunk;
-  for (int g0 = 0; g0 < kDispatchChunk; g0 += 64) {
-    const long long a = a0 + g0 + lane;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const long long a = a0 + g * 64 + lane;
     const bool ok = a < A;
-    const int e = ok ? idx[a] : -1;
+    const int e = ev[g];
     int before = 0, same = 0;
     for (int j = 0; j < 64; ++j) {
       const int ej = __builtin_amdgcn_readlane(e, j);

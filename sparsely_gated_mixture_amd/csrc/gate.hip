@@ -197,13 +197,28 @@ __global__ __launch_bounds__(256) void topk_kernel(const TopkArgs p) {
   }
 }
 
-__global__ void colsum_kernel(const float* __restrict__ part, int nparts, int n,
-                              float* __restrict__ out) {
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= n) return;
+// out[j] = sum of part[p][j] over p.  64 columns per block; 16 part-lanes per
+// column each add every 16th partial in ascending order (coalesced rows,
+// many loads in flight), then lane sums are added in lane order: the same
+// order on every call.
+constexpr int kColLanes = 16;
+__global__ __launch_bounds__(1024) void colsum_kernel(const float* __restrict__ part, int nparts,
+                                                      int n, float* __restrict__ out) {
+  __shared__ double sh[kColLanes][64];
+  const int c = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int j = blockIdx.x * 64 + c;
   double s = 0.0;
-  for (int q = 0; q < nparts; ++q) s += (double)part[(long long)q * n + j];
-  out[j] = (float)s;
+  if (j < n) {
+#pragma unroll 8
+    for (int p = q; p < nparts; p += kColLanes) s += (double)part[(long long)p * n + j];
+  }
+  sh[q][c] = s;
+  __syncthreads();
+  if (q == 0 && j < n) {
+    double t = 0.0;
+    for (int r = 0; r < kColLanes; ++r) t += sh[r][c];
+    out[j] = (float)t;
+  }
 }
 
 // One thread per (group g, expert e): sum the tiles of group g in order.
@@ -262,7 +277,7 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
 hipError_t launch_colsum(const float* part, int nparts, int n, float* out, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   ProfScope ps("gate_colsum", s);
-  colsum_kernel<<<dim3((n + 255) / 256), dim3(256), 0, s>>>(part, nparts, n, out);
+  colsum_kernel<<<dim3((n + 63) / 64), dim3(64 * kColLanes), 0, s>>>(part, nparts, n, out);
   return hipGetLastError();
 }
 
