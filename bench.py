@@ -71,14 +71,14 @@ def kernel_work(name, cfg, rows, nonempty, T):
     if name == "dispatch_permute":
         return (T * k * 4 * 2 + rows * 4, 0.0, "i32")
     if name == "dispatch_hist":
-        return (T * k * 4 + ((T * k + 1023) // 1024) * n * 4, 0.0, "i32")
-    rpb = max(16, -(-((T + 255) // 256) // 4) * 4)
+        return (T * k * 4 + ((T * k + 255) // 256) * n * 4, 0.0, "i32")
+    rpb = max(16, -(-((T + 255) // 256) // 8) * 8)
     nparts = (T + rpb - 1) // rpb
     if name == "gate_colsum":
         return (nparts * n * 4 + n * 4, 0.0, "f32")
     if name == "dispatch_colscan":
-        return (((T * k + 1023) // 1024) * n * 8 + n * 4, 0.0, "i32")
-    if name in ("dispatch_offsets", "ffn_tilemap", "aux_loss"):
+        return (((T * k + 255) // 256) * n * 8 + n * 4, 0.0, "i32")
+    if name in ("dispatch_finalize", "dispatch_offsets", "ffn_tilemap", "aux_loss"):
         return (n * 12, 0.0, "i32")
     return (0.0, 0.0, "")
 
@@ -136,6 +136,8 @@ def main():
     ap.add_argument("--profile-steps", type=int, default=20)
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches only (default: also replay a HIP graph)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the layer is built and "
@@ -164,14 +166,42 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps")
 
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
+    def timed(step_fn):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step_fn()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    def eager_step():
         layer.forward(inp["x"], inp.get("noise"), inp.get("noise2"), y=y, losses=losses)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+
+    eager_elapsed = timed(eager_step)
+    log(f"[bench] eager: {eager_elapsed / args.steps * 1e6:.1f} us/step, "
+        f"{T * args.steps / eager_elapsed / 1e6:.2f} M tokens/s")
+    mode, elapsed = "eager launches", eager_elapsed
+    graph = None
+    if not args.eager:
+        # The whole forward captured once as a HIP graph and replayed: the
+        # same kernels, with the per-launch host and queue overhead removed.
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            eager_step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            eager_step()
+        for _ in range(args.warmup):
+            graph.replay()
+        graph_elapsed = timed(graph.replay)
+        log(f"[bench] graph: {graph_elapsed / args.steps * 1e6:.1f} us/step, "
+            f"{T * args.steps / graph_elapsed / 1e6:.2f} M tokens/s")
+        if graph_elapsed < elapsed:
+            mode, elapsed = "HIP graph replay of the whole forward", graph_elapsed
     ms_per_step = elapsed / args.steps * 1e3
     tokens_per_s = T * args.steps / elapsed
-    log(f"[bench] {ms_per_step * 1e3:.1f} us/step, {tokens_per_s / 1e6:.2f} M tokens/s")
 
     # Per-kernel durations: HIP events recorded by the library on its stream.
     moe.moe_profile_enable(True)
@@ -229,6 +259,8 @@ def main():
                    "rows": rows, "nonempty_experts": nonempty, "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "kernels": kernels,
+        "timing": {"mode": mode, "eager_us_per_step": eager_elapsed / args.steps * 1e6,
+                   "graph_us_per_step": (graph_elapsed / args.steps * 1e6) if graph else None},
     }
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle on the first {args.cpu_sample_tokens} tokens")

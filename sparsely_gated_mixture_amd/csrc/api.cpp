@@ -116,6 +116,24 @@ long long capacity(const moe_config& c) {
 
 long long round_up(long long v, long long m) { return (v + m - 1) / m * m; }
 
+}  // namespace
+
+int moe::device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
+
+namespace {
+
 // ---------------------------------------------------------------------------
 // Workspace layout.  [stage scratch: max over gate / dispatch / ffn]
 // [forward intermediates].  Stage calls use only the first part.
@@ -141,7 +159,7 @@ struct Plan {
   size_t gate_bytes = 0, dispatch_bytes = 0, ffn_bytes = 0, stage_bytes = 0;
   // forward intermediates
   Region f_idx, f_w, f_imp, f_load, f_counts_pre, f_counts, f_offsets, f_perm, f_slot, f_xperm,
-      f_yperm;
+      f_yperm, f_tile_expert, f_tile_row0, f_tile_count;
   size_t total = 0;
 };
 
@@ -166,12 +184,12 @@ Plan make_plan(const moe_config& c) {
   p.ldl = (int)round_up(ncols, 4);
   {
     const long long t128 = ((T + 127) / 128) * ((ncols + 127) / 128);
-    p.gemm_bm = t128 >= 256 ? 128 : 64;
+    p.gemm_bm = t128 >= 512 ? 128 : 64;
   }
   {
     // one partial vector per block; at most 256 blocks (one per CU) once T
     // is large, so the column sums stay short
-    long long rpb = std::max(16LL, round_up((T + 255) / 256, 4));
+    long long rpb = std::max(16LL, round_up((T + 255) / 256, kTopkWaves));
     p.rows_per_block = (int)rpb;
     p.nparts = (int)((T + rpb - 1) / rpb);
   }
@@ -241,6 +259,9 @@ Plan make_plan(const moe_config& c) {
   p.f_slot = w.take(A1 * 4);
   p.f_xperm = w.take(A1 * d * (c.expert_dtype == MOE_BF16 ? 2 : 4));
   p.f_yperm = w.take(A1 * d * 4);
+  p.f_tile_expert = w.take((size_t)p.max_mtiles * 4);
+  p.f_tile_row0 = w.take((size_t)p.max_mtiles * 4);
+  p.f_tile_count = w.take(4);
   p.total = w.at;
   return p;
 }
@@ -302,8 +323,8 @@ moe_status run_gate(const moe_config& c, const Plan& p, const float* x, const fl
   t.part_load = noisy ? at<float>(ws, p.part_load) : nullptr;
   t.rows_per_block = p.rows_per_block;
   HIP_TRY(launch_topk(t, s));
-  HIP_TRY(launch_colsum(t.part_imp, p.nparts, n, importance, s));
-  if (noisy) HIP_TRY(launch_colsum(t.part_load, p.nparts, n, load, s));
+  HIP_TRY(launch_colsum(t.part_imp, p.nparts, n, importance, noisy ? t.part_load : nullptr,
+                        load, s));
   return MOE_OK;
 }
 
@@ -349,20 +370,35 @@ moe_status run_gate_hier(const moe_config& c, const Plan& p, const float* x, con
   t.part_load = noisy ? at<float>(ws, p.part_load) : nullptr;
   t.rows_per_block = p.rows_per_block;
   HIP_TRY(launch_topk(t, s));
-  HIP_TRY(launch_colsum(t.part_imp, p.nparts, a, at<float>(ws, p.prim_imp), s));
-  if (noisy) HIP_TRY(launch_colsum(t.part_load, p.nparts, a, at<float>(ws, p.prim_load), s));
+  HIP_TRY(launch_colsum(t.part_imp, p.nparts, a, at<float>(ws, p.prim_imp),
+                        noisy ? t.part_load : nullptr, at<float>(ws, p.prim_load), s));
   // 2. rows of each group (tokens ascending)
   int32_t* g_counts_pre = at<int32_t>(ws, p.g_counts_pre);
   int32_t* g_offsets = at<int32_t>(ws, p.g_offsets);
   int32_t* g_perm = at<int32_t>(ws, p.g_perm);
-  HIP_TRY(launch_dispatch(prim_idx, c.T, k1, a, (long long)1 << 62, g_counts_pre,
-                          at<int32_t>(ws, p.g_counts), g_offsets, g_perm,
-                          at<int32_t>(ws, p.g_slot), at<int32_t>(ws, p.g_chunk_hist),
-                          at<int32_t>(ws, p.g_chunk_base), s));
   int32_t* t2e = at<int32_t>(ws, p.t2_expert);
   int32_t* t2r = at<int32_t>(ws, p.t2_row0);
   int32_t* t2c = at<int32_t>(ws, p.t2_count);
-  HIP_TRY(launch_tilemap(g_offsets, a, kSecondaryBM, t2e, t2r, t2c, s));
+  {
+    DispatchArgs da{};
+    da.topk_idx = prim_idx;
+    da.T = c.T;
+    da.k = k1;
+    da.n = a;
+    da.cap = (long long)1 << 62;
+    da.counts_pre = g_counts_pre;
+    da.counts = at<int32_t>(ws, p.g_counts);
+    da.offsets = g_offsets;
+    da.perm = g_perm;
+    da.slot_pos = at<int32_t>(ws, p.g_slot);
+    da.chunk_hist = at<int32_t>(ws, p.g_chunk_hist);
+    da.chunk_base = at<int32_t>(ws, p.g_chunk_base);
+    da.tile_bm = kSecondaryBM;
+    da.tile_expert = t2e;
+    da.tile_row0 = t2r;
+    da.tile_count = t2c;
+    HIP_TRY(launch_dispatch(da, s));
+  }
   // 3. secondary logits: each group's own gate over its rows
   {
     GemmF32Args g{};
@@ -416,26 +452,63 @@ moe_status run_gate_hier(const moe_config& c, const Plan& p, const float* x, con
   return MOE_OK;
 }
 
+// Optional extras of the layer forward (fused into the dispatch finalize):
+// the grouped GEMM's tile map and the auxiliary losses.
+struct ForwardExtras {
+  int32_t* tile_expert = nullptr;
+  int32_t* tile_row0 = nullptr;
+  int32_t* tile_count = nullptr;
+  float* losses = nullptr;
+  const float* importance = nullptr;
+  const float* load = nullptr;
+};
+
 moe_status run_dispatch(const moe_config& c, const Plan& p, const int32_t* topk_idx,
                         const float* x, int32_t* counts_pre, int32_t* counts, int32_t* offsets,
-                        int32_t* perm, int32_t* slot_pos, void* x_perm, void* ws, hipStream_t s) {
-  HIP_TRY(launch_dispatch(topk_idx, c.T, c.k, c.n_experts, capacity(c), counts_pre, counts,
-                          offsets, perm, slot_pos, at<int32_t>(ws, p.chunk_hist),
-                          at<int32_t>(ws, p.chunk_base), s));
-  HIP_TRY(launch_gather(x, perm, offsets + c.n_experts, c.T * c.k, c.d_model,
-                        c.expert_dtype == MOE_BF16, x_perm, s));
+                        int32_t* perm, int32_t* slot_pos, void* x_perm, void* ws, hipStream_t s,
+                        const ForwardExtras* fx = nullptr) {
+  DispatchArgs da{};
+  da.topk_idx = topk_idx;
+  da.T = c.T;
+  da.k = c.k;
+  da.n = c.n_experts;
+  da.cap = capacity(c);
+  da.counts_pre = counts_pre;
+  da.counts = counts;
+  da.offsets = offsets;
+  da.perm = perm;
+  da.slot_pos = slot_pos;
+  da.chunk_hist = at<int32_t>(ws, p.chunk_hist);
+  da.chunk_base = at<int32_t>(ws, p.chunk_base);
+  if (fx) {
+    da.tile_bm = p.ffn_bm;
+    da.tile_expert = fx->tile_expert;
+    da.tile_row0 = fx->tile_row0;
+    da.tile_count = fx->tile_count;
+    da.losses = fx->losses;
+    da.importance = fx->importance;
+    da.load = fx->load;
+    da.w_imp = c.w_importance;
+    da.w_load = c.w_load;
+    da.alpha = c.alpha_switch;
+  }
+  HIP_TRY(launch_dispatch(da, s));
+  HIP_TRY(launch_gather(x, slot_pos, c.T, c.k, c.d_model, c.expert_dtype == MOE_BF16, x_perm, s));
   return MOE_OK;
 }
 
+// `fx` (layer forward) carries a tile map the dispatch already wrote;
+// otherwise the tile map is built here from `offsets`.
 moe_status run_ffn(const moe_config& c, const Plan& p, const void* x_perm,
                    const int32_t* offsets, const void* w1, const float* b1, const void* w3,
-                   const void* w2, const float* b2, float* y_perm, void* ws, hipStream_t s) {
+                   const void* w2, const float* b2, float* y_perm, void* ws, hipStream_t s,
+                   const ForwardExtras* fx = nullptr) {
   const int n = c.n_experts, d = c.d_model, h = c.d_hidden;
-  int32_t* te = at<int32_t>(ws, p.t_expert);
-  int32_t* tr = at<int32_t>(ws, p.t_row0);
-  int32_t* tc = at<int32_t>(ws, p.t_count);
+  int32_t* te = fx ? fx->tile_expert : at<int32_t>(ws, p.t_expert);
+  int32_t* tr = fx ? fx->tile_row0 : at<int32_t>(ws, p.t_row0);
+  int32_t* tc = fx ? fx->tile_count : at<int32_t>(ws, p.t_count);
   void* hidden = at<void>(ws, p.hidden);
-  HIP_TRY(launch_tilemap(offsets, n, p.ffn_bm, te, tr, tc, s));
+  if (!fx) HIP_TRY(launch_tilemap(offsets, n, p.ffn_bm, te, tr, tc, s));
   if (c.expert_dtype == MOE_BF16) {
     GemmBf16Args g{};
     g.A = (const uint16_t*)x_perm;
@@ -453,6 +526,7 @@ moe_status run_ffn(const moe_config& c, const Plan& p, const void* x_perm,
     g.offsets = offsets;
     g.tile_count = tc;
     g.max_mtiles = p.max_mtiles;
+    g.num_cus = device_cus();
     HIP_TRY(launch_gemm_bf16(g, c.act == MOE_ACT_SWIGLU ? EPI_SWIGLU_BF16 : EPI_RELU_BF16, s));
     GemmBf16Args g2 = g;
     g2.A = (const uint16_t*)hidden;
@@ -698,11 +772,16 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const float
   } else {
     CHECK(run_gate(c, p, x, wt->w_gate, wt->b_gate, wt->w_noise, noise, idx, w, imp, ld, ws, s));
   }
-  CHECK(run_dispatch(c, p, idx, x, counts_pre, counts, offsets, perm, slot, xperm, ws, s));
-  CHECK(run_ffn(c, p, xperm, offsets, wt->w1, wt->b1, wt->w3, wt->w2, wt->b2, yperm, ws, s));
+  ForwardExtras fx;
+  fx.tile_expert = at<int32_t>(ws, p.f_tile_expert);
+  fx.tile_row0 = at<int32_t>(ws, p.f_tile_row0);
+  fx.tile_count = at<int32_t>(ws, p.f_tile_count);
+  fx.losses = losses;
+  fx.importance = imp;
+  fx.load = has_load ? ld : nullptr;
+  CHECK(run_dispatch(c, p, idx, x, counts_pre, counts, offsets, perm, slot, xperm, ws, s, &fx));
+  CHECK(run_ffn(c, p, xperm, offsets, wt->w1, wt->b1, wt->w3, wt->w2, wt->b2, yperm, ws, s, &fx));
   HIP_TRY(launch_combine(yperm, slot, w, c.T, c.k, c.d_model, y, s));
-  HIP_TRY(launch_aux(imp, has_load ? ld : nullptr, counts_pre, c.T, c.k, c.n_experts,
-                     c.w_importance, c.w_load, c.alpha_switch, losses, s));
   return MOE_OK;
 }
 

@@ -38,52 +38,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
-// Fixed-shape tree sum over the 256 threads (same order every call).
-__device__ double block_sum(double v, double* sh) {
-  sh[threadIdx.x] = v;
-  __syncthreads();
-  for (int off = 128; off >= 1; off >>= 1) {
-    if ((int)threadIdx.x < off) sh[threadIdx.x] += sh[threadIdx.x + off];
-    __syncthreads();
-  }
-  const double r = sh[0];
-  __syncthreads();
-  return r;
-}
-
-__device__ double cv2_block(const float* v, int n, double* sh) {
-  double s = 0.0;
-  for (int i = threadIdx.x; i < n; i += 256) s += (double)v[i];
-  const double mean = block_sum(s, sh) / n;
-  if (mean == 0.0) return 0.0;
-  double q = 0.0;
-  for (int i = threadIdx.x; i < n; i += 256) {
-    const double dv = (double)v[i] - mean;
-    q += dv * dv;
-  }
-  const double var = block_sum(q, sh) / n;
-  return var / (mean * mean);
-}
-
 __global__ __launch_bounds__(256) void aux_kernel(const float* __restrict__ importance,
                                                   const float* __restrict__ load,
                                                   const int32_t* __restrict__ counts_pre, int T,
                                                   int k, int n, float w_imp, float w_load,
                                                   float alpha, float* __restrict__ losses) {
   __shared__ double sh[256];
-  const double li = (double)w_imp * cv2_block(importance, n, sh);
-  const double ll = load ? (double)w_load * cv2_block(load, n, sh) : 0.0;
-  double fp = 0.0;
-  if (T > 0) {
-    for (int i = threadIdx.x; i < n; i += 256)
-      fp += ((double)counts_pre[i] / ((double)T * k)) * ((double)importance[i] / T);
-  }
-  const double sw = (double)alpha * n * block_sum(fp, sh);
-  if (threadIdx.x == 0) {
-    losses[0] = (float)li;
-    losses[1] = (float)ll;
-    losses[2] = (float)sw;
-  }
+  block_aux_losses<256>(importance, load, counts_pre, T, k, n, w_imp, w_load, alpha, losses, sh);
 }
 
 }  // namespace

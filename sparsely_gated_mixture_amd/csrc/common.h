@@ -38,6 +38,46 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
   return __uint_as_float(u);
 }
 
+// Wave-wide reductions with DPP: pairwise and quad swaps, then rotations by
+// 4 and 8 inside each 16-lane row, then the four row results (lanes 0, 16,
+// 32, 48) combined in a fixed order in scalar registers.  The result is
+// wave-uniform and the summation order is the same on every call.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL,
+                                                    0xF, 0xF, false));
+}
+constexpr int kDppSwap1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppSwap2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kDppRor4 = 0x124;  // row_ror:4
+constexpr int kDppRor8 = 0x128;  // row_ror:8
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<kDppSwap1>(v));
+  v = max(v, dpp_u32<kDppSwap2>(v));
+  v = max(v, dpp_u32<kDppRor4>(v));
+  v = max(v, dpp_u32<kDppRor8>(v));
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_f32<kDppSwap1>(v);
+  v += dpp_f32<kDppSwap2>(v);
+  v += dpp_f32<kDppRor4>(v);
+  v += dpp_f32<kDppRor8>(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
 // Butterfly reductions over the 64 lanes.  Every lane ends with the same
 // bits (each step adds / compares the same two operands in both partners).
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
@@ -53,6 +93,86 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
   return v;
+}
+
+// Sum over the NT threads of a block: a butterfly inside each wavefront (all
+// lanes end with the same bits), then the NT/64 wave sums added in wave
+// order.  Same order on every call.  `sh` holds at least NT/64 doubles; every
+// thread gets the total.
+template <int NT>
+__device__ __forceinline__ double block_sum(double v, double* sh) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double r = 0.0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) r += sh[i];
+  __syncthreads();
+  return r;
+}
+
+// Exclusive prefix sum of one int per thread over a block of NT threads
+// (shuffle scan inside each wavefront, wave totals in LDS); also returns the
+// block total.  `sh` holds at least NT/64 ints.
+template <int NT>
+__device__ __forceinline__ int2 block_exscan(int v, int* sh) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) sh[w] = incl;
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    base += i < w ? sh[i] : 0;
+    total += sh[i];
+  }
+  __syncthreads();
+  return make_int2(base + incl - v, total);
+}
+
+// Squared coefficient of variation of v[0..n) with the population variance,
+// two passes, 0 when the mean is 0 (arXiv 1701.06538 summary, xyznot.com,
+// load-balancing losses: L = w * CV(.)^2).
+template <int NT>
+__device__ double block_cv2(const float* v, int n, double* sh) {
+  double s = 0.0;
+  for (int i = threadIdx.x; i < n; i += NT) s += (double)v[i];
+  const double mean = block_sum<NT>(s, sh) / n;
+  if (mean == 0.0) return 0.0;
+  double q = 0.0;
+  for (int i = threadIdx.x; i < n; i += NT) {
+    const double dv = (double)v[i] - mean;
+    q += dv * dv;
+  }
+  return (block_sum<NT>(q, sh) / n) / (mean * mean);
+}
+
+// losses[0] = w_imp * CV(importance)^2, losses[1] = w_load * CV(load)^2 (0
+// without load), losses[2] = alpha * n * sum_i f_i P_i with f_i =
+// counts_pre[i]/(T*k) and P_i = importance[i]/T (MoE survey, tufusi.com 3.2).
+template <int NT>
+__device__ void block_aux_losses(const float* importance, const float* load,
+                                 const int32_t* counts_pre, int T, int k, int n, float w_imp,
+                                 float w_load, float alpha, float* losses, double* sh) {
+  const double li = (double)w_imp * block_cv2<NT>(importance, n, sh);
+  const double ll = load ? (double)w_load * block_cv2<NT>(load, n, sh) : 0.0;
+  double fp = 0.0;
+  if (T > 0) {
+    for (int i = threadIdx.x; i < n; i += NT)
+      fp += ((double)counts_pre[i] / ((double)T * k)) * ((double)importance[i] / T);
+  }
+  const double sw = (double)alpha * n * block_sum<NT>(fp, sh);
+  if (threadIdx.x == 0) {
+    losses[0] = (float)li;
+    losses[1] = (float)ll;
+    losses[2] = (float)sw;
+  }
 }
 
 // Block index -> linear tile index such that each XCD gets one contiguous

@@ -7,15 +7,18 @@
 //   1. chunk_hist_kernel: per-chunk expert histogram (integer LDS atomics,
 //      whose result does not depend on their order).
 //   2. column_scan_kernel: per expert, exclusive prefix over chunks, and the
-//      total count (counts_pre).
-//   3. offsets_kernel: counts = min(counts_pre, C), exclusive scan -> offsets.
+//      total count (counts_pre); four threads per expert each walk a quarter
+//      of the chunks, and the quarters are joined in order.
+//   3. finalize_kernel: counts = min(counts_pre, C), exclusive scan ->
+//      offsets; in the layer forward it also writes the grouped GEMM's tile
+//      map and the auxiliary losses (all single-block work, one launch).
 //   4. permute_kernel: one wavefront walks its chunk in order, 64 slots at a
 //      time; a slot's rank inside its group of 64 is the number of earlier
 //      lanes with the same expert (found with wave-uniform readlanes), so
 //      the resulting order is exactly (token, slot) order -- stable, and
 //      independent of scheduling.
-//   5. gather_kernel: x_perm[row] = x[perm[row]], converted to bf16 (RNE)
-//      or copied as fp32.
+//   5. gather_kernel: one wavefront per token reads its row once and writes
+//      it to each kept slot's row, converted to bf16 (RNE) or copied as fp32.
 #include "common.h"
 #include "launch.h"
 
@@ -38,53 +41,79 @@ __global__ __launch_bounds__(256) void chunk_hist_kernel(const int32_t* __restri
     chunk_hist[(long long)blockIdx.x * n + e] = hist[e];
 }
 
+// 64 experts per block; thread (e, q) covers chunks [q*G, (q+1)*G).
 __global__ __launch_bounds__(256) void column_scan_kernel(const int32_t* __restrict__ chunk_hist,
                                                           int nchunks, int n,
                                                           int32_t* __restrict__ chunk_base,
                                                           int32_t* __restrict__ counts_pre) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= n) return;
-  int run = 0;
+  __shared__ int32_t qs[4][64];
+  const int el = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + el;
+  const int G = (nchunks + 3) / 4;
+  const int c0 = q * G, c1 = min(nchunks, c0 + G);
+  int sum = 0;
+  if (e < n) {
 #pragma unroll 8
-  for (int c = 0; c < nchunks; ++c) {
-    const int h = chunk_hist[(long long)c * n + e];
-    chunk_base[(long long)c * n + e] = run;
-    run += h;
+    for (int c = c0; c < c1; ++c) sum += chunk_hist[(long long)c * n + e];
   }
-  counts_pre[e] = run;
+  qs[q][el] = sum;
+  __syncthreads();
+  int run = 0;
+  for (int r = 0; r < q; ++r) run += qs[r][el];
+  if (e < n) {
+#pragma unroll 8
+    for (int c = c0; c < c1; ++c) {
+      const int h = chunk_hist[(long long)c * n + e];
+      chunk_base[(long long)c * n + e] = run;
+      run += h;
+    }
+    if (q == 3) counts_pre[e] = run;
+  }
 }
 
-// Single block: counts = min(counts_pre, cap); offsets = exclusive scan.
-__global__ __launch_bounds__(1024) void offsets_kernel(const int32_t* __restrict__ counts_pre,
-                                                       int n, long long cap,
-                                                       int32_t* __restrict__ counts,
-                                                       int32_t* __restrict__ offsets) {
-  __shared__ int32_t tsum[1024];
-  const int per = (n + 1023) / 1024;
-  const int b = threadIdx.x * per;
+// Single block of kFinThreads threads; thread t owns the contiguous experts
+// [t*per, t*per + per).
+constexpr int kFinThreads = 256;
+__global__ __launch_bounds__(kFinThreads) void finalize_kernel(const DispatchArgs a) {
+  __shared__ int32_t si[kFinThreads / 64];
+  __shared__ double sd[kFinThreads / 64];
+  const int n = a.n;
+  const int per = (n + kFinThreads - 1) / kFinThreads;
+  const int b = min(n, (int)threadIdx.x * per), e1 = min(n, b + per);
   int local = 0;
-  for (int i = 0; i < per && b + i < n; ++i) {
-    const long long c = counts_pre[b + i];
-    local += (int)(c < cap ? c : cap);
+  for (int e = b; e < e1; ++e) {
+    const long long c = a.counts_pre[e];
+    const int kept = (int)(c < a.cap ? c : a.cap);
+    a.counts[e] = kept;
+    local += kept;
   }
-  tsum[threadIdx.x] = local;
-  __syncthreads();
-  // Hillis-Steele inclusive scan over the 1024 thread sums.
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = threadIdx.x >= off ? tsum[threadIdx.x - off] : 0;
-    __syncthreads();
-    tsum[threadIdx.x] += v;
-    __syncthreads();
-  }
-  int run = threadIdx.x ? tsum[threadIdx.x - 1] : 0;
-  for (int i = 0; i < per && b + i < n; ++i) {
-    const long long c = counts_pre[b + i];
-    const int kept = (int)(c < cap ? c : cap);
-    counts[b + i] = kept;
-    offsets[b + i] = run;
+  const int2 sc = block_exscan<kFinThreads>(local, si);
+  int run = sc.x, nt = 0;
+  for (int e = b; e < e1; ++e) {
+    a.offsets[e] = run;
+    const int kept = a.counts[e];
     run += kept;
+    if (a.tile_bm > 0) nt += (kept + a.tile_bm - 1) / a.tile_bm;
   }
-  if (threadIdx.x == 1023) offsets[n] = tsum[1023];
+  if (threadIdx.x == kFinThreads - 1) a.offsets[n] = sc.y;
+  if (a.tile_bm > 0) {
+    const int2 tc = block_exscan<kFinThreads>(nt, si);
+    int t = tc.x;
+    int off = sc.x;
+    for (int e = b; e < e1; ++e) {
+      const int kept = a.counts[e];
+      for (int m = 0; m < kept; m += a.tile_bm) {
+        a.tile_expert[t] = e;
+        a.tile_row0[t] = off + m;
+        ++t;
+      }
+      off += kept;
+    }
+    if (threadIdx.x == kFinThreads - 1) *a.tile_count = tc.y;
+  }
+  if (a.losses)
+    block_aux_losses<kFinThreads>(a.importance, a.load, a.counts_pre, a.T, a.k, n, a.w_imp,
+                                  a.w_load, a.alpha, a.losses, sd);
 }
 
 // One wavefront per chunk.
@@ -137,30 +166,36 @@ __global__ __launch_bounds__(64) void permute_kernel(const int32_t* __restrict__
   }
 }
 
-// One wavefront per row; 8 elements per lane per step.
+// One wavefront per token; 8 elements per lane per step.
 __global__ __launch_bounds__(256) void gather_kernel(const float* __restrict__ x,
-                                                     const int32_t* __restrict__ perm,
-                                                     const int32_t* __restrict__ rows_dev,
-                                                     int d, int bf16_out, void* __restrict__ out) {
+                                                     const int32_t* __restrict__ slot_pos, int T,
+                                                     int k, int d, int bf16_out,
+                                                     void* __restrict__ out) {
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= *rows_dev) return;
-  const float* src = x + (long long)perm[row] * d;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* src = x + (long long)t * d;
+  const int32_t* sp = slot_pos + (long long)t * k;
   for (int c = lane * 8; c < d; c += 64 * 8) {
     const f32x4 v0 = *(const f32x4*)(src + c);
     const f32x4 v1 = *(const f32x4*)(src + c + 4);
+    uint4 pk = make_uint4(0u, 0u, 0u, 0u);
     if (bf16_out) {
-      uint32_t w[4];
-      w[0] = (uint32_t)f32_to_bf16(v0[0]) | ((uint32_t)f32_to_bf16(v0[1]) << 16);
-      w[1] = (uint32_t)f32_to_bf16(v0[2]) | ((uint32_t)f32_to_bf16(v0[3]) << 16);
-      w[2] = (uint32_t)f32_to_bf16(v1[0]) | ((uint32_t)f32_to_bf16(v1[1]) << 16);
-      w[3] = (uint32_t)f32_to_bf16(v1[2]) | ((uint32_t)f32_to_bf16(v1[3]) << 16);
-      uint4 pk = make_uint4(w[0], w[1], w[2], w[3]);
-      *(uint4*)((uint16_t*)out + (long long)row * d + c) = pk;
-    } else {
-      float* dst = (float*)out + (long long)row * d + c;
-      *(f32x4*)dst = v0;
-      *(f32x4*)(dst + 4) = v1;
+      pk.x = (uint32_t)f32_to_bf16(v0[0]) | ((uint32_t)f32_to_bf16(v0[1]) << 16);
+      pk.y = (uint32_t)f32_to_bf16(v0[2]) | ((uint32_t)f32_to_bf16(v0[3]) << 16);
+      pk.z = (uint32_t)f32_to_bf16(v1[0]) | ((uint32_t)f32_to_bf16(v1[1]) << 16);
+      pk.w = (uint32_t)f32_to_bf16(v1[2]) | ((uint32_t)f32_to_bf16(v1[3]) << 16);
+    }
+    for (int s = 0; s < k; ++s) {
+      const int row = sp[s];
+      if (row < 0) continue;
+      if (bf16_out) {
+        *(uint4*)((uint16_t*)out + (long long)row * d + c) = pk;
+      } else {
+        float* dst = (float*)out + (long long)row * d + c;
+        *(f32x4*)dst = v0;
+        *(f32x4*)(dst + 4) = v1;
+      }
     }
   }
 }
@@ -201,47 +236,45 @@ __global__ __launch_bounds__(1024) void tilemap_kernel(const int32_t* __restrict
 
 }  // namespace
 
-hipError_t launch_dispatch(const int32_t* topk_idx, int T, int k, int n, long long cap,
-                           int32_t* counts_pre, int32_t* counts, int32_t* offsets,
-                           int32_t* perm, int32_t* slot_pos, int32_t* chunk_hist,
-                           int32_t* chunk_base, hipStream_t s) {
-  const long long A = (long long)T * k;
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
+  const long long A = (long long)a.T * a.k;
+  const int n = a.n;
   const int nchunks = (int)((A + kDispatchChunk - 1) / kDispatchChunk);
   const size_t shm = (size_t)n * sizeof(int32_t);
   if (nchunks > 0) {
     ProfScope ps("dispatch_hist", s);
-    chunk_hist_kernel<<<dim3(nchunks), dim3(256), shm, s>>>(topk_idx, A, n, chunk_hist);
+    chunk_hist_kernel<<<dim3(nchunks), dim3(256), shm, s>>>(a.topk_idx, A, n, a.chunk_hist);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   {
     ProfScope ps("dispatch_colscan", s);
-    column_scan_kernel<<<dim3((n + 255) / 256), dim3(256), 0, s>>>(chunk_hist, nchunks, n,
-                                                                    chunk_base, counts_pre);
+    column_scan_kernel<<<dim3((n + 63) / 64), dim3(256), 0, s>>>(a.chunk_hist, nchunks, n,
+                                                                  a.chunk_base, a.counts_pre);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
-    ProfScope ps("dispatch_offsets", s);
-    offsets_kernel<<<dim3(1), dim3(1024), 0, s>>>(counts_pre, n, cap, counts, offsets);
+    ProfScope ps("dispatch_finalize", s);
+    finalize_kernel<<<dim3(1), dim3(kFinThreads), 0, s>>>(a);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (nchunks > 0) {
     ProfScope ps("dispatch_permute", s);
-    permute_kernel<<<dim3(nchunks), dim3(64), shm, s>>>(topk_idx, A, k, n, cap, chunk_base,
-                                                         offsets, perm, slot_pos);
+    permute_kernel<<<dim3(nchunks), dim3(64), shm, s>>>(a.topk_idx, A, a.k, n, a.cap,
+                                                         a.chunk_base, a.offsets, a.perm,
+                                                         a.slot_pos);
     e = hipGetLastError();
   }
   return e;
 }
 
-hipError_t launch_gather(const float* x, const int32_t* perm, const int32_t* rows_dev,
-                         int max_rows, int d, int bf16_out, void* x_perm, hipStream_t s) {
-  if (max_rows <= 0) return hipSuccess;
+hipError_t launch_gather(const float* x, const int32_t* slot_pos, int T, int k, int d,
+                         int bf16_out, void* x_perm, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
   ProfScope ps("dispatch_gather", s);
-  gather_kernel<<<dim3((max_rows + 3) / 4), dim3(256), 0, s>>>(x, perm, rows_dev, d, bf16_out,
-                                                               x_perm);
+  gather_kernel<<<dim3((T + 3) / 4), dim3(256), 0, s>>>(x, slot_pos, T, k, d, bf16_out, x_perm);
   return hipGetLastError();
 }
 

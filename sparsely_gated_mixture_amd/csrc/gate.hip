@@ -1,10 +1,13 @@
-// Gating network epilogue on gfx950: one wavefront per token row.
+// Gating network epilogue on gfx950: one wavefront per token row, eight
+// wavefronts per block, each prefetching its next row while it works on the
+// current one.
 //
 // Reads the fp32 logits written by the gate GEMM and computes, per row,
 //   H_j = clean_j (+ bias_j) + z_j * Softplus(raw_j)      (noisy gate)
-// then KeepTopK by k+1 rounds of a wave-wide arg-max over 64-bit keys
-// (ordered float bits << 32 | ~index: larger H first, lower index first on
-// equal H), the softmax over the kept values (or the Switch full softmax),
+// then KeepTopK by k+1 rounds of a wave-wide arg-max (DPP max of the ordered
+// float keys, then a ballot for the lowest index holding the maximum: larger
+// H first, lower index first on equal H), the softmax over the kept values
+// (or the Switch full softmax),
 // and the per-expert sums behind the auxiliary losses:
 //   Importance_j += G_j,  Load_j += Phi((clean_j - thr_j) / Softplus(raw_j)),
 // thr_j = H_(k+1) if j is kept, H_(k) otherwise.
@@ -32,9 +35,17 @@ __device__ __forceinline__ float readlane_f(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
+// Per-row inputs of one wavefront: lane owns experts j = lane + 64 q.
 template <int NPL>
-__global__ __launch_bounds__(256) void topk_kernel(const TopkArgs p) {
-  extern __shared__ float red[];  // [2][4][n]
+struct RowIn {
+  float c[NPL];  // clean logit (+ bias)
+  float r[NPL];  // raw noise logit (noisy gate only)
+  float z[NPL];  // standard normal draw (noisy gate only)
+};
+
+template <int NPL>
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs p) {
+  extern __shared__ float red[];  // [kTopkWaves][n]
   const int n = p.n, k = p.k;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
@@ -52,16 +63,8 @@ __global__ __launch_bounds__(256) void topk_kernel(const TopkArgs p) {
     row_end = min(row_begin + p.rows_per_block, p.rows);
   }
 
-  float imp[NPL], ld[NPL];
-#pragma unroll
-  for (int q = 0; q < NPL; ++q) imp[q] = ld[q] = 0.f;
-
-  const int R = min(k + 1, n);
-  for (int r = row_begin + wave; r < row_end; r += 4) {
-    // Token / slot of this row, and where its noise and outputs live.
-    long long noise_row, out_base;
-    float wprim = 1.f;
-    int id_base = 0;
+  // Where row r's noise and outputs live.
+  auto locate = [&](int r, long long& noise_row, long long& out_base, float& wprim) {
     if (grouped) {
       const int t = p.row_token[r];
       int s = 0;
@@ -70,50 +73,86 @@ __global__ __launch_bounds__(256) void topk_kernel(const TopkArgs p) {
       noise_row = ((long long)t * p.k1 + s) * n;
       out_base = (long long)t * p.k1 * k + (long long)s * k;
       wprim = p.prim_w[(long long)t * p.k1 + s];
-      id_base = g * n;
     } else {
       noise_row = (long long)r * n;
       out_base = (long long)r * k;
+      wprim = 1.f;
     }
+  };
+  auto fetch = [&](int r, RowIn<NPL>& in) {
+    long long nrow, ob;
+    float wp;
+    locate(r, nrow, ob, wp);
     const float* lg = p.logits + (long long)r * p.ldl;
-
-    float cl[NPL], sp[NPL], hv[NPL];
-    unsigned long long key[NPL];
 #pragma unroll
     for (int q = 0; q < NPL; ++q) {
       const int j = lane + 64 * q;
       const bool ok = j < n;
-      float c = 0.f, s = 1.f, h = 0.f;
-      if (ok) {
-        c = lg[j];
-        if (p.bias) c += p.bias[j];
-        h = c;
-        if (p.noisy) {
-          s = softplus_f(lg[n + j]);
-          h = c + p.noise[noise_row + j] * s;
-        }
+      in.c[q] = ok ? lg[j] : 0.f;
+      in.r[q] = (ok && p.noisy) ? lg[n + j] : 0.f;
+      in.z[q] = (ok && p.noisy) ? p.noise[nrow + j] : 0.f;
+    }
+  };
+
+  float imp[NPL], ld[NPL], bias[NPL];
+#pragma unroll
+  for (int q = 0; q < NPL; ++q) {
+    imp[q] = ld[q] = 0.f;
+    const int j = lane + 64 * q;
+    bias[q] = (p.bias && j < n) ? p.bias[j] : 0.f;
+  }
+
+  const int R = min(k + 1, n);
+  RowIn<NPL> cur, nxt;
+  int r = row_begin + wave;
+  if (r < row_end) fetch(r, cur);
+  for (; r < row_end; r += kTopkWaves) {
+    if (r + kTopkWaves < row_end) fetch(r + kTopkWaves, nxt);  // next row in flight
+    long long noise_row, out_base;
+    float wprim;
+    locate(r, noise_row, out_base, wprim);
+
+    float cl[NPL], sp[NPL], hv[NPL];
+    uint32_t key[NPL];
+#pragma unroll
+    for (int q = 0; q < NPL; ++q) {
+      const int j = lane + 64 * q;
+      const bool ok = j < n;
+      cl[q] = cur.c[q] + bias[q];
+      sp[q] = 1.f;
+      hv[q] = cl[q];
+      if (p.noisy) {
+        sp[q] = softplus_f(cur.r[q]);
+        hv[q] = cl[q] + cur.z[q] * sp[q];
       }
-      cl[q] = c;
-      sp[q] = s;
-      hv[q] = h;
-      key[q] = ok ? (((unsigned long long)ordered_key(h) << 32) | (unsigned)(~j)) : 0ull;
+      key[q] = ok ? ordered_key(hv[q]) : 0u;
     }
 
-    unsigned selmask = 0;
+    // k+1 rounds of arg-max: the largest key wins; among equal keys the
+    // lowest index (lowest q, then lowest lane) wins.
+    uint32_t selmask = 0;
     int my_j = 0;
     float my_v = 0.f, v0 = 0.f, v_km1 = 0.f, v_k = -INFINITY;
     for (int rd = 0; rd < R; ++rd) {
-      unsigned long long best = 0;
+      uint32_t best = 0;
 #pragma unroll
-      for (int q = 0; q < NPL; ++q) best = key[q] > best ? key[q] : best;
-      best = wave_max_u64(best);
-      const int j = (int)(~(unsigned)(best & 0xffffffffull));
-      const float v = key_to_float((unsigned)(best >> 32));
+      for (int q = 0; q < NPL; ++q) best = max(best, key[q]);
+      const uint32_t m = wave_max_u32(best);
+      int j = 0;
+#pragma unroll
+      for (int q = 0; q < NPL; ++q) {
+        const unsigned long long b = __ballot(key[q] == m);
+        if (b) {
+          j = 64 * q + __builtin_ctzll(b);
+          break;
+        }
+      }
+      const float v = key_to_float(m);
       if (lane == (j & 63)) {
 #pragma unroll
         for (int q = 0; q < NPL; ++q)
           if (q == (j >> 6)) {
-            key[q] = 0ull;
+            key[q] = 0u;
             if (rd < k) selmask |= 1u << q;
           }
       }
@@ -127,22 +166,21 @@ __global__ __launch_bounds__(256) void topk_kernel(const TopkArgs p) {
     }
 
     // Gate weights of the kept slots (lane s holds slot s).
-    float w;
-    float zsum = 0.f;
+    float w, zsum;
     if (p.switch_mode) {
       float ls = 0.f;
 #pragma unroll
       for (int q = 0; q < NPL; ++q)
         if (lane + 64 * q < n) ls += expf(hv[q] - v0);
-      zsum = wave_sum_f32(ls);
+      zsum = wave_sum_dpp(ls);
       w = (lane < k) ? expf(my_v - v0) / zsum : 0.f;
     } else {
       const float e = (lane < k) ? expf(my_v - v0) : 0.f;
-      zsum = wave_sum_f32(e);
+      zsum = wave_sum_dpp(e);
       w = e / zsum;
     }
     if (lane < k) {
-      p.topk_idx[out_base + lane] = id_base + my_j;
+      p.topk_idx[out_base + lane] = (grouped ? g * n : 0) + my_j;
       p.topk_w[out_base + lane] = wprim * w;
     }
 
@@ -168,32 +206,30 @@ __global__ __launch_bounds__(256) void topk_kernel(const TopkArgs p) {
       for (int q = 0; q < NPL; ++q) {
         if (lane + 64 * q < n) {
           const float thr = ((selmask >> q) & 1u) ? v_k : v_km1;
-          const float z = (cl[q] - thr) / sp[q];
-          ld[q] += 0.5f * erfcf(-z * 0.70710678118654752f);
+          const float zz = (cl[q] - thr) / sp[q];
+          ld[q] += 0.5f * erfcf(-zz * 0.70710678118654752f);
         }
       }
     }
+    cur = nxt;
   }
 
-  // Combine the 4 waves in a fixed order, then write this block's partials.
-  float* ri = red;
-  float* rl = red + 4 * n;
+  // Combine the waves in a fixed order, then write this block's partials.
+  for (int pass = 0; pass < 2; ++pass) {
+    float* out = pass == 0 ? p.part_imp : p.part_load;
+    if (!out) break;
 #pragma unroll
-  for (int q = 0; q < NPL; ++q) {
-    const int j = lane + 64 * q;
-    if (j < n) {
-      ri[wave * n + j] = imp[q];
-      rl[wave * n + j] = ld[q];
+    for (int q = 0; q < NPL; ++q) {
+      const int j = lane + 64 * q;
+      if (j < n) red[wave * n + j] = pass == 0 ? imp[q] : ld[q];
     }
-  }
-  __syncthreads();
-  for (int j = threadIdx.x; j < n; j += 256) {
-    const float si = ((ri[j] + ri[n + j]) + ri[2 * n + j]) + ri[3 * n + j];
-    p.part_imp[(long long)part * n + j] = si;
-    if (p.part_load) {
-      const float sl = ((rl[j] + rl[n + j]) + rl[2 * n + j]) + rl[3 * n + j];
-      p.part_load[(long long)part * n + j] = sl;
+    __syncthreads();
+    for (int j = threadIdx.x; j < n; j += kTopkThreads) {
+      float sacc = red[j];
+      for (int w2 = 1; w2 < kTopkWaves; ++w2) sacc += red[w2 * n + j];
+      out[(long long)part * n + j] = sacc;
     }
+    __syncthreads();
   }
 }
 
@@ -202,9 +238,14 @@ __global__ __launch_bounds__(256) void topk_kernel(const TopkArgs p) {
 // many loads in flight), then lane sums are added in lane order: the same
 // order on every call.
 constexpr int kColLanes = 16;
-__global__ __launch_bounds__(1024) void colsum_kernel(const float* __restrict__ part, int nparts,
-                                                      int n, float* __restrict__ out) {
+// blockIdx.y selects the vector: 0 = (part, out), 1 = (part2, out2).
+__global__ __launch_bounds__(1024) void colsum_kernel(const float* __restrict__ part0, int nparts,
+                                                      int n, float* __restrict__ out0,
+                                                      const float* __restrict__ part1,
+                                                      float* __restrict__ out1) {
   __shared__ double sh[kColLanes][64];
+  const float* part = blockIdx.y ? part1 : part0;
+  float* out = blockIdx.y ? out1 : out0;
   const int c = threadIdx.x & 63, q = threadIdx.x >> 6;
   const int j = blockIdx.x * 64 + c;
   double s = 0.0;
@@ -253,9 +294,9 @@ __global__ void hier_finalize_kernel(const float* __restrict__ part_imp,
 
 template <int NPL>
 hipError_t launch_topk_t(const TopkArgs& a, int grid, hipStream_t s) {
-  const size_t shm = (size_t)2 * 4 * a.n * sizeof(float);
+  const size_t shm = (size_t)kTopkWaves * a.n * sizeof(float);
   ProfScope ps(a.tile_expert ? "gate_topk_grouped" : "gate_topk", s);
-  topk_kernel<NPL><<<dim3(grid), dim3(256), shm, s>>>(a);
+  topk_kernel<NPL><<<dim3(grid), dim3(kTopkThreads), shm, s>>>(a);
   return hipGetLastError();
 }
 
@@ -274,10 +315,12 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   return launch_topk_t<32>(a, grid, s);
 }
 
-hipError_t launch_colsum(const float* part, int nparts, int n, float* out, hipStream_t s) {
+hipError_t launch_colsum(const float* part, int nparts, int n, float* out, const float* part2,
+                         float* out2, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   ProfScope ps("gate_colsum", s);
-  colsum_kernel<<<dim3((n + 63) / 64), dim3(64 * kColLanes), 0, s>>>(part, nparts, n, out);
+  colsum_kernel<<<dim3((n + 63) / 64, part2 ? 2 : 1), dim3(64 * kColLanes), 0, s>>>(
+      part, nparts, n, out, part2, out2);
   return hipGetLastError();
 }
 

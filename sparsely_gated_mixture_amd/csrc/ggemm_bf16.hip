@@ -1,138 +1,200 @@
 // Grouped GEMM of the expert FFNs on the gfx950 matrix cores
 // (v_mfma_f32_32x32x16_bf16: bf16 operands, fp32 accumulation).
 //
-// One launch covers every expert: a device-side tile map lists the M-tiles
-// (kBf16BM rows of one expert's merged batch) and every workgroup takes one
-// (M-tile, N-tile) pair.  The weights of expert e are B[e] = [N, K] (out x in,
-// K contiguous) and the activations A = [rows, K], so both operands stream
-// along K.  Tile 128 x 128 (SwiGLU: 128 x 64 outputs over the W1 and W3 rows),
-// BK = 64, four waves in a 2x2 grid, double-buffered padded LDS (one barrier
-// per K step), epilogue staged through LDS for 16-byte coalesced stores.
-// Epilogues: ReLU(+bias) -> bf16 hidden, silu(g)*u -> bf16 hidden,
-// identity(+bias) -> fp32 expert output.
-// Workgroups are mapped so that each XCD owns a contiguous run of tiles: the
-// N-tiles of one M-tile (which share the activation tile) and the M-tiles of
-// one expert (which share its weight tiles) meet in the same L2.
+// One launch covers every expert.  A device-side tile map lists the M-tiles
+// (128 rows of one expert's merged batch); the work items are (M-tile,
+// N-tile) pairs.  Expert e's weights are W[e] = [N, K] (out x in, K
+// contiguous) and the activations X = [rows, K], so both operands stream
+// along K.
+//
+// The expert weights are read once per layer and dominate the bytes, so the
+// kernel is shaped for HBM streaming:
+//  * persistent: one 8-wave workgroup per CU walks a strided run of tiles
+//    inside its XCD's contiguous share of the tile list (N-tiles of one
+//    M-tile, which share the activation tile, and M-tiles of one expert,
+//    which share its weights, run on the same L2 at about the same time);
+//  * K advances 64 at a time, so every row of both operands is read in whole
+//    128-byte lines (narrower per-row reads measured about 30% slower);
+//  * a ring of kStages LDS buffers is filled by direct global->LDS copies
+//    (global_load_lds_dwordx4) kStages-1 steps ahead of the MFMAs, and the
+//    ring runs on across tile boundaries, so a tile's epilogue overlaps the
+//    next tile's loads; one barrier per step;
+//  * N-tiles are 256 wide (SwiGLU: 128 columns of both W1 and W3), so each
+//    activation tile is fetched from L2 N/256 times; this measured faster than
+//    128-wide tiles with a deeper ring (activation re-reads through L2 cost
+//    about as much as the weight stream itself);
+//  * LDS rows are 128 bytes (8 chunks of 16 bytes); chunk c of row r sits at
+//    position c ^ ((r >> 1) & 7), so the 16-byte fragment reads of 16
+//    consecutive rows hit 16 distinct bank groups.
+// The MFMA computes D = W . X^T (weights as the A operand), so each lane ends
+// with 4 consecutive output columns of one row and stores them directly.
+// Epilogues: ReLU(+bias) -> bf16 hidden; silu(x.W1^T) * (x.W3^T) -> bf16
+// hidden; identity(+bias) -> fp32 expert output.
+// Rows past a segment's end and columns past N copy clamped (valid) rows and
+// are never stored; K-tail chunks copy a 16-byte zero constant.
 #include <math.h>
 
 #include "common.h"
 #include "launch.h"
 
+#pragma clang diagnostic ignored "-Winline-asm"
+
 namespace moe {
 namespace {
 
-constexpr int kBK = 64;
-constexpr int kLDK = kBK + 8;  // padded LDS row (bf16): 144 B, conflict-free b128 reads
+constexpr int kBM = kBf16BM;  // rows per M-tile (the tile map's granularity)
+constexpr int kBK = 64;       // K per pipeline step
+constexpr int kRowB = 128;    // bytes per LDS row (kBK bf16)
+constexpr int kStages = 3;    // LDS ring depth
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
 
-template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(256) void ggemm_bf16_kernel(const GemmBf16Args p) {
+__device__ __attribute__((aligned(16))) const uint32_t kZeroChunk[4] = {0u, 0u, 0u, 0u};
+
+// 16-byte global -> LDS copy.  Lane i of the wave writes LDS bytes
+// [lds + 16 i, lds + 16 i + 16); `lds` must be wave-uniform.  The copy has no
+// register result; its completion is tracked with vmcnt (wait_vm).
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off" ::"v"(g),
+      "s"(lds)
+      : "memory");
+}
+
+// Wait until at most N vector memory operations of this wave are in flight.
+// Loads complete in order, so this covers every copy issued more than N
+// loads ago.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ int swz(int r, int c) { return (c ^ ((r >> 1) & 7)) << 4; }
+
+// HAS_BIAS is a template parameter so that the usual bias-free kernels have
+// no global loads in the epilogue (the compiler would otherwise wait there
+// for every copy in flight).
+template <int BN, int EPI, int WGM, bool HAS_BIAS>
+__global__ __launch_bounds__(kThreads) void ggemm_bf16_kernel(const GemmBf16Args p) {
   constexpr int NB = (EPI == EPI_SWIGLU_BF16) ? 2 : 1;  // weight matrices per tile
   constexpr int BROWS = NB * BN;                         // weight rows per tile
-  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int A_BYTES = kBM * kRowB, B_BYTES = BROWS * kRowB;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int ADMA = A_BYTES / 1024 / kWaves, BDMA = B_BYTES / 1024 / kWaves;
+  constexpr int PER_STEP = ADMA + BDMA;  // copies per thread per step
+  constexpr int WGN = kWaves / WGM;
+  constexpr int WM = kBM / WGM, WN = BN / WGN;
   constexpr int FM = WM / 32, FN = WN / 32;
-  constexpr int ACH = BM * kBK / 8 / 256;     // 16-byte chunks per thread
-  constexpr int BCH = BROWS * kBK / 8 / 256;
-  constexpr int STAGE = (BM + BROWS) * kLDK;  // bf16 elements per stage
-  constexpr int LDC = BN + 4;
-  static_assert(BM * LDC * 4 <= 2 * STAGE * 2, "epilogue staging must fit");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+  static_assert(ADMA >= 1 && BDMA >= 1 && FM >= 1 && FN >= 1, "bad tile shape");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * STAGE];
+  __shared__ int4 meta[kMaxTilesPerWG];  // per tile: expert, first row, end row, first column
 
+  // This workgroup's tiles: XCD x owns tiles [x*per, (x+1)*per); its
+  // workgroups take every wpx-th of them.
   const int nN = (p.N + BN - 1) / BN;
-  const int L = xcd_tile(*p.tile_count * nN);
-  if (L < 0) return;
-  const int mt = L / nN, nt = L % nN;
-  const int e = p.tile_expert[mt];
-  const int row0 = p.tile_row0[mt];
-  const int row_end = p.offsets[e + 1];
-  const int n0 = nt * BN;
-  const int K = p.K;
+  const int total = *p.tile_count * nN;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int xcd = (int)(blockIdx.x % kXcds), slot = (int)(blockIdx.x / kXcds);
+  const int wpx = (int)(gridDim.x / kXcds);
+  const int first = xcd * per + slot;
+  const int last = min(total, (xcd + 1) * per);
+  const int ntiles = first < last ? (last - first + wpx - 1) / wpx : 0;
+  if (ntiles == 0) return;
   const int tid = threadIdx.x;
-
-  const uint16_t* asrc[ACH];
-  bool aok[ACH];
-  int aoff[ACH], akc[ACH];
-#pragma unroll
-  for (int i = 0; i < ACH; ++i) {
-    const int c = tid + 256 * i;
-    const int r = c / (kBK / 8), kc = (c % (kBK / 8)) * 8;
-    aoff[i] = r * kLDK + kc;
-    akc[i] = kc;
-    aok[i] = row0 + r < row_end;
-    asrc[i] = p.A + (long long)(aok[i] ? row0 + r : row0) * p.lda + kc;
+  for (int t = tid; t < ntiles; t += kThreads) {
+    const int L = first + t * wpx;
+    const int mt = L / nN, nt = L % nN;
+    const int e = p.tile_expert[mt];
+    meta[t] = make_int4(e, p.tile_row0[mt], p.offsets[e + 1], nt * BN);
   }
-  const uint16_t* bsrc[BCH];
-  bool bok[BCH];
-  int boff[BCH], bkc[BCH];
-#pragma unroll
-  for (int i = 0; i < BCH; ++i) {
-    const int c = tid + 256 * i;
-    const int r = c / (kBK / 8), kc = (c % (kBK / 8)) * 8;
-    const int which = r / BN, rn = r % BN;
-    boff[i] = r * kLDK + kc;
-    bkc[i] = kc;
-    bok[i] = n0 + rn < p.N;
-    const uint16_t* base = (which == 0 ? p.B1 : p.B3) + (long long)e * p.strideB;
-    bsrc[i] = base + (long long)(bok[i] ? n0 + rn : 0) * K + kc;
-  }
+  __syncthreads();
 
-  uint4 ra[ACH], rb[BCH];
-  auto load = [&](int k0) {
+  const int K = p.K;
+  const int nk = (K + kBK - 1) / kBK;
+  const int nsteps = ntiles * nk;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+
+  // Copy step g (tile g / nk, K-step g % nk) into ring slot g % kStages.
+  // Lane covers row (blk*8 + lane/8), chunk (lane%8) swizzled.
+  auto issue = [&](int g) {
+    const int ti = g / nk, kt = g - ti * nk;
+    const int4 m = meta[ti];
+    const int k0 = kt * kBK;
+    const uint32_t sb = lds0 + (g % kStages) * STAGE;
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) {
-      const bool ok = aok[i] && (k0 + akc[i] < K);
-      ra[i] = ok ? *(const uint4*)(asrc[i] + k0) : make_uint4(0u, 0u, 0u, 0u);
+    for (int j = 0; j < ADMA; ++j) {
+      const int blk = wave + kWaves * j;
+      const int r = blk * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      const int gr = min(m.y + r, m.z - 1);
+      const void* src = k0 + c * 8 < K ? (const void*)(p.A + (long long)gr * p.lda + k0 + c * 8)
+                                       : (const void*)kZeroChunk;
+      dma16(src, sb + blk * 1024);
     }
 #pragma unroll
-    for (int i = 0; i < BCH; ++i) {
-      const bool ok = bok[i] && (k0 + bkc[i] < K);
-      rb[i] = ok ? *(const uint4*)(bsrc[i] + k0) : make_uint4(0u, 0u, 0u, 0u);
+    for (int j = 0; j < BDMA; ++j) {
+      const int blk = wave + kWaves * j;
+      const int r = blk * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      const int which = r / BN, rn = r % BN;
+      const int gn = min(m.w + rn, p.N - 1);
+      const uint16_t* w = (which == 0 ? p.B1 : p.B3) + (long long)m.x * p.strideB;
+      const void* src = k0 + c * 8 < K ? (const void*)(w + (long long)gn * K + k0 + c * 8)
+                                       : (const void*)kZeroChunk;
+      dma16(src, sb + A_BYTES + blk * 1024);
     }
   };
-  auto store = [&](int buf) {
-    uint16_t* As = smem + buf * STAGE;
-    uint16_t* Bs = As + BM * kLDK;
-#pragma unroll
-    for (int i = 0; i < ACH; ++i) *(uint4*)(As + aoff[i]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < BCH; ++i) *(uint4*)(Bs + boff[i]) = rb[i];
-  };
 
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   const int lr = lane & 31, lh = lane >> 5;
 
   f32x16 acc[NB][FM][FN];
+  auto zero_acc = [&]() {
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[b][i][j][v] = 0.f;
-
-  const int nk = (K + kBK - 1) / kBK;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load((kt + 1) * kBK);
-    const uint16_t* As = smem + cur * STAGE;
-    const uint16_t* Bs = As + BM * kLDK;
-    // 32x32x16 operand layout: lane supplies row (lane%32), k = 8*(lane/32)..+7.
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      bf16x8 af[FM], bfr[NB][FN];
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        af[i] = *(const bf16x8*)(As + (wm * WM + i * 32 + lr) * kLDK + kk * 16 + lh * 8);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[b][i][j][v] = 0.f;
+  };
+  zero_acc();
+
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s)
+    if (s < nsteps) issue(s);
+
+  for (int g = 0; g < nsteps; ++g) {
+    const int ahead = nsteps - 1 - g;  // steps issued after this one, at most kStages-2
+    static_assert(kStages == 3, "the waits below assume a 3-deep ring");
+    if (ahead >= 1)
+      wait_vm<PER_STEP>();
+    else
+      wait_vm<0>();
+    __syncthreads();
+    const uint8_t* As = smem + (g % kStages) * STAGE;
+    const uint8_t* Bs = As + A_BYTES;
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      const int c = 2 * kk + lh;  // 32x32x16 operand: row lane%32, k = 8*(lane/32)..+7
+      bf16x8 xf[FM], wf[NB][FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = wm * WM + i * 32 + lr;
+        xf[i] = *(const bf16x8*)(As + r * kRowB + swz(r, c));
+      }
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          bfr[b][j] =
-              *(const bf16x8*)(Bs + (b * BN + wn * WN + j * 32 + lr) * kLDK + kk * 16 + lh * 8);
+        for (int j = 0; j < FN; ++j) {
+          const int r = b * BN + wn * WN + j * 32 + lr;
+          wf[b][j] = *(const bf16x8*)(Bs + r * kRowB + swz(r, c));
+        }
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -140,93 +202,86 @@ __global__ __launch_bounds__(256) void ggemm_bf16_kernel(const GemmBf16Args p) {
 #pragma unroll
           for (int j = 0; j < FN; ++j)
             acc[b][i][j] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[b][j], acc[b][i][j], 0, 0, 0);
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[b][j], xf[i], acc[b][i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) store(cur ^ 1);
-    __syncthreads();
-  }
+    if (g + kStages - 1 < nsteps) issue(g + kStages - 1);
 
-  // Stage the (activated) tile as fp32 in LDS: accumulator element v of a
-  // 32x32 block sits at column lane%32, row 8*(v/4) + 4*(lane/32) + v%4.
-  float* Cs = (float*)smem;
+    if (g % nk == nk - 1) {
+      // Tile done.  D[n][m] layout: lane holds column m = lane%32 of each
+      // 32x32 block and rows n = 8*(v/4) + 4*(lane/32) + v%4.
+      const int4 m = meta[g / nk];
+      const int e = m.x, row_end = m.z;
+      const float* bias = HAS_BIAS ? p.bias + (long long)e * p.N : nullptr;
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM; ++i) {
+        const int gr = m.y + wm * WM + i * 32 + lr;
+        if (gr >= row_end) continue;
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+        for (int j = 0; j < FN; ++j) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = wm * WM + i * 32 + (v >> 2) * 8 + lh * 4 + (v & 3);
-        const int c = wn * WN + j * 32 + lr;
-        float val;
-        if constexpr (EPI == EPI_SWIGLU_BF16) {
-          const float gv = acc[0][i][j][v], uv = acc[NB - 1][i][j][v];
-          val = gv / (1.f + expf(-gv)) * uv;
-        } else {
-          val = acc[0][i][j][v];
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int gc = m.w + wn * WN + j * 32 + q4 * 8 + lh * 4;
+            if (gc >= p.N) continue;
+            float f[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              if constexpr (EPI == EPI_SWIGLU_BF16) {
+                const float gv = acc[0][i][j][4 * q4 + q], uv = acc[NB - 1][i][j][4 * q4 + q];
+                f[q] = gv / (1.f + expf(-gv)) * uv;
+              } else {
+                f[q] = acc[0][i][j][4 * q4 + q];
+                if constexpr (HAS_BIAS) f[q] += bias[gc + q];
+                if constexpr (EPI == EPI_RELU_BF16) f[q] = fmaxf(f[q], 0.f);
+              }
+            }
+            if constexpr (EPI == EPI_IDENT_F32) {
+              *(f32x4*)((float*)p.C + (long long)gr * p.ldc + gc) = f32x4{f[0], f[1], f[2], f[3]};
+            } else {
+              uint2 pk;
+              pk.x = (uint32_t)f32_to_bf16(f[0]) | ((uint32_t)f32_to_bf16(f[1]) << 16);
+              pk.y = (uint32_t)f32_to_bf16(f[2]) | ((uint32_t)f32_to_bf16(f[3]) << 16);
+              *(uint2*)((uint16_t*)p.C + (long long)gr * p.ldc + gc) = pk;
+            }
+          }
         }
-        Cs[r * LDC + c] = val;
       }
-  __syncthreads();
-
-  const float* bias = p.bias ? p.bias + (long long)e * p.N : nullptr;
-  if constexpr (EPI == EPI_IDENT_F32) {
-    for (int c = tid; c < BM * BN / 4; c += 256) {
-      const int r = c / (BN / 4), cc = (c % (BN / 4)) * 4;
-      const int gr = row0 + r, gc = n0 + cc;
-      if (gr >= row_end || gc >= p.N) continue;
-      f32x4 v = *(const f32x4*)(Cs + r * LDC + cc);
-      if (bias) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] += bias[gc + q];
-      }
-      *(f32x4*)((float*)p.C + (long long)gr * p.ldc + gc) = v;
-    }
-  } else {
-    for (int c = tid; c < BM * BN / 8; c += 256) {
-      const int r = c / (BN / 8), cc = (c % (BN / 8)) * 8;
-      const int gr = row0 + r, gc = n0 + cc;
-      if (gr >= row_end || gc >= p.N) continue;
-      const f32x4 v0 = *(const f32x4*)(Cs + r * LDC + cc);
-      const f32x4 v1 = *(const f32x4*)(Cs + r * LDC + cc + 4);
-      float f[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-      if constexpr (EPI == EPI_RELU_BF16) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) f[q] = fmaxf(f[q] + (bias ? bias[gc + q] : 0.f), 0.f);
-      }
-      uint4 pk;
-      pk.x = (uint32_t)f32_to_bf16(f[0]) | ((uint32_t)f32_to_bf16(f[1]) << 16);
-      pk.y = (uint32_t)f32_to_bf16(f[2]) | ((uint32_t)f32_to_bf16(f[3]) << 16);
-      pk.z = (uint32_t)f32_to_bf16(f[4]) | ((uint32_t)f32_to_bf16(f[5]) << 16);
-      pk.w = (uint32_t)f32_to_bf16(f[6]) | ((uint32_t)f32_to_bf16(f[7]) << 16);
-      *(uint4*)((uint16_t*)p.C + (long long)gr * p.ldc + gc) = pk;
+      zero_acc();
     }
   }
 }
 
-template <int BM, int BN, int EPI>
+template <int BN, int EPI, int WGM, bool HAS_BIAS>
 hipError_t launch_t(const GemmBf16Args& a, hipStream_t s) {
   const int nN = (a.N + BN - 1) / BN;
   const long long max_total = (long long)a.max_mtiles * nN;
   if (max_total <= 0) return hipSuccess;
-  const long long grid = (max_total + kXcds - 1) / kXcds * kXcds;
+  // One workgroup per CU, a multiple of the XCD count, and enough of them
+  // that no workgroup holds more than kMaxTilesPerWG tiles.
+  long long grid = (long long)a.num_cus / kXcds * kXcds;
+  if (grid < kXcds) grid = kXcds;
+  const long long per = (max_total + kXcds - 1) / kXcds;
+  while ((per + grid / kXcds - 1) / (grid / kXcds) > kMaxTilesPerWG) grid += kXcds;
   ProfScope ps(EPI == EPI_RELU_BF16     ? "ggemm_bf16_relu"
                : EPI == EPI_SWIGLU_BF16 ? "ggemm_bf16_swiglu"
                                         : "ggemm_bf16_out",
                s);
-  ggemm_bf16_kernel<BM, BN, EPI><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
+  ggemm_bf16_kernel<BN, EPI, WGM, HAS_BIAS><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm_bf16(const GemmBf16Args& a, int epi, hipStream_t s) {
+  const bool bias = a.bias != nullptr;
   switch (epi) {
     case EPI_RELU_BF16:
-      return launch_t<kBf16BM, 128, EPI_RELU_BF16>(a, s);
+      return bias ? launch_t<256, EPI_RELU_BF16, 2, true>(a, s)
+                  : launch_t<256, EPI_RELU_BF16, 2, false>(a, s);
     case EPI_SWIGLU_BF16:
-      return launch_t<kBf16BM, 64, EPI_SWIGLU_BF16>(a, s);
+      return launch_t<128, EPI_SWIGLU_BF16, 2, false>(a, s);
     default:
-      return launch_t<kBf16BM, 128, EPI_IDENT_F32>(a, s);
+      return bias ? launch_t<256, EPI_IDENT_F32, 2, true>(a, s)
+                  : launch_t<256, EPI_IDENT_F32, 2, false>(a, s);
   }
 }
 

@@ -69,8 +69,13 @@ struct GemmBf16Args {
   const int32_t* offsets;
   const int32_t* tile_count;
   int max_mtiles;
+  int num_cus;           // compute units of the device (persistent grid size)
 };
 constexpr int kBf16BM = 128;
+constexpr int kMaxTilesPerWG = 512;  // tiles one persistent workgroup can hold
+
+// Compute units of the current device (queried once per device).
+int device_cus();
 hipError_t launch_gemm_bf16(const GemmBf16Args& a, int epi, hipStream_t s);
 
 // Tile map of a grouped GEMM: for every expert e with rows in
@@ -111,9 +116,13 @@ struct TopkArgs {
   int max_tiles;
   int tile_rows;
 };
+constexpr int kTopkWaves = 8;  // wavefronts (rows in flight) per gate-epilogue block
+constexpr int kTopkThreads = kTopkWaves * 64;
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
-// out[j] = sum over parts p < nparts (ascending) of part[p*n + j]  (double sum)
-hipError_t launch_colsum(const float* part, int nparts, int n, float* out, hipStream_t s);
+// out[j] = sum over parts p < nparts of part[p*n + j] (double sum, fixed
+// order); likewise out2 from part2 when part2 is not null (same launch).
+hipError_t launch_colsum(const float* part, int nparts, int n, float* out, const float* part2,
+                         float* out2, hipStream_t s);
 // Two-level aux vectors: per-tile partials of the secondary gate are summed
 // per group (tiles of a group are consecutive), then combined with the
 // primary vectors: load[g*b+e] = load_p[g]*load_g[e]/|X_g|.
@@ -125,14 +134,35 @@ hipError_t launch_hier_finalize(const float* part_imp, const float* part_load,
 // ---------------------------------------------------------------------------
 // Dispatch.
 // ---------------------------------------------------------------------------
-constexpr int kDispatchChunk = 1024;  // assignments per chunk
-hipError_t launch_dispatch(const int32_t* topk_idx, int T, int k, int n, long long cap,
-                           int32_t* counts_pre, int32_t* counts, int32_t* offsets,
-                           int32_t* perm, int32_t* slot_pos, int32_t* chunk_hist,
-                           int32_t* chunk_base, hipStream_t s);
-// x_perm[r] = convert(x[perm[r]]) for r < offsets[n].
-hipError_t launch_gather(const float* x, const int32_t* perm, const int32_t* rows_dev,
-                         int max_rows, int d, int bf16_out, void* x_perm, hipStream_t s);
+constexpr int kDispatchChunk = 256;  // assignments per chunk (one wavefront each in the permute)
+struct DispatchArgs {
+  const int32_t* topk_idx;
+  int T, k, n;
+  long long cap;
+  int32_t* counts_pre;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* slot_pos;
+  int32_t* chunk_hist;
+  int32_t* chunk_base;
+  // Optional: the grouped GEMM's tile map for tile_bm-row M-tiles (0 = none).
+  int tile_bm;
+  int32_t* tile_expert;
+  int32_t* tile_row0;
+  int32_t* tile_count;
+  // Optional: auxiliary losses from importance / load (load may be null) and
+  // the pre-capacity counts (losses == null: none).
+  float* losses;
+  const float* importance;
+  const float* load;
+  float w_imp, w_load, alpha;
+};
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
+// Scatter each token's row to its kept slots: x_perm[slot_pos[t, s]] =
+// convert(x[t]) (bf16 round to nearest even, or an fp32 copy).
+hipError_t launch_gather(const float* x, const int32_t* slot_pos, int T, int k, int d,
+                         int bf16_out, void* x_perm, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Combine and aux.

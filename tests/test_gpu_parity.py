@@ -279,3 +279,36 @@ def test_stage_dispatch_and_ffn(cf):
 def ew_stack(ew, name):
     d = ew[name]
     return np.stack([d[e] for e in sorted(d)])
+
+
+def test_graph_replay_matches_eager():
+    # The forward captured into a HIP graph: every replay (with eager work and
+    # synchronisations in between) must equal the eager result bit for bit.
+    cfg = PRESETS["lm_layer"].replace(T=1024)
+    inp = dev_inputs(cfg, T=1024)
+    layer = moe.MoELayer(cfg, inp)
+    log("[parity] graph replay lm_layer T=1024")
+    y_ref, l_ref = layer.forward(inp["x"], inp["noise"])
+    torch.cuda.synchronize()
+    y_ref, l_ref = y_ref.clone(), l_ref.clone()
+    y = torch.empty_like(y_ref)
+    losses = torch.empty_like(l_ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer.forward(inp["x"], inp["noise"], y=y, losses=losses)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward(inp["x"], inp["noise"], y=y, losses=losses)
+    for rep in range(4):
+        y.fill_(float("nan"))
+        losses.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), f"replay {rep}"
+        assert torch.equal(losses, l_ref), f"replay {rep}"
+        # eager work between replays, on the same buffers of another layer call
+        y2, _ = layer.forward(inp["x"], inp["noise"])
+        torch.cuda.synchronize()
+        assert torch.equal(y2, y_ref)
