@@ -143,3 +143,91 @@ def _stack(dct):
 
 def y_tolerance(cfg):
     return TOL_BF16 if cfg.expert_dtype == DTYPE_BF16 else TOL_F32
+
+
+def oracle_gate_any(cfg, h):
+    """Oracle gating of a flat or two-level config on host inputs `h`.
+    Returns (topk_idx, topk_w, importance, load, H_for_ties, near_tie)."""
+    if cfg.hierarchical:
+        gh = oracle.gate_hier(h["x"], h["w_gate"], h.get("w_noise"), h.get("noise"),
+                              cfg.k_groups, h["w_gate2"], h.get("w_noise2"), h.get("noise2"),
+                              cfg.k2, b_gate=h.get("b_gate"))
+        return gh["topk_idx"], gh["topk_w"], gh["importance"], gh["load"], None, gh["near_tie"]
+    g = oracle.gate(h["x"], h["w_gate"], cfg.k, h.get("b_gate"), h.get("w_noise"),
+                    h.get("noise"), cfg.gate)
+    return g.topk_idx, g.topk_w, g.importance, g.load, g.H, g.near_tie
+
+
+def check_routing_any(cfg, gpu_idx, orc_idx, H, near_tie):
+    """Routing check for flat (sorted-gap rule on H) or two-level configs
+    (the oracle's per-level near-tie flags)."""
+    if H is not None:
+        return routing_mismatches(gpu_idx, orc_idx, H, cfg.k)
+    bad = np.nonzero(np.any(gpu_idx != orc_idx, axis=1))[0]
+    for t in bad:
+        assert near_tie[t], f"token {t} routes differently without a near-tie"
+    assert len(bad) <= MISMATCH_BUDGET * gpu_idx.shape[0]
+    return bad
+
+
+def sampled_y_reference(cfg, inp, x64, idx, w, slot_pos, tokens):
+    """y rows of `tokens` from the oracle's expert FFNs, given a routing
+    (idx, w, slot_pos); only the experts these tokens use are copied."""
+    experts = sorted({int(idx[t, s]) for t in tokens for s in range(idx.shape[1])
+                      if slot_pos[t, s] >= 0})
+    bf = cfg.expert_dtype == DTYPE_BF16
+
+    def host32(name, e):
+        t = inp.get(name)
+        return None if t is None else t[e].detach().float().cpu().numpy()
+
+    ys = np.zeros((len(tokens), cfg.d_model))
+    for e in experts:
+        w1, w2, w3 = host32("w1", e), host32("w2", e), host32("w3", e)
+        b1, b2 = host32("b1", e), host32("b2", e)
+        for r, t in enumerate(tokens):
+            for s in range(idx.shape[1]):
+                if int(idx[t, s]) != e or slot_pos[t, s] < 0:
+                    continue
+                out = oracle.expert_ffn(x64[t:t + 1], w1, w2, b1=b1, w3=w3, b2=b2,
+                                        act=cfg.act, bf16=bf)
+                ys[r] += w[t, s] * out[0]
+    return ys
+
+
+def full_size_sampled(cfg, n_sample=48, seed=0):
+    """Full-size forward of `cfg`: routing for every token against the
+    oracle gate, dispatch bit-exact, aux losses, and y on sampled tokens."""
+    log(f"[full-size] {cfg.name} T={cfg.T} d={cfg.d_model} h={cfg.d_hidden} "
+        f"n={cfg.n_experts} k={cfg.k}")
+    inp = dev_inputs(cfg)
+    gpu = gpu_forward(cfg, inp)
+    h = host(inp)
+    oidx, ow, oimp, oload, H, near = oracle_gate_any(cfg, h)
+    bad = check_routing_any(cfg, gpu["topk_idx"], oidx, H, near)
+    ok = np.setdiff1d(np.arange(cfg.T), bad)
+    np.testing.assert_allclose(gpu["topk_w"][ok], ow[ok], rtol=TOL_W_REL, atol=TOL_W)
+    d = check_dispatch_exact(cfg, gpu, cfg.T)
+    if len(bad) == 0:
+        assert_close_rel(gpu["importance"], oimp, 1e-5, 1e-5, "importance")
+        if oload is not None:
+            assert_close_rel(gpu["load"], oload, 1e-5, 1e-5, "load")
+        losses = oracle.aux(cfg.T, cfg.k, oimp, oload, d["counts_pre"], cfg.w_importance,
+                            cfg.w_load, cfg.alpha_switch)
+        assert_close_rel(gpu["losses"], losses, TOL_AUX, 1e-7, "losses")
+    # sampled outputs: ends of the batch, random tokens, and tokens routed to
+    # the most loaded expert
+    r = np.random.default_rng(seed)
+    hot = int(np.argmax(d["counts"]))
+    hot_tokens = np.nonzero(np.any(gpu["topk_idx"] == hot, axis=1))[0][:4]
+    pool = np.setdiff1d(ok, np.concatenate([[0, 1, cfg.T - 2, cfg.T - 1], hot_tokens]))
+    tokens = np.unique(np.concatenate([
+        [0, 1, cfg.T - 2, cfg.T - 1], hot_tokens,
+        r.choice(pool, size=min(len(pool), max(0, n_sample - 8)), replace=False)]))
+    tokens = np.intersect1d(tokens, ok)
+    ys = sampled_y_reference(cfg, inp, h["x"], gpu["topk_idx"], ow, gpu["slot_pos"], tokens)
+    err = max_abs_norm(gpu["y"][tokens], ys)
+    log(f"  routing mismatches {len(bad)}, kept rows {d['rows']}, sampled tokens {len(tokens)}, "
+        f"y error {err:.3e}")
+    assert err <= y_tolerance(cfg)
+    return gpu

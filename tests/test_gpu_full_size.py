@@ -1,0 +1,92 @@
+"""Every workload preset at its full size on the GPU (through the C ABI),
+checked against the oracle: routing of every token (bit-exact up to near
+ties), dispatch bit-exact, importance / load / losses, and y on sampled
+tokens (the oracle recomputes those rows expert by expert)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparsely_gated_mixture_amd as moe
+from sparsely_gated_mixture_amd.workloads import PRESETS, MoEConfig, make_inputs
+from _support import (TOL_AUX, assert_close_rel, check_dispatch_exact, dev_inputs,
+                      expert_weights_host, full_size_sampled, gpu_forward, host, log,
+                      max_abs_norm, oracle_gate_any, y_tolerance)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["lm_layer", "switch_cf", "hierarchical", "fine_swiglu"])
+def test_full_size(name):
+    cfg = PRESETS[name]
+    n_sample = 6 if name == "fine_swiglu" else 48
+    gpu = full_size_sampled(cfg, n_sample=n_sample)
+    if name == "switch_cf":
+        C = int(np.floor(cfg.capacity_factor * cfg.T * cfg.k / cfg.n_experts))
+        assert np.all(gpu["counts"] <= C)
+        dropped = np.mean(gpu["slot_pos"] < 0)
+        log(f"  dropped fraction {dropped:.3f}")
+        assert dropped > 0.1
+
+
+def test_hierarchical_element_wise():
+    # Two-level layer (a = b = 64 groups/experts, top-2 at each level) on 192
+    # tokens, every output element against the oracle's two-level forward.
+    cfg = PRESETS["hierarchical"]
+    T = 192
+    c = cfg.replace(T=T)
+    log(f"[parity] hierarchical T={T}")
+    inp = dev_inputs(c, T)
+    gpu = gpu_forward(c, inp)
+    h = host(inp)
+
+    class Lazy:
+        """Expert weights fetched from the device one expert at a time."""
+
+        def __init__(self, t):
+            self.t = t
+
+        def __getitem__(self, e):
+            return self.t[e].float().cpu().numpy()
+
+    ref = oracle.forward_hier(h["x"], h["w_gate"], h["w_noise"], h["noise"], cfg.k_groups,
+                              h["w_gate2"], h["w_noise2"], h["noise2"], cfg.k2, Lazy(inp["w1"]),
+                              Lazy(inp["w2"]), bf16=True, w_importance=cfg.w_importance,
+                              w_load=cfg.w_load, alpha=cfg.alpha_switch)
+    gh = ref["gate"]
+    bad = np.nonzero(np.any(gpu["topk_idx"] != gh["topk_idx"], axis=1))[0]
+    assert all(gh["near_tie"][t] for t in bad) and len(bad) == 0
+    np.testing.assert_allclose(gpu["topk_w"], gh["topk_w"], rtol=1e-4, atol=1e-6)
+    check_dispatch_exact(c, gpu, T)
+    assert max_abs_norm(gpu["y"], ref["y"]) <= y_tolerance(c)
+    assert_close_rel(gpu["importance"], gh["importance"], 1e-5, 1e-5, "importance")
+    assert_close_rel(gpu["load"], gh["load"], 1e-5, 1e-5, "load")
+    assert_close_rel(gpu["losses"], ref["losses"], TOL_AUX, 1e-7, "losses")
+
+
+def test_stage_gate_hier():
+    cfg = PRESETS["hierarchical"]
+    T = 2048
+    c = cfg.replace(T=T)
+    log(f"[stage gate_hier] T={T}")
+    small = c.replace(d_hidden=8)  # same gate seeds, tiny experts
+    inp = make_inputs(small, device="cuda", T=T)
+    n, k = c.n_experts, c.k
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    imp = torch.empty(n, dtype=torch.float32, device="cuda")
+    ld = torch.empty(n, dtype=torch.float32, device="cuda")
+    ws = torch.empty(moe.moe_workspace_size(c), dtype=torch.uint8, device="cuda")
+    moe.moe_gate_hier(c, inp["x"], inp["w_gate"], inp["b_gate"], inp["w_noise"], inp["noise"],
+                      inp["w_gate2"], inp["w_noise2"], inp["noise2"], idx, w, imp, ld, ws)
+    torch.cuda.synchronize()
+    h = host(inp)
+    oidx, ow, oimp, oload, _, near = oracle_gate_any(c, h)
+    gi = idx.cpu().numpy()
+    bad = np.nonzero(np.any(gi != oidx, axis=1))[0]
+    assert all(near[t] for t in bad) and len(bad) <= 1e-4 * T
+    ok = np.setdiff1d(np.arange(T), bad)
+    np.testing.assert_allclose(w.cpu().numpy()[ok], ow[ok], rtol=1e-4, atol=1e-6)
+    if len(bad) == 0:
+        assert_close_rel(imp.cpu().numpy(), oimp, 1e-5, 1e-5, "importance")
+        assert_close_rel(ld.cpu().numpy(), oload, 1e-5, 1e-5, "load")
