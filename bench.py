@@ -11,11 +11,13 @@ HBM.  Prints one JSON line:
                synchronised loop);
   roofline     the dominant kernel's algorithmic bytes (or flops) per launch
                over its average duration, measured with HIP events recorded
-               on the library's stream (moe_profile_*), against the MI355X
+               on the library's stream (moe_profile_*) around every launch of
+               the timed eager steps, against the MI355X
                peak (HBM 8 TB/s, bf16 MFMA 2.5 PFLOP/s, fp32 157.3 TFLOP/s);
   kernels      the same figures for every kernel of the step;
   cpu_baseline the CPU oracle timed on a bounded sample of the same workload
-               (its first tokens) on this host's cores;
+               (its first tokens, run repeatedly for about --cpu-seconds) on
+               this host's cores;
   check        the GPU output on that sample against the oracle.
 """
 from __future__ import annotations
@@ -35,10 +37,14 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer fwd tokens/sec at 1 GPU; expert-GEMM % MFMA peak; routing % HBM BW"
 PEAK_HBM_GBS = 8000.0
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
-# rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE of the dominant kernel, per launch
-# (KiB, scaled by the copy-kernel calibration); null until measured for the
-# current kernel.
-TRAFFIC_BYTES = None
+# HBM bytes per launch of a kernel at a workload: rocprofv3 --pmc FETCH_SIZE
+# and WRITE_SIZE (separate runs, KiB per dispatch), each scaled by what the
+# same counter reads for a plain copy of known size (FETCH_SIZE x 2.0,
+# WRITE_SIZE x 1.0).  An entry is removed whenever its kernel changes; a
+# missing entry reports null.
+TRAFFIC_BYTES = {
+    ("lm_layer", "ggemm_bf16_out"): 414722669,
+}
 
 
 def log(*a):
@@ -95,7 +101,7 @@ def roofline_entry(bytes_, flops, dtype, avg_s):
                 frac=gbs / PEAK_HBM_GBS), gbs, tfs
 
 
-def cpu_baseline(cfg, inp, y_gpu, idx_gpu, sample_tokens):
+def cpu_baseline(cfg, inp, y_gpu, idx_gpu, sample_tokens, seconds):
     """Time the CPU oracle on the first `sample_tokens` tokens (their gate,
     dispatch, experts, combine and losses) and check the GPU output there."""
     import oracle
@@ -108,23 +114,45 @@ def cpu_baseline(cfg, inp, y_gpu, idx_gpu, sample_tokens):
     w2 = to_numpy64(inp["w2"])
     w3 = to_numpy64(inp["w3"]) if inp.get("w3") is not None else None
     oracle.lib()
-    t0 = time.perf_counter()
-    ref = oracle.forward(x, g["w_gate"], cfg.k, w1, w2, b_gate=g["b_gate"], w_noise=g["w_noise"],
-                         noise=noise, w3=w3, mode=cfg.gate, act=cfg.act,
-                         bf16=cfg.expert_dtype == 1, capacity_factor=cfg.capacity_factor,
-                         w_importance=cfg.w_importance, w_load=cfg.w_load,
-                         alpha=cfg.alpha_switch)
-    dt = time.perf_counter() - t0
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    # The same sample is run back to back until about `seconds` of wall time
+    # have passed, so that the rate is not a one-second figure.
+    reps, dt = 0, 0.0
+    while reps == 0 or dt < seconds:
+        t0 = time.perf_counter()
+        ref = oracle.forward(x, g["w_gate"], cfg.k, w1, w2, b_gate=g["b_gate"],
+                             w_noise=g["w_noise"], noise=noise, w3=w3, mode=cfg.gate,
+                             act=cfg.act, bf16=cfg.expert_dtype == 1,
+                             capacity_factor=cfg.capacity_factor,
+                             w_importance=cfg.w_importance, w_load=cfg.w_load,
+                             alpha=cfg.alpha_switch)
+        dt += time.perf_counter() - t0
+        reps += 1
+    cores = oracle.num_threads()
     same = np.all(idx_gpu[:S] == ref["gate"].topk_idx, axis=1)
     scale = np.max(np.abs(ref["y"][same])) if same.any() else 1.0
     err = float(np.max(np.abs(y_gpu[:S][same] - ref["y"][same])) / scale) if same.any() else None
-    base = {"value": S / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    base = {"value": S * reps / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"first {S} of {cfg.T} tokens of the {cfg.name} workload "
-                      f"(gate, dispatch, experts, combine, losses in float64); {dt:.2f} s"}
+                      f"(gate, dispatch, experts, combine, losses in float64), "
+                      f"{reps} runs in {dt:.2f} s"}
     check = {"tokens": S, "routing_match": float(same.mean()), "y_max_abs_norm_err": err,
              "tolerance": 2e-2 if cfg.expert_dtype == 1 else 1e-4}
     return base, check
+
+
+def calibrate_copy():
+    """A plain elementwise device copy (y = -x, fp32) of 256 MiB, five
+    launches: the reference kernel against which the rocprofv3 FETCH_SIZE /
+    WRITE_SIZE readings of the layer's kernels are scaled."""
+    n = 64 << 20
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "neg copy", "read_bytes": n * 4, "write_bytes": n * 4,
+                      "launches": 5}), flush=True)
 
 
 def main():
@@ -133,12 +161,19 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="lm_layer")
-    ap.add_argument("--profile-steps", type=int, default=20)
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="run the oracle sample repeatedly for about this long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches only (default: also replay a HIP graph)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of known size (256 MiB read, "
+                         "256 MiB written, 5 launches) for scaling HBM byte counters")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the layer is built and "
               "measured on a single MI355X, with no collectives.", file=sys.stderr)
@@ -177,9 +212,30 @@ def main():
     def eager_step():
         layer.forward(inp["x"], inp.get("noise"), inp.get("noise2"), y=y, losses=losses)
 
+    # Fill the library's event pool with one untimed profiled pass, so that
+    # the timed pass below creates no events.
+    moe.moe_profile_enable(True)
+    for _ in range(args.steps):
+        eager_step()
+    torch.cuda.synchronize()
+    moe.moe_profile_enable(False)
+    moe.moe_profile_collect()
+
+    # Timed region 1: eager launches, nothing else on the stream.
     eager_elapsed = timed(eager_step)
     log(f"[bench] eager: {eager_elapsed / args.steps * 1e6:.1f} us/step, "
         f"{T * args.steps / eager_elapsed / 1e6:.2f} M tokens/s")
+
+    # Timed region 2: the same K eager steps with every kernel bracketed by
+    # two HIP events recorded on the library's stream; the per-kernel
+    # durations (and the roofline) come from these steps.  The events add a
+    # few microseconds between launches, so this region does not set `value`.
+    moe.moe_profile_enable(True)
+    prof_elapsed = timed(eager_step)
+    moe.moe_profile_enable(False)
+    nk = moe.moe_profile_collect()
+    stats = [moe.moe_profile_entry(i) for i in range(nk)]
+    log(f"[bench] eager with per-kernel events: {prof_elapsed / args.steps * 1e6:.1f} us/step")
     mode, elapsed = "eager launches", eager_elapsed
     graph = None
     if not args.eager:
@@ -203,15 +259,6 @@ def main():
     ms_per_step = elapsed / args.steps * 1e3
     tokens_per_s = T * args.steps / elapsed
 
-    # Per-kernel durations: HIP events recorded by the library on its stream.
-    moe.moe_profile_enable(True)
-    for _ in range(args.profile_steps):
-        layer.forward(inp["x"], inp.get("noise"), inp.get("noise2"), y=y, losses=losses)
-    torch.cuda.synchronize()
-    moe.moe_profile_enable(False)
-    nk = moe.moe_profile_collect()
-    stats = [moe.moe_profile_entry(i) for i in range(nk)]
-
     # Realised routing of this batch (identical every step).
     layer.forward(inp["x"], inp.get("noise"), inp.get("noise2"), y=y, losses=losses, diag=diag)
     torch.cuda.synchronize()
@@ -224,7 +271,7 @@ def main():
     for name, total_ms, launches in stats:
         avg_s = total_ms / launches / 1e3
         b, f, dt = kernel_work(name, cfg, rows, nonempty, T)
-        entry = {"avg_us": avg_s * 1e6, "launches_per_step": launches / args.profile_steps}
+        entry = {"avg_us": avg_s * 1e6, "launches_per_step": launches / args.steps}
         if b:
             rl, gbs, tfs = roofline_entry(b, f, dt, avg_s)
             entry.update({"algo_bytes": b, "GB_s": gbs, "hbm_frac": gbs / PEAK_HBM_GBS})
@@ -242,7 +289,7 @@ def main():
     dk = kernels[dname]
     roofline = dict(dk["roofline"])
     roofline["kernel"] = dname
-    roofline["traffic"] = TRAFFIC_BYTES
+    roofline["traffic"] = TRAFFIC_BYTES.get((cfg.name, dname))
     roofline["algo_bytes_per_launch"] = dk["algo_bytes"]
     roofline["avg_us"] = dk["avg_us"]
 
@@ -260,13 +307,14 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "timing": {"mode": mode, "eager_us_per_step": eager_elapsed / args.steps * 1e6,
+                   "eager_with_events_us_per_step": prof_elapsed / args.steps * 1e6,
                    "graph_us_per_step": (graph_elapsed / args.steps * 1e6) if graph else None},
     }
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle on the first {args.cpu_sample_tokens} tokens")
         yh = y.cpu().double().numpy()
         ih = diag["topk_idx"].cpu().numpy()
-        base, check = cpu_baseline(cfg, inp, yh, ih, args.cpu_sample_tokens)
+        base, check = cpu_baseline(cfg, inp, yh, ih, args.cpu_sample_tokens, args.cpu_seconds)
         result["cpu_baseline"] = base
         result["check"] = check
     else:

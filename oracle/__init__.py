@@ -66,6 +66,11 @@ def _opt(ptr_type):
     return _Opt
 
 
+def num_threads() -> int:
+    """Threads the oracle's OpenMP loops run on."""
+    return int(lib().oracle_num_threads())
+
+
 def lib():
     global _lib
     if _lib is None:
@@ -74,6 +79,8 @@ def lib():
         L = ctypes.CDLL(_LIB_PATH)
         c_int, c_dbl, c_i64 = ctypes.c_int, ctypes.c_double, ctypes.c_int64
         odp, oip = _opt(_dp), _opt(_ip)
+        L.oracle_num_threads.argtypes = []
+        L.oracle_num_threads.restype = c_int
         L.oracle_softplus.argtypes = [c_dbl]
         L.oracle_softplus.restype = c_dbl
         L.oracle_phi.argtypes = [c_dbl]

@@ -38,6 +38,7 @@
  *     (round to nearest, ties to even) before each product; sums in double.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -46,6 +47,9 @@
 #define ORACLE_GATE_SWITCH_TOP1 1
 #define ORACLE_ACT_RELU 0
 #define ORACLE_ACT_SWIGLU 1
+
+/* Threads the OpenMP loops below use (for reporting the baseline's cores). */
+int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------------------ */
 /* Scalar helpers                                                            */
