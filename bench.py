@@ -78,7 +78,8 @@ def kernel_work(name, cfg, rows, nonempty, T):
         return (T * k * 4 * 2 + rows * 4, 0.0, "i32")
     if name == "dispatch_hist":
         return (T * k * 4 + ((T * k + 255) // 256) * n * 4, 0.0, "i32")
-    rpb = max(16, -(-((T + 255) // 256) // 8) * 8)
+    w = 16 if (cfg.n_groups or n) <= 512 else 8
+    rpb = max(2 * w, -(-((T + 255) // 256) // w) * w)
     nparts = (T + rpb - 1) // rpb
     if name == "gate_colsum":
         return (nparts * n * 4 + n * 4, 0.0, "f32")

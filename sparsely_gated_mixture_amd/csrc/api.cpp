@@ -189,7 +189,8 @@ Plan make_plan(const moe_config& c) {
   {
     // one partial vector per block; at most 256 blocks (one per CU) once T
     // is large, so the column sums stay short
-    long long rpb = std::max(16LL, round_up((T + 255) / 256, kTopkWaves));
+    const long long w = topk_waves(p.n_gate);
+    long long rpb = std::max(2 * w, round_up((T + 255) / 256, w));
     p.rows_per_block = (int)rpb;
     p.nparts = (int)((T + rpb - 1) / rpb);
   }

@@ -1,6 +1,7 @@
-// Gating network epilogue on gfx950: one wavefront per token row, eight
-// wavefronts per block, each prefetching its next row while it works on the
-// current one.
+// Gating network epilogue on gfx950: one wavefront per token row, 16 (large
+// n: 8) wavefronts per block, each prefetching its next row while it works on
+// the current one, so every row of a block is in flight at once for the usual
+// row counts.
 //
 // Reads the fp32 logits written by the gate GEMM and computes, per row,
 //   H_j = clean_j (+ bias_j) + z_j * Softplus(raw_j)      (noisy gate)
@@ -26,8 +27,27 @@
 namespace moe {
 namespace {
 
+// Softplus(z) = max(z, 0) + log1p(e), e = exp(-|z|) in (0, 1].  e comes
+// from the hardware exp2 and log1p(e) from Goldberg's correction: with
+// u = 1 + e rounded, log1p(e) = log(u) * e / (u - 1), within a few ulps when
+// log is (D. Goldberg, "What every computer scientist should know about
+// floating-point arithmetic", 1991, Theorem 4), and e itself when u rounds
+// to 1.  About a tenth of the instructions of log1pf(expf(.)).
+// v_exp_f32 / v_log_f32 / v_rcp_f32 (base-2 exponential and logarithm and
+// the reciprocal, each within about 1 ulp).
+__device__ __forceinline__ float hw_exp(float x) {
+  return __builtin_amdgcn_exp2f(x * 1.44269504088896341f);
+}
+__device__ __forceinline__ float hw_log(float x) {
+  return __builtin_amdgcn_logf(x) * 0.693147180559945309f;
+}
+__device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
 __device__ __forceinline__ float softplus_f(float z) {
-  return fmaxf(z, 0.f) + log1pf(expf(-fabsf(z)));
+  const float e = hw_exp(-fabsf(z));
+  const float u = 1.f + e;
+  const float l = u == 1.f ? e : hw_log(u) * (e * hw_rcp(u - 1.f));
+  return fmaxf(z, 0.f) + l;
 }
 
 __device__ __forceinline__ int readlane_i(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
@@ -43,9 +63,9 @@ struct RowIn {
   float z[NPL];  // standard normal draw (noisy gate only)
 };
 
-template <int NPL>
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs p) {
-  extern __shared__ float red[];  // [kTopkWaves][n]
+template <int NPL, int NW>
+__global__ __launch_bounds__(NW * 64) void topk_kernel(const TopkArgs p) {
+  extern __shared__ float red[];  // [NW][n]
   const int n = p.n, k = p.k;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
@@ -106,8 +126,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs p) {
   RowIn<NPL> cur, nxt;
   int r = row_begin + wave;
   if (r < row_end) fetch(r, cur);
-  for (; r < row_end; r += kTopkWaves) {
-    if (r + kTopkWaves < row_end) fetch(r + kTopkWaves, nxt);  // next row in flight
+  for (; r < row_end; r += NW) {
+    if (r + NW < row_end) fetch(r + NW, nxt);  // next row in flight
     long long noise_row, out_base;
     float wprim;
     locate(r, noise_row, out_base, wprim);
@@ -206,7 +226,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs p) {
       for (int q = 0; q < NPL; ++q) {
         if (lane + 64 * q < n) {
           const float thr = ((selmask >> q) & 1u) ? v_k : v_km1;
-          const float zz = (cl[q] - thr) / sp[q];
+          const float zz = (cl[q] - thr) * hw_rcp(sp[q]);
           ld[q] += 0.5f * erfcf(-zz * 0.70710678118654752f);
         }
       }
@@ -224,9 +244,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const TopkArgs p) {
       if (j < n) red[wave * n + j] = pass == 0 ? imp[q] : ld[q];
     }
     __syncthreads();
-    for (int j = threadIdx.x; j < n; j += kTopkThreads) {
+    for (int j = threadIdx.x; j < n; j += NW * 64) {
       float sacc = red[j];
-      for (int w2 = 1; w2 < kTopkWaves; ++w2) sacc += red[w2 * n + j];
+      for (int w2 = 1; w2 < NW; ++w2) sacc += red[w2 * n + j];
       out[(long long)part * n + j] = sacc;
     }
     __syncthreads();
@@ -294,9 +314,10 @@ __global__ void hier_finalize_kernel(const float* __restrict__ part_imp,
 
 template <int NPL>
 hipError_t launch_topk_t(const TopkArgs& a, int grid, hipStream_t s) {
-  const size_t shm = (size_t)kTopkWaves * a.n * sizeof(float);
+  constexpr int NW = NPL <= 8 ? 16 : 8;  // the same rule as topk_waves()
+  const size_t shm = (size_t)NW * a.n * sizeof(float);
   ProfScope ps(a.tile_expert ? "gate_topk_grouped" : "gate_topk", s);
-  topk_kernel<NPL><<<dim3(grid), dim3(kTopkThreads), shm, s>>>(a);
+  topk_kernel<NPL, NW><<<dim3(grid), dim3(NW * 64), shm, s>>>(a);
   return hipGetLastError();
 }
 

@@ -116,8 +116,10 @@ struct TopkArgs {
   int max_tiles;
   int tile_rows;
 };
-constexpr int kTopkWaves = 8;  // wavefronts (rows in flight) per gate-epilogue block
-constexpr int kTopkThreads = kTopkWaves * 64;
+// Wavefronts (rows in flight) per gate-epilogue block: 16 while a row fits in
+// at most 8 registers per lane (n <= 512), else 8 (larger rows need the
+// registers).  The host's rows-per-block is a multiple of this.
+inline int topk_waves(int n) { return (n + 63) / 64 <= 8 ? 16 : 8; }
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 // out[j] = sum over parts p < nparts of part[p*n + j] (double sum, fixed
 // order); likewise out2 from part2 when part2 is not null (same launch).
