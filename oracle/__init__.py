@@ -32,6 +32,7 @@ _lib = None
 
 GATE_TOPK_SOFTMAX = 0
 GATE_SWITCH_TOP1 = 1
+GATE_SIGMOID_BIAS = 2
 ACT_RELU = 0
 ACT_SWIGLU = 1
 NEAR_TIE_REL = 1e-4
@@ -100,7 +101,14 @@ def lib():
         L.oracle_combine.argtypes = [c_int, c_int, c_int, _dp, _ip, _dp, _dp]
         L.oracle_cv2.argtypes = [c_int, _dp]
         L.oracle_cv2.restype = c_dbl
-        L.oracle_aux.argtypes = [c_int, c_int, c_int, _dp, odp, _ip, c_dbl, c_dbl, c_dbl, _dp]
+        L.oracle_aux.argtypes = [c_int, c_int, c_int, _dp, odp, _ip, c_dbl, c_dbl, c_dbl, c_dbl,
+                                 c_dbl, c_dbl, c_dbl, _dp]
+        L.oracle_sigmoid_gate_weights.argtypes = [c_int, c_int, c_int, _dp, _ip, _dp, odp]
+        L.oracle_zloss_sum.argtypes = [c_int, c_int, _dp]
+        L.oracle_zloss_sum.restype = c_dbl
+        L.oracle_entropy_sum.argtypes = [c_int, c_int, _dp]
+        L.oracle_entropy_sum.restype = c_dbl
+        L.oracle_bias_update.argtypes = [c_int, c_int, c_int, _ip, c_dbl, _dp]
         L.oracle_hier_load.argtypes = [c_int, c_int, _dp, _dp, _ip, _dp]
         _lib = L
     return _lib
@@ -175,6 +183,37 @@ def gate_weights(H, topk_idx, mode=GATE_TOPK_SOFTMAX):
     return w, probs
 
 
+def sigmoid_gate_weights(h, topk_idx):
+    """[SURVEY] 6.2: kept weights s_i / sum s_j with s = Sigmoid(h), h the
+    bias-free logits; also the dense gate vector."""
+    h = _d(h)
+    topk_idx = _i(topk_idx)
+    T, n = h.shape
+    k = topk_idx.shape[1]
+    w = np.empty((T, k))
+    probs = np.empty((T, n))
+    lib().oracle_sigmoid_gate_weights(T, n, k, h, topk_idx, w, probs)
+    return w, probs
+
+
+def zloss_sum(Z) -> float:
+    Z = _d(Z)
+    return float(lib().oracle_zloss_sum(Z.shape[0], Z.shape[1] if Z.ndim == 2 else 0, Z))
+
+
+def entropy_sum(G) -> float:
+    G = _d(G)
+    return float(lib().oracle_entropy_sum(G.shape[0], G.shape[1] if G.ndim == 2 else 0, G))
+
+
+def bias_update(bias, counts_pre, T, k, gamma):
+    """[SURVEY] 6.3 controller; returns the updated bias (float64)."""
+    b = _d(bias).copy()
+    c = _i(counts_pre)
+    lib().oracle_bias_update(b.size, int(T), int(k), c, float(gamma), b)
+    return b
+
+
 def importance(probs):
     probs = _d(probs)
     T, n = probs.shape
@@ -229,13 +268,16 @@ def combine(y_perm, slot_pos, topk_w, d):
     return y
 
 
-def aux(T, k, importance_v, load_v, counts_pre, w_importance, w_load, alpha):
+def aux(T, k, importance_v, load_v, counts_pre, w_importance, w_load, alpha, zsum=0.0,
+        entsum=0.0, w_z=1.0, w_entropy=1.0):
+    """The five losses: importance, load, Switch, z-loss, -entropy."""
     importance_v = _d(importance_v)
     load_v = _d(load_v)
     counts_pre = _i(counts_pre)
-    out = np.empty(3)
+    out = np.empty(5)
     lib().oracle_aux(T, k, importance_v.size, importance_v, load_v, counts_pre,
-                     float(w_importance), float(w_load), float(alpha), out)
+                     float(w_importance), float(w_load), float(alpha), float(zsum),
+                     float(entsum), float(w_z), float(w_entropy), out)
     return out
 
 
@@ -274,10 +316,26 @@ class GateResult:
     load: np.ndarray | None
     P: np.ndarray | None
     near_tie: np.ndarray
+    zsum: float = 0.0       # sum over tokens of the squared norm of the softmax's logits
+    entsum: float = 0.0     # sum over tokens of the gate distribution's entropy
 
 
 def gate(x, w_gate, k, b_gate=None, w_noise=None, noise=None, mode=GATE_TOPK_SOFTMAX):
-    """[PAPER] Noisy Top-K gating plus its Importance / Load vectors."""
+    """[PAPER] Noisy Top-K gating plus its Importance / Load vectors, the
+    z-loss and entropy statistics ([WIKI] part 2).
+    GATE_SIGMOID_BIAS ([SURVEY] 6.2, 6.3): selection on h + b, weights from
+    Sigmoid(h) normalised over the kept experts; no noise, no Load; the
+    z-loss statistic is taken over h (the bias is not a network output)."""
+    if mode == GATE_SIGMOID_BIAS:
+        if w_noise is not None:
+            raise ValueError("the sigmoid gate takes no noise")
+        h, _, _ = gate_logits(x, w_gate)
+        H = h + (_d(b_gate) if b_gate is not None else 0.0)
+        idx, hk, hk1 = keep_topk(H, k)
+        w, probs = sigmoid_gate_weights(h, idx)
+        imp = importance(probs)
+        return GateResult(H, None, H, idx, w, probs, hk, hk1, imp, None, None,
+                          near_ties(hk, hk1), zloss_sum(h), entropy_sum(probs))
     clean, sp, H = gate_logits(x, w_gate, b_gate, w_noise, noise)
     idx, hk, hk1 = keep_topk(H, k)
     w, probs = gate_weights(H, idx, mode)
@@ -285,7 +343,8 @@ def gate(x, w_gate, k, b_gate=None, w_noise=None, noise=None, mode=GATE_TOPK_SOF
     ld, P = (None, None)
     if sp is not None:
         ld, P = load(clean, sp, idx, hk, hk1)
-    return GateResult(clean, sp, H, idx, w, probs, hk, hk1, imp, ld, P, near_ties(hk, hk1))
+    return GateResult(clean, sp, H, idx, w, probs, hk, hk1, imp, ld, P, near_ties(hk, hk1),
+                      zloss_sum(H), entropy_sum(probs))
 
 
 def experts_apply(x, perm, offsets, w1, w2, b1=None, w3=None, b2=None, act=ACT_RELU, bf16=False,
@@ -309,16 +368,24 @@ def experts_apply(x, perm, offsets, w1, w2, b1=None, w3=None, b2=None, act=ACT_R
 
 def forward(x, w_gate, k, w1, w2, *, b_gate=None, w_noise=None, noise=None, b1=None, w3=None,
             b2=None, mode=GATE_TOPK_SOFTMAX, act=ACT_RELU, bf16=False, capacity_factor=0.0,
-            w_importance=0.1, w_load=0.1, alpha=1.0):
-    """The whole flat layer: gate -> dispatch -> experts -> combine -> losses."""
+            w_importance=0.1, w_load=0.1, alpha=1.0, w_z=1.0, w_entropy=1.0, ws1=None,
+            ws3=None, ws2=None):
+    """The whole flat layer: gate -> dispatch -> experts -> combine -> losses.
+    ws1/ws3/ws2: the always-active shared expert ([SURVEY] 5.2, 6.2),
+    y = E_shared(x) + sum_i g_i E_i(x)."""
     T, d = np.asarray(x).shape
     n = np.asarray(w_gate).shape[0]
     g = gate(x, w_gate, k, b_gate, w_noise, noise, mode)
     disp = dispatch(g.topk_idx, n, capacity_factor)
     y_perm = experts_apply(x, disp["perm"], disp["offsets"], w1, w2, b1, w3, b2, act, bf16)
     y = combine(y_perm, disp["slot_pos"], g.topk_w, d)
-    losses = aux(T, k, g.importance, g.load, disp["counts_pre"], w_importance, w_load, alpha)
-    return dict(gate=g, dispatch=disp, y_perm=y_perm, y=y, losses=losses)
+    y_shared = None
+    if ws1 is not None:
+        y_shared = expert_ffn(np.asarray(x), ws1, ws2, None, ws3, None, act, bf16)
+        y = y_shared + y
+    losses = aux(T, k, g.importance, g.load, disp["counts_pre"], w_importance, w_load, alpha,
+                 g.zsum, g.entsum, w_z, w_entropy)
+    return dict(gate=g, dispatch=disp, y_perm=y_perm, y=y, y_shared=y_shared, losses=losses)
 
 
 def gate_hier(x, w_gate, w_noise, noise, k1, w_gate2, w_noise2, noise2, k2, b_gate=None,
@@ -337,6 +404,7 @@ def gate_hier(x, w_gate, w_noise, noise, k1, w_gate2, w_noise2, noise2, k2, b_ga
     idx = np.empty((T, k1 * k2), np.int32)
     wts = np.empty((T, k1 * k2))
     near = pg.near_tie.copy()
+    zsum = pg.zsum
     load_sec = np.zeros((a, b))
     group_tokens = np.zeros(a, np.int32)
     noise2 = _d(noise2) if noise2 is not None else None
@@ -350,6 +418,7 @@ def gate_hier(x, w_gate, w_noise, noise, k1, w_gate2, w_noise2, noise2, k2, b_ga
         z2 = noise2[toks, slots] if noise2 is not None else None
         sg = gate(x[toks], w_gate2[g], k2, None if b_gate2 is None else b_gate2[g],
                   None if w_noise2 is None else w_noise2[g], z2)
+        zsum += sg.zsum
         for r, (t, s) in enumerate(zip(toks, slots)):
             idx[t, s * k2:(s + 1) * k2] = g * b + sg.topk_idx[r]
             wts[t, s * k2:(s + 1) * k2] = pg.topk_w[t, s] * sg.topk_w[r]
@@ -363,11 +432,13 @@ def gate_hier(x, w_gate, w_noise, noise, k1, w_gate2, w_noise2, noise2, k2, b_ga
     imp = importance(dense)
     ld = hier_load(pg.load, load_sec, group_tokens) if pg.load is not None else None
     return dict(primary=pg, topk_idx=idx, topk_w=wts, importance=imp, load=ld,
-                load_secondary=load_sec, group_tokens=group_tokens, near_tie=near)
+                load_secondary=load_sec, group_tokens=group_tokens, near_tie=near,
+                zsum=zsum, entsum=entropy_sum(dense))
 
 
 def forward_hier(x, w_gate, w_noise, noise, k1, w_gate2, w_noise2, noise2, k2, w1, w2, *,
-                 b1=None, b2=None, bf16=False, w_importance=0.1, w_load=0.1, alpha=1.0):
+                 b1=None, b2=None, bf16=False, w_importance=0.1, w_load=0.1, alpha=1.0,
+                 w_z=1.0, w_entropy=1.0):
     T, d = np.asarray(x).shape
     gh = gate_hier(x, w_gate, w_noise, noise, k1, w_gate2, w_noise2, noise2, k2)
     n = np.asarray(w_gate2).shape[0] * np.asarray(w_gate2).shape[1]
@@ -375,5 +446,5 @@ def forward_hier(x, w_gate, w_noise, noise, k1, w_gate2, w_noise2, noise2, k2, w
     y_perm = experts_apply(x, disp["perm"], disp["offsets"], w1, w2, b1, None, b2, ACT_RELU, bf16)
     y = combine(y_perm, disp["slot_pos"], gh["topk_w"], d)
     losses = aux(T, k1 * k2, gh["importance"], gh["load"], disp["counts_pre"], w_importance,
-                 w_load, alpha)
+                 w_load, alpha, gh["zsum"], gh["entsum"], w_z, w_entropy)
     return dict(gate=gh, dispatch=disp, y_perm=y_perm, y=y, losses=losses)

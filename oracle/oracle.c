@@ -24,7 +24,11 @@
  *   [SURVEY] "MoE 稀疏架构深度解析" (tufusi.com), section 3.1 (Switch router)
  *            and 3.2 (auxiliary loss, expert capacity).
  *   [WIKI]   "MoE (Mixture-of-Experts) 算法介绍" (wkbse.com), part 2 (top-k
- *            weights renormalised to sum to one).
+ *            weights renormalised to sum to one; router z-loss and gate
+ *            entropy among the auxiliary losses).
+ *   [SURVEY] sections 5.2 (shared expert), 6.2 (sigmoid affinities
+ *            normalised over the top k) and 6.3 (selection-only bias and its
+ *            non-gradient update).
  *
  * Readings where the pages are silent (each also listed in the design notes):
  *   - KeepTopK ties: the lower expert index wins; -0.0 equals +0.0.
@@ -45,6 +49,7 @@
 
 #define ORACLE_GATE_TOPK_SOFTMAX 0
 #define ORACLE_GATE_SWITCH_TOP1 1
+#define ORACLE_GATE_SIGMOID_BIAS 2
 #define ORACLE_ACT_RELU 0
 #define ORACLE_ACT_SWIGLU 1
 
@@ -184,6 +189,74 @@ void oracle_gate_weights(int T, int n, int k, int mode, const double* H,
         for (int s = 0; s < k; ++s) g[idx[s]] = w[s];
       }
     }
+  }
+}
+
+/* O4 for the sigmoid gate.  [SURVEY] 6.2: s_i = Sigmoid(h_i(x)) and the kept
+ * experts get g_i = s_i / sum over the kept j of s_j.  [SURVEY] 6.3: the
+ * per-expert bias enters only the selection score h_i + b_i, so the caller
+ * selects on h + b and passes the bias-free logits h here.  probs[T][n] is
+ * the dense gate vector (g on the kept experts, 0 elsewhere). */
+void oracle_sigmoid_gate_weights(int T, int n, int k, const double* h,
+                                 const int32_t* topk_idx, double* topk_w, double* probs) {
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < T; ++t) {
+    const double* v = h + (size_t)t * n;
+    const int32_t* idx = topk_idx + (size_t)t * k;
+    double* w = topk_w + (size_t)t * k;
+    double z = 0.0;
+    for (int s = 0; s < k; ++s) {
+      w[s] = 1.0 / (1.0 + exp(-v[idx[s]]));
+      z += w[s];
+    }
+    for (int s = 0; s < k; ++s) w[s] /= z;
+    if (probs) {
+      double* g = probs + (size_t)t * n;
+      for (int j = 0; j < n; ++j) g[j] = 0.0;
+      for (int s = 0; s < k; ++s) g[idx[s]] = w[s];
+    }
+  }
+}
+
+/* Router z-loss statistic.  [WIKI] part 2: the z-loss penalises the L2 norm
+ * of the logits the gate feeds to its softmax.  Read as the squared norm,
+ * summed over tokens: sum_t sum_j Z[t][j]^2 (the caller divides by T). */
+double oracle_zloss_sum(int T, int n, const double* Z) {
+  double acc = 0.0;
+  for (int t = 0; t < T; ++t) {
+    double r = 0.0;
+    for (int j = 0; j < n; ++j) r += Z[(size_t)t * n + j] * Z[(size_t)t * n + j];
+    acc += r;
+  }
+  return acc;
+}
+
+/* Gate entropy statistic.  [WIKI] part 2: the gate-entropy loss rewards a
+ * high entropy of the gate's output distribution.  Sum over tokens of
+ * -sum_j G[t][j] ln G[t][j], with 0 ln 0 = 0. */
+double oracle_entropy_sum(int T, int n, const double* G) {
+  double acc = 0.0;
+  for (int t = 0; t < T; ++t) {
+    double r = 0.0;
+    for (int j = 0; j < n; ++j) {
+      double g = G[(size_t)t * n + j];
+      if (g > 0.0) r -= g * log(g);
+    }
+    acc += r;
+  }
+  return acc;
+}
+
+/* [SURVEY] 6.3 non-gradient bias controller: an expert that received more
+ * than its even share of the step's assignments (counts_pre[i] > T*k/n)
+ * loses gamma from its selection bias, one that received fewer gains gamma,
+ * one exactly at the share keeps it. */
+void oracle_bias_update(int n, int T, int k, const int32_t* counts_pre, double gamma,
+                        double* bias) {
+  double share = (double)T * (double)k / (double)n;
+  for (int i = 0; i < n; ++i) {
+    if ((double)counts_pre[i] > share) bias[i] -= gamma;
+    else if ((double)counts_pre[i] < share) bias[i] += gamma;
   }
 }
 
@@ -356,10 +429,12 @@ double oracle_cv2(int n, const double* v) {
  *            losses[1] = w_load * CV(Load)^2 (0 when load is NULL),
  *            losses[2] = alpha * n * sum_i f_i * P_i  ([SURVEY] 3.2), with
  *              f_i = counts_pre[i] / (T*k) (fraction of routed slots) and
- *              P_i = Importance_i / T (mean router probability). */
+ *              P_i = Importance_i / T (mean router probability),
+ *            losses[3] = w_z * zsum / T, losses[4] = -w_entropy * entsum / T
+ *              (zsum, entsum: oracle_zloss_sum / oracle_entropy_sum). */
 void oracle_aux(int T, int k, int n, const double* importance, const double* load,
                 const int32_t* counts_pre, double w_importance, double w_load, double alpha,
-                double* losses) {
+                double zsum, double entsum, double w_z, double w_entropy, double* losses) {
   losses[0] = w_importance * oracle_cv2(n, importance);
   losses[1] = load ? w_load * oracle_cv2(n, load) : 0.0;
   double acc = 0.0;
@@ -371,6 +446,10 @@ void oracle_aux(int T, int k, int n, const double* importance, const double* loa
     }
   }
   losses[2] = alpha * (double)n * acc;
+  /* [WIKI] part 2: mean squared logit norm (z-loss) and minus the mean gate
+   * entropy (minimising it raises the entropy); 0 when T == 0. */
+  losses[3] = T > 0 ? w_z * zsum / (double)T : 0.0;
+  losses[4] = T > 0 ? -w_entropy * entsum / (double)T : 0.0;
 }
 
 /* O10 aux part.  Hierarchical load: for primary group g and expert e of that

@@ -82,7 +82,7 @@ def _golden():
         g = json.load(f)
     e = math.e
     ns = {"a": e / (1 + e), "b": 1 / (1 + e), "L": math.log(2.0),
-          "Phi": lambda z: float(ndtr(z))}
+          "Phi": lambda z: float(ndtr(z)), "log": math.log}
 
     def ev(v):
         if isinstance(v, list):
@@ -125,6 +125,8 @@ def test_golden_worked_layer():
     imp = np.array(ev(exp["importance"]))
     cv2 = np.mean((imp - imp.mean()) ** 2) / imp.mean() ** 2
     assert out["losses"][0] == pytest.approx(0.1 * cv2, rel=1e-14)
+    assert out["losses"][3] == pytest.approx(ev(exp["zloss_mean"]), rel=1e-15)
+    assert out["losses"][4] == pytest.approx(ev(exp["entropy_loss"]), rel=1e-14)
 
     cap = exp["capacity_1"]
     out = oracle.forward(x, w_gate, k, w1, w2, b_gate=b_gate, w_noise=w_noise, noise=noise,
@@ -133,6 +135,130 @@ def test_golden_worked_layer():
     for key in ("counts_pre", "counts", "offsets", "perm", "slot_pos"):
         np.testing.assert_array_equal(d[key], cap[key], err_msg=key)
     np.testing.assert_allclose(out["y"], ev(cap["y"]), rtol=1e-15, atol=1e-15)
+
+
+def test_golden_sigmoid_gate_shared_expert():
+    """Selection-only bias, sigmoid weights normalised over the kept experts,
+    the shared expert, the bias controller and the z / entropy losses, against
+    the hand-worked tests/golden/sigmoid_gate.json."""
+    with open(os.path.join(GOLDEN, "sigmoid_gate.json")) as f:
+        g = json.load(f)
+
+    def ev(v):
+        if isinstance(v, list):
+            return [ev(u) for u in v]
+        if isinstance(v, str):
+            return float(eval(v, {"__builtins__": {}}, {"log": math.log}))
+        return v
+    inp, exp = g["inputs"], g["expected"]
+    n, k = inp["n"], inp["k"]
+    x = np.array(inp["x"])
+    w_gate = np.array(ev(inp["w_gate"]))
+    bias = np.array(inp["bias"])
+    w1 = np.stack([np.array(inp["w1_each"])] * n)
+    w2 = np.stack([np.full((1, 2), float(e + 1)) for e in range(n)])
+    out = oracle.forward(x, w_gate, k, w1, w2, b_gate=bias, mode=oracle.GATE_SIGMOID_BIAS,
+                         ws1=np.array(inp["ws1"]), ws2=np.array(inp["ws2"]))
+    gt = out["gate"]
+    np.testing.assert_array_equal(gt.topk_idx, exp["topk_idx"])
+    np.testing.assert_allclose(gt.topk_w, ev(exp["topk_w"]), rtol=1e-15)
+    np.testing.assert_allclose(gt.importance, ev(exp["importance"]), rtol=1e-15, atol=1e-300)
+    np.testing.assert_array_equal(out["dispatch"]["counts_pre"], exp["counts_pre"])
+    np.testing.assert_allclose(out["y"], ev(exp["y"]), rtol=1e-15)
+    assert out["losses"][3] == pytest.approx(ev(exp["zloss_mean"]), rel=1e-15)
+    assert out["losses"][4] == pytest.approx(ev(exp["entropy_loss"]), rel=1e-14)
+    nb = oracle.bias_update(bias, out["dispatch"]["counts_pre"], len(x), k, inp["gamma"])
+    np.testing.assert_allclose(nb, ev(exp["bias_after"]), rtol=1e-15, atol=1e-18)
+
+
+def test_sigmoid_gate_bias_selects_only():
+    """[SURVEY] 6.3: the bias moves the selection, never the weights.  Adding
+    a large bias to a fixed set of experts forces exactly that set; scaling
+    the bias leaves the weights unchanged; the weights equal Sigmoid(h) of the
+    kept experts over their sum (checked with scipy's expit)."""
+    from scipy.special import expit
+    rng = np.random.default_rng(11)
+    T, d, n, k = 12, 6, 10, 3
+    x = rng.standard_normal((T, d))
+    w_gate = rng.standard_normal((n, d))
+    forced = [7, 2, 5]
+    bias = np.zeros(n)
+    bias[forced] = [300.0, 200.0, 100.0]
+    g1 = oracle.gate(x, w_gate, k, b_gate=bias, mode=oracle.GATE_SIGMOID_BIAS)
+    g2 = oracle.gate(x, w_gate, k, b_gate=2 * bias, mode=oracle.GATE_SIGMOID_BIAS)
+    np.testing.assert_array_equal(g1.topk_idx, np.tile(forced, (T, 1)))
+    np.testing.assert_array_equal(g2.topk_idx, g1.topk_idx)
+    np.testing.assert_allclose(g2.topk_w, g1.topk_w, rtol=0, atol=0)
+    h = x @ w_gate.T
+    s = expit(h[:, forced])
+    np.testing.assert_allclose(g1.topk_w, s / s.sum(1, keepdims=True), rtol=1e-14)
+    assert g1.load is None
+
+
+def test_bias_update_controller_cases():
+    """Counts above, at and below the even share T*k/n move the bias by -gamma,
+    0, +gamma; a non-integral share (T*k/n = 2.5) puts 2 below and 3 above."""
+    T, k, n = 10, 1, 4
+    b = oracle.bias_update(np.zeros(n), [4, 2, 3, 1], T, k, 0.25)
+    np.testing.assert_array_equal(b, [-0.25, 0.25, -0.25, 0.25])
+    b = oracle.bias_update(np.ones(2), [5, 5], 5, 2, 0.5)
+    np.testing.assert_array_equal(b, [1.0, 1.0])
+
+
+def test_zloss_and_entropy_closed_forms():
+    """Equal logits c: z statistic T*n*c^2, top-k weights 1/k (entropy ln k),
+    Switch gate p = 1/n (entropy ln n), sigmoid gate 1/k; zero logits give a
+    zero z statistic; doubling the logits multiplies it by 4."""
+    T, d, n, k = 7, 3, 6, 2
+    x = np.zeros((T, d))
+    c = 0.75
+    b = np.full(n, c)
+    w = np.zeros((n, d))
+    for mode, ent in ((oracle.GATE_TOPK_SOFTMAX, math.log(k)),
+                      (oracle.GATE_SWITCH_TOP1, math.log(n))):
+        kk = 1 if mode == oracle.GATE_SWITCH_TOP1 else k
+        g = oracle.gate(x, w, kk, b_gate=b, mode=mode)
+        assert g.zsum == pytest.approx(T * n * c * c, rel=1e-15)
+        assert g.entsum == pytest.approx(T * ent, rel=1e-14)
+    g = oracle.gate(x, w, k, b_gate=b, mode=oracle.GATE_SIGMOID_BIAS)
+    assert g.zsum == 0.0            # the bias is not part of the network's logits
+    assert g.entsum == pytest.approx(T * math.log(k), rel=1e-14)
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((T, d))
+    w = rng.standard_normal((n, d))
+    z1 = oracle.gate(x, w, k).zsum
+    z2 = oracle.gate(x, 2 * w, k).zsum
+    assert z2 == pytest.approx(4 * z1, rel=1e-14)
+
+
+def test_hierarchical_equal_logits_entropy_adds():
+    """Two-level gate with every logit equal: the product distribution is
+    uniform over k1*k2 experts, so its entropy is ln k1 + ln k2 per token."""
+    T, d, a, b, k1, k2 = 5, 2, 4, 3, 2, 2
+    x = np.zeros((T, d))
+    gh = oracle.gate_hier(x, np.zeros((a, d)), None, None, k1, np.zeros((a, b, d)), None, None,
+                          k2)
+    assert gh["entsum"] == pytest.approx(T * math.log(k1 * k2), rel=1e-14)
+    assert gh["zsum"] == 0.0
+
+
+def test_shared_expert_single_routed_expert():
+    """n = k = 1 with the sigmoid gate (weight 1) plus a shared expert: y is
+    the sum of two dense bf16 FFNs, computed here with numpy on the same
+    bf16-rounded operands."""
+    rng = np.random.default_rng(5)
+    T, d, h = 9, 16, 24
+    x = rng.standard_normal((T, d))
+    r = lambda *s: oracle.bf16_round(rng.standard_normal(s) / 4)
+    w1, w2 = r(1, h, d), r(1, d, h)
+    ws1, ws2 = r(h, d), r(d, h)
+    out = oracle.forward(x, rng.standard_normal((1, d)), 1, w1, w2, mode=oracle.GATE_SIGMOID_BIAS,
+                         bf16=True, ws1=ws1, ws2=ws2)
+    xb = oracle.bf16_round(x)
+    ffn = lambda a, b: oracle.bf16_round(np.maximum(xb @ a.T, 0)) @ b.T
+    np.testing.assert_allclose(out["gate"].topk_w, 1.0, rtol=0, atol=0)
+    np.testing.assert_allclose(out["y"], ffn(w1[0], w2[0]) + ffn(ws1, ws2), rtol=1e-12,
+                               atol=1e-12)
 
 
 # ---------------------------------------------------------------------------
@@ -487,7 +613,14 @@ def test_hierarchical_one_group_reduces_to_flat():
     np.testing.assert_allclose(hier["gate"]["importance"], flat["gate"].importance, rtol=1e-14)
     np.testing.assert_allclose(hier["gate"]["load"], flat["gate"].load, rtol=1e-14)
     np.testing.assert_array_equal(hier["gate"]["topk_idx"], flat["gate"].topk_idx)
-    np.testing.assert_allclose(hier["losses"], flat["losses"], rtol=1e-12, atol=1e-15)
+    sel = [0, 1, 2, 4]
+    np.testing.assert_allclose(hier["losses"][sel], flat["losses"][sel], rtol=1e-12, atol=1e-15)
+    # The z-loss statistic covers both gating networks: with one group the
+    # primary gate's single logit per token is the only extra term.
+    T = len(hier["y"])
+    prim = hier["gate"]["primary"].H
+    np.testing.assert_allclose(hier["losses"][3], flat["losses"][3] + float(np.sum(prim * prim)) / T,
+                               rtol=1e-12)
 
 
 def test_hierarchical_matches_dense_two_level_sum():
