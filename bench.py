@@ -66,14 +66,21 @@ def kernel_work(name, cfg, rows, nonempty, T):
                 "bf16")
     if name == "ggemm_bf16_out":
         return (nonempty * d * h * 2 + rows * h * 2 + rows * d * 4, 2.0 * rows * d * h, "bf16")
+    hs = cfg.d_hidden_shared
+    if name == "shared_bf16_relu":
+        return (hs * d * 2 + T * d * 2 + T * hs * 2, 2.0 * T * hs * d, "bf16")
+    if name == "shared_bf16_swiglu":
+        return (2 * hs * d * 2 + T * d * 2 + T * hs * 2, 4.0 * T * hs * d, "bf16")
+    if name == "shared_bf16_out":
+        return (d * hs * 2 + T * hs * 2 + T * d * 4, 2.0 * T * d * hs, "bf16")
     if name.startswith("gemm_f32"):
         return (T * d * 4 + ncols * d * 4 + T * ncols * 4, 2.0 * T * ncols * d, "f32")
     if name == "gate_topk":
         return (T * ncols * 4 + (T * n * 4 if noisy else 0) + T * k * 8, 0.0, "f32")
     if name == "dispatch_gather":
-        return (T * d * 4 + rows * d * wsz + rows * 4, 0.0, "f32")
+        return (T * d * 4 + rows * d * wsz + rows * 4 + (T * d * 2 if hs else 0), 0.0, "f32")
     if name == "combine":
-        return (rows * d * 4 + T * d * 4 + T * k * 8, 0.0, "f32")
+        return (rows * d * 4 + T * d * 4 + T * k * 8 + (T * d * 4 if hs else 0), 0.0, "f32")
     if name == "dispatch_permute":
         return (T * k * 4 * 2 + rows * 4, 0.0, "i32")
     if name == "dispatch_hist":
@@ -88,6 +95,14 @@ def kernel_work(name, cfg, rows, nonempty, T):
     if name in ("dispatch_finalize", "dispatch_offsets", "ffn_tilemap", "aux_loss"):
         return (n * 12, 0.0, "i32")
     return (0.0, 0.0, "")
+
+
+def gate_text(cfg):
+    if cfg.gate == 1:
+        return "Switch top-1 softmax, fp32"
+    if cfg.gate == 2:
+        return "sigmoid top-k with selection-only bias, fp32"
+    return ("noisy " if cfg.noisy else "") + "top-k softmax, fp32"
 
 
 def roofline_entry(bytes_, flops, dtype, avg_s):
@@ -195,7 +210,7 @@ def main():
     diag = {"topk_idx": torch.empty((T, k), **i32), "counts": torch.empty(n, **i32),
             "offsets": torch.empty(n + 1, **i32)}
     y = torch.empty((T, cfg.d_model), dtype=torch.float32, device="cuda")
-    losses = torch.empty(3, dtype=torch.float32, device="cuda")
+    losses = torch.empty(moe.N_LOSSES, dtype=torch.float32, device="cuda")
 
     for _ in range(args.warmup):
         layer.forward(inp["x"], inp.get("noise"), inp.get("noise2"), y=y, losses=losses)
@@ -301,9 +316,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": T, "d_model": cfg.d_model,
                    "d_hidden": cfg.d_hidden, "n_experts": n, "k": k,
-                   "gate": "noisy top-k softmax, fp32" if cfg.noisy else "top-k softmax, fp32",
-                   "experts": "bf16 ReLU FFN, fp32 accumulate" if cfg.expert_dtype == 1
-                   else "fp32 ReLU FFN",
+                   "gate": gate_text(cfg),
+                   "experts": ("bf16 " if cfg.expert_dtype == 1 else "fp32 ")
+                   + ("SwiGLU" if cfg.act == 1 else "ReLU") + " FFN, fp32 accumulate"
+                   + (f", shared expert h={cfg.d_hidden_shared}" if cfg.d_hidden_shared else ""),
                    "rows": rows, "nonempty_experts": nonempty, "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "kernels": kernels,

@@ -12,9 +12,12 @@
  *   sections "Sparsely-Gated MoE layer architecture", "Noisy Top-K Gating",
  *   "Balancing expert utilization", "Hierarchical MoE".
  * Also supported: the Switch top-1 router with expert capacity and its
- * n * sum f_i P_i loss (MoE survey, tufusi.com, sections 3.1 and 3.2), and
+ * n * sum f_i P_i loss (MoE survey, tufusi.com, sections 3.1 and 3.2),
  * renormalised top-k over a gated (SwiGLU) expert FFN (same survey, section
- * 6.2, fine-grained routed experts).
+ * 6.2, fine-grained routed experts), the sigmoid gate with a selection-only
+ * bias, its bias controller and an always-active shared expert (same survey,
+ * sections 5.2, 6.2, 6.3), and the router z-loss and gate-entropy losses
+ * (MoE algorithm introduction, wkbse.com, part 2).
  *
  * Conventions shared by every call
  * --------------------------------
@@ -57,7 +60,9 @@ typedef enum {
 
 typedef enum {
   MOE_GATE_TOPK_SOFTMAX = 0, /* G = Softmax(KeepTopK(H, k)); noisy iff w_noise != NULL */
-  MOE_GATE_SWITCH_TOP1 = 1   /* p = softmax(h) over all n; top-1 with weight p_argmax; k = 1 */
+  MOE_GATE_SWITCH_TOP1 = 1,  /* p = softmax(h) over all n; top-1 with weight p_argmax; k = 1 */
+  MOE_GATE_SIGMOID_BIAS = 2  /* top-k of h + b_gate; g = Sigmoid(h) / sum over the kept of
+                                Sigmoid(h); no noise; flat layers only */
 } moe_gate_kind;
 
 typedef enum {
@@ -83,6 +88,10 @@ typedef struct {
   float w_importance;     /* weight of CV(Importance)^2 */
   float w_load;           /* weight of CV(Load)^2 */
   float alpha_switch;     /* weight of n * sum_i f_i P_i */
+  float w_z;              /* weight of the router z-loss */
+  float w_entropy;        /* weight of the gate-entropy loss */
+  int32_t d_hidden_shared;/* hidden width of the shared expert, multiple of 8; 0 = none.
+                             The shared expert uses `act` and needs bf16 experts. */
 } moe_config;
 
 /* Weight pointers for moe_forward (a host struct holding device pointers). */
@@ -97,6 +106,9 @@ typedef struct {
   const void* w3;        /* [n, h, d] expert_dtype, SwiGLU only */
   const void* w2;        /* [n, d, h] expert_dtype */
   const float* b2;       /* [n, d] fp32, optional (ReLU only) */
+  const void* ws1;       /* shared expert [h_s, d] bf16 (h_s = d_hidden_shared) */
+  const void* ws3;       /* shared expert [h_s, d] bf16, SwiGLU only */
+  const void* ws2;       /* shared expert [d, h_s] bf16 */
 } moe_weights;
 
 /* Optional intermediate outputs of moe_forward; every field may be NULL
@@ -132,12 +144,21 @@ size_t moe_workspace_size(const moe_config* cfg);
  *      of the full softmax p);
  *      load [n] fp32 -- sum over tokens of P(x,i) = Phi((clean_i - thr_i) /
  *      Softplus(raw_i)), thr_i = H_(k+1) if i is kept else H_(k); required iff
- *      w_noise != NULL, ignored otherwise (may be NULL).
+ *      w_noise != NULL, ignored otherwise (may be NULL);
+ *      gate_stats [2] fp32, optional -- [0] = sum over tokens of the squared
+ *      L2 norm of the logits the gate's softmax sees (H; the sigmoid gate:
+ *      the bias-free logits h), [1] = sum over tokens of the entropy of the
+ *      gate distribution (the kept weights; Switch: the full softmax p).
+ *      Definition: wkbse.com MoE introduction, part 2 (router z-loss, gate
+ *      entropy loss).
+ * MOE_GATE_SIGMOID_BIAS (tufusi.com survey 6.2, 6.3): b_gate only moves the
+ * selection (top-k of h + b); the weights are Sigmoid(h) renormalised over
+ * the kept experts; w_noise must be NULL.
  * Flat configs only (n_groups == 0); n <= 2048. */
 moe_status moe_gate(const moe_config* cfg, const float* x, const float* w_gate,
                     const float* b_gate, const float* w_noise, const float* noise,
-                    int32_t* topk_idx, float* topk_w, float* importance, float* load, void* ws,
-                    size_t ws_bytes, void* stream);
+                    int32_t* topk_idx, float* topk_w, float* importance, float* load,
+                    float* gate_stats, void* ws, size_t ws_bytes, void* stream);
 
 /* Two-level gate: a primary gate picks k1 of a groups, then each chosen
  * group's own secondary gate picks k2 of its b experts.
@@ -152,13 +173,16 @@ moe_status moe_gate(const moe_config* cfg, const float* x, const float* w_gate,
  *      importance [a*b] = sum of those products per expert;
  *      load [a*b] = Load_primary[g] * Load_g[e] / |X_g| (0 when no token
  *      reaches g), Load_g the secondary gate's load over the tokens X_g routed
- *      to g; required iff w_noise != NULL (both levels must then be noisy).
+ *      to g; required iff w_noise != NULL (both levels must then be noisy);
+ *      gate_stats [2], optional: [0] = squared logit norms of both levels'
+ *      gates summed over tokens, [1] = entropy of the product distribution
+ *      summed over tokens.
  * cfg->n_groups = a, cfg->k_groups = k1, cfg->k = k1*k2, n = a*b. */
 moe_status moe_gate_hier(const moe_config* cfg, const float* x, const float* w_gate,
                          const float* b_gate, const float* w_noise, const float* noise,
                          const float* w_gate2, const float* w_noise2, const float* noise2,
                          int32_t* topk_idx, float* topk_w, float* importance, float* load,
-                         void* ws, size_t ws_bytes, void* stream);
+                         float* gate_stats, void* ws, size_t ws_bytes, void* stream);
 
 /* Merge every position routed to an expert into one contiguous batch.
  *   Definition: chenshi221.pages.dev notes, "Engineering" (all time steps
@@ -195,30 +219,61 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32
                           const float* b2, float* y_perm, void* ws, size_t ws_bytes,
                           void* stream);
 
-/* y[t] = sum over the token's slots s (in slot order) of topk_w[t,s] *
- * y_perm[slot_pos[t,s]]; slots with slot_pos < 0 add nothing.  A gather:
- * every output row is written exactly once, no atomics.
- *   Definition: xyznot.com summary, "Method and key formulas" (layer output).
- * In: y_perm [*, d] fp32, slot_pos [T, k], topk_w [T, k].  Out: y [T, d] fp32. */
-moe_status moe_combine(const moe_config* cfg, const float* y_perm, const int32_t* slot_pos,
-                       const float* topk_w, float* y, void* stream);
+/* The shared expert on every token: y_shared[t] = E_shared(x[t]) with
+ * E(u) = ReLU(u ws1^T) ws2^T or (silu(u ws1^T) * (u ws3^T)) ws2^T (cfg->act),
+ * bf16 weights, fp32 accumulation, hidden activations rounded to bf16.
+ *   Definition: tufusi.com survey, sections 5.2 (shared experts, always
+ *   active) and 6.2 (one shared expert of the routed experts' width).
+ * In:  x [T, d] fp32; ws1 [h_s, d], ws3 [h_s, d] (SwiGLU), ws2 [d, h_s] bf16,
+ *      h_s = cfg->d_hidden_shared > 0.
+ * Out: y_shared [T, d] fp32. */
+moe_status moe_shared_ffn(const moe_config* cfg, const float* x, const void* ws1,
+                          const void* ws3, const void* ws2, float* y_shared, void* ws,
+                          size_t ws_bytes, void* stream);
 
-/* Auxiliary losses, losses[3] fp32 on the device:
+/* y[t] = y_base[t] (optional; e.g. the shared expert's output) + the sum over
+ * the token's slots s (in slot order) of topk_w[t,s] * y_perm[slot_pos[t,s]];
+ * slots with slot_pos < 0 add nothing.  A gather: every output row is written
+ * exactly once, no atomics.
+ *   Definition: xyznot.com summary, "Method and key formulas" (layer output);
+ *   tufusi.com survey 6.2 (shared expert added to the routed sum).
+ * In: y_perm [*, d] fp32, slot_pos [T, k], topk_w [T, k], y_base [T, d] or
+ * NULL.  Out: y [T, d] fp32. */
+moe_status moe_combine(const moe_config* cfg, const float* y_perm, const int32_t* slot_pos,
+                       const float* topk_w, const float* y_base, float* y, void* stream);
+
+/* Auxiliary losses, losses[5] fp32 on the device:
  *   losses[0] = w_importance * CV(importance)^2
  *   losses[1] = w_load * CV(load)^2 (0 when load == NULL)
  *   losses[2] = alpha_switch * n * sum_i f_i P_i, f_i = counts_pre[i]/(T*k),
  *               P_i = importance[i]/T (0 when T == 0)
+ *   losses[3] = w_z * gate_stats[0] / T        (router z-loss)
+ *   losses[4] = -w_entropy * gate_stats[1] / T (minus the mean gate entropy)
+ *               (both 0 when gate_stats == NULL or T == 0)
  * CV uses the population variance; CV^2 = 0 when the mean is 0.
  *   Definition: xyznot.com summary, "Method and key formulas" (L_importance,
- *   L_load); tufusi.com survey 3.2 (Switch auxiliary loss). */
+ *   L_load); tufusi.com survey 3.2 (Switch auxiliary loss); wkbse.com MoE
+ *   introduction, part 2 (z-loss on the L2 norm of the pre-softmax logits,
+ *   read as its square; entropy loss rewarding a high gate entropy). */
 moe_status moe_aux_loss(const moe_config* cfg, const float* importance, const float* load,
-                        const int32_t* counts_pre, float* losses, void* stream);
+                        const int32_t* counts_pre, const float* gate_stats, float* losses,
+                        void* stream);
 
-/* The whole layer: gate (flat or two-level), dispatch, experts, combine,
- * losses, all on `stream` with no host synchronisation.
+/* Non-gradient selection-bias controller of the sigmoid gate: for every
+ * expert, bias[i] -= gamma if counts_pre[i] > T*k/n (overloaded),
+ * bias[i] += gamma if counts_pre[i] < T*k/n, unchanged at the even share.
+ *   Definition: tufusi.com survey, section 6.3.
+ * In: counts_pre [n] int32 (e.g. from moe_dispatch or the forward's diag).
+ * In/out: bias [n] fp32 (the b_gate of the next step). */
+moe_status moe_router_bias_update(const moe_config* cfg, const int32_t* counts_pre, float* bias,
+                                  float gamma, void* stream);
+
+/* The whole layer: gate (flat or two-level), dispatch, experts, the shared
+ * expert (cfg->d_hidden_shared > 0), combine, losses, all on `stream` with no
+ * host synchronisation.
  * In:  weights (see moe_weights), x [T, d], noise [T, n_gate] (required iff
  *      weights->w_noise), noise2 [T, k1, b] (two-level, iff w_noise2).
- * Out: y [T, d] fp32 (no residual added), losses [3] fp32 (as moe_aux_loss),
+ * Out: y [T, d] fp32 (no residual added), losses [5] fp32 (as moe_aux_loss),
  *      diag: optional intermediates (may be NULL). */
 moe_status moe_forward(const moe_config* cfg, const moe_weights* weights, const float* x,
                        const float* noise, const float* noise2, float* y, float* losses,

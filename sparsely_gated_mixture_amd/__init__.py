@@ -10,11 +10,12 @@ from __future__ import annotations
 
 from . import workloads
 from ._lib import (EXPORTS, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED,
-                   MOE_ERR_WORKSPACE, MOE_OK, MoeConfig, MoeDiag, MoEError, MoeWeights,
-                   load_library, make_config, make_diag, make_weights, moe_aux_loss,
-                   moe_profile_collect, moe_profile_enable, moe_profile_entry,
-                   moe_combine, moe_dispatch, moe_expert_ffn, moe_forward, moe_gate,
-                   moe_gate_hier, moe_last_error, moe_status_string, moe_workspace_size)
+                   MOE_ERR_WORKSPACE, MOE_OK, N_LOSSES, MoeConfig, MoeDiag, MoEError,
+                   MoeWeights, load_library, make_config, make_diag, make_weights,
+                   moe_aux_loss, moe_combine, moe_dispatch, moe_expert_ffn, moe_forward,
+                   moe_gate, moe_gate_hier, moe_last_error, moe_profile_collect,
+                   moe_profile_enable, moe_profile_entry, moe_router_bias_update,
+                   moe_shared_ffn, moe_status_string, moe_workspace_size)
 
 load_library()
 
@@ -33,7 +34,8 @@ class MoELayer:
         self.w = make_weights(weights["w_gate"], weights.get("b_gate"), weights.get("w_noise"),
                               weights.get("w_gate2"), weights.get("w_noise2"), weights["w1"],
                               weights.get("b1"), weights.get("w3"), weights["w2"],
-                              weights.get("b2"))
+                              weights.get("b2"), weights.get("ws1"), weights.get("ws3"),
+                              weights.get("ws2"))
         size = moe_workspace_size(self.c)
         if size == 0:
             raise MoEError(MOE_ERR_INVALID_ARG, moe_last_error())
@@ -44,7 +46,7 @@ class MoELayer:
         if y is None:
             y = torch.empty((self.c.T, self.c.d_model), dtype=torch.float32, device=self.device)
         if losses is None:
-            losses = torch.empty(3, dtype=torch.float32, device=self.device)
+            losses = torch.empty(N_LOSSES, dtype=torch.float32, device=self.device)
         dg = make_diag(**diag) if diag else None
         moe_forward(self.c, self.w, x, noise, noise2, y, losses, dg, self.ws)
         return y, losses
@@ -52,7 +54,7 @@ class MoELayer:
 
 __all__ = ["workloads", "EXPORTS", "MoELayer", "MoEError", "MoeConfig", "MoeWeights", "MoeDiag",
            "make_config", "make_weights", "make_diag", "moe_workspace_size", "moe_gate",
-           "moe_gate_hier", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_aux_loss",
-           "moe_forward", "moe_status_string", "moe_last_error", "moe_profile_enable",
+           "moe_gate_hier", "moe_dispatch", "moe_expert_ffn", "moe_shared_ffn", "moe_combine",
+           "moe_aux_loss", "moe_router_bias_update", "moe_forward", "N_LOSSES", "moe_status_string", "moe_last_error", "moe_profile_enable",
            "moe_profile_collect", "moe_profile_entry", "MOE_OK", "MOE_ERR_INVALID_ARG",
            "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP"]

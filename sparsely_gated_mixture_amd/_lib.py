@@ -21,8 +21,11 @@ MOE_ERR_WORKSPACE = 3
 MOE_ERR_HIP = 4
 
 EXPORTS = ["moe_workspace_size", "moe_gate", "moe_gate_hier", "moe_dispatch", "moe_expert_ffn",
-           "moe_combine", "moe_aux_loss", "moe_forward", "moe_status_string", "moe_last_error",
-           "moe_profile_enable", "moe_profile_collect", "moe_profile_entry"]
+           "moe_shared_ffn", "moe_combine", "moe_aux_loss", "moe_router_bias_update",
+           "moe_forward", "moe_status_string", "moe_last_error", "moe_profile_enable",
+           "moe_profile_collect", "moe_profile_entry"]
+
+N_LOSSES = 5  # importance, load, Switch, router z-loss, -gate entropy
 
 
 class MoEError(RuntimeError):
@@ -37,7 +40,9 @@ class MoeConfig(ctypes.Structure):
                 ("act", ctypes.c_int32), ("expert_dtype", ctypes.c_int32),
                 ("n_groups", ctypes.c_int32), ("k_groups", ctypes.c_int32),
                 ("capacity_factor", ctypes.c_float), ("w_importance", ctypes.c_float),
-                ("w_load", ctypes.c_float), ("alpha_switch", ctypes.c_float)]
+                ("w_load", ctypes.c_float), ("alpha_switch", ctypes.c_float),
+                ("w_z", ctypes.c_float), ("w_entropy", ctypes.c_float),
+                ("d_hidden_shared", ctypes.c_int32)]
 
 
 _vp = ctypes.c_void_p
@@ -46,7 +51,7 @@ _vp = ctypes.c_void_p
 class MoeWeights(ctypes.Structure):
     _fields_ = [("w_gate", _vp), ("b_gate", _vp), ("w_noise", _vp), ("w_gate2", _vp),
                 ("w_noise2", _vp), ("w1", _vp), ("b1", _vp), ("w3", _vp), ("w2", _vp),
-                ("b2", _vp)]
+                ("b2", _vp), ("ws1", _vp), ("ws3", _vp), ("ws2", _vp)]
 
 
 class MoeDiag(ctypes.Structure):
@@ -72,12 +77,14 @@ def load_library():
     cfgp = ctypes.POINTER(MoeConfig)
     L.moe_workspace_size.argtypes = [cfgp]
     L.moe_workspace_size.restype = S
-    L.moe_gate.argtypes = [cfgp] + [P] * 9 + [P, S, P]
-    L.moe_gate_hier.argtypes = [cfgp] + [P] * 12 + [P, S, P]
+    L.moe_gate.argtypes = [cfgp] + [P] * 10 + [P, S, P]
+    L.moe_gate_hier.argtypes = [cfgp] + [P] * 13 + [P, S, P]
     L.moe_dispatch.argtypes = [cfgp] + [P] * 8 + [P, S, P]
     L.moe_expert_ffn.argtypes = [cfgp] + [P] * 8 + [P, S, P]
-    L.moe_combine.argtypes = [cfgp] + [P] * 4 + [P]
-    L.moe_aux_loss.argtypes = [cfgp] + [P] * 4 + [P]
+    L.moe_shared_ffn.argtypes = [cfgp] + [P] * 5 + [P, S, P]
+    L.moe_combine.argtypes = [cfgp] + [P] * 5 + [P]
+    L.moe_aux_loss.argtypes = [cfgp] + [P] * 5 + [P]
+    L.moe_router_bias_update.argtypes = [cfgp, P, P, ctypes.c_float, P]
     L.moe_forward.argtypes = [cfgp, ctypes.POINTER(MoeWeights)] + [P] * 5 + \
         [ctypes.POINTER(MoeDiag), P, S, P]
     L.moe_status_string.argtypes = [ctypes.c_int]
@@ -92,8 +99,8 @@ def load_library():
                                     ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(ctypes.c_longlong)]
     L.moe_profile_entry.restype = ctypes.c_int
-    for name in ("moe_gate", "moe_gate_hier", "moe_dispatch", "moe_expert_ffn", "moe_combine",
-                 "moe_aux_loss", "moe_forward"):
+    for name in ("moe_gate", "moe_gate_hier", "moe_dispatch", "moe_expert_ffn", "moe_shared_ffn",
+                 "moe_combine", "moe_aux_loss", "moe_router_bias_update", "moe_forward"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -107,7 +114,9 @@ def make_config(cfg) -> MoeConfig:
     return MoeConfig(int(cfg.T), int(cfg.d_model), int(cfg.d_hidden), int(cfg.n_experts),
                      int(cfg.k), int(cfg.gate), int(cfg.act), int(cfg.expert_dtype),
                      int(cfg.n_groups), int(cfg.k_groups), float(cfg.capacity_factor),
-                     float(cfg.w_importance), float(cfg.w_load), float(cfg.alpha_switch))
+                     float(cfg.w_importance), float(cfg.w_load), float(cfg.alpha_switch),
+                     float(getattr(cfg, "w_z", 1.0)), float(getattr(cfg, "w_entropy", 1.0)),
+                     int(getattr(cfg, "d_hidden_shared", 0)))
 
 
 def _ptr(t):
@@ -154,23 +163,24 @@ def moe_workspace_size(cfg) -> int:
     return load_library().moe_workspace_size(ctypes.byref(c))
 
 
-def moe_gate(cfg, x, w_gate, b_gate, w_noise, noise, topk_idx, topk_w, importance, load, ws,
-             stream=None):
+def moe_gate(cfg, x, w_gate, b_gate, w_noise, noise, topk_idx, topk_w, importance, load,
+             gate_stats, ws, stream=None):
     c = make_config(cfg)
     wp, wb = _ws(ws)
     _check(load_library().moe_gate(ctypes.byref(c), _ptr(x), _ptr(w_gate), _ptr(b_gate),
                                    _ptr(w_noise), _ptr(noise), _ptr(topk_idx), _ptr(topk_w),
-                                   _ptr(importance), _ptr(load), wp, wb, _stream(stream)))
+                                   _ptr(importance), _ptr(load), _ptr(gate_stats), wp, wb,
+                                   _stream(stream)))
 
 
 def moe_gate_hier(cfg, x, w_gate, b_gate, w_noise, noise, w_gate2, w_noise2, noise2, topk_idx,
-                  topk_w, importance, load, ws, stream=None):
+                  topk_w, importance, load, gate_stats, ws, stream=None):
     c = make_config(cfg)
     wp, wb = _ws(ws)
     _check(load_library().moe_gate_hier(
         ctypes.byref(c), _ptr(x), _ptr(w_gate), _ptr(b_gate), _ptr(w_noise), _ptr(noise),
         _ptr(w_gate2), _ptr(w_noise2), _ptr(noise2), _ptr(topk_idx), _ptr(topk_w),
-        _ptr(importance), _ptr(load), wp, wb, _stream(stream)))
+        _ptr(importance), _ptr(load), _ptr(gate_stats), wp, wb, _stream(stream)))
 
 
 def moe_dispatch(cfg, topk_idx, x, counts_pre, counts, offsets, perm, slot_pos, x_perm, ws,
@@ -191,22 +201,38 @@ def moe_expert_ffn(cfg, x_perm, offsets, w1, b1, w3, w2, b2, y_perm, ws, stream=
                                          wp, wb, _stream(stream)))
 
 
-def moe_combine(cfg, y_perm, slot_pos, topk_w, y, stream=None):
+def moe_shared_ffn(cfg, x, ws1, ws3, ws2, y_shared, ws, stream=None):
+    c = make_config(cfg)
+    wp, wb = _ws(ws)
+    _check(load_library().moe_shared_ffn(ctypes.byref(c), _ptr(x), _ptr(ws1), _ptr(ws3),
+                                         _ptr(ws2), _ptr(y_shared), wp, wb, _stream(stream)))
+
+
+def moe_combine(cfg, y_perm, slot_pos, topk_w, y_base, y, stream=None):
     c = make_config(cfg)
     _check(load_library().moe_combine(ctypes.byref(c), _ptr(y_perm), _ptr(slot_pos),
-                                      _ptr(topk_w), _ptr(y), _stream(stream)))
+                                      _ptr(topk_w), _ptr(y_base), _ptr(y), _stream(stream)))
 
 
-def moe_aux_loss(cfg, importance, load, counts_pre, losses, stream=None):
+def moe_aux_loss(cfg, importance, load, counts_pre, gate_stats, losses, stream=None):
     c = make_config(cfg)
     _check(load_library().moe_aux_loss(ctypes.byref(c), _ptr(importance), _ptr(load),
-                                       _ptr(counts_pre), _ptr(losses), _stream(stream)))
+                                       _ptr(counts_pre), _ptr(gate_stats), _ptr(losses),
+                                       _stream(stream)))
+
+
+def moe_router_bias_update(cfg, counts_pre, bias, gamma, stream=None):
+    c = make_config(cfg)
+    _check(load_library().moe_router_bias_update(ctypes.byref(c), _ptr(counts_pre), _ptr(bias),
+                                                 float(gamma), _stream(stream)))
 
 
 def make_weights(w_gate, b_gate=None, w_noise=None, w_gate2=None, w_noise2=None, w1=None,
-                 b1=None, w3=None, w2=None, b2=None) -> MoeWeights:
+                 b1=None, w3=None, w2=None, b2=None, ws1=None, ws3=None,
+                 ws2=None) -> MoeWeights:
     return MoeWeights(_ptr(w_gate), _ptr(b_gate), _ptr(w_noise), _ptr(w_gate2), _ptr(w_noise2),
-                      _ptr(w1), _ptr(b1), _ptr(w3), _ptr(w2), _ptr(b2))
+                      _ptr(w1), _ptr(b1), _ptr(w3), _ptr(w2), _ptr(b2), _ptr(ws1), _ptr(ws3),
+                      _ptr(ws2))
 
 
 def make_diag(**kw) -> MoeDiag:

@@ -72,7 +72,8 @@ moe_status validate(const moe_config* c) {
     return fail(MOE_ERR_INVALID_ARG, "k must be in [1, n_experts] (k=%d, n=%d)", c->k,
                 c->n_experts);
   if (c->k > kMaxK) return fail(MOE_ERR_UNSUPPORTED, "k must be <= %d", kMaxK);
-  if (c->gate != MOE_GATE_TOPK_SOFTMAX && c->gate != MOE_GATE_SWITCH_TOP1)
+  if (c->gate != MOE_GATE_TOPK_SOFTMAX && c->gate != MOE_GATE_SWITCH_TOP1 &&
+      c->gate != MOE_GATE_SIGMOID_BIAS)
     return fail(MOE_ERR_INVALID_ARG, "unknown gate kind %d", c->gate);
   if (c->act != MOE_ACT_RELU && c->act != MOE_ACT_SWIGLU)
     return fail(MOE_ERR_INVALID_ARG, "unknown activation %d", c->act);
@@ -84,6 +85,10 @@ moe_status validate(const moe_config* c) {
     return fail(MOE_ERR_UNSUPPORTED, "SwiGLU experts are implemented for bf16 only");
   if (!std::isfinite(c->capacity_factor))
     return fail(MOE_ERR_INVALID_ARG, "capacity_factor must be finite");
+  if (c->d_hidden_shared < 0 || c->d_hidden_shared % 8)
+    return fail(MOE_ERR_INVALID_ARG, "d_hidden_shared must be a non-negative multiple of 8");
+  if (c->d_hidden_shared > 0 && c->expert_dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "the shared expert is implemented for bf16 only");
   if (c->n_experts > kMaxExperts)
     return fail(MOE_ERR_UNSUPPORTED, "n_experts must be <= %d", kMaxExperts);
   if ((long long)c->T * c->k > (1LL << 30))
@@ -96,6 +101,8 @@ moe_status validate(const moe_config* c) {
                   c->n_experts, a);
     if (c->gate != MOE_GATE_TOPK_SOFTMAX)
       return fail(MOE_ERR_INVALID_ARG, "the two-level layer uses the top-k softmax gate");
+    if (c->d_hidden_shared > 0)
+      return fail(MOE_ERR_UNSUPPORTED, "the shared expert is implemented for flat layers");
     if (c->k_groups < 1 || c->k_groups > a || c->k % c->k_groups)
       return fail(MOE_ERR_INVALID_ARG, "k_groups must be in [1, n_groups] and divide k");
     const int b = c->n_experts / a, k2 = c->k / c->k_groups;
@@ -145,11 +152,12 @@ struct Region {
 struct Plan {
   // gate (flat or primary)
   int n_gate = 0, ldl = 0, gemm_bm = 128, rows_per_block = 16, nparts = 0;
-  Region logits, part_imp, part_load;
+  Region logits, part_imp, part_load, part_stats, prim_stats;
   // two-level extras
   int a = 0, b = 0, k1 = 0, k2 = 0, ldl2 = 0, max_tiles2 = 0;
   Region prim_idx, prim_w, prim_imp, prim_load, g_counts_pre, g_counts, g_offsets, g_perm,
-      g_slot, g_chunk_hist, g_chunk_base, t2_expert, t2_row0, t2_count, part2_imp, part2_load;
+      g_slot, g_chunk_hist, g_chunk_base, t2_expert, t2_row0, t2_count, part2_imp, part2_load,
+      part2_stats;
   // dispatch
   int nchunks = 0;
   Region chunk_hist, chunk_base;
@@ -159,7 +167,10 @@ struct Plan {
   size_t gate_bytes = 0, dispatch_bytes = 0, ffn_bytes = 0, stage_bytes = 0;
   // forward intermediates
   Region f_idx, f_w, f_imp, f_load, f_counts_pre, f_counts, f_offsets, f_perm, f_slot, f_xperm,
-      f_yperm, f_tile_expert, f_tile_row0, f_tile_count;
+      f_yperm, f_tile_expert, f_tile_row0, f_tile_count, f_stats;
+  // shared expert (d_hidden_shared > 0): bf16 copy of x, hidden, output, tile map
+  int sh_tiles = 0;
+  Region sh_xb, sh_hidden, sh_y, sh_te, sh_tr, sh_tc, sh_off;
   size_t total = 0;
 };
 
@@ -207,6 +218,8 @@ Plan make_plan(const moe_config& c) {
     p.logits = g.take(logit_elems * 4);
     p.part_imp = g.take((size_t)p.nparts * p.a * 4);
     p.part_load = g.take((size_t)p.nparts * p.a * 4);
+    p.part_stats = g.take((size_t)p.nparts * 2 * 4);
+    p.prim_stats = g.take(2 * 4);
     p.prim_idx = g.take(T * p.k1 * 4);
     p.prim_w = g.take(T * p.k1 * 4);
     p.prim_imp = g.take(p.a * 4);
@@ -224,10 +237,12 @@ Plan make_plan(const moe_config& c) {
     p.t2_count = g.take(4);
     p.part2_imp = g.take((size_t)p.max_tiles2 * p.b * 4);
     p.part2_load = g.take((size_t)p.max_tiles2 * p.b * 4);
+    p.part2_stats = g.take((size_t)p.max_tiles2 * 2 * 4);
   } else {
     p.logits = g.take(T * p.ldl * 4);
     p.part_imp = g.take((size_t)p.nparts * n * 4);
     p.part_load = g.take((size_t)p.nparts * n * 4);
+    p.part_stats = g.take((size_t)p.nparts * 2 * 4);
   }
   p.gate_bytes = g.at;
   // dispatch scratch
@@ -263,6 +278,18 @@ Plan make_plan(const moe_config& c) {
   p.f_tile_expert = w.take((size_t)p.max_mtiles * 4);
   p.f_tile_row0 = w.take((size_t)p.max_mtiles * 4);
   p.f_tile_count = w.take(4);
+  p.f_stats = w.take(2 * 4);
+  if (c.d_hidden_shared > 0) {
+    const long long hs = c.d_hidden_shared;
+    p.sh_tiles = (int)((T + kBf16BM - 1) / kBf16BM + 1);
+    p.sh_xb = w.take(std::max(1LL, T) * d * 2);
+    p.sh_hidden = w.take(std::max(1LL, T) * hs * 2);
+    p.sh_y = w.take(std::max(1LL, T) * d * 4);
+    p.sh_te = w.take((size_t)p.sh_tiles * 4);
+    p.sh_tr = w.take((size_t)p.sh_tiles * 4);
+    p.sh_tc = w.take(4);
+    p.sh_off = w.take(2 * 4);
+  }
   p.total = w.at;
   return p;
 }
@@ -287,8 +314,8 @@ moe_status check_ws(void* ws, size_t ws_bytes, size_t need_bytes, const char* wh
 // ---------------------------------------------------------------------------
 moe_status run_gate(const moe_config& c, const Plan& p, const float* x, const float* w_gate,
                     const float* b_gate, const float* w_noise, const float* noise,
-                    int32_t* topk_idx, float* topk_w, float* importance, float* load, void* ws,
-                    hipStream_t s) {
+                    int32_t* topk_idx, float* topk_w, float* importance, float* load,
+                    float* gate_stats, void* ws, hipStream_t s) {
   const int n = c.n_experts;
   const bool noisy = w_noise != nullptr;
   float* logits = at<float>(ws, p.logits);
@@ -313,6 +340,7 @@ moe_status run_gate(const moe_config& c, const Plan& p, const float* x, const fl
   t.n = n;
   t.k = c.k;
   t.switch_mode = c.gate == MOE_GATE_SWITCH_TOP1;
+  t.sigmoid_mode = c.gate == MOE_GATE_SIGMOID_BIAS;
   t.noisy = noisy;
   t.logits = logits;
   t.ldl = p.ldl;
@@ -322,10 +350,12 @@ moe_status run_gate(const moe_config& c, const Plan& p, const float* x, const fl
   t.topk_w = topk_w;
   t.part_imp = at<float>(ws, p.part_imp);
   t.part_load = noisy ? at<float>(ws, p.part_load) : nullptr;
+  t.part_stats = gate_stats ? at<float>(ws, p.part_stats) : nullptr;
   t.rows_per_block = p.rows_per_block;
   HIP_TRY(launch_topk(t, s));
-  HIP_TRY(launch_colsum(t.part_imp, p.nparts, n, importance, noisy ? t.part_load : nullptr,
-                        load, s));
+  HIP_TRY(launch_colsum(p.nparts, ColsumVec{t.part_imp, n, importance},
+                        ColsumVec{t.part_load, n, load}, ColsumVec{t.part_stats, 2, gate_stats},
+                        s));
   return MOE_OK;
 }
 
@@ -333,7 +363,7 @@ moe_status run_gate_hier(const moe_config& c, const Plan& p, const float* x, con
                          const float* b_gate, const float* w_noise, const float* noise,
                          const float* w_gate2, const float* w_noise2, const float* noise2,
                          int32_t* topk_idx, float* topk_w, float* importance, float* load,
-                         void* ws, hipStream_t s) {
+                         float* gate_stats, void* ws, hipStream_t s) {
   const bool noisy = w_noise != nullptr;
   const int a = p.a, b = p.b, k1 = p.k1;
   float* logits = at<float>(ws, p.logits);
@@ -369,10 +399,12 @@ moe_status run_gate_hier(const moe_config& c, const Plan& p, const float* x, con
   t.topk_w = prim_w;
   t.part_imp = at<float>(ws, p.part_imp);
   t.part_load = noisy ? at<float>(ws, p.part_load) : nullptr;
+  t.part_stats = gate_stats ? at<float>(ws, p.part_stats) : nullptr;
   t.rows_per_block = p.rows_per_block;
   HIP_TRY(launch_topk(t, s));
-  HIP_TRY(launch_colsum(t.part_imp, p.nparts, a, at<float>(ws, p.prim_imp),
-                        noisy ? t.part_load : nullptr, at<float>(ws, p.prim_load), s));
+  HIP_TRY(launch_colsum(p.nparts, ColsumVec{t.part_imp, a, at<float>(ws, p.prim_imp)},
+                        ColsumVec{t.part_load, a, at<float>(ws, p.prim_load)},
+                        ColsumVec{t.part_stats, 2, at<float>(ws, p.prim_stats)}, s));
   // 2. rows of each group (tokens ascending)
   int32_t* g_counts_pre = at<int32_t>(ws, p.g_counts_pre);
   int32_t* g_offsets = at<int32_t>(ws, p.g_offsets);
@@ -434,6 +466,7 @@ moe_status run_gate_hier(const moe_config& c, const Plan& p, const float* x, con
   u.topk_w = topk_w;
   u.part_imp = at<float>(ws, p.part2_imp);
   u.part_load = u.noisy ? at<float>(ws, p.part2_load) : nullptr;
+  u.part_stats = gate_stats ? at<float>(ws, p.part2_stats) : nullptr;
   u.row_token = g_perm;
   u.prim_idx = prim_idx;
   u.prim_w = prim_w;
@@ -450,6 +483,8 @@ moe_status run_gate_hier(const moe_config& c, const Plan& p, const float* x, con
   HIP_TRY(launch_hier_finalize(u.part_imp, both_noisy ? u.part_load : nullptr, t2e, t2c,
                                g_counts_pre, at<float>(ws, p.prim_load), a, b, importance,
                                both_noisy ? load : nullptr, s));
+  if (gate_stats)
+    HIP_TRY(launch_hier_stats(at<float>(ws, p.prim_stats), u.part_stats, t2c, gate_stats, s));
   return MOE_OK;
 }
 
@@ -462,6 +497,8 @@ struct ForwardExtras {
   float* losses = nullptr;
   const float* importance = nullptr;
   const float* load = nullptr;
+  const float* gate_stats = nullptr;
+  uint16_t* x_bf16 = nullptr;  // the shared expert's input, written by the gather
 };
 
 moe_status run_dispatch(const moe_config& c, const Plan& p, const int32_t* topk_idx,
@@ -489,12 +526,16 @@ moe_status run_dispatch(const moe_config& c, const Plan& p, const int32_t* topk_
     da.losses = fx->losses;
     da.importance = fx->importance;
     da.load = fx->load;
+    da.gate_stats = fx->gate_stats;
     da.w_imp = c.w_importance;
     da.w_load = c.w_load;
     da.alpha = c.alpha_switch;
+    da.w_z = c.w_z;
+    da.w_ent = c.w_entropy;
   }
   HIP_TRY(launch_dispatch(da, s));
-  HIP_TRY(launch_gather(x, slot_pos, c.T, c.k, c.d_model, c.expert_dtype == MOE_BF16, x_perm, s));
+  HIP_TRY(launch_gather(x, slot_pos, c.T, c.k, c.d_model, c.expert_dtype == MOE_BF16, x_perm,
+                        fx ? fx->x_bf16 : nullptr, s));
   return MOE_OK;
 }
 
@@ -579,6 +620,59 @@ moe_status run_ffn(const moe_config& c, const Plan& p, const void* x_perm,
   return MOE_OK;
 }
 
+// The shared expert over all T rows of x_bf16: a one-segment tile map, then
+// the same grouped GEMMs as the routed experts.
+moe_status run_shared_ffn(const moe_config& c, const Plan& p, const uint16_t* xb,
+                          const void* ws1, const void* ws3, const void* ws2, float* y_shared,
+                          void* ws, hipStream_t s) {
+  if (c.T == 0) return MOE_OK;
+  const int d = c.d_model, hs = c.d_hidden_shared;
+  int32_t* off = at<int32_t>(ws, p.sh_off);
+  int32_t* te = at<int32_t>(ws, p.sh_te);
+  int32_t* tr = at<int32_t>(ws, p.sh_tr);
+  int32_t* tc = at<int32_t>(ws, p.sh_tc);
+  uint16_t* hidden = at<uint16_t>(ws, p.sh_hidden);
+  HIP_TRY(launch_shared_tilemap(c.T, kBf16BM, off, te, tr, tc, s));
+  GemmBf16Args g{};
+  g.A = xb;
+  g.lda = d;
+  g.B1 = (const uint16_t*)ws1;
+  g.B3 = (const uint16_t*)ws3;
+  g.strideB = 0;
+  g.N = hs;
+  g.K = d;
+  g.C = hidden;
+  g.ldc = hs;
+  g.tile_expert = te;
+  g.tile_row0 = tr;
+  g.offsets = off;
+  g.tile_count = tc;
+  g.max_mtiles = p.sh_tiles;
+  g.num_cus = device_cus();
+  g.shared = 1;
+  HIP_TRY(launch_gemm_bf16(g, c.act == MOE_ACT_SWIGLU ? EPI_SWIGLU_BF16 : EPI_RELU_BF16, s));
+  GemmBf16Args g2 = g;
+  g2.A = hidden;
+  g2.lda = hs;
+  g2.B1 = (const uint16_t*)ws2;
+  g2.B3 = nullptr;
+  g2.N = d;
+  g2.K = hs;
+  g2.C = y_shared;
+  g2.ldc = d;
+  HIP_TRY(launch_gemm_bf16(g2, EPI_IDENT_F32, s));
+  return MOE_OK;
+}
+
+moe_status check_shared_ptrs(const moe_config& c, const void* ws1, const void* ws3,
+                             const void* ws2) {
+  CHECK(need(ws1, "ws1 (shared expert)"));
+  CHECK(need(ws2, "ws2 (shared expert)"));
+  if (c.act == MOE_ACT_SWIGLU) CHECK(need(ws3, "ws3 (shared SwiGLU expert)"));
+  else CHECK(optional(ws3, "ws3"));
+  return MOE_OK;
+}
+
 moe_status check_gate_ptrs(const moe_config& c, const float* x, const float* w_gate,
                            const float* b_gate, const float* w_noise, const float* noise) {
   CHECK(need(x, "x", c.T == 0));
@@ -588,6 +682,8 @@ moe_status check_gate_ptrs(const moe_config& c, const float* x, const float* w_g
   if (w_noise) CHECK(need(noise, "noise (required with w_noise)", c.T == 0));
   if (w_noise && c.gate == MOE_GATE_SWITCH_TOP1)
     return fail(MOE_ERR_INVALID_ARG, "the Switch router is noiseless (w_noise must be NULL)");
+  if (w_noise && c.gate == MOE_GATE_SIGMOID_BIAS)
+    return fail(MOE_ERR_INVALID_ARG, "the sigmoid gate is noiseless (w_noise must be NULL)");
   return MOE_OK;
 }
 
@@ -602,8 +698,8 @@ size_t moe_workspace_size(const moe_config* cfg) {
 
 moe_status moe_gate(const moe_config* cfg, const float* x, const float* w_gate,
                     const float* b_gate, const float* w_noise, const float* noise,
-                    int32_t* topk_idx, float* topk_w, float* importance, float* load, void* ws,
-                    size_t ws_bytes, void* stream) {
+                    int32_t* topk_idx, float* topk_w, float* importance, float* load,
+                    float* gate_stats, void* ws, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   CHECK(validate(cfg));
   const moe_config& c = *cfg;
@@ -613,17 +709,18 @@ moe_status moe_gate(const moe_config* cfg, const float* x, const float* w_gate,
   CHECK(need(topk_w, "topk_w", c.T == 0));
   CHECK(need(importance, "importance"));
   if (w_noise) CHECK(need(load, "load (required for a noisy gate)"));
+  CHECK(optional(gate_stats, "gate_stats"));
   const Plan p = make_plan(c);
   CHECK(check_ws(ws, ws_bytes, p.gate_bytes, "moe_gate"));
-  return run_gate(c, p, x, w_gate, b_gate, w_noise, noise, topk_idx, topk_w, importance, load, ws,
-                  (hipStream_t)stream);
+  return run_gate(c, p, x, w_gate, b_gate, w_noise, noise, topk_idx, topk_w, importance, load,
+                  gate_stats, ws, (hipStream_t)stream);
 }
 
 moe_status moe_gate_hier(const moe_config* cfg, const float* x, const float* w_gate,
                          const float* b_gate, const float* w_noise, const float* noise,
                          const float* w_gate2, const float* w_noise2, const float* noise2,
                          int32_t* topk_idx, float* topk_w, float* importance, float* load,
-                         void* ws, size_t ws_bytes, void* stream) {
+                         float* gate_stats, void* ws, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   CHECK(validate(cfg));
   const moe_config& c = *cfg;
@@ -636,10 +733,11 @@ moe_status moe_gate_hier(const moe_config* cfg, const float* x, const float* w_g
   CHECK(need(topk_w, "topk_w", c.T == 0));
   CHECK(need(importance, "importance"));
   if (w_noise && w_noise2) CHECK(need(load, "load (required for noisy gates)"));
+  CHECK(optional(gate_stats, "gate_stats"));
   const Plan p = make_plan(c);
   CHECK(check_ws(ws, ws_bytes, p.gate_bytes, "moe_gate_hier"));
   return run_gate_hier(c, p, x, w_gate, b_gate, w_noise, noise, w_gate2, w_noise2, noise2,
-                       topk_idx, topk_w, importance, load, ws, (hipStream_t)stream);
+                       topk_idx, topk_w, importance, load, gate_stats, ws, (hipStream_t)stream);
 }
 
 moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, const float* x,
@@ -688,30 +786,67 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32
   return run_ffn(c, p, x_perm, offsets, w1, b1, w3, w2, b2, y_perm, ws, (hipStream_t)stream);
 }
 
+moe_status moe_shared_ffn(const moe_config* cfg, const float* x, const void* ws1,
+                          const void* ws3, const void* ws2, float* y_shared, void* ws,
+                          size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  CHECK(validate(cfg));
+  const moe_config& c = *cfg;
+  if (c.d_hidden_shared <= 0)
+    return fail(MOE_ERR_INVALID_ARG, "moe_shared_ffn needs d_hidden_shared > 0");
+  CHECK(need(x, "x", c.T == 0));
+  CHECK(check_shared_ptrs(c, ws1, ws3, ws2));
+  CHECK(need(y_shared, "y_shared", c.T == 0));
+  const Plan p = make_plan(c);
+  CHECK(check_ws(ws, ws_bytes, p.total, "moe_shared_ffn"));
+  hipStream_t s = (hipStream_t)stream;
+  uint16_t* xb = at<uint16_t>(ws, p.sh_xb);
+  HIP_TRY(launch_to_bf16(x, (long long)c.T * c.d_model, xb, s));
+  return run_shared_ffn(c, p, xb, ws1, ws3, ws2, y_shared, ws, s);
+}
+
 moe_status moe_combine(const moe_config* cfg, const float* y_perm, const int32_t* slot_pos,
-                       const float* topk_w, float* y, void* stream) {
+                       const float* topk_w, const float* y_base, float* y, void* stream) {
   g_err[0] = 0;
   CHECK(validate(cfg));
   const moe_config& c = *cfg;
   CHECK(need(y_perm, "y_perm", c.T == 0));
   CHECK(need(slot_pos, "slot_pos", c.T == 0));
   CHECK(need(topk_w, "topk_w", c.T == 0));
+  CHECK(optional(y_base, "y_base"));
   CHECK(need(y, "y", c.T == 0));
-  HIP_TRY(launch_combine(y_perm, slot_pos, topk_w, c.T, c.k, c.d_model, y, (hipStream_t)stream));
+  HIP_TRY(launch_combine(y_perm, slot_pos, topk_w, y_base, c.T, c.k, c.d_model, y,
+                         (hipStream_t)stream));
   return MOE_OK;
 }
 
 moe_status moe_aux_loss(const moe_config* cfg, const float* importance, const float* load,
-                        const int32_t* counts_pre, float* losses, void* stream) {
+                        const int32_t* counts_pre, const float* gate_stats, float* losses,
+                        void* stream) {
   g_err[0] = 0;
   CHECK(validate(cfg));
   const moe_config& c = *cfg;
   CHECK(need(importance, "importance"));
   CHECK(optional(load, "load"));
   CHECK(need(counts_pre, "counts_pre"));
+  CHECK(optional(gate_stats, "gate_stats"));
   CHECK(need(losses, "losses"));
-  HIP_TRY(launch_aux(importance, load, counts_pre, c.T, c.k, c.n_experts, c.w_importance,
-                     c.w_load, c.alpha_switch, losses, (hipStream_t)stream));
+  HIP_TRY(launch_aux(importance, load, counts_pre, gate_stats, c.T, c.k, c.n_experts,
+                     c.w_importance, c.w_load, c.alpha_switch, c.w_z, c.w_entropy, losses,
+                     (hipStream_t)stream));
+  return MOE_OK;
+}
+
+moe_status moe_router_bias_update(const moe_config* cfg, const int32_t* counts_pre, float* bias,
+                                  float gamma, void* stream) {
+  g_err[0] = 0;
+  CHECK(validate(cfg));
+  const moe_config& c = *cfg;
+  if (!std::isfinite(gamma)) return fail(MOE_ERR_INVALID_ARG, "gamma must be finite");
+  CHECK(need(counts_pre, "counts_pre"));
+  CHECK(need(bias, "bias"));
+  HIP_TRY(launch_bias_update(counts_pre, c.n_experts, c.T, c.k, gamma, bias,
+                             (hipStream_t)stream));
   return MOE_OK;
 }
 
@@ -737,6 +872,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const float
   }
   CHECK(optional(wt->b1, "weights->b1"));
   CHECK(optional(wt->b2, "weights->b2"));
+  if (c.d_hidden_shared > 0) CHECK(check_shared_ptrs(c, wt->ws1, wt->ws3, wt->ws2));
   CHECK(need(y, "y", c.T == 0));
   CHECK(need(losses, "losses"));
   moe_diag dg{};
@@ -767,12 +903,15 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const float
   void* xperm = at<void>(ws, p.f_xperm);
   float* yperm = at<float>(ws, p.f_yperm);
   const bool has_load = hier ? (wt->w_noise && wt->w_noise2) : (wt->w_noise != nullptr);
+  float* stats = at<float>(ws, p.f_stats);
   if (hier) {
     CHECK(run_gate_hier(c, p, x, wt->w_gate, wt->b_gate, wt->w_noise, noise, wt->w_gate2,
-                        wt->w_noise2, noise2, idx, w, imp, ld, ws, s));
+                        wt->w_noise2, noise2, idx, w, imp, ld, stats, ws, s));
   } else {
-    CHECK(run_gate(c, p, x, wt->w_gate, wt->b_gate, wt->w_noise, noise, idx, w, imp, ld, ws, s));
+    CHECK(run_gate(c, p, x, wt->w_gate, wt->b_gate, wt->w_noise, noise, idx, w, imp, ld, stats,
+                   ws, s));
   }
+  const bool shared = c.d_hidden_shared > 0;
   ForwardExtras fx;
   fx.tile_expert = at<int32_t>(ws, p.f_tile_expert);
   fx.tile_row0 = at<int32_t>(ws, p.f_tile_row0);
@@ -780,9 +919,13 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const float
   fx.losses = losses;
   fx.importance = imp;
   fx.load = has_load ? ld : nullptr;
+  fx.gate_stats = stats;
+  fx.x_bf16 = shared ? at<uint16_t>(ws, p.sh_xb) : nullptr;
   CHECK(run_dispatch(c, p, idx, x, counts_pre, counts, offsets, perm, slot, xperm, ws, s, &fx));
   CHECK(run_ffn(c, p, xperm, offsets, wt->w1, wt->b1, wt->w3, wt->w2, wt->b2, yperm, ws, s, &fx));
-  HIP_TRY(launch_combine(yperm, slot, w, c.T, c.k, c.d_model, y, s));
+  float* ysh = shared ? at<float>(ws, p.sh_y) : nullptr;
+  if (shared) CHECK(run_shared_ffn(c, p, fx.x_bf16, wt->ws1, wt->ws3, wt->ws2, ysh, ws, s));
+  HIP_TRY(launch_combine(yperm, slot, w, ysh, c.T, c.k, c.d_model, y, s));
   return MOE_OK;
 }
 

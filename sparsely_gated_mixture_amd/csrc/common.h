@@ -155,11 +155,15 @@ __device__ double block_cv2(const float* v, int n, double* sh) {
 
 // losses[0] = w_imp * CV(importance)^2, losses[1] = w_load * CV(load)^2 (0
 // without load), losses[2] = alpha * n * sum_i f_i P_i with f_i =
-// counts_pre[i]/(T*k) and P_i = importance[i]/T (MoE survey, tufusi.com 3.2).
+// counts_pre[i]/(T*k) and P_i = importance[i]/T (MoE survey, tufusi.com 3.2);
+// losses[3] = w_z * stats[0] / T (router z-loss: mean squared norm of the
+// pre-softmax logits) and losses[4] = -w_ent * stats[1] / T (minus the mean
+// gate entropy), both 0 without stats or tokens (wkbse.com, part 2).
 template <int NT>
 __device__ void block_aux_losses(const float* importance, const float* load,
-                                 const int32_t* counts_pre, int T, int k, int n, float w_imp,
-                                 float w_load, float alpha, float* losses, double* sh) {
+                                 const int32_t* counts_pre, const float* stats, int T, int k,
+                                 int n, float w_imp, float w_load, float alpha, float w_z,
+                                 float w_ent, float* losses, double* sh) {
   const double li = (double)w_imp * block_cv2<NT>(importance, n, sh);
   const double ll = load ? (double)w_load * block_cv2<NT>(load, n, sh) : 0.0;
   double fp = 0.0;
@@ -172,6 +176,9 @@ __device__ void block_aux_losses(const float* importance, const float* load,
     losses[0] = (float)li;
     losses[1] = (float)ll;
     losses[2] = (float)sw;
+    const bool st = stats && T > 0;
+    losses[3] = st ? (float)((double)w_z * (double)stats[0] / T) : 0.f;
+    losses[4] = st ? (float)(-(double)w_ent * (double)stats[1] / T) : 0.f;
   }
 }
 

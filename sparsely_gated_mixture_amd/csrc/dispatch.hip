@@ -19,6 +19,8 @@
 //      independent of scheduling.
 //   5. gather_kernel: one wavefront per token reads its row once and writes
 //      it to each kept slot's row, converted to bf16 (RNE) or copied as fp32.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -112,8 +114,8 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(const DispatchArg
     if (threadIdx.x == kFinThreads - 1) *a.tile_count = tc.y;
   }
   if (a.losses)
-    block_aux_losses<kFinThreads>(a.importance, a.load, a.counts_pre, a.T, a.k, n, a.w_imp,
-                                  a.w_load, a.alpha, a.losses, sd);
+    block_aux_losses<kFinThreads>(a.importance, a.load, a.counts_pre, a.gate_stats, a.T, a.k, n,
+                                  a.w_imp, a.w_load, a.alpha, a.w_z, a.w_ent, a.losses, sd);
 }
 
 // One wavefront per chunk.
@@ -170,7 +172,8 @@ __global__ __launch_bounds__(64) void permute_kernel(const int32_t* __restrict__
 __global__ __launch_bounds__(256) void gather_kernel(const float* __restrict__ x,
                                                      const int32_t* __restrict__ slot_pos, int T,
                                                      int k, int d, int bf16_out,
-                                                     void* __restrict__ out) {
+                                                     void* __restrict__ out,
+                                                     uint16_t* __restrict__ x_bf16) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -180,12 +183,13 @@ __global__ __launch_bounds__(256) void gather_kernel(const float* __restrict__ x
     const f32x4 v0 = *(const f32x4*)(src + c);
     const f32x4 v1 = *(const f32x4*)(src + c + 4);
     uint4 pk = make_uint4(0u, 0u, 0u, 0u);
-    if (bf16_out) {
+    if (bf16_out || x_bf16) {
       pk.x = (uint32_t)f32_to_bf16(v0[0]) | ((uint32_t)f32_to_bf16(v0[1]) << 16);
       pk.y = (uint32_t)f32_to_bf16(v0[2]) | ((uint32_t)f32_to_bf16(v0[3]) << 16);
       pk.z = (uint32_t)f32_to_bf16(v1[0]) | ((uint32_t)f32_to_bf16(v1[1]) << 16);
       pk.w = (uint32_t)f32_to_bf16(v1[2]) | ((uint32_t)f32_to_bf16(v1[3]) << 16);
     }
+    if (x_bf16) *(uint4*)(x_bf16 + (long long)t * d + c) = pk;
     for (int s = 0; s < k; ++s) {
       const int row = sp[s];
       if (row < 0) continue;
@@ -198,6 +202,52 @@ __global__ __launch_bounds__(256) void gather_kernel(const float* __restrict__ x
       }
     }
   }
+}
+
+// out[i] = bf16(x[i]), 8 elements per thread (elems is a multiple of 8).
+__global__ __launch_bounds__(256) void to_bf16_kernel(const float* __restrict__ x, long long n8,
+                                                      uint16_t* __restrict__ out) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n8;
+       i += (long long)gridDim.x * 256) {
+    const f32x4 v0 = *(const f32x4*)(x + i * 8);
+    const f32x4 v1 = *(const f32x4*)(x + i * 8 + 4);
+    uint4 pk;
+    pk.x = (uint32_t)f32_to_bf16(v0[0]) | ((uint32_t)f32_to_bf16(v0[1]) << 16);
+    pk.y = (uint32_t)f32_to_bf16(v0[2]) | ((uint32_t)f32_to_bf16(v0[3]) << 16);
+    pk.z = (uint32_t)f32_to_bf16(v1[0]) | ((uint32_t)f32_to_bf16(v1[1]) << 16);
+    pk.w = (uint32_t)f32_to_bf16(v1[2]) | ((uint32_t)f32_to_bf16(v1[3]) << 16);
+    *(uint4*)(out + i * 8) = pk;
+  }
+}
+
+// One segment of T rows: offsets2 = {0, T} and its M-tiles.
+__global__ __launch_bounds__(256) void shared_tilemap_kernel(int T, int bm,
+                                                             int32_t* __restrict__ offsets2,
+                                                             int32_t* __restrict__ tile_expert,
+                                                             int32_t* __restrict__ tile_row0,
+                                                             int32_t* __restrict__ tile_count) {
+  const int nt = (T + bm - 1) / bm;
+  for (int t = threadIdx.x; t < nt; t += 256) {
+    tile_expert[t] = 0;
+    tile_row0[t] = t * bm;
+  }
+  if (threadIdx.x == 0) {
+    offsets2[0] = 0;
+    offsets2[1] = T;
+    *tile_count = nt;
+  }
+}
+
+// One thread per expert.  counts_pre[i] * n against T * k compares the
+// count with the even share T*k/n exactly.
+__global__ __launch_bounds__(256) void bias_update_kernel(const int32_t* __restrict__ counts_pre,
+                                                          int n, long long tk, float gamma,
+                                                          float* __restrict__ bias) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const long long c = (long long)counts_pre[i] * n;
+  if (c > tk) bias[i] = bias[i] - gamma;
+  else if (c < tk) bias[i] = bias[i] + gamma;
 }
 
 // Single block: M-tiles of every expert segment, in expert order.
@@ -271,10 +321,37 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_gather(const float* x, const int32_t* slot_pos, int T, int k, int d,
-                         int bf16_out, void* x_perm, hipStream_t s) {
+                         int bf16_out, void* x_perm, uint16_t* x_bf16, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   ProfScope ps("dispatch_gather", s);
-  gather_kernel<<<dim3((T + 3) / 4), dim3(256), 0, s>>>(x, slot_pos, T, k, d, bf16_out, x_perm);
+  gather_kernel<<<dim3((T + 3) / 4), dim3(256), 0, s>>>(x, slot_pos, T, k, d, bf16_out, x_perm,
+                                                        x_bf16);
+  return hipGetLastError();
+}
+
+hipError_t launch_to_bf16(const float* x, long long elems, uint16_t* out, hipStream_t s) {
+  const long long n8 = elems / 8;
+  if (n8 <= 0) return hipSuccess;
+  ProfScope ps("to_bf16", s);
+  const long long blocks = std::min<long long>((n8 + 255) / 256, 4096);
+  to_bf16_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(x, n8, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_shared_tilemap(int T, int bm, int32_t* offsets2, int32_t* tile_expert,
+                                 int32_t* tile_row0, int32_t* tile_count, hipStream_t s) {
+  ProfScope ps("shared_tilemap", s);
+  shared_tilemap_kernel<<<dim3(1), dim3(256), 0, s>>>(T, bm, offsets2, tile_expert, tile_row0,
+                                                      tile_count);
+  return hipGetLastError();
+}
+
+hipError_t launch_bias_update(const int32_t* counts_pre, int n, int T, int k, float gamma,
+                              float* bias, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  ProfScope ps("bias_update", s);
+  bias_update_kernel<<<dim3((n + 255) / 256), dim3(256), 0, s>>>(counts_pre, n,
+                                                                 (long long)T * k, gamma, bias);
   return hipGetLastError();
 }
 

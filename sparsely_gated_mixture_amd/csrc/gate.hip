@@ -8,13 +8,17 @@
 // then KeepTopK by k+1 rounds of a wave-wide arg-max (DPP max of the ordered
 // float keys, then a ballot for the lowest index holding the maximum: larger
 // H first, lower index first on equal H), the softmax over the kept values
-// (or the Switch full softmax),
-// and the per-expert sums behind the auxiliary losses:
+// (or the Switch full softmax, or the sigmoid gate's renormalised
+// affinities), and the per-expert sums behind the auxiliary losses:
 //   Importance_j += G_j,  Load_j += Phi((clean_j - thr_j) / Softplus(raw_j)),
-// thr_j = H_(k+1) if j is kept, H_(k) otherwise.
+// thr_j = H_(k+1) if j is kept, H_(k) otherwise; per block also the sum of
+// the squared pre-softmax logits (router z-loss) and of the gate
+// distributions' entropies.
 // Definitions: arXiv 1701.06538 summary (xyznot.com), "Method and key
 // formulas": Noisy Top-K gating and the load-balancing losses; Switch router:
-// MoE survey (tufusi.com) section 3.1.
+// MoE survey (tufusi.com) section 3.1; sigmoid gate with a selection-only
+// bias: same survey, sections 6.2 and 6.3; z-loss and gate entropy: wkbse.com
+// MoE introduction, part 2.
 //
 // Sums are deterministic: each lane owns fixed experts (j = lane + 64q) and
 // accumulates its rows in order; waves are combined in LDS in a fixed order;
@@ -114,6 +118,7 @@ __global__ __launch_bounds__(NW * 64) void topk_kernel(const TopkArgs p) {
     }
   };
 
+  float zacc = 0.f, eacc = 0.f;  // this wave's z-loss and entropy sums
   float imp[NPL], ld[NPL], bias[NPL];
 #pragma unroll
   for (int q = 0; q < NPL; ++q) {
@@ -146,6 +151,17 @@ __global__ __launch_bounds__(NW * 64) void topk_kernel(const TopkArgs p) {
         hv[q] = cl[q] + cur.z[q] * sp[q];
       }
       key[q] = ok ? ordered_key(hv[q]) : 0u;
+    }
+    // Router z-loss statistic: the logits the softmax sees (the sigmoid
+    // gate's are the bias-free network logits).
+    {
+      float zl = 0.f;
+#pragma unroll
+      for (int q = 0; q < NPL; ++q) {
+        const float v = p.sigmoid_mode ? cur.c[q] : hv[q];
+        if (lane + 64 * q < n) zl = fmaf(v, v, zl);
+      }
+      zacc += wave_sum_dpp(zl);
     }
 
     // k+1 rounds of arg-max: the largest key wins; among equal keys the
@@ -194,6 +210,18 @@ __global__ __launch_bounds__(NW * 64) void topk_kernel(const TopkArgs p) {
         if (lane + 64 * q < n) ls += expf(hv[q] - v0);
       zsum = wave_sum_dpp(ls);
       w = (lane < k) ? expf(my_v - v0) / zsum : 0.f;
+    } else if (p.sigmoid_mode) {
+      // s = Sigmoid(h) of the kept expert's bias-free logit, fetched from the
+      // lane that owns it; weights s / sum of the kept s.
+      float hsel = 0.f;
+#pragma unroll
+      for (int q = 0; q < NPL; ++q) {
+        const float t = __shfl(cur.c[q], my_j & 63, kWave);
+        if (q == (my_j >> 6)) hsel = t;
+      }
+      const float sg = (lane < k) ? hw_rcp(1.f + hw_exp(-hsel)) : 0.f;
+      zsum = wave_sum_dpp(sg);
+      w = sg * hw_rcp(zsum);
     } else {
       const float e = (lane < k) ? expf(my_v - v0) : 0.f;
       zsum = wave_sum_dpp(e);
@@ -204,12 +232,25 @@ __global__ __launch_bounds__(NW * 64) void topk_kernel(const TopkArgs p) {
       p.topk_w[out_base + lane] = wprim * w;
     }
 
-    // Importance: the dense gate vector (Switch: the full softmax).
+    // Importance: the dense gate vector (Switch: the full softmax).  Entropy
+    // of the gate distribution: Switch -sum p ln p = ln Z - sum p (H - H_max);
+    // otherwise over the kept weights (times the primary weight in the
+    // two-level secondary gate, which makes the rows of a token add up to the
+    // entropy of the product distribution).
     if (p.switch_mode) {
+      float pe = 0.f;
 #pragma unroll
       for (int q = 0; q < NPL; ++q)
-        if (lane + 64 * q < n) imp[q] += expf(hv[q] - v0) / zsum;
+        if (lane + 64 * q < n) {
+          const float dl = hv[q] - v0;
+          const float pj = expf(dl) / zsum;
+          imp[q] += pj;
+          pe = fmaf(pj, dl, pe);
+        }
+      eacc += hw_log(zsum) - wave_sum_dpp(pe);
     } else {
+      const float W = wprim * w;
+      eacc += wave_sum_dpp((lane < k && W > 0.f) ? -W * hw_log(W) : 0.f);
       for (int s = 0; s < k; ++s) {
         const int js = readlane_i(my_j, s);
         const float ws = readlane_f(w, s) * wprim;
@@ -235,6 +276,19 @@ __global__ __launch_bounds__(NW * 64) void topk_kernel(const TopkArgs p) {
   }
 
   // Combine the waves in a fixed order, then write this block's partials.
+  if (p.part_stats) {
+    __shared__ float st[2][NW];
+    if (lane == 0) {
+      st[0][wave] = zacc;
+      st[1][wave] = eacc;
+    }
+    __syncthreads();
+    if (threadIdx.x < 2) {
+      float a = 0.f;
+      for (int w2 = 0; w2 < NW; ++w2) a += st[threadIdx.x][w2];
+      p.part_stats[(long long)part * 2 + threadIdx.x] = a;
+    }
+  }
   for (int pass = 0; pass < 2; ++pass) {
     float* out = pass == 0 ? p.part_imp : p.part_load;
     if (!out) break;
@@ -258,14 +312,15 @@ __global__ __launch_bounds__(NW * 64) void topk_kernel(const TopkArgs p) {
 // many loads in flight), then lane sums are added in lane order: the same
 // order on every call.
 constexpr int kColLanes = 16;
-// blockIdx.y selects the vector: 0 = (part, out), 1 = (part2, out2).
-__global__ __launch_bounds__(1024) void colsum_kernel(const float* __restrict__ part0, int nparts,
-                                                      int n, float* __restrict__ out0,
-                                                      const float* __restrict__ part1,
-                                                      float* __restrict__ out1) {
+// blockIdx.y selects the vector.
+struct ColsumArgs {
+  ColsumVec v[3];
+};
+__global__ __launch_bounds__(1024) void colsum_kernel(const ColsumArgs a, int nparts) {
   __shared__ double sh[kColLanes][64];
-  const float* part = blockIdx.y ? part1 : part0;
-  float* out = blockIdx.y ? out1 : out0;
+  const float* part = a.v[blockIdx.y].part;
+  float* out = a.v[blockIdx.y].out;
+  const int n = a.v[blockIdx.y].n;
   const int c = threadIdx.x & 63, q = threadIdx.x >> 6;
   const int j = blockIdx.x * 64 + c;
   double s = 0.0;
@@ -279,6 +334,27 @@ __global__ __launch_bounds__(1024) void colsum_kernel(const float* __restrict__ 
     double t = 0.0;
     for (int r = 0; r < kColLanes; ++r) t += sh[r][c];
     out[j] = (float)t;
+  }
+}
+
+// One block: the secondary tiles' statistics in tile order, plus the
+// primary gate's z statistic.
+__global__ __launch_bounds__(256) void hier_stats_kernel(const float* __restrict__ prim,
+                                                         const float* __restrict__ part,
+                                                         const int32_t* __restrict__ tile_count,
+                                                         float* __restrict__ out) {
+  __shared__ double sh[4];
+  const int nt = *tile_count;
+  double z = 0.0, e = 0.0;
+  for (int t = threadIdx.x; t < nt; t += 256) {
+    z += (double)part[2 * t];
+    e += (double)part[2 * t + 1];
+  }
+  z = block_sum<256>(z, sh);
+  e = block_sum<256>(e, sh);
+  if (threadIdx.x == 0) {
+    out[0] = (float)((double)prim[0] + z);
+    out[1] = (float)e;
   }
 }
 
@@ -336,12 +412,24 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   return launch_topk_t<32>(a, grid, s);
 }
 
-hipError_t launch_colsum(const float* part, int nparts, int n, float* out, const float* part2,
-                         float* out2, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
+hipError_t launch_colsum(int nparts, ColsumVec v0, ColsumVec v1, ColsumVec v2, hipStream_t s) {
+  ColsumArgs a{};
+  int nv = 0, nmax = 0;
+  for (const ColsumVec& v : {v0, v1, v2})
+    if (v.part && v.n > 0) {
+      a.v[nv++] = v;
+      nmax = v.n > nmax ? v.n : nmax;
+    }
+  if (nv == 0) return hipSuccess;
   ProfScope ps("gate_colsum", s);
-  colsum_kernel<<<dim3((n + 63) / 64, part2 ? 2 : 1), dim3(64 * kColLanes), 0, s>>>(
-      part, nparts, n, out, part2, out2);
+  colsum_kernel<<<dim3((nmax + 63) / 64, nv), dim3(64 * kColLanes), 0, s>>>(a, nparts);
+  return hipGetLastError();
+}
+
+hipError_t launch_hier_stats(const float* prim, const float* part, const int32_t* tile_count,
+                             float* out, hipStream_t s) {
+  ProfScope ps("hier_stats", s);
+  hier_stats_kernel<<<dim3(1), dim3(256), 0, s>>>(prim, part, tile_count, out);
   return hipGetLastError();
 }
 

@@ -261,9 +261,12 @@ hipError_t launch_t(const GemmBf16Args& a, hipStream_t s) {
   if (grid < kXcds) grid = kXcds;
   const long long per = (max_total + kXcds - 1) / kXcds;
   while ((per + grid / kXcds - 1) / (grid / kXcds) > kMaxTilesPerWG) grid += kXcds;
-  ProfScope ps(EPI == EPI_RELU_BF16     ? "ggemm_bf16_relu"
-               : EPI == EPI_SWIGLU_BF16 ? "ggemm_bf16_swiglu"
-                                        : "ggemm_bf16_out",
+  static const char* const kNames[2][3] = {
+      {"ggemm_bf16_relu", "ggemm_bf16_swiglu", "ggemm_bf16_out"},
+      {"shared_bf16_relu", "shared_bf16_swiglu", "shared_bf16_out"}};
+  ProfScope ps(kNames[a.shared ? 1 : 0][EPI == EPI_RELU_BF16     ? 0
+                                        : EPI == EPI_SWIGLU_BF16 ? 1
+                                                                 : 2],
                s);
   ggemm_bf16_kernel<BN, EPI, WGM, HAS_BIAS><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(a);
   return hipGetLastError();

@@ -70,6 +70,7 @@ struct GemmBf16Args {
   const int32_t* tile_count;
   int max_mtiles;
   int num_cus;           // compute units of the device (persistent grid size)
+  int shared;            // 1: the shared expert (only the profiler name differs)
 };
 constexpr int kBf16BM = 128;
 constexpr int kMaxTilesPerWG = 512;  // tiles one persistent workgroup can hold
@@ -95,6 +96,7 @@ hipError_t launch_tilemap(const int32_t* offsets, int n, int bm, int32_t* tile_e
 // ---------------------------------------------------------------------------
 struct TopkArgs {
   int rows, n, k, switch_mode, noisy;
+  int sigmoid_mode;         // selection on logit + bias, weights Sigmoid(logit) renormalised
   const float* logits;
   long long ldl;
   const float* bias;
@@ -103,6 +105,8 @@ struct TopkArgs {
   float* topk_w;
   float* part_imp;          // [nparts, n]
   float* part_load;         // [nparts, n]
+  float* part_stats;        // [nparts, 2]: sum of squared pre-softmax logits, sum of gate
+                            // entropies over the block's rows (null: not computed)
   int rows_per_block;       // flat mode
   // grouped mode
   const int32_t* row_token;     // perm of the group dispatch
@@ -122,9 +126,19 @@ struct TopkArgs {
 inline int topk_waves(int n) { return (n + 63) / 64 <= 8 ? 16 : 8; }
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 // out[j] = sum over parts p < nparts of part[p*n + j] (double sum, fixed
-// order); likewise out2 from part2 when part2 is not null (same launch).
-hipError_t launch_colsum(const float* part, int nparts, int n, float* out, const float* part2,
-                         float* out2, hipStream_t s);
+// order), for up to three (part, n, out) vectors in one launch; a vector with
+// a null part is skipped.
+struct ColsumVec {
+  const float* part;
+  int n;
+  float* out;
+};
+hipError_t launch_colsum(int nparts, ColsumVec v0, ColsumVec v1, ColsumVec v2, hipStream_t s);
+// Two-level gate statistics: out[0] = prim[0] + sum over the secondary tiles
+// of part[t*2], out[1] = sum of part[t*2+1] (the product gate's entropy is
+// carried entirely by the secondary rows).
+hipError_t launch_hier_stats(const float* prim, const float* part, const int32_t* tile_count,
+                             float* out, hipStream_t s);
 // Two-level aux vectors: per-tile partials of the secondary gate are summed
 // per group (tiles of a group are consecutive), then combined with the
 // primary vectors: load[g*b+e] = load_p[g]*load_g[e]/|X_g|.
@@ -158,21 +172,33 @@ struct DispatchArgs {
   float* losses;
   const float* importance;
   const float* load;
-  float w_imp, w_load, alpha;
+  const float* gate_stats;  // [2] or null: z-loss and entropy sums
+  float w_imp, w_load, alpha, w_z, w_ent;
 };
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
 // Scatter each token's row to its kept slots: x_perm[slot_pos[t, s]] =
-// convert(x[t]) (bf16 round to nearest even, or an fp32 copy).
+// convert(x[t]) (bf16 round to nearest even, or an fp32 copy); x_bf16 (may be
+// null) also receives every row in token order, in bf16.
 hipError_t launch_gather(const float* x, const int32_t* slot_pos, int T, int k, int d,
-                         int bf16_out, void* x_perm, hipStream_t s);
+                         int bf16_out, void* x_perm, uint16_t* x_bf16, hipStream_t s);
+// x_bf16[t] = bf16(x[t]) for every token.
+hipError_t launch_to_bf16(const float* x, long long elems, uint16_t* out, hipStream_t s);
+// Tile map of one segment of T rows (the shared expert): offsets2 = {0, T}.
+hipError_t launch_shared_tilemap(int T, int bm, int32_t* offsets2, int32_t* tile_expert,
+                                 int32_t* tile_row0, int32_t* tile_count, hipStream_t s);
+// Selection-bias controller: bias[i] -= gamma if counts_pre[i]*n > T*k,
+// += gamma if counts_pre[i]*n < T*k.
+hipError_t launch_bias_update(const int32_t* counts_pre, int n, int T, int k, float gamma,
+                              float* bias, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Combine and aux.
 // ---------------------------------------------------------------------------
+// y[t] = y_base[t] (when given) + sum over kept slots, in slot order.
 hipError_t launch_combine(const float* y_perm, const int32_t* slot_pos, const float* topk_w,
-                          int T, int k, int d, float* y, hipStream_t s);
+                          const float* y_base, int T, int k, int d, float* y, hipStream_t s);
 hipError_t launch_aux(const float* importance, const float* load, const int32_t* counts_pre,
-                      int T, int k, int n, float w_imp, float w_load, float alpha,
-                      float* losses, hipStream_t s);
+                      const float* gate_stats, int T, int k, int n, float w_imp, float w_load,
+                      float alpha, float w_z, float w_ent, float* losses, hipStream_t s);
 
 }  // namespace moe

@@ -4,11 +4,13 @@ This module only draws random inputs; it holds none of the layer's
 arithmetic.  The same tensors feed the HIP library and, in tests, the CPU
 oracle.
 
-The five presets follow the workloads the pages describe: the LSTM language
-model layer with thousands of experts (positions flattened into one batch),
-its two-level variant, a Switch-style top-1 router with expert capacity and a
-fine-grained routed-expert layer with a gated (SwiGLU) FFN.  No dataset is
-used; every tensor is a seeded draw:
+The five main presets follow the workloads the pages describe: the LSTM
+language model layer with thousands of experts (positions flattened into one
+batch), its two-level variant, a Switch-style top-1 router with expert
+capacity and a fine-grained routed-expert layer with a gated (SwiGLU) FFN.  A
+sixth gives the fine-grained layer the sigmoid gate with a selection-only bias
+and one always-active shared expert of the routed experts' width.  No dataset
+is used; every tensor is a seeded draw:
 
 * x ~ N(0, 1); gate and expert weights ~ N(0, 1/fan_in) (variance);
 * noise ~ N(0, 1) per (token, expert), supplied as a tensor;
@@ -26,6 +28,7 @@ import torch
 
 GATE_TOPK_SOFTMAX = 0
 GATE_SWITCH_TOP1 = 1
+GATE_SIGMOID_BIAS = 2
 ACT_RELU = 0
 ACT_SWIGLU = 1
 DTYPE_F32 = 0
@@ -48,6 +51,9 @@ class MoEConfig:
     w_importance: float = 0.1
     w_load: float = 0.1
     alpha_switch: float = 1.0
+    w_z: float = 1.0           # router z-loss weight (1: the raw mean statistic)
+    w_entropy: float = 1.0     # gate-entropy loss weight
+    d_hidden_shared: int = 0   # shared expert's hidden width (0: none)
     n_groups: int = 0          # hierarchical: a
     k_groups: int = 0          # hierarchical: k1 (k = k1 * k2)
     logit_bias: str = "none"   # none | normal0.5 | normal1 | zipf1.1
@@ -82,6 +88,10 @@ PRESETS = {
                            logit_bias="normal1", seed=1004),
     "fine_swiglu": MoEConfig("fine_swiglu", T=4096, d_model=7168, d_hidden=2048, n_experts=256,
                              k=8, act=ACT_SWIGLU, noisy=False, logit_bias="zipf1.1", seed=1005),
+    "sigmoid_shared": MoEConfig("sigmoid_shared", T=4096, d_model=7168, d_hidden=2048,
+                                n_experts=256, k=8, act=ACT_SWIGLU, gate=GATE_SIGMOID_BIAS,
+                                noisy=False, logit_bias="normal0.5", d_hidden_shared=2048,
+                                seed=1006),
 }
 CONFIG_ORDER = ["tiny_f32", "lm_layer", "hierarchical", "switch_cf", "fine_swiglu"]
 
@@ -119,8 +129,8 @@ def make_inputs(cfg: MoEConfig, device="cpu", T: int | None = None):
     """All layer inputs for ``cfg`` as torch tensors on ``device``.
 
     Returns a dict with x, w_gate, b_gate, w_noise, noise, (w_gate2, w_noise2,
-    noise2 for the hierarchical preset), w1, w3, w2, b1, b2.  Absent inputs are
-    None.  Expert weights are drawn per (tensor, expert) with derived seeds, in
+    noise2 for the hierarchical preset), w1, w3, w2, b1, b2, (ws1, ws3, ws2 of
+    the shared expert).  Absent inputs are None.  Expert weights are drawn per (tensor, expert) with derived seeds, in
     bf16 when the preset's experts are bf16.
     """
     T = cfg.T if T is None else T
@@ -152,6 +162,12 @@ def make_inputs(cfg: MoEConfig, device="cpu", T: int | None = None):
     out["w1"] = experts(10, (h, d), d)
     out["w3"] = experts(11, (h, d), d) if cfg.act == ACT_SWIGLU else None
     out["w2"] = experts(12, (d, h), h)
+    hs = cfg.d_hidden_shared
+    if hs:
+        out["ws1"] = _normal((hs, d), 1.0 / math.sqrt(d), device, _derived(s, 13)).to(wdt)
+        out["ws3"] = (_normal((hs, d), 1.0 / math.sqrt(d), device, _derived(s, 14)).to(wdt)
+                      if cfg.act == ACT_SWIGLU else None)
+        out["ws2"] = _normal((d, hs), 1.0 / math.sqrt(hs), device, _derived(s, 15)).to(wdt)
     if cfg.zero_expert_bias:
         out["b1"] = torch.zeros((n, h), dtype=torch.float32, device=device)
         out["b2"] = torch.zeros((n, d), dtype=torch.float32, device=device)

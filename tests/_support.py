@@ -132,7 +132,8 @@ def oracle_flat(cfg, h, ew):
         w_noise=h.get("w_noise"), noise=h.get("noise"), b1=_stack(ew["b1"]), w3=_stack(ew["w3"]),
         b2=_stack(ew["b2"]), mode=cfg.gate, act=cfg.act, bf16=cfg.expert_dtype == DTYPE_BF16,
         capacity_factor=cfg.capacity_factor, w_importance=cfg.w_importance, w_load=cfg.w_load,
-        alpha=cfg.alpha_switch)
+        alpha=cfg.alpha_switch, w_z=cfg.w_z, w_entropy=cfg.w_entropy, ws1=h.get("ws1"),
+        ws3=h.get("ws3"), ws2=h.get("ws2"))
 
 
 def _stack(dct):
@@ -147,15 +148,17 @@ def y_tolerance(cfg):
 
 def oracle_gate_any(cfg, h):
     """Oracle gating of a flat or two-level config on host inputs `h`.
-    Returns (topk_idx, topk_w, importance, load, H_for_ties, near_tie)."""
+    Returns (topk_idx, topk_w, importance, load, H_for_ties, near_tie, zsum,
+    entsum)."""
     if cfg.hierarchical:
         gh = oracle.gate_hier(h["x"], h["w_gate"], h.get("w_noise"), h.get("noise"),
                               cfg.k_groups, h["w_gate2"], h.get("w_noise2"), h.get("noise2"),
                               cfg.k2, b_gate=h.get("b_gate"))
-        return gh["topk_idx"], gh["topk_w"], gh["importance"], gh["load"], None, gh["near_tie"]
+        return (gh["topk_idx"], gh["topk_w"], gh["importance"], gh["load"], None,
+                gh["near_tie"], gh["zsum"], gh["entsum"])
     g = oracle.gate(h["x"], h["w_gate"], cfg.k, h.get("b_gate"), h.get("w_noise"),
                     h.get("noise"), cfg.gate)
-    return g.topk_idx, g.topk_w, g.importance, g.load, g.H, g.near_tie
+    return g.topk_idx, g.topk_w, g.importance, g.load, g.H, g.near_tie, g.zsum, g.entsum
 
 
 def check_routing_any(cfg, gpu_idx, orc_idx, H, near_tie):
@@ -182,6 +185,11 @@ def sampled_y_reference(cfg, inp, x64, idx, w, slot_pos, tokens):
         return None if t is None else t[e].detach().float().cpu().numpy()
 
     ys = np.zeros((len(tokens), cfg.d_model))
+    if cfg.d_hidden_shared:
+        ws = {k: (None if inp.get(k) is None else inp[k].detach().float().cpu().numpy())
+              for k in ("ws1", "ws3", "ws2")}
+        ys += oracle.expert_ffn(x64[tokens], ws["ws1"], ws["ws2"], w3=ws["ws3"], act=cfg.act,
+                                bf16=bf)
     for e in experts:
         w1, w2, w3 = host32("w1", e), host32("w2", e), host32("w3", e)
         b1, b2 = host32("b1", e), host32("b2", e)
@@ -203,7 +211,7 @@ def full_size_sampled(cfg, n_sample=48, seed=0):
     inp = dev_inputs(cfg)
     gpu = gpu_forward(cfg, inp)
     h = host(inp)
-    oidx, ow, oimp, oload, H, near = oracle_gate_any(cfg, h)
+    oidx, ow, oimp, oload, H, near, zsum, entsum = oracle_gate_any(cfg, h)
     bad = check_routing_any(cfg, gpu["topk_idx"], oidx, H, near)
     ok = np.setdiff1d(np.arange(cfg.T), bad)
     np.testing.assert_allclose(gpu["topk_w"][ok], ow[ok], rtol=TOL_W_REL, atol=TOL_W)
@@ -213,7 +221,7 @@ def full_size_sampled(cfg, n_sample=48, seed=0):
         if oload is not None:
             assert_close_rel(gpu["load"], oload, 1e-5, 1e-5, "load")
         losses = oracle.aux(cfg.T, cfg.k, oimp, oload, d["counts_pre"], cfg.w_importance,
-                            cfg.w_load, cfg.alpha_switch)
+                            cfg.w_load, cfg.alpha_switch, zsum, entsum, cfg.w_z, cfg.w_entropy)
         assert_close_rel(gpu["losses"], losses, TOL_AUX, 1e-7, "losses")
     # sampled outputs: ends of the batch, random tokens, and tokens routed to
     # the most loaded expert

@@ -26,7 +26,7 @@ def test_header_declares_expected_calls():
     decl = declared_functions()
     for name in ["moe_gate", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_aux_loss",
                  "moe_forward", "moe_workspace_size", "moe_status_string", "moe_last_error",
-                 "moe_gate_hier"]:
+                 "moe_gate_hier", "moe_shared_ffn", "moe_router_bias_update"]:
         assert name in decl
     assert sorted(_lib.EXPORTS) == decl
 
@@ -78,13 +78,18 @@ def base_cfg(**kw):
     (dict(n_groups=3), moe.MOE_ERR_INVALID_ARG),           # 8 % 3
     (dict(n_groups=2, k_groups=3), moe.MOE_ERR_INVALID_ARG),
     (dict(capacity_factor=float("nan")), moe.MOE_ERR_INVALID_ARG),
+    (dict(gate=2, n_groups=2, k_groups=1), moe.MOE_ERR_INVALID_ARG),  # two-level: softmax gate
+    (dict(d_hidden_shared=12), moe.MOE_ERR_INVALID_ARG),
+    (dict(d_hidden_shared=-8), moe.MOE_ERR_INVALID_ARG),
+    (dict(d_hidden_shared=16, expert_dtype=0), moe.MOE_ERR_UNSUPPORTED),
+    (dict(d_hidden_shared=16, n_groups=2, k_groups=1), moe.MOE_ERR_UNSUPPORTED),
 ])
 def test_invalid_configs(kw, status):
     c = _lib.make_config(base_cfg(**kw))
     L = moe.load_library()
     assert L.moe_workspace_size(ctypes.byref(c)) == 0
     with pytest.raises(moe.MoEError) as ei:
-        moe.moe_combine(c, FAKE, FAKE, FAKE, FAKE, stream=0)
+        moe.moe_combine(c, FAKE, FAKE, FAKE, None, FAKE, stream=0)
     assert ei.value.status == status
     assert moe.moe_last_error()
 
@@ -92,23 +97,54 @@ def test_invalid_configs(kw, status):
 def test_null_and_misaligned_pointers():
     c = base_cfg()
     with pytest.raises(moe.MoEError) as ei:
-        moe.moe_combine(c, None, FAKE, FAKE, FAKE, stream=0)
+        moe.moe_combine(c, None, FAKE, FAKE, None, FAKE, stream=0)
     assert ei.value.status == moe.MOE_ERR_INVALID_ARG and "y_perm" in str(ei.value)
     with pytest.raises(moe.MoEError) as ei:
-        moe.moe_combine(c, FAKE + 4, FAKE, FAKE, FAKE, stream=0)
+        moe.moe_combine(c, FAKE + 4, FAKE, FAKE, None, FAKE, stream=0)
     assert ei.value.status == moe.MOE_ERR_INVALID_ARG and "aligned" in str(ei.value)
     with pytest.raises(moe.MoEError) as ei:   # noisy gate without its noise tensor
-        moe.moe_gate(c, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, FAKE, (FAKE, 1 << 30),
-                     stream=0)
+        moe.moe_gate(c, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, FAKE, None,
+                     (FAKE, 1 << 30), stream=0)
     assert ei.value.status == moe.MOE_ERR_INVALID_ARG and "noise" in str(ei.value)
     with pytest.raises(moe.MoEError) as ei:   # Switch router is noiseless
         moe.moe_gate(base_cfg(gate=1, k=1), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
-                     FAKE, (FAKE, 1 << 30), stream=0)
+                     FAKE, None, (FAKE, 1 << 30), stream=0)
     assert ei.value.status == moe.MOE_ERR_INVALID_ARG
     with pytest.raises(moe.MoEError) as ei:   # flat call on a two-level config
         moe.moe_gate(base_cfg(n_groups=2, k_groups=1), FAKE, FAKE, None, None, None, FAKE, FAKE,
-                     FAKE, None, (FAKE, 1 << 30), stream=0)
+                     FAKE, None, None, (FAKE, 1 << 30), stream=0)
     assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+
+
+def test_sigmoid_gate_shared_expert_and_bias_update_arguments():
+    c = base_cfg(gate=2)
+    with pytest.raises(moe.MoEError) as ei:   # the sigmoid gate is noiseless
+        moe.moe_gate(c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                     (FAKE, 1 << 30), stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG and "sigmoid" in str(ei.value)
+    with pytest.raises(moe.MoEError) as ei:   # no shared expert configured
+        moe.moe_shared_ffn(c, FAKE, FAKE, None, FAKE, FAKE, (FAKE, 1 << 30), stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    cs = base_cfg(d_hidden_shared=16, act=1)
+    with pytest.raises(moe.MoEError) as ei:   # SwiGLU shared expert needs ws3
+        moe.moe_shared_ffn(cs, FAKE, FAKE, None, FAKE, FAKE, (FAKE, 1 << 30), stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG and "ws3" in str(ei.value)
+    with pytest.raises(moe.MoEError) as ei:   # workspace sized without the shared expert
+        moe.moe_shared_ffn(cs, FAKE, FAKE, FAKE, FAKE, FAKE,
+                           (FAKE, moe.moe_workspace_size(base_cfg(act=1))), stream=0)
+    assert ei.value.status == moe.MOE_ERR_WORKSPACE
+    w = moe.make_weights(FAKE, w1=FAKE, w2=FAKE, w3=FAKE)
+    with pytest.raises(moe.MoEError) as ei:   # forward with a shared expert but no ws1
+        moe.moe_forward(cs, w, FAKE, None, None, FAKE, FAKE, None,
+                        (FAKE, moe.moe_workspace_size(cs)), stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG and "ws1" in str(ei.value)
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_router_bias_update(c, FAKE, None, 0.01, stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG and "bias" in str(ei.value)
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_router_bias_update(c, FAKE, FAKE, float("nan"), stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG and "gamma" in str(ei.value)
+    assert moe.moe_workspace_size(cs) > moe.moe_workspace_size(base_cfg(act=1))
 
 
 def test_workspace_too_small_rejected_before_launch():

@@ -16,10 +16,11 @@ from _support import (TOL_AUX, assert_close_rel, check_dispatch_exact, dev_input
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name", ["lm_layer", "switch_cf", "hierarchical", "fine_swiglu"])
+@pytest.mark.parametrize("name", ["lm_layer", "switch_cf", "hierarchical", "fine_swiglu",
+                                  "sigmoid_shared"])
 def test_full_size(name):
     cfg = PRESETS[name]
-    n_sample = 6 if name == "fine_swiglu" else 48
+    n_sample = 6 if name in ("fine_swiglu", "sigmoid_shared") else 48
     gpu = full_size_sampled(cfg, n_sample=n_sample)
     if name == "switch_cf":
         C = int(np.floor(cfg.capacity_factor * cfg.T * cfg.k / cfg.n_experts))
@@ -76,12 +77,13 @@ def test_stage_gate_hier():
     w = torch.empty((T, k), dtype=torch.float32, device="cuda")
     imp = torch.empty(n, dtype=torch.float32, device="cuda")
     ld = torch.empty(n, dtype=torch.float32, device="cuda")
+    st = torch.empty(2, dtype=torch.float32, device="cuda")
     ws = torch.empty(moe.moe_workspace_size(c), dtype=torch.uint8, device="cuda")
     moe.moe_gate_hier(c, inp["x"], inp["w_gate"], inp["b_gate"], inp["w_noise"], inp["noise"],
-                      inp["w_gate2"], inp["w_noise2"], inp["noise2"], idx, w, imp, ld, ws)
+                      inp["w_gate2"], inp["w_noise2"], inp["noise2"], idx, w, imp, ld, st, ws)
     torch.cuda.synchronize()
     h = host(inp)
-    oidx, ow, oimp, oload, _, near = oracle_gate_any(c, h)
+    oidx, ow, oimp, oload, _, near, zsum, entsum = oracle_gate_any(c, h)
     gi = idx.cpu().numpy()
     bad = np.nonzero(np.any(gi != oidx, axis=1))[0]
     assert all(near[t] for t in bad) and len(bad) <= 1e-4 * T
@@ -90,3 +92,4 @@ def test_stage_gate_hier():
     if len(bad) == 0:
         assert_close_rel(imp.cpu().numpy(), oimp, 1e-5, 1e-5, "importance")
         assert_close_rel(ld.cpu().numpy(), oload, 1e-5, 1e-5, "load")
+        assert_close_rel(st.cpu().numpy(), [zsum, entsum], TOL_AUX, 1e-7, "gate stats")

@@ -18,7 +18,8 @@ import sparsely_gated_mixture_amd as moe
 from sparsely_gated_mixture_amd.workloads import (ACT_RELU, ACT_SWIGLU, DTYPE_BF16, DTYPE_F32,
                                                   GATE_SWITCH_TOP1, GATE_TOPK_SOFTMAX, PRESETS,
                                                   MoEConfig, make_inputs, to_numpy64)
-from _support import (TOL_AUX, TOL_W, TOL_W_REL, assert_close_rel, check_dispatch_exact, dev_inputs,
+from _support import (TOL_AUX, TOL_BF16, TOL_W, TOL_W_REL, assert_close_rel, check_dispatch_exact,
+                      dev_inputs,
                       expert_weights_host, gpu_forward, host, log, max_abs_norm, oracle_flat,
                       routing_mismatches, y_tolerance)
 
@@ -182,22 +183,24 @@ def _ws(cfg):
     return torch.empty(moe.moe_workspace_size(cfg), dtype=torch.uint8, device="cuda")
 
 
-@pytest.mark.parametrize("name", ["tiny_f32", "lm_layer", "switch_cf", "fine_swiglu"])
+@pytest.mark.parametrize("name", ["tiny_f32", "lm_layer", "switch_cf", "fine_swiglu",
+                                  "sigmoid_shared"])
 def test_stage_gate(name):
     cfg = PRESETS[name]
     T = min(cfg.T, 4096)
     c = cfg.replace(T=T)
     log(f"[stage gate] {name} T={T}")
-    inp = make_inputs(c, device="cuda", T=T) if name != "fine_swiglu" else None
-    if inp is None:  # skip the 22 GB of expert weights: the gate needs none
-        inp = _gate_only_inputs(c)
+    big = name in ("fine_swiglu", "sigmoid_shared")
+    # the gate needs no expert weights: skip the 22 GB of them for the big layers
+    inp = _gate_only_inputs(c) if big else make_inputs(c, device="cuda", T=T)
     n, k = c.n_experts, c.k
     idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
     w = torch.empty((T, k), dtype=torch.float32, device="cuda")
     imp = torch.empty(n, dtype=torch.float32, device="cuda")
     ld = torch.zeros(n, dtype=torch.float32, device="cuda")
+    st = torch.empty(2, dtype=torch.float32, device="cuda")
     moe.moe_gate(c, inp["x"], inp["w_gate"], inp["b_gate"], inp["w_noise"], inp["noise"], idx, w,
-                 imp, ld, _ws(c))
+                 imp, ld, st, _ws(c))
     torch.cuda.synchronize()
     h = host(inp, ["x", "w_gate", "b_gate", "w_noise", "noise"])
     g = oracle.gate(h["x"], h["w_gate"], k, h["b_gate"], h["w_noise"], h["noise"], c.gate)
@@ -209,10 +212,11 @@ def test_stage_gate(name):
         assert_close_rel(imp.cpu().numpy(), g.importance, 1e-5, 1e-5, "importance")
         if g.load is not None:
             assert_close_rel(ld.cpu().numpy(), g.load, 1e-5, 1e-5, "load")
+        assert_close_rel(st.cpu().numpy(), [g.zsum, g.entsum], TOL_AUX, 1e-7, "gate stats")
 
 
 def _gate_only_inputs(cfg):
-    small = cfg.replace(d_hidden=8, n_experts=cfg.n_experts)
+    small = cfg.replace(d_hidden=8, n_experts=cfg.n_experts, d_hidden_shared=0)
     # Same seeds for x / gate / noise as the full preset; tiny experts.
     inp = make_inputs(small.replace(act=ACT_RELU), device="cuda", T=cfg.T)
     return inp
@@ -260,20 +264,82 @@ def test_stage_dispatch_and_ffn(cf):
     # combine given the same y_perm
     y = torch.empty((T, d), dtype=torch.float32, device="cuda")
     wt = torch.from_numpy(g.topk_w.astype(np.float32)).to("cuda")
-    moe.moe_combine(c, yp, slot, wt, y)
+    moe.moe_combine(c, yp, slot, wt, None, y)
     torch.cuda.synchronize()
     y_comb = oracle.combine(yp[:rows].cpu().double().numpy(), ref["slot_pos"],
                             g.topk_w.astype(np.float32), d)
     assert max_abs_norm(y.cpu().double().numpy(), y_comb) <= 1e-6
+    # combine with a base row added first (the shared expert's place)
+    base = torch.randn((T, d), dtype=torch.float32, device="cuda")
+    moe.moe_combine(c, yp, slot, wt, base, y)
+    torch.cuda.synchronize()
+    assert max_abs_norm(y.cpu().double().numpy(),
+                        base.cpu().double().numpy() + y_comb) <= 1e-6
     # aux losses from the same vectors
-    losses = torch.empty(3, dtype=torch.float32, device="cuda")
+    losses = torch.empty(moe.N_LOSSES, dtype=torch.float32, device="cuda")
     imp32 = torch.from_numpy(g.importance.astype(np.float32)).to("cuda")
     ld32 = torch.from_numpy(g.load.astype(np.float32)).to("cuda")
-    moe.moe_aux_loss(c, imp32, ld32, cp, losses)
+    st32 = np.array([g.zsum, g.entsum], np.float32)
+    moe.moe_aux_loss(c, imp32, ld32, cp, torch.from_numpy(st32).to("cuda"), losses)
     torch.cuda.synchronize()
     ref_l = oracle.aux(T, k, g.importance.astype(np.float32), g.load.astype(np.float32),
-                       ref["counts_pre"], c.w_importance, c.w_load, c.alpha_switch)
+                       ref["counts_pre"], c.w_importance, c.w_load, c.alpha_switch,
+                       float(st32[0]), float(st32[1]), c.w_z, c.w_entropy)
     assert_close_rel(losses.cpu().numpy(), ref_l, 1e-6, 1e-9, "aux")
+    moe.moe_aux_loss(c, imp32, ld32, cp, None, losses)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(losses.cpu().numpy()[3:], 0.0)
+
+
+def test_forward_sigmoid_shared_reduced_width():
+    # The sigmoid gate with a selection-only bias and a shared SwiGLU expert
+    # (n=256, k=8) at reduced width, every element against the oracle.
+    cfg = PRESETS["sigmoid_shared"].replace(d_model=256, d_hidden=128, d_hidden_shared=192)
+    gpu, ref = full_parity(cfg, T=512)
+    np.testing.assert_allclose(gpu["topk_w"].sum(1), 1.0, rtol=1e-5)
+
+
+def test_forward_sigmoid_relu_shared_f32_gate_odd():
+    # ReLU experts, ragged T and n, the shared expert wider than the routed ones.
+    cfg = MoEConfig("sig_odd", T=333, d_model=72, d_hidden=40, n_experts=100, k=6,
+                    gate=2, noisy=False, logit_bias="normal1", d_hidden_shared=88, seed=81)
+    full_parity(cfg)
+
+
+@pytest.mark.parametrize("act", [0, 1])
+def test_stage_shared_ffn(act):
+    cfg = MoEConfig("shared", T=300, d_model=64, d_hidden=32, n_experts=4, k=1, act=act,
+                    noisy=False, d_hidden_shared=96, seed=82)
+    log(f"[stage shared ffn] act={act} T=300")
+    inp = dev_inputs(cfg)
+    y = torch.empty((cfg.T, cfg.d_model), dtype=torch.float32, device="cuda")
+    moe.moe_shared_ffn(cfg, inp["x"], inp["ws1"], inp.get("ws3"), inp["ws2"], y, _ws(cfg))
+    torch.cuda.synchronize()
+    h = host(inp)
+    ref = oracle.expert_ffn(h["x"], h["ws1"], h["ws2"], w3=h.get("ws3"), act=act, bf16=True)
+    err = max_abs_norm(y.cpu().double().numpy(), ref)
+    log(f"  shared expert error {err:.3e}")
+    assert err <= TOL_BF16
+
+
+def test_router_bias_update():
+    # Counts above, at and below the even share (T*k/n = 7.5 and 8), bit-exact
+    # against the controller applied in fp32 to the same bias.
+    rng = np.random.default_rng(9)
+    for T, k, n in ((30, 1, 4), (64, 2, 16)):
+        cfg = MoEConfig("bias", T=T, d_model=8, d_hidden=8, n_experts=n, k=k,
+                        gate=2, noisy=False)
+        share = T * k / n
+        counts = rng.integers(0, 2 * int(share) + 2, n).astype(np.int32)
+        counts[0] = int(share) if share == int(share) else counts[0]
+        bias = rng.standard_normal(n).astype(np.float32)
+        gamma = np.float32(0.001)
+        b = torch.from_numpy(bias.copy()).to("cuda")
+        moe.moe_router_bias_update(cfg, torch.from_numpy(counts).to("cuda"), b, float(gamma))
+        torch.cuda.synchronize()
+        sign = np.sign(oracle.bias_update(np.zeros(n), counts, T, k, 1.0))
+        expect = np.where(sign < 0, bias - gamma, np.where(sign > 0, bias + gamma, bias))
+        np.testing.assert_array_equal(b.cpu().numpy(), expect.astype(np.float32))
 
 
 def ew_stack(ew, name):
