@@ -16,9 +16,13 @@
 //  * K advances 64 at a time, so every row of both operands is read in whole
 //    128-byte lines (narrower per-row reads measured about 30% slower);
 //  * a ring of kStages LDS buffers is filled by direct global->LDS copies
-//    (global_load_lds_dwordx4) kStages-1 steps ahead of the MFMAs, and the
-//    ring runs on across tile boundaries, so a tile's epilogue overlaps the
-//    next tile's loads; one barrier per step;
+//    (global_load_lds_dwordx4); step g+2 is copied right after the barrier
+//    that opens step g, so two steps are in flight while step g computes;
+//    the ring runs on across tile boundaries, so a tile's epilogue overlaps
+//    the next tile's loads; one barrier per step;
+//  * each lane keeps the global addresses of the rows it copies and updates
+//    them only when the copy cursor enters a new tile, so a step's copies
+//    are an add and an instruction each;
 //  * N-tiles are 256 wide (SwiGLU: 128 columns of both W1 and W3), so each
 //    activation tile is fetched from L2 N/256 times; this measured faster than
 //    128-wide tiles with a deeper ring (activation re-reads through L2 cost
@@ -71,13 +75,27 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// wait_vm<n>() for a run-time n in [0, MAX] (a wave-uniform value).
+template <int MAX>
+__device__ __forceinline__ void wait_vm_upto(int n) {
+  if constexpr (MAX > 0) {
+    if (n >= MAX) {
+      wait_vm<MAX>();
+      return;
+    }
+    wait_vm_upto<MAX - 1>(n);
+  } else {
+    wait_vm<0>();
+  }
+}
+
 __device__ __forceinline__ int swz(int r, int c) { return (c ^ ((r >> 1) & 7)) << 4; }
 
 // HAS_BIAS is a template parameter so that the usual bias-free kernels have
 // no global loads in the epilogue (the compiler would otherwise wait there
 // for every copy in flight).
 template <int BN, int EPI, int WGM, bool HAS_BIAS>
-__global__ __launch_bounds__(kThreads) void ggemm_bf16_kernel(const GemmBf16Args p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void ggemm_bf16_kernel(const GemmBf16Args p) {
   constexpr int NB = (EPI == EPI_SWIGLU_BF16) ? 2 : 1;  // weight matrices per tile
   constexpr int BROWS = NB * BN;                         // weight rows per tile
   constexpr int A_BYTES = kBM * kRowB, B_BYTES = BROWS * kRowB;
@@ -118,34 +136,67 @@ __global__ __launch_bounds__(kThreads) void ggemm_bf16_kernel(const GemmBf16Args
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
-  // Copy step g (tile g / nk, K-step g % nk) into ring slot g % kStages.
-  // Lane covers row (blk*8 + lane/8), chunk (lane%8) swizzled.
-  auto issue = [&](int g) {
-    const int ti = g / nk, kt = g - ti * nk;
+  // Copy cursor: the next step to copy is step gi (tile it, K-step ikt).
+  // Each lane keeps the global address of its rows' 16-byte chunk for the
+  // cursor's tile (row blk*8 + lane/8, chunk (lane%8) swizzled), recomputed
+  // only when the cursor enters a new tile.
+  const uint16_t* a_src[ADMA];
+  const uint16_t* b_src[BDMA];
+  int a_chunk[ADMA], b_chunk[BDMA];  // element offset of the lane's chunk within a step
+  int gi = 0, it = 0, ikt = 0;
+  int a_live = 0;    // copies j < a_live of the activation tile hold real rows
+  int last_cnt = 0;  // copies this wave issued for the most recent step
+  auto set_tile = [&](int ti) {
     const int4 m = meta[ti];
-    const int k0 = kt * kBK;
-    const uint32_t sb = lds0 + (g % kStages) * STAGE;
+    // Row groups (8 rows per copy) past the segment's end are not copied:
+    // their LDS rows only ever feed output columns that are not stored.
+    a_live = 0;
+#pragma unroll
+    for (int j = 0; j < ADMA; ++j) a_live += m.y + (wave + kWaves * j) * 8 < m.z ? 1 : 0;
 #pragma unroll
     for (int j = 0; j < ADMA; ++j) {
-      const int blk = wave + kWaves * j;
-      const int r = blk * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ ((r >> 1) & 7);
-      const int gr = min(m.y + r, m.z - 1);
-      const void* src = k0 + c * 8 < K ? (const void*)(p.A + (long long)gr * p.lda + k0 + c * 8)
-                                       : (const void*)kZeroChunk;
-      dma16(src, sb + blk * 1024);
+      const int r = (wave + kWaves * j) * 8 + (lane >> 3);
+      a_chunk[j] = ((lane & 7) ^ ((r >> 1) & 7)) * 8;
+      a_src[j] = p.A + (long long)min(m.y + r, m.z - 1) * p.lda + a_chunk[j];
     }
 #pragma unroll
     for (int j = 0; j < BDMA; ++j) {
-      const int blk = wave + kWaves * j;
-      const int r = blk * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      const int r = (wave + kWaves * j) * 8 + (lane >> 3);
       const int which = r / BN, rn = r % BN;
-      const int gn = min(m.w + rn, p.N - 1);
       const uint16_t* w = (which == 0 ? p.B1 : p.B3) + (long long)m.x * p.strideB;
-      const void* src = k0 + c * 8 < K ? (const void*)(w + (long long)gn * K + k0 + c * 8)
-                                       : (const void*)kZeroChunk;
-      dma16(src, sb + A_BYTES + blk * 1024);
+      b_chunk[j] = ((lane & 7) ^ ((r >> 1) & 7)) * 8;
+      b_src[j] = w + (long long)min(m.w + rn, p.N - 1) * K + b_chunk[j];
+    }
+  };
+  // Copy step gi into ring slot gi % kStages and advance the cursor.  A step
+  // that reaches past K copies a 16-byte zero constant for the chunks beyond
+  // it (same number of copies per step).
+  auto issue_next = [&]() {
+    const uint32_t sb = lds0 + (gi % kStages) * STAGE;
+    const int k0 = ikt * kBK;
+    if (k0 + kBK <= K) {
+#pragma unroll
+      for (int j = 0; j < ADMA; ++j)
+        if (j < a_live) dma16(a_src[j] + k0, sb + (wave + kWaves * j) * 1024);
+#pragma unroll
+      for (int j = 0; j < BDMA; ++j)
+        dma16(b_src[j] + k0, sb + A_BYTES + (wave + kWaves * j) * 1024);
+    } else {
+#pragma unroll
+      for (int j = 0; j < ADMA; ++j)
+        if (j < a_live)
+          dma16(k0 + a_chunk[j] < K ? (const void*)(a_src[j] + k0) : (const void*)kZeroChunk,
+                sb + (wave + kWaves * j) * 1024);
+#pragma unroll
+      for (int j = 0; j < BDMA; ++j)
+        dma16(k0 + b_chunk[j] < K ? (const void*)(b_src[j] + k0) : (const void*)kZeroChunk,
+              sb + A_BYTES + (wave + kWaves * j) * 1024);
+    }
+    last_cnt = a_live + BDMA;
+    ++gi;
+    if (++ikt == nk) {
+      ikt = 0;
+      if (++it < ntiles) set_tile(it);
     }
   };
 
@@ -165,51 +216,67 @@ __global__ __launch_bounds__(kThreads) void ggemm_bf16_kernel(const GemmBf16Args
   };
   zero_acc();
 
+  int4 cm = meta[0];  // the computing tile
+  set_tile(0);
 #pragma unroll
   for (int s = 0; s < kStages - 1; ++s)
-    if (s < nsteps) issue(s);
+    if (gi < nsteps) issue_next();
 
   for (int g = 0; g < nsteps; ++g) {
-    const int ahead = nsteps - 1 - g;  // steps issued after this one, at most kStages-2
+    // Steps copied after this one: at most kStages-2.  Wait until only the
+    // copies of step g+1 (last_cnt of them) may still be in flight; loads
+    // complete in order, so step g's copies have then landed.
+    const int ahead = min(nsteps, g + kStages - 1) - 1 - g;
     static_assert(kStages == 3, "the waits below assume a 3-deep ring");
-    if (ahead >= 1)
-      wait_vm<PER_STEP>();
-    else
-      wait_vm<0>();
+    wait_vm_upto<PER_STEP>(ahead >= 1 ? last_cnt : 0);
     __syncthreads();
+    if (g % nk == 0) cm = meta[g / nk];
+    // Every wave is past step g-1, so its ring slot can take step g+2 now,
+    // while this step computes.
+    if (gi < nsteps) issue_next();
     const uint8_t* As = smem + (g % kStages) * STAGE;
     const uint8_t* Bs = As + A_BYTES;
+    // A wave whose token rows all lie past the segment's end has nothing to
+    // compute this tile.
+    if (cm.y + wm * WM < cm.z) {
+    // All fragments of the step first (the LDS reads overlap one another),
+    // then the MFMAs.
+    bf16x8 xf[kBK / 16][FM], wf[kBK / 16][NB][FN];
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
       const int c = 2 * kk + lh;  // 32x32x16 operand: row lane%32, k = 8*(lane/32)..+7
-      bf16x8 xf[FM], wf[NB][FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int r = wm * WM + i * 32 + lr;
-        xf[i] = *(const bf16x8*)(As + r * kRowB + swz(r, c));
+        xf[kk][i] = *(const bf16x8*)(As + r * kRowB + swz(r, c));
       }
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const int r = b * BN + wn * WN + j * 32 + lr;
-          wf[b][j] = *(const bf16x8*)(Bs + r * kRowB + swz(r, c));
+          wf[kk][b][j] = *(const bf16x8*)(Bs + r * kRowB + swz(r, c));
         }
+    }
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk)
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int j = 0; j < FN; ++j)
-            acc[b][i][j] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[b][j], xf[i], acc[b][i][j], 0, 0, 0);
+            acc[b][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[kk][b][j], xf[kk][i],
+                                                                   acc[b][i][j], 0, 0, 0);
+    // Scheduling groups: every LDS read of the step, then every MFMA.
+    __builtin_amdgcn_sched_group_barrier(0x100, (kBK / 16) * (FM + NB * FN), 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, (kBK / 16) * NB * FM * FN, 0);
     }
-    if (g + kStages - 1 < nsteps) issue(g + kStages - 1);
 
     if (g % nk == nk - 1) {
       // Tile done.  D[n][m] layout: lane holds column m = lane%32 of each
       // 32x32 block and rows n = 8*(v/4) + 4*(lane/32) + v%4.
-      const int4 m = meta[g / nk];
+      const int4 m = cm;
       const int e = m.x, row_end = m.z;
       const float* bias = HAS_BIAS ? p.bias + (long long)e * p.N : nullptr;
 #pragma unroll
