@@ -109,6 +109,12 @@ def lib():
         L.oracle_entropy_sum.argtypes = [c_int, c_int, _dp]
         L.oracle_entropy_sum.restype = c_dbl
         L.oracle_bias_update.argtypes = [c_int, c_int, c_int, _ip, c_dbl, _dp]
+        L.oracle_e4m3_decode.argtypes = [c_int]
+        L.oracle_e4m3_decode.restype = c_dbl
+        L.oracle_e4m3_encode.argtypes = [c_dbl]
+        L.oracle_e4m3_encode.restype = c_int
+        L.oracle_quantize_fp8_rows.argtypes = [c_int, c_int, _dp,
+                                               np.ctypeslib.ndpointer(np.uint8, flags="C"), _dp]
         L.oracle_hier_load.argtypes = [c_int, c_int, _dp, _dp, _ip, _dp]
         _lib = L
     return _lib
@@ -212,6 +218,41 @@ def bias_update(bias, counts_pre, T, k, gamma):
     c = _i(counts_pre)
     lib().oracle_bias_update(b.size, int(T), int(k), c, float(gamma), b)
     return b
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    c = np.asarray(codes, dtype=np.int64)
+    L = lib()
+    return np.array([L.oracle_e4m3_decode(int(v)) for v in c.reshape(-1)]).reshape(c.shape)
+
+
+def e4m3_encode(values) -> np.ndarray:
+    v = np.asarray(values, dtype=np.float64)
+    L = lib()
+    return np.array([L.oracle_e4m3_encode(float(a)) for a in v.reshape(-1)],
+                    dtype=np.uint8).reshape(v.shape)
+
+
+def quantize_fp8_rows(w):
+    """[SURVEY] section 9 read as FP8 E4M3 weights with a per-row scale:
+    returns (codes uint8 [rows, K], scales float64 [rows])."""
+    w = _d(w)
+    rows, K = w.shape
+    codes = np.empty((rows, K), np.uint8)
+    scales = np.empty(rows)
+    lib().oracle_quantize_fp8_rows(rows, K, w, codes, scales)
+    return codes, scales
+
+
+_E4M3_TABLE = None
+
+
+def dequantize_fp8_rows(codes, scales) -> np.ndarray:
+    """The values the codes stand for: decode(code) * scale of the row."""
+    global _E4M3_TABLE
+    if _E4M3_TABLE is None:
+        _E4M3_TABLE = e4m3_decode(np.arange(256))
+    return _E4M3_TABLE[np.asarray(codes)] * np.asarray(scales, dtype=np.float64)[:, None]
 
 
 def importance(probs):

@@ -218,6 +218,66 @@ void oracle_sigmoid_gate_weights(int T, int n, int k, const double* h,
   }
 }
 
+/* ------------------------------------------------------------------------ */
+/* FP8 expert weights                                                        */
+/* ------------------------------------------------------------------------ */
+
+/* [SURVEY] section 9 (DeepSeek-V3 summary): the main computation runs in FP8.
+ * Read here as FP8 E4M3 expert weights with one scale per output row (the
+ * activations stay bf16).  The E4M3 format (the "e4m3fn" variant): 1 sign, 4
+ * exponent bits with bias 7, 3 mantissa bits; exponent field 1..15 gives
+ * (1 + m/8) 2^(e-7), field 0 gives the subnormals (m/8) 2^-6; the code
+ * S.1111.111 is NaN; there are no infinities; the largest finite value is
+ * 448 = 1.75 * 2^8. */
+double oracle_e4m3_decode(int code) {
+  int e = (code >> 3) & 15, m = code & 7;
+  if (e == 15 && m == 7) return NAN;
+  double v = e == 0 ? ldexp(m / 8.0, -6) : ldexp(1.0 + m / 8.0, e - 7);
+  return (code & 0x80) ? -v : v;
+}
+
+/* Nearest E4M3 value, ties to the even code (round to nearest even), found
+ * by scanning every finite magnitude; magnitudes beyond 448 give 448
+ * (saturation); NaN gives 0x7f; the sign of zero is kept. */
+int oracle_e4m3_encode(double v) {
+  if (v != v) return 0x7f;
+  int sign = signbit(v) ? 0x80 : 0;
+  double a = fabs(v);
+  int bc = 0;
+  double best = 0.0;
+  for (int c = 1; c <= 0x7e; ++c) {
+    double m = oracle_e4m3_decode(c);
+    double dc = fabs(a - m), db = fabs(a - best);
+    if (dc < db || (dc == db && (c & 1) == 0)) {
+      best = m;
+      bc = c;
+    }
+  }
+  return sign | bc;
+}
+
+/* Per-row quantization of a weight matrix w[rows][K] (fp32 or bf16 values):
+ * scale s = amax / 448 and code = E4M3(w / s), both divisions in IEEE single
+ * precision (a zero row gets s = 1); the value a code stands for is
+ * decode(code) * s.  The single-precision arithmetic is part of the format's
+ * definition here, so that the codes are reproducible bit for bit. */
+void oracle_quantize_fp8_rows(int rows, int K, const double* w, uint8_t* codes,
+                              double* scales) {
+  for (int r = 0; r < rows; ++r) {
+    double amax = 0.0;
+    for (int k = 0; k < K; ++k) {
+      double a = fabs(w[(size_t)r * K + k]);
+      if (a > amax) amax = a;
+    }
+    float s = amax > 0.0 ? (float)amax / 448.0f : 1.0f;
+    scales[r] = s;
+    for (int k = 0; k < K; ++k) {
+      float q = (float)w[(size_t)r * K + k] / s;
+      codes[(size_t)r * K + k] = (uint8_t)oracle_e4m3_encode(q);
+    }
+  }
+}
+
 /* Router z-loss statistic.  [WIKI] part 2: the z-loss penalises the L2 norm
  * of the logits the gate feeds to its softmax.  Read as the squared norm,
  * summed over tokens: sum_t sum_j Z[t][j]^2 (the caller divides by T). */

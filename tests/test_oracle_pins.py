@@ -652,3 +652,67 @@ def test_hierarchical_matches_dense_two_level_sum():
                 imp[g * b + e] += wp[s] * w
     np.testing.assert_allclose(out["y"], y, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(out["gate"]["importance"], imp, rtol=1e-12, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 expert weights
+# ---------------------------------------------------------------------------
+
+def test_e4m3_decode_every_code_matches_torch():
+    """All 256 codes against torch's float8_e4m3fn decoding (NaN at
+    S.1111.111, signed zero, subnormals below 2^-6, largest 448)."""
+    ours = oracle.e4m3_decode(np.arange(256))
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan) and nan.sum() == 2
+    np.testing.assert_array_equal(ours[~nan], ref[~nan])
+    np.testing.assert_array_equal(np.signbit(ours[~nan]), np.signbit(ref[~nan]))
+    assert ours[0x7e] == 448.0 and ours[0x08] == 2.0 ** -6 and ours[0x01] == 2.0 ** -9
+
+
+def test_e4m3_encode_matches_torch_rounding():
+    """Round to nearest even against torch's float -> float8_e4m3fn cast, on
+    every code value, every midpoint between neighbours (the ties), points
+    just off the midpoints and random values in [-448, 448]."""
+    mags = oracle.e4m3_decode(np.arange(0x7f))
+    mids = (mags[:-1] + mags[1:]) / 2
+    vals = np.concatenate([mags, mids, np.nextafter(mids, 0), np.nextafter(mids, 1000),
+                           np.random.default_rng(0).uniform(-448, 448, 4000)])
+    vals = np.concatenate([vals, -vals]).astype(np.float32).astype(np.float64)
+    ours = oracle.e4m3_encode(vals)
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(ours, ref)
+    # beyond the largest finite value the encoder saturates
+    np.testing.assert_array_equal(oracle.e4m3_encode([460.0, -1e6]), [0x7e, 0xfe])
+
+
+def test_fp8_row_quantization_closed_form_and_bound():
+    """Row (1, -2, 0.5, 4): scale 4/448 in single precision, codes of 112,
+    -224, 56, 448; a zero row gets scale 1 and zero codes.  On random rows
+    every dequantized value is within half an E4M3 step of the weight:
+    2^-4 relative for normals, 2^-10 * scale below 2^-6 * scale."""
+    c, s = oracle.quantize_fp8_rows(np.array([[1, -2, 0.5, 4], [0, 0, 0, 0]], float))
+    assert s[0] == float(np.float32(4.0) / np.float32(448.0)) and s[1] == 1.0
+    np.testing.assert_array_equal(c[0], oracle.e4m3_encode([112, -224, 56, 448]))
+    np.testing.assert_array_equal(c[1], 0)
+    w = oracle.bf16_round(np.random.default_rng(1).standard_normal((16, 64)) * 0.05)
+    c, s = oracle.quantize_fp8_rows(w)
+    deq = oracle.dequantize_fp8_rows(c, s)
+    bound = np.maximum(np.abs(w) * 2.0 ** -4, 2.0 ** -10 * s[:, None]) * (1 + 1e-6)
+    assert np.all(np.abs(deq - w) <= bound)
+    assert np.allclose(np.max(np.abs(deq), axis=1), 448 * s, rtol=1e-6)
+
+
+def test_fp8_expert_single_expert_numpy():
+    """One expert with FP8 weights: the oracle FFN on the dequantized weights
+    equals a numpy dense FFN over the same values (bf16 activations)."""
+    rng = np.random.default_rng(6)
+    T, d, h = 7, 64, 128
+    x = rng.standard_normal((T, d))
+    w1 = oracle.bf16_round(rng.standard_normal((h, d)) / 8)
+    w2 = oracle.bf16_round(rng.standard_normal((d, h)) / 11)
+    q1 = oracle.dequantize_fp8_rows(*oracle.quantize_fp8_rows(w1))
+    q2 = oracle.dequantize_fp8_rows(*oracle.quantize_fp8_rows(w2))
+    y = oracle.expert_ffn(x, q1, q2, bf16=True)
+    hid = oracle.bf16_round(np.maximum(oracle.bf16_round(x) @ q1.T, 0))
+    np.testing.assert_allclose(y, hid @ q2.T, rtol=1e-12, atol=1e-12)
