@@ -53,7 +53,7 @@ def kernel_work(name, cfg, rows, nonempty, T):
     """(algorithmic bytes, flops, dtype) of one launch of kernel `name` for
     this step's realised routing."""
     d, h, n, k = cfg.d_model, cfg.d_hidden, cfg.n_experts, cfg.k
-    bf = cfg.expert_dtype == 1
+    bf = cfg.expert_dtype != 0
     wsz = 2 if bf else 4
     noisy = cfg.noisy
     ncols = 2 * n if noisy else n
@@ -64,6 +64,16 @@ def kernel_work(name, cfg, rows, nonempty, T):
                 "bf16")
     if name == "ggemm_bf16_out":
         return (nonempty * d * h * 2 + rows * h * 2 + rows * d * 4, 2.0 * rows * d * h, "bf16")
+    # FP8 experts: one byte per weight plus one fp32 scale per weight row
+    if name == "ggemm_fp8_relu":
+        return (nonempty * (h * d + 4 * h) + rows * d * 2 + rows * h * 2, 2.0 * rows * h * d,
+                "bf16")
+    if name == "ggemm_fp8_swiglu":
+        return (nonempty * 2 * (h * d + 4 * h) + rows * d * 2 + rows * h * 2,
+                4.0 * rows * h * d, "bf16")
+    if name == "ggemm_fp8_out":
+        return (nonempty * (d * h + 4 * d) + rows * h * 2 + rows * d * 4, 2.0 * rows * d * h,
+                "bf16")
     hs = cfg.d_hidden_shared
     if name == "shared_bf16_relu":
         return (hs * d * 2 + T * d * 2 + T * hs * 2, 2.0 * T * hs * d, "bf16")
@@ -315,7 +325,8 @@ def main():
         "config": {"workload": cfg.name, "T": T, "d_model": cfg.d_model,
                    "d_hidden": cfg.d_hidden, "n_experts": n, "k": k,
                    "gate": gate_text(cfg),
-                   "experts": ("bf16 " if cfg.expert_dtype == 1 else "fp32 ")
+                   "experts": {0: "fp32 ", 1: "bf16 ", 2: "FP8 E4M3 weights, bf16 activations, "}[
+                       cfg.expert_dtype]
                    + ("SwiGLU" if cfg.act == 1 else "ReLU") + " FFN, fp32 accumulate"
                    + (f", shared expert h={cfg.d_hidden_shared}" if cfg.d_hidden_shared else ""),
                    "rows": rows, "nonempty_experts": nonempty, "parallelism": "none (1 GPU)"},

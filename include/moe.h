@@ -70,7 +70,12 @@ typedef enum {
   MOE_ACT_SWIGLU = 1 /* E(u) = (silu(u W1^T) * (u W3^T)) W2^T; bf16 experts only */
 } moe_act;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+typedef enum {
+  MOE_F32 = 0,
+  MOE_BF16 = 1,
+  MOE_FP8 = 2 /* expert weights only: packed E4M3 codes with a per-row scale (see
+                 moe_pack_fp8_weights); activations stay bf16 */
+} moe_dtype;
 
 /* Layer shape and options.  All fields are 4 bytes. */
 typedef struct {
@@ -81,7 +86,8 @@ typedef struct {
   int32_t k;              /* experts per token, 1..min(n,64) (two-level: k1*k2) */
   int32_t gate;           /* moe_gate_kind */
   int32_t act;            /* moe_act */
-  int32_t expert_dtype;   /* moe_dtype of w1/w3/w2 and of x_perm */
+  int32_t expert_dtype;   /* moe_dtype of w1/w3/w2; x_perm is fp32 for MOE_F32, else bf16.
+                             MOE_FP8 needs d_model and d_hidden multiples of 64 */
   int32_t n_groups;       /* two-level layer: a groups of b = n/a experts; 0 = flat */
   int32_t k_groups;       /* two-level layer: k1 groups per token, k = k1*k2 */
   float capacity_factor;  /* > 0: expert capacity floor(cf*T*k/n); <= 0: none */
@@ -124,6 +130,26 @@ typedef struct {
   int32_t* perm;       /* [T*k] */
   int32_t* slot_pos;   /* [T, k] */
 } moe_diag;
+
+/* FP8 expert weights.  Definition: the MoE survey's DeepSeek-V3 summary
+ * (tufusi.com, section 9: FP8 for the main computation), read as E4M3 codes
+ * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; largest finite 448;
+ * the "e4m3fn" variant) with one fp32 scale per output row:
+ *   scale = amax(row) / 448 (1 for an all-zero row), code = E4M3(w / scale),
+ * both divisions in IEEE single precision, nearest code with ties to an
+ * even mantissa, saturating at 448.  The expert computes with the value
+ * decode(code) * scale; activations stay bf16.
+ * Packed layout of one [N, K] matrix (N % 8 == 0, K % 64 == 0), N*K + 4*N bytes:
+ * the codes of rows 2p, 2p+1 over columns 64b..64b+63 are the 128 bytes at
+ * offset (p*(K/64) + b)*128 (row 2p first), then the N fp32 scales.
+ * n_experts such matrices follow one another.
+ * moe_fp8_weight_bytes: bytes of n_experts packed [N, K] matrices (0 on
+ * invalid sizes).  moe_pack_fp8_weights: src [n_experts, N, K] of src_dtype
+ * (MOE_F32 or MOE_BF16) -> dst (that many bytes, 16-byte aligned), on
+ * `stream`.  Pack w1 and w3 as [n, h, d] and w2 as [n, d, h]. */
+size_t moe_fp8_weight_bytes(int32_t n_experts, int32_t N, int32_t K);
+moe_status moe_pack_fp8_weights(int32_t n_experts, int32_t N, int32_t K, int32_t src_dtype,
+                                const void* src, void* dst, void* stream);
 
 /* Bytes of workspace that every call below accepts as sufficient (the
  * forward's need; each stage needs at most this).  0 on an invalid config. */

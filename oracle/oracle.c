@@ -236,24 +236,38 @@ double oracle_e4m3_decode(int code) {
   return (code & 0x80) ? -v : v;
 }
 
-/* Nearest E4M3 value, ties to the even code (round to nearest even), found
- * by scanning every finite magnitude; magnitudes beyond 448 give 448
- * (saturation); NaN gives 0x7f; the sign of zero is kept. */
+/* Nearest E4M3 value, ties to the even code (round to nearest even):
+ * the finite magnitudes, in code order 0..0x7e, increase; bisect for the
+ * first one >= |v| and take the nearer of it and its predecessor (the even
+ * code on a tie).  Magnitudes beyond 448 give 448 (saturation); NaN gives
+ * 0x7f; the sign of zero is kept. */
+static double e4m3_mag[0x7f]; /* decode(c) for the finite codes 0..0x7e */
+static int e4m3_mag_ready = 0;
+
+static void e4m3_table(void) {
+  if (e4m3_mag_ready) return;
+  for (int c = 0; c <= 0x7e; ++c) e4m3_mag[c] = oracle_e4m3_decode(c);
+  e4m3_mag_ready = 1;
+}
+
 int oracle_e4m3_encode(double v) {
   if (v != v) return 0x7f;
+  e4m3_table();
   int sign = signbit(v) ? 0x80 : 0;
   double a = fabs(v);
-  int bc = 0;
-  double best = 0.0;
-  for (int c = 1; c <= 0x7e; ++c) {
-    double m = oracle_e4m3_decode(c);
-    double dc = fabs(a - m), db = fabs(a - best);
-    if (dc < db || (dc == db && (c & 1) == 0)) {
-      best = m;
-      bc = c;
-    }
+  if (a >= 448.0) return sign | 0x7e;
+  int lo = 0, hi = 0x7e; /* find the first code with decode >= a */
+  while (lo < hi) {
+    int mid = (lo + hi) / 2;
+    if (e4m3_mag[mid] < a) lo = mid + 1;
+    else hi = mid;
   }
-  return sign | bc;
+  int c = lo; /* decode(c) >= a, decode(c - 1) < a (or c == 0) */
+  if (c > 0) {
+    double up = e4m3_mag[c] - a, down = a - e4m3_mag[c - 1];
+    if (down < up || (down == up && ((c - 1) & 1) == 0)) c = c - 1;
+  }
+  return sign | c;
 }
 
 /* Per-row quantization of a weight matrix w[rows][K] (fp32 or bf16 values):
@@ -263,6 +277,8 @@ int oracle_e4m3_encode(double v) {
  * definition here, so that the codes are reproducible bit for bit. */
 void oracle_quantize_fp8_rows(int rows, int K, const double* w, uint8_t* codes,
                               double* scales) {
+  e4m3_table();
+#pragma omp parallel for schedule(static)
   for (int r = 0; r < rows; ++r) {
     double amax = 0.0;
     for (int k = 0; k < K; ++k) {

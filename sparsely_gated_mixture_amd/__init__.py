@@ -12,12 +12,31 @@ from . import workloads
 from ._lib import (EXPORTS, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED,
                    MOE_ERR_WORKSPACE, MOE_OK, N_LOSSES, MoeConfig, MoeDiag, MoEError,
                    MoeWeights, load_library, make_config, make_diag, make_weights,
-                   moe_aux_loss, moe_combine, moe_dispatch, moe_expert_ffn, moe_forward,
+                   moe_aux_loss, moe_combine, moe_dispatch, moe_expert_ffn,
+                   moe_fp8_weight_bytes, moe_forward, moe_pack_fp8_weights,
                    moe_gate, moe_gate_hier, moe_last_error, moe_profile_collect,
                    moe_profile_enable, moe_profile_entry, moe_router_bias_update,
                    moe_shared_ffn, moe_status_string, moe_workspace_size)
 
 load_library()
+
+MOE_F32, MOE_BF16, MOE_FP8 = 0, 1, 2
+
+
+def pack_fp8(w, stream=None):
+    """Pack a [n, N, K] (or [N, K]) bf16 / fp32 device tensor of expert
+    weights into the library's FP8 E4M3 layout (uint8 tensor)."""
+    import torch
+    w3 = w if w.dim() == 3 else w.unsqueeze(0)
+    n, N, K = w3.shape
+    size = moe_fp8_weight_bytes(n, N, K)
+    if size == 0:
+        raise MoEError(MOE_ERR_UNSUPPORTED, f"cannot pack a [{n}, {N}, {K}] matrix as FP8")
+    out = torch.empty(size, dtype=torch.uint8, device=w.device)
+    src = w3.contiguous()
+    moe_pack_fp8_weights(n, N, K, MOE_BF16 if src.dtype == torch.bfloat16 else MOE_F32, src, out,
+                         stream)
+    return out
 
 
 class MoELayer:
@@ -30,6 +49,14 @@ class MoELayer:
         self.cfg = cfg
         self.c = make_config(cfg)
         self.device = device
+        if int(cfg.expert_dtype) == MOE_FP8:
+            # FP8 experts: pack bf16 / fp32 weights once (already packed
+            # uint8 buffers pass through).
+            weights = dict(weights)
+            for name in ("w1", "w3", "w2"):
+                t = weights.get(name)
+                if t is not None and t.dtype != torch.uint8:
+                    weights[name] = pack_fp8(t)
         self.weights = weights
         self.w = make_weights(weights["w_gate"], weights.get("b_gate"), weights.get("w_noise"),
                               weights.get("w_gate2"), weights.get("w_noise2"), weights["w1"],
@@ -52,7 +79,8 @@ class MoELayer:
         return y, losses
 
 
-__all__ = ["workloads", "EXPORTS", "MoELayer", "MoEError", "MoeConfig", "MoeWeights", "MoeDiag",
+__all__ = ["workloads", "EXPORTS", "MoELayer", "pack_fp8", "moe_fp8_weight_bytes",
+           "moe_pack_fp8_weights", "MOE_F32", "MOE_BF16", "MOE_FP8", "MoEError", "MoeConfig", "MoeWeights", "MoeDiag",
            "make_config", "make_weights", "make_diag", "moe_workspace_size", "moe_gate",
            "moe_gate_hier", "moe_dispatch", "moe_expert_ffn", "moe_shared_ffn", "moe_combine",
            "moe_aux_loss", "moe_router_bias_update", "moe_forward", "N_LOSSES", "moe_status_string", "moe_last_error", "moe_profile_enable",

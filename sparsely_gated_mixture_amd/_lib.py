@@ -20,7 +20,7 @@ MOE_ERR_UNSUPPORTED = 2
 MOE_ERR_WORKSPACE = 3
 MOE_ERR_HIP = 4
 
-EXPORTS = ["moe_workspace_size", "moe_gate", "moe_gate_hier", "moe_dispatch", "moe_expert_ffn",
+EXPORTS = ["moe_workspace_size", "moe_fp8_weight_bytes", "moe_pack_fp8_weights", "moe_gate", "moe_gate_hier", "moe_dispatch", "moe_expert_ffn",
            "moe_shared_ffn", "moe_combine", "moe_aux_loss", "moe_router_bias_update",
            "moe_forward", "moe_status_string", "moe_last_error", "moe_profile_enable",
            "moe_profile_collect", "moe_profile_entry"]
@@ -77,6 +77,11 @@ def load_library():
     cfgp = ctypes.POINTER(MoeConfig)
     L.moe_workspace_size.argtypes = [cfgp]
     L.moe_workspace_size.restype = S
+    i32 = ctypes.c_int32
+    L.moe_fp8_weight_bytes.argtypes = [i32, i32, i32]
+    L.moe_fp8_weight_bytes.restype = S
+    L.moe_pack_fp8_weights.argtypes = [i32, i32, i32, i32, P, P, P]
+    L.moe_pack_fp8_weights.restype = ctypes.c_int
     L.moe_gate.argtypes = [cfgp] + [P] * 10 + [P, S, P]
     L.moe_gate_hier.argtypes = [cfgp] + [P] * 13 + [P, S, P]
     L.moe_dispatch.argtypes = [cfgp] + [P] * 8 + [P, S, P]
@@ -161,6 +166,15 @@ def moe_last_error() -> str:
 def moe_workspace_size(cfg) -> int:
     c = make_config(cfg)
     return load_library().moe_workspace_size(ctypes.byref(c))
+
+
+def moe_fp8_weight_bytes(n_experts: int, N: int, K: int) -> int:
+    return load_library().moe_fp8_weight_bytes(int(n_experts), int(N), int(K))
+
+
+def moe_pack_fp8_weights(n_experts, N, K, src_dtype, src, dst, stream=None):
+    _check(load_library().moe_pack_fp8_weights(int(n_experts), int(N), int(K), int(src_dtype),
+                                               _ptr(src), _ptr(dst), _stream(stream)))
 
 
 def moe_gate(cfg, x, w_gate, b_gate, w_noise, noise, topk_idx, topk_w, importance, load,

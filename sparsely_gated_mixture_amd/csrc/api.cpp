@@ -77,18 +77,21 @@ moe_status validate(const moe_config* c) {
     return fail(MOE_ERR_INVALID_ARG, "unknown gate kind %d", c->gate);
   if (c->act != MOE_ACT_RELU && c->act != MOE_ACT_SWIGLU)
     return fail(MOE_ERR_INVALID_ARG, "unknown activation %d", c->act);
-  if (c->expert_dtype != MOE_F32 && c->expert_dtype != MOE_BF16)
+  if (c->expert_dtype != MOE_F32 && c->expert_dtype != MOE_BF16 && c->expert_dtype != MOE_FP8)
     return fail(MOE_ERR_INVALID_ARG, "unknown expert dtype %d", c->expert_dtype);
+  if (c->expert_dtype == MOE_FP8 && (c->d_model % 64 || c->d_hidden % 64))
+    return fail(MOE_ERR_UNSUPPORTED, "FP8 experts need d_model (%d) and d_hidden (%d) to be "
+                "multiples of 64", c->d_model, c->d_hidden);
   if (c->gate == MOE_GATE_SWITCH_TOP1 && c->k != 1)
     return fail(MOE_ERR_INVALID_ARG, "the Switch router needs k = 1");
-  if (c->act == MOE_ACT_SWIGLU && c->expert_dtype != MOE_BF16)
-    return fail(MOE_ERR_UNSUPPORTED, "SwiGLU experts are implemented for bf16 only");
+  if (c->act == MOE_ACT_SWIGLU && c->expert_dtype == MOE_F32)
+    return fail(MOE_ERR_UNSUPPORTED, "SwiGLU experts are implemented for bf16 and FP8 only");
   if (!std::isfinite(c->capacity_factor))
     return fail(MOE_ERR_INVALID_ARG, "capacity_factor must be finite");
   if (c->d_hidden_shared < 0 || c->d_hidden_shared % 8)
     return fail(MOE_ERR_INVALID_ARG, "d_hidden_shared must be a non-negative multiple of 8");
   if (c->d_hidden_shared > 0 && c->expert_dtype != MOE_BF16)
-    return fail(MOE_ERR_UNSUPPORTED, "the shared expert is implemented for bf16 only");
+    return fail(MOE_ERR_UNSUPPORTED, "the shared expert is implemented for bf16 experts only");
   if (c->n_experts > kMaxExperts)
     return fail(MOE_ERR_UNSUPPORTED, "n_experts must be <= %d", kMaxExperts);
   if ((long long)c->T * c->k > (1LL << 30))
@@ -253,12 +256,12 @@ Plan make_plan(const moe_config& c) {
   p.dispatch_bytes = dsp.at;
   // ffn scratch
   Cursor f{0};
-  p.ffn_bm = c.expert_dtype == MOE_BF16 ? kBf16BM : kF32ExpertBM;
+  p.ffn_bm = c.expert_dtype != MOE_F32 ? kBf16BM : kF32ExpertBM;
   p.max_mtiles = (int)((A + p.ffn_bm - 1) / p.ffn_bm + n);
   p.t_expert = f.take((size_t)p.max_mtiles * 4);
   p.t_row0 = f.take((size_t)p.max_mtiles * 4);
   p.t_count = f.take(4);
-  p.hidden = f.take(std::max(1LL, A) * h * (c.expert_dtype == MOE_BF16 ? 2 : 4));
+  p.hidden = f.take(std::max(1LL, A) * h * (c.expert_dtype != MOE_F32 ? 2 : 4));
   p.ffn_bytes = f.at;
   p.stage_bytes = std::max(p.gate_bytes, std::max(p.dispatch_bytes, p.ffn_bytes));
   // forward intermediates
@@ -273,7 +276,7 @@ Plan make_plan(const moe_config& c) {
   p.f_offsets = w.take((n + 1) * 4);
   p.f_perm = w.take(A1 * 4);
   p.f_slot = w.take(A1 * 4);
-  p.f_xperm = w.take(A1 * d * (c.expert_dtype == MOE_BF16 ? 2 : 4));
+  p.f_xperm = w.take(A1 * d * (c.expert_dtype != MOE_F32 ? 2 : 4));
   p.f_yperm = w.take(A1 * d * 4);
   p.f_tile_expert = w.take((size_t)p.max_mtiles * 4);
   p.f_tile_row0 = w.take((size_t)p.max_mtiles * 4);
@@ -534,7 +537,7 @@ moe_status run_dispatch(const moe_config& c, const Plan& p, const int32_t* topk_
     da.w_ent = c.w_entropy;
   }
   HIP_TRY(launch_dispatch(da, s));
-  HIP_TRY(launch_gather(x, slot_pos, c.T, c.k, c.d_model, c.expert_dtype == MOE_BF16, x_perm,
+  HIP_TRY(launch_gather(x, slot_pos, c.T, c.k, c.d_model, c.expert_dtype != MOE_F32, x_perm,
                         fx ? fx->x_bf16 : nullptr, s));
   return MOE_OK;
 }
@@ -551,13 +554,15 @@ moe_status run_ffn(const moe_config& c, const Plan& p, const void* x_perm,
   int32_t* tc = fx ? fx->tile_count : at<int32_t>(ws, p.t_count);
   void* hidden = at<void>(ws, p.hidden);
   if (!fx) HIP_TRY(launch_tilemap(offsets, n, p.ffn_bm, te, tr, tc, s));
-  if (c.expert_dtype == MOE_BF16) {
+  if (c.expert_dtype != MOE_F32) {
+    const bool fp8 = c.expert_dtype == MOE_FP8;
     GemmBf16Args g{};
     g.A = (const uint16_t*)x_perm;
     g.lda = d;
-    g.B1 = (const uint16_t*)w1;
-    g.B3 = (const uint16_t*)w3;
-    g.strideB = (long long)h * d;
+    g.B1 = w1;
+    g.B3 = w3;
+    g.strideB = fp8 ? (long long)h * d + 4LL * h : (long long)h * d * 2;
+    g.fp8 = fp8;
     g.N = h;
     g.K = d;
     g.C = hidden;
@@ -573,9 +578,9 @@ moe_status run_ffn(const moe_config& c, const Plan& p, const void* x_perm,
     GemmBf16Args g2 = g;
     g2.A = (const uint16_t*)hidden;
     g2.lda = h;
-    g2.B1 = (const uint16_t*)w2;
+    g2.B1 = w2;
     g2.B3 = nullptr;
-    g2.strideB = (long long)d * h;
+    g2.strideB = fp8 ? (long long)d * h + 4LL * d : (long long)d * h * 2;
     g2.N = d;
     g2.K = h;
     g2.C = y_perm;
@@ -636,8 +641,8 @@ moe_status run_shared_ffn(const moe_config& c, const Plan& p, const uint16_t* xb
   GemmBf16Args g{};
   g.A = xb;
   g.lda = d;
-  g.B1 = (const uint16_t*)ws1;
-  g.B3 = (const uint16_t*)ws3;
+  g.B1 = ws1;
+  g.B3 = ws3;
   g.strideB = 0;
   g.N = hs;
   g.K = d;
@@ -654,7 +659,7 @@ moe_status run_shared_ffn(const moe_config& c, const Plan& p, const uint16_t* xb
   GemmBf16Args g2 = g;
   g2.A = hidden;
   g2.lda = hs;
-  g2.B1 = (const uint16_t*)ws2;
+  g2.B1 = ws2;
   g2.B3 = nullptr;
   g2.N = d;
   g2.K = hs;
@@ -690,6 +695,28 @@ moe_status check_gate_ptrs(const moe_config& c, const float* x, const float* w_g
 }  // namespace
 
 extern "C" {
+
+size_t moe_fp8_weight_bytes(int32_t n_experts, int32_t N, int32_t K) {
+  if (n_experts < 0 || N <= 0 || K <= 0 || N % 8 || K % 64) return 0;
+  return (size_t)n_experts * ((size_t)N * K + 4 * (size_t)N);
+}
+
+moe_status moe_pack_fp8_weights(int32_t n_experts, int32_t N, int32_t K, int32_t src_dtype,
+                                const void* src, void* dst, void* stream) {
+  g_err[0] = 0;
+  if (n_experts < 0 || N <= 0 || K <= 0)
+    return fail(MOE_ERR_INVALID_ARG, "n_experts >= 0, N > 0 and K > 0 required");
+  if (N % 8 || K % 64)
+    return fail(MOE_ERR_UNSUPPORTED, "FP8 packing needs N %% 8 == 0 and K %% 64 == 0 (N=%d, K=%d)",
+                N, K);
+  if (src_dtype != MOE_F32 && src_dtype != MOE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "src_dtype must be MOE_F32 or MOE_BF16");
+  if (n_experts > 65535) return fail(MOE_ERR_UNSUPPORTED, "at most 65535 experts per call");
+  CHECK(need(src, "src", n_experts == 0));
+  CHECK(need(dst, "dst", n_experts == 0));
+  HIP_TRY(launch_pack_fp8(n_experts, N, K, src_dtype == MOE_BF16, src, dst, (hipStream_t)stream));
+  return MOE_OK;
+}
 
 size_t moe_workspace_size(const moe_config* cfg) {
   if (validate(cfg) != MOE_OK) return 0;

@@ -49,7 +49,6 @@ namespace {
 constexpr int kBM = kBf16BM;  // rows per M-tile (the tile map's granularity)
 constexpr int kBK = 64;       // K per pipeline step
 constexpr int kRowB = 128;    // bytes per LDS row (kBK bf16)
-constexpr int kStages = 3;    // LDS ring depth
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 
@@ -91,21 +90,44 @@ __device__ __forceinline__ void wait_vm_upto(int n) {
 
 __device__ __forceinline__ int swz(int r, int c) { return (c ^ ((r >> 1) & 7)) << 4; }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Eight E4M3 codes (bytes of `raw`, lowest first) as eight bf16 values.
+// Every E4M3 value is exact in bf16, so the widening loses nothing.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint2 raw) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.x, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.x, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.y, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.y, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 // HAS_BIAS is a template parameter so that the usual bias-free kernels have
 // no global loads in the epilogue (the compiler would otherwise wait there
 // for every copy in flight).
-template <int BN, int EPI, int WGM, bool HAS_BIAS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void ggemm_bf16_kernel(const GemmBf16Args p) {
+//
+// FP8: the weights are E4M3 codes in the packed layout of
+// moe_pack_fp8_weights (row pairs, 128 bytes per pair and 64-wide K block,
+// then one fp32 scale per row).  A weight row takes 64 bytes of LDS per step,
+// so a step is 32 KB and the ring is 4 deep; fragments are read as 8 bytes,
+// widened to bf16 in registers, and each output row is multiplied by its
+// scale in the epilogue.
+template <int BN, int EPI, int WGM, bool HAS_BIAS, bool FP8>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+ggemm_bf16_kernel(const GemmBf16Args p) {
   constexpr int NB = (EPI == EPI_SWIGLU_BF16) ? 2 : 1;  // weight matrices per tile
   constexpr int BROWS = NB * BN;                         // weight rows per tile
-  constexpr int A_BYTES = kBM * kRowB, B_BYTES = BROWS * kRowB;
+  constexpr int kStages = FP8 ? 4 : 3;                   // LDS ring depth
+  constexpr int B_ROWB = FP8 ? 64 : kRowB;               // LDS bytes per weight row
+  constexpr int A_BYTES = kBM * kRowB, B_BYTES = BROWS * B_ROWB;
   constexpr int STAGE = A_BYTES + B_BYTES;
   constexpr int ADMA = A_BYTES / 1024 / kWaves, BDMA = B_BYTES / 1024 / kWaves;
-  constexpr int PER_STEP = ADMA + BDMA;  // copies per thread per step
+  constexpr int PER_STEP = ADMA + BDMA;  // copies per thread per step (at most)
   constexpr int WGN = kWaves / WGM;
   constexpr int WM = kBM / WGM, WN = BN / WGN;
   constexpr int FM = WM / 32, FN = WN / 32;
   static_assert(ADMA >= 1 && BDMA >= 1 && FM >= 1 && FN >= 1, "bad tile shape");
+  static_assert(BN % 16 == 0, "a copy block must not straddle the two weight matrices");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * STAGE];
   __shared__ int4 meta[kMaxTilesPerWG];  // per tile: expert, first row, end row, first column
 
@@ -137,62 +159,75 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
   // Copy cursor: the next step to copy is step gi (tile it, K-step ikt).
-  // Each lane keeps the global address of its rows' 16-byte chunk for the
-  // cursor's tile (row blk*8 + lane/8, chunk (lane%8) swizzled), recomputed
-  // only when the cursor enters a new tile.
-  const uint16_t* a_src[ADMA];
-  const uint16_t* b_src[BDMA];
-  int a_chunk[ADMA], b_chunk[BDMA];  // element offset of the lane's chunk within a step
+  // Each lane keeps the global address of the 16 bytes it copies for the
+  // cursor's tile (both layouts advance 128 bytes per K-step), recomputed
+  // only when the cursor enters a new tile.  Activations: row blk*8 +
+  // lane/8, chunk (lane%8) swizzled.  bf16 weights: the same.  FP8 weights:
+  // row blk*16 + lane/4, 16-byte chunk (lane%4) swizzled.
+  const uint8_t* a_src[ADMA];
+  const uint8_t* b_src[BDMA];
+  int a_chunk[ADMA], b_chunk[BDMA];  // element offset of the lane's chunk (bf16 K tail)
   int gi = 0, it = 0, ikt = 0;
-  int a_live = 0;    // copies j < a_live of the activation tile hold real rows
-  int last_cnt = 0;  // copies this wave issued for the most recent step
+  int a_live = 0;                    // copies j < a_live of the activation tile hold real rows
+  int cnt_last = 0, cnt_prev = 0;    // copies of the two most recently copied steps
   auto set_tile = [&](int ti) {
     const int4 m = meta[ti];
     // Row groups (8 rows per copy) past the segment's end are not copied:
     // their LDS rows only ever feed output columns that are not stored.
     a_live = 0;
 #pragma unroll
-    for (int j = 0; j < ADMA; ++j) a_live += m.y + (wave + kWaves * j) * 8 < m.z ? 1 : 0;
-#pragma unroll
     for (int j = 0; j < ADMA; ++j) {
       const int r = (wave + kWaves * j) * 8 + (lane >> 3);
+      a_live += m.y + (wave + kWaves * j) * 8 < m.z ? 1 : 0;
       a_chunk[j] = ((lane & 7) ^ ((r >> 1) & 7)) * 8;
-      a_src[j] = p.A + (long long)min(m.y + r, m.z - 1) * p.lda + a_chunk[j];
+      a_src[j] = (const uint8_t*)(p.A + (long long)min(m.y + r, m.z - 1) * p.lda + a_chunk[j]);
     }
 #pragma unroll
     for (int j = 0; j < BDMA; ++j) {
-      const int r = (wave + kWaves * j) * 8 + (lane >> 3);
-      const int which = r / BN, rn = r % BN;
-      const uint16_t* w = (which == 0 ? p.B1 : p.B3) + (long long)m.x * p.strideB;
-      b_chunk[j] = ((lane & 7) ^ ((r >> 1) & 7)) * 8;
-      b_src[j] = w + (long long)min(m.w + rn, p.N - 1) * K + b_chunk[j];
+      if constexpr (FP8) {
+        const int r = (wave + kWaves * j) * 16 + (lane >> 2);
+        const int which = r / BN, rn = r % BN;
+        const int n = min(m.w + rn, p.N - 1);
+        const uint8_t* w = (const uint8_t*)(which == 0 ? p.B1 : p.B3) + (long long)m.x * p.strideB;
+        const int lc = (lane & 3) ^ ((r >> 1) & 3);  // logical 16-byte chunk of this slot
+        b_chunk[j] = 0;
+        b_src[j] = w + ((long long)(n >> 1) * (K / 64)) * 128 + (n & 1) * 64 + lc * 16;
+      } else {
+        const int r = (wave + kWaves * j) * 8 + (lane >> 3);
+        const int which = r / BN, rn = r % BN;
+        const uint8_t* w = (const uint8_t*)(which == 0 ? p.B1 : p.B3) + (long long)m.x * p.strideB;
+        b_chunk[j] = ((lane & 7) ^ ((r >> 1) & 7)) * 8;
+        b_src[j] = w + ((long long)min(m.w + rn, p.N - 1) * K + b_chunk[j]) * 2;
+      }
     }
   };
-  // Copy step gi into ring slot gi % kStages and advance the cursor.  A step
-  // that reaches past K copies a 16-byte zero constant for the chunks beyond
-  // it (same number of copies per step).
+  // Copy step gi into ring slot gi % kStages and advance the cursor.  A bf16
+  // step that reaches past K copies a 16-byte zero constant for the chunks
+  // beyond it (FP8 weights need K % 64 == 0).
   auto issue_next = [&]() {
     const uint32_t sb = lds0 + (gi % kStages) * STAGE;
     const int k0 = ikt * kBK;
-    if (k0 + kBK <= K) {
+    const long long adv = (long long)ikt * 128;
+    if (FP8 || k0 + kBK <= K) {
 #pragma unroll
       for (int j = 0; j < ADMA; ++j)
-        if (j < a_live) dma16(a_src[j] + k0, sb + (wave + kWaves * j) * 1024);
+        if (j < a_live) dma16(a_src[j] + adv, sb + (wave + kWaves * j) * 1024);
 #pragma unroll
       for (int j = 0; j < BDMA; ++j)
-        dma16(b_src[j] + k0, sb + A_BYTES + (wave + kWaves * j) * 1024);
+        dma16(b_src[j] + adv, sb + A_BYTES + (wave + kWaves * j) * 1024);
     } else {
 #pragma unroll
       for (int j = 0; j < ADMA; ++j)
         if (j < a_live)
-          dma16(k0 + a_chunk[j] < K ? (const void*)(a_src[j] + k0) : (const void*)kZeroChunk,
+          dma16(k0 + a_chunk[j] < K ? (const void*)(a_src[j] + adv) : (const void*)kZeroChunk,
                 sb + (wave + kWaves * j) * 1024);
 #pragma unroll
       for (int j = 0; j < BDMA; ++j)
-        dma16(k0 + b_chunk[j] < K ? (const void*)(b_src[j] + k0) : (const void*)kZeroChunk,
+        dma16(k0 + b_chunk[j] < K ? (const void*)(b_src[j] + adv) : (const void*)kZeroChunk,
               sb + A_BYTES + (wave + kWaves * j) * 1024);
     }
-    last_cnt = a_live + BDMA;
+    cnt_prev = cnt_last;
+    cnt_last = a_live + BDMA;
     ++gi;
     if (++ikt == nk) {
       ikt = 0;
@@ -223,16 +258,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if (gi < nsteps) issue_next();
 
   for (int g = 0; g < nsteps; ++g) {
-    // Steps copied after this one: at most kStages-2.  Wait until only the
-    // copies of step g+1 (last_cnt of them) may still be in flight; loads
-    // complete in order, so step g's copies have then landed.
+    // Steps copied after this one (at most kStages-2).  Wait until only
+    // their copies may still be in flight; loads complete in order, so
+    // step g's copies have then landed.
     const int ahead = min(nsteps, g + kStages - 1) - 1 - g;
-    static_assert(kStages == 3, "the waits below assume a 3-deep ring");
-    wait_vm_upto<PER_STEP>(ahead >= 1 ? last_cnt : 0);
+    static_assert(kStages == 3 || kStages == 4, "the waits below cover 3- or 4-deep rings");
+    wait_vm_upto<(kStages - 2) * PER_STEP>(ahead <= 0 ? 0 : ahead == 1 ? cnt_last
+                                                                      : cnt_last + cnt_prev);
     __syncthreads();
     if (g % nk == 0) cm = meta[g / nk];
-    // Every wave is past step g-1, so its ring slot can take step g+2 now,
-    // while this step computes.
+    // Every wave is past step g-1, so its ring slot can take step
+    // g+kStages-1 now, while this step computes.
     if (gi < nsteps) issue_next();
     const uint8_t* As = smem + (g % kStages) * STAGE;
     const uint8_t* Bs = As + A_BYTES;
@@ -240,8 +276,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // compute this tile.
     if (cm.y + wm * WM < cm.z) {
     // All fragments of the step first (the LDS reads overlap one another),
-    // then the MFMAs.
+    // then the MFMAs (FP8: the widening of slice kk runs beside the MFMAs
+    // of slice kk-1).
     bf16x8 xf[kBK / 16][FM], wf[kBK / 16][NB][FN];
+    uint2 wraw[kBK / 16][NB][FN];
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
       const int c = 2 * kk + lh;  // 32x32x16 operand: row lane%32, k = 8*(lane/32)..+7
@@ -255,11 +293,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const int r = b * BN + wn * WN + j * 32 + lr;
-          wf[kk][b][j] = *(const bf16x8*)(Bs + r * kRowB + swz(r, c));
+          if constexpr (FP8) {
+            wraw[kk][b][j] = *(const uint2*)(Bs + r * 64 + ((kk ^ ((r >> 1) & 3)) << 4) + lh * 8);
+          } else {
+            wf[kk][b][j] = *(const bf16x8*)(Bs + r * kRowB + swz(r, c));
+          }
         }
     }
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk)
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      if constexpr (FP8) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) wf[kk][b][j] = e4m3x8_to_bf16(wraw[kk][b][j]);
+      }
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -268,9 +316,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
           for (int j = 0; j < FN; ++j)
             acc[b][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[kk][b][j], xf[kk][i],
                                                                    acc[b][i][j], 0, 0, 0);
-    // Scheduling groups: every LDS read of the step, then every MFMA.
+    }
+    // Scheduling groups: every LDS read of the step, then the MFMAs (FP8:
+    // each slice's widening, 4 instructions per fragment, then its MFMAs).
     __builtin_amdgcn_sched_group_barrier(0x100, (kBK / 16) * (FM + NB * FN), 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, (kBK / 16) * NB * FM * FN, 0);
+    if constexpr (FP8) {
+#pragma unroll
+      for (int kk = 0; kk < kBK / 16; ++kk) {
+        __builtin_amdgcn_sched_group_barrier(0x002, 4 * NB * FN, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, NB * FM * FN, 0);
+      }
+    } else {
+      __builtin_amdgcn_sched_group_barrier(0x008, (kBK / 16) * NB * FM * FN, 0);
+    }
     }
 
     if (g % nk == nk - 1) {
@@ -279,6 +337,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const int4 m = cm;
       const int e = m.x, row_end = m.z;
       const float* bias = HAS_BIAS ? p.bias + (long long)e * p.N : nullptr;
+      // FP8: the row scales follow each expert's codes.
+      const float* sc1 = FP8 ? (const float*)((const uint8_t*)p.B1 + (long long)e * p.strideB +
+                                             (long long)p.N * K)
+                             : nullptr;
+      const float* sc3 = (FP8 && NB == 2) ? (const float*)((const uint8_t*)p.B3 +
+                                                           (long long)e * p.strideB +
+                                                           (long long)p.N * K)
+                                          : nullptr;
+      // FP8: this lane's row scales for every (j, q4), read once per tile;
+      // each group of 8 rows comes from a wave-uniform address (scalar loads).
+      float s1[FN][4][4], s3[FN][4][4];
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int gc0 = m.w + wn * WN + j * 32 + q4 * 8;  // first of 8 rows (N % 8 == 0)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) s1[j][q4][q] = s3[j][q4][q] = 1.f;
+          if constexpr (FP8) {
+            if (gc0 < p.N) {
+              float u1[8], u3[8];
+#pragma unroll
+              for (int q = 0; q < 8; ++q) {
+                u1[q] = sc1[gc0 + q];
+                u3[q] = NB == 2 ? sc3[gc0 + q] : 1.f;
+              }
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                s1[j][q4][q] = lh ? u1[4 + q] : u1[q];
+                s3[j][q4][q] = lh ? u3[4 + q] : u3[q];
+              }
+            }
+          }
+        }
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int gr = m.y + wm * WM + i * 32 + lr;
@@ -293,10 +385,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               if constexpr (EPI == EPI_SWIGLU_BF16) {
-                const float gv = acc[0][i][j][4 * q4 + q], uv = acc[NB - 1][i][j][4 * q4 + q];
+                const float gv = acc[0][i][j][4 * q4 + q] * s1[j][q4][q];
+                const float uv = acc[NB - 1][i][j][4 * q4 + q] * s3[j][q4][q];
                 f[q] = gv / (1.f + expf(-gv)) * uv;
               } else {
-                f[q] = acc[0][i][j][4 * q4 + q];
+                f[q] = acc[0][i][j][4 * q4 + q] * s1[j][q4][q];
                 if constexpr (HAS_BIAS) f[q] += bias[gc + q];
                 if constexpr (EPI == EPI_RELU_BF16) f[q] = fmaxf(f[q], 0.f);
               }
@@ -317,7 +410,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 }
 
-template <int BN, int EPI, int WGM, bool HAS_BIAS>
+template <int BN, int EPI, int WGM, bool HAS_BIAS, bool FP8>
 hipError_t launch_t(const GemmBf16Args& a, hipStream_t s) {
   const int nN = (a.N + BN - 1) / BN;
   const long long max_total = (long long)a.max_mtiles * nN;
@@ -328,31 +421,38 @@ hipError_t launch_t(const GemmBf16Args& a, hipStream_t s) {
   if (grid < kXcds) grid = kXcds;
   const long long per = (max_total + kXcds - 1) / kXcds;
   while ((per + grid / kXcds - 1) / (grid / kXcds) > kMaxTilesPerWG) grid += kXcds;
-  static const char* const kNames[2][3] = {
+  static const char* const kNames[3][3] = {
       {"ggemm_bf16_relu", "ggemm_bf16_swiglu", "ggemm_bf16_out"},
-      {"shared_bf16_relu", "shared_bf16_swiglu", "shared_bf16_out"}};
-  ProfScope ps(kNames[a.shared ? 1 : 0][EPI == EPI_RELU_BF16     ? 0
-                                        : EPI == EPI_SWIGLU_BF16 ? 1
-                                                                 : 2],
+      {"shared_bf16_relu", "shared_bf16_swiglu", "shared_bf16_out"},
+      {"ggemm_fp8_relu", "ggemm_fp8_swiglu", "ggemm_fp8_out"}};
+  ProfScope ps(kNames[FP8 ? 2 : a.shared ? 1 : 0][EPI == EPI_RELU_BF16     ? 0
+                                                  : EPI == EPI_SWIGLU_BF16 ? 1
+                                                                           : 2],
                s);
-  ggemm_bf16_kernel<BN, EPI, WGM, HAS_BIAS><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(a);
+  ggemm_bf16_kernel<BN, EPI, WGM, HAS_BIAS, FP8>
+      <<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(a);
   return hipGetLastError();
+}
+
+template <bool FP8>
+hipError_t launch_typed(const GemmBf16Args& a, int epi, hipStream_t s) {
+  const bool bias = a.bias != nullptr;
+  switch (epi) {
+    case EPI_RELU_BF16:
+      return bias ? launch_t<256, EPI_RELU_BF16, 2, true, FP8>(a, s)
+                  : launch_t<256, EPI_RELU_BF16, 2, false, FP8>(a, s);
+    case EPI_SWIGLU_BF16:
+      return launch_t<128, EPI_SWIGLU_BF16, 2, false, FP8>(a, s);
+    default:
+      return bias ? launch_t<256, EPI_IDENT_F32, 2, true, FP8>(a, s)
+                  : launch_t<256, EPI_IDENT_F32, 2, false, FP8>(a, s);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_gemm_bf16(const GemmBf16Args& a, int epi, hipStream_t s) {
-  const bool bias = a.bias != nullptr;
-  switch (epi) {
-    case EPI_RELU_BF16:
-      return bias ? launch_t<256, EPI_RELU_BF16, 2, true>(a, s)
-                  : launch_t<256, EPI_RELU_BF16, 2, false>(a, s);
-    case EPI_SWIGLU_BF16:
-      return launch_t<128, EPI_SWIGLU_BF16, 2, false>(a, s);
-    default:
-      return bias ? launch_t<256, EPI_IDENT_F32, 2, true>(a, s)
-                  : launch_t<256, EPI_IDENT_F32, 2, false>(a, s);
-  }
+  return a.fp8 ? launch_typed<true>(a, epi, s) : launch_typed<false>(a, epi, s);
 }
 
 }  // namespace moe

@@ -57,9 +57,9 @@ enum GemmEpi { EPI_RELU_BF16 = 0, EPI_SWIGLU_BF16 = 1, EPI_IDENT_F32 = 2 };
 struct GemmBf16Args {
   const uint16_t* A;     // [rows, K] bf16, rows contiguous
   long long lda;
-  const uint16_t* B1;    // [n, N, K] bf16
-  const uint16_t* B3;    // SwiGLU second matrix [n, N, K]
-  long long strideB;     // N * K
+  const void* B1;        // [n, N, K] bf16, or n packed FP8 experts (fp8 = 1)
+  const void* B3;        // SwiGLU second matrix, same layout
+  long long strideB;     // bytes from one expert's weights to the next
   int N, K;
   void* C;               // bf16 [rows, N] or f32 [rows, N]
   long long ldc;
@@ -71,9 +71,16 @@ struct GemmBf16Args {
   int max_mtiles;
   int num_cus;           // compute units of the device (persistent grid size)
   int shared;            // 1: the shared expert (only the profiler name differs)
+  int fp8;               // 1: B1/B3 are packed E4M3 weights with per-row scales
 };
 constexpr int kBf16BM = 128;
 constexpr int kMaxTilesPerWG = 512;  // tiles one persistent workgroup can hold
+
+// Pack n_experts [N, K] weight matrices (fp32, or bf16 when src_bf16) into
+// the FP8 E4M3 layout the grouped GEMM reads (codes by row pair and 64-wide
+// K block, then one fp32 scale per row); N*K + 4*N bytes per expert.
+hipError_t launch_pack_fp8(int n_experts, int N, int K, int src_bf16, const void* src, void* dst,
+                           hipStream_t s);
 
 // Compute units of the current device (queried once per device).
 int device_cus();

@@ -33,6 +33,7 @@ ACT_RELU = 0
 ACT_SWIGLU = 1
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
+DTYPE_FP8 = 2   # the library packs the bf16 draws into E4M3 codes with per-row scales
 
 
 @dataclass(frozen=True)
@@ -88,6 +89,11 @@ PRESETS = {
                            logit_bias="normal1", seed=1004),
     "fine_swiglu": MoEConfig("fine_swiglu", T=4096, d_model=7168, d_hidden=2048, n_experts=256,
                              k=8, act=ACT_SWIGLU, noisy=False, logit_bias="zipf1.1", seed=1005),
+    "lm_layer_fp8": MoEConfig("lm_layer_fp8", T=8192, d_model=512, d_hidden=1024, n_experts=256,
+                              k=4, expert_dtype=DTYPE_FP8, logit_bias="normal0.5", seed=1002),
+    "fine_swiglu_fp8": MoEConfig("fine_swiglu_fp8", T=4096, d_model=7168, d_hidden=2048,
+                                 n_experts=256, k=8, act=ACT_SWIGLU, expert_dtype=DTYPE_FP8,
+                                 noisy=False, logit_bias="zipf1.1", seed=1005),
     "sigmoid_shared": MoEConfig("sigmoid_shared", T=4096, d_model=7168, d_hidden=2048,
                                 n_experts=256, k=8, act=ACT_SWIGLU, gate=GATE_SIGMOID_BIAS,
                                 noisy=False, logit_bias="normal0.5", d_hidden_shared=2048,
@@ -150,7 +156,7 @@ def make_inputs(cfg: MoEConfig, device="cpu", T: int | None = None):
         out["w_noise2"] = (_normal((a, b, d), 1.0 / math.sqrt(d), device, _derived(s, 7))
                            if cfg.noisy else None)
         out["noise2"] = _normal((T, k1, b), 1.0, device, _derived(s, 8)) if cfg.noisy else None
-    wdt = torch.bfloat16 if cfg.expert_dtype == DTYPE_BF16 else torch.float32
+    wdt = torch.float32 if cfg.expert_dtype == DTYPE_F32 else torch.bfloat16
 
     def experts(tensor_id, shape, fan_in):
         buf = torch.empty((n,) + shape, dtype=wdt, device=device)

@@ -11,7 +11,8 @@ import torch
 
 import oracle
 import sparsely_gated_mixture_amd as moe
-from sparsely_gated_mixture_amd.workloads import DTYPE_BF16, make_inputs, to_numpy64
+from sparsely_gated_mixture_amd.workloads import (DTYPE_BF16, DTYPE_F32, DTYPE_FP8, make_inputs,
+                                                  to_numpy64)
 
 TOL_F32 = 1e-4     # max-abs-normalised, fp32 experts
 TOL_BF16 = 2e-2    # max-abs-normalised, bf16 experts
@@ -126,11 +127,28 @@ def check_dispatch_exact(cfg, gpu, T):
     return d
 
 
+def fp8_dequant(w):
+    """The values FP8 experts compute with: the oracle's E4M3 row
+    quantization of the bf16 weights, dequantized."""
+    return oracle.dequantize_fp8_rows(*oracle.quantize_fp8_rows(w))
+
+
+def fp8_view(ew):
+    """expert_weights_host dict with every w1/w3/w2 matrix dequantized."""
+    out = dict(ew)
+    for name in ("w1", "w3", "w2"):
+        if ew.get(name) is not None:
+            out[name] = {e: fp8_dequant(m) for e, m in ew[name].items()}
+    return out
+
+
 def oracle_flat(cfg, h, ew):
+    if cfg.expert_dtype == DTYPE_FP8:
+        ew = fp8_view(ew)
     return oracle.forward(
         h["x"], h["w_gate"], cfg.k, _stack(ew["w1"]), _stack(ew["w2"]), b_gate=h.get("b_gate"),
         w_noise=h.get("w_noise"), noise=h.get("noise"), b1=_stack(ew["b1"]), w3=_stack(ew["w3"]),
-        b2=_stack(ew["b2"]), mode=cfg.gate, act=cfg.act, bf16=cfg.expert_dtype == DTYPE_BF16,
+        b2=_stack(ew["b2"]), mode=cfg.gate, act=cfg.act, bf16=cfg.expert_dtype != DTYPE_F32,
         capacity_factor=cfg.capacity_factor, w_importance=cfg.w_importance, w_load=cfg.w_load,
         alpha=cfg.alpha_switch, w_z=cfg.w_z, w_entropy=cfg.w_entropy, ws1=h.get("ws1"),
         ws3=h.get("ws3"), ws2=h.get("ws2"))
@@ -143,7 +161,7 @@ def _stack(dct):
 
 
 def y_tolerance(cfg):
-    return TOL_BF16 if cfg.expert_dtype == DTYPE_BF16 else TOL_F32
+    return TOL_F32 if cfg.expert_dtype == DTYPE_F32 else TOL_BF16
 
 
 def oracle_gate_any(cfg, h):
@@ -178,11 +196,15 @@ def sampled_y_reference(cfg, inp, x64, idx, w, slot_pos, tokens):
     (idx, w, slot_pos); only the experts these tokens use are copied."""
     experts = sorted({int(idx[t, s]) for t in tokens for s in range(idx.shape[1])
                       if slot_pos[t, s] >= 0})
-    bf = cfg.expert_dtype == DTYPE_BF16
+    bf = cfg.expert_dtype != DTYPE_F32
 
     def host32(name, e):
         t = inp.get(name)
-        return None if t is None else t[e].detach().float().cpu().numpy()
+        if t is None:
+            return None
+        m = t[e].detach().float().cpu().numpy()
+        return fp8_dequant(m) if cfg.expert_dtype == DTYPE_FP8 and name != "b1" and name != "b2" \
+            else m
 
     ys = np.zeros((len(tokens), cfg.d_model))
     if cfg.d_hidden_shared:
@@ -239,3 +261,32 @@ def full_size_sampled(cfg, n_sample=48, seed=0):
         f"y error {err:.3e}")
     assert err <= y_tolerance(cfg)
     return gpu
+
+
+def full_parity(cfg, T=None, aux=True):
+    """End-to-end forward of `cfg` (T tokens) against the oracle, element by
+    element."""
+    T = cfg.T if T is None else T
+    c = cfg.replace(T=T)
+    log(f"[parity] {cfg.name} T={T} d={c.d_model} h={c.d_hidden} n={c.n_experts} k={c.k}")
+    inp = dev_inputs(c, T)
+    gpu = gpu_forward(c, inp)
+    h = host(inp)
+    ew = expert_weights_host(inp, range(c.n_experts))
+    ref = oracle_flat(c, h, ew)
+    g = ref["gate"]
+    bad = routing_mismatches(gpu["topk_idx"], g.topk_idx, g.H, c.k)
+    ok = np.setdiff1d(np.arange(T), bad)
+    np.testing.assert_allclose(gpu["topk_w"][ok], g.topk_w[ok], rtol=TOL_W_REL, atol=TOL_W)
+    d = check_dispatch_exact(c, gpu, T)
+    if len(bad) == 0:
+        np.testing.assert_array_equal(d["perm"], ref["dispatch"]["perm"])
+    err = max_abs_norm(gpu["y"][ok], ref["y"][ok])
+    log(f"  y max-abs-normalised error {err:.3e}")
+    assert err <= y_tolerance(c)
+    if aux and len(bad) == 0:
+        assert_close_rel(gpu["importance"], g.importance, 1e-5, 1e-5, "importance")
+        if g.load is not None:
+            assert_close_rel(gpu["load"], g.load, 1e-5, 1e-5, "load")
+        assert_close_rel(gpu["losses"], ref["losses"], TOL_AUX, 1e-7, "losses")
+    return gpu, ref

@@ -19,14 +19,15 @@ FAKE = 0x10000  # an aligned non-null address; never dereferenced by these calls
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_expected_calls():
     decl = declared_functions()
     for name in ["moe_gate", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_aux_loss",
                  "moe_forward", "moe_workspace_size", "moe_status_string", "moe_last_error",
-                 "moe_gate_hier", "moe_shared_ffn", "moe_router_bias_update"]:
+                 "moe_gate_hier", "moe_shared_ffn", "moe_router_bias_update",
+                 "moe_fp8_weight_bytes", "moe_pack_fp8_weights"]:
         assert name in decl
     assert sorted(_lib.EXPORTS) == decl
 
@@ -55,7 +56,7 @@ def test_workspace_size_of_presets(name):
     assert size > 0
     # the forward keeps x_perm and y_perm for every routed slot
     rows = cfg.T * cfg.k
-    per = 2 if cfg.expert_dtype == 1 else 4
+    per = 4 if cfg.expert_dtype == 0 else 2  # x_perm is bf16 for bf16 and FP8 experts
     assert size >= rows * cfg.d_model * (per + 4)
 
 
@@ -83,6 +84,8 @@ def base_cfg(**kw):
     (dict(d_hidden_shared=-8), moe.MOE_ERR_INVALID_ARG),
     (dict(d_hidden_shared=16, expert_dtype=0), moe.MOE_ERR_UNSUPPORTED),
     (dict(d_hidden_shared=16, n_groups=2, k_groups=1), moe.MOE_ERR_UNSUPPORTED),
+    (dict(expert_dtype=2), moe.MOE_ERR_UNSUPPORTED),                  # d = 32: not a multiple of 64
+    (dict(expert_dtype=2, d_model=64, d_hidden=128, d_hidden_shared=64), moe.MOE_ERR_UNSUPPORTED),
 ])
 def test_invalid_configs(kw, status):
     c = _lib.make_config(base_cfg(**kw))
@@ -145,6 +148,23 @@ def test_sigmoid_gate_shared_expert_and_bias_update_arguments():
         moe.moe_router_bias_update(c, FAKE, FAKE, float("nan"), stream=0)
     assert ei.value.status == moe.MOE_ERR_INVALID_ARG and "gamma" in str(ei.value)
     assert moe.moe_workspace_size(cs) > moe.moe_workspace_size(base_cfg(act=1))
+
+
+def test_fp8_sizes_and_arguments():
+    assert moe.moe_fp8_weight_bytes(3, 64, 128) == 3 * (64 * 128 + 4 * 64)
+    assert moe.moe_fp8_weight_bytes(1, 64, 100) == 0     # K % 64
+    assert moe.moe_fp8_weight_bytes(1, 60, 128) == 0     # N % 8
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_pack_fp8_weights(1, 64, 100, 1, FAKE, FAKE, stream=0)
+    assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_pack_fp8_weights(1, 64, 128, 2, FAKE, FAKE, stream=0)   # src must be f32/bf16
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_pack_fp8_weights(1, 64, 128, 1, None, FAKE, stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    ok = _lib.make_config(base_cfg(d_model=64, d_hidden=128, expert_dtype=2, act=1))
+    assert moe.load_library().moe_workspace_size(ctypes.byref(ok)) > 0
 
 
 def test_workspace_too_small_rejected_before_launch():

@@ -19,40 +19,11 @@ from sparsely_gated_mixture_amd.workloads import (ACT_RELU, ACT_SWIGLU, DTYPE_BF
                                                   GATE_SWITCH_TOP1, GATE_TOPK_SOFTMAX, PRESETS,
                                                   MoEConfig, make_inputs, to_numpy64)
 from _support import (TOL_AUX, TOL_BF16, TOL_W, TOL_W_REL, assert_close_rel, check_dispatch_exact,
-                      dev_inputs,
+                      dev_inputs, full_parity,
                       expert_weights_host, gpu_forward, host, log, max_abs_norm, oracle_flat,
                       routing_mismatches, y_tolerance)
 
 pytestmark = pytest.mark.gpu
-
-
-def full_parity(cfg, T=None, aux=True):
-    """End-to-end forward of `cfg` (T tokens) against the oracle, element by
-    element."""
-    T = cfg.T if T is None else T
-    c = cfg.replace(T=T)
-    log(f"[parity] {cfg.name} T={T} d={c.d_model} h={c.d_hidden} n={c.n_experts} k={c.k}")
-    inp = dev_inputs(c, T)
-    gpu = gpu_forward(c, inp)
-    h = host(inp)
-    ew = expert_weights_host(inp, range(c.n_experts))
-    ref = oracle_flat(c, h, ew)
-    g = ref["gate"]
-    bad = routing_mismatches(gpu["topk_idx"], g.topk_idx, g.H, c.k)
-    ok = np.setdiff1d(np.arange(T), bad)
-    np.testing.assert_allclose(gpu["topk_w"][ok], g.topk_w[ok], rtol=TOL_W_REL, atol=TOL_W)
-    d = check_dispatch_exact(c, gpu, T)
-    if len(bad) == 0:
-        np.testing.assert_array_equal(d["perm"], ref["dispatch"]["perm"])
-    err = max_abs_norm(gpu["y"][ok], ref["y"][ok])
-    log(f"  y max-abs-normalised error {err:.3e}")
-    assert err <= y_tolerance(c)
-    if aux and len(bad) == 0:
-        assert_close_rel(gpu["importance"], g.importance, 1e-5, 1e-5, "importance")
-        if g.load is not None:
-            assert_close_rel(gpu["load"], g.load, 1e-5, 1e-5, "load")
-        assert_close_rel(gpu["losses"], ref["losses"], TOL_AUX, 1e-7, "losses")
-    return gpu, ref
 
 
 # ---------------------------------------------------------------------------
