@@ -21,6 +21,17 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Two fp32 values as packed bf16 bits (a in the low half) with the gfx950
+// conversion instruction (v_cvt_pk_bf16_f32): round to nearest, ties to
+// even, NaN stays NaN -- the same bits as f32_to_bf16 for every non-NaN
+// input.
+__device__ __forceinline__ uint32_t bf16x2_bits(float a, float b) {
+  typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  const bf2_t v = __builtin_convertvector((f2_t){a, b}, bf2_t);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float((uint32_t)h << 16);
 }

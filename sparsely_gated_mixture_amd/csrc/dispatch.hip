@@ -184,10 +184,10 @@ __global__ __launch_bounds__(256) void gather_kernel(const float* __restrict__ x
     const f32x4 v1 = *(const f32x4*)(src + c + 4);
     uint4 pk = make_uint4(0u, 0u, 0u, 0u);
     if (bf16_out || x_bf16) {
-      pk.x = (uint32_t)f32_to_bf16(v0[0]) | ((uint32_t)f32_to_bf16(v0[1]) << 16);
-      pk.y = (uint32_t)f32_to_bf16(v0[2]) | ((uint32_t)f32_to_bf16(v0[3]) << 16);
-      pk.z = (uint32_t)f32_to_bf16(v1[0]) | ((uint32_t)f32_to_bf16(v1[1]) << 16);
-      pk.w = (uint32_t)f32_to_bf16(v1[2]) | ((uint32_t)f32_to_bf16(v1[3]) << 16);
+      pk.x = bf16x2_bits(v0[0], v0[1]);
+      pk.y = bf16x2_bits(v0[2], v0[3]);
+      pk.z = bf16x2_bits(v1[0], v1[1]);
+      pk.w = bf16x2_bits(v1[2], v1[3]);
     }
     if (x_bf16) *(uint4*)(x_bf16 + (long long)t * d + c) = pk;
     for (int s = 0; s < k; ++s) {
@@ -212,10 +212,10 @@ __global__ __launch_bounds__(256) void to_bf16_kernel(const float* __restrict__ 
     const f32x4 v0 = *(const f32x4*)(x + i * 8);
     const f32x4 v1 = *(const f32x4*)(x + i * 8 + 4);
     uint4 pk;
-    pk.x = (uint32_t)f32_to_bf16(v0[0]) | ((uint32_t)f32_to_bf16(v0[1]) << 16);
-    pk.y = (uint32_t)f32_to_bf16(v0[2]) | ((uint32_t)f32_to_bf16(v0[3]) << 16);
-    pk.z = (uint32_t)f32_to_bf16(v1[0]) | ((uint32_t)f32_to_bf16(v1[1]) << 16);
-    pk.w = (uint32_t)f32_to_bf16(v1[2]) | ((uint32_t)f32_to_bf16(v1[3]) << 16);
+    pk.x = bf16x2_bits(v0[0], v0[1]);
+    pk.y = bf16x2_bits(v0[2], v0[3]);
+    pk.z = bf16x2_bits(v1[0], v1[1]);
+    pk.w = bf16x2_bits(v1[2], v1[3]);
     *(uint4*)(out + i * 8) = pk;
   }
 }

@@ -167,7 +167,7 @@ ggemm_bf16_kernel(const GemmBf16Args p) {
   const uint8_t* a_src[ADMA];
   const uint8_t* b_src[BDMA];
   int a_chunk[ADMA], b_chunk[BDMA];  // element offset of the lane's chunk (bf16 K tail)
-  int gi = 0, it = 0, ikt = 0;
+  int gi = 0, it = 0, ikt = 0, islot = 0;  // islot = gi % kStages
   int a_live = 0;                    // copies j < a_live of the activation tile hold real rows
   int cnt_last = 0, cnt_prev = 0;    // copies of the two most recently copied steps
   auto set_tile = [&](int ti) {
@@ -205,7 +205,7 @@ ggemm_bf16_kernel(const GemmBf16Args p) {
   // step that reaches past K copies a 16-byte zero constant for the chunks
   // beyond it (FP8 weights need K % 64 == 0).
   auto issue_next = [&]() {
-    const uint32_t sb = lds0 + (gi % kStages) * STAGE;
+    const uint32_t sb = lds0 + islot * STAGE;
     const int k0 = ikt * kBK;
     const long long adv = (long long)ikt * 128;
     if (FP8 || k0 + kBK <= K) {
@@ -229,6 +229,7 @@ ggemm_bf16_kernel(const GemmBf16Args p) {
     cnt_prev = cnt_last;
     cnt_last = a_live + BDMA;
     ++gi;
+    islot = islot == kStages - 1 ? 0 : islot + 1;
     if (++ikt == nk) {
       ikt = 0;
       if (++it < ntiles) set_tile(it);
@@ -251,12 +252,41 @@ ggemm_bf16_kernel(const GemmBf16Args p) {
   };
   zero_acc();
 
+  // Finished results of the last tile, stored one step later.
+  f32x4 pend_f[EPI == EPI_IDENT_F32 ? FM : 1][EPI == EPI_IDENT_F32 ? FN : 1][4];
+  uint2 pend_h[EPI == EPI_IDENT_F32 ? 1 : FM][EPI == EPI_IDENT_F32 ? 1 : FN][4];
+  int pend_row = 0, pend_end = 0, pend_col = 0;
+  bool pend = false;
+  auto store_pending = [&]() {
+    if (!pend) return;
+    pend = false;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int gr = pend_row + i * 32;
+      if (gr >= pend_end) continue;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int gc = pend_col + j * 32 + q4 * 8;
+          if (gc >= p.N) continue;
+          if constexpr (EPI == EPI_IDENT_F32)
+            *(f32x4*)((float*)p.C + (long long)gr * p.ldc + gc) = pend_f[i][j][q4];
+          else
+            *(uint2*)((uint16_t*)p.C + (long long)gr * p.ldc + gc) = pend_h[i][j][q4];
+        }
+    }
+  };
+
   int4 cm = meta[0];  // the computing tile
   set_tile(0);
 #pragma unroll
   for (int s = 0; s < kStages - 1; ++s)
     if (gi < nsteps) issue_next();
 
+  // Compute position: tile ct, K-step ck within it, ring slot cslot (kept
+  // incrementally: no integer division per step).
+  int ct = 0, ck = 0, cslot = 0;
   for (int g = 0; g < nsteps; ++g) {
     // Steps copied after this one (at most kStages-2).  Wait until only
     // their copies may still be in flight; loads complete in order, so
@@ -266,11 +296,12 @@ ggemm_bf16_kernel(const GemmBf16Args p) {
     wait_vm_upto<(kStages - 2) * PER_STEP>(ahead <= 0 ? 0 : ahead == 1 ? cnt_last
                                                                       : cnt_last + cnt_prev);
     __syncthreads();
-    if (g % nk == 0) cm = meta[g / nk];
+    if (ck == 0) cm = meta[ct];
     // Every wave is past step g-1, so its ring slot can take step
     // g+kStages-1 now, while this step computes.
     if (gi < nsteps) issue_next();
-    const uint8_t* As = smem + (g % kStages) * STAGE;
+    store_pending();
+    const uint8_t* As = smem + cslot * STAGE;
     const uint8_t* Bs = As + A_BYTES;
     // A wave whose token rows all lie past the segment's end has nothing to
     // compute this tile.
@@ -331,11 +362,17 @@ ggemm_bf16_kernel(const GemmBf16Args p) {
     }
     }
 
-    if (g % nk == nk - 1) {
+    cslot = cslot == kStages - 1 ? 0 : cslot + 1;
+    if (++ck == nk) {
+      ck = 0;
+      ++ct;
       // Tile done.  D[n][m] layout: lane holds column m = lane%32 of each
-      // 32x32 block and rows n = 8*(v/4) + 4*(lane/32) + v%4.
+      // 32x32 block and rows n = 8*(v/4) + 4*(lane/32) + v%4.  The results
+      // are finished (scale, bias, activation, bf16 rounding) into registers
+      // here and stored at the next step, after its copies are issued, so
+      // the stores drain while that step computes.
       const int4 m = cm;
-      const int e = m.x, row_end = m.z;
+      const int e = m.x;
       const float* bias = HAS_BIAS ? p.bias + (long long)e * p.N : nullptr;
       // FP8: the row scales follow each expert's codes.
       const float* sc1 = FP8 ? (const float*)((const uint8_t*)p.B1 + (long long)e * p.strideB +
@@ -372,15 +409,12 @@ ggemm_bf16_kernel(const GemmBf16Args p) {
           }
         }
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int gr = m.y + wm * WM + i * 32 + lr;
-        if (gr >= row_end) continue;
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
             const int gc = m.w + wn * WN + j * 32 + q4 * 8 + lh * 4;
-            if (gc >= p.N) continue;
             float f[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -390,24 +424,24 @@ ggemm_bf16_kernel(const GemmBf16Args p) {
                 f[q] = gv / (1.f + expf(-gv)) * uv;
               } else {
                 f[q] = acc[0][i][j][4 * q4 + q] * s1[j][q4][q];
-                if constexpr (HAS_BIAS) f[q] += bias[gc + q];
+                if constexpr (HAS_BIAS) f[q] += gc < p.N ? bias[gc + q] : 0.f;
                 if constexpr (EPI == EPI_RELU_BF16) f[q] = fmaxf(f[q], 0.f);
               }
             }
             if constexpr (EPI == EPI_IDENT_F32) {
-              *(f32x4*)((float*)p.C + (long long)gr * p.ldc + gc) = f32x4{f[0], f[1], f[2], f[3]};
+              pend_f[i][j][q4] = f32x4{f[0], f[1], f[2], f[3]};
             } else {
-              uint2 pk;
-              pk.x = (uint32_t)f32_to_bf16(f[0]) | ((uint32_t)f32_to_bf16(f[1]) << 16);
-              pk.y = (uint32_t)f32_to_bf16(f[2]) | ((uint32_t)f32_to_bf16(f[3]) << 16);
-              *(uint2*)((uint16_t*)p.C + (long long)gr * p.ldc + gc) = pk;
+              pend_h[i][j][q4] = make_uint2(bf16x2_bits(f[0], f[1]), bf16x2_bits(f[2], f[3]));
             }
           }
-        }
-      }
+      pend_row = m.y + wm * WM + lr;
+      pend_end = m.z;
+      pend_col = m.w + wn * WN + lh * 4;
+      pend = true;
       zero_acc();
     }
   }
+  store_pending();
 }
 
 template <int BN, int EPI, int WGM, bool HAS_BIAS, bool FP8>
