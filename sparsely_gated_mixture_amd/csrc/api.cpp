@@ -197,8 +197,9 @@ Plan make_plan(const moe_config& c) {
   const int ncols = 2 * p.n_gate;  // clean | raw (the raw half is unused when noiseless)
   p.ldl = (int)round_up(ncols, 4);
   {
+    // 128x128 tiles (8 waves) once they give every CU a tile; 64x64 below.
     const long long t128 = ((T + 127) / 128) * ((ncols + 127) / 128);
-    p.gemm_bm = t128 >= 512 ? 128 : 64;
+    p.gemm_bm = t128 >= 256 ? 128 : 64;
   }
   {
     // one partial vector per block; at most 256 blocks (one per CU) once T

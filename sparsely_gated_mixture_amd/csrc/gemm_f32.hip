@@ -3,9 +3,10 @@
 // Used where the layer must stay in fp32: the gate logits x.W_g | x.W_noise
 // (the gating decision needs fp32 accuracy), the two-level secondary gate
 // (grouped rows), and fp32 experts.  C = A . B^T with both operands
-// K-contiguous; tiles BMxBM (64 or 128), BK = 32, 4 waves in a 2x2 grid,
-// double-buffered LDS, one barrier per K step, epilogue staged through LDS
-// for full-width stores.
+// K-contiguous; tiles 64x64 (4 waves in a 2x2 grid) or 128x128 (8 waves in
+// a 2x4 grid: half the operand re-reads of 64x64 tiles, two waves per SIMD),
+// BK = 32, double-buffered LDS with register prefetch, one barrier per K
+// step, epilogue staged through LDS for full-width stores.
 #include "common.h"
 #include "launch.h"
 
@@ -15,13 +16,15 @@ namespace {
 constexpr int kBK = 32;
 constexpr int kLDK = kBK + 4;  // padded LDS row (floats): conflict-free b128 reads
 
-template <int BM>
-__global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmF32Args p) {
+template <int BM, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_f32_kernel(const GemmF32Args p) {
+  constexpr int NT = 64 * WGM * WGN;  // threads
   constexpr int BN = BM;
-  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int FM = WM / 32, FN = WN / 32;
-  constexpr int ACH = BM * kBK / 4 / 256;  // float4 chunks per thread (A)
-  constexpr int BCH = BN * kBK / 4 / 256;
+  constexpr int ACH = BM * kBK / 4 / NT;  // float4 chunks per thread (A)
+  constexpr int BCH = BN * kBK / 4 / NT;
+  static_assert(ACH >= 1 && BCH >= 1 && FM >= 1 && FN >= 1, "bad tile shape");
   constexpr int STAGE = (BM + BN) * kLDK;
   constexpr int LDC = BN + 4;
   static_assert(BM * LDC <= 2 * STAGE, "epilogue staging must fit");
@@ -51,7 +54,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmF32Args p) {
   int akc[ACH], arow[ACH];
 #pragma unroll
   for (int i = 0; i < ACH; ++i) {
-    const int c = tid + 256 * i;
+    const int c = tid + NT * i;
     const int r = c / (kBK / 4);
     akc[i] = (c % (kBK / 4)) * 4;
     arow[i] = r;
@@ -65,7 +68,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmF32Args p) {
   int bkc[BCH], brow[BCH];
 #pragma unroll
   for (int i = 0; i < BCH; ++i) {
-    const int c = tid + 256 * i;
+    const int c = tid + NT * i;
     const int r = c / (kBK / 4);
     bkc[i] = (c % (kBK / 4)) * 4;
     brow[i] = r;
@@ -99,7 +102,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmF32Args p) {
   };
 
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   const int lr = lane & 31, lh = lane >> 5;
 
   f32x16 acc[FM][FN];
@@ -159,7 +162,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmF32Args p) {
       }
   __syncthreads();
   const float* bias = p.bias ? p.bias + (long long)g * p.stride_bias : nullptr;
-  for (int c = tid; c < BM * BN / 4; c += 256) {
+  for (int c = tid; c < BM * BN / 4; c += NT) {
     const int r = c / (BN / 4);
     const int cc = (c % (BN / 4)) * 4;
     const int gr = row0 + r;
@@ -195,9 +198,9 @@ hipError_t launch_gemm_f32(const GemmF32Args& a, int bm, hipStream_t s) {
   const long long grid = (max_total + kXcds - 1) / kXcds * kXcds;
   ProfScope ps(bm == 128 ? "gemm_f32_bm128" : "gemm_f32_bm64", s);
   if (bm == 128)
-    gemm_f32_kernel<128><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
+    gemm_f32_kernel<128, 2, 4><<<dim3((unsigned)grid), dim3(512), 0, s>>>(a);
   else
-    gemm_f32_kernel<64><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
+    gemm_f32_kernel<64, 2, 2><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
 
