@@ -1,4 +1,5 @@
-"""CPU oracle of the Sparsely-Gated MoE layer forward (double precision).
+"""CPU oracle of the Sparsely-Gated MoE layer, forward and backward
+(double precision).
 
 TEST INFRASTRUCTURE ONLY: the test suite, the package smoke check and the
 benchmark's CPU-baseline leg are the only users.  The product path never
@@ -12,7 +13,8 @@ the pages give them:
 * the Importance and Load vectors and the auxiliary losses,
 * dispatch into one merged batch per expert (with optional capacity),
 * expert FFNs, gate-weighted combine,
-* the two-level (hierarchical) composition.
+* the two-level (hierarchical) composition,
+* the backward pass of the flat layer (``backward``).
 
 Citations use the page titles listed at the top of ``oracle.c``.
 """
@@ -116,6 +118,10 @@ def lib():
         L.oracle_quantize_fp8_rows.argtypes = [c_int, c_int, _dp,
                                                np.ctypeslib.ndpointer(np.uint8, flags="C"), _dp]
         L.oracle_hier_load.argtypes = [c_int, c_int, _dp, _dp, _ip, _dp]
+        L.oracle_cv2_grad.argtypes = [c_int, _dp, c_dbl, _dp]
+        L.oracle_gate_backward.argtypes = [c_int, c_int, c_int, c_int, _dp, _dp, _dp, odp, odp,
+                                           odp, _ip, _dp, _dp, _dp, _dp, _dp, _dp, odp, c_dbl,
+                                           c_dbl, _dp, odp]
         _lib = L
     return _lib
 
@@ -489,3 +495,186 @@ def forward_hier(x, w_gate, w_noise, noise, k1, w_gate2, w_noise2, noise2, k2, w
     losses = aux(T, k1 * k2, gh["importance"], gh["load"], disp["counts_pre"], w_importance,
                  w_load, alpha, gh["zsum"], gh["entsum"], w_z, w_entropy)
     return dict(gate=gh, dispatch=disp, y_perm=y_perm, y=y, losses=losses)
+
+
+# --------------------------------------------------------------------------
+# backward
+# --------------------------------------------------------------------------
+
+def cv2_grad(v, scale=1.0) -> np.ndarray:
+    """scale * d CV(v)^2 / d v (population variance; 0 when the mean is 0)."""
+    v = _d(v)
+    out = np.empty(v.size)
+    lib().oracle_cv2_grad(v.size, v, float(scale), out)
+    return out
+
+
+def _sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def expert_ffn_backward(u, w1, w2, gout, b1=None, w3=None, b2=None, act=ACT_RELU, bf16=False):
+    """Backward of one expert on its merged rows u [rows, d] (the forward of
+    ``expert_ffn``), given gout = dL/d(expert output) [rows, d].  Returns
+    (du, dw1, db1, dw3, dw2, db2); the absent parts are None.
+    RELU: pre = u W1^T + b1, hid = max(0, pre), out = hid W2^T + b2:
+      dW2 = gout^T hid, db2 = sum of gout rows, dhid = gout W2,
+      dpre = dhid where pre > 0 else 0, dW1 = dpre^T u, db1 = sum of dpre rows,
+      du = dpre W1.
+    SWIGLU: hid = silu(a) * b with a = u W1^T, b = u W3^T:
+      da = dhid * b * silu'(a), silu'(a) = s (1 + a (1 - s)) with s = Sigmoid(a),
+      db = dhid * silu(a), dW1 = da^T u, dW3 = db^T u, du = da W1 + db W3.
+    With bf16 the forward's rounded u and hid are the values used (the
+    rounding itself is taken as the identity)."""
+    u, w1, w2, gout, b1, w3, b2 = map(_d, (u, w1, w2, gout, b1, w3, b2))
+    uq = bf16_round(u) if bf16 else u
+    if act == ACT_SWIGLU:
+        a = uq @ w1.T
+        b = uq @ w3.T
+        s = _sigmoid(a)
+        hid = a * s * b
+    else:
+        pre = uq @ w1.T + (b1 if b1 is not None else 0.0)
+        hid = np.maximum(pre, 0.0)
+    hq = bf16_round(hid) if bf16 else hid
+    dw2 = gout.T @ hq
+    db2 = gout.sum(axis=0) if b2 is not None else None
+    dhid = gout @ w2
+    if act == ACT_SWIGLU:
+        da = dhid * b * s * (1.0 + a * (1.0 - s))
+        dbv = dhid * a * s
+        return da @ w1 + dbv @ w3, da.T @ uq, None, dbv.T @ uq, dw2, db2
+    dpre = np.where(pre > 0.0, dhid, 0.0)
+    db1 = dpre.sum(axis=0) if b1 is not None else None
+    return dpre @ w1, dpre.T @ uq, db1, None, dw2, db2
+
+
+def backward(x, w_gate, k, w1, w2, dy, dlosses, *, b_gate=None, w_noise=None, noise=None,
+             b1=None, w3=None, b2=None, mode=GATE_TOPK_SOFTMAX, act=ACT_RELU, bf16=False,
+             capacity_factor=0.0, w_importance=0.1, w_load=0.1, alpha=1.0, w_z=1.0,
+             w_entropy=1.0, ws1=None, ws3=None, ws2=None):
+    """Gradients of L = sum_t <dy_t, y_t> + sum_j dlosses[j] * losses[j] for
+    the flat layer of ``forward`` (same arguments), the routing held fixed.
+    Returns a dict with dx, dw_gate, db_gate (None for the sigmoid gate,
+    whose bias only moves the selection), dw_noise, dw1, db1, dw3, dw2, db2,
+    dws1, dws3, dws2 (absent parts None) and the forward's results ("fwd").
+
+    Stages, in reverse order of the forward ([PAPER] FAQ: the kept gate
+    values are differentiable because the selection comes before the
+    softmax; [NOTES] "Noisy Top-K Gating": the noise lets the load loss pass
+    gradients):
+      1. combine: dG[t,s] = <dy_t, y_perm[slot_pos[t,s]]> and the expert
+         output rows receive topk_w[t,s] * dy_t (dropped slots neither);
+      2. each expert (and the shared one, with weight 1) by
+         ``expert_ffn_backward``; a token's input gradient sums its rows';
+      3. the losses: dImportance = dl0 w_imp dCV^2 + dl2 alpha n f / T,
+         dLoad = dl1 w_load dCV^2, the z and entropy coefficients
+         dl3 w_z / T and dl4 w_entropy / T (losses[4] = w_entropy / T *
+         sum g ln g);
+      4. the gate by ``oracle_gate_backward`` (dclean, draw);
+      5. the gate's linear maps: dW_g = dclean^T x, db = column sums of dclean,
+         dW_noise = draw^T x, dx += dclean W_g + draw W_noise."""
+    x = _d(x)
+    T, d = x.shape
+    w_gate = _d(w_gate)
+    n = w_gate.shape[0]
+    dy = _d(dy)
+    dl = _d(dlosses)
+    fwd = forward(x, w_gate, k, w1, w2, b_gate=b_gate, w_noise=w_noise, noise=noise, b1=b1,
+                  w3=w3, b2=b2, mode=mode, act=act, bf16=bf16, capacity_factor=capacity_factor,
+                  w_importance=w_importance, w_load=w_load, alpha=alpha, w_z=w_z,
+                  w_entropy=w_entropy, ws1=ws1, ws3=ws3, ws2=ws2)
+    g = fwd["gate"]
+    disp = fwd["dispatch"]
+    slot_pos = disp["slot_pos"]
+    perm = disp["perm"]
+    offsets = disp["offsets"]
+    y_perm = fwd["y_perm"]
+
+    # 1. combine
+    dG = np.zeros((T, k))
+    rows = int(offsets[n])
+    gout = np.zeros((rows, d))
+    for t in range(T):
+        for s in range(k):
+            r = slot_pos[t, s]
+            if r < 0:
+                continue
+            dG[t, s] = dy[t] @ y_perm[r]
+            gout[r] = g.topk_w[t, s] * dy[t]
+
+    # 2. experts
+    w1, w2, w3, b1, b2 = map(_d, (w1, w2, w3, b1, b2))
+    h = w1.shape[1]
+    dw1 = np.zeros_like(w1)
+    dw2 = np.zeros_like(w2)
+    dw3 = np.zeros_like(w3) if w3 is not None else None
+    db1 = np.zeros((n, h)) if b1 is not None else None
+    db2 = np.zeros((n, d)) if b2 is not None else None
+    du_perm = np.zeros((rows, d))
+    for e in range(n):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        res = expert_ffn_backward(x[perm[lo:hi]], w1[e], w2[e], gout[lo:hi],
+                                  None if b1 is None else b1[e],
+                                  None if w3 is None else w3[e],
+                                  None if b2 is None else b2[e], act, bf16)
+        du_perm[lo:hi], dw1[e] = res[0], res[1]
+        if db1 is not None:
+            db1[e] = res[2]
+        if dw3 is not None:
+            dw3[e] = res[3]
+        dw2[e] = res[4]
+        if db2 is not None:
+            db2[e] = res[5]
+    dx = np.zeros((T, d))
+    for t in range(T):
+        for s in range(k):
+            r = slot_pos[t, s]
+            if r >= 0:
+                dx[t] += du_perm[r]
+    dws1 = dws3 = dws2 = None
+    if ws1 is not None:
+        res = expert_ffn_backward(x, ws1, ws2, dy, None, ws3, None, act, bf16)
+        dx += res[0]
+        dws1, dws3, dws2 = res[1], res[3], res[4]
+
+    # 3. losses
+    f = disp["counts_pre"] / float(T * k)
+    dimp = cv2_grad(g.importance, dl[0] * w_importance) + dl[2] * alpha * n * f / T
+    dload = cv2_grad(g.load, dl[1] * w_load) if g.load is not None else None
+    c_z = dl[3] * w_z / T
+    c_ent = dl[4] * w_entropy / T
+
+    # 4. gate
+    noisy = g.sp is not None
+    if mode == GATE_SIGMOID_BIAS:
+        Zs = x @ w_gate.T           # the bias-free logits h
+        clean = Zs
+    else:
+        Zs = g.H
+        clean = g.clean
+    raw = x @ _d(w_noise).T if noisy else None
+    z = _d(noise) if noisy else None
+    dclean = np.empty((T, n))
+    draw = np.empty((T, n)) if noisy else None
+    lib().oracle_gate_backward(T, n, k, mode, _d(g.H), _d(Zs), _d(clean),
+                               _d(g.sp) if noisy else None, z, raw, _i(g.topk_idx),
+                               _d(g.topk_w), _d(g.probs), _d(g.hk), _d(g.hk1), dG, dimp,
+                               _d(dload) if dload is not None else None, c_z, c_ent, dclean,
+                               draw)
+
+    # 5. the gate's linear maps
+    dw_gate = dclean.T @ x
+    dx += dclean @ w_gate
+    db_gate = None
+    if b_gate is not None and mode != GATE_SIGMOID_BIAS:
+        db_gate = dclean.sum(axis=0)
+    dw_noise = None
+    if noisy:
+        dw_noise = draw.T @ x
+        dx += draw @ _d(w_noise)
+    return dict(dx=dx, dw_gate=dw_gate, db_gate=db_gate, dw_noise=dw_noise, dw1=dw1, db1=db1,
+                dw3=dw3, dw2=dw2, db2=db2, dws1=dws1, dws3=dws3, dws2=dws2, dG=dG, dclean=dclean,
+                draw=draw, fwd=fwd)

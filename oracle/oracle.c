@@ -1,5 +1,6 @@
 /*
- * Plain CPU oracle for the Sparsely-Gated Mixture-of-Experts layer forward.
+ * Plain CPU oracle for the Sparsely-Gated Mixture-of-Experts layer, forward
+ * and backward.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or
  * load this library: only the test suite, the package's smoke check and the
@@ -541,4 +542,162 @@ void oracle_hier_load(int a, int b, const double* load_primary, const double* lo
           group_tokens[g] > 0
               ? load_primary[g] * load_secondary[(size_t)g * b + e] / (double)group_tokens[g]
               : 0.0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Backward                                                                  */
+/* ------------------------------------------------------------------------ */
+
+/* The backward pass differentiates the scalar objective
+ *   L = sum_t <dy_t, y_t> + sum_j dl_j * losses_j
+ * (dy and dl are the upstream gradients) by the chain rule, one stage at a
+ * time in reverse.  [PAPER] FAQ on back-propagating through the discrete
+ * top-k: the selection happens before the softmax, so the kept gate values
+ * stay differentiable functions of the gate's weights while the selection
+ * itself is held fixed; [NOTES] "Noisy Top-K Gating": the noise term is what
+ * lets the load-balancing loss pass gradients (through the smooth P(x,i)).
+ * The bf16 roundings of the forward are taken as the identity (their
+ * rounded values are used wherever the forward used them). */
+
+/* d CV(v)^2 / d v_i with the population variance: writing m for the mean and
+ * var for the variance, CV^2 = var / m^2, d var / d v_i = 2 (v_i - m) / n and
+ * d m / d v_i = 1 / n, so the derivative is
+ *   (2 / (n m^2)) * ((v_i - m) - var / m),
+ * times `scale`; 0 where CV^2 is defined as 0 (mean 0). */
+void oracle_cv2_grad(int n, const double* v, double scale, double* out) {
+  double s = 0.0;
+  for (int i = 0; i < n; ++i) s += v[i];
+  double m = s / n;
+  if (m == 0.0) {
+    for (int i = 0; i < n; ++i) out[i] = 0.0;
+    return;
+  }
+  double q = 0.0;
+  for (int i = 0; i < n; ++i) q += (v[i] - m) * (v[i] - m);
+  double var = q / n;
+  for (int i = 0; i < n; ++i) out[i] = scale * (2.0 / (n * m * m)) * ((v[i] - m) - var / m);
+}
+
+/* Standard normal density, the derivative of Phi. */
+static double std_normal_pdf(double z) { return exp(-0.5 * z * z) / sqrt(2.0 * acos(-1.0)); }
+
+/* Gate backward for every token, the selection held fixed.
+ * In (per token t, n experts):
+ *   Hsel    the values the selection ranks (H; sigmoid gate: h + b),
+ *   Zs      the logits the gate's softmax / sigmoid sees (H; sigmoid: h),
+ *   clean, sp, z, raw   the noisy gate's parts (sp/z/raw NULL when
+ *           noiseless): H = clean + z * Softplus(raw),
+ *   topk_idx, topk_w, probs (the forward's outputs), h_k, h_k1 (H_(k) and
+ *           H_(k+1)),
+ *   dG      [T][k] gradient of L with respect to topk_w from the combine,
+ *   dImp    [n] gradient of L with respect to Importance,
+ *   dLoad   [n] gradient of L with respect to Load (NULL: none),
+ *   c_z     dL / d(sum over tokens and experts of Zs^2),
+ *   c_ent   dL / d(sum over tokens and experts of g ln g).
+ * Out: dclean [T][n] = dL / d clean (sigmoid gate: dL / d h), and, for a
+ *      noisy gate, draw [T][n] = dL / d raw.
+ * Steps, per token:
+ *  1. gradient on the gate distribution: the combine's dG on the kept
+ *     slots, dImp (Importance sums the distribution), and c_ent (ln g + 1)
+ *     from the entropy statistic (0 ln 0 terms contribute nothing);
+ *  2. through the normalisation: softmax over the kept values (top-k),
+ *     over all n (Switch), or Sigmoid then division by the kept sum;
+ *  3. the z statistic adds 2 c_z Zs_j for every expert;
+ *  4. Load: P_i = Phi((clean_i - thr_i) / sp_i) moves with clean_i, with
+ *     sp_i and with its threshold thr_i, which is the H of another expert:
+ *     the expert of rank k (H_(k+1)) for a kept i, the one of rank k-1
+ *     (H_(k)) otherwise; no gradient where the threshold is -inf;
+ *  5. H = clean + z sp: d clean += dH, d sp += z dH, and
+ *     d raw = d sp * Sigmoid(raw) (the derivative of Softplus). */
+void oracle_gate_backward(int T, int n, int k, int mode, const double* Hsel, const double* Zs,
+                          const double* clean, const double* sp, const double* z,
+                          const double* raw, const int32_t* topk_idx, const double* topk_w,
+                          const double* probs, const double* h_k, const double* h_k1,
+                          const double* dG, const double* dImp, const double* dLoad,
+                          double c_z, double c_ent, double* dclean, double* draw) {
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < T; ++t) {
+    const double* hs = Hsel + (size_t)t * n;
+    const double* zs = Zs + (size_t)t * n;
+    const int32_t* idx = topk_idx + (size_t)t * k;
+    const double* w = topk_w + (size_t)t * k;
+    const double* p = probs + (size_t)t * n;
+    const double* dg = dG + (size_t)t * k;
+    double* dH = (double*)calloc((size_t)n, sizeof(double));
+    double* dsp = (double*)calloc((size_t)n, sizeof(double));
+    double* dc = dclean + (size_t)t * n;
+    for (int j = 0; j < n; ++j) dc[j] = 0.0;
+
+    /* 1 + 2: the gate distribution and its normalisation. */
+    if (mode == ORACLE_GATE_SWITCH_TOP1) {
+      double* gp = (double*)malloc(sizeof(double) * (size_t)n);
+      for (int j = 0; j < n; ++j) {
+        gp[j] = dImp[j];
+        if (p[j] > 0.0) gp[j] += c_ent * (log(p[j]) + 1.0);
+      }
+      gp[idx[0]] += dg[0];
+      double dot = 0.0;
+      for (int j = 0; j < n; ++j) dot += p[j] * gp[j];
+      for (int j = 0; j < n; ++j) dH[j] += p[j] * (gp[j] - dot);
+      free(gp);
+    } else {
+      double* gg = (double*)malloc(sizeof(double) * (size_t)k);
+      for (int s = 0; s < k; ++s) {
+        gg[s] = dg[s] + dImp[idx[s]];
+        if (w[s] > 0.0) gg[s] += c_ent * (log(w[s]) + 1.0);
+      }
+      double dot = 0.0;
+      for (int s = 0; s < k; ++s) dot += w[s] * gg[s];
+      if (mode == ORACLE_GATE_SIGMOID_BIAS) {
+        /* g_s = sig_s / S: d g_s / d h_j = sig'_j / S * ([s == j] - g_s). */
+        double S = 0.0;
+        for (int s = 0; s < k; ++s) S += 1.0 / (1.0 + exp(-zs[idx[s]]));
+        for (int s = 0; s < k; ++s) {
+          double sg = 1.0 / (1.0 + exp(-zs[idx[s]]));
+          dH[idx[s]] += sg * (1.0 - sg) / S * (gg[s] - dot);
+        }
+      } else {
+        for (int s = 0; s < k; ++s) dH[idx[s]] += w[s] * (gg[s] - dot);
+      }
+      free(gg);
+    }
+
+    /* 3: the z statistic. */
+    for (int j = 0; j < n; ++j) dH[j] += 2.0 * c_z * zs[j];
+
+    /* 4: the smooth load estimator. */
+    if (dLoad && sp) {
+      int owner_k = -1; /* the expert of rank k: largest H outside the kept set */
+      for (int j = 0; j < n; ++j) {
+        int kept = 0;
+        for (int s = 0; s < k; ++s) kept |= (idx[s] == j);
+        if (kept) continue;
+        if (owner_k < 0 || hs[j] > hs[owner_k]) owner_k = j;
+      }
+      for (int i = 0; i < n; ++i) {
+        int kept = 0;
+        for (int s = 0; s < k; ++s) kept |= (idx[s] == i);
+        double thr = kept ? h_k1[t] : h_k[t];
+        if (isinf(thr)) continue;
+        double spi = sp[(size_t)t * n + i];
+        double zeta = (clean[(size_t)t * n + i] - thr) / spi;
+        double q = dLoad[i] * std_normal_pdf(zeta) / spi;
+        dc[i] += q;
+        dsp[i] -= q * zeta;
+        dH[kept ? owner_k : idx[k - 1]] -= q;
+      }
+    }
+
+    /* 5: back to clean and raw. */
+    for (int j = 0; j < n; ++j) dc[j] += dH[j];
+    if (draw && sp) {
+      for (int j = 0; j < n; ++j) {
+        double zz = z ? z[(size_t)t * n + j] : 0.0;
+        double r = raw[(size_t)t * n + j];
+        draw[(size_t)t * n + j] = (dsp[j] + zz * dH[j]) / (1.0 + exp(-r));
+      }
+    }
+    free(dH);
+    free(dsp);
+  }
 }
