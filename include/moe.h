@@ -1,6 +1,6 @@
 /*
  * moe.h -- C ABI of the MI355X (gfx950) Sparsely-Gated Mixture-of-Experts
- * layer forward.
+ * layer: forward and backward.
  *
  * The layer computes y = sum_i G(x)_i * E_i(x) over n experts, with the
  * noisy top-k gate G(x) = Softmax(KeepTopK(H(x), k)),
@@ -304,6 +304,56 @@ moe_status moe_router_bias_update(const moe_config* cfg, const int32_t* counts_p
 moe_status moe_forward(const moe_config* cfg, const moe_weights* weights, const float* x,
                        const float* noise, const float* noise2, float* y, float* losses,
                        const moe_diag* diag, void* ws, size_t ws_bytes, void* stream);
+
+/* Gradient outputs of moe_backward (a host struct holding device pointers),
+ * all fp32, shaped like the matching weights.  A gradient is written iff its
+ * weight is present (then the pointer is required); db_gate also needs a
+ * softmax or Switch gate (the sigmoid gate's bias only moves the selection
+ * and receives no gradient; db_gate must then be NULL). */
+typedef struct {
+  float* dx;       /* [T, d] */
+  float* dw_gate;  /* [n, d] */
+  float* db_gate;  /* [n] */
+  float* dw_noise; /* [n, d] */
+  float* dw1;      /* [n, h, d] */
+  float* db1;      /* [n, h] */
+  float* dw3;      /* [n, h, d] */
+  float* dw2;      /* [n, d, h] */
+  float* db2;      /* [n, d] */
+  float* dws1;     /* [h_s, d] */
+  float* dws3;     /* [h_s, d] */
+  float* dws2;     /* [d, h_s] */
+} moe_grads;
+
+/* Bytes of workspace moe_backward needs (0 on an invalid or unsupported
+ * config). */
+size_t moe_backward_workspace_size(const moe_config* cfg);
+
+/* Backward pass of the flat layer: the gradients of
+ *   L = sum_t <dy_t, y_t> + sum_j dlosses[j] * losses[j]
+ * (y and losses[5] as moe_forward computes them) with respect to x and every
+ * weight, the routing (the top-k selection and the capacity drops) held
+ * fixed.  The forward's routing and activations are recomputed first with
+ * the forward's kernels, so they are the forward's bit for bit.
+ *   Definition: xyznot.com summary, FAQ on training through the top-k (the
+ *   selection precedes the softmax, so the kept gate values are
+ *   differentiable in the gate's weights); chenshi221.pages.dev notes,
+ *   "Noisy Top-K Gating" (the noise term lets the load loss pass gradients,
+ *   through P(x,i) into the clean logit, the noise scale and the
+ *   threshold's logit).  The bf16 roundings of the forward pass gradients
+ *   unchanged.
+ * Arithmetic: the expert gradients are bf16 MFMA products with fp32
+ * accumulation (the gradient rows entering them are rounded to bf16); the
+ * gate's gradients are fp32.
+ * In:  weights, x [T, d], noise [T, n] as for moe_forward; dy [T, d] fp32;
+ *      dlosses [5] fp32 device vector.
+ * Out: every gradient of `grads` (see moe_grads).
+ * Supported: flat layers (n_groups == 0), expert_dtype MOE_BF16, d_model,
+ * d_hidden and d_hidden_shared multiples of 64; MOE_ERR_UNSUPPORTED
+ * otherwise.  ws: moe_backward_workspace_size(cfg) bytes. */
+moe_status moe_backward(const moe_config* cfg, const moe_weights* weights, const float* x,
+                        const float* noise, const float* dy, const float* dlosses,
+                        const moe_grads* grads, void* ws, size_t ws_bytes, void* stream);
 
 /* Kernel timing, a tracing aid (off by default).  moe_profile_enable(1)
  * clears earlier results and starts bracketing every kernel launch of the

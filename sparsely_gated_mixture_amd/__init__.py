@@ -1,4 +1,4 @@
-"""MI355X-native Sparsely-Gated Mixture-of-Experts layer forward.
+"""MI355X-native Sparsely-Gated Mixture-of-Experts layer: forward and backward.
 
 The computation lives in libmoe.so (hand-written HIP for gfx950 behind the C
 ABI of include/moe.h).  This package holds the ctypes binding, a small helper
@@ -11,8 +11,9 @@ from __future__ import annotations
 from . import workloads
 from ._lib import (EXPORTS, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED,
                    MOE_ERR_WORKSPACE, MOE_OK, N_LOSSES, MoeConfig, MoeDiag, MoEError,
-                   MoeWeights, load_library, make_config, make_diag, make_weights,
-                   moe_aux_loss, moe_combine, moe_dispatch, moe_expert_ffn,
+                   MoeGrads, MoeWeights, load_library, make_config, make_diag, make_grads,
+                   make_weights, moe_aux_loss, moe_backward, moe_backward_workspace_size,
+                   moe_combine, moe_dispatch, moe_expert_ffn,
                    moe_fp8_weight_bytes, moe_forward, moe_pack_fp8_weights,
                    moe_gate, moe_gate_hier, moe_last_error, moe_profile_collect,
                    moe_profile_enable, moe_profile_entry, moe_router_bias_update,
@@ -78,11 +79,40 @@ class MoELayer:
         moe_forward(self.c, self.w, x, noise, noise2, y, losses, dg, self.ws)
         return y, losses
 
+    # gradient name -> weight it belongs to
+    _GRAD_OF = dict(dw_gate="w_gate", db_gate="b_gate", dw_noise="w_noise", dw1="w1",
+                    db1="b1", dw3="w3", dw2="w2", db2="b2", dws1="ws1", dws3="ws3", dws2="ws2")
+
+    def backward(self, x, dy, dlosses=None, noise=None):
+        """Gradients of sum <dy, y> + sum dlosses * losses (dlosses: 5 values,
+        default zeros) through moe_backward; returns a dict of fp32 tensors
+        (dx and one per present weight; no db_gate for the sigmoid gate)."""
+        import torch
+        if getattr(self, "ws_bwd", None) is None:
+            size = moe_backward_workspace_size(self.c)
+            if size == 0:
+                raise MoEError(MOE_ERR_UNSUPPORTED, "the backward pass does not cover this "
+                               "configuration (flat bf16 layers, sizes multiples of 64)")
+            self.ws_bwd = torch.empty(size, dtype=torch.uint8, device=self.device)
+        if dlosses is None:
+            dlosses = torch.zeros(N_LOSSES, dtype=torch.float32, device=self.device)
+        grads = {"dx": torch.empty((self.c.T, self.c.d_model), dtype=torch.float32,
+                                   device=self.device)}
+        for g, wname in self._GRAD_OF.items():
+            t = self.weights.get(wname)
+            if t is None or (g == "db_gate" and int(self.cfg.gate) == 2):
+                continue
+            grads[g] = torch.empty(t.shape, dtype=torch.float32, device=self.device)
+        moe_backward(self.c, self.w, x, noise, dy, dlosses, make_grads(**grads), self.ws_bwd)
+        return grads
+
 
 __all__ = ["workloads", "EXPORTS", "MoELayer", "pack_fp8", "moe_fp8_weight_bytes",
-           "moe_pack_fp8_weights", "MOE_F32", "MOE_BF16", "MOE_FP8", "MoEError", "MoeConfig", "MoeWeights", "MoeDiag",
-           "make_config", "make_weights", "make_diag", "moe_workspace_size", "moe_gate",
-           "moe_gate_hier", "moe_dispatch", "moe_expert_ffn", "moe_shared_ffn", "moe_combine",
-           "moe_aux_loss", "moe_router_bias_update", "moe_forward", "N_LOSSES", "moe_status_string", "moe_last_error", "moe_profile_enable",
-           "moe_profile_collect", "moe_profile_entry", "MOE_OK", "MOE_ERR_INVALID_ARG",
-           "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP"]
+           "moe_pack_fp8_weights", "MOE_F32", "MOE_BF16", "MOE_FP8", "MoEError", "MoeConfig",
+           "MoeWeights", "MoeDiag", "MoeGrads", "make_config", "make_weights", "make_diag",
+           "make_grads", "moe_workspace_size", "moe_gate", "moe_gate_hier", "moe_dispatch",
+           "moe_expert_ffn", "moe_shared_ffn", "moe_combine", "moe_aux_loss",
+           "moe_router_bias_update", "moe_forward", "moe_backward_workspace_size",
+           "moe_backward", "N_LOSSES", "moe_status_string", "moe_last_error",
+           "moe_profile_enable", "moe_profile_collect", "moe_profile_entry", "MOE_OK",
+           "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP"]

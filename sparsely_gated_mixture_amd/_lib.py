@@ -20,10 +20,11 @@ MOE_ERR_UNSUPPORTED = 2
 MOE_ERR_WORKSPACE = 3
 MOE_ERR_HIP = 4
 
-EXPORTS = ["moe_workspace_size", "moe_fp8_weight_bytes", "moe_pack_fp8_weights", "moe_gate", "moe_gate_hier", "moe_dispatch", "moe_expert_ffn",
-           "moe_shared_ffn", "moe_combine", "moe_aux_loss", "moe_router_bias_update",
-           "moe_forward", "moe_status_string", "moe_last_error", "moe_profile_enable",
-           "moe_profile_collect", "moe_profile_entry"]
+EXPORTS = ["moe_workspace_size", "moe_fp8_weight_bytes", "moe_pack_fp8_weights", "moe_gate",
+           "moe_gate_hier", "moe_dispatch", "moe_expert_ffn", "moe_shared_ffn", "moe_combine",
+           "moe_aux_loss", "moe_router_bias_update", "moe_forward",
+           "moe_backward_workspace_size", "moe_backward", "moe_status_string",
+           "moe_last_error", "moe_profile_enable", "moe_profile_collect", "moe_profile_entry"]
 
 N_LOSSES = 5  # importance, load, Switch, router z-loss, -gate entropy
 
@@ -60,6 +61,12 @@ class MoeDiag(ctypes.Structure):
                 ("slot_pos", _vp)]
 
 
+class MoeGrads(ctypes.Structure):
+    _fields_ = [("dx", _vp), ("dw_gate", _vp), ("db_gate", _vp), ("dw_noise", _vp),
+                ("dw1", _vp), ("db1", _vp), ("dw3", _vp), ("dw2", _vp), ("db2", _vp),
+                ("dws1", _vp), ("dws3", _vp), ("dws2", _vp)]
+
+
 _lib = None
 
 
@@ -92,6 +99,10 @@ def load_library():
     L.moe_router_bias_update.argtypes = [cfgp, P, P, ctypes.c_float, P]
     L.moe_forward.argtypes = [cfgp, ctypes.POINTER(MoeWeights)] + [P] * 5 + \
         [ctypes.POINTER(MoeDiag), P, S, P]
+    L.moe_backward_workspace_size.argtypes = [cfgp]
+    L.moe_backward_workspace_size.restype = S
+    L.moe_backward.argtypes = [cfgp, ctypes.POINTER(MoeWeights)] + [P] * 4 + \
+        [ctypes.POINTER(MoeGrads), P, S, P]
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_last_error.argtypes = []
@@ -105,7 +116,8 @@ def load_library():
                                     ctypes.POINTER(ctypes.c_longlong)]
     L.moe_profile_entry.restype = ctypes.c_int
     for name in ("moe_gate", "moe_gate_hier", "moe_dispatch", "moe_expert_ffn", "moe_shared_ffn",
-                 "moe_combine", "moe_aux_loss", "moe_router_bias_update", "moe_forward"):
+                 "moe_combine", "moe_aux_loss", "moe_router_bias_update", "moe_forward",
+                 "moe_backward"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -261,6 +273,24 @@ def moe_forward(cfg, weights: MoeWeights, x, noise, noise2, y, losses, diag: Moe
                                       _ptr(noise), _ptr(noise2), _ptr(y), _ptr(losses),
                                       ctypes.byref(diag) if diag is not None else None, wp, wb,
                                       _stream(stream)))
+
+
+def moe_backward_workspace_size(cfg) -> int:
+    c = make_config(cfg)
+    return int(load_library().moe_backward_workspace_size(ctypes.byref(c)))
+
+
+def make_grads(**kw) -> MoeGrads:
+    return MoeGrads(*[_ptr(kw.get(f)) for f, _ in MoeGrads._fields_])
+
+
+def moe_backward(cfg, weights: MoeWeights, x, noise, dy, dlosses, grads: MoeGrads, ws,
+                 stream=None):
+    c = make_config(cfg)
+    wp, wb = _ws(ws)
+    _check(load_library().moe_backward(ctypes.byref(c), ctypes.byref(weights), _ptr(x),
+                                       _ptr(noise), _ptr(dy), _ptr(dlosses),
+                                       ctypes.byref(grads), wp, wb, _stream(stream)))
 
 
 def moe_profile_enable(on: bool) -> None:

@@ -1,5 +1,5 @@
-// C ABI of the MoE layer forward: argument validation, workspace layout and
-// the launch sequence of each stage.  Validation runs before any HIP call,
+// C ABI of the MoE layer (forward and backward): argument validation,
+// workspace layout and the launch sequence of each stage.  Validation runs before any HIP call,
 // so a failing call enqueues nothing.
 #include <hip/hip_runtime.h>
 
@@ -693,6 +693,207 @@ moe_status check_gate_ptrs(const moe_config& c, const float* x, const float* w_g
   return MOE_OK;
 }
 
+
+// ---------------------------------------------------------------------------
+// Backward workspace: the forward's plan, with the gate logits and the hidden
+// activations moved out of the stage scratch (the backward reads them after
+// later stages ran), followed by the backward's own buffers.
+// ---------------------------------------------------------------------------
+struct BwdPlan {
+  Plan f;  // forward plan (logits / hidden relocated)
+  int M = 0, ldk = 0, splits = 0, tps = 0, hw = 0, hws = 0;
+  Region losses, dG, dout, dimp, dload, coef, dlogits, part_db, dpre, a_pre, b_pre, du_perm,
+      dx_gate, wt, wpart, a_s, b_s, dout_s, dpre_s, du_s;
+  size_t total = 0;
+};
+
+BwdPlan make_bwd_plan(const moe_config& c) {
+  BwdPlan b;
+  b.f = make_plan(c);
+  const long long T = c.T, d = c.d_model, h = c.d_hidden, n = c.n_experts;
+  const long long A1 = std::max(1LL, (long long)T * c.k);
+  const long long T1 = std::max(1LL, T);
+  const bool swiglu = c.act == MOE_ACT_SWIGLU;
+  Cursor w{b.f.total};
+  b.f.logits = w.take(T1 * b.f.ldl * 4);
+  b.f.hidden = w.take(A1 * h * 2);
+  b.losses = w.take(8 * 4);
+  b.dG = w.take(A1 * 4);
+  b.dout = w.take(A1 * d * 2);
+  b.dimp = w.take(n * 4);
+  b.dload = w.take(n * 4);
+  b.coef = w.take(4 * 4);
+  b.dlogits = w.take(T1 * b.f.ldl * 4);
+  b.part_db = w.take((size_t)std::max(1, b.f.nparts) * n * 4);
+  b.hw = swiglu ? 2 * (int)h : (int)h;  // width of the hidden-layer gradient rows
+  b.dpre = w.take(A1 * b.hw * 2);
+  if (swiglu) {
+    b.a_pre = w.take(A1 * h * 4);
+    b.b_pre = w.take(A1 * h * 4);
+  }
+  b.du_perm = w.take(A1 * d * 4);
+  b.dx_gate = w.take(T1 * d * 4);
+  b.M = (int)n * 2;  // dclean | draw columns of dlogits (draw unused when noiseless)
+  b.ldk = (int)round_up(b.M, 4);
+  b.wt = w.take(d * b.ldk * 4);
+  b.splits = gate_wgrad_splits((int)T, (int)d, b.M);
+  b.tps = (int)std::max(1LL, (T + b.splits - 1) / b.splits);
+  b.wpart = w.take((size_t)b.splits * b.M * d * 4);
+  if (c.d_hidden_shared > 0) {
+    const long long hs = c.d_hidden_shared;
+    b.hws = swiglu ? 2 * (int)hs : (int)hs;
+    if (swiglu) {
+      b.a_s = w.take(T1 * hs * 4);
+      b.b_s = w.take(T1 * hs * 4);
+    }
+    b.dout_s = w.take(T1 * d * 2);
+    b.dpre_s = w.take(T1 * b.hws * 2);
+    b.du_s = w.take(T1 * d * 4);
+  }
+  b.total = w.at;
+  return b;
+}
+
+moe_status validate_bwd(const moe_config& c) {
+  if (c.n_groups > 0)
+    return fail(MOE_ERR_UNSUPPORTED, "the backward pass covers flat layers (n_groups == 0)");
+  if (c.expert_dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "the backward pass needs bf16 experts");
+  if (c.d_model % 64 || c.d_hidden % 64 || c.d_hidden_shared % 64)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "the backward pass needs d_model, d_hidden and d_hidden_shared multiples of 64");
+  return MOE_OK;
+}
+
+// First GEMM of an expert FFN for the backward: the hidden activations (bf16)
+// and, for SwiGLU, the two fp32 pre-activations they come from.
+moe_status bwd_hidden(const moe_config& c, GemmBf16Args g, int h, uint16_t* hidden, float* a_pre,
+                      float* b_pre, long long elems, hipStream_t s) {
+  g.N = h;
+  g.ldc = h;
+  if (c.act == MOE_ACT_SWIGLU) {
+    const void* w3 = g.B3;
+    g.B3 = nullptr;
+    g.C = a_pre;
+    HIP_TRY(launch_gemm_bf16(g, EPI_IDENT_F32, s));
+    g.B1 = w3;
+    g.C = b_pre;
+    HIP_TRY(launch_gemm_bf16(g, EPI_IDENT_F32, s));
+    HIP_TRY(launch_swiglu_hidden(a_pre, b_pre, elems, hidden, s));
+  } else {
+    g.C = hidden;
+    HIP_TRY(launch_gemm_bf16(g, EPI_RELU_BF16, s));
+  }
+  return MOE_OK;
+}
+
+// The four products of one FFN's backward over merged rows (routed experts:
+// the dispatch's tile map; shared expert: a one-segment map).
+struct FfnBwd {
+  const uint16_t* u;       // inputs [rows, d] bf16
+  const uint16_t* hidden;  // [rows, h]
+  const float* a_pre;      // SwiGLU pre-activations [rows, h]
+  const float* b_pre;
+  const uint16_t* gout;    // output gradient rows [rows, d] bf16
+  uint16_t* dpre;          // [rows, hw]
+  float* du;               // [rows, d]
+  const void* w1;
+  const void* w3;
+  const void* w2;
+  long long stride1, stride2;  // elements between experts' w1 (and w3) / w2
+  float* dw1;
+  float* dw3;
+  float* dw2;
+  const int32_t* tile_expert;
+  const int32_t* tile_row0;
+  const int32_t* offsets;
+  const int32_t* tile_count;
+  int max_tiles, n_experts, h;
+  const char* names[4];
+};
+
+moe_status ffn_bwd(const moe_config& c, const FfnBwd& f, hipStream_t s) {
+  const int d = c.d_model, h = f.h;
+  const bool swiglu = c.act == MOE_ACT_SWIGLU;
+  const int hw = swiglu ? 2 * h : h;
+  GemmBwdArgs g{};
+  g.tile_expert = f.tile_expert;
+  g.tile_row0 = f.tile_row0;
+  g.offsets = f.offsets;
+  g.tile_count = f.tile_count;
+  g.max_tiles = f.max_tiles;
+  g.n_experts = f.n_experts;
+  // (i) dhid = gout . W2 -> dpre (ReLU mask or SwiGLU da | db)
+  g.A = (const uint16_t*)f.w2;
+  g.lda = h;
+  g.strideA = f.stride2;
+  g.k_split = d;
+  g.B = f.gout;
+  g.ldb = d;
+  g.M = h;
+  g.N = 0;
+  g.K = d;
+  g.Cb = f.dpre;
+  g.ldc = hw;
+  g.c_split = h;
+  g.aux_h = f.hidden;
+  g.aux_a = f.a_pre;
+  g.aux_b = f.b_pre;
+  g.ldaux = h;
+  HIP_TRY(launch_gemm_bwd(g, BWD_ROWS, swiglu ? BEPI_SWIGLU : BEPI_RELU_MASK, f.names[0], s));
+  // (ii) du = dpre . [W1; W3]
+  GemmBwdArgs g2{};
+  g2.tile_expert = f.tile_expert;
+  g2.tile_row0 = f.tile_row0;
+  g2.offsets = f.offsets;
+  g2.tile_count = f.tile_count;
+  g2.max_tiles = f.max_tiles;
+  g2.A = (const uint16_t*)f.w1;
+  g2.A2 = swiglu ? (const uint16_t*)f.w3 : nullptr;
+  g2.lda = d;
+  g2.strideA = f.stride1;
+  g2.k_split = h;
+  g2.B = f.dpre;
+  g2.ldb = hw;
+  g2.M = d;
+  g2.K = hw;
+  g2.C = f.du;
+  g2.ldc = d;
+  HIP_TRY(launch_gemm_bwd(g2, BWD_ROWS, BEPI_F32, f.names[1], s));
+  // (iii) dW2[e] = gout^T . hidden over the expert's rows
+  GemmBwdArgs g3{};
+  g3.offsets = f.offsets;
+  g3.n_experts = f.n_experts;
+  g3.A = f.hidden;
+  g3.lda = h;
+  g3.B = f.gout;
+  g3.ldb = d;
+  g3.M = h;
+  g3.N = d;
+  g3.C = f.dw2;
+  g3.ldc = h;
+  g3.strideC = (long long)d * h;
+  g3.c_split = d;
+  HIP_TRY(launch_gemm_bwd(g3, BWD_WGRAD, BEPI_F32, f.names[2], s));
+  // (iv) [dW1; dW3][e] = dpre^T . u
+  GemmBwdArgs g4{};
+  g4.offsets = f.offsets;
+  g4.n_experts = f.n_experts;
+  g4.A = f.u;
+  g4.lda = d;
+  g4.B = f.dpre;
+  g4.ldb = hw;
+  g4.M = d;
+  g4.N = hw;
+  g4.C = f.dw1;
+  g4.C2 = f.dw3;
+  g4.ldc = d;
+  g4.strideC = (long long)h * d;
+  g4.c_split = h;
+  HIP_TRY(launch_gemm_bwd(g4, BWD_WGRAD, BEPI_F32, f.names[3], s));
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -954,6 +1155,274 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const float
   float* ysh = shared ? at<float>(ws, p.sh_y) : nullptr;
   if (shared) CHECK(run_shared_ffn(c, p, fx.x_bf16, wt->ws1, wt->ws3, wt->ws2, ysh, ws, s));
   HIP_TRY(launch_combine(yperm, slot, w, ysh, c.T, c.k, c.d_model, y, s));
+  return MOE_OK;
+}
+
+size_t moe_backward_workspace_size(const moe_config* cfg) {
+  if (validate(cfg) != MOE_OK || validate_bwd(*cfg) != MOE_OK) return 0;
+  return make_bwd_plan(*cfg).total;
+}
+
+moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const float* x,
+                        const float* noise, const float* dy, const float* dlosses,
+                        const moe_grads* gr, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  CHECK(validate(cfg));
+  const moe_config& c = *cfg;
+  CHECK(validate_bwd(c));
+  if (!wt) return fail(MOE_ERR_INVALID_ARG, "weights must not be NULL");
+  if (!gr) return fail(MOE_ERR_INVALID_ARG, "grads must not be NULL");
+  CHECK(check_gate_ptrs(c, x, wt->w_gate, wt->b_gate, wt->w_noise, noise));
+  const bool swiglu = c.act == MOE_ACT_SWIGLU;
+  const bool shared = c.d_hidden_shared > 0;
+  const bool noisy = wt->w_noise != nullptr;
+  CHECK(need(wt->w1, "weights->w1"));
+  CHECK(need(wt->w2, "weights->w2"));
+  if (swiglu) {
+    CHECK(need(wt->w3, "weights->w3 (required for SwiGLU)"));
+    if (wt->b1 || wt->b2) return fail(MOE_ERR_UNSUPPORTED, "SwiGLU experts take no biases");
+  }
+  CHECK(optional(wt->b1, "weights->b1"));
+  CHECK(optional(wt->b2, "weights->b2"));
+  if (shared) CHECK(check_shared_ptrs(c, wt->ws1, wt->ws3, wt->ws2));
+  CHECK(need(dy, "dy", c.T == 0));
+  CHECK(need(dlosses, "dlosses"));
+  CHECK(need(gr->dx, "grads->dx", c.T == 0));
+  CHECK(need(gr->dw_gate, "grads->dw_gate"));
+  const bool want_db = wt->b_gate && c.gate != MOE_GATE_SIGMOID_BIAS;
+  if (want_db) CHECK(need(gr->db_gate, "grads->db_gate"));
+  if (noisy) CHECK(need(gr->dw_noise, "grads->dw_noise"));
+  CHECK(need(gr->dw1, "grads->dw1"));
+  CHECK(need(gr->dw2, "grads->dw2"));
+  if (swiglu) CHECK(need(gr->dw3, "grads->dw3"));
+  if (wt->b1) CHECK(need(gr->db1, "grads->db1"));
+  if (wt->b2) CHECK(need(gr->db2, "grads->db2"));
+  if (shared) {
+    CHECK(need(gr->dws1, "grads->dws1"));
+    CHECK(need(gr->dws2, "grads->dws2"));
+    if (swiglu) CHECK(need(gr->dws3, "grads->dws3"));
+  }
+  const BwdPlan b = make_bwd_plan(c);
+  const Plan& p = b.f;
+  CHECK(check_ws(ws, ws_bytes, b.total, "moe_backward"));
+  hipStream_t s = (hipStream_t)stream;
+  const int T = c.T, d = c.d_model, h = c.d_hidden, n = c.n_experts, k = c.k;
+  const long long A = (long long)T * k;
+
+  // ---- forward recompute ------------------------------------------------
+  int32_t* idx = at<int32_t>(ws, p.f_idx);
+  float* w = at<float>(ws, p.f_w);
+  float* imp = at<float>(ws, p.f_imp);
+  float* ld = at<float>(ws, p.f_load);
+  int32_t* counts_pre = at<int32_t>(ws, p.f_counts_pre);
+  int32_t* counts = at<int32_t>(ws, p.f_counts);
+  int32_t* offsets = at<int32_t>(ws, p.f_offsets);
+  int32_t* perm = at<int32_t>(ws, p.f_perm);
+  int32_t* slot = at<int32_t>(ws, p.f_slot);
+  uint16_t* xperm = at<uint16_t>(ws, p.f_xperm);
+  float* yperm = at<float>(ws, p.f_yperm);
+  float* stats = at<float>(ws, p.f_stats);
+  uint16_t* hidden = at<uint16_t>(ws, p.hidden);
+  float* a_pre = swiglu ? at<float>(ws, b.a_pre) : nullptr;
+  float* b_pre = swiglu ? at<float>(ws, b.b_pre) : nullptr;
+  CHECK(run_gate(c, p, x, wt->w_gate, wt->b_gate, wt->w_noise, noise, idx, w, imp, ld, stats, ws,
+                 s));
+  ForwardExtras fx;
+  fx.tile_expert = at<int32_t>(ws, p.f_tile_expert);
+  fx.tile_row0 = at<int32_t>(ws, p.f_tile_row0);
+  fx.tile_count = at<int32_t>(ws, p.f_tile_count);
+  fx.losses = at<float>(ws, b.losses);
+  fx.importance = imp;
+  fx.load = noisy ? ld : nullptr;
+  fx.gate_stats = stats;
+  fx.x_bf16 = shared ? at<uint16_t>(ws, p.sh_xb) : nullptr;
+  CHECK(run_dispatch(c, p, idx, x, counts_pre, counts, offsets, perm, slot, xperm, ws, s, &fx));
+  GemmBf16Args g1{};
+  g1.A = xperm;
+  g1.lda = d;
+  g1.B1 = wt->w1;
+  g1.B3 = wt->w3;
+  g1.strideB = (long long)h * d * 2;
+  g1.K = d;
+  g1.bias = wt->b1;
+  g1.tile_expert = fx.tile_expert;
+  g1.tile_row0 = fx.tile_row0;
+  g1.offsets = offsets;
+  g1.tile_count = fx.tile_count;
+  g1.max_mtiles = p.max_mtiles;
+  g1.num_cus = device_cus();
+  CHECK(bwd_hidden(c, g1, h, hidden, a_pre, b_pre, A * h, s));
+  GemmBf16Args g2 = g1;
+  g2.A = hidden;
+  g2.lda = h;
+  g2.B1 = wt->w2;
+  g2.B3 = nullptr;
+  g2.strideB = (long long)d * h * 2;
+  g2.N = d;
+  g2.K = h;
+  g2.C = yperm;
+  g2.ldc = d;
+  g2.bias = wt->b2;
+  HIP_TRY(launch_gemm_bf16(g2, EPI_IDENT_F32, s));
+  const int hs = c.d_hidden_shared;
+  uint16_t* xb = shared ? at<uint16_t>(ws, p.sh_xb) : nullptr;
+  uint16_t* hid_s = shared ? at<uint16_t>(ws, p.sh_hidden) : nullptr;
+  int32_t* sh_off = shared ? at<int32_t>(ws, p.sh_off) : nullptr;
+  int32_t* sh_te = shared ? at<int32_t>(ws, p.sh_te) : nullptr;
+  int32_t* sh_tr = shared ? at<int32_t>(ws, p.sh_tr) : nullptr;
+  int32_t* sh_tc = shared ? at<int32_t>(ws, p.sh_tc) : nullptr;
+  float* a_s = shared && swiglu ? at<float>(ws, b.a_s) : nullptr;
+  float* b_s = shared && swiglu ? at<float>(ws, b.b_s) : nullptr;
+  if (shared) {
+    HIP_TRY(launch_shared_tilemap(T, kBf16BM, sh_off, sh_te, sh_tr, sh_tc, s));
+    GemmBf16Args gs{};
+    gs.A = xb;
+    gs.lda = d;
+    gs.B1 = wt->ws1;
+    gs.B3 = wt->ws3;
+    gs.K = d;
+    gs.tile_expert = sh_te;
+    gs.tile_row0 = sh_tr;
+    gs.offsets = sh_off;
+    gs.tile_count = sh_tc;
+    gs.max_mtiles = p.sh_tiles;
+    gs.num_cus = device_cus();
+    gs.shared = 1;
+    CHECK(bwd_hidden(c, gs, hs, hid_s, a_s, b_s, (long long)T * hs, s));
+  }
+
+  // ---- backward ---------------------------------------------------------
+  float* dG = at<float>(ws, b.dG);
+  uint16_t* dout = at<uint16_t>(ws, b.dout);
+  float* dimp = at<float>(ws, b.dimp);
+  float* dload = at<float>(ws, b.dload);
+  float* coef = at<float>(ws, b.coef);
+  float* dlogits = at<float>(ws, b.dlogits);
+  HIP_TRY(launch_combine_bwd(dy, yperm, slot, w, T, k, d, dG, dout, s));
+  HIP_TRY(launch_loss_grad(imp, noisy ? ld : nullptr, counts_pre, dlosses, T, k, n,
+                           c.w_importance, c.w_load, c.alpha_switch, c.w_z, c.w_entropy, dimp,
+                           dload, coef, s));
+  GateBwdArgs gb{};
+  gb.T = T;
+  gb.n = n;
+  gb.k = k;
+  gb.switch_mode = c.gate == MOE_GATE_SWITCH_TOP1;
+  gb.sigmoid_mode = c.gate == MOE_GATE_SIGMOID_BIAS;
+  gb.noisy = noisy;
+  gb.logits = at<float>(ws, p.logits);
+  gb.ldl = p.ldl;
+  gb.bias = wt->b_gate;
+  gb.noise = noise;
+  gb.topk_idx = idx;
+  gb.topk_w = w;
+  gb.dG = dG;
+  gb.dimp = dimp;
+  gb.dload = dload;
+  gb.coef = coef;
+  gb.dlogits = dlogits;
+  gb.ldd = p.ldl;
+  gb.part_db = want_db ? at<float>(ws, b.part_db) : nullptr;
+  gb.rows_per_block = p.rows_per_block;
+  HIP_TRY(launch_gate_bwd(gb, s));
+  if (want_db)
+    HIP_TRY(launch_colsum(p.nparts, ColsumVec{gb.part_db, n, gr->db_gate},
+                          ColsumVec{nullptr, 0, nullptr}, ColsumVec{nullptr, 0, nullptr}, s));
+  const int M = noisy ? 2 * n : n;
+  GateWgradArgs gw{};
+  gw.x = x;
+  gw.dlogits = dlogits;
+  gw.ldd = p.ldl;
+  gw.T = T;
+  gw.d = d;
+  gw.M = M;
+  gw.n = n;
+  gw.splits = b.splits;
+  gw.tokens_per_split = b.tps;
+  gw.partial = at<float>(ws, b.wpart);
+  HIP_TRY(launch_gate_wgrad(gw, gr->dw_gate, gr->dw_noise, s));
+  float* dx_gate = at<float>(ws, b.dx_gate);
+  if (T > 0) {
+    const int ldk = (int)round_up(M, 4);
+    float* wtr = at<float>(ws, b.wt);
+    HIP_TRY(launch_transpose_gate(wt->w_gate, wt->w_noise, n, d, ldk, wtr, s));
+    GemmF32Args gx{};
+    gx.A = dlogits;
+    gx.lda = p.ldl;
+    gx.B1 = wtr;
+    gx.B2 = wtr;
+    gx.n1 = d;
+    gx.N = d;
+    gx.K = ldk;
+    gx.C = dx_gate;
+    gx.ldc = d;
+    gx.M = T;
+    gx.mtiles = (T + p.gemm_bm - 1) / p.gemm_bm;
+    gx.max_mtiles = gx.mtiles;
+    HIP_TRY(launch_gemm_f32(gx, p.gemm_bm, s));
+  }
+  FfnBwd fb{};
+  fb.u = xperm;
+  fb.hidden = hidden;
+  fb.a_pre = a_pre;
+  fb.b_pre = b_pre;
+  fb.gout = dout;
+  fb.dpre = at<uint16_t>(ws, b.dpre);
+  fb.du = at<float>(ws, b.du_perm);
+  fb.w1 = wt->w1;
+  fb.w3 = wt->w3;
+  fb.w2 = wt->w2;
+  fb.stride1 = (long long)h * d;
+  fb.stride2 = (long long)d * h;
+  fb.dw1 = gr->dw1;
+  fb.dw3 = gr->dw3;
+  fb.dw2 = gr->dw2;
+  fb.tile_expert = fx.tile_expert;
+  fb.tile_row0 = fx.tile_row0;
+  fb.offsets = offsets;
+  fb.tile_count = fx.tile_count;
+  fb.max_tiles = p.max_mtiles;
+  fb.n_experts = n;
+  fb.h = h;
+  fb.names[0] = "bwd_ggemm_dhidden";
+  fb.names[1] = "bwd_ggemm_dinput";
+  fb.names[2] = "bwd_ggemm_dw2";
+  fb.names[3] = "bwd_ggemm_dw1";
+  CHECK(ffn_bwd(c, fb, s));
+  if (wt->b2) HIP_TRY(launch_seg_colsum(dout, d, offsets, n, d, gr->db2, s));
+  if (wt->b1) HIP_TRY(launch_seg_colsum(fb.dpre, h, offsets, n, h, gr->db1, s));
+  float* du_s = nullptr;
+  if (shared) {
+    uint16_t* dout_s = at<uint16_t>(ws, b.dout_s);
+    du_s = at<float>(ws, b.du_s);
+    HIP_TRY(launch_to_bf16(dy, (long long)T * d, dout_s, s));
+    FfnBwd fs{};
+    fs.u = xb;
+    fs.hidden = hid_s;
+    fs.a_pre = a_s;
+    fs.b_pre = b_s;
+    fs.gout = dout_s;
+    fs.dpre = at<uint16_t>(ws, b.dpre_s);
+    fs.du = du_s;
+    fs.w1 = wt->ws1;
+    fs.w3 = wt->ws3;
+    fs.w2 = wt->ws2;
+    fs.dw1 = gr->dws1;
+    fs.dw3 = gr->dws3;
+    fs.dw2 = gr->dws2;
+    fs.tile_expert = sh_te;
+    fs.tile_row0 = sh_tr;
+    fs.offsets = sh_off;
+    fs.tile_count = sh_tc;
+    fs.max_tiles = p.sh_tiles;
+    fs.n_experts = 1;
+    fs.h = hs;
+    fs.names[0] = "bwd_shared_dhidden";
+    fs.names[1] = "bwd_shared_dinput";
+    fs.names[2] = "bwd_shared_dw2";
+    fs.names[3] = "bwd_shared_dw1";
+    CHECK(ffn_bwd(c, fs, s));
+  }
+  HIP_TRY(launch_dx_gather(dx_gate, du_s, fb.du, slot, T, k, d, gr->dx, s));
   return MOE_OK;
 }
 

@@ -307,6 +307,237 @@ __global__ __launch_bounds__(NW * 64) void topk_kernel(const TopkArgs p) {
   }
 }
 
+// Backward of the flat gate for one token row per wavefront, the selection
+// (topk_idx) held fixed.  The chain, per row (arXiv 1701.06538 summary,
+// xyznot.com, FAQ on back-propagating through the top-k: the kept values
+// stay differentiable; reading notes, chenshi221.pages.dev, "Noisy Top-K
+// Gating": the noise lets the load loss pass gradients):
+//  1. gradient on the gate distribution: dG from the combine on the kept
+//     slots, dImportance, and c_ent (ln g + 1) from the entropy statistic;
+//  2. through the normalisation: softmax over the kept values, softmax over
+//     all n (Switch), or Sigmoid divided by the kept sum;
+//  3. + 2 c_z Z_j from the z statistic (Z = H; the sigmoid gate: h);
+//  4. the smooth load P_j = Phi((clean_j - thr_j) / sp_j): into clean_j,
+//     sp_j and the threshold, which is the H of the rank-k expert (kept j)
+//     or of the rank k-1 expert (other j);
+//  5. H = clean + z sp: d raw = (d sp + z dH) Sigmoid(raw).
+// H, sp and the thresholds are recomputed with the forward's arithmetic.
+// Writes dlogits[r][j] = dL/d clean_j (sigmoid gate: dL/d h_j) and, for a
+// noisy gate, dlogits[r][n + j] = dL/d raw_j, zeros in the rest of the row;
+// per block, the column sums of the clean part in row order (for the logit
+// bias).
+template <int NPL, int NW>
+__global__ __launch_bounds__(NW * 64) void gate_bwd_kernel(const GateBwdArgs p) {
+  extern __shared__ float red[];  // [NW][n]
+  const int n = p.n, k = p.k;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int part = blockIdx.x;
+  const int row_begin = part * p.rows_per_block;
+  const int row_end = min(row_begin + p.rows_per_block, p.T);
+  const float c_z = p.coef[0], c_ent = p.coef[1];
+
+  float bias[NPL], dimp[NPL], dload[NPL], dbacc[NPL];
+#pragma unroll
+  for (int q = 0; q < NPL; ++q) {
+    const int j = lane + 64 * q;
+    const bool ok = j < n;
+    bias[q] = (p.bias && ok) ? p.bias[j] : 0.f;
+    dimp[q] = ok ? p.dimp[j] : 0.f;
+    dload[q] = (p.noisy && ok) ? p.dload[j] : 0.f;
+    dbacc[q] = 0.f;
+  }
+
+  for (int r = row_begin + wave; r < row_end; r += NW) {
+    const float* lg = p.logits + (long long)r * p.ldl;
+    float c[NPL], cl[NPL], sp[NPL], hv[NPL], rw[NPL], zn[NPL];
+#pragma unroll
+    for (int q = 0; q < NPL; ++q) {
+      const int j = lane + 64 * q;
+      const bool ok = j < n;
+      c[q] = ok ? lg[j] : 0.f;
+      rw[q] = (ok && p.noisy) ? lg[n + j] : 0.f;
+      zn[q] = (ok && p.noisy) ? p.noise[(long long)r * n + j] : 0.f;
+      cl[q] = c[q] + bias[q];
+      sp[q] = 1.f;
+      hv[q] = cl[q];
+      if (p.noisy) {
+        sp[q] = softplus_f(rw[q]);
+        hv[q] = cl[q] + zn[q] * sp[q];
+      }
+    }
+    // Slots: lane s < k holds slot s.
+    const int my_j = lane < k ? p.topk_idx[(long long)r * k + lane] : 0;
+    const float my_w = lane < k ? p.topk_w[(long long)r * k + lane] : 0.f;
+    const float my_dg = lane < k ? p.dG[(long long)r * k + lane] : 0.f;
+    uint32_t kept = 0;
+    for (int s = 0; s < k; ++s) {
+      const int js = readlane_i(my_j, s);
+      if (lane == (js & 63)) kept |= 1u << (js >> 6);
+    }
+    // H of the expert in slot s (fetched from the lane that owns it).
+    auto h_of = [&](int js) {
+      float v = 0.f;
+#pragma unroll
+      for (int q = 0; q < NPL; ++q) {
+        const float t = __shfl(hv[q], js & 63, kWave);
+        if (q == (js >> 6)) v = t;
+      }
+      return v;
+    };
+
+    float dH[NPL];
+#pragma unroll
+    for (int q = 0; q < NPL; ++q) dH[q] = 0.f;
+    if (p.switch_mode) {
+      const int j0 = readlane_i(my_j, 0);
+      const float v0 = h_of(j0);
+      float ls = 0.f;
+#pragma unroll
+      for (int q = 0; q < NPL; ++q)
+        if (lane + 64 * q < n) ls += expf(hv[q] - v0);
+      const float Z = wave_sum_dpp(ls);
+      const float lnZ = hw_log(Z);
+      const float dg0 = readlane_f(my_dg, 0);
+      float pr[NPL], gp[NPL], dotl = 0.f;
+#pragma unroll
+      for (int q = 0; q < NPL; ++q) {
+        const int j = lane + 64 * q;
+        pr[q] = 0.f;
+        gp[q] = 0.f;
+        if (j < n) {
+          pr[q] = expf(hv[q] - v0) / Z;
+          gp[q] = dimp[q] + (pr[q] > 0.f ? c_ent * ((hv[q] - v0) - lnZ + 1.f) : 0.f) +
+                  (j == j0 ? dg0 : 0.f);
+          dotl = fmaf(pr[q], gp[q], dotl);
+        }
+      }
+      const float dot = wave_sum_dpp(dotl);
+#pragma unroll
+      for (int q = 0; q < NPL; ++q) dH[q] = pr[q] * (gp[q] - dot);
+    } else {
+      float gg = 0.f;
+      if (lane < k) {
+        gg = my_dg + p.dimp[my_j];
+        if (my_w > 0.f) gg += c_ent * (hw_log(my_w) + 1.f);
+      }
+      const float dot = wave_sum_dpp(lane < k ? my_w * gg : 0.f);
+      float dz;
+      if (p.sigmoid_mode) {
+        float hsel = 0.f;
+#pragma unroll
+        for (int q = 0; q < NPL; ++q) {
+          const float t = __shfl(c[q], my_j & 63, kWave);
+          if (q == (my_j >> 6)) hsel = t;
+        }
+        const float sg = lane < k ? hw_rcp(1.f + hw_exp(-hsel)) : 0.f;
+        const float S = wave_sum_dpp(sg);
+        dz = lane < k ? sg * (1.f - sg) / S * (gg - dot) : 0.f;
+      } else {
+        dz = lane < k ? my_w * (gg - dot) : 0.f;
+      }
+      for (int s = 0; s < k; ++s) {
+        const int js = readlane_i(my_j, s);
+        const float v = readlane_f(dz, s);
+        if (lane == (js & 63)) {
+#pragma unroll
+          for (int q = 0; q < NPL; ++q)
+            if (q == (js >> 6)) dH[q] += v;
+        }
+      }
+    }
+    // z statistic
+#pragma unroll
+    for (int q = 0; q < NPL; ++q)
+      if (lane + 64 * q < n) dH[q] = fmaf(2.f * c_z, p.sigmoid_mode ? c[q] : hv[q], dH[q]);
+
+    float dcl[NPL], dsp[NPL];
+#pragma unroll
+    for (int q = 0; q < NPL; ++q) dcl[q] = dsp[q] = 0.f;
+    if (p.noisy) {
+      // The rank-k expert: the largest H outside the kept set, lowest index
+      // first on equal H (as in the forward's selection).
+      uint32_t key[NPL], best = 0;
+#pragma unroll
+      for (int q = 0; q < NPL; ++q) {
+        const bool ok = lane + 64 * q < n && !((kept >> q) & 1u);
+        key[q] = ok ? ordered_key(hv[q]) : 0u;
+        best = max(best, key[q]);
+      }
+      const uint32_t m = wave_max_u32(best);
+      int jk = -1;
+      if (m != 0u) {
+#pragma unroll
+        for (int q = 0; q < NPL; ++q) {
+          const unsigned long long b = __ballot(key[q] == m);
+          if (b) {
+            jk = 64 * q + __builtin_ctzll(b);
+            break;
+          }
+        }
+      }
+      const float v_k = jk >= 0 ? key_to_float(m) : -INFINITY;
+      const int jkm1 = readlane_i(my_j, k - 1);
+      const float v_km1 = h_of(jkm1);
+      float sk = 0.f, sn = 0.f;
+#pragma unroll
+      for (int q = 0; q < NPL; ++q) {
+        if (lane + 64 * q < n) {
+          const bool kq = (kept >> q) & 1u;
+          const float thr = kq ? v_k : v_km1;
+          if (thr != -INFINITY) {
+            const float rs = hw_rcp(sp[q]);
+            const float zz = (cl[q] - thr) * rs;
+            const float g = dload[q] * (expf(-0.5f * zz * zz) * 0.398942280401432678f) * rs;
+            dcl[q] = g;
+            dsp[q] = -g * zz;
+            if (kq) sk += g; else sn += g;
+          }
+        }
+      }
+      const float SK = wave_sum_dpp(sk), SN = wave_sum_dpp(sn);
+      if (jk >= 0 && lane == (jk & 63)) {
+#pragma unroll
+        for (int q = 0; q < NPL; ++q)
+          if (q == (jk >> 6)) dH[q] -= SK;
+      }
+      if (lane == (jkm1 & 63)) {
+#pragma unroll
+        for (int q = 0; q < NPL; ++q)
+          if (q == (jkm1 >> 6)) dH[q] -= SN;
+      }
+    }
+
+    float* out = p.dlogits + (long long)r * p.ldd;
+#pragma unroll
+    for (int q = 0; q < NPL; ++q) {
+      const int j = lane + 64 * q;
+      if (j < n) {
+        const float dc = dH[q] + dcl[q];
+        out[j] = dc;
+        dbacc[q] += dc;
+        if (p.noisy) out[n + j] = (dsp[q] + zn[q] * dH[q]) * hw_rcp(1.f + hw_exp(-rw[q]));
+      }
+    }
+    // Columns past the written ones are zero: products over the padded row
+    // width then add nothing.
+    for (int j = (p.noisy ? 2 * n : n) + lane; j < p.ldd; j += 64) out[j] = 0.f;
+  }
+
+  if (p.part_db) {
+#pragma unroll
+    for (int q = 0; q < NPL; ++q) {
+      const int j = lane + 64 * q;
+      if (j < n) red[wave * n + j] = dbacc[q];
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < n; j += NW * 64) {
+      float sacc = red[j];
+      for (int w2 = 1; w2 < NW; ++w2) sacc += red[w2 * n + j];
+      p.part_db[(long long)part * n + j] = sacc;
+    }
+  }
+}
+
 // out[j] = sum of part[p][j] over p.  64 columns per block; 16 part-lanes per
 // column each add every 16th partial in ascending order (coalesced rows,
 // many loads in flight), then lane sums are added in lane order: the same
@@ -397,6 +628,17 @@ hipError_t launch_topk_t(const TopkArgs& a, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int NPL>
+hipError_t launch_gate_bwd_t(const GateBwdArgs& a, int grid, hipStream_t s) {
+  // Fewer rows in flight than the forward (more live values per row); every
+  // choice divides the forward's rows-per-block.
+  constexpr int NW = NPL <= 4 ? 16 : NPL <= 16 ? 8 : 4;
+  const size_t shm = (size_t)NW * a.n * sizeof(float);
+  ProfScope ps("bwd_gate", s);
+  gate_bwd_kernel<NPL, NW><<<dim3(grid), dim3(NW * 64), shm, s>>>(a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
@@ -410,6 +652,18 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   if (npl <= 8) return launch_topk_t<8>(a, grid, s);
   if (npl <= 16) return launch_topk_t<16>(a, grid, s);
   return launch_topk_t<32>(a, grid, s);
+}
+
+hipError_t launch_gate_bwd(const GateBwdArgs& a, hipStream_t s) {
+  const int grid = (a.T + a.rows_per_block - 1) / a.rows_per_block;
+  if (grid <= 0) return hipSuccess;
+  const int npl = (a.n + 63) / 64;
+  if (npl <= 1) return launch_gate_bwd_t<1>(a, grid, s);
+  if (npl <= 2) return launch_gate_bwd_t<2>(a, grid, s);
+  if (npl <= 4) return launch_gate_bwd_t<4>(a, grid, s);
+  if (npl <= 8) return launch_gate_bwd_t<8>(a, grid, s);
+  if (npl <= 16) return launch_gate_bwd_t<16>(a, grid, s);
+  return launch_gate_bwd_t<32>(a, grid, s);
 }
 
 hipError_t launch_colsum(int nparts, ColsumVec v0, ColsumVec v1, ColsumVec v2, hipStream_t s) {

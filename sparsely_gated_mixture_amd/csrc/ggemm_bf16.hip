@@ -40,8 +40,7 @@
 
 #include "common.h"
 #include "launch.h"
-
-#pragma clang diagnostic ignored "-Winline-asm"
+#include "lds_dma.h"
 
 namespace moe {
 namespace {
@@ -51,42 +50,6 @@ constexpr int kBK = 64;       // K per pipeline step
 constexpr int kRowB = 128;    // bytes per LDS row (kBK bf16)
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-
-__device__ __attribute__((aligned(16))) const uint32_t kZeroChunk[4] = {0u, 0u, 0u, 0u};
-
-// 16-byte global -> LDS copy.  Lane i of the wave writes LDS bytes
-// [lds + 16 i, lds + 16 i + 16); `lds` must be wave-uniform.  The copy has no
-// register result; its completion is tracked with vmcnt (wait_vm).
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off" ::"v"(g),
-      "s"(lds)
-      : "memory");
-}
-
-// Wait until at most N vector memory operations of this wave are in flight.
-// Loads complete in order, so this covers every copy issued more than N
-// loads ago.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// wait_vm<n>() for a run-time n in [0, MAX] (a wave-uniform value).
-template <int MAX>
-__device__ __forceinline__ void wait_vm_upto(int n) {
-  if constexpr (MAX > 0) {
-    if (n >= MAX) {
-      wait_vm<MAX>();
-      return;
-    }
-    wait_vm_upto<MAX - 1>(n);
-  } else {
-    wait_vm<0>();
-  }
-}
 
 __device__ __forceinline__ int swz(int r, int c) { return (c ^ ((r >> 1) & 7)) << 4; }
 

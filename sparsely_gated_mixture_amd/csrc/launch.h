@@ -86,6 +86,50 @@ hipError_t launch_pack_fp8(int n_experts, int N, int K, int src_bf16, const void
 int device_cus();
 hipError_t launch_gemm_bf16(const GemmBf16Args& a, int epi, hipStream_t s);
 
+// ---------------------------------------------------------------------------
+// bf16 MFMA GEMMs of the expert backward: C[c][m] = sum_k A[k][m] * B(k, c).
+// A is K-major (row k holds M contiguous columns; rows k >= k_split come from
+// A2 at row k - k_split), offset by e * strideA for expert e.
+// BWD_ROWS: c runs over the merged rows of the dispatch's 128-row tiles
+//   (tile_expert / tile_row0 / offsets / tile_count); B[c][k] row-major with
+//   K contiguous (ldb); K = p.K (a multiple of 64).
+// BWD_WGRAD: one [N][M] output per expert e < n_experts; k runs over the
+//   expert's merged rows offsets[e] .. offsets[e+1]; B[k][c] K-major.
+// Epilogues: BEPI_F32 -> C (+ e*strideC; WGRAD rows c >= c_split go to C2
+//   at row c - c_split); BEPI_RELU_MASK -> Cb = bf16(D where aux_h > 0);
+//   BEPI_SWIGLU -> Cb[c][m] = bf16(da), Cb[c][c_split + m] = bf16(db) from
+//   aux_a / aux_b (fp32 pre-activations, row stride ldaux).
+// M and N multiples of 8; every pointer 16-byte aligned.
+// ---------------------------------------------------------------------------
+enum BwdMode { BWD_ROWS = 0, BWD_WGRAD = 1 };
+enum BwdEpi { BEPI_F32 = 0, BEPI_RELU_MASK = 1, BEPI_SWIGLU = 2 };
+struct GemmBwdArgs {
+  const uint16_t* A;
+  const uint16_t* A2;
+  long long lda, strideA;
+  int k_split;
+  const uint16_t* B;
+  long long ldb;
+  int M, N, K;
+  float* C;
+  float* C2;
+  uint16_t* Cb;
+  long long ldc, strideC;
+  int c_split;
+  const uint16_t* aux_h;
+  const float* aux_a;
+  const float* aux_b;
+  long long ldaux;
+  const int32_t* tile_expert;
+  const int32_t* tile_row0;
+  const int32_t* offsets;
+  const int32_t* tile_count;
+  int max_tiles;
+  int n_experts;
+};
+hipError_t launch_gemm_bwd(const GemmBwdArgs& a, int mode, int epi, const char* name,
+                           hipStream_t s);
+
 // Tile map of a grouped GEMM: for every expert e with rows in
 // [offsets[e], offsets[e+1]), ceil(rows/bm) M-tiles in expert order.
 hipError_t launch_tilemap(const int32_t* offsets, int n, int bm, int32_t* tile_expert,
@@ -132,6 +176,30 @@ struct TopkArgs {
 // registers).  The host's rows-per-block is a multiple of this.
 inline int topk_waves(int n) { return (n + 63) / 64 <= 8 ? 16 : 8; }
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+// Backward of the flat gate (one wavefront per token row; rows_per_block a
+// multiple of topk_waves(n)).  Reads the forward's logits (clean without the
+// bias | raw, row stride ldl), bias, noise, topk_idx / topk_w, the combine's
+// dG [T, k], dimp / dload [n] and coef = {c_z, c_ent}; writes dlogits [T,
+// ldd] (dL/d clean | dL/d raw) and, if part_db, per-block column sums of the
+// clean part [nblocks, n].
+struct GateBwdArgs {
+  int T, n, k, switch_mode, sigmoid_mode, noisy;
+  const float* logits;
+  long long ldl;
+  const float* bias;
+  const float* noise;
+  const int32_t* topk_idx;
+  const float* topk_w;
+  const float* dG;
+  const float* dimp;
+  const float* dload;
+  const float* coef;
+  float* dlogits;
+  long long ldd;
+  float* part_db;
+  int rows_per_block;
+};
+hipError_t launch_gate_bwd(const GateBwdArgs& a, hipStream_t s);
 // out[j] = sum over parts p < nparts of part[p*n + j] (double sum, fixed
 // order), for up to three (part, n, out) vectors in one launch; a vector with
 // a null part is skipped.
@@ -207,5 +275,48 @@ hipError_t launch_combine(const float* y_perm, const int32_t* slot_pos, const fl
 hipError_t launch_aux(const float* importance, const float* load, const int32_t* counts_pre,
                       const float* gate_stats, int T, int k, int n, float w_imp, float w_load,
                       float alpha, float w_z, float w_ent, float* losses, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Backward (backward.hip).
+// ---------------------------------------------------------------------------
+// Per token, per kept slot: dG[t,s] = <dy_t, y_perm[row]>, dout[row] =
+// bf16(topk_w[t,s] * dy_t); dropped slots get dG = 0.
+hipError_t launch_combine_bwd(const float* dy, const float* y_perm, const int32_t* slot_pos,
+                              const float* topk_w, int T, int k, int d, float* dG,
+                              uint16_t* dout, hipStream_t s);
+// dimp = dl0 w_imp dCV^2(importance) + dl2 alpha n f / T, dload = dl1 w_load
+// dCV^2(load) (skipped when load is null), coef = {dl3 w_z / T, dl4 w_ent / T};
+// dlosses is a device vector of 5.
+hipError_t launch_loss_grad(const float* importance, const float* load,
+                            const int32_t* counts_pre, const float* dlosses, int T, int k, int n,
+                            float w_imp, float w_load, float alpha, float w_z, float w_ent,
+                            float* dimp, float* dload, float* coef, hipStream_t s);
+// Gate weight gradients: rows m < M of dlogits^T x, split over tokens into
+// `splits` partial products of tokens_per_split tokens each (partial holds
+// splits * M * d floats), then summed in split order into dw_gate (rows m <
+// n) and dw_noise (rows m >= n).  d % 4 == 0, ldd % 4 == 0.
+struct GateWgradArgs {
+  const float* x;
+  const float* dlogits;
+  long long ldd;
+  int T, d, M, n, splits, tokens_per_split;
+  float* partial;
+};
+int gate_wgrad_splits(int T, int d, int M);
+hipError_t launch_gate_wgrad(const GateWgradArgs& a, float* dw_gate, float* dw_noise,
+                             hipStream_t s);
+// wt [d, ldk] = [w_gate; w_noise (if given)]^T, zero past the stacked rows.
+hipError_t launch_transpose_gate(const float* w_gate, const float* w_noise, int n, int d,
+                                 int ldk, float* wt, hipStream_t s);
+// out[e][c] = sum over rows offsets[e] .. offsets[e+1]-1 of src[row][c] (bf16).
+hipError_t launch_seg_colsum(const uint16_t* src, long long ld, const int32_t* offsets,
+                             int n_seg, int N, float* out, hipStream_t s);
+// dx[t] = dx_gate[t] (+ dx_shared[t]) + sum over kept slots of du_perm[row].
+hipError_t launch_dx_gather(const float* dx_gate, const float* dx_shared, const float* du_perm,
+                            const int32_t* slot_pos, int T, int k, int d, float* dx,
+                            hipStream_t s);
+// hid[i] = bf16(silu(a[i]) * b[i]) for i < elems (a multiple of 4).
+hipError_t launch_swiglu_hidden(const float* a, const float* b, long long elems, uint16_t* hid,
+                                hipStream_t s);
 
 }  // namespace moe

@@ -59,6 +59,7 @@ class MoEConfig:
     k_groups: int = 0          # hierarchical: k1 (k = k1 * k2)
     logit_bias: str = "none"   # none | normal0.5 | normal1 | zipf1.1
     zero_expert_bias: bool = False
+    expert_bias_std: float = 0.0  # > 0: ReLU expert biases b1, b2 ~ N(0, std^2)
     seed: int = 1000
 
     @property
@@ -177,10 +178,22 @@ def make_inputs(cfg: MoEConfig, device="cpu", T: int | None = None):
     if cfg.zero_expert_bias:
         out["b1"] = torch.zeros((n, h), dtype=torch.float32, device=device)
         out["b2"] = torch.zeros((n, d), dtype=torch.float32, device=device)
+    elif cfg.expert_bias_std > 0:
+        out["b1"] = _normal((n, h), cfg.expert_bias_std, device, _derived(s, 16))
+        out["b2"] = _normal((n, d), cfg.expert_bias_std, device, _derived(s, 17))
     else:
         out["b1"] = None
         out["b2"] = None
     return out
+
+
+def make_grad_inputs(cfg: MoEConfig, device="cpu", T: int | None = None):
+    """Upstream gradients for the backward pass: dy ~ N(0, 1) [T, d] and
+    dlosses ~ N(0, 1) [5] (one per auxiliary loss)."""
+    T = cfg.T if T is None else T
+    dy = _normal((T, cfg.d_model), 1.0, device, _derived(cfg.seed, 20))
+    dlosses = _normal((5,), 1.0, device, _derived(cfg.seed, 21))
+    return dy, dlosses
 
 
 def to_numpy64(t):
