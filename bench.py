@@ -19,6 +19,12 @@ HBM.  Prints one JSON line:
                (its first tokens, run repeatedly for about --cpu-seconds) on
                this host's cores;
   check        the GPU output on that sample against the oracle.
+
+    python bench.py --backward [--steps K] [--warmup W] [--workload lm_layer]
+
+times moe_backward instead (one step: the forward's routing and activations
+recomputed, then every gradient) and prints one JSON line of the same shape,
+its cpu_baseline the oracle's backward on a bounded token sample.
 """
 from __future__ import annotations
 
@@ -103,6 +109,53 @@ def kernel_work(name, cfg, rows, nonempty, T):
     if name in ("dispatch_finalize", "dispatch_offsets", "ffn_tilemap", "aux_loss"):
         return (n * 12, 0.0, "i32")
     return (0.0, 0.0, "")
+
+
+def bwd_kernel_work(name, cfg, rows, nonempty, T):
+    """(algorithmic bytes, flops, dtype) of one launch of a backward kernel."""
+    d, h, n, k = cfg.d_model, cfg.d_hidden, cfg.n_experts, cfg.k
+    sw = cfg.act == 1
+    hw = 2 * h if sw else h
+    M = 2 * n if cfg.noisy else n
+    hs = cfg.d_hidden_shared
+    hws = 2 * hs if sw else hs
+    if name == "bwd_ggemm_preact":   # x W1^T and x W3^T kept in fp32 (SwiGLU)
+        return (nonempty * h * d * 2 + rows * d * 2 + rows * h * 4, 2.0 * rows * h * d, "bf16")
+    if name == "bwd_shared_preact":
+        return (hs * d * 2 + T * d * 2 + T * hs * 4, 2.0 * T * hs * d, "bf16")
+    if name == "bwd_swiglu_hidden":
+        return (0.0, 0.0, "")  # rows differ between the routed and shared launches
+    if name == "bwd_ggemm_dhidden":
+        aux = rows * h * (8 if sw else 2)
+        return (nonempty * d * h * 2 + rows * d * 2 + aux + rows * hw * 2, 2.0 * rows * d * h,
+                "bf16")
+    if name == "bwd_ggemm_dinput":
+        return (nonempty * hw * d * 2 + rows * hw * 2 + rows * d * 4, 2.0 * rows * hw * d, "bf16")
+    if name == "bwd_ggemm_dw2":
+        return (rows * h * 2 + rows * d * 2 + n * d * h * 4, 2.0 * rows * d * h, "bf16")
+    if name == "bwd_ggemm_dw1":
+        return (rows * d * 2 + rows * hw * 2 + n * hw * d * 4, 2.0 * rows * hw * d, "bf16")
+    if name == "bwd_shared_dhidden":
+        aux = T * hs * (8 if sw else 2)
+        return (d * hs * 2 + T * d * 2 + aux + T * hws * 2, 2.0 * T * d * hs, "bf16")
+    if name == "bwd_shared_dinput":
+        return (hws * d * 2 + T * hws * 2 + T * d * 4, 2.0 * T * hws * d, "bf16")
+    if name == "bwd_shared_dw2":
+        return (T * hs * 2 + T * d * 2 + d * hs * 4, 2.0 * T * d * hs, "bf16")
+    if name == "bwd_shared_dw1":
+        return (T * d * 2 + T * hws * 2 + hws * d * 4, 2.0 * T * hws * d, "bf16")
+    if name == "bwd_gate_wgrad":
+        return (T * d * 4 + T * M * 4 + M * d * 4, 2.0 * T * M * d, "f32")
+    if name == "bwd_gate_dx":
+        return (T * M * 4 + M * d * 4 + T * d * 4, 2.0 * T * M * d, "f32")
+    if name == "bwd_combine":
+        return (T * d * 4 + rows * d * 4 + rows * d * 2 + T * k * 12, 0.0, "f32")
+    if name == "bwd_gate":
+        return (T * M * 4 + (T * n * 4 if cfg.noisy else 0) + T * k * 12 + T * M * 4, 0.0,
+                "f32")
+    if name == "bwd_dx_gather":
+        return (T * d * 4 + rows * d * 4 + (T * d * 4 if hs else 0) + T * d * 4, 0.0, "f32")
+    return kernel_work(name, cfg, rows, nonempty, T)
 
 
 def gate_text(cfg):
@@ -191,6 +244,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches only (default: also replay a HIP graph)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time moe_backward (forward recompute + every gradient)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (256 MiB read, "
                          "256 MiB written, 5 launches) for scaling HBM byte counters")
@@ -208,6 +263,9 @@ def main():
 
     cfg = PRESETS[args.workload]
     torch.cuda.set_device(0)
+    if args.backward:
+        bench_backward(args, cfg)
+        return
     log(f"[bench] workload {cfg.name}: T={cfg.T} d={cfg.d_model} h={cfg.d_hidden} "
         f"n={cfg.n_experts} k={cfg.k}")
     inp = make_inputs(cfg, device="cuda")
@@ -346,6 +404,138 @@ def main():
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
+
+
+def bench_backward(args, cfg):
+    """moe_backward timed like the forward (eager launches; per-kernel events
+    in a second pass), one JSON line."""
+    import sparsely_gated_mixture_amd as moe
+    from sparsely_gated_mixture_amd.workloads import make_grad_inputs, make_inputs
+    log(f"[bench] backward, workload {cfg.name}: T={cfg.T} d={cfg.d_model} h={cfg.d_hidden} "
+        f"n={cfg.n_experts} k={cfg.k}")
+    inp = make_inputs(cfg, device="cuda")
+    dy, dl = make_grad_inputs(cfg, device="cuda")
+    torch.cuda.synchronize()
+    layer = moe.MoELayer(cfg, inp)
+    T, n, k = cfg.T, cfg.n_experts, cfg.k
+
+    def step():
+        return layer.backward(inp["x"], dy, dl, inp.get("noise"))
+
+    for _ in range(args.warmup):
+        grads = step()
+    torch.cuda.synchronize()
+    # gradient buffers allocated once, reused by the timed steps
+    g = moe.make_grads(**grads)
+
+    def eager_step():
+        moe.moe_backward(layer.c, layer.w, inp["x"], inp.get("noise"), dy, dl, g, layer.ws_bwd)
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    moe.moe_profile_enable(True)
+    for _ in range(args.steps):
+        eager_step()
+    torch.cuda.synchronize()
+    moe.moe_profile_enable(False)
+    moe.moe_profile_collect()
+    elapsed = timed(eager_step)
+    log(f"[bench] backward eager: {elapsed / args.steps * 1e6:.1f} us/step, "
+        f"{T * args.steps / elapsed / 1e6:.2f} M tokens/s")
+    moe.moe_profile_enable(True)
+    prof_elapsed = timed(eager_step)
+    moe.moe_profile_enable(False)
+    nk = moe.moe_profile_collect()
+    stats = [moe.moe_profile_entry(i) for i in range(nk)]
+
+    i32 = dict(dtype=torch.int32, device="cuda")
+    diag = {"topk_idx": torch.empty((T, k), **i32), "counts": torch.empty(n, **i32)}
+    layer.forward(inp["x"], inp.get("noise"), diag=diag)
+    torch.cuda.synchronize()
+    counts = diag["counts"].cpu().numpy()
+    rows = int(counts.sum())
+    nonempty = int((counts > 0).sum())
+    kernels, dominant = {}, None
+    for name, total_ms, launches in stats:
+        avg_s = total_ms / launches / 1e3
+        b, f, dt = bwd_kernel_work(name, cfg, rows, nonempty, T)
+        entry = {"avg_us": avg_s * 1e6, "launches_per_step": launches / args.steps}
+        if b:
+            rl, gbs, tfs = roofline_entry(b, f, dt, avg_s)
+            entry.update({"algo_bytes": b, "GB_s": gbs, "hbm_frac": gbs / PEAK_HBM_GBS})
+            if f:
+                entry.update({"flops": f, "TFLOP_s": tfs, "mfma_frac": tfs / PEAK_TFLOPS[dt]})
+            entry["roofline"] = rl
+        kernels[name] = entry
+        if b and (dominant is None or total_ms > dominant[1]):
+            dominant = (name, total_ms)
+    for name, e in sorted(kernels.items(),
+                          key=lambda kv: -kv[1]["avg_us"] * kv[1]["launches_per_step"]):
+        log(f"[bench]   {name:24s} {e['avg_us']:9.1f} us x{e['launches_per_step']:.0f}"
+            + (f"  {e['GB_s']:8.1f} GB/s" if "GB_s" in e else "")
+            + (f"  {e['TFLOP_s']:7.1f} TFLOP/s" if "TFLOP_s" in e else ""))
+    dname = dominant[0]
+    roofline = dict(kernels[dname]["roofline"])
+    roofline.update(kernel=dname, traffic=TRAFFIC_BYTES.get((cfg.name + ":bwd", dname)),
+                    algo_bytes_per_launch=kernels[dname]["algo_bytes"],
+                    avg_us=kernels[dname]["avg_us"])
+    result = {
+        "metric": "MoE-layer backward (forward recompute + all gradients) tokens/sec at 1 GPU",
+        "value": T * args.steps / elapsed, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name + " backward", "T": T, "d_model": cfg.d_model,
+                   "d_hidden": cfg.d_hidden, "n_experts": n, "k": k, "gate": gate_text(cfg),
+                   "gradients": "fp32; expert products bf16 MFMA with fp32 accumulation",
+                   "rows": rows, "nonempty_experts": nonempty, "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "kernels": kernels,
+        "timing": {"mode": "eager launches",
+                   "eager_with_events_us_per_step": prof_elapsed / args.steps * 1e6},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_backward(cfg, inp, dy, dl, args.cpu_sample_tokens,
+                                                       args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_backward(cfg, inp, dy, dl, sample_tokens, seconds):
+    """The oracle's backward (its forward recompute included) on the first
+    tokens of the batch, repeated for about `seconds`."""
+    import oracle
+    from sparsely_gated_mixture_amd.workloads import to_numpy64
+    S = min(sample_tokens, cfg.T)
+    h = {k: to_numpy64(v) for k, v in inp.items() if v is not None}
+    x = h["x"][:S]
+    noise = h["noise"][:S] if "noise" in h else None
+    dyh = to_numpy64(dy)[:S]
+    dlh = to_numpy64(dl)
+    oracle.lib()
+    reps, dt = 0, 0.0
+    while reps == 0 or dt < seconds:
+        t0 = time.perf_counter()
+        oracle.backward(x, h["w_gate"], cfg.k, h["w1"], h["w2"], dyh, dlh,
+                        b_gate=h.get("b_gate"), w_noise=h.get("w_noise"), noise=noise,
+                        b1=h.get("b1"), w3=h.get("w3"), b2=h.get("b2"), mode=cfg.gate,
+                        act=cfg.act, bf16=True, capacity_factor=cfg.capacity_factor,
+                        w_importance=cfg.w_importance, w_load=cfg.w_load,
+                        alpha=cfg.alpha_switch, w_z=cfg.w_z, w_entropy=cfg.w_entropy,
+                        ws1=h.get("ws1"), ws3=h.get("ws3"), ws2=h.get("ws2"))
+        dt += time.perf_counter() - t0
+        reps += 1
+    return {"value": S * reps / dt, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"first {S} of {cfg.T} tokens of the {cfg.name} workload (forward "
+                      f"recompute and every gradient in float64), {reps} runs in {dt:.2f} s"}
 
 
 if __name__ == "__main__":

@@ -774,6 +774,7 @@ moe_status bwd_hidden(const moe_config& c, GemmBf16Args g, int h, uint16_t* hidd
   if (c.act == MOE_ACT_SWIGLU) {
     const void* w3 = g.B3;
     g.B3 = nullptr;
+    g.prof_name = g.shared ? "bwd_shared_preact" : "bwd_ggemm_preact";
     g.C = a_pre;
     HIP_TRY(launch_gemm_bf16(g, EPI_IDENT_F32, s));
     g.B1 = w3;
@@ -1358,6 +1359,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const floa
     gx.M = T;
     gx.mtiles = (T + p.gemm_bm - 1) / p.gemm_bm;
     gx.max_mtiles = gx.mtiles;
+    gx.prof_name = "bwd_gate_dx";
     HIP_TRY(launch_gemm_f32(gx, p.gemm_bm, s));
   }
   FfnBwd fb{};

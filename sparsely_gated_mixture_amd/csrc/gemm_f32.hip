@@ -196,7 +196,7 @@ hipError_t launch_gemm_f32(const GemmF32Args& a, int bm, hipStream_t s) {
   const long long max_total = (long long)a.max_mtiles * nN;
   if (max_total <= 0) return hipSuccess;
   const long long grid = (max_total + kXcds - 1) / kXcds * kXcds;
-  ProfScope ps(bm == 128 ? "gemm_f32_bm128" : "gemm_f32_bm64", s);
+  ProfScope ps(a.prof_name ? a.prof_name : bm == 128 ? "gemm_f32_bm128" : "gemm_f32_bm64", s);
   if (bm == 128)
     gemm_f32_kernel<128, 2, 4><<<dim3((unsigned)grid), dim3(512), 0, s>>>(a);
   else

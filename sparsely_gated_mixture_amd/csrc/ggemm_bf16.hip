@@ -422,9 +422,10 @@ hipError_t launch_t(const GemmBf16Args& a, hipStream_t s) {
       {"ggemm_bf16_relu", "ggemm_bf16_swiglu", "ggemm_bf16_out"},
       {"shared_bf16_relu", "shared_bf16_swiglu", "shared_bf16_out"},
       {"ggemm_fp8_relu", "ggemm_fp8_swiglu", "ggemm_fp8_out"}};
-  ProfScope ps(kNames[FP8 ? 2 : a.shared ? 1 : 0][EPI == EPI_RELU_BF16     ? 0
-                                                  : EPI == EPI_SWIGLU_BF16 ? 1
-                                                                           : 2],
+  ProfScope ps(a.prof_name ? a.prof_name
+                           : kNames[FP8 ? 2 : a.shared ? 1 : 0][EPI == EPI_RELU_BF16     ? 0
+                                                                : EPI == EPI_SWIGLU_BF16 ? 1
+                                                                                         : 2],
                s);
   ggemm_bf16_kernel<BN, EPI, WGM, HAS_BIAS, FP8>
       <<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(a);

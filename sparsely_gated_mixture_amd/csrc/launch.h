@@ -46,6 +46,7 @@ struct GemmF32Args {
   const int32_t* offsets;
   const int32_t* tile_count;  // device total of M-tiles (grouped mode)
   int max_mtiles;             // upper bound of M-tiles (grid sizing)
+  const char* prof_name;      // profiler name of this launch (null: by tile size)
 };
 // bm: 64 or 128 (BN = bm).
 hipError_t launch_gemm_f32(const GemmF32Args& a, int bm, hipStream_t s);
@@ -72,6 +73,7 @@ struct GemmBf16Args {
   int num_cus;           // compute units of the device (persistent grid size)
   int shared;            // 1: the shared expert (only the profiler name differs)
   int fp8;               // 1: B1/B3 are packed E4M3 weights with per-row scales
+  const char* prof_name; // profiler name of this launch (null: by epilogue and kind)
 };
 constexpr int kBf16BM = 128;
 constexpr int kMaxTilesPerWG = 512;  // tiles one persistent workgroup can hold
