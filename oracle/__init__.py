@@ -513,7 +513,11 @@ def _sigmoid(z):
     return 1.0 / (1.0 + np.exp(-z))
 
 
-def expert_ffn_backward(u, w1, w2, gout, b1=None, w3=None, b2=None, act=ACT_RELU, bf16=False):
+RELU_NEAR_ZERO = 2e-5  # |pre| at or below this fraction of sum |u_c w_jc| + |b_j|: either mask
+
+
+def expert_ffn_backward(u, w1, w2, gout, b1=None, w3=None, b2=None, act=ACT_RELU, bf16=False,
+                        slack=False):
     """Backward of one expert on its merged rows u [rows, d] (the forward of
     ``expert_ffn``), given gout = dL/d(expert output) [rows, d].  Returns
     (du, dw1, db1, dw3, dw2, db2); the absent parts are None.
@@ -525,7 +529,13 @@ def expert_ffn_backward(u, w1, w2, gout, b1=None, w3=None, b2=None, act=ACT_RELU
       da = dhid * b * silu'(a), silu'(a) = s (1 + a (1 - s)) with s = Sigmoid(a),
       db = dhid * silu(a), dW1 = da^T u, dW3 = db^T u, du = da W1 + db W3.
     With bf16 the forward's rounded u and hid are the values used (the
-    rounding itself is taken as the identity)."""
+    rounding itself is taken as the identity).
+    ReLU'(0) is not defined, and a pre-activation within rounding of zero can
+    take either mask value in an implementation that computes it in lower
+    precision.  With slack=True a seventh value is returned: for ReLU, the
+    largest change either choice can make, (s_du, s_dw1, s_db1), for the
+    pre-activations with |pre| <= RELU_NEAR_ZERO * (sum_c |u_c w_jc| + |b_j|);
+    None for SwiGLU (no discrete decision)."""
     u, w1, w2, gout, b1, w3, b2 = map(_d, (u, w1, w2, gout, b1, w3, b2))
     uq = bf16_round(u) if bf16 else u
     if act == ACT_SWIGLU:
@@ -546,7 +556,12 @@ def expert_ffn_backward(u, w1, w2, gout, b1=None, w3=None, b2=None, act=ACT_RELU
         return da @ w1 + dbv @ w3, da.T @ uq, None, dbv.T @ uq, dw2, db2
     dpre = np.where(pre > 0.0, dhid, 0.0)
     db1 = dpre.sum(axis=0) if b1 is not None else None
-    return dpre @ w1, dpre.T @ uq, db1, None, dw2, db2
+    out = (dpre @ w1, dpre.T @ uq, db1, None, dw2, db2)
+    if not slack:
+        return out
+    mag = np.abs(uq) @ np.abs(w1).T + (np.abs(b1) if b1 is not None else 0.0)
+    amb = np.where(np.abs(pre) <= RELU_NEAR_ZERO * mag, np.abs(dhid), 0.0)
+    return out + ((amb @ np.abs(w1), amb.T @ np.abs(uq), amb.sum(axis=0)),)
 
 
 def backward(x, w_gate, k, w1, w2, dy, dlosses, *, b_gate=None, w_noise=None, noise=None,
@@ -557,7 +572,10 @@ def backward(x, w_gate, k, w1, w2, dy, dlosses, *, b_gate=None, w_noise=None, no
     the flat layer of ``forward`` (same arguments), the routing held fixed.
     Returns a dict with dx, dw_gate, db_gate (None for the sigmoid gate,
     whose bias only moves the selection), dw_noise, dw1, db1, dw3, dw2, db2,
-    dws1, dws3, dws2 (absent parts None) and the forward's results ("fwd").
+    dws1, dws3, dws2 (absent parts None), the forward's results ("fwd") and
+    "slack": for ReLU experts, the largest change that either value of the
+    mask at pre-activations within rounding of zero can make to dx, dw1, db1
+    and dws1 (see expert_ffn_backward); zeros elsewhere.
 
     Stages, in reverse order of the forward ([PAPER] FAQ: the kept gate
     values are differentiable because the selection comes before the
@@ -612,6 +630,10 @@ def backward(x, w_gate, k, w1, w2, dy, dlosses, *, b_gate=None, w_noise=None, no
     db1 = np.zeros((n, h)) if b1 is not None else None
     db2 = np.zeros((n, d)) if b2 is not None else None
     du_perm = np.zeros((rows, d))
+    relu = act != ACT_SWIGLU
+    slack_du = np.zeros((rows, d))
+    slack = dict(dx=np.zeros((T, d)), dw1=np.zeros_like(w1),
+                 db1=np.zeros((n, h)) if b1 is not None else None, dws1=None)
     for e in range(n):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if hi == lo:
@@ -619,7 +641,11 @@ def backward(x, w_gate, k, w1, w2, dy, dlosses, *, b_gate=None, w_noise=None, no
         res = expert_ffn_backward(x[perm[lo:hi]], w1[e], w2[e], gout[lo:hi],
                                   None if b1 is None else b1[e],
                                   None if w3 is None else w3[e],
-                                  None if b2 is None else b2[e], act, bf16)
+                                  None if b2 is None else b2[e], act, bf16, slack=relu)
+        if relu:
+            slack_du[lo:hi], slack["dw1"][e] = res[6][0], res[6][1]
+            if b1 is not None:
+                slack["db1"][e] = res[6][2]
         du_perm[lo:hi], dw1[e] = res[0], res[1]
         if db1 is not None:
             db1[e] = res[2]
@@ -634,11 +660,15 @@ def backward(x, w_gate, k, w1, w2, dy, dlosses, *, b_gate=None, w_noise=None, no
             r = slot_pos[t, s]
             if r >= 0:
                 dx[t] += du_perm[r]
+                slack["dx"][t] += slack_du[r]
     dws1 = dws3 = dws2 = None
     if ws1 is not None:
-        res = expert_ffn_backward(x, ws1, ws2, dy, None, ws3, None, act, bf16)
+        res = expert_ffn_backward(x, ws1, ws2, dy, None, ws3, None, act, bf16, slack=relu)
         dx += res[0]
         dws1, dws3, dws2 = res[1], res[3], res[4]
+        if relu:
+            slack["dx"] += res[6][0]
+            slack["dws1"] = res[6][1]
 
     # 3. losses
     f = disp["counts_pre"] / float(T * k)
@@ -677,4 +707,4 @@ def backward(x, w_gate, k, w1, w2, dy, dlosses, *, b_gate=None, w_noise=None, no
         dx += draw @ _d(w_noise)
     return dict(dx=dx, dw_gate=dw_gate, db_gate=db_gate, dw_noise=dw_noise, dw1=dw1, db1=db1,
                 dw3=dw3, dw2=dw2, db2=db2, dws1=dws1, dws3=dws3, dws2=dws2, dG=dG, dclean=dclean,
-                draw=draw, fwd=fwd)
+                draw=draw, fwd=fwd, slack=slack)

@@ -9,7 +9,12 @@ activations).  The discrete decisions must be the oracle's: the routing is
 compared exactly, and for a noisy gate, whose load estimator sends part of a
 token's gradient to the logit of the rank-k expert (the largest one not
 kept), the cases use inputs where the k+1-th and k+2-th largest gate values
-are not within 1e-4 of each other (checked).
+are not within 1e-4 of each other (checked).  ReLU'(0) is undefined: where
+a pre-activation lies within rounding of zero (the oracle flags |pre| <= 2e-5
+of the sum of its terms' magnitudes), the GPU's fp32 mask may take either
+value; an entry that such a pre-activation feeds may differ from the
+oracle's by at most the oracle's bound on that choice ("slack") plus the bar,
+and every other entry meets the bar.
 """
 import numpy as np
 import pytest
@@ -18,9 +23,9 @@ import torch
 import oracle
 from _support import TOL_BF16, log, max_abs_norm
 from sparsely_gated_mixture_amd import MoELayer
-from sparsely_gated_mixture_amd.workloads import (ACT_RELU, ACT_SWIGLU, GATE_SIGMOID_BIAS,
-                                                  GATE_SWITCH_TOP1, MoEConfig, make_grad_inputs,
-                                                  make_inputs, to_numpy64)
+from sparsely_gated_mixture_amd.workloads import (ACT_SWIGLU, GATE_SIGMOID_BIAS,
+                                                  GATE_SWITCH_TOP1, PRESETS, MoEConfig,
+                                                  make_grad_inputs, make_inputs, to_numpy64)
 
 pytestmark = pytest.mark.gpu
 
@@ -84,10 +89,10 @@ def _run(cfg, T=None):
     return inp, dy, dl, layer, {k: v.cpu().double().numpy() for k, v in g.items()}
 
 
-def _compare(cfg, inp, dy, dl, got):
+def _compare(cfg, inp, dy, dl, got, check_rank_k=True):
     h = {k: to_numpy64(v) for k, v in inp.items() if v is not None}
     ref = _oracle_backward(cfg, h, to_numpy64(dy), to_numpy64(dl))
-    if h.get("w_noise") is not None:
+    if check_rank_k and h.get("w_noise") is not None:
         assert _rank_k_unambiguous(ref["fwd"]["gate"].H, cfg.k), \
             "the case's inputs have a near-tie at rank k: pick another seed"
     names = ["dx"] + [g for g, w in GRAD_OF.items() if w in h]
@@ -98,9 +103,20 @@ def _compare(cfg, inp, dy, dl, got):
         b = ref[name]
         assert a.shape == b.shape, name
         assert np.isfinite(a).all(), name
-        err = max_abs_norm(a, b)
-        log(f"  {name}: max-abs-normalised error {err:.2e}")
+        sl = ref["slack"].get(name)
+        if sl is None or not sl.any():
+            err = max_abs_norm(a, b)
+            log(f"  {name}: max-abs-normalised error {err:.2e}")
+            assert err <= TOL_BF16, (name, err)
+            continue
+        scale = np.max(np.abs(b))
+        free = sl == 0
+        err = float(np.max(np.abs(a - b)[free])) / scale if free.any() else 0.0
+        log(f"  {name}: max-abs-normalised error {err:.2e} ({(~free).sum()} entries fed by "
+            f"a ReLU mask at zero)")
         assert err <= TOL_BF16, (name, err)
+        over = np.abs(a - b) > sl + TOL_BF16 * scale
+        assert not over.any(), (name, int(over.sum()))
     return ref
 
 
@@ -153,3 +169,20 @@ def test_backward_upstream_losses_only():
     for name in ("dw1", "db1", "dw2", "db2"):
         assert not got[name].any(), name
     _compare(cfg, inp, dy, dl, got)
+
+
+@pytest.mark.parametrize("name", ["lm_layer", "switch_cf"])
+def test_backward_full_size(name):
+    """The whole workload at its full size, every gradient against the
+    oracle's.  These batches hold a few tokens whose k+1-th and k+2-th gate
+    values lie within 1e-4 of each other; the bar holds with them (their
+    share of any gradient entry is small), so that check is not applied."""
+    cfg = PRESETS[name]
+    log(f"[backward] full size {name}: T={cfg.T} d={cfg.d_model} h={cfg.d_hidden} "
+        f"n={cfg.n_experts} k={cfg.k}")
+    inp, dy, dl, layer, got = _run(cfg)
+    idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+    layer.forward(inp["x"], inp.get("noise"), diag=dict(topk_idx=idx))
+    torch.cuda.synchronize()
+    ref = _compare(cfg, inp, dy, dl, got, check_rank_k=False)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref["fwd"]["gate"].topk_idx)
