@@ -87,6 +87,9 @@ def kernel_work(name, cfg, rows, nonempty, T):
         return (2 * hs * d * 2 + T * d * 2 + T * hs * 2, 4.0 * T * hs * d, "bf16")
     if name == "shared_bf16_out":
         return (d * hs * 2 + T * hs * 2 + T * d * 4, 2.0 * T * d * hs, "bf16")
+    if name == "gate_gemm_bf16x6":
+        # fp32 operands split into three bf16 parts, six bf16 products per term
+        return (T * d * 4 + ncols * d * 4 + T * ncols * 4, 6 * 2.0 * T * ncols * d, "bf16")
     if name.startswith("gemm_f32"):
         return (T * d * 4 + ncols * d * 4 + T * ncols * 4, 2.0 * T * ncols * d, "f32")
     if name == "gate_topk":

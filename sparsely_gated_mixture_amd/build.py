@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["gemm_f32.hip", "gate.hip", "dispatch.hip", "ggemm_bf16.hip", "combine.hip",
+HIP_SOURCES = ["gemm_f32.hip", "gemm_gate.hip", "gate.hip", "dispatch.hip", "ggemm_bf16.hip", "combine.hip",
                "fp8.hip", "backward.hip", "ggemm_bwd.hip"]
 HOST_SOURCES = ["api.cpp", "profile.cpp"]
 

@@ -337,7 +337,7 @@ moe_status run_gate(const moe_config& c, const Plan& p, const float* x, const fl
     g.M = c.T;
     g.mtiles = (c.T + p.gemm_bm - 1) / p.gemm_bm;
     g.max_mtiles = g.mtiles;
-    HIP_TRY(launch_gemm_f32(g, p.gemm_bm, s));
+    HIP_TRY(launch_gemm_gate(g, p.gemm_bm, s));
   }
   TopkArgs t{};
   t.rows = c.T;
@@ -388,7 +388,7 @@ moe_status run_gate_hier(const moe_config& c, const Plan& p, const float* x, con
     g.M = c.T;
     g.mtiles = (c.T + p.gemm_bm - 1) / p.gemm_bm;
     g.max_mtiles = g.mtiles;
-    HIP_TRY(launch_gemm_f32(g, p.gemm_bm, s));
+    HIP_TRY(launch_gemm_gate(g, p.gemm_bm, s));
   }
   TopkArgs t{};
   t.rows = c.T;

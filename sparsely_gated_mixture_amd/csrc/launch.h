@@ -50,6 +50,10 @@ struct GemmF32Args {
 };
 // bm: 64 or 128 (BN = bm).
 hipError_t launch_gemm_f32(const GemmF32Args& a, int bm, hipStream_t s);
+// The same product in flat mode (no row map, bias or ReLU; a.mtiles M-tiles of
+// bm rows) on the bf16 matrix cores, each fp32 operand split into three bf16
+// parts (fp32 accuracy).  K % 4 == 0.
+hipError_t launch_gemm_gate(const GemmF32Args& a, int bm, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // bf16 MFMA grouped GEMM for the expert FFNs.
