@@ -149,8 +149,8 @@ def bwd_kernel_work(name, cfg, rows, nonempty, T):
         return (T * d * 2 + T * hws * 2 + hws * d * 4, 2.0 * T * hws * d, "bf16")
     if name == "bwd_gate_wgrad":
         return (T * d * 4 + T * M * 4 + M * d * 4, 2.0 * T * M * d, "f32")
-    if name == "bwd_gate_dx":
-        return (T * M * 4 + M * d * 4 + T * d * 4, 2.0 * T * M * d, "f32")
+    if name == "bwd_gate_dx":  # split-bf16 GEMM: six bf16 products per term
+        return (T * M * 4 + M * d * 4 + T * d * 4, 6 * 2.0 * T * M * d, "bf16")
     if name == "bwd_combine":
         return (T * d * 4 + rows * d * 4 + rows * d * 2 + T * k * 12, 0.0, "f32")
     if name == "bwd_gate":

@@ -1360,7 +1360,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const floa
     gx.mtiles = (T + p.gemm_bm - 1) / p.gemm_bm;
     gx.max_mtiles = gx.mtiles;
     gx.prof_name = "bwd_gate_dx";
-    HIP_TRY(launch_gemm_f32(gx, p.gemm_bm, s));
+    HIP_TRY(launch_gemm_gate(gx, p.gemm_bm, s));
   }
   FfnBwd fb{};
   fb.u = xperm;
