@@ -342,14 +342,14 @@ size_t moe_backward_workspace_size(const moe_config* cfg);
  *   through P(x,i) into the clean logit, the noise scale and the
  *   threshold's logit).  The bf16 roundings of the forward pass gradients
  *   unchanged.
- * Arithmetic: the expert gradients are bf16 MFMA products with fp32
- * accumulation (the gradient rows entering them are rounded to bf16); the
- * gate's gradients are fp32.
+ * Arithmetic: for bf16 experts the expert gradients are bf16 MFMA products
+ * with fp32 accumulation (the gradient rows entering them are rounded to
+ * bf16); for fp32 experts everything is fp32; the gate's gradients are fp32.
  * In:  weights, x [T, d], noise [T, n] as for moe_forward; dy [T, d] fp32;
  *      dlosses [5] fp32 device vector.
  * Out: every gradient of `grads` (see moe_grads).
- * Supported: flat layers (n_groups == 0), expert_dtype MOE_BF16, d_model,
- * d_hidden and d_hidden_shared multiples of 64; MOE_ERR_UNSUPPORTED
+ * Supported: flat layers (n_groups == 0), expert_dtype MOE_BF16 or MOE_F32,
+ * d_model, d_hidden and d_hidden_shared multiples of 64; MOE_ERR_UNSUPPORTED
  * otherwise.  ws: moe_backward_workspace_size(cfg) bytes. */
 moe_status moe_backward(const moe_config* cfg, const moe_weights* weights, const float* x,
                         const float* noise, const float* dy, const float* dlosses,

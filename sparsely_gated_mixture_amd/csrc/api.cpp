@@ -715,18 +715,19 @@ BwdPlan make_bwd_plan(const moe_config& c) {
   const long long T1 = std::max(1LL, T);
   const bool swiglu = c.act == MOE_ACT_SWIGLU;
   Cursor w{b.f.total};
+  const long long esz = c.expert_dtype == MOE_F32 ? 4 : 2;  // activations and their gradients
   b.f.logits = w.take(T1 * b.f.ldl * 4);
-  b.f.hidden = w.take(A1 * h * 2);
+  b.f.hidden = w.take(A1 * h * esz);
   b.losses = w.take(8 * 4);
   b.dG = w.take(A1 * 4);
-  b.dout = w.take(A1 * d * 2);
+  b.dout = w.take(A1 * d * esz);
   b.dimp = w.take(n * 4);
   b.dload = w.take(n * 4);
   b.coef = w.take(4 * 4);
   b.dlogits = w.take(T1 * b.f.ldl * 4);
   b.part_db = w.take((size_t)std::max(1, b.f.nparts) * n * 4);
   b.hw = swiglu ? 2 * (int)h : (int)h;  // width of the hidden-layer gradient rows
-  b.dpre = w.take(A1 * b.hw * 2);
+  b.dpre = w.take(A1 * b.hw * esz);
   if (swiglu) {
     b.a_pre = w.take(A1 * h * 4);
     b.b_pre = w.take(A1 * h * 4);
@@ -757,8 +758,8 @@ BwdPlan make_bwd_plan(const moe_config& c) {
 moe_status validate_bwd(const moe_config& c) {
   if (c.n_groups > 0)
     return fail(MOE_ERR_UNSUPPORTED, "the backward pass covers flat layers (n_groups == 0)");
-  if (c.expert_dtype != MOE_BF16)
-    return fail(MOE_ERR_UNSUPPORTED, "the backward pass needs bf16 experts");
+  if (c.expert_dtype == MOE_FP8)
+    return fail(MOE_ERR_UNSUPPORTED, "the backward pass needs bf16 or fp32 experts");
   if (c.d_model % 64 || c.d_hidden % 64 || c.d_hidden_shared % 64)
     return fail(MOE_ERR_UNSUPPORTED,
                 "the backward pass needs d_model, d_hidden and d_hidden_shared multiples of 64");
@@ -791,12 +792,12 @@ moe_status bwd_hidden(const moe_config& c, GemmBf16Args g, int h, uint16_t* hidd
 // The four products of one FFN's backward over merged rows (routed experts:
 // the dispatch's tile map; shared expert: a one-segment map).
 struct FfnBwd {
-  const uint16_t* u;       // inputs [rows, d] bf16
-  const uint16_t* hidden;  // [rows, h]
+  const uint16_t* u;       // inputs [rows, d] bf16 (fp32 experts: fp32)
+  const uint16_t* hidden;  // [rows, h], same type
   const float* a_pre;      // SwiGLU pre-activations [rows, h]
   const float* b_pre;
-  const uint16_t* gout;    // output gradient rows [rows, d] bf16
-  uint16_t* dpre;          // [rows, hw]
+  const uint16_t* gout;    // output gradient rows [rows, d], same type
+  uint16_t* dpre;          // [rows, hw], same type
   float* du;               // [rows, d]
   const void* w1;
   const void* w3;
@@ -809,7 +810,8 @@ struct FfnBwd {
   const int32_t* tile_row0;
   const int32_t* offsets;
   const int32_t* tile_count;
-  int max_tiles, n_experts, h;
+  int max_tiles, tile_rows, n_experts, h;
+  bool f32;  // fp32 experts (activations and gradient rows in fp32)
   const char* names[4];
 };
 
@@ -823,7 +825,12 @@ moe_status ffn_bwd(const moe_config& c, const FfnBwd& f, hipStream_t s) {
   g.offsets = f.offsets;
   g.tile_count = f.tile_count;
   g.max_tiles = f.max_tiles;
+  g.tile_rows = f.tile_rows;
   g.n_experts = f.n_experts;
+  auto launch = [&](const GemmBwdArgs& a, int mode, int epi, const char* name) {
+    return f.f32 ? launch_gemm_bwd_f32(a, mode, epi, name, s)
+                 : launch_gemm_bwd(a, mode, epi, name, s);
+  };
   // (i) dhid = gout . W2 -> dpre (ReLU mask or SwiGLU da | db)
   g.A = (const uint16_t*)f.w2;
   g.lda = h;
@@ -838,10 +845,11 @@ moe_status ffn_bwd(const moe_config& c, const FfnBwd& f, hipStream_t s) {
   g.ldc = hw;
   g.c_split = h;
   g.aux_h = f.hidden;
-  g.aux_a = f.a_pre;
+  g.aux_a = f.f32 ? (const float*)f.hidden : f.a_pre;
   g.aux_b = f.b_pre;
   g.ldaux = h;
-  HIP_TRY(launch_gemm_bwd(g, BWD_ROWS, swiglu ? BEPI_SWIGLU : BEPI_RELU_MASK, f.names[0], s));
+  if (f.f32) g.C = (float*)f.dpre;  // fp32 gradient rows
+  HIP_TRY(launch(g, BWD_ROWS, swiglu ? BEPI_SWIGLU : BEPI_RELU_MASK, f.names[0]));
   // (ii) du = dpre . [W1; W3]
   GemmBwdArgs g2{};
   g2.tile_expert = f.tile_expert;
@@ -849,6 +857,7 @@ moe_status ffn_bwd(const moe_config& c, const FfnBwd& f, hipStream_t s) {
   g2.offsets = f.offsets;
   g2.tile_count = f.tile_count;
   g2.max_tiles = f.max_tiles;
+  g2.tile_rows = f.tile_rows;
   g2.A = (const uint16_t*)f.w1;
   g2.A2 = swiglu ? (const uint16_t*)f.w3 : nullptr;
   g2.lda = d;
@@ -860,7 +869,7 @@ moe_status ffn_bwd(const moe_config& c, const FfnBwd& f, hipStream_t s) {
   g2.K = hw;
   g2.C = f.du;
   g2.ldc = d;
-  HIP_TRY(launch_gemm_bwd(g2, BWD_ROWS, BEPI_F32, f.names[1], s));
+  HIP_TRY(launch(g2, BWD_ROWS, BEPI_F32, f.names[1]));
   // (iii) dW2[e] = gout^T . hidden over the expert's rows
   GemmBwdArgs g3{};
   g3.offsets = f.offsets;
@@ -875,7 +884,7 @@ moe_status ffn_bwd(const moe_config& c, const FfnBwd& f, hipStream_t s) {
   g3.ldc = h;
   g3.strideC = (long long)d * h;
   g3.c_split = d;
-  HIP_TRY(launch_gemm_bwd(g3, BWD_WGRAD, BEPI_F32, f.names[2], s));
+  HIP_TRY(launch(g3, BWD_WGRAD, BEPI_F32, f.names[2]));
   // (iv) [dW1; dW3][e] = dpre^T . u
   GemmBwdArgs g4{};
   g4.offsets = f.offsets;
@@ -891,7 +900,7 @@ moe_status ffn_bwd(const moe_config& c, const FfnBwd& f, hipStream_t s) {
   g4.ldc = d;
   g4.strideC = (long long)h * d;
   g4.c_split = h;
-  HIP_TRY(launch_gemm_bwd(g4, BWD_WGRAD, BEPI_F32, f.names[3], s));
+  HIP_TRY(launch(g4, BWD_WGRAD, BEPI_F32, f.names[3]));
   return MOE_OK;
 }
 
@@ -1238,6 +1247,13 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const floa
   fx.gate_stats = stats;
   fx.x_bf16 = shared ? at<uint16_t>(ws, p.sh_xb) : nullptr;
   CHECK(run_dispatch(c, p, idx, x, counts_pre, counts, offsets, perm, slot, xperm, ws, s, &fx));
+  const bool f32 = c.expert_dtype == MOE_F32;
+  if (f32) {
+    // fp32 experts: the forward's own expert stage (hidden goes to the
+    // relocated region of this plan)
+    CHECK(run_ffn(c, p, xperm, offsets, wt->w1, wt->b1, wt->w3, wt->w2, wt->b2, yperm, ws, s,
+                  &fx));
+  } else {
   GemmBf16Args g1{};
   g1.A = xperm;
   g1.lda = d;
@@ -1265,6 +1281,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const floa
   g2.ldc = d;
   g2.bias = wt->b2;
   HIP_TRY(launch_gemm_bf16(g2, EPI_IDENT_F32, s));
+  }
   const int hs = c.d_hidden_shared;
   uint16_t* xb = shared ? at<uint16_t>(ws, p.sh_xb) : nullptr;
   uint16_t* hid_s = shared ? at<uint16_t>(ws, p.sh_hidden) : nullptr;
@@ -1299,7 +1316,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const floa
   float* dload = at<float>(ws, b.dload);
   float* coef = at<float>(ws, b.coef);
   float* dlogits = at<float>(ws, b.dlogits);
-  HIP_TRY(launch_combine_bwd(dy, yperm, slot, w, T, k, d, dG, dout, s));
+  HIP_TRY(launch_combine_bwd(dy, yperm, slot, w, T, k, d, dG, dout, f32, s));
   HIP_TRY(launch_loss_grad(imp, noisy ? ld : nullptr, counts_pre, dlosses, T, k, n,
                            c.w_importance, c.w_load, c.alpha_switch, c.w_z, c.w_entropy, dimp,
                            dload, coef, s));
@@ -1383,15 +1400,17 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const floa
   fb.offsets = offsets;
   fb.tile_count = fx.tile_count;
   fb.max_tiles = p.max_mtiles;
+  fb.tile_rows = p.ffn_bm;
   fb.n_experts = n;
   fb.h = h;
+  fb.f32 = f32;
   fb.names[0] = "bwd_ggemm_dhidden";
   fb.names[1] = "bwd_ggemm_dinput";
   fb.names[2] = "bwd_ggemm_dw2";
   fb.names[3] = "bwd_ggemm_dw1";
   CHECK(ffn_bwd(c, fb, s));
-  if (wt->b2) HIP_TRY(launch_seg_colsum(dout, d, offsets, n, d, gr->db2, s));
-  if (wt->b1) HIP_TRY(launch_seg_colsum(fb.dpre, h, offsets, n, h, gr->db1, s));
+  if (wt->b2) HIP_TRY(launch_seg_colsum(dout, f32, d, offsets, n, d, gr->db2, s));
+  if (wt->b1) HIP_TRY(launch_seg_colsum(fb.dpre, f32, h, offsets, n, h, gr->db1, s));
   float* du_s = nullptr;
   if (shared) {
     uint16_t* dout_s = at<uint16_t>(ws, b.dout_s);
@@ -1416,6 +1435,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const floa
     fs.offsets = sh_off;
     fs.tile_count = sh_tc;
     fs.max_tiles = p.sh_tiles;
+    fs.tile_rows = kBf16BM;
     fs.n_experts = 1;
     fs.h = hs;
     fs.names[0] = "bwd_shared_dhidden";

@@ -30,10 +30,11 @@
 namespace moe {
 namespace {
 
+template <bool F32OUT>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(
     const float* __restrict__ dy, const float* __restrict__ y_perm,
     const int32_t* __restrict__ slot_pos, const float* __restrict__ topk_w, int T, int k, int d,
-    float* __restrict__ dG, uint16_t* __restrict__ dout) {
+    float* __restrict__ dG, void* __restrict__ dout) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -46,15 +47,19 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
     }
     const float w = topk_w[(long long)t * k + s];
     const float* yr = y_perm + (long long)pos * d;
-    uint16_t* orow = dout + (long long)pos * d;
     float acc = 0.f;
     for (int c = lane * 4; c < d; c += 256) {
       const f32x4 g = *(const f32x4*)(dyr + c);
       const f32x4 v = *(const f32x4*)(yr + c);
 #pragma unroll
       for (int q = 0; q < 4; ++q) acc = fmaf(g[q], v[q], acc);
-      *(uint2*)(orow + c) =
-          make_uint2(bf16x2_bits(w * g[0], w * g[1]), bf16x2_bits(w * g[2], w * g[3]));
+      if constexpr (F32OUT) {
+        *(f32x4*)((float*)dout + (long long)pos * d + c) =
+            f32x4{w * g[0], w * g[1], w * g[2], w * g[3]};
+      } else {
+        *(uint2*)((uint16_t*)dout + (long long)pos * d + c) =
+            make_uint2(bf16x2_bits(w * g[0], w * g[1]), bf16x2_bits(w * g[2], w * g[3]));
+      }
     }
     const float tot = wave_sum_dpp(acc);
     if (lane == 0) dG[(long long)t * k + s] = tot;
@@ -252,7 +257,8 @@ __global__ __launch_bounds__(256) void transpose_gate_kernel(const float* __rest
 }
 
 // out[e][c] = sum over the rows of segment e (in row order) of src[row][c].
-__global__ __launch_bounds__(256) void seg_colsum_kernel(const uint16_t* __restrict__ src,
+template <bool F32>
+__global__ __launch_bounds__(256) void seg_colsum_kernel(const void* __restrict__ src,
                                                          long long ld,
                                                          const int32_t* __restrict__ offsets,
                                                          int N, float* __restrict__ out) {
@@ -260,8 +266,10 @@ __global__ __launch_bounds__(256) void seg_colsum_kernel(const uint16_t* __restr
   const int c = blockIdx.x * 256 + threadIdx.x;
   if (c >= N) return;
   double s = 0.0;
-  for (int r = offsets[e]; r < offsets[e + 1]; ++r)
-    s += (double)bf16_to_f32(src[(long long)r * ld + c]);
+  for (int r = offsets[e]; r < offsets[e + 1]; ++r) {
+    const long long i = (long long)r * ld + c;
+    s += F32 ? (double)((const float*)src)[i] : (double)bf16_to_f32(((const uint16_t*)src)[i]);
+  }
   out[(long long)e * N + c] = (float)s;
 }
 
@@ -310,12 +318,17 @@ __global__ __launch_bounds__(256) void swiglu_hidden_kernel(const float* __restr
 }  // namespace
 
 hipError_t launch_combine_bwd(const float* dy, const float* y_perm, const int32_t* slot_pos,
-                              const float* topk_w, int T, int k, int d, float* dG,
-                              uint16_t* dout, hipStream_t s) {
+                              const float* topk_w, int T, int k, int d, float* dG, void* dout,
+                              int dout_f32, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   ProfScope ps("bwd_combine", s);
-  combine_bwd_kernel<<<dim3((T + 3) / 4), dim3(256), 0, s>>>(dy, y_perm, slot_pos, topk_w, T, k,
-                                                             d, dG, dout);
+  const dim3 grid((T + 3) / 4);
+  if (dout_f32)
+    combine_bwd_kernel<true><<<grid, dim3(256), 0, s>>>(dy, y_perm, slot_pos, topk_w, T, k, d,
+                                                        dG, dout);
+  else
+    combine_bwd_kernel<false><<<grid, dim3(256), 0, s>>>(dy, y_perm, slot_pos, topk_w, T, k, d,
+                                                         dG, dout);
   return hipGetLastError();
 }
 
@@ -365,11 +378,15 @@ hipError_t launch_transpose_gate(const float* w_gate, const float* w_noise, int 
   return hipGetLastError();
 }
 
-hipError_t launch_seg_colsum(const uint16_t* src, long long ld, const int32_t* offsets,
+hipError_t launch_seg_colsum(const void* src, int src_f32, long long ld, const int32_t* offsets,
                              int n_seg, int N, float* out, hipStream_t s) {
   if (n_seg <= 0 || N <= 0) return hipSuccess;
   ProfScope ps("bwd_bias_colsum", s);
-  seg_colsum_kernel<<<dim3((N + 255) / 256, n_seg), dim3(256), 0, s>>>(src, ld, offsets, N, out);
+  const dim3 grid((N + 255) / 256, n_seg);
+  if (src_f32)
+    seg_colsum_kernel<true><<<grid, dim3(256), 0, s>>>(src, ld, offsets, N, out);
+  else
+    seg_colsum_kernel<false><<<grid, dim3(256), 0, s>>>(src, ld, offsets, N, out);
   return hipGetLastError();
 }
 

@@ -131,10 +131,15 @@ struct GemmBwdArgs {
   const int32_t* offsets;
   const int32_t* tile_count;
   int max_tiles;
+  int tile_rows;  // rows per tile of the tile map (the bf16 kernels: kBf16BM)
   int n_experts;
 };
 hipError_t launch_gemm_bwd(const GemmBwdArgs& a, int mode, int epi, const char* name,
                            hipStream_t s);
+// The same products for fp32 experts (A, A2, B hold fp32; the ReLU mask reads
+// the fp32 hidden values from aux_a; no SwiGLU).  tile_rows is a multiple of 64.
+hipError_t launch_gemm_bwd_f32(const GemmBwdArgs& a, int mode, int epi, const char* name,
+                               hipStream_t s);
 
 // Tile map of a grouped GEMM: for every expert e with rows in
 // [offsets[e], offsets[e+1]), ceil(rows/bm) M-tiles in expert order.
@@ -286,10 +291,10 @@ hipError_t launch_aux(const float* importance, const float* load, const int32_t*
 // Backward (backward.hip).
 // ---------------------------------------------------------------------------
 // Per token, per kept slot: dG[t,s] = <dy_t, y_perm[row]>, dout[row] =
-// bf16(topk_w[t,s] * dy_t); dropped slots get dG = 0.
+// topk_w[t,s] * dy_t (bf16, or fp32 when dout_f32); dropped slots get dG = 0.
 hipError_t launch_combine_bwd(const float* dy, const float* y_perm, const int32_t* slot_pos,
-                              const float* topk_w, int T, int k, int d, float* dG,
-                              uint16_t* dout, hipStream_t s);
+                              const float* topk_w, int T, int k, int d, float* dG, void* dout,
+                              int dout_f32, hipStream_t s);
 // dimp = dl0 w_imp dCV^2(importance) + dl2 alpha n f / T, dload = dl1 w_load
 // dCV^2(load) (skipped when load is null), coef = {dl3 w_z / T, dl4 w_ent / T};
 // dlosses is a device vector of 5.
@@ -314,8 +319,9 @@ hipError_t launch_gate_wgrad(const GateWgradArgs& a, float* dw_gate, float* dw_n
 // wt [d, ldk] = [w_gate; w_noise (if given)]^T, zero past the stacked rows.
 hipError_t launch_transpose_gate(const float* w_gate, const float* w_noise, int n, int d,
                                  int ldk, float* wt, hipStream_t s);
-// out[e][c] = sum over rows offsets[e] .. offsets[e+1]-1 of src[row][c] (bf16).
-hipError_t launch_seg_colsum(const uint16_t* src, long long ld, const int32_t* offsets,
+// out[e][c] = sum over rows offsets[e] .. offsets[e+1]-1 of src[row][c] (bf16,
+// or fp32 when src_f32).
+hipError_t launch_seg_colsum(const void* src, int src_f32, long long ld, const int32_t* offsets,
                              int n_seg, int N, float* out, hipStream_t s);
 // dx[t] = dx_gate[t] (+ dx_shared[t]) + sum over kept slots of du_perm[row].
 hipError_t launch_dx_gather(const float* dx_gate, const float* dx_shared, const float* du_perm,

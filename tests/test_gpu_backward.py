@@ -2,10 +2,10 @@
 oracle's backward on the same seeded inputs.
 
 Bar: every gradient tensor within 2e-2 max-abs-normalised of the oracle's
-(the bf16 bar of the layer: the expert products round their operands to
-bf16 -- the gradient rows entering them as well -- and accumulate in fp32;
-the oracle computes in fp64 with the forward's bf16-rounded inputs and hidden
-activations).  The discrete decisions must be the oracle's: the routing is
+for bf16 experts (the bf16 bar of the layer: the expert products round their
+operands to bf16 -- the gradient rows entering them as well -- and
+accumulate in fp32; the oracle computes in fp64 with the forward's
+bf16-rounded inputs and hidden activations), 1e-4 for fp32 experts.  The discrete decisions must be the oracle's: the routing is
 compared exactly, and for a noisy gate, whose load estimator sends part of a
 token's gradient to the logit of the rank-k expert (the largest one not
 kept), the cases use inputs where the k+1-th and k+2-th largest gate values
@@ -21,9 +21,9 @@ import pytest
 import torch
 
 import oracle
-from _support import TOL_BF16, log, max_abs_norm
+from _support import TOL_BF16, TOL_F32, log, max_abs_norm
 from sparsely_gated_mixture_amd import MoELayer
-from sparsely_gated_mixture_amd.workloads import (ACT_SWIGLU, GATE_SIGMOID_BIAS,
+from sparsely_gated_mixture_amd.workloads import (ACT_SWIGLU, DTYPE_F32, GATE_SIGMOID_BIAS,
                                                   GATE_SWITCH_TOP1, PRESETS, MoEConfig,
                                                   make_grad_inputs, make_inputs, to_numpy64)
 
@@ -53,6 +53,12 @@ CASES = {
     # ReLU experts with a shared ReLU expert, noisy gate
     "relu_shared": MoEConfig("bwd_relu_shared", T=384, d_model=64, d_hidden=128, n_experts=8,
                              k=2, d_hidden_shared=128, seed=2106),
+    # fp32 experts: the small correctness workload as it is, and one with
+    # capacity drops and expert biases
+    "tiny_f32": PRESETS["tiny_f32"],
+    "f32_capacity": MoEConfig("bwd_f32_capacity", T=300, d_model=64, d_hidden=192, n_experts=8,
+                              k=2, expert_dtype=DTYPE_F32, capacity_factor=0.9,
+                              expert_bias_std=0.1, seed=2107),
 }
 
 GRAD_OF = dict(dw_gate="w_gate", db_gate="b_gate", dw_noise="w_noise", dw1="w1", db1="b1",
@@ -63,7 +69,7 @@ def _oracle_backward(cfg, h, dy, dl):
     return oracle.backward(
         h["x"], h["w_gate"], cfg.k, h["w1"], h["w2"], dy, dl, b_gate=h.get("b_gate"),
         w_noise=h.get("w_noise"), noise=h.get("noise"), b1=h.get("b1"), w3=h.get("w3"),
-        b2=h.get("b2"), mode=cfg.gate, act=cfg.act, bf16=True,
+        b2=h.get("b2"), mode=cfg.gate, act=cfg.act, bf16=cfg.expert_dtype != DTYPE_F32,
         capacity_factor=cfg.capacity_factor, w_importance=cfg.w_importance, w_load=cfg.w_load,
         alpha=cfg.alpha_switch, w_z=cfg.w_z, w_entropy=cfg.w_entropy, ws1=h.get("ws1"),
         ws3=h.get("ws3"), ws2=h.get("ws2"))
@@ -95,6 +101,7 @@ def _compare(cfg, inp, dy, dl, got, check_rank_k=True):
     if check_rank_k and h.get("w_noise") is not None:
         assert _rank_k_unambiguous(ref["fwd"]["gate"].H, cfg.k), \
             "the case's inputs have a near-tie at rank k: pick another seed"
+    tol = TOL_F32 if cfg.expert_dtype == DTYPE_F32 else TOL_BF16
     names = ["dx"] + [g for g, w in GRAD_OF.items() if w in h]
     if cfg.gate == GATE_SIGMOID_BIAS:
         names.remove("db_gate")
@@ -107,15 +114,15 @@ def _compare(cfg, inp, dy, dl, got, check_rank_k=True):
         if sl is None or not sl.any():
             err = max_abs_norm(a, b)
             log(f"  {name}: max-abs-normalised error {err:.2e}")
-            assert err <= TOL_BF16, (name, err)
+            assert err <= tol, (name, err)
             continue
         scale = np.max(np.abs(b))
         free = sl == 0
         err = float(np.max(np.abs(a - b)[free])) / scale if free.any() else 0.0
         log(f"  {name}: max-abs-normalised error {err:.2e} ({(~free).sum()} entries fed by "
             f"a ReLU mask at zero)")
-        assert err <= TOL_BF16, (name, err)
-        over = np.abs(a - b) > sl + TOL_BF16 * scale
+        assert err <= tol, (name, err)
+        over = np.abs(a - b) > sl + tol * scale
         assert not over.any(), (name, int(over.sum()))
     return ref
 
