@@ -454,6 +454,7 @@ def gate_hier(x, w_gate, w_noise, noise, k1, w_gate2, w_noise2, noise2, k2, b_ga
     zsum = pg.zsum
     load_sec = np.zeros((a, b))
     group_tokens = np.zeros(a, np.int32)
+    secondary = []  # (group, tokens, primary slots, GateResult) of each reached group
     noise2 = _d(noise2) if noise2 is not None else None
     w_noise2 = _d(w_noise2) if w_noise2 is not None else None
     for g in range(a):
@@ -465,6 +466,7 @@ def gate_hier(x, w_gate, w_noise, noise, k1, w_gate2, w_noise2, noise2, k2, b_ga
         z2 = noise2[toks, slots] if noise2 is not None else None
         sg = gate(x[toks], w_gate2[g], k2, None if b_gate2 is None else b_gate2[g],
                   None if w_noise2 is None else w_noise2[g], z2)
+        secondary.append((g, toks, slots, sg))
         zsum += sg.zsum
         for r, (t, s) in enumerate(zip(toks, slots)):
             idx[t, s * k2:(s + 1) * k2] = g * b + sg.topk_idx[r]
@@ -480,7 +482,7 @@ def gate_hier(x, w_gate, w_noise, noise, k1, w_gate2, w_noise2, noise2, k2, b_ga
     ld = hier_load(pg.load, load_sec, group_tokens) if pg.load is not None else None
     return dict(primary=pg, topk_idx=idx, topk_w=wts, importance=imp, load=ld,
                 load_secondary=load_sec, group_tokens=group_tokens, near_tie=near,
-                zsum=zsum, entsum=entropy_sum(dense))
+                zsum=zsum, entsum=entropy_sum(dense), secondary=secondary)
 
 
 def forward_hier(x, w_gate, w_noise, noise, k1, w_gate2, w_noise2, noise2, k2, w1, w2, *,
@@ -564,54 +566,11 @@ def expert_ffn_backward(u, w1, w2, gout, b1=None, w3=None, b2=None, act=ACT_RELU
     return out + ((amb @ np.abs(w1), amb.T @ np.abs(uq), amb.sum(axis=0)),)
 
 
-def backward(x, w_gate, k, w1, w2, dy, dlosses, *, b_gate=None, w_noise=None, noise=None,
-             b1=None, w3=None, b2=None, mode=GATE_TOPK_SOFTMAX, act=ACT_RELU, bf16=False,
-             capacity_factor=0.0, w_importance=0.1, w_load=0.1, alpha=1.0, w_z=1.0,
-             w_entropy=1.0, ws1=None, ws3=None, ws2=None):
-    """Gradients of L = sum_t <dy_t, y_t> + sum_j dlosses[j] * losses[j] for
-    the flat layer of ``forward`` (same arguments), the routing held fixed.
-    Returns a dict with dx, dw_gate, db_gate (None for the sigmoid gate,
-    whose bias only moves the selection), dw_noise, dw1, db1, dw3, dw2, db2,
-    dws1, dws3, dws2 (absent parts None), the forward's results ("fwd") and
-    "slack": for ReLU experts, the largest change that either value of the
-    mask at pre-activations within rounding of zero can make to dx, dw1, db1
-    and dws1 (see expert_ffn_backward); zeros elsewhere.
-
-    Stages, in reverse order of the forward ([PAPER] FAQ: the kept gate
-    values are differentiable because the selection comes before the
-    softmax; [NOTES] "Noisy Top-K Gating": the noise lets the load loss pass
-    gradients):
-      1. combine: dG[t,s] = <dy_t, y_perm[slot_pos[t,s]]> and the expert
-         output rows receive topk_w[t,s] * dy_t (dropped slots neither);
-      2. each expert (and the shared one, with weight 1) by
-         ``expert_ffn_backward``; a token's input gradient sums its rows';
-      3. the losses: dImportance = dl0 w_imp dCV^2 + dl2 alpha n f / T,
-         dLoad = dl1 w_load dCV^2, the z and entropy coefficients
-         dl3 w_z / T and dl4 w_entropy / T (losses[4] = w_entropy / T *
-         sum g ln g);
-      4. the gate by ``oracle_gate_backward`` (dclean, draw);
-      5. the gate's linear maps: dW_g = dclean^T x, db = column sums of dclean,
-         dW_noise = draw^T x, dx += dclean W_g + draw W_noise."""
-    x = _d(x)
-    T, d = x.shape
-    w_gate = _d(w_gate)
-    n = w_gate.shape[0]
-    dy = _d(dy)
-    dl = _d(dlosses)
-    fwd = forward(x, w_gate, k, w1, w2, b_gate=b_gate, w_noise=w_noise, noise=noise, b1=b1,
-                  w3=w3, b2=b2, mode=mode, act=act, bf16=bf16, capacity_factor=capacity_factor,
-                  w_importance=w_importance, w_load=w_load, alpha=alpha, w_z=w_z,
-                  w_entropy=w_entropy, ws1=ws1, ws3=ws3, ws2=ws2)
-    g = fwd["gate"]
-    disp = fwd["dispatch"]
-    slot_pos = disp["slot_pos"]
-    perm = disp["perm"]
-    offsets = disp["offsets"]
-    y_perm = fwd["y_perm"]
-
-    # 1. combine
+def _combine_backward(dy, y_perm, slot_pos, topk_w, rows, d):
+    """dG[t,s] = <dy_t, y_perm[row]> and the expert output gradients
+    gout[row] = topk_w[t,s] * dy_t for the kept slots (dropped slots: 0)."""
+    T, k = slot_pos.shape
     dG = np.zeros((T, k))
-    rows = int(offsets[n])
     gout = np.zeros((rows, d))
     for t in range(T):
         for s in range(k):
@@ -619,11 +578,18 @@ def backward(x, w_gate, k, w1, w2, dy, dlosses, *, b_gate=None, w_noise=None, no
             if r < 0:
                 continue
             dG[t, s] = dy[t] @ y_perm[r]
-            gout[r] = g.topk_w[t, s] * dy[t]
+            gout[r] = topk_w[t, s] * dy[t]
+    return dG, gout
 
-    # 2. experts
-    w1, w2, w3, b1, b2 = map(_d, (w1, w2, w3, b1, b2))
+
+def _experts_backward(x, disp, gout, w1, w2, w3, b1, b2, act, bf16):
+    """Every expert's backward on its merged rows; returns (dx, grads, slack)
+    with dx the tokens' input gradients summed in slot order."""
+    T, d = x.shape
+    n = w1.shape[0]
     h = w1.shape[1]
+    offsets, perm, slot_pos = disp["offsets"], disp["perm"], disp["slot_pos"]
+    rows = int(offsets[n])
     dw1 = np.zeros_like(w1)
     dw2 = np.zeros_like(w2)
     dw3 = np.zeros_like(w3) if w3 is not None else None
@@ -655,14 +621,98 @@ def backward(x, w_gate, k, w1, w2, dy, dlosses, *, b_gate=None, w_noise=None, no
         if db2 is not None:
             db2[e] = res[5]
     dx = np.zeros((T, d))
+    k = slot_pos.shape[1]
     for t in range(T):
         for s in range(k):
             r = slot_pos[t, s]
             if r >= 0:
                 dx[t] += du_perm[r]
                 slack["dx"][t] += slack_du[r]
+    grads = dict(dw1=dw1, db1=db1, dw3=dw3, dw2=dw2, db2=db2)
+    return dx, grads, slack
+
+
+def _loss_coefficients(dl, T, k, n, importance_v, load_v, counts_pre, w_importance, w_load,
+                       alpha, w_z, w_entropy):
+    """dImportance = dl0 w_imp dCV^2 + dl2 alpha n f / T, dLoad = dl1 w_load
+    dCV^2 (None without Load), and the z and entropy coefficients dl3 w_z / T
+    and dl4 w_entropy / T (losses[4] = w_entropy / T * sum g ln g)."""
+    f = np.asarray(counts_pre) / float(T * k)
+    dimp = cv2_grad(importance_v, dl[0] * w_importance) + dl[2] * alpha * n * f / T
+    dload = cv2_grad(load_v, dl[1] * w_load) if load_v is not None else None
+    return dimp, dload, dl[3] * w_z / T, dl[4] * w_entropy / T
+
+
+def _gate_backward(x, gr, k, mode, w_gate, w_noise, noise, dG, dimp, dload, c_z, c_ent):
+    """oracle_gate_backward for one gate over the rows of x (GateResult gr);
+    returns (dclean, draw or None)."""
+    T, n = gr.H.shape
+    noisy = gr.sp is not None
+    if mode == GATE_SIGMOID_BIAS:
+        Zs = x @ _d(w_gate).T        # the bias-free logits h
+        clean = Zs
+    else:
+        Zs = gr.H
+        clean = gr.clean
+    raw = x @ _d(w_noise).T if noisy else None
+    z = _d(noise) if noisy else None
+    dclean = np.empty((T, n))
+    draw = np.empty((T, n)) if noisy else None
+    if T:
+        lib().oracle_gate_backward(T, n, k, mode, _d(gr.H), _d(Zs), _d(clean),
+                                   _d(gr.sp) if noisy else None, z, raw, _i(gr.topk_idx),
+                                   _d(gr.topk_w), _d(gr.probs), _d(gr.hk), _d(gr.hk1),
+                                   _d(dG), _d(dimp), _d(dload) if dload is not None else None,
+                                   float(c_z), float(c_ent), dclean, draw)
+    return dclean, draw
+
+
+def backward(x, w_gate, k, w1, w2, dy, dlosses, *, b_gate=None, w_noise=None, noise=None,
+             b1=None, w3=None, b2=None, mode=GATE_TOPK_SOFTMAX, act=ACT_RELU, bf16=False,
+             capacity_factor=0.0, w_importance=0.1, w_load=0.1, alpha=1.0, w_z=1.0,
+             w_entropy=1.0, ws1=None, ws3=None, ws2=None):
+    """Gradients of L = sum_t <dy_t, y_t> + sum_j dlosses[j] * losses[j] for
+    the flat layer of ``forward`` (same arguments), the routing held fixed.
+    Returns a dict with dx, dw_gate, db_gate (None for the sigmoid gate,
+    whose bias only moves the selection), dw_noise, dw1, db1, dw3, dw2, db2,
+    dws1, dws3, dws2 (absent parts None), the forward's results ("fwd") and
+    "slack": for ReLU experts, the largest change that either value of the
+    mask at pre-activations within rounding of zero can make to dx, dw1, db1
+    and dws1 (see expert_ffn_backward); zeros elsewhere.
+
+    Stages, in reverse order of the forward ([PAPER] FAQ: the kept gate
+    values are differentiable because the selection comes before the
+    softmax; [NOTES] "Noisy Top-K Gating": the noise lets the load loss pass
+    gradients):
+      1. combine: dG[t,s] = <dy_t, y_perm[slot_pos[t,s]]> and the expert
+         output rows receive topk_w[t,s] * dy_t (dropped slots neither);
+      2. each expert (and the shared one, with weight 1) by
+         ``expert_ffn_backward``; a token's input gradient sums its rows';
+      3. the losses (``_loss_coefficients``);
+      4. the gate by ``oracle_gate_backward`` (dclean, draw);
+      5. the gate's linear maps: dW_g = dclean^T x, db = column sums of dclean,
+         dW_noise = draw^T x, dx += dclean W_g + draw W_noise."""
+    x = _d(x)
+    T, d = x.shape
+    w_gate = _d(w_gate)
+    n = w_gate.shape[0]
+    dy = _d(dy)
+    dl = _d(dlosses)
+    fwd = forward(x, w_gate, k, w1, w2, b_gate=b_gate, w_noise=w_noise, noise=noise, b1=b1,
+                  w3=w3, b2=b2, mode=mode, act=act, bf16=bf16, capacity_factor=capacity_factor,
+                  w_importance=w_importance, w_load=w_load, alpha=alpha, w_z=w_z,
+                  w_entropy=w_entropy, ws1=ws1, ws3=ws3, ws2=ws2)
+    g = fwd["gate"]
+    disp = fwd["dispatch"]
+    rows = int(disp["offsets"][n])
+
+    # 1-2. combine and experts
+    dG, gout = _combine_backward(dy, fwd["y_perm"], disp["slot_pos"], g.topk_w, rows, d)
+    w1, w2, w3, b1, b2 = map(_d, (w1, w2, w3, b1, b2))
+    dx, eg, slack = _experts_backward(x, disp, gout, w1, w2, w3, b1, b2, act, bf16)
     dws1 = dws3 = dws2 = None
     if ws1 is not None:
+        relu = act != ACT_SWIGLU
         res = expert_ffn_backward(x, ws1, ws2, dy, None, ws3, None, act, bf16, slack=relu)
         dx += res[0]
         dws1, dws3, dws2 = res[1], res[3], res[4]
@@ -670,30 +720,12 @@ def backward(x, w_gate, k, w1, w2, dy, dlosses, *, b_gate=None, w_noise=None, no
             slack["dx"] += res[6][0]
             slack["dws1"] = res[6][1]
 
-    # 3. losses
-    f = disp["counts_pre"] / float(T * k)
-    dimp = cv2_grad(g.importance, dl[0] * w_importance) + dl[2] * alpha * n * f / T
-    dload = cv2_grad(g.load, dl[1] * w_load) if g.load is not None else None
-    c_z = dl[3] * w_z / T
-    c_ent = dl[4] * w_entropy / T
-
-    # 4. gate
-    noisy = g.sp is not None
-    if mode == GATE_SIGMOID_BIAS:
-        Zs = x @ w_gate.T           # the bias-free logits h
-        clean = Zs
-    else:
-        Zs = g.H
-        clean = g.clean
-    raw = x @ _d(w_noise).T if noisy else None
-    z = _d(noise) if noisy else None
-    dclean = np.empty((T, n))
-    draw = np.empty((T, n)) if noisy else None
-    lib().oracle_gate_backward(T, n, k, mode, _d(g.H), _d(Zs), _d(clean),
-                               _d(g.sp) if noisy else None, z, raw, _i(g.topk_idx),
-                               _d(g.topk_w), _d(g.probs), _d(g.hk), _d(g.hk1), dG, dimp,
-                               _d(dload) if dload is not None else None, c_z, c_ent, dclean,
-                               draw)
+    # 3-4. losses and gate
+    dimp, dload, c_z, c_ent = _loss_coefficients(
+        dl, T, k, n, g.importance, g.load, disp["counts_pre"], w_importance, w_load, alpha,
+        w_z, w_entropy)
+    dclean, draw = _gate_backward(x, g, k, mode, w_gate, w_noise, noise, dG, dimp, dload, c_z,
+                                  c_ent)
 
     # 5. the gate's linear maps
     dw_gate = dclean.T @ x
@@ -702,9 +734,117 @@ def backward(x, w_gate, k, w1, w2, dy, dlosses, *, b_gate=None, w_noise=None, no
     if b_gate is not None and mode != GATE_SIGMOID_BIAS:
         db_gate = dclean.sum(axis=0)
     dw_noise = None
-    if noisy:
+    if draw is not None:
         dw_noise = draw.T @ x
         dx += draw @ _d(w_noise)
-    return dict(dx=dx, dw_gate=dw_gate, db_gate=db_gate, dw_noise=dw_noise, dw1=dw1, db1=db1,
-                dw3=dw3, dw2=dw2, db2=db2, dws1=dws1, dws3=dws3, dws2=dws2, dG=dG, dclean=dclean,
-                draw=draw, fwd=fwd, slack=slack)
+    return dict(dx=dx, dw_gate=dw_gate, db_gate=db_gate, dw_noise=dw_noise, dws1=dws1,
+                dws3=dws3, dws2=dws2, dG=dG, dclean=dclean, draw=draw, fwd=fwd, slack=slack,
+                **eg)
+
+
+def backward_hier(x, w_gate, w_noise, noise, k1, w_gate2, w_noise2, noise2, k2, w1, w2, dy,
+                  dlosses, *, b1=None, b2=None, bf16=False, w_importance=0.1, w_load=0.1,
+                  alpha=1.0, w_z=1.0, w_entropy=1.0):
+    """Gradients of L for the two-level layer of ``forward_hier`` (same
+    arguments), the routing held fixed.  Returns dx, dw_gate, dw_noise,
+    dw_gate2, dw_noise2 ([a, b, d]), dw1, db1, dw2, db2, "fwd" and "slack".
+
+    The chain ([NOTES] "分层 MoE" for the structure; the readings of the
+    two-level Importance and Load are those of the forward):
+      1. combine and experts as for the flat layer, on the combined slots;
+      2. the losses over Importance_H and Load_H, as for the flat layer;
+      3. on each combined slot (s, s2) the gradient of the product weight
+         w = w1_s * w2_{s,s2} is gw = dG + dImportance_H[expert] + c_ent (ln w
+         + 1) (Importance_H and the entropy are taken over the products);
+         then dw1_s = sum over s2 of gw * w2 and dw2_{s,s2} = gw * w1_s;
+      4. Load_H[g*b+e] = Load_p[g] Load_g[e] / |X_g|: dLoad_p[g] = sum over e
+         of dLoad_H * Load_g[e] / |X_g|, dLoad_g[e] = dLoad_H * Load_p[g] / |X_g|
+         (0 when no token reaches g);
+      5. the primary gate's backward with dG = dw1, no Importance or entropy
+         term of its own, dLoad_p and the z coefficient; each group's secondary
+         gate's backward over its rows likewise, with dw2 and dLoad_g;
+      6. the linear maps of both levels (the secondary per group, over the
+         rows routed to it)."""
+    x = _d(x)
+    T, d = x.shape
+    dy = _d(dy)
+    dl = _d(dlosses)
+    w_gate2 = _d(w_gate2)
+    a, b, _ = w_gate2.shape
+    n = a * b
+    k = k1 * k2
+    fwd = forward_hier(x, w_gate, w_noise, noise, k1, w_gate2, w_noise2, noise2, k2, w1, w2,
+                       b1=b1, b2=b2, bf16=bf16, w_importance=w_importance, w_load=w_load,
+                       alpha=alpha, w_z=w_z, w_entropy=w_entropy)
+    gh = fwd["gate"]
+    disp = fwd["dispatch"]
+    rows = int(disp["offsets"][n])
+
+    # 1. combine and experts
+    dG, gout = _combine_backward(dy, fwd["y_perm"], disp["slot_pos"], gh["topk_w"], rows, d)
+    w1, w2, b1, b2 = map(_d, (w1, w2, b1, b2))
+    dx, eg, slack = _experts_backward(x, disp, gout, w1, w2, None, b1, b2, ACT_RELU, bf16)
+
+    # 2. losses
+    dimp, dload, c_z, c_ent = _loss_coefficients(
+        dl, T, k, n, gh["importance"], gh["load"], disp["counts_pre"], w_importance, w_load,
+        alpha, w_z, w_entropy)
+
+    # 3. product weights
+    pg = gh["primary"]
+    w2_of = np.zeros((T, k1, k2))  # secondary weights by (token, primary slot)
+    for g, toks, slots, sg in gh["secondary"]:
+        w2_of[toks, slots] = sg.topk_w
+    dw1 = np.zeros((T, k1))
+    dw2 = np.zeros((T, k1, k2))
+    for t in range(T):
+        for s in range(k1):
+            for s2 in range(k2):
+                j = s * k2 + s2
+                wv = gh["topk_w"][t, j]
+                gw = dG[t, j] + dimp[gh["topk_idx"][t, j]]
+                if wv > 0.0:
+                    gw += c_ent * (np.log(wv) + 1.0)
+                dw1[t, s] += gw * w2_of[t, s, s2]
+                dw2[t, s, s2] = gw * pg.topk_w[t, s]
+
+    # 4. the factorised load
+    dload_p = np.zeros(a) if dload is not None else None
+    dload_g = np.zeros((a, b)) if dload is not None else None
+    if dload is not None:
+        cnt = gh["group_tokens"]
+        lg = gh["load_secondary"]
+        for g in range(a):
+            if cnt[g] == 0:
+                continue
+            seg = dload[g * b:(g + 1) * b]
+            dload_p[g] = (seg * lg[g]).sum() / cnt[g]
+            dload_g[g] = seg * pg.load[g] / cnt[g]
+
+    # 5-6. both gates
+    zero_a, zero_b = np.zeros(a), np.zeros(b)
+    dclean, draw = _gate_backward(x, pg, k1, GATE_TOPK_SOFTMAX, w_gate, w_noise, noise, dw1,
+                                  zero_a, dload_p, c_z, 0.0)
+    dw_gate = dclean.T @ x
+    dx += dclean @ _d(w_gate)
+    dw_noise = None
+    if draw is not None:
+        dw_noise = draw.T @ x
+        dx += draw @ _d(w_noise)
+    dw_gate2 = np.zeros_like(w_gate2)
+    dw_noise2 = np.zeros_like(w_gate2) if w_noise2 is not None else None
+    noise2 = _d(noise2) if noise2 is not None else None
+    for g, toks, slots, sg in gh["secondary"]:
+        xg = x[toks]
+        z2 = noise2[toks, slots] if noise2 is not None else None
+        dc2, dr2 = _gate_backward(xg, sg, k2, GATE_TOPK_SOFTMAX, w_gate2[g],
+                                  None if w_noise2 is None else _d(w_noise2)[g], z2,
+                                  dw2[toks, slots], zero_b,
+                                  None if dload_g is None else dload_g[g], c_z, 0.0)
+        dw_gate2[g] = dc2.T @ xg
+        dx[toks] += dc2 @ w_gate2[g]
+        if dr2 is not None:
+            dw_noise2[g] = dr2.T @ xg
+            dx[toks] += dr2 @ _d(w_noise2)[g]
+    return dict(dx=dx, dw_gate=dw_gate, dw_noise=dw_noise, dw_gate2=dw_gate2,
+                dw_noise2=dw_noise2, dG=dG, fwd=fwd, slack=slack, **eg)

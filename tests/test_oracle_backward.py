@@ -134,3 +134,53 @@ def test_dropped_slots_carry_no_expert_gradient():
     for name in ("dw1", "db1", "dw2", "db2"):
         assert not g[name].any(), name
     assert not g["dG"].any()
+
+
+@pytest.mark.parametrize("noisy", [True, False], ids=["noisy", "clean"])
+def test_two_level_backward_matches_finite_differences(noisy):
+    """The two-level layer: product weights, the factorised load and both
+    levels' gates, pinned by finite differences of forward_hier."""
+    rng = np.random.default_rng(11)
+    T, d, a, b, k1, k2, h = 36, 10, 3, 4, 2, 2, 8
+    P = dict(x=rng.standard_normal((T, d)), w_gate=rng.standard_normal((a, d)) * 0.5,
+             w_gate2=rng.standard_normal((a, b, d)) * 0.5,
+             w1=rng.standard_normal((a * b, h, d)) / np.sqrt(d),
+             w2=rng.standard_normal((a * b, d, h)) / np.sqrt(h),
+             b1=rng.standard_normal((a * b, h)) * 0.1, b2=rng.standard_normal((a * b, d)) * 0.1)
+    if noisy:
+        P["w_noise"] = rng.standard_normal((a, d)) * 0.3
+        P["w_noise2"] = rng.standard_normal((a, b, d)) * 0.3
+    noise = rng.standard_normal((T, a)) if noisy else None
+    noise2 = rng.standard_normal((T, k1, b)) if noisy else None
+    dy = rng.standard_normal((T, d))
+    dl = rng.standard_normal(5)
+    kw = dict(w_importance=0.3, w_load=0.4, alpha=0.5, w_z=0.2, w_entropy=0.7)
+
+    def objective(P):
+        f = O.forward_hier(P["x"], P["w_gate"], P.get("w_noise"), noise, k1, P["w_gate2"],
+                           P.get("w_noise2"), noise2, k2, P["w1"], P["w2"], b1=P["b1"],
+                           b2=P["b2"], **kw)
+        return float((dy * f["y"]).sum() + (dl * f["losses"]).sum()), f
+
+    _, f0 = objective(P)
+    assert not f0["gate"]["near_tie"].any()
+    g = O.backward_hier(P["x"], P["w_gate"], P.get("w_noise"), noise, k1, P["w_gate2"],
+                        P.get("w_noise2"), noise2, k2, P["w1"], P["w2"], dy, dl, b1=P["b1"],
+                        b2=P["b2"], **kw)
+    names = dict(x="dx", w_gate="dw_gate", w_noise="dw_noise", w_gate2="dw_gate2",
+                 w_noise2="dw_noise2", w1="dw1", w2="dw2", b1="db1", b2="db2")
+    for name, v in P.items():
+        an = g[names[name]]
+        assert an.shape == v.shape
+        for fi in rng.choice(v.size, size=min(8, v.size), replace=False):
+            Pp = {q: r.copy() for q, r in P.items()}
+            Pm = {q: r.copy() for q, r in P.items()}
+            Pp[name].flat[fi] += EPS
+            Pm[name].flat[fi] -= EPS
+            lp, fp = objective(Pp)
+            lm, fm = objective(Pm)
+            assert (fp["gate"]["topk_idx"] == f0["gate"]["topk_idx"]).all()
+            assert (fm["gate"]["topk_idx"] == f0["gate"]["topk_idx"]).all()
+            fd = (lp - lm) / (2 * EPS)
+            assert abs(fd - an.flat[fi]) <= TOL * (1 + abs(an.flat[fi])), (name, fi, fd,
+                                                                           an.flat[fi])
