@@ -62,7 +62,15 @@ def kernel_work(name, cfg, rows, nonempty, T):
     bf = cfg.expert_dtype != 0
     wsz = 2 if bf else 4
     noisy = cfg.noisy
-    ncols = 2 * n if noisy else n
+    ng = cfg.n_groups if cfg.hierarchical else n  # the flat or primary gate's width
+    ncols = 2 * ng if noisy else ng
+    if cfg.hierarchical:
+        # the two-level secondary gate: T*k1 rows of 2b logits (grouped fp32 GEMM)
+        r2, c2 = T * cfg.k_groups, (2 if noisy else 1) * cfg.b
+        if name.startswith("gemm_f32"):
+            return (r2 * d * 4 + cfg.n_groups * c2 * d * 4 + r2 * c2 * 4, 2.0 * r2 * c2 * d, "f32")
+        if name == "gate_topk_grouped":
+            return (r2 * c2 * 4 + (r2 * cfg.b * 4 if noisy else 0) + T * k * 8, 0.0, "f32")
     if name == "ggemm_bf16_relu":
         return (nonempty * h * d * 2 + rows * d * 2 + rows * h * 2, 2.0 * rows * h * d, "bf16")
     if name == "ggemm_bf16_swiglu":
@@ -93,7 +101,7 @@ def kernel_work(name, cfg, rows, nonempty, T):
     if name.startswith("gemm_f32"):
         return (T * d * 4 + ncols * d * 4 + T * ncols * 4, 2.0 * T * ncols * d, "f32")
     if name == "gate_topk":
-        return (T * ncols * 4 + (T * n * 4 if noisy else 0) + T * k * 8, 0.0, "f32")
+        return (T * ncols * 4 + (T * ng * 4 if noisy else 0) + T * k * 8, 0.0, "f32")
     if name == "dispatch_gather":
         return (T * d * 4 + rows * d * wsz + rows * 4 + (T * d * 2 if hs else 0), 0.0, "f32")
     if name == "combine":
@@ -119,7 +127,8 @@ def bwd_kernel_work(name, cfg, rows, nonempty, T):
     d, h, n, k = cfg.d_model, cfg.d_hidden, cfg.n_experts, cfg.k
     sw = cfg.act == 1
     hw = 2 * h if sw else h
-    M = 2 * n if cfg.noisy else n
+    ng = cfg.n_groups if cfg.hierarchical else n
+    M = 2 * ng if cfg.noisy else ng
     hs = cfg.d_hidden_shared
     hws = 2 * hs if sw else hs
     if name == "bwd_ggemm_preact":   # x W1^T and x W3^T kept in fp32 (SwiGLU)
@@ -154,8 +163,14 @@ def bwd_kernel_work(name, cfg, rows, nonempty, T):
     if name == "bwd_combine":
         return (T * d * 4 + rows * d * 4 + rows * d * 2 + T * k * 12, 0.0, "f32")
     if name == "bwd_gate":
+        if cfg.hierarchical:
+            return (0.0, 0.0, "")  # the primary and secondary gates share the name
         return (T * M * 4 + (T * n * 4 if cfg.noisy else 0) + T * k * 12 + T * M * 4, 0.0,
                 "f32")
+    if name in ("bwd_gate2_wgrad", "bwd_gate2_dx"):
+        r2, c2 = T * cfg.k_groups, (2 if cfg.noisy else 1) * cfg.b
+        wbytes = cfg.n_groups * c2 * d * 4
+        return (r2 * d * 4 + r2 * c2 * 4 + wbytes, 2.0 * r2 * c2 * d, "f32")
     if name == "bwd_dx_gather":
         return (T * d * 4 + rows * d * 4 + (T * d * 4 if hs else 0) + T * d * 4, 0.0, "f32")
     return kernel_work(name, cfg, rows, nonempty, T)
@@ -423,7 +438,7 @@ def bench_backward(args, cfg):
     T, n, k = cfg.T, cfg.n_experts, cfg.k
 
     def step():
-        return layer.backward(inp["x"], dy, dl, inp.get("noise"))
+        return layer.backward(inp["x"], dy, dl, inp.get("noise"), inp.get("noise2"))
 
     for _ in range(args.warmup):
         grads = step()
@@ -432,7 +447,8 @@ def bench_backward(args, cfg):
     g = moe.make_grads(**grads)
 
     def eager_step():
-        moe.moe_backward(layer.c, layer.w, inp["x"], inp.get("noise"), dy, dl, g, layer.ws_bwd)
+        moe.moe_backward(layer.c, layer.w, inp["x"], inp.get("noise"), inp.get("noise2"), dy, dl,
+                         g, layer.ws_bwd)
 
     def timed(fn):
         torch.cuda.synchronize()
@@ -459,7 +475,7 @@ def bench_backward(args, cfg):
 
     i32 = dict(dtype=torch.int32, device="cuda")
     diag = {"topk_idx": torch.empty((T, k), **i32), "counts": torch.empty(n, **i32)}
-    layer.forward(inp["x"], inp.get("noise"), diag=diag)
+    layer.forward(inp["x"], inp.get("noise"), inp.get("noise2"), diag=diag)
     torch.cuda.synchronize()
     counts = diag["counts"].cpu().numpy()
     rows = int(counts.sum())
@@ -524,15 +540,24 @@ def cpu_baseline_backward(cfg, inp, dy, dl, sample_tokens, seconds):
     dlh = to_numpy64(dl)
     oracle.lib()
     reps, dt = 0, 0.0
+    bf16 = cfg.expert_dtype != 0
     while reps == 0 or dt < seconds:
         t0 = time.perf_counter()
-        oracle.backward(x, h["w_gate"], cfg.k, h["w1"], h["w2"], dyh, dlh,
-                        b_gate=h.get("b_gate"), w_noise=h.get("w_noise"), noise=noise,
-                        b1=h.get("b1"), w3=h.get("w3"), b2=h.get("b2"), mode=cfg.gate,
-                        act=cfg.act, bf16=True, capacity_factor=cfg.capacity_factor,
-                        w_importance=cfg.w_importance, w_load=cfg.w_load,
-                        alpha=cfg.alpha_switch, w_z=cfg.w_z, w_entropy=cfg.w_entropy,
-                        ws1=h.get("ws1"), ws3=h.get("ws3"), ws2=h.get("ws2"))
+        if cfg.hierarchical:
+            oracle.backward_hier(x, h["w_gate"], h.get("w_noise"), noise, cfg.k_groups,
+                                 h["w_gate2"], h.get("w_noise2"),
+                                 h["noise2"][:S] if "noise2" in h else None, cfg.k2, h["w1"],
+                                 h["w2"], dyh, dlh, b1=h.get("b1"), b2=h.get("b2"), bf16=bf16,
+                                 w_importance=cfg.w_importance, w_load=cfg.w_load,
+                                 alpha=cfg.alpha_switch, w_z=cfg.w_z, w_entropy=cfg.w_entropy)
+        else:
+            oracle.backward(x, h["w_gate"], cfg.k, h["w1"], h["w2"], dyh, dlh,
+                            b_gate=h.get("b_gate"), w_noise=h.get("w_noise"), noise=noise,
+                            b1=h.get("b1"), w3=h.get("w3"), b2=h.get("b2"), mode=cfg.gate,
+                            act=cfg.act, bf16=bf16, capacity_factor=cfg.capacity_factor,
+                            w_importance=cfg.w_importance, w_load=cfg.w_load,
+                            alpha=cfg.alpha_switch, w_z=cfg.w_z, w_entropy=cfg.w_entropy,
+                            ws1=h.get("ws1"), ws3=h.get("ws3"), ws2=h.get("ws2"))
         dt += time.perf_counter() - t0
         reps += 1
     return {"value": S * reps / dt, "unit": "tokens/s", "cores": oracle.num_threads(),

@@ -323,13 +323,15 @@ typedef struct {
   float* dws1;     /* [h_s, d] */
   float* dws3;     /* [h_s, d] */
   float* dws2;     /* [d, h_s] */
+  float* dw_gate2; /* [a, b, d] (two-level layer) */
+  float* dw_noise2;/* [a, b, d] (two-level layer with w_noise2) */
 } moe_grads;
 
 /* Bytes of workspace moe_backward needs (0 on an invalid or unsupported
  * config). */
 size_t moe_backward_workspace_size(const moe_config* cfg);
 
-/* Backward pass of the flat layer: the gradients of
+/* Backward pass of the layer: the gradients of
  *   L = sum_t <dy_t, y_t> + sum_j dlosses[j] * losses[j]
  * (y and losses[5] as moe_forward computes them) with respect to x and every
  * weight, the routing (the top-k selection and the capacity drops) held
@@ -345,15 +347,23 @@ size_t moe_backward_workspace_size(const moe_config* cfg);
  * Arithmetic: for bf16 experts the expert gradients are bf16 MFMA products
  * with fp32 accumulation (the gradient rows entering them are rounded to
  * bf16); for fp32 experts everything is fp32; the gate's gradients are fp32.
- * In:  weights, x [T, d], noise [T, n] as for moe_forward; dy [T, d] fp32;
- *      dlosses [5] fp32 device vector.
+ * Two-level layer (chenshi221.pages.dev notes, "Hierarchical MoE"): a
+ * combined slot's weight is w1_s * w2_{s,s2}, Importance and the entropy
+ * are over these products and Load is the factorised form (see
+ * moe_gate_hier); the chain runs through both gates, each group's over the
+ * rows routed to it.
+ * In:  weights, x [T, d], noise [T, n_gate], noise2 [T, k1, b] as for
+ *      moe_forward; dy [T, d] fp32; dlosses [5] fp32 device vector.
  * Out: every gradient of `grads` (see moe_grads).
- * Supported: flat layers (n_groups == 0), expert_dtype MOE_BF16 or MOE_F32,
- * d_model, d_hidden and d_hidden_shared multiples of 64; MOE_ERR_UNSUPPORTED
- * otherwise.  ws: moe_backward_workspace_size(cfg) bytes. */
+ * Supported: expert_dtype MOE_BF16 or MOE_F32; d_model, d_hidden and
+ * d_hidden_shared multiples of 64; for the two-level layer the secondary
+ * gate's logit columns (b, or 2b with w_noise2) a multiple of 16;
+ * MOE_ERR_UNSUPPORTED otherwise.  ws: moe_backward_workspace_size(cfg)
+ * bytes. */
 moe_status moe_backward(const moe_config* cfg, const moe_weights* weights, const float* x,
-                        const float* noise, const float* dy, const float* dlosses,
-                        const moe_grads* grads, void* ws, size_t ws_bytes, void* stream);
+                        const float* noise, const float* noise2, const float* dy,
+                        const float* dlosses, const moe_grads* grads, void* ws, size_t ws_bytes,
+                        void* stream);
 
 /* Kernel timing, a tracing aid (off by default).  moe_profile_enable(1)
  * clears earlier results and starts bracketing every kernel launch of the

@@ -81,9 +81,10 @@ class MoELayer:
 
     # gradient name -> weight it belongs to
     _GRAD_OF = dict(dw_gate="w_gate", db_gate="b_gate", dw_noise="w_noise", dw1="w1",
-                    db1="b1", dw3="w3", dw2="w2", db2="b2", dws1="ws1", dws3="ws3", dws2="ws2")
+                    db1="b1", dw3="w3", dw2="w2", db2="b2", dws1="ws1", dws3="ws3", dws2="ws2",
+                    dw_gate2="w_gate2", dw_noise2="w_noise2")
 
-    def backward(self, x, dy, dlosses=None, noise=None):
+    def backward(self, x, dy, dlosses=None, noise=None, noise2=None):
         """Gradients of sum <dy, y> + sum dlosses * losses (dlosses: 5 values,
         default zeros) through moe_backward; returns a dict of fp32 tensors
         (dx and one per present weight; no db_gate for the sigmoid gate)."""
@@ -92,7 +93,7 @@ class MoELayer:
             size = moe_backward_workspace_size(self.c)
             if size == 0:
                 raise MoEError(MOE_ERR_UNSUPPORTED, "the backward pass does not cover this "
-                               "configuration (flat bf16 layers, sizes multiples of 64)")
+                               "configuration (bf16 or fp32 experts, sizes multiples of 64)")
             self.ws_bwd = torch.empty(size, dtype=torch.uint8, device=self.device)
         if dlosses is None:
             dlosses = torch.zeros(N_LOSSES, dtype=torch.float32, device=self.device)
@@ -103,7 +104,8 @@ class MoELayer:
             if t is None or (g == "db_gate" and int(self.cfg.gate) == 2):
                 continue
             grads[g] = torch.empty(t.shape, dtype=torch.float32, device=self.device)
-        moe_backward(self.c, self.w, x, noise, dy, dlosses, make_grads(**grads), self.ws_bwd)
+        moe_backward(self.c, self.w, x, noise, noise2, dy, dlosses, make_grads(**grads),
+                     self.ws_bwd)
         return grads
 
 

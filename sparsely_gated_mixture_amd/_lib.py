@@ -64,7 +64,8 @@ class MoeDiag(ctypes.Structure):
 class MoeGrads(ctypes.Structure):
     _fields_ = [("dx", _vp), ("dw_gate", _vp), ("db_gate", _vp), ("dw_noise", _vp),
                 ("dw1", _vp), ("db1", _vp), ("dw3", _vp), ("dw2", _vp), ("db2", _vp),
-                ("dws1", _vp), ("dws3", _vp), ("dws2", _vp)]
+                ("dws1", _vp), ("dws3", _vp), ("dws2", _vp), ("dw_gate2", _vp),
+                ("dw_noise2", _vp)]
 
 
 _lib = None
@@ -101,7 +102,7 @@ def load_library():
         [ctypes.POINTER(MoeDiag), P, S, P]
     L.moe_backward_workspace_size.argtypes = [cfgp]
     L.moe_backward_workspace_size.restype = S
-    L.moe_backward.argtypes = [cfgp, ctypes.POINTER(MoeWeights)] + [P] * 4 + \
+    L.moe_backward.argtypes = [cfgp, ctypes.POINTER(MoeWeights)] + [P] * 5 + \
         [ctypes.POINTER(MoeGrads), P, S, P]
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_status_string.restype = ctypes.c_char_p
@@ -284,12 +285,12 @@ def make_grads(**kw) -> MoeGrads:
     return MoeGrads(*[_ptr(kw.get(f)) for f, _ in MoeGrads._fields_])
 
 
-def moe_backward(cfg, weights: MoeWeights, x, noise, dy, dlosses, grads: MoeGrads, ws,
+def moe_backward(cfg, weights: MoeWeights, x, noise, noise2, dy, dlosses, grads: MoeGrads, ws,
                  stream=None):
     c = make_config(cfg)
     wp, wb = _ws(ws)
     _check(load_library().moe_backward(ctypes.byref(c), ctypes.byref(weights), _ptr(x),
-                                       _ptr(noise), _ptr(dy), _ptr(dlosses),
+                                       _ptr(noise), _ptr(noise2), _ptr(dy), _ptr(dlosses),
                                        ctypes.byref(grads), wp, wb, _stream(stream)))
 
 

@@ -363,14 +363,18 @@ moe_status run_gate(const moe_config& c, const Plan& p, const float* x, const fl
   return MOE_OK;
 }
 
+// logits2 (null: the primary's buffer, overwritten) receives the secondary
+// logits; load_g (null: not kept) the per-group secondary loads [a, b].
 moe_status run_gate_hier(const moe_config& c, const Plan& p, const float* x, const float* w_gate,
                          const float* b_gate, const float* w_noise, const float* noise,
                          const float* w_gate2, const float* w_noise2, const float* noise2,
                          int32_t* topk_idx, float* topk_w, float* importance, float* load,
-                         float* gate_stats, void* ws, hipStream_t s) {
+                         float* gate_stats, void* ws, hipStream_t s, float* logits2 = nullptr,
+                         float* load_g = nullptr) {
   const bool noisy = w_noise != nullptr;
   const int a = p.a, b = p.b, k1 = p.k1;
   float* logits = at<float>(ws, p.logits);
+  if (!logits2) logits2 = logits;
   int32_t* prim_idx = at<int32_t>(ws, p.prim_idx);
   float* prim_w = at<float>(ws, p.prim_w);
   // 1. primary gate over the a groups
@@ -449,7 +453,7 @@ moe_status run_gate_hier(const moe_config& c, const Plan& p, const float* x, con
     g.n1 = b;
     g.N = w_noise2 ? 2 * b : b;
     g.K = c.d_model;
-    g.C = logits;
+    g.C = logits2;
     g.ldc = p.ldl2;
     g.tile_expert = t2e;
     g.tile_row0 = t2r;
@@ -463,7 +467,7 @@ moe_status run_gate_hier(const moe_config& c, const Plan& p, const float* x, con
   u.n = b;
   u.k = p.k2;
   u.noisy = w_noise2 != nullptr;
-  u.logits = logits;
+  u.logits = logits2;
   u.ldl = p.ldl2;
   u.noise = noise2;
   u.topk_idx = topk_idx;
@@ -486,7 +490,7 @@ moe_status run_gate_hier(const moe_config& c, const Plan& p, const float* x, con
   const bool both_noisy = noisy && w_noise2 != nullptr;
   HIP_TRY(launch_hier_finalize(u.part_imp, both_noisy ? u.part_load : nullptr, t2e, t2c,
                                g_counts_pre, at<float>(ws, p.prim_load), a, b, importance,
-                               both_noisy ? load : nullptr, s));
+                               both_noisy ? load : nullptr, both_noisy ? load_g : nullptr, s));
   if (gate_stats)
     HIP_TRY(launch_hier_stats(at<float>(ws, p.prim_stats), u.part_stats, t2c, gate_stats, s));
   return MOE_OK;
@@ -704,6 +708,9 @@ struct BwdPlan {
   int M = 0, ldk = 0, splits = 0, tps = 0, hw = 0, hws = 0;
   Region losses, dG, dout, dimp, dload, coef, dlogits, part_db, dpre, a_pre, b_pre, du_perm,
       dx_gate, wt, wpart, a_s, b_s, dout_s, dpre_s, du_s;
+  // two-level layer: secondary logits and their gradients, the split slot
+  // gradients, the factorised load's parts, the secondary rows' dx
+  Region logits2, dlogits2, dG1, dG2, dload_p, dload_g, load_g, du2;
   size_t total = 0;
 };
 
@@ -721,11 +728,12 @@ BwdPlan make_bwd_plan(const moe_config& c) {
   b.losses = w.take(8 * 4);
   b.dG = w.take(A1 * 4);
   b.dout = w.take(A1 * d * esz);
+  const long long ng = b.f.n_gate;  // the flat or primary gate's width
   b.dimp = w.take(n * 4);
   b.dload = w.take(n * 4);
   b.coef = w.take(4 * 4);
   b.dlogits = w.take(T1 * b.f.ldl * 4);
-  b.part_db = w.take((size_t)std::max(1, b.f.nparts) * n * 4);
+  b.part_db = w.take((size_t)std::max(1, b.f.nparts) * ng * 4);
   b.hw = swiglu ? 2 * (int)h : (int)h;  // width of the hidden-layer gradient rows
   b.dpre = w.take(A1 * b.hw * esz);
   if (swiglu) {
@@ -734,12 +742,23 @@ BwdPlan make_bwd_plan(const moe_config& c) {
   }
   b.du_perm = w.take(A1 * d * 4);
   b.dx_gate = w.take(T1 * d * 4);
-  b.M = (int)n * 2;  // dclean | draw columns of dlogits (draw unused when noiseless)
+  b.M = (int)ng * 2;  // dclean | draw columns of dlogits (draw unused when noiseless)
   b.ldk = (int)round_up(b.M, 4);
   b.wt = w.take(d * b.ldk * 4);
   b.splits = gate_wgrad_splits((int)T, (int)d, b.M);
   b.tps = (int)std::max(1LL, (T + b.splits - 1) / b.splits);
   b.wpart = w.take((size_t)b.splits * b.M * d * 4);
+  if (c.n_groups > 0) {
+    const long long rows2 = std::max(1LL, T * b.f.k1);
+    b.logits2 = w.take(rows2 * b.f.ldl2 * 4);
+    b.dlogits2 = w.take(rows2 * b.f.ldl2 * 4);
+    b.dG1 = w.take(rows2 * 4);
+    b.dG2 = w.take(A1 * 4);
+    b.dload_p = w.take(ng * 4);
+    b.dload_g = w.take(n * 4);
+    b.load_g = w.take(n * 4);
+    b.du2 = w.take(rows2 * d * 4);
+  }
   if (c.d_hidden_shared > 0) {
     const long long hs = c.d_hidden_shared;
     b.hws = swiglu ? 2 * (int)hs : (int)hs;
@@ -756,8 +775,6 @@ BwdPlan make_bwd_plan(const moe_config& c) {
 }
 
 moe_status validate_bwd(const moe_config& c) {
-  if (c.n_groups > 0)
-    return fail(MOE_ERR_UNSUPPORTED, "the backward pass covers flat layers (n_groups == 0)");
   if (c.expert_dtype == MOE_FP8)
     return fail(MOE_ERR_UNSUPPORTED, "the backward pass needs bf16 or fp32 experts");
   if (c.d_model % 64 || c.d_hidden % 64 || c.d_hidden_shared % 64)
@@ -1174,8 +1191,9 @@ size_t moe_backward_workspace_size(const moe_config* cfg) {
 }
 
 moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const float* x,
-                        const float* noise, const float* dy, const float* dlosses,
-                        const moe_grads* gr, void* ws, size_t ws_bytes, void* stream) {
+                        const float* noise, const float* noise2, const float* dy,
+                        const float* dlosses, const moe_grads* gr, void* ws, size_t ws_bytes,
+                        void* stream) {
   g_err[0] = 0;
   CHECK(validate(cfg));
   const moe_config& c = *cfg;
@@ -1186,6 +1204,21 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const floa
   const bool swiglu = c.act == MOE_ACT_SWIGLU;
   const bool shared = c.d_hidden_shared > 0;
   const bool noisy = wt->w_noise != nullptr;
+  const bool hier = c.n_groups > 0;
+  const bool noisy2 = hier && wt->w_noise2 != nullptr;
+  const bool has_load = hier ? (noisy && noisy2) : noisy;
+  if (hier) {
+    CHECK(need(wt->w_gate2, "weights->w_gate2"));
+    CHECK(optional(wt->w_noise2, "weights->w_noise2"));
+    if (noisy2) CHECK(need(noise2, "noise2 (required with w_noise2)", c.T == 0));
+    CHECK(need(gr->dw_gate2, "grads->dw_gate2"));
+    if (noisy2) CHECK(need(gr->dw_noise2, "grads->dw_noise2"));
+    const int b2 = c.n_experts / c.n_groups;
+    if ((noisy2 ? 2 * b2 : b2) % 16)
+      return fail(MOE_ERR_UNSUPPORTED,
+                  "the two-level backward needs the secondary gate's logit columns (b, or 2b "
+                  "with noise) to be a multiple of 16");
+  }
   CHECK(need(wt->w1, "weights->w1"));
   CHECK(need(wt->w2, "weights->w2"));
   if (swiglu) {
@@ -1235,15 +1268,22 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const floa
   uint16_t* hidden = at<uint16_t>(ws, p.hidden);
   float* a_pre = swiglu ? at<float>(ws, b.a_pre) : nullptr;
   float* b_pre = swiglu ? at<float>(ws, b.b_pre) : nullptr;
-  CHECK(run_gate(c, p, x, wt->w_gate, wt->b_gate, wt->w_noise, noise, idx, w, imp, ld, stats, ws,
-                 s));
+  float* logits2 = hier ? at<float>(ws, b.logits2) : nullptr;
+  float* load_g = hier ? at<float>(ws, b.load_g) : nullptr;
+  if (hier) {
+    CHECK(run_gate_hier(c, p, x, wt->w_gate, wt->b_gate, wt->w_noise, noise, wt->w_gate2,
+                        wt->w_noise2, noise2, idx, w, imp, ld, stats, ws, s, logits2, load_g));
+  } else {
+    CHECK(run_gate(c, p, x, wt->w_gate, wt->b_gate, wt->w_noise, noise, idx, w, imp, ld, stats,
+                   ws, s));
+  }
   ForwardExtras fx;
   fx.tile_expert = at<int32_t>(ws, p.f_tile_expert);
   fx.tile_row0 = at<int32_t>(ws, p.f_tile_row0);
   fx.tile_count = at<int32_t>(ws, p.f_tile_count);
   fx.losses = at<float>(ws, b.losses);
   fx.importance = imp;
-  fx.load = noisy ? ld : nullptr;
+  fx.load = has_load ? ld : nullptr;
   fx.gate_stats = stats;
   fx.x_bf16 = shared ? at<uint16_t>(ws, p.sh_xb) : nullptr;
   CHECK(run_dispatch(c, p, idx, x, counts_pre, counts, offsets, perm, slot, xperm, ws, s, &fx));
@@ -1317,13 +1357,27 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const floa
   float* coef = at<float>(ws, b.coef);
   float* dlogits = at<float>(ws, b.dlogits);
   HIP_TRY(launch_combine_bwd(dy, yperm, slot, w, T, k, d, dG, dout, f32, s));
-  HIP_TRY(launch_loss_grad(imp, noisy ? ld : nullptr, counts_pre, dlosses, T, k, n,
+  HIP_TRY(launch_loss_grad(imp, has_load ? ld : nullptr, counts_pre, dlosses, T, k, n,
                            c.w_importance, c.w_load, c.alpha_switch, c.w_z, c.w_entropy, dimp,
                            dload, coef, s));
+  // The flat gate, or the two-level layer's primary gate (whose slots carry
+  // the product weights' split gradients and no Importance or entropy term).
+  const int ng = p.n_gate;
+  const int kg = hier ? p.k1 : k;
+  float* dG1 = hier ? at<float>(ws, b.dG1) : nullptr;
+  float* dG2 = hier ? at<float>(ws, b.dG2) : nullptr;
+  float* dload_p = hier && has_load ? at<float>(ws, b.dload_p) : nullptr;
+  float* dload_g = hier && has_load ? at<float>(ws, b.dload_g) : nullptr;
+  if (hier) {
+    HIP_TRY(launch_hier_product_bwd(idx, w, at<float>(ws, p.prim_w), dG, dimp, coef, T, p.k1,
+                                    p.k2, dG1, dG2, s));
+    if (has_load)
+      HIP_TRY(launch_hier_dload(dload, at<float>(ws, p.prim_load), load_g,
+                                at<int32_t>(ws, p.g_counts_pre), p.a, p.b, dload_p, dload_g, s));
+  }
   GateBwdArgs gb{};
   gb.T = T;
-  gb.n = n;
-  gb.k = k;
+  gb.n = ng;
   gb.switch_mode = c.gate == MOE_GATE_SWITCH_TOP1;
   gb.sigmoid_mode = c.gate == MOE_GATE_SIGMOID_BIAS;
   gb.noisy = noisy;
@@ -1331,21 +1385,22 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const floa
   gb.ldl = p.ldl;
   gb.bias = wt->b_gate;
   gb.noise = noise;
-  gb.topk_idx = idx;
-  gb.topk_w = w;
-  gb.dG = dG;
-  gb.dimp = dimp;
-  gb.dload = dload;
-  gb.coef = coef;
+  gb.k = kg;
+  gb.topk_idx = hier ? at<int32_t>(ws, p.prim_idx) : idx;
+  gb.topk_w = hier ? at<float>(ws, p.prim_w) : w;
+  gb.dG = hier ? dG1 : dG;
+  gb.dimp = hier ? nullptr : dimp;
+  gb.dload = hier ? dload_p : (noisy ? dload : nullptr);
+  gb.coef = hier ? coef + 2 : coef;
   gb.dlogits = dlogits;
   gb.ldd = p.ldl;
   gb.part_db = want_db ? at<float>(ws, b.part_db) : nullptr;
   gb.rows_per_block = p.rows_per_block;
   HIP_TRY(launch_gate_bwd(gb, s));
   if (want_db)
-    HIP_TRY(launch_colsum(p.nparts, ColsumVec{gb.part_db, n, gr->db_gate},
+    HIP_TRY(launch_colsum(p.nparts, ColsumVec{gb.part_db, ng, gr->db_gate},
                           ColsumVec{nullptr, 0, nullptr}, ColsumVec{nullptr, 0, nullptr}, s));
-  const int M = noisy ? 2 * n : n;
+  const int M = noisy ? 2 * ng : ng;
   GateWgradArgs gw{};
   gw.x = x;
   gw.dlogits = dlogits;
@@ -1353,7 +1408,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const floa
   gw.T = T;
   gw.d = d;
   gw.M = M;
-  gw.n = n;
+  gw.n = ng;
   gw.splits = b.splits;
   gw.tokens_per_split = b.tps;
   gw.partial = at<float>(ws, b.wpart);
@@ -1362,7 +1417,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const floa
   if (T > 0) {
     const int ldk = (int)round_up(M, 4);
     float* wtr = at<float>(ws, b.wt);
-    HIP_TRY(launch_transpose_gate(wt->w_gate, wt->w_noise, n, d, ldk, wtr, s));
+    HIP_TRY(launch_transpose_gate(wt->w_gate, wt->w_noise, ng, d, ldk, wtr, s));
     GemmF32Args gx{};
     gx.A = dlogits;
     gx.lda = p.ldl;
@@ -1444,7 +1499,79 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const floa
     fs.names[3] = "bwd_shared_dw1";
     CHECK(ffn_bwd(c, fs, s));
   }
-  HIP_TRY(launch_dx_gather(dx_gate, du_s, fb.du, slot, T, k, d, gr->dx, s));
+  float* du2 = nullptr;
+  if (hier) {
+    // Each group's secondary gate over the rows routed to it.
+    const int bb = p.b;
+    float* dlogits2 = at<float>(ws, b.dlogits2);
+    const int32_t* g_perm = at<int32_t>(ws, p.g_perm);
+    const int32_t* g_offsets = at<int32_t>(ws, p.g_offsets);
+    GateBwdArgs g2{};
+    g2.T = T;
+    g2.n = bb;
+    g2.k = p.k2;
+    g2.noisy = noisy2;
+    g2.logits = logits2;
+    g2.ldl = p.ldl2;
+    g2.noise = noise2;
+    g2.topk_idx = idx;
+    g2.dG = dG2;
+    g2.dload = dload_g;
+    g2.coef = coef + 2;
+    g2.dlogits = dlogits2;
+    g2.ldd = p.ldl2;
+    g2.row_token = g_perm;
+    g2.prim_idx = at<int32_t>(ws, p.prim_idx);
+    g2.k1 = p.k1;
+    g2.tile_expert = at<int32_t>(ws, p.t2_expert);
+    g2.tile_row0 = at<int32_t>(ws, p.t2_row0);
+    g2.offsets = g_offsets;
+    g2.tile_count = at<int32_t>(ws, p.t2_count);
+    g2.max_tiles = p.max_tiles2;
+    g2.tile_rows = kSecondaryBM;
+    HIP_TRY(launch_gate_bwd(g2, s));
+    const int K2 = noisy2 ? 2 * bb : bb;
+    // dW_gate2 | dW_noise2 [g] = dlogits2^T x over the group's rows
+    GemmBwdArgs gw2{};
+    gw2.A = (const uint16_t*)x;
+    gw2.lda = d;
+    gw2.rowmap_a = g_perm;
+    gw2.B = (const uint16_t*)dlogits2;
+    gw2.ldb = p.ldl2;
+    gw2.M = d;
+    gw2.N = K2;
+    gw2.C = gr->dw_gate2;
+    gw2.C2 = gr->dw_noise2;
+    gw2.ldc = d;
+    gw2.strideC = (long long)bb * d;
+    gw2.c_split = bb;
+    gw2.offsets = g_offsets;
+    gw2.n_experts = p.a;
+    HIP_TRY(launch_gemm_bwd_f32(gw2, BWD_WGRAD, BEPI_F32, "bwd_gate2_wgrad", s));
+    // the rows' input gradients dlogits2 . [W_gate2; W_noise2][g]
+    du2 = at<float>(ws, b.du2);
+    GemmBwdArgs gx2{};
+    gx2.A = (const uint16_t*)wt->w_gate2;
+    gx2.A2 = (const uint16_t*)wt->w_noise2;
+    gx2.lda = d;
+    gx2.strideA = (long long)bb * d;
+    gx2.k_split = bb;
+    gx2.B = (const uint16_t*)dlogits2;
+    gx2.ldb = p.ldl2;
+    gx2.M = d;
+    gx2.K = K2;
+    gx2.C = du2;
+    gx2.ldc = d;
+    gx2.tile_expert = g2.tile_expert;
+    gx2.tile_row0 = g2.tile_row0;
+    gx2.offsets = g_offsets;
+    gx2.tile_count = g2.tile_count;
+    gx2.max_tiles = p.max_tiles2;
+    gx2.tile_rows = kSecondaryBM;
+    HIP_TRY(launch_gemm_bwd_f32(gx2, BWD_ROWS, BEPI_F32, "bwd_gate2_dx", s));
+  }
+  HIP_TRY(launch_dx_gather(dx_gate, du_s, fb.du, slot, T, k, d, du2,
+                           hier ? at<int32_t>(ws, p.g_slot) : nullptr, p.k1, gr->dx, s));
   return MOE_OK;
 }
 

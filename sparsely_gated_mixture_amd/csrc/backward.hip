@@ -99,6 +99,8 @@ __global__ __launch_bounds__(256) void loss_grad_kernel(
   if (threadIdx.x == 0) {
     coef[0] = T > 0 ? (float)(d3 * w_z / T) : 0.f;
     coef[1] = T > 0 ? (float)(d4 * w_ent / T) : 0.f;
+    coef[2] = coef[0];  // the same z coefficient without an entropy term
+    coef[3] = 0.f;
   }
 }
 
@@ -278,6 +280,8 @@ __global__ __launch_bounds__(256) void dx_gather_kernel(const float* __restrict_
                                                         const float* __restrict__ du_perm,
                                                         const int32_t* __restrict__ slot_pos,
                                                         int T, int k, int d,
+                                                        const float* __restrict__ du2,
+                                                        const int32_t* __restrict__ slot2, int k2,
                                                         float* __restrict__ dx) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -290,6 +294,12 @@ __global__ __launch_bounds__(256) void dx_gather_kernel(const float* __restrict_
 #pragma unroll
       for (int q = 0; q < 4; ++q) acc[q] += v[q];
     }
+    for (int s = 0; s < k2; ++s) {  // the two-level secondary gates' rows
+      const int pos = slot2[(long long)t * k2 + s];
+      const f32x4 v = *(const f32x4*)(du2 + (long long)pos * d + c);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] += v[q];
+    }
     for (int s = 0; s < k; ++s) {
       const int pos = sp[s];
       if (pos < 0) continue;
@@ -299,6 +309,58 @@ __global__ __launch_bounds__(256) void dx_gather_kernel(const float* __restrict_
     }
     *(f32x4*)(dx + (long long)t * d + c) = acc;
   }
+}
+
+// Two-level layer, per token: the gradient of each combined slot's product
+// weight w = w1_s * w2_{s,s2}, gw = dG + dImportance[expert] + c_ent (ln w + 1)
+// (Importance and the entropy are taken over the products), becomes
+// dG1[t,s] = sum over s2 of gw * w2 (in slot order) and dG2[t,s,s2] = gw * w1_s,
+// with w2 = w / w1_s.  One thread per (token, primary slot).
+__global__ __launch_bounds__(256) void hier_product_bwd_kernel(
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w,
+    const float* __restrict__ prim_w, const float* __restrict__ dG,
+    const float* __restrict__ dimp, const float* __restrict__ coef, int T, int k1, int k2,
+    float* __restrict__ dG1, float* __restrict__ dG2) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long long)T * k1) return;
+  const int k = k1 * k2;
+  const long long t = i / k1;
+  const int s = (int)(i % k1);
+  const float c_ent = coef[1];
+  const float w1 = prim_w[i];
+  float acc = 0.f;
+  for (int s2 = 0; s2 < k2; ++s2) {
+    const long long j = t * k + (long long)s * k2 + s2;
+    const float w = topk_w[j];
+    float gw = dG[j] + dimp[topk_idx[j]];
+    if (w > 0.f) gw += c_ent * (logf(w) + 1.f);
+    acc = fmaf(gw, w / w1, acc);
+    dG2[i * k2 + s2] = gw * w1;
+  }
+  dG1[i] = acc;
+}
+
+// Two-level factorised load Load_H[g*b+e] = Load_p[g] Load_g[e] / |X_g|:
+// dLoad_p[g] = sum over e of dLoad_H * Load_g[e] / |X_g| (in e order),
+// dLoad_g[g][e] = dLoad_H * Load_p[g] / |X_g|; zero for a group no token
+// reaches.  One block per group.
+__global__ __launch_bounds__(64) void hier_dload_kernel(const float* __restrict__ dload_h,
+                                                        const float* __restrict__ load_p,
+                                                        const float* __restrict__ load_g,
+                                                        const int32_t* __restrict__ counts,
+                                                        int b, float* __restrict__ dload_p,
+                                                        float* __restrict__ dload_g) {
+  const int g = blockIdx.x;
+  const int cnt = counts[g];
+  const float inv = cnt > 0 ? 1.f / (float)cnt : 0.f;
+  float part = 0.f;
+  for (int e = threadIdx.x; e < b; e += 64) {
+    const float dh = dload_h[(long long)g * b + e];
+    dload_g[(long long)g * b + e] = dh * load_p[g] * inv;
+    part = fmaf(dh, load_g[(long long)g * b + e], part);
+  }
+  const float tot = wave_sum_dpp(part);
+  if (threadIdx.x == 0) dload_p[g] = tot * inv;
 }
 
 // hid = bf16(silu(a) * b) with the forward epilogue's expression.
@@ -391,12 +453,34 @@ hipError_t launch_seg_colsum(const void* src, int src_f32, long long ld, const i
 }
 
 hipError_t launch_dx_gather(const float* dx_gate, const float* dx_shared, const float* du_perm,
-                            const int32_t* slot_pos, int T, int k, int d, float* dx,
-                            hipStream_t s) {
+                            const int32_t* slot_pos, int T, int k, int d, const float* du2,
+                            const int32_t* slot2, int k2, float* dx, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   ProfScope ps("bwd_dx_gather", s);
   dx_gather_kernel<<<dim3((T + 3) / 4), dim3(256), 0, s>>>(dx_gate, dx_shared, du_perm, slot_pos,
-                                                           T, k, d, dx);
+                                                           T, k, d, du2, slot2, du2 ? k2 : 0, dx);
+  return hipGetLastError();
+}
+
+hipError_t launch_hier_product_bwd(const int32_t* topk_idx, const float* topk_w,
+                                   const float* prim_w, const float* dG, const float* dimp,
+                                   const float* coef, int T, int k1, int k2, float* dG1,
+                                   float* dG2, hipStream_t s) {
+  const long long rows = (long long)T * k1;
+  if (rows <= 0) return hipSuccess;
+  ProfScope ps("bwd_hier_product", s);
+  hier_product_bwd_kernel<<<dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s>>>(
+      topk_idx, topk_w, prim_w, dG, dimp, coef, T, k1, k2, dG1, dG2);
+  return hipGetLastError();
+}
+
+hipError_t launch_hier_dload(const float* dload_h, const float* load_p, const float* load_g,
+                             const int32_t* counts, int a, int b, float* dload_p,
+                             float* dload_g, hipStream_t s) {
+  if (a <= 0) return hipSuccess;
+  ProfScope ps("bwd_hier_dload", s);
+  hier_dload_kernel<<<dim3(a), dim3(64), 0, s>>>(dload_h, load_p, load_g, counts, b, dload_p,
+                                                 dload_g);
   return hipGetLastError();
 }
 

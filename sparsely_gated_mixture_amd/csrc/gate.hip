@@ -332,9 +332,19 @@ __global__ __launch_bounds__(NW * 64) void gate_bwd_kernel(const GateBwdArgs p) 
   const int n = p.n, k = p.k;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int part = blockIdx.x;
-  const int row_begin = part * p.rows_per_block;
-  const int row_end = min(row_begin + p.rows_per_block, p.T);
+  const bool grouped = p.tile_expert != nullptr;
+  int row_begin, row_end, g = 0;
+  if (grouped) {
+    if (part >= *p.tile_count) return;
+    g = p.tile_expert[part];
+    row_begin = p.tile_row0[part];
+    row_end = min(row_begin + p.tile_rows, p.offsets[g + 1]);
+  } else {
+    row_begin = part * p.rows_per_block;
+    row_end = min(row_begin + p.rows_per_block, p.T);
+  }
   const float c_z = p.coef[0], c_ent = p.coef[1];
+  const float* dload_v = (p.noisy && p.dload) ? p.dload + (long long)g * n : nullptr;
 
   float bias[NPL], dimp[NPL], dload[NPL], dbacc[NPL];
 #pragma unroll
@@ -342,12 +352,30 @@ __global__ __launch_bounds__(NW * 64) void gate_bwd_kernel(const GateBwdArgs p) 
     const int j = lane + 64 * q;
     const bool ok = j < n;
     bias[q] = (p.bias && ok) ? p.bias[j] : 0.f;
-    dimp[q] = ok ? p.dimp[j] : 0.f;
-    dload[q] = (p.noisy && ok) ? p.dload[j] : 0.f;
+    dimp[q] = (p.dimp && ok) ? p.dimp[j] : 0.f;
+    dload[q] = (dload_v && ok) ? dload_v[j] : 0.f;
     dbacc[q] = 0.f;
   }
 
   for (int r = row_begin + wave; r < row_end; r += NW) {
+    // Where row r's noise, slots and slot gradients live: flat, token r;
+    // grouped, the (token, primary slot) pair dispatched to row r, whose
+    // secondary slots are the combined slots s*k .. s*k+k-1 of the token.
+    long long noise_row, slot_base, dg_base;
+    int id_off = 0;
+    if (grouped) {
+      const int t = p.row_token[r];
+      int sl = 0;
+      for (int q = 0; q < p.k1; ++q)
+        if (p.prim_idx[(long long)t * p.k1 + q] == g) sl = q;
+      noise_row = ((long long)t * p.k1 + sl) * n;
+      slot_base = (long long)t * p.k1 * k + (long long)sl * k;
+      dg_base = ((long long)t * p.k1 + sl) * k;
+      id_off = g * n;
+    } else {
+      noise_row = (long long)r * n;
+      slot_base = dg_base = (long long)r * k;
+    }
     const float* lg = p.logits + (long long)r * p.ldl;
     float c[NPL], cl[NPL], sp[NPL], hv[NPL], rw[NPL], zn[NPL];
 #pragma unroll
@@ -356,7 +384,7 @@ __global__ __launch_bounds__(NW * 64) void gate_bwd_kernel(const GateBwdArgs p) 
       const bool ok = j < n;
       c[q] = ok ? lg[j] : 0.f;
       rw[q] = (ok && p.noisy) ? lg[n + j] : 0.f;
-      zn[q] = (ok && p.noisy) ? p.noise[(long long)r * n + j] : 0.f;
+      zn[q] = (ok && p.noisy) ? p.noise[noise_row + j] : 0.f;
       cl[q] = c[q] + bias[q];
       sp[q] = 1.f;
       hv[q] = cl[q];
@@ -366,9 +394,8 @@ __global__ __launch_bounds__(NW * 64) void gate_bwd_kernel(const GateBwdArgs p) 
       }
     }
     // Slots: lane s < k holds slot s.
-    const int my_j = lane < k ? p.topk_idx[(long long)r * k + lane] : 0;
-    const float my_w = lane < k ? p.topk_w[(long long)r * k + lane] : 0.f;
-    const float my_dg = lane < k ? p.dG[(long long)r * k + lane] : 0.f;
+    const int my_j = lane < k ? p.topk_idx[slot_base + lane] - id_off : 0;
+    const float my_dg = lane < k ? p.dG[dg_base + lane] : 0.f;
     uint32_t kept = 0;
     for (int s = 0; s < k; ++s) {
       const int js = readlane_i(my_j, s);
@@ -384,6 +411,18 @@ __global__ __launch_bounds__(NW * 64) void gate_bwd_kernel(const GateBwdArgs p) 
       }
       return v;
     };
+    // The slot's gate weight: the forward's (flat), or the secondary
+    // softmax over the kept values recomputed with the forward's arithmetic
+    // (grouped: the stored weight is the product with the primary weight).
+    float my_w;
+    if (grouped) {
+      const float v0 = h_of(readlane_i(my_j, 0));
+      const float hj = h_of(my_j);
+      const float e = lane < k ? expf(hj - v0) : 0.f;
+      my_w = e / wave_sum_dpp(e);
+    } else {
+      my_w = lane < k ? p.topk_w[slot_base + lane] : 0.f;
+    }
 
     float dH[NPL];
 #pragma unroll
@@ -417,7 +456,7 @@ __global__ __launch_bounds__(NW * 64) void gate_bwd_kernel(const GateBwdArgs p) 
     } else {
       float gg = 0.f;
       if (lane < k) {
-        gg = my_dg + p.dimp[my_j];
+        gg = my_dg + (p.dimp ? p.dimp[my_j] : 0.f);
         if (my_w > 0.f) gg += c_ent * (hw_log(my_w) + 1.f);
       }
       const float dot = wave_sum_dpp(lane < k ? my_w * gg : 0.f);
@@ -596,7 +635,8 @@ __global__ void hier_finalize_kernel(const float* __restrict__ part_imp,
                                      const int32_t* __restrict__ tile_count,
                                      const int32_t* __restrict__ group_counts,
                                      const float* __restrict__ load_primary, int a, int b,
-                                     float* __restrict__ importance, float* __restrict__ load) {
+                                     float* __restrict__ importance, float* __restrict__ load,
+                                     float* __restrict__ load_g) {
   const int id = blockIdx.x * blockDim.x + threadIdx.x;
   if (id >= a * b) return;
   const int g = id / b, e = id % b;
@@ -613,6 +653,7 @@ __global__ void hier_finalize_kernel(const float* __restrict__ part_imp,
     if (part_load) sl += (double)part_load[(long long)t * b + e];
   }
   importance[id] = (float)si;
+  if (load_g) load_g[id] = (float)sl;
   if (load) {
     const int cnt = group_counts[g];
     load[id] = cnt > 0 ? (float)((double)load_primary[g] * sl / (double)cnt) : 0.f;
@@ -655,7 +696,7 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_gate_bwd(const GateBwdArgs& a, hipStream_t s) {
-  const int grid = (a.T + a.rows_per_block - 1) / a.rows_per_block;
+  const int grid = a.tile_expert ? a.max_tiles : (a.T + a.rows_per_block - 1) / a.rows_per_block;
   if (grid <= 0) return hipSuccess;
   const int npl = (a.n + 63) / 64;
   if (npl <= 1) return launch_gate_bwd_t<1>(a, grid, s);
@@ -690,13 +731,14 @@ hipError_t launch_hier_stats(const float* prim, const float* part, const int32_t
 hipError_t launch_hier_finalize(const float* part_imp, const float* part_load,
                                 const int32_t* tile_expert, const int32_t* tile_count,
                                 const int32_t* group_counts, const float* load_primary, int a,
-                                int b, float* importance, float* load, hipStream_t s) {
+                                int b, float* importance, float* load, float* load_g,
+                                hipStream_t s) {
   const int total = a * b;
   if (total <= 0) return hipSuccess;
   ProfScope ps("hier_finalize", s);
   hier_finalize_kernel<<<dim3((total + 255) / 256), dim3(256), 0, s>>>(
       part_imp, part_load, tile_expert, tile_count, group_counts, load_primary, a, b,
-      importance, load);
+      importance, load, load_g);
   return hipGetLastError();
 }
 

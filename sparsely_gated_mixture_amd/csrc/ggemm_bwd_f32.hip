@@ -72,8 +72,9 @@ __global__ __launch_bounds__(kThreads) void ggemm_bwd_f32_kernel(GemmBwdArgs p) 
     const int k = k_lo + step * kBK + kr;
     ra = f32x4{0.f, 0.f, 0.f, 0.f};
     if (k < k_hi && m0 + cc < p.M) {
+      const long long ka = p.rowmap_a ? (long long)p.rowmap_a[k] : (long long)k;
       const float* src = (A2 && k >= p.k_split) ? A2 + (long long)(k - p.k_split) * p.lda
-                                                : A + (long long)k * p.lda;
+                                                : A + ka * p.lda;
       ra = *(const f32x4*)(src + m0 + cc);
     }
     rb = f32x4{0.f, 0.f, 0.f, 0.f};

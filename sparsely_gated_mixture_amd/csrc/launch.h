@@ -112,6 +112,7 @@ enum BwdEpi { BEPI_F32 = 0, BEPI_RELU_MASK = 1, BEPI_SWIGLU = 2 };
 struct GemmBwdArgs {
   const uint16_t* A;
   const uint16_t* A2;
+  const int32_t* rowmap_a;  // fp32 WGRAD only: A's row k is rowmap_a[k] (null: k)
   long long lda, strideA;
   int k_split;
   const uint16_t* B;
@@ -187,12 +188,18 @@ struct TopkArgs {
 // registers).  The host's rows-per-block is a multiple of this.
 inline int topk_waves(int n) { return (n + 63) / 64 <= 8 ? 16 : 8; }
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
-// Backward of the flat gate (one wavefront per token row; rows_per_block a
-// multiple of topk_waves(n)).  Reads the forward's logits (clean without the
-// bias | raw, row stride ldl), bias, noise, topk_idx / topk_w, the combine's
-// dG [T, k], dimp / dload [n] and coef = {c_z, c_ent}; writes dlogits [T,
-// ldd] (dL/d clean | dL/d raw) and, if part_db, per-block column sums of the
-// clean part [nblocks, n].
+// Backward of a gate, one wavefront per row.  Flat mode: row r is token r
+// (rows_per_block a multiple of topk_waves(n)); reads the forward's logits
+// (clean without the bias | raw, row stride ldl), bias, noise [T, n],
+// topk_idx / topk_w [T, k], the slot gradients dG [T, k], dimp [n] (null: 0),
+// dload [n] and coef = {c_z, c_ent}; writes dlogits [rows, ldd] (dL/d clean |
+// dL/d raw, zero-padded) and, if part_db, per-block column sums of the clean
+// part [nblocks, n].  Grouped mode (tile_expert != null: a two-level
+// secondary gate): rows are the group dispatch's (token, primary slot)
+// pairs in tiles of tile_rows; noise [T, k1, n]; the slots are the token's
+// combined slots s*k .. s*k+k-1 of topk_idx [T, k1*k] (ids g*n + e); the
+// secondary weights are recomputed from the logits; dG [T, k1, k]; dload
+// [groups, n].
 struct GateBwdArgs {
   int T, n, k, switch_mode, sigmoid_mode, noisy;
   const float* logits;
@@ -209,6 +216,16 @@ struct GateBwdArgs {
   long long ldd;
   float* part_db;
   int rows_per_block;
+  // grouped mode
+  const int32_t* row_token;
+  const int32_t* prim_idx;
+  int k1;
+  const int32_t* tile_expert;
+  const int32_t* tile_row0;
+  const int32_t* offsets;
+  const int32_t* tile_count;
+  int max_tiles;
+  int tile_rows;
 };
 hipError_t launch_gate_bwd(const GateBwdArgs& a, hipStream_t s);
 // out[j] = sum over parts p < nparts of part[p*n + j] (double sum, fixed
@@ -228,10 +245,12 @@ hipError_t launch_hier_stats(const float* prim, const float* part, const int32_t
 // Two-level aux vectors: per-tile partials of the secondary gate are summed
 // per group (tiles of a group are consecutive), then combined with the
 // primary vectors: load[g*b+e] = load_p[g]*load_g[e]/|X_g|.
+// load_g (may be null) receives the per-group secondary loads [a, b].
 hipError_t launch_hier_finalize(const float* part_imp, const float* part_load,
                                 const int32_t* tile_expert, const int32_t* tile_count,
                                 const int32_t* group_counts, const float* load_primary, int a,
-                                int b, float* importance, float* load, hipStream_t s);
+                                int b, float* importance, float* load, float* load_g,
+                                hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Dispatch.
@@ -296,8 +315,9 @@ hipError_t launch_combine_bwd(const float* dy, const float* y_perm, const int32_
                               const float* topk_w, int T, int k, int d, float* dG, void* dout,
                               int dout_f32, hipStream_t s);
 // dimp = dl0 w_imp dCV^2(importance) + dl2 alpha n f / T, dload = dl1 w_load
-// dCV^2(load) (skipped when load is null), coef = {dl3 w_z / T, dl4 w_ent / T};
-// dlosses is a device vector of 5.
+// dCV^2(load) (skipped when load is null), coef = {dl3 w_z / T, dl4 w_ent / T,
+// dl3 w_z / T, 0} (the last pair for a gate without an entropy term of its
+// own); dlosses is a device vector of 5.
 hipError_t launch_loss_grad(const float* importance, const float* load,
                             const int32_t* counts_pre, const float* dlosses, int T, int k, int n,
                             float w_imp, float w_load, float alpha, float w_z, float w_ent,
@@ -323,10 +343,23 @@ hipError_t launch_transpose_gate(const float* w_gate, const float* w_noise, int 
 // or fp32 when src_f32).
 hipError_t launch_seg_colsum(const void* src, int src_f32, long long ld, const int32_t* offsets,
                              int n_seg, int N, float* out, hipStream_t s);
-// dx[t] = dx_gate[t] (+ dx_shared[t]) + sum over kept slots of du_perm[row].
+// dx[t] = dx_gate[t] (+ dx_shared[t]) (+ the two-level secondary gates' rows
+// du2[slot2[t, s]], s < k2) + sum over kept slots of du_perm[row].
 hipError_t launch_dx_gather(const float* dx_gate, const float* dx_shared, const float* du_perm,
-                            const int32_t* slot_pos, int T, int k, int d, float* dx,
-                            hipStream_t s);
+                            const int32_t* slot_pos, int T, int k, int d, const float* du2,
+                            const int32_t* slot2, int k2, float* dx, hipStream_t s);
+// Two-level layer: the product weights' gradients split into the primary
+// slots' dG1 [T, k1] and the secondary slots' dG2 [T, k1, k2] (coef[1] =
+// c_ent, dimp over the a*b experts).
+hipError_t launch_hier_product_bwd(const int32_t* topk_idx, const float* topk_w,
+                                   const float* prim_w, const float* dG, const float* dimp,
+                                   const float* coef, int T, int k1, int k2, float* dG1,
+                                   float* dG2, hipStream_t s);
+// Two-level layer: dLoad_H [a*b] into dLoad_p [a] and dLoad_g [a, b] through
+// Load_H = Load_p Load_g / |X_g| (counts = |X_g|).
+hipError_t launch_hier_dload(const float* dload_h, const float* load_p, const float* load_g,
+                             const int32_t* counts, int a, int b, float* dload_p,
+                             float* dload_g, hipStream_t s);
 // hid[i] = bf16(silu(a[i]) * b[i]) for i < elems (a multiple of 4).
 hipError_t launch_swiglu_hidden(const float* a, const float* b, long long elems, uint16_t* hid,
                                 hipStream_t s);

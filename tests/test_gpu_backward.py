@@ -59,13 +59,27 @@ CASES = {
     "f32_capacity": MoEConfig("bwd_f32_capacity", T=300, d_model=64, d_hidden=192, n_experts=8,
                               k=2, expert_dtype=DTYPE_F32, capacity_factor=0.9,
                               expert_bias_std=0.1, seed=2107),
+    # the two-level layer: 8 groups of 8 (noisy), 4 groups of 16 (clean, fp32 experts)
+    "two_level": MoEConfig("bwd_two_level", T=320, d_model=128, d_hidden=128, n_experts=64,
+                           k=4, n_groups=8, k_groups=2, seed=2108),
+    "two_level_clean_f32": MoEConfig("bwd_two_level_clean", T=200, d_model=64, d_hidden=64,
+                                     n_experts=64, k=4, n_groups=4, k_groups=2, noisy=False,
+                                     expert_dtype=DTYPE_F32, seed=2109),
 }
 
 GRAD_OF = dict(dw_gate="w_gate", db_gate="b_gate", dw_noise="w_noise", dw1="w1", db1="b1",
-               dw3="w3", dw2="w2", db2="b2", dws1="ws1", dws3="ws3", dws2="ws2")
+               dw3="w3", dw2="w2", db2="b2", dws1="ws1", dws3="ws3", dws2="ws2",
+               dw_gate2="w_gate2", dw_noise2="w_noise2")
 
 
 def _oracle_backward(cfg, h, dy, dl):
+    if cfg.hierarchical:
+        return oracle.backward_hier(
+            h["x"], h["w_gate"], h.get("w_noise"), h.get("noise"), cfg.k_groups, h["w_gate2"],
+            h.get("w_noise2"), h.get("noise2"), cfg.k2, h["w1"], h["w2"], dy, dl,
+            b1=h.get("b1"), b2=h.get("b2"), bf16=cfg.expert_dtype != DTYPE_F32,
+            w_importance=cfg.w_importance, w_load=cfg.w_load, alpha=cfg.alpha_switch,
+            w_z=cfg.w_z, w_entropy=cfg.w_entropy)
     return oracle.backward(
         h["x"], h["w_gate"], cfg.k, h["w1"], h["w2"], dy, dl, b_gate=h.get("b_gate"),
         w_noise=h.get("w_noise"), noise=h.get("noise"), b1=h.get("b1"), w3=h.get("w3"),
@@ -90,7 +104,7 @@ def _run(cfg, T=None):
     dy, dl = make_grad_inputs(cfg, device="cuda", T=T)
     layer = MoELayer(cfg.replace(T=inp["x"].shape[0]), inp)
     torch.cuda.synchronize()
-    g = layer.backward(inp["x"], dy, dl, inp.get("noise"))
+    g = layer.backward(inp["x"], dy, dl, inp.get("noise"), inp.get("noise2"))
     torch.cuda.synchronize()
     return inp, dy, dl, layer, {k: v.cpu().double().numpy() for k, v in g.items()}
 
@@ -98,7 +112,7 @@ def _run(cfg, T=None):
 def _compare(cfg, inp, dy, dl, got, check_rank_k=True):
     h = {k: to_numpy64(v) for k, v in inp.items() if v is not None}
     ref = _oracle_backward(cfg, h, to_numpy64(dy), to_numpy64(dl))
-    if check_rank_k and h.get("w_noise") is not None:
+    if check_rank_k and h.get("w_noise") is not None and not cfg.hierarchical:
         assert _rank_k_unambiguous(ref["fwd"]["gate"].H, cfg.k), \
             "the case's inputs have a near-tie at rank k: pick another seed"
     tol = TOL_F32 if cfg.expert_dtype == DTYPE_F32 else TOL_BF16
@@ -136,10 +150,11 @@ def test_backward_parity(case):
     # the recomputed routing is the forward's: compare with the oracle's
     n, k, T = cfg.n_experts, cfg.k, cfg.T
     idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
-    layer.forward(inp["x"], inp.get("noise"), diag=dict(topk_idx=idx))
+    layer.forward(inp["x"], inp.get("noise"), inp.get("noise2"), diag=dict(topk_idx=idx))
     torch.cuda.synchronize()
     ref = _compare(cfg, inp, dy, dl, got)
-    np.testing.assert_array_equal(idx.cpu().numpy(), ref["fwd"]["gate"].topk_idx)
+    orc_idx = ref["fwd"]["gate"]["topk_idx"] if cfg.hierarchical else ref["fwd"]["gate"].topk_idx
+    np.testing.assert_array_equal(idx.cpu().numpy(), orc_idx)
     if cfg.capacity_factor > 0:
         assert (ref["fwd"]["dispatch"]["slot_pos"] < 0).any(), "the case should drop slots"
 
@@ -178,7 +193,7 @@ def test_backward_upstream_losses_only():
     _compare(cfg, inp, dy, dl, got)
 
 
-@pytest.mark.parametrize("name", ["lm_layer", "switch_cf"])
+@pytest.mark.parametrize("name", ["lm_layer", "switch_cf", "hierarchical"])
 def test_backward_full_size(name):
     """The whole workload at its full size, every gradient against the
     oracle's.  These batches hold a few tokens whose k+1-th and k+2-th gate
@@ -189,7 +204,8 @@ def test_backward_full_size(name):
         f"n={cfg.n_experts} k={cfg.k}")
     inp, dy, dl, layer, got = _run(cfg)
     idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
-    layer.forward(inp["x"], inp.get("noise"), diag=dict(topk_idx=idx))
+    layer.forward(inp["x"], inp.get("noise"), inp.get("noise2"), diag=dict(topk_idx=idx))
     torch.cuda.synchronize()
     ref = _compare(cfg, inp, dy, dl, got, check_rank_k=False)
-    np.testing.assert_array_equal(idx.cpu().numpy(), ref["fwd"]["gate"].topk_idx)
+    orc_idx = ref["fwd"]["gate"]["topk_idx"] if cfg.hierarchical else ref["fwd"]["gate"].topk_idx
+    np.testing.assert_array_equal(idx.cpu().numpy(), orc_idx)
