@@ -25,6 +25,12 @@ HBM.  Prints one JSON line:
 times moe_backward instead (one step: the forward's routing and activations
 recomputed, then every gradient) and prints one JSON line of the same shape,
 its cpu_baseline the oracle's backward on a bounded token sample.
+
+    python bench.py --train [--steps K] [--warmup W] [--workload lm_layer]
+
+times a training step: moe_forward_train (the forward, y and losses, keeping
+its intermediates) then moe_backward_saved (every gradient from them); same
+line shape, same cpu_baseline (the oracle's backward includes its forward).
 """
 from __future__ import annotations
 
@@ -264,6 +270,8 @@ def main():
                     help="time eager launches only (default: also replay a HIP graph)")
     ap.add_argument("--backward", action="store_true",
                     help="time moe_backward (forward recompute + every gradient)")
+    ap.add_argument("--train", action="store_true",
+                    help="time moe_forward_train + moe_backward_saved (one training step)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (256 MiB read, "
                          "256 MiB written, 5 launches) for scaling HBM byte counters")
@@ -281,8 +289,8 @@ def main():
 
     cfg = PRESETS[args.workload]
     torch.cuda.set_device(0)
-    if args.backward:
-        bench_backward(args, cfg)
+    if args.backward or args.train:
+        bench_backward(args, cfg, train=args.train)
         return
     log(f"[bench] workload {cfg.name}: T={cfg.T} d={cfg.d_model} h={cfg.d_hidden} "
         f"n={cfg.n_experts} k={cfg.k}")
@@ -424,12 +432,14 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def bench_backward(args, cfg):
-    """moe_backward timed like the forward (eager launches; per-kernel events
-    in a second pass), one JSON line."""
+def bench_backward(args, cfg, train=False):
+    """moe_backward (train: moe_forward_train + moe_backward_saved) timed
+    like the forward (eager launches; per-kernel events in a second pass),
+    one JSON line."""
     import sparsely_gated_mixture_amd as moe
     from sparsely_gated_mixture_amd.workloads import make_grad_inputs, make_inputs
-    log(f"[bench] backward, workload {cfg.name}: T={cfg.T} d={cfg.d_model} h={cfg.d_hidden} "
+    what = "training step" if train else "backward"
+    log(f"[bench] {what}, workload {cfg.name}: T={cfg.T} d={cfg.d_model} h={cfg.d_hidden} "
         f"n={cfg.n_experts} k={cfg.k}")
     inp = make_inputs(cfg, device="cuda")
     dy, dl = make_grad_inputs(cfg, device="cuda")
@@ -437,8 +447,14 @@ def bench_backward(args, cfg):
     layer = moe.MoELayer(cfg, inp)
     T, n, k = cfg.T, cfg.n_experts, cfg.k
 
+    y = torch.empty((T, cfg.d_model), dtype=torch.float32, device="cuda")
+    losses = torch.empty(moe.N_LOSSES, dtype=torch.float32, device="cuda")
+    x, noise, noise2 = inp["x"], inp.get("noise"), inp.get("noise2")
+
     def step():
-        return layer.backward(inp["x"], dy, dl, inp.get("noise"), inp.get("noise2"))
+        if train:
+            layer.forward_train(x, noise, noise2, y=y, losses=losses)
+        return layer.backward(x, dy, dl, noise, noise2, saved=train)
 
     for _ in range(args.warmup):
         grads = step()
@@ -447,8 +463,11 @@ def bench_backward(args, cfg):
     g = moe.make_grads(**grads)
 
     def eager_step():
-        moe.moe_backward(layer.c, layer.w, inp["x"], inp.get("noise"), inp.get("noise2"), dy, dl,
-                         g, layer.ws_bwd)
+        if train:
+            moe.moe_forward_train(layer.c, layer.w, x, noise, noise2, y, losses, layer.ws_bwd)
+            moe.moe_backward_saved(layer.c, layer.w, x, noise, noise2, dy, dl, g, layer.ws_bwd)
+        else:
+            moe.moe_backward(layer.c, layer.w, x, noise, noise2, dy, dl, g, layer.ws_bwd)
 
     def timed(fn):
         torch.cuda.synchronize()
@@ -465,7 +484,7 @@ def bench_backward(args, cfg):
     moe.moe_profile_enable(False)
     moe.moe_profile_collect()
     elapsed = timed(eager_step)
-    log(f"[bench] backward eager: {elapsed / args.steps * 1e6:.1f} us/step, "
+    log(f"[bench] {what} eager: {elapsed / args.steps * 1e6:.1f} us/step, "
         f"{T * args.steps / elapsed / 1e6:.2f} M tokens/s")
     moe.moe_profile_enable(True)
     prof_elapsed = timed(eager_step)
@@ -501,16 +520,20 @@ def bench_backward(args, cfg):
             + (f"  {e['TFLOP_s']:7.1f} TFLOP/s" if "TFLOP_s" in e else ""))
     dname = dominant[0]
     roofline = dict(kernels[dname]["roofline"])
-    roofline.update(kernel=dname, traffic=TRAFFIC_BYTES.get((cfg.name + ":bwd", dname)),
+    roofline.update(kernel=dname, traffic=TRAFFIC_BYTES.get((cfg.name + ":bwd", dname))
+                    if not train else TRAFFIC_BYTES.get((cfg.name + ":train", dname)),
                     algo_bytes_per_launch=kernels[dname]["algo_bytes"],
                     avg_us=kernels[dname]["avg_us"])
+    metric = ("MoE-layer training step (forward + all gradients) tokens/sec at 1 GPU" if train
+              else "MoE-layer backward (forward recompute + all gradients) tokens/sec at 1 GPU")
     result = {
-        "metric": "MoE-layer backward (forward recompute + all gradients) tokens/sec at 1 GPU",
+        "metric": metric,
         "value": T * args.steps / elapsed, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": elapsed / args.steps * 1e3,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": cfg.name + " backward", "T": T, "d_model": cfg.d_model,
+        "config": {"workload": cfg.name + (" training step" if train else " backward"), "T": T,
+                   "d_model": cfg.d_model,
                    "d_hidden": cfg.d_hidden, "n_experts": n, "k": k, "gate": gate_text(cfg),
                    "gradients": "fp32; expert products bf16 MFMA with fp32 accumulation",
                    "rows": rows, "nonempty_experts": nonempty, "parallelism": "none (1 GPU)"},

@@ -365,6 +365,30 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* weights, const
                         const float* dlosses, const moe_grads* grads, void* ws, size_t ws_bytes,
                         void* stream);
 
+/* A training step in two calls, with no forward recomputation: the layer
+ * forward of moe_forward that also keeps, in ws, every intermediate the
+ * backward reads (routing, merged batches, hidden activations, gate logits).
+ * Same definition and arguments as moe_forward (no diag); the routing and
+ * losses are moe_forward's bit for bit; y agrees with moe_forward's to fp32
+ * rounding (for SwiGLU bf16 experts the hidden value comes from the two fp32
+ * pre-activations kept for the backward).
+ * ws: moe_backward_workspace_size(cfg) bytes, owned by the caller and kept
+ * untouched until the matching moe_backward_saved. */
+moe_status moe_forward_train(const moe_config* cfg, const moe_weights* weights, const float* x,
+                             const float* noise, const float* noise2, float* y, float* losses,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* The gradients of moe_backward from the intermediates the last
+ * moe_forward_train left in ws.  Precondition (not checkable here): the
+ * same cfg, weights, x, noise, noise2 and ws as that call, none modified
+ * since, and the call ordered after it (same stream, or synchronised).  The
+ * result is then moe_backward's bit for bit.  Arguments and errors as
+ * moe_backward. */
+moe_status moe_backward_saved(const moe_config* cfg, const moe_weights* weights, const float* x,
+                              const float* noise, const float* noise2, const float* dy,
+                              const float* dlosses, const moe_grads* grads, void* ws,
+                              size_t ws_bytes, void* stream);
+
 /* Kernel timing, a tracing aid (off by default).  moe_profile_enable(1)
  * clears earlier results and starts bracketing every kernel launch of the
  * library with two HIP events recorded on that launch's stream;

@@ -14,7 +14,8 @@ from ._lib import (EXPORTS, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTE
                    MoeGrads, MoeWeights, load_library, make_config, make_diag, make_grads,
                    make_weights, moe_aux_loss, moe_backward, moe_backward_workspace_size,
                    moe_combine, moe_dispatch, moe_expert_ffn,
-                   moe_fp8_weight_bytes, moe_forward, moe_pack_fp8_weights,
+                   moe_backward_saved, moe_fp8_weight_bytes, moe_forward,
+                   moe_forward_train, moe_pack_fp8_weights,
                    moe_gate, moe_gate_hier, moe_last_error, moe_profile_collect,
                    moe_profile_enable, moe_profile_entry, moe_router_bias_update,
                    moe_shared_ffn, moe_status_string, moe_workspace_size)
@@ -84,10 +85,7 @@ class MoELayer:
                     db1="b1", dw3="w3", dw2="w2", db2="b2", dws1="ws1", dws3="ws3", dws2="ws2",
                     dw_gate2="w_gate2", dw_noise2="w_noise2")
 
-    def backward(self, x, dy, dlosses=None, noise=None, noise2=None):
-        """Gradients of sum <dy, y> + sum dlosses * losses (dlosses: 5 values,
-        default zeros) through moe_backward; returns a dict of fp32 tensors
-        (dx and one per present weight; no db_gate for the sigmoid gate)."""
+    def _bwd_ws(self):
         import torch
         if getattr(self, "ws_bwd", None) is None:
             size = moe_backward_workspace_size(self.c)
@@ -95,6 +93,27 @@ class MoELayer:
                 raise MoEError(MOE_ERR_UNSUPPORTED, "the backward pass does not cover this "
                                "configuration (bf16 or fp32 experts, sizes multiples of 64)")
             self.ws_bwd = torch.empty(size, dtype=torch.uint8, device=self.device)
+        return self.ws_bwd
+
+    def forward_train(self, x, noise=None, noise2=None, y=None, losses=None):
+        """The forward through moe_forward_train: y and losses as ``forward``,
+        with the intermediates kept for ``backward(..., saved=True)``."""
+        import torch
+        if y is None:
+            y = torch.empty((self.c.T, self.c.d_model), dtype=torch.float32, device=self.device)
+        if losses is None:
+            losses = torch.empty(N_LOSSES, dtype=torch.float32, device=self.device)
+        moe_forward_train(self.c, self.w, x, noise, noise2, y, losses, self._bwd_ws())
+        return y, losses
+
+    def backward(self, x, dy, dlosses=None, noise=None, noise2=None, saved=False):
+        """Gradients of sum <dy, y> + sum dlosses * losses (dlosses: 5 values,
+        default zeros); returns a dict of fp32 tensors (dx and one per present
+        weight; no db_gate for the sigmoid gate).  saved=False: moe_backward
+        (recomputes the forward); saved=True: moe_backward_saved, after a
+        ``forward_train`` on the same inputs."""
+        import torch
+        ws = self._bwd_ws()
         if dlosses is None:
             dlosses = torch.zeros(N_LOSSES, dtype=torch.float32, device=self.device)
         grads = {"dx": torch.empty((self.c.T, self.c.d_model), dtype=torch.float32,
@@ -104,10 +123,9 @@ class MoELayer:
             if t is None or (g == "db_gate" and int(self.cfg.gate) == 2):
                 continue
             grads[g] = torch.empty(t.shape, dtype=torch.float32, device=self.device)
-        moe_backward(self.c, self.w, x, noise, noise2, dy, dlosses, make_grads(**grads),
-                     self.ws_bwd)
+        call = moe_backward_saved if saved else moe_backward
+        call(self.c, self.w, x, noise, noise2, dy, dlosses, make_grads(**grads), ws)
         return grads
-
 
 __all__ = ["workloads", "EXPORTS", "MoELayer", "pack_fp8", "moe_fp8_weight_bytes",
            "moe_pack_fp8_weights", "MOE_F32", "MOE_BF16", "MOE_FP8", "MoEError", "MoeConfig",
@@ -115,6 +133,6 @@ __all__ = ["workloads", "EXPORTS", "MoELayer", "pack_fp8", "moe_fp8_weight_bytes
            "make_grads", "moe_workspace_size", "moe_gate", "moe_gate_hier", "moe_dispatch",
            "moe_expert_ffn", "moe_shared_ffn", "moe_combine", "moe_aux_loss",
            "moe_router_bias_update", "moe_forward", "moe_backward_workspace_size",
-           "moe_backward", "N_LOSSES", "moe_status_string", "moe_last_error",
+           "moe_backward", "moe_forward_train", "moe_backward_saved", "N_LOSSES", "moe_status_string", "moe_last_error",
            "moe_profile_enable", "moe_profile_collect", "moe_profile_entry", "MOE_OK",
            "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP"]

@@ -23,7 +23,8 @@ MOE_ERR_HIP = 4
 EXPORTS = ["moe_workspace_size", "moe_fp8_weight_bytes", "moe_pack_fp8_weights", "moe_gate",
            "moe_gate_hier", "moe_dispatch", "moe_expert_ffn", "moe_shared_ffn", "moe_combine",
            "moe_aux_loss", "moe_router_bias_update", "moe_forward",
-           "moe_backward_workspace_size", "moe_backward", "moe_status_string",
+           "moe_backward_workspace_size", "moe_backward", "moe_forward_train",
+           "moe_backward_saved", "moe_status_string",
            "moe_last_error", "moe_profile_enable", "moe_profile_collect", "moe_profile_entry"]
 
 N_LOSSES = 5  # importance, load, Switch, router z-loss, -gate entropy
@@ -104,6 +105,8 @@ def load_library():
     L.moe_backward_workspace_size.restype = S
     L.moe_backward.argtypes = [cfgp, ctypes.POINTER(MoeWeights)] + [P] * 5 + \
         [ctypes.POINTER(MoeGrads), P, S, P]
+    L.moe_forward_train.argtypes = [cfgp, ctypes.POINTER(MoeWeights)] + [P] * 5 + [P, S, P]
+    L.moe_backward_saved.argtypes = L.moe_backward.argtypes
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_last_error.argtypes = []
@@ -118,7 +121,7 @@ def load_library():
     L.moe_profile_entry.restype = ctypes.c_int
     for name in ("moe_gate", "moe_gate_hier", "moe_dispatch", "moe_expert_ffn", "moe_shared_ffn",
                  "moe_combine", "moe_aux_loss", "moe_router_bias_update", "moe_forward",
-                 "moe_backward"):
+                 "moe_backward", "moe_forward_train", "moe_backward_saved"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -292,6 +295,24 @@ def moe_backward(cfg, weights: MoeWeights, x, noise, noise2, dy, dlosses, grads:
     _check(load_library().moe_backward(ctypes.byref(c), ctypes.byref(weights), _ptr(x),
                                        _ptr(noise), _ptr(noise2), _ptr(dy), _ptr(dlosses),
                                        ctypes.byref(grads), wp, wb, _stream(stream)))
+
+
+def moe_forward_train(cfg, weights: MoeWeights, x, noise, noise2, y, losses, ws, stream=None):
+    c = make_config(cfg)
+    wp, wb = _ws(ws)
+    _check(load_library().moe_forward_train(ctypes.byref(c), ctypes.byref(weights), _ptr(x),
+                                            _ptr(noise), _ptr(noise2), _ptr(y), _ptr(losses),
+                                            wp, wb, _stream(stream)))
+
+
+def moe_backward_saved(cfg, weights: MoeWeights, x, noise, noise2, dy, dlosses,
+                       grads: MoeGrads, ws, stream=None):
+    c = make_config(cfg)
+    wp, wb = _ws(ws)
+    _check(load_library().moe_backward_saved(ctypes.byref(c), ctypes.byref(weights), _ptr(x),
+                                             _ptr(noise), _ptr(noise2), _ptr(dy),
+                                             _ptr(dlosses), ctypes.byref(grads), wp, wb,
+                                             _stream(stream)))
 
 
 def moe_profile_enable(on: bool) -> None:

@@ -921,6 +921,433 @@ moe_status ffn_bwd(const moe_config& c, const FfnBwd& f, hipStream_t s) {
   return MOE_OK;
 }
 
+// Pointer checks of the training entry points (gr == null: forward only).
+moe_status check_bwd_args(const moe_config& c, const moe_weights* wt, const float* x,
+                          const float* noise, const float* noise2, const float* dy,
+                          const float* dlosses, const moe_grads* gr) {
+  if (!wt) return fail(MOE_ERR_INVALID_ARG, "weights must not be NULL");
+  CHECK(check_gate_ptrs(c, x, wt->w_gate, wt->b_gate, wt->w_noise, noise));
+  const bool swiglu = c.act == MOE_ACT_SWIGLU;
+  const bool shared = c.d_hidden_shared > 0;
+  const bool noisy = wt->w_noise != nullptr;
+  const bool hier = c.n_groups > 0;
+  const bool noisy2 = hier && wt->w_noise2 != nullptr;
+  const bool has_load = hier ? (noisy && noisy2) : noisy;
+  if (hier) {
+    CHECK(need(wt->w_gate2, "weights->w_gate2"));
+    CHECK(optional(wt->w_noise2, "weights->w_noise2"));
+    if (noisy2) CHECK(need(noise2, "noise2 (required with w_noise2)", c.T == 0));
+    const int b2 = c.n_experts / c.n_groups;
+    if ((noisy2 ? 2 * b2 : b2) % 16)
+      return fail(MOE_ERR_UNSUPPORTED,
+                  "the two-level backward needs the secondary gate's logit columns (b, or 2b "
+                  "with noise) to be a multiple of 16");
+  }
+  CHECK(need(wt->w1, "weights->w1"));
+  CHECK(need(wt->w2, "weights->w2"));
+  if (swiglu) {
+    CHECK(need(wt->w3, "weights->w3 (required for SwiGLU)"));
+    if (wt->b1 || wt->b2) return fail(MOE_ERR_UNSUPPORTED, "SwiGLU experts take no biases");
+  }
+  CHECK(optional(wt->b1, "weights->b1"));
+  CHECK(optional(wt->b2, "weights->b2"));
+  if (shared) CHECK(check_shared_ptrs(c, wt->ws1, wt->ws3, wt->ws2));
+  if (!gr) return MOE_OK;  // forward only
+  CHECK(need(dy, "dy", c.T == 0));
+  CHECK(need(dlosses, "dlosses"));
+  CHECK(need(gr->dx, "grads->dx", c.T == 0));
+  CHECK(need(gr->dw_gate, "grads->dw_gate"));
+  const bool want_db = wt->b_gate && c.gate != MOE_GATE_SIGMOID_BIAS;
+  if (want_db) CHECK(need(gr->db_gate, "grads->db_gate"));
+  if (noisy) CHECK(need(gr->dw_noise, "grads->dw_noise"));
+  CHECK(need(gr->dw1, "grads->dw1"));
+  CHECK(need(gr->dw2, "grads->dw2"));
+  if (swiglu) CHECK(need(gr->dw3, "grads->dw3"));
+  if (wt->b1) CHECK(need(gr->db1, "grads->db1"));
+  if (wt->b2) CHECK(need(gr->db2, "grads->db2"));
+  if (hier) {
+    CHECK(need(gr->dw_gate2, "grads->dw_gate2"));
+    if (noisy2) CHECK(need(gr->dw_noise2, "grads->dw_noise2"));
+  }
+  if (shared) {
+    CHECK(need(gr->dws1, "grads->dws1"));
+    CHECK(need(gr->dws2, "grads->dws2"));
+    if (swiglu) CHECK(need(gr->dws3, "grads->dws3"));
+  }
+  return MOE_OK;
+}
+
+// The training path over the backward's workspace layout (every intermediate
+// the backward reads survives the forward).  do_fwd: the layer forward (y
+// and losses may be null); do_bwd: the gradients from the intermediates the
+// forward left in ws.
+moe_status train_run(const moe_config& c, const moe_weights* wt, const float* x,
+                     const float* noise, const float* noise2, const float* dy,
+                     const float* dlosses, const moe_grads* gr, float* y, float* losses,
+                     void* ws, size_t ws_bytes, hipStream_t s, bool do_fwd, bool do_bwd,
+                     const char* what) {
+  const bool swiglu = c.act == MOE_ACT_SWIGLU;
+  const bool shared = c.d_hidden_shared > 0;
+  const bool noisy = wt->w_noise != nullptr;
+  const bool hier = c.n_groups > 0;
+  const bool noisy2 = hier && wt->w_noise2 != nullptr;
+  const bool has_load = hier ? (noisy && noisy2) : noisy;
+  const bool want_db = wt->b_gate && c.gate != MOE_GATE_SIGMOID_BIAS;
+  const BwdPlan b = make_bwd_plan(c);
+  const Plan& p = b.f;
+  CHECK(check_ws(ws, ws_bytes, b.total, what));
+  const int T = c.T, d = c.d_model, h = c.d_hidden, n = c.n_experts, k = c.k;
+  const long long A = (long long)T * k;
+  int32_t* idx = at<int32_t>(ws, p.f_idx);
+  float* w = at<float>(ws, p.f_w);
+  float* imp = at<float>(ws, p.f_imp);
+  float* ld = at<float>(ws, p.f_load);
+  int32_t* counts_pre = at<int32_t>(ws, p.f_counts_pre);
+  int32_t* counts = at<int32_t>(ws, p.f_counts);
+  int32_t* offsets = at<int32_t>(ws, p.f_offsets);
+  int32_t* perm = at<int32_t>(ws, p.f_perm);
+  int32_t* slot = at<int32_t>(ws, p.f_slot);
+  uint16_t* xperm = at<uint16_t>(ws, p.f_xperm);
+  float* yperm = at<float>(ws, p.f_yperm);
+  float* stats = at<float>(ws, p.f_stats);
+  uint16_t* hidden = at<uint16_t>(ws, p.hidden);
+  float* a_pre = swiglu ? at<float>(ws, b.a_pre) : nullptr;
+  float* b_pre = swiglu ? at<float>(ws, b.b_pre) : nullptr;
+  float* logits2 = hier ? at<float>(ws, b.logits2) : nullptr;
+  float* load_g = hier ? at<float>(ws, b.load_g) : nullptr;
+  ForwardExtras fx;
+  fx.tile_expert = at<int32_t>(ws, p.f_tile_expert);
+  fx.tile_row0 = at<int32_t>(ws, p.f_tile_row0);
+  fx.tile_count = at<int32_t>(ws, p.f_tile_count);
+  fx.losses = losses ? losses : at<float>(ws, b.losses);
+  fx.importance = imp;
+  fx.load = has_load ? ld : nullptr;
+  fx.gate_stats = stats;
+  fx.x_bf16 = shared ? at<uint16_t>(ws, p.sh_xb) : nullptr;
+  const bool f32 = c.expert_dtype == MOE_F32;
+  const int hs = c.d_hidden_shared;
+  uint16_t* xb = shared ? at<uint16_t>(ws, p.sh_xb) : nullptr;
+  uint16_t* hid_s = shared ? at<uint16_t>(ws, p.sh_hidden) : nullptr;
+  int32_t* sh_off = shared ? at<int32_t>(ws, p.sh_off) : nullptr;
+  int32_t* sh_te = shared ? at<int32_t>(ws, p.sh_te) : nullptr;
+  int32_t* sh_tr = shared ? at<int32_t>(ws, p.sh_tr) : nullptr;
+  int32_t* sh_tc = shared ? at<int32_t>(ws, p.sh_tc) : nullptr;
+  float* a_s = shared && swiglu ? at<float>(ws, b.a_s) : nullptr;
+  float* b_s = shared && swiglu ? at<float>(ws, b.b_s) : nullptr;
+
+  if (do_fwd) {
+  if (hier) {
+    CHECK(run_gate_hier(c, p, x, wt->w_gate, wt->b_gate, wt->w_noise, noise, wt->w_gate2,
+                        wt->w_noise2, noise2, idx, w, imp, ld, stats, ws, s, logits2, load_g));
+  } else {
+    CHECK(run_gate(c, p, x, wt->w_gate, wt->b_gate, wt->w_noise, noise, idx, w, imp, ld, stats,
+                   ws, s));
+  }
+  CHECK(run_dispatch(c, p, idx, x, counts_pre, counts, offsets, perm, slot, xperm, ws, s, &fx));
+  if (f32) {
+    // fp32 experts: the forward's own expert stage (hidden goes to the
+    // relocated region of this plan)
+    CHECK(run_ffn(c, p, xperm, offsets, wt->w1, wt->b1, wt->w3, wt->w2, wt->b2, yperm, ws, s,
+                  &fx));
+  } else {
+  GemmBf16Args g1{};
+  g1.A = xperm;
+  g1.lda = d;
+  g1.B1 = wt->w1;
+  g1.B3 = wt->w3;
+  g1.strideB = (long long)h * d * 2;
+  g1.K = d;
+  g1.bias = wt->b1;
+  g1.tile_expert = fx.tile_expert;
+  g1.tile_row0 = fx.tile_row0;
+  g1.offsets = offsets;
+  g1.tile_count = fx.tile_count;
+  g1.max_mtiles = p.max_mtiles;
+  g1.num_cus = device_cus();
+  CHECK(bwd_hidden(c, g1, h, hidden, a_pre, b_pre, A * h, s));
+  GemmBf16Args g2 = g1;
+  g2.A = hidden;
+  g2.lda = h;
+  g2.B1 = wt->w2;
+  g2.B3 = nullptr;
+  g2.strideB = (long long)d * h * 2;
+  g2.N = d;
+  g2.K = h;
+  g2.C = yperm;
+  g2.ldc = d;
+  g2.bias = wt->b2;
+  HIP_TRY(launch_gemm_bf16(g2, EPI_IDENT_F32, s));
+  }
+  if (shared) {
+    HIP_TRY(launch_shared_tilemap(T, kBf16BM, sh_off, sh_te, sh_tr, sh_tc, s));
+    GemmBf16Args gs{};
+    gs.A = xb;
+    gs.lda = d;
+    gs.B1 = wt->ws1;
+    gs.B3 = wt->ws3;
+    gs.K = d;
+    gs.tile_expert = sh_te;
+    gs.tile_row0 = sh_tr;
+    gs.offsets = sh_off;
+    gs.tile_count = sh_tc;
+    gs.max_mtiles = p.sh_tiles;
+    gs.num_cus = device_cus();
+    gs.shared = 1;
+    CHECK(bwd_hidden(c, gs, hs, hid_s, a_s, b_s, (long long)T * hs, s));
+  }
+  if (y) {
+    float* ysh = nullptr;
+    if (shared && T > 0) {
+      // the shared expert's output (its hidden values are kept above)
+      ysh = at<float>(ws, p.sh_y);
+      GemmBf16Args go{};
+      go.A = hid_s;
+      go.lda = hs;
+      go.B1 = wt->ws2;
+      go.N = d;
+      go.K = hs;
+      go.C = ysh;
+      go.ldc = d;
+      go.tile_expert = sh_te;
+      go.tile_row0 = sh_tr;
+      go.offsets = sh_off;
+      go.tile_count = sh_tc;
+      go.max_mtiles = p.sh_tiles;
+      go.num_cus = device_cus();
+      go.shared = 1;
+      HIP_TRY(launch_gemm_bf16(go, EPI_IDENT_F32, s));
+    }
+    HIP_TRY(launch_combine(yperm, slot, w, ysh, T, k, d, y, s));
+  }
+  }
+  if (!do_bwd) return MOE_OK;
+
+  // ---- backward ---------------------------------------------------------
+  float* dG = at<float>(ws, b.dG);
+  uint16_t* dout = at<uint16_t>(ws, b.dout);
+  float* dimp = at<float>(ws, b.dimp);
+  float* dload = at<float>(ws, b.dload);
+  float* coef = at<float>(ws, b.coef);
+  float* dlogits = at<float>(ws, b.dlogits);
+  HIP_TRY(launch_combine_bwd(dy, yperm, slot, w, T, k, d, dG, dout, f32, s));
+  HIP_TRY(launch_loss_grad(imp, has_load ? ld : nullptr, counts_pre, dlosses, T, k, n,
+                           c.w_importance, c.w_load, c.alpha_switch, c.w_z, c.w_entropy, dimp,
+                           dload, coef, s));
+  // The flat gate, or the two-level layer's primary gate (whose slots carry
+  // the product weights' split gradients and no Importance or entropy term).
+  const int ng = p.n_gate;
+  const int kg = hier ? p.k1 : k;
+  float* dG1 = hier ? at<float>(ws, b.dG1) : nullptr;
+  float* dG2 = hier ? at<float>(ws, b.dG2) : nullptr;
+  float* dload_p = hier && has_load ? at<float>(ws, b.dload_p) : nullptr;
+  float* dload_g = hier && has_load ? at<float>(ws, b.dload_g) : nullptr;
+  if (hier) {
+    HIP_TRY(launch_hier_product_bwd(idx, w, at<float>(ws, p.prim_w), dG, dimp, coef, T, p.k1,
+                                    p.k2, dG1, dG2, s));
+    if (has_load)
+      HIP_TRY(launch_hier_dload(dload, at<float>(ws, p.prim_load), load_g,
+                                at<int32_t>(ws, p.g_counts_pre), p.a, p.b, dload_p, dload_g, s));
+  }
+  GateBwdArgs gb{};
+  gb.T = T;
+  gb.n = ng;
+  gb.switch_mode = c.gate == MOE_GATE_SWITCH_TOP1;
+  gb.sigmoid_mode = c.gate == MOE_GATE_SIGMOID_BIAS;
+  gb.noisy = noisy;
+  gb.logits = at<float>(ws, p.logits);
+  gb.ldl = p.ldl;
+  gb.bias = wt->b_gate;
+  gb.noise = noise;
+  gb.k = kg;
+  gb.topk_idx = hier ? at<int32_t>(ws, p.prim_idx) : idx;
+  gb.topk_w = hier ? at<float>(ws, p.prim_w) : w;
+  gb.dG = hier ? dG1 : dG;
+  gb.dimp = hier ? nullptr : dimp;
+  gb.dload = hier ? dload_p : (noisy ? dload : nullptr);
+  gb.coef = hier ? coef + 2 : coef;
+  gb.dlogits = dlogits;
+  gb.ldd = p.ldl;
+  gb.part_db = want_db ? at<float>(ws, b.part_db) : nullptr;
+  gb.rows_per_block = p.rows_per_block;
+  HIP_TRY(launch_gate_bwd(gb, s));
+  if (want_db)
+    HIP_TRY(launch_colsum(p.nparts, ColsumVec{gb.part_db, ng, gr->db_gate},
+                          ColsumVec{nullptr, 0, nullptr}, ColsumVec{nullptr, 0, nullptr}, s));
+  const int M = noisy ? 2 * ng : ng;
+  GateWgradArgs gw{};
+  gw.x = x;
+  gw.dlogits = dlogits;
+  gw.ldd = p.ldl;
+  gw.T = T;
+  gw.d = d;
+  gw.M = M;
+  gw.n = ng;
+  gw.splits = b.splits;
+  gw.tokens_per_split = b.tps;
+  gw.partial = at<float>(ws, b.wpart);
+  HIP_TRY(launch_gate_wgrad(gw, gr->dw_gate, gr->dw_noise, s));
+  float* dx_gate = at<float>(ws, b.dx_gate);
+  if (T > 0) {
+    const int ldk = (int)round_up(M, 4);
+    float* wtr = at<float>(ws, b.wt);
+    HIP_TRY(launch_transpose_gate(wt->w_gate, wt->w_noise, ng, d, ldk, wtr, s));
+    GemmF32Args gx{};
+    gx.A = dlogits;
+    gx.lda = p.ldl;
+    gx.B1 = wtr;
+    gx.B2 = wtr;
+    gx.n1 = d;
+    gx.N = d;
+    gx.K = ldk;
+    gx.C = dx_gate;
+    gx.ldc = d;
+    gx.M = T;
+    gx.mtiles = (T + p.gemm_bm - 1) / p.gemm_bm;
+    gx.max_mtiles = gx.mtiles;
+    gx.prof_name = "bwd_gate_dx";
+    HIP_TRY(launch_gemm_gate(gx, p.gemm_bm, s));
+  }
+  FfnBwd fb{};
+  fb.u = xperm;
+  fb.hidden = hidden;
+  fb.a_pre = a_pre;
+  fb.b_pre = b_pre;
+  fb.gout = dout;
+  fb.dpre = at<uint16_t>(ws, b.dpre);
+  fb.du = at<float>(ws, b.du_perm);
+  fb.w1 = wt->w1;
+  fb.w3 = wt->w3;
+  fb.w2 = wt->w2;
+  fb.stride1 = (long long)h * d;
+  fb.stride2 = (long long)d * h;
+  fb.dw1 = gr->dw1;
+  fb.dw3 = gr->dw3;
+  fb.dw2 = gr->dw2;
+  fb.tile_expert = fx.tile_expert;
+  fb.tile_row0 = fx.tile_row0;
+  fb.offsets = offsets;
+  fb.tile_count = fx.tile_count;
+  fb.max_tiles = p.max_mtiles;
+  fb.tile_rows = p.ffn_bm;
+  fb.n_experts = n;
+  fb.h = h;
+  fb.f32 = f32;
+  fb.names[0] = "bwd_ggemm_dhidden";
+  fb.names[1] = "bwd_ggemm_dinput";
+  fb.names[2] = "bwd_ggemm_dw2";
+  fb.names[3] = "bwd_ggemm_dw1";
+  CHECK(ffn_bwd(c, fb, s));
+  if (wt->b2) HIP_TRY(launch_seg_colsum(dout, f32, d, offsets, n, d, gr->db2, s));
+  if (wt->b1) HIP_TRY(launch_seg_colsum(fb.dpre, f32, h, offsets, n, h, gr->db1, s));
+  float* du_s = nullptr;
+  if (shared) {
+    uint16_t* dout_s = at<uint16_t>(ws, b.dout_s);
+    du_s = at<float>(ws, b.du_s);
+    HIP_TRY(launch_to_bf16(dy, (long long)T * d, dout_s, s));
+    FfnBwd fs{};
+    fs.u = xb;
+    fs.hidden = hid_s;
+    fs.a_pre = a_s;
+    fs.b_pre = b_s;
+    fs.gout = dout_s;
+    fs.dpre = at<uint16_t>(ws, b.dpre_s);
+    fs.du = du_s;
+    fs.w1 = wt->ws1;
+    fs.w3 = wt->ws3;
+    fs.w2 = wt->ws2;
+    fs.dw1 = gr->dws1;
+    fs.dw3 = gr->dws3;
+    fs.dw2 = gr->dws2;
+    fs.tile_expert = sh_te;
+    fs.tile_row0 = sh_tr;
+    fs.offsets = sh_off;
+    fs.tile_count = sh_tc;
+    fs.max_tiles = p.sh_tiles;
+    fs.tile_rows = kBf16BM;
+    fs.n_experts = 1;
+    fs.h = hs;
+    fs.names[0] = "bwd_shared_dhidden";
+    fs.names[1] = "bwd_shared_dinput";
+    fs.names[2] = "bwd_shared_dw2";
+    fs.names[3] = "bwd_shared_dw1";
+    CHECK(ffn_bwd(c, fs, s));
+  }
+  float* du2 = nullptr;
+  if (hier) {
+    // Each group's secondary gate over the rows routed to it.
+    const int bb = p.b;
+    float* dlogits2 = at<float>(ws, b.dlogits2);
+    const int32_t* g_perm = at<int32_t>(ws, p.g_perm);
+    const int32_t* g_offsets = at<int32_t>(ws, p.g_offsets);
+    GateBwdArgs g2{};
+    g2.T = T;
+    g2.n = bb;
+    g2.k = p.k2;
+    g2.noisy = noisy2;
+    g2.logits = logits2;
+    g2.ldl = p.ldl2;
+    g2.noise = noise2;
+    g2.topk_idx = idx;
+    g2.dG = dG2;
+    g2.dload = dload_g;
+    g2.coef = coef + 2;
+    g2.dlogits = dlogits2;
+    g2.ldd = p.ldl2;
+    g2.row_token = g_perm;
+    g2.prim_idx = at<int32_t>(ws, p.prim_idx);
+    g2.k1 = p.k1;
+    g2.tile_expert = at<int32_t>(ws, p.t2_expert);
+    g2.tile_row0 = at<int32_t>(ws, p.t2_row0);
+    g2.offsets = g_offsets;
+    g2.tile_count = at<int32_t>(ws, p.t2_count);
+    g2.max_tiles = p.max_tiles2;
+    g2.tile_rows = kSecondaryBM;
+    HIP_TRY(launch_gate_bwd(g2, s));
+    const int K2 = noisy2 ? 2 * bb : bb;
+    // dW_gate2 | dW_noise2 [g] = dlogits2^T x over the group's rows
+    GemmBwdArgs gw2{};
+    gw2.A = (const uint16_t*)x;
+    gw2.lda = d;
+    gw2.rowmap_a = g_perm;
+    gw2.B = (const uint16_t*)dlogits2;
+    gw2.ldb = p.ldl2;
+    gw2.M = d;
+    gw2.N = K2;
+    gw2.C = gr->dw_gate2;
+    gw2.C2 = gr->dw_noise2;
+    gw2.ldc = d;
+    gw2.strideC = (long long)bb * d;
+    gw2.c_split = bb;
+    gw2.offsets = g_offsets;
+    gw2.n_experts = p.a;
+    HIP_TRY(launch_gemm_bwd_f32(gw2, BWD_WGRAD, BEPI_F32, "bwd_gate2_wgrad", s));
+    // the rows' input gradients dlogits2 . [W_gate2; W_noise2][g]
+    du2 = at<float>(ws, b.du2);
+    GemmBwdArgs gx2{};
+    gx2.A = (const uint16_t*)wt->w_gate2;
+    gx2.A2 = (const uint16_t*)wt->w_noise2;
+    gx2.lda = d;
+    gx2.strideA = (long long)bb * d;
+    gx2.k_split = bb;
+    gx2.B = (const uint16_t*)dlogits2;
+    gx2.ldb = p.ldl2;
+    gx2.M = d;
+    gx2.K = K2;
+    gx2.C = du2;
+    gx2.ldc = d;
+    gx2.tile_expert = g2.tile_expert;
+    gx2.tile_row0 = g2.tile_row0;
+    gx2.offsets = g_offsets;
+    gx2.tile_count = g2.tile_count;
+    gx2.max_tiles = p.max_tiles2;
+    gx2.tile_rows = kSecondaryBM;
+    HIP_TRY(launch_gemm_bwd_f32(gx2, BWD_ROWS, BEPI_F32, "bwd_gate2_dx", s));
+  }
+  HIP_TRY(launch_dx_gather(dx_gate, du_s, fb.du, slot, T, k, d, du2,
+                           hier ? at<int32_t>(ws, p.g_slot) : nullptr, p.k1, gr->dx, s));
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1196,383 +1623,37 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const floa
                         void* stream) {
   g_err[0] = 0;
   CHECK(validate(cfg));
-  const moe_config& c = *cfg;
-  CHECK(validate_bwd(c));
-  if (!wt) return fail(MOE_ERR_INVALID_ARG, "weights must not be NULL");
+  CHECK(validate_bwd(*cfg));
   if (!gr) return fail(MOE_ERR_INVALID_ARG, "grads must not be NULL");
-  CHECK(check_gate_ptrs(c, x, wt->w_gate, wt->b_gate, wt->w_noise, noise));
-  const bool swiglu = c.act == MOE_ACT_SWIGLU;
-  const bool shared = c.d_hidden_shared > 0;
-  const bool noisy = wt->w_noise != nullptr;
-  const bool hier = c.n_groups > 0;
-  const bool noisy2 = hier && wt->w_noise2 != nullptr;
-  const bool has_load = hier ? (noisy && noisy2) : noisy;
-  if (hier) {
-    CHECK(need(wt->w_gate2, "weights->w_gate2"));
-    CHECK(optional(wt->w_noise2, "weights->w_noise2"));
-    if (noisy2) CHECK(need(noise2, "noise2 (required with w_noise2)", c.T == 0));
-    CHECK(need(gr->dw_gate2, "grads->dw_gate2"));
-    if (noisy2) CHECK(need(gr->dw_noise2, "grads->dw_noise2"));
-    const int b2 = c.n_experts / c.n_groups;
-    if ((noisy2 ? 2 * b2 : b2) % 16)
-      return fail(MOE_ERR_UNSUPPORTED,
-                  "the two-level backward needs the secondary gate's logit columns (b, or 2b "
-                  "with noise) to be a multiple of 16");
-  }
-  CHECK(need(wt->w1, "weights->w1"));
-  CHECK(need(wt->w2, "weights->w2"));
-  if (swiglu) {
-    CHECK(need(wt->w3, "weights->w3 (required for SwiGLU)"));
-    if (wt->b1 || wt->b2) return fail(MOE_ERR_UNSUPPORTED, "SwiGLU experts take no biases");
-  }
-  CHECK(optional(wt->b1, "weights->b1"));
-  CHECK(optional(wt->b2, "weights->b2"));
-  if (shared) CHECK(check_shared_ptrs(c, wt->ws1, wt->ws3, wt->ws2));
-  CHECK(need(dy, "dy", c.T == 0));
-  CHECK(need(dlosses, "dlosses"));
-  CHECK(need(gr->dx, "grads->dx", c.T == 0));
-  CHECK(need(gr->dw_gate, "grads->dw_gate"));
-  const bool want_db = wt->b_gate && c.gate != MOE_GATE_SIGMOID_BIAS;
-  if (want_db) CHECK(need(gr->db_gate, "grads->db_gate"));
-  if (noisy) CHECK(need(gr->dw_noise, "grads->dw_noise"));
-  CHECK(need(gr->dw1, "grads->dw1"));
-  CHECK(need(gr->dw2, "grads->dw2"));
-  if (swiglu) CHECK(need(gr->dw3, "grads->dw3"));
-  if (wt->b1) CHECK(need(gr->db1, "grads->db1"));
-  if (wt->b2) CHECK(need(gr->db2, "grads->db2"));
-  if (shared) {
-    CHECK(need(gr->dws1, "grads->dws1"));
-    CHECK(need(gr->dws2, "grads->dws2"));
-    if (swiglu) CHECK(need(gr->dws3, "grads->dws3"));
-  }
-  const BwdPlan b = make_bwd_plan(c);
-  const Plan& p = b.f;
-  CHECK(check_ws(ws, ws_bytes, b.total, "moe_backward"));
-  hipStream_t s = (hipStream_t)stream;
-  const int T = c.T, d = c.d_model, h = c.d_hidden, n = c.n_experts, k = c.k;
-  const long long A = (long long)T * k;
+  CHECK(check_bwd_args(*cfg, wt, x, noise, noise2, dy, dlosses, gr));
+  return train_run(*cfg, wt, x, noise, noise2, dy, dlosses, gr, nullptr, nullptr, ws, ws_bytes,
+                   (hipStream_t)stream, true, true, "moe_backward");
+}
 
-  // ---- forward recompute ------------------------------------------------
-  int32_t* idx = at<int32_t>(ws, p.f_idx);
-  float* w = at<float>(ws, p.f_w);
-  float* imp = at<float>(ws, p.f_imp);
-  float* ld = at<float>(ws, p.f_load);
-  int32_t* counts_pre = at<int32_t>(ws, p.f_counts_pre);
-  int32_t* counts = at<int32_t>(ws, p.f_counts);
-  int32_t* offsets = at<int32_t>(ws, p.f_offsets);
-  int32_t* perm = at<int32_t>(ws, p.f_perm);
-  int32_t* slot = at<int32_t>(ws, p.f_slot);
-  uint16_t* xperm = at<uint16_t>(ws, p.f_xperm);
-  float* yperm = at<float>(ws, p.f_yperm);
-  float* stats = at<float>(ws, p.f_stats);
-  uint16_t* hidden = at<uint16_t>(ws, p.hidden);
-  float* a_pre = swiglu ? at<float>(ws, b.a_pre) : nullptr;
-  float* b_pre = swiglu ? at<float>(ws, b.b_pre) : nullptr;
-  float* logits2 = hier ? at<float>(ws, b.logits2) : nullptr;
-  float* load_g = hier ? at<float>(ws, b.load_g) : nullptr;
-  if (hier) {
-    CHECK(run_gate_hier(c, p, x, wt->w_gate, wt->b_gate, wt->w_noise, noise, wt->w_gate2,
-                        wt->w_noise2, noise2, idx, w, imp, ld, stats, ws, s, logits2, load_g));
-  } else {
-    CHECK(run_gate(c, p, x, wt->w_gate, wt->b_gate, wt->w_noise, noise, idx, w, imp, ld, stats,
-                   ws, s));
-  }
-  ForwardExtras fx;
-  fx.tile_expert = at<int32_t>(ws, p.f_tile_expert);
-  fx.tile_row0 = at<int32_t>(ws, p.f_tile_row0);
-  fx.tile_count = at<int32_t>(ws, p.f_tile_count);
-  fx.losses = at<float>(ws, b.losses);
-  fx.importance = imp;
-  fx.load = has_load ? ld : nullptr;
-  fx.gate_stats = stats;
-  fx.x_bf16 = shared ? at<uint16_t>(ws, p.sh_xb) : nullptr;
-  CHECK(run_dispatch(c, p, idx, x, counts_pre, counts, offsets, perm, slot, xperm, ws, s, &fx));
-  const bool f32 = c.expert_dtype == MOE_F32;
-  if (f32) {
-    // fp32 experts: the forward's own expert stage (hidden goes to the
-    // relocated region of this plan)
-    CHECK(run_ffn(c, p, xperm, offsets, wt->w1, wt->b1, wt->w3, wt->w2, wt->b2, yperm, ws, s,
-                  &fx));
-  } else {
-  GemmBf16Args g1{};
-  g1.A = xperm;
-  g1.lda = d;
-  g1.B1 = wt->w1;
-  g1.B3 = wt->w3;
-  g1.strideB = (long long)h * d * 2;
-  g1.K = d;
-  g1.bias = wt->b1;
-  g1.tile_expert = fx.tile_expert;
-  g1.tile_row0 = fx.tile_row0;
-  g1.offsets = offsets;
-  g1.tile_count = fx.tile_count;
-  g1.max_mtiles = p.max_mtiles;
-  g1.num_cus = device_cus();
-  CHECK(bwd_hidden(c, g1, h, hidden, a_pre, b_pre, A * h, s));
-  GemmBf16Args g2 = g1;
-  g2.A = hidden;
-  g2.lda = h;
-  g2.B1 = wt->w2;
-  g2.B3 = nullptr;
-  g2.strideB = (long long)d * h * 2;
-  g2.N = d;
-  g2.K = h;
-  g2.C = yperm;
-  g2.ldc = d;
-  g2.bias = wt->b2;
-  HIP_TRY(launch_gemm_bf16(g2, EPI_IDENT_F32, s));
-  }
-  const int hs = c.d_hidden_shared;
-  uint16_t* xb = shared ? at<uint16_t>(ws, p.sh_xb) : nullptr;
-  uint16_t* hid_s = shared ? at<uint16_t>(ws, p.sh_hidden) : nullptr;
-  int32_t* sh_off = shared ? at<int32_t>(ws, p.sh_off) : nullptr;
-  int32_t* sh_te = shared ? at<int32_t>(ws, p.sh_te) : nullptr;
-  int32_t* sh_tr = shared ? at<int32_t>(ws, p.sh_tr) : nullptr;
-  int32_t* sh_tc = shared ? at<int32_t>(ws, p.sh_tc) : nullptr;
-  float* a_s = shared && swiglu ? at<float>(ws, b.a_s) : nullptr;
-  float* b_s = shared && swiglu ? at<float>(ws, b.b_s) : nullptr;
-  if (shared) {
-    HIP_TRY(launch_shared_tilemap(T, kBf16BM, sh_off, sh_te, sh_tr, sh_tc, s));
-    GemmBf16Args gs{};
-    gs.A = xb;
-    gs.lda = d;
-    gs.B1 = wt->ws1;
-    gs.B3 = wt->ws3;
-    gs.K = d;
-    gs.tile_expert = sh_te;
-    gs.tile_row0 = sh_tr;
-    gs.offsets = sh_off;
-    gs.tile_count = sh_tc;
-    gs.max_mtiles = p.sh_tiles;
-    gs.num_cus = device_cus();
-    gs.shared = 1;
-    CHECK(bwd_hidden(c, gs, hs, hid_s, a_s, b_s, (long long)T * hs, s));
-  }
+moe_status moe_forward_train(const moe_config* cfg, const moe_weights* wt, const float* x,
+                             const float* noise, const float* noise2, float* y, float* losses,
+                             void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  CHECK(validate(cfg));
+  CHECK(validate_bwd(*cfg));
+  CHECK(check_bwd_args(*cfg, wt, x, noise, noise2, nullptr, nullptr, nullptr));
+  CHECK(need(y, "y", cfg->T == 0));
+  CHECK(need(losses, "losses"));
+  return train_run(*cfg, wt, x, noise, noise2, nullptr, nullptr, nullptr, y, losses, ws,
+                   ws_bytes, (hipStream_t)stream, true, false, "moe_forward_train");
+}
 
-  // ---- backward ---------------------------------------------------------
-  float* dG = at<float>(ws, b.dG);
-  uint16_t* dout = at<uint16_t>(ws, b.dout);
-  float* dimp = at<float>(ws, b.dimp);
-  float* dload = at<float>(ws, b.dload);
-  float* coef = at<float>(ws, b.coef);
-  float* dlogits = at<float>(ws, b.dlogits);
-  HIP_TRY(launch_combine_bwd(dy, yperm, slot, w, T, k, d, dG, dout, f32, s));
-  HIP_TRY(launch_loss_grad(imp, has_load ? ld : nullptr, counts_pre, dlosses, T, k, n,
-                           c.w_importance, c.w_load, c.alpha_switch, c.w_z, c.w_entropy, dimp,
-                           dload, coef, s));
-  // The flat gate, or the two-level layer's primary gate (whose slots carry
-  // the product weights' split gradients and no Importance or entropy term).
-  const int ng = p.n_gate;
-  const int kg = hier ? p.k1 : k;
-  float* dG1 = hier ? at<float>(ws, b.dG1) : nullptr;
-  float* dG2 = hier ? at<float>(ws, b.dG2) : nullptr;
-  float* dload_p = hier && has_load ? at<float>(ws, b.dload_p) : nullptr;
-  float* dload_g = hier && has_load ? at<float>(ws, b.dload_g) : nullptr;
-  if (hier) {
-    HIP_TRY(launch_hier_product_bwd(idx, w, at<float>(ws, p.prim_w), dG, dimp, coef, T, p.k1,
-                                    p.k2, dG1, dG2, s));
-    if (has_load)
-      HIP_TRY(launch_hier_dload(dload, at<float>(ws, p.prim_load), load_g,
-                                at<int32_t>(ws, p.g_counts_pre), p.a, p.b, dload_p, dload_g, s));
-  }
-  GateBwdArgs gb{};
-  gb.T = T;
-  gb.n = ng;
-  gb.switch_mode = c.gate == MOE_GATE_SWITCH_TOP1;
-  gb.sigmoid_mode = c.gate == MOE_GATE_SIGMOID_BIAS;
-  gb.noisy = noisy;
-  gb.logits = at<float>(ws, p.logits);
-  gb.ldl = p.ldl;
-  gb.bias = wt->b_gate;
-  gb.noise = noise;
-  gb.k = kg;
-  gb.topk_idx = hier ? at<int32_t>(ws, p.prim_idx) : idx;
-  gb.topk_w = hier ? at<float>(ws, p.prim_w) : w;
-  gb.dG = hier ? dG1 : dG;
-  gb.dimp = hier ? nullptr : dimp;
-  gb.dload = hier ? dload_p : (noisy ? dload : nullptr);
-  gb.coef = hier ? coef + 2 : coef;
-  gb.dlogits = dlogits;
-  gb.ldd = p.ldl;
-  gb.part_db = want_db ? at<float>(ws, b.part_db) : nullptr;
-  gb.rows_per_block = p.rows_per_block;
-  HIP_TRY(launch_gate_bwd(gb, s));
-  if (want_db)
-    HIP_TRY(launch_colsum(p.nparts, ColsumVec{gb.part_db, ng, gr->db_gate},
-                          ColsumVec{nullptr, 0, nullptr}, ColsumVec{nullptr, 0, nullptr}, s));
-  const int M = noisy ? 2 * ng : ng;
-  GateWgradArgs gw{};
-  gw.x = x;
-  gw.dlogits = dlogits;
-  gw.ldd = p.ldl;
-  gw.T = T;
-  gw.d = d;
-  gw.M = M;
-  gw.n = ng;
-  gw.splits = b.splits;
-  gw.tokens_per_split = b.tps;
-  gw.partial = at<float>(ws, b.wpart);
-  HIP_TRY(launch_gate_wgrad(gw, gr->dw_gate, gr->dw_noise, s));
-  float* dx_gate = at<float>(ws, b.dx_gate);
-  if (T > 0) {
-    const int ldk = (int)round_up(M, 4);
-    float* wtr = at<float>(ws, b.wt);
-    HIP_TRY(launch_transpose_gate(wt->w_gate, wt->w_noise, ng, d, ldk, wtr, s));
-    GemmF32Args gx{};
-    gx.A = dlogits;
-    gx.lda = p.ldl;
-    gx.B1 = wtr;
-    gx.B2 = wtr;
-    gx.n1 = d;
-    gx.N = d;
-    gx.K = ldk;
-    gx.C = dx_gate;
-    gx.ldc = d;
-    gx.M = T;
-    gx.mtiles = (T + p.gemm_bm - 1) / p.gemm_bm;
-    gx.max_mtiles = gx.mtiles;
-    gx.prof_name = "bwd_gate_dx";
-    HIP_TRY(launch_gemm_gate(gx, p.gemm_bm, s));
-  }
-  FfnBwd fb{};
-  fb.u = xperm;
-  fb.hidden = hidden;
-  fb.a_pre = a_pre;
-  fb.b_pre = b_pre;
-  fb.gout = dout;
-  fb.dpre = at<uint16_t>(ws, b.dpre);
-  fb.du = at<float>(ws, b.du_perm);
-  fb.w1 = wt->w1;
-  fb.w3 = wt->w3;
-  fb.w2 = wt->w2;
-  fb.stride1 = (long long)h * d;
-  fb.stride2 = (long long)d * h;
-  fb.dw1 = gr->dw1;
-  fb.dw3 = gr->dw3;
-  fb.dw2 = gr->dw2;
-  fb.tile_expert = fx.tile_expert;
-  fb.tile_row0 = fx.tile_row0;
-  fb.offsets = offsets;
-  fb.tile_count = fx.tile_count;
-  fb.max_tiles = p.max_mtiles;
-  fb.tile_rows = p.ffn_bm;
-  fb.n_experts = n;
-  fb.h = h;
-  fb.f32 = f32;
-  fb.names[0] = "bwd_ggemm_dhidden";
-  fb.names[1] = "bwd_ggemm_dinput";
-  fb.names[2] = "bwd_ggemm_dw2";
-  fb.names[3] = "bwd_ggemm_dw1";
-  CHECK(ffn_bwd(c, fb, s));
-  if (wt->b2) HIP_TRY(launch_seg_colsum(dout, f32, d, offsets, n, d, gr->db2, s));
-  if (wt->b1) HIP_TRY(launch_seg_colsum(fb.dpre, f32, h, offsets, n, h, gr->db1, s));
-  float* du_s = nullptr;
-  if (shared) {
-    uint16_t* dout_s = at<uint16_t>(ws, b.dout_s);
-    du_s = at<float>(ws, b.du_s);
-    HIP_TRY(launch_to_bf16(dy, (long long)T * d, dout_s, s));
-    FfnBwd fs{};
-    fs.u = xb;
-    fs.hidden = hid_s;
-    fs.a_pre = a_s;
-    fs.b_pre = b_s;
-    fs.gout = dout_s;
-    fs.dpre = at<uint16_t>(ws, b.dpre_s);
-    fs.du = du_s;
-    fs.w1 = wt->ws1;
-    fs.w3 = wt->ws3;
-    fs.w2 = wt->ws2;
-    fs.dw1 = gr->dws1;
-    fs.dw3 = gr->dws3;
-    fs.dw2 = gr->dws2;
-    fs.tile_expert = sh_te;
-    fs.tile_row0 = sh_tr;
-    fs.offsets = sh_off;
-    fs.tile_count = sh_tc;
-    fs.max_tiles = p.sh_tiles;
-    fs.tile_rows = kBf16BM;
-    fs.n_experts = 1;
-    fs.h = hs;
-    fs.names[0] = "bwd_shared_dhidden";
-    fs.names[1] = "bwd_shared_dinput";
-    fs.names[2] = "bwd_shared_dw2";
-    fs.names[3] = "bwd_shared_dw1";
-    CHECK(ffn_bwd(c, fs, s));
-  }
-  float* du2 = nullptr;
-  if (hier) {
-    // Each group's secondary gate over the rows routed to it.
-    const int bb = p.b;
-    float* dlogits2 = at<float>(ws, b.dlogits2);
-    const int32_t* g_perm = at<int32_t>(ws, p.g_perm);
-    const int32_t* g_offsets = at<int32_t>(ws, p.g_offsets);
-    GateBwdArgs g2{};
-    g2.T = T;
-    g2.n = bb;
-    g2.k = p.k2;
-    g2.noisy = noisy2;
-    g2.logits = logits2;
-    g2.ldl = p.ldl2;
-    g2.noise = noise2;
-    g2.topk_idx = idx;
-    g2.dG = dG2;
-    g2.dload = dload_g;
-    g2.coef = coef + 2;
-    g2.dlogits = dlogits2;
-    g2.ldd = p.ldl2;
-    g2.row_token = g_perm;
-    g2.prim_idx = at<int32_t>(ws, p.prim_idx);
-    g2.k1 = p.k1;
-    g2.tile_expert = at<int32_t>(ws, p.t2_expert);
-    g2.tile_row0 = at<int32_t>(ws, p.t2_row0);
-    g2.offsets = g_offsets;
-    g2.tile_count = at<int32_t>(ws, p.t2_count);
-    g2.max_tiles = p.max_tiles2;
-    g2.tile_rows = kSecondaryBM;
-    HIP_TRY(launch_gate_bwd(g2, s));
-    const int K2 = noisy2 ? 2 * bb : bb;
-    // dW_gate2 | dW_noise2 [g] = dlogits2^T x over the group's rows
-    GemmBwdArgs gw2{};
-    gw2.A = (const uint16_t*)x;
-    gw2.lda = d;
-    gw2.rowmap_a = g_perm;
-    gw2.B = (const uint16_t*)dlogits2;
-    gw2.ldb = p.ldl2;
-    gw2.M = d;
-    gw2.N = K2;
-    gw2.C = gr->dw_gate2;
-    gw2.C2 = gr->dw_noise2;
-    gw2.ldc = d;
-    gw2.strideC = (long long)bb * d;
-    gw2.c_split = bb;
-    gw2.offsets = g_offsets;
-    gw2.n_experts = p.a;
-    HIP_TRY(launch_gemm_bwd_f32(gw2, BWD_WGRAD, BEPI_F32, "bwd_gate2_wgrad", s));
-    // the rows' input gradients dlogits2 . [W_gate2; W_noise2][g]
-    du2 = at<float>(ws, b.du2);
-    GemmBwdArgs gx2{};
-    gx2.A = (const uint16_t*)wt->w_gate2;
-    gx2.A2 = (const uint16_t*)wt->w_noise2;
-    gx2.lda = d;
-    gx2.strideA = (long long)bb * d;
-    gx2.k_split = bb;
-    gx2.B = (const uint16_t*)dlogits2;
-    gx2.ldb = p.ldl2;
-    gx2.M = d;
-    gx2.K = K2;
-    gx2.C = du2;
-    gx2.ldc = d;
-    gx2.tile_expert = g2.tile_expert;
-    gx2.tile_row0 = g2.tile_row0;
-    gx2.offsets = g_offsets;
-    gx2.tile_count = g2.tile_count;
-    gx2.max_tiles = p.max_tiles2;
-    gx2.tile_rows = kSecondaryBM;
-    HIP_TRY(launch_gemm_bwd_f32(gx2, BWD_ROWS, BEPI_F32, "bwd_gate2_dx", s));
-  }
-  HIP_TRY(launch_dx_gather(dx_gate, du_s, fb.du, slot, T, k, d, du2,
-                           hier ? at<int32_t>(ws, p.g_slot) : nullptr, p.k1, gr->dx, s));
-  return MOE_OK;
+moe_status moe_backward_saved(const moe_config* cfg, const moe_weights* wt, const float* x,
+                              const float* noise, const float* noise2, const float* dy,
+                              const float* dlosses, const moe_grads* gr, void* ws,
+                              size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  CHECK(validate(cfg));
+  CHECK(validate_bwd(*cfg));
+  if (!gr) return fail(MOE_ERR_INVALID_ARG, "grads must not be NULL");
+  CHECK(check_bwd_args(*cfg, wt, x, noise, noise2, dy, dlosses, gr));
+  return train_run(*cfg, wt, x, noise, noise2, dy, dlosses, gr, nullptr, nullptr, ws, ws_bytes,
+                   (hipStream_t)stream, false, true, "moe_backward_saved");
 }
 
 const char* moe_status_string(moe_status status) {
