@@ -15,9 +15,16 @@ HBM.  Prints one JSON line:
                the timed eager steps, against the MI355X
                peak (HBM 8 TB/s, bf16 MFMA 2.5 PFLOP/s, fp32 157.3 TFLOP/s);
   kernels      the same figures for every kernel of the step;
+  timing       also per-step HIP-event medians, p10 and p90, warm (back to
+               back) and cold (a 512 MiB write before each step evicts L2
+               and the Infinity Cache);
+  peaks_measured  attainable HBM (a 1 GiB read stream, moe_probe_hbm_read,
+               and a 1 GiB device copy) and MFMA (moe_probe_mfma) rates;
+               every roofline entry also carries its fraction of these
+               (frac_measured: HBM-bound kernels against the read stream);
   cpu_baseline the CPU oracle timed on a bounded sample of the same workload
                (its first tokens, run repeatedly for about --cpu-seconds) on
-               this host's cores;
+               this host's cores, and on one core (single_core);
   check        the GPU output on that sample against the oracle.
 
     python bench.py --backward [--steps K] [--warmup W] [--workload lm_layer]
@@ -202,6 +209,59 @@ def roofline_entry(bytes_, flops, dtype, avg_s):
                 frac=gbs / PEAK_HBM_GBS), gbs, tfs
 
 
+def event_percentiles(fn, reps, flush=None):
+    """Per-step device time of fn (HIP events on the current stream, which is
+    the library's stream), optionally after a cache flush outside the timed
+    interval: median, p10 and p90 in microseconds."""
+    pairs = []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in pairs])
+    return {"median_us": float(np.median(us)), "p10_us": float(np.percentile(us, 10)),
+            "p90_us": float(np.percentile(us, 90)), "reps": reps}
+
+
+def measure_peaks():
+    """Attainable peaks on this device, measured beside the datasheet ones:
+    HBM from a plain device copy of 1 GiB into another 1 GiB (bytes read +
+    written over the time), the matrix units from the library's MFMA loop
+    probe (moe_probe_mfma: register operands only)."""
+    import sparsely_gated_mixture_amd as moe
+    out = {}
+    n = 256 << 20  # fp32 elements: 1 GiB
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    r = event_percentiles(lambda: dst.copy_(src), 5)
+    out["hbm_copy_GB_s"] = 2 * n * 4 / (r["median_us"] * 1e-6) / 1e9
+    del dst
+    blocks, iters = 2048, 1000
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    moe.moe_probe_hbm_read(src, n * 4, blocks, sink)
+    r = event_percentiles(lambda: moe.moe_probe_hbm_read(src, n * 4, blocks, sink), 5)
+    out["hbm_read_GB_s"] = n * 4 / (r["median_us"] * 1e-6) / 1e9
+    del src
+    for name, dt in (("bf16", moe.MOE_BF16), ("f32", moe.MOE_F32)):
+        flops = moe.moe_probe_mfma(dt, blocks, iters, sink)
+        r = event_percentiles(lambda: moe.moe_probe_mfma(dt, blocks, iters, sink), 5)
+        out[f"mfma_{name}_TFLOP_s"] = flops / (r["median_us"] * 1e-6) / 1e12
+    out["method"] = ("HBM: torch copy_ of 1 GiB fp32 (read + write bytes / median of 5) and "
+                     "moe_probe_hbm_read over 1 GiB (2048 blocks, eight 16-byte loads in flight "
+                     "per thread; read bytes / median of 5); "
+                     "MFMA: moe_probe_mfma, 2048 blocks x 4 waves x 1000 iterations of 4 "
+                     "independent 32x32 MFMAs (median of 5)")
+    torch.cuda.synchronize()
+    return out
+
+
 def cpu_baseline(cfg, inp, y_gpu, idx_gpu, sample_tokens, seconds):
     """Time the CPU oracle on the first `sample_tokens` tokens (their gate,
     dispatch, experts, combine and losses) and check the GPU output there."""
@@ -229,13 +289,32 @@ def cpu_baseline(cfg, inp, y_gpu, idx_gpu, sample_tokens, seconds):
         dt += time.perf_counter() - t0
         reps += 1
     cores = oracle.num_threads()
+    # The same oracle on one core, on a smaller sample (its results do not
+    # depend on the thread count).
+    S1 = min(512, S)
+    oracle.set_num_threads(1)
+    try:
+        reps1, dt1 = 0, 0.0
+        while reps1 == 0 or dt1 < seconds / 2:
+            t0 = time.perf_counter()
+            oracle.forward(x[:S1], g["w_gate"], cfg.k, w1, w2, b_gate=g["b_gate"],
+                           w_noise=g["w_noise"], noise=None if noise is None else noise[:S1],
+                           w3=w3, mode=cfg.gate, act=cfg.act, bf16=cfg.expert_dtype == 1,
+                           capacity_factor=cfg.capacity_factor, w_importance=cfg.w_importance,
+                           w_load=cfg.w_load, alpha=cfg.alpha_switch)
+            dt1 += time.perf_counter() - t0
+            reps1 += 1
+    finally:
+        oracle.set_num_threads(cores)
     same = np.all(idx_gpu[:S] == ref["gate"].topk_idx, axis=1)
     scale = np.max(np.abs(ref["y"][same])) if same.any() else 1.0
     err = float(np.max(np.abs(y_gpu[:S][same] - ref["y"][same])) / scale) if same.any() else None
     base = {"value": S * reps / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"first {S} of {cfg.T} tokens of the {cfg.name} workload "
                       f"(gate, dispatch, experts, combine, losses in float64), "
-                      f"{reps} runs in {dt:.2f} s"}
+                      f"{reps} runs in {dt:.2f} s",
+            "single_core": {"value": S1 * reps1 / dt1, "unit": "tokens/s", "cores": 1,
+                            "sample": f"first {S1} tokens, {reps1} runs in {dt1:.2f} s"}}
     check = {"tokens": S, "routing_match": float(same.mean()), "y_max_abs_norm_err": err,
              "tolerance": 2e-2 if cfg.expert_dtype == 1 else 1e-4}
     return base, check
@@ -384,7 +463,8 @@ def main():
             rl, gbs, tfs = roofline_entry(b, f, dt, avg_s)
             entry.update({"algo_bytes": b, "GB_s": gbs, "hbm_frac": gbs / PEAK_HBM_GBS})
             if f:
-                entry.update({"flops": f, "TFLOP_s": tfs, "mfma_frac": tfs / PEAK_TFLOPS[dt]})
+                entry.update({"flops": f, "TFLOP_s": tfs, "mfma_frac": tfs / PEAK_TFLOPS[dt],
+                              "ai_flop_per_byte": f / b})
             entry["roofline"] = rl
         kernels[name] = entry
         if dominant is None or total_ms > dominant[1]:
@@ -393,6 +473,29 @@ def main():
         log(f"[bench]   {name:22s} {e['avg_us']:9.1f} us x{e['launches_per_step']:.0f}"
             + (f"  {e['GB_s']:8.1f} GB/s" if "GB_s" in e else "")
             + (f"  {e['TFLOP_s']:7.1f} TFLOP/s" if "TFLOP_s" in e else ""))
+    # Per-step device time, warm (back to back) and cold (a 512 MiB buffer
+    # written before each step, outside its events, evicts L2 and the 256 MB
+    # Infinity Cache).
+    warm = event_percentiles(eager_step, args.steps)
+    flush_buf = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
+    cold = event_percentiles(eager_step, args.steps, flush=lambda: flush_buf.fill_(1.0))
+    del flush_buf
+    log(f"[bench] per-step events: warm median {warm['median_us']:.1f} us "
+        f"(p10 {warm['p10_us']:.1f}, p90 {warm['p90_us']:.1f}); cold median "
+        f"{cold['median_us']:.1f} us (p10 {cold['p10_us']:.1f}, p90 {cold['p90_us']:.1f})")
+    peaks = measure_peaks()
+    log(f"[bench] measured peaks: read {peaks['hbm_read_GB_s']:.0f} GB/s, "
+        f"copy {peaks['hbm_copy_GB_s']:.0f} GB/s, bf16 MFMA "
+        f"{peaks['mfma_bf16_TFLOP_s']:.0f} TFLOP/s, fp32 MFMA {peaks['mfma_f32_TFLOP_s']:.1f} "
+        f"TFLOP/s")
+    for e in kernels.values():
+        rl = e.get("roofline")
+        if rl:
+            mp = (peaks["hbm_read_GB_s"] if rl["bound"] == "hbm" else
+                  peaks["mfma_bf16_TFLOP_s"] if rl["peak"] == PEAK_TFLOPS["bf16"] else
+                  peaks["mfma_f32_TFLOP_s"])
+            rl["peak_measured"] = mp
+            rl["frac_measured"] = rl["achieved"] / mp
     dname = dominant[0]
     dk = kernels[dname]
     roofline = dict(dk["roofline"])
@@ -418,7 +521,9 @@ def main():
         "kernels": kernels,
         "timing": {"mode": mode, "eager_us_per_step": eager_elapsed / args.steps * 1e6,
                    "eager_with_events_us_per_step": prof_elapsed / args.steps * 1e6,
-                   "graph_us_per_step": (graph_elapsed / args.steps * 1e6) if graph else None},
+                   "graph_us_per_step": (graph_elapsed / args.steps * 1e6) if graph else None,
+                   "warm_events": warm, "cold_events": cold},
+        "peaks_measured": peaks,
     }
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle on the first {args.cpu_sample_tokens} tokens")

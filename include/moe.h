@@ -403,6 +403,28 @@ int moe_profile_collect(void);
 moe_status moe_profile_entry(int i, char* name, size_t name_len, double* total_ms,
                              long long* launches);
 
+/* Matrix-unit peak probe, a measurement aid (not part of the layer): a loop
+ * of MFMA instructions on register operands, nothing else, so that the
+ * attainable bf16 (dtype MOE_BF16, v_mfma_f32_32x32x16_bf16) or fp32
+ * (MOE_F32, v_mfma_f32_32x32x2f32) matrix rate can be measured beside the
+ * datasheet peaks.  Launches `blocks` blocks of 4 waves; each wave runs
+ * `iters` iterations of 4 independent MFMAs.  sink: device buffer of at least
+ * blocks * 256 floats (overwritten with a checksum per lane); *flops (host,
+ * may be NULL) receives the launch's flop count.  Asynchronous on `stream`;
+ * time it with events around the call. */
+moe_status moe_probe_mfma(int32_t dtype, int32_t blocks, int32_t iters, float* sink,
+                          double* flops, void* stream);
+
+/* HBM read-bandwidth probe, a measurement aid (not part of the layer): reads
+ * the first floor(bytes / 16) * 16 bytes of the device buffer `buf` (16-byte
+ * aligned) once; each of `blocks` blocks of 256 threads streams its own
+ * contiguous segment with eight 16-byte loads per thread in flight, and
+ * writes a checksum per thread to `sink` (device, at least blocks * 256
+ * floats).  Asynchronous on `stream`; time it with
+ * events around the call. */
+moe_status moe_probe_hbm_read(const void* buf, size_t bytes, int32_t blocks, float* sink,
+                              void* stream);
+
 /* Static text for a status code. */
 const char* moe_status_string(moe_status status);
 

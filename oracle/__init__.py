@@ -74,6 +74,11 @@ def num_threads() -> int:
     return int(lib().oracle_num_threads())
 
 
+def set_num_threads(n: int) -> None:
+    """Run the oracle's OpenMP loops on n threads (results do not depend on n)."""
+    lib().oracle_set_num_threads(int(n))
+
+
 def lib():
     global _lib
     if _lib is None:
@@ -84,6 +89,8 @@ def lib():
         odp, oip = _opt(_dp), _opt(_ip)
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = c_int
+        L.oracle_set_num_threads.argtypes = [c_int]
+        L.oracle_set_num_threads.restype = None
         L.oracle_softplus.argtypes = [c_dbl]
         L.oracle_softplus.restype = c_dbl
         L.oracle_phi.argtypes = [c_dbl]

@@ -57,6 +57,13 @@
 /* Threads the OpenMP loops below use (for reporting the baseline's cores). */
 int oracle_num_threads(void) { return omp_get_max_threads(); }
 
+/* Sets the thread count of later OpenMP loops (n >= 1).  The results do not
+ * depend on it: every per-element loop writes disjoint outputs in a fixed
+ * order and every sum over tokens is serial. */
+void oracle_set_num_threads(int n) {
+  if (n >= 1) omp_set_num_threads(n);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Scalar helpers                                                            */
 /* ------------------------------------------------------------------------ */

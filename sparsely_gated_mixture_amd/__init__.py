@@ -17,7 +17,9 @@ from ._lib import (EXPORTS, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTE
                    moe_backward_saved, moe_fp8_weight_bytes, moe_forward,
                    moe_forward_train, moe_pack_fp8_weights,
                    moe_gate, moe_gate_hier, moe_last_error, moe_profile_collect,
-                   moe_profile_enable, moe_profile_entry, moe_router_bias_update,
+                   moe_probe_hbm_read, moe_probe_mfma, moe_profile_enable,
+                   moe_profile_entry,
+                   moe_router_bias_update,
                    moe_shared_ffn, moe_status_string, moe_workspace_size)
 
 load_library()
@@ -134,5 +136,6 @@ __all__ = ["workloads", "EXPORTS", "MoELayer", "pack_fp8", "moe_fp8_weight_bytes
            "moe_expert_ffn", "moe_shared_ffn", "moe_combine", "moe_aux_loss",
            "moe_router_bias_update", "moe_forward", "moe_backward_workspace_size",
            "moe_backward", "moe_forward_train", "moe_backward_saved", "N_LOSSES", "moe_status_string", "moe_last_error",
-           "moe_profile_enable", "moe_profile_collect", "moe_profile_entry", "MOE_OK",
+           "moe_probe_mfma", "moe_probe_hbm_read", "moe_profile_enable", "moe_profile_collect", "moe_profile_entry",
+           "MOE_OK",
            "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP"]

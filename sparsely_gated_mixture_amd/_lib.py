@@ -25,7 +25,7 @@ EXPORTS = ["moe_workspace_size", "moe_fp8_weight_bytes", "moe_pack_fp8_weights",
            "moe_aux_loss", "moe_router_bias_update", "moe_forward",
            "moe_backward_workspace_size", "moe_backward", "moe_forward_train",
            "moe_backward_saved", "moe_status_string",
-           "moe_last_error", "moe_profile_enable", "moe_profile_collect", "moe_profile_entry"]
+           "moe_last_error", "moe_probe_mfma", "moe_probe_hbm_read", "moe_profile_enable", "moe_profile_collect", "moe_profile_entry"]
 
 N_LOSSES = 5  # importance, load, Switch, router z-loss, -gate entropy
 
@@ -107,6 +107,11 @@ def load_library():
         [ctypes.POINTER(MoeGrads), P, S, P]
     L.moe_forward_train.argtypes = [cfgp, ctypes.POINTER(MoeWeights)] + [P] * 5 + [P, S, P]
     L.moe_backward_saved.argtypes = L.moe_backward.argtypes
+    L.moe_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P,
+                                 ctypes.POINTER(ctypes.c_double), P]
+    L.moe_probe_mfma.restype = ctypes.c_int
+    L.moe_probe_hbm_read.argtypes = [P, S, ctypes.c_int32, P, P]
+    L.moe_probe_hbm_read.restype = ctypes.c_int
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_last_error.argtypes = []
@@ -312,6 +317,20 @@ def moe_backward_saved(cfg, weights: MoeWeights, x, noise, noise2, dy, dlosses,
     _check(load_library().moe_backward_saved(ctypes.byref(c), ctypes.byref(weights), _ptr(x),
                                              _ptr(noise), _ptr(noise2), _ptr(dy),
                                              _ptr(dlosses), ctypes.byref(grads), wp, wb,
+                                             _stream(stream)))
+
+
+def moe_probe_mfma(dtype: int, blocks: int, iters: int, sink, stream=None) -> float:
+    """Launch the matrix-unit peak probe; returns its flop count."""
+    f = ctypes.c_double(0.0)
+    _check(load_library().moe_probe_mfma(int(dtype), int(blocks), int(iters), _ptr(sink),
+                                         ctypes.byref(f), _stream(stream)))
+    return f.value
+
+
+def moe_probe_hbm_read(buf, nbytes: int, blocks: int, sink, stream=None) -> None:
+    """Launch the HBM read-stream probe over the first nbytes of buf."""
+    _check(load_library().moe_probe_hbm_read(_ptr(buf), int(nbytes), int(blocks), _ptr(sink),
                                              _stream(stream)))
 
 

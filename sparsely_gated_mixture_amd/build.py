@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libmoe.so")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["gemm_f32.hip", "gemm_gate.hip", "gate.hip", "dispatch.hip", "ggemm_bf16.hip", "combine.hip",
-               "fp8.hip", "backward.hip", "ggemm_bwd.hip", "ggemm_bwd_f32.hip"]
+               "fp8.hip", "backward.hip", "ggemm_bwd.hip", "ggemm_bwd_f32.hip", "probe.hip"]
 HOST_SOURCES = ["api.cpp", "profile.cpp"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-I", CSRC, "-I", os.path.join(ROOT, "include")]

@@ -1656,6 +1656,31 @@ moe_status moe_backward_saved(const moe_config* cfg, const moe_weights* wt, cons
                    (hipStream_t)stream, false, true, "moe_backward_saved");
 }
 
+moe_status moe_probe_mfma(int32_t dtype, int32_t blocks, int32_t iters, float* sink,
+                          double* flops, void* stream) {
+  g_err[0] = 0;
+  if (dtype != MOE_BF16 && dtype != MOE_F32)
+    return fail(MOE_ERR_INVALID_ARG, "moe_probe_mfma: dtype must be MOE_BF16 or MOE_F32");
+  if (blocks <= 0 || iters <= 0)
+    return fail(MOE_ERR_INVALID_ARG, "moe_probe_mfma: blocks and iters must be positive");
+  CHECK(need(sink, "sink"));
+  if (flops)
+    *flops = (double)blocks * 4 * (double)iters * 4 * (dtype == MOE_BF16 ? 32768.0 : 4096.0);
+  HIP_TRY(launch_mfma_probe(dtype == MOE_BF16, blocks, iters, sink, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+moe_status moe_probe_hbm_read(const void* buf, size_t bytes, int32_t blocks, float* sink,
+                              void* stream) {
+  g_err[0] = 0;
+  if (blocks <= 0) return fail(MOE_ERR_INVALID_ARG, "moe_probe_hbm_read: blocks must be positive");
+  if (bytes < 16) return fail(MOE_ERR_INVALID_ARG, "moe_probe_hbm_read: bytes must be >= 16");
+  CHECK(need(buf, "buf"));
+  CHECK(need(sink, "sink"));
+  HIP_TRY(launch_hbm_read_probe(buf, (long long)bytes, blocks, sink, (hipStream_t)stream));
+  return MOE_OK;
+}
+
 const char* moe_status_string(moe_status status) {
   switch (status) {
     case MOE_OK: return "ok";

@@ -54,6 +54,13 @@ hipError_t launch_gemm_f32(const GemmF32Args& a, int bm, hipStream_t s);
 // bm rows) on the bf16 matrix cores, each fp32 operand split into three bf16
 // parts (fp32 accuracy).  K % 4 == 0.
 hipError_t launch_gemm_gate(const GemmF32Args& a, int bm, hipStream_t s);
+// Matrix-unit peak probe (probe.hip): `blocks` blocks of 4 waves, `iters`
+// iterations of 4 MFMAs each; sink receives blocks * 256 floats.
+hipError_t launch_mfma_probe(bool bf16, int blocks, int iters, float* sink, hipStream_t s);
+// HBM read-stream probe (probe.hip): reads the first bytes (rounded down to
+// 16) of buf; sink receives blocks * 256 floats.
+hipError_t launch_hbm_read_probe(const void* buf, long long bytes, int blocks, float* sink,
+                                 hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // bf16 MFMA grouped GEMM for the expert FFNs.

@@ -192,3 +192,20 @@ def test_swiglu_requires_w3_and_no_bias():
         moe.moe_expert_ffn(c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, (FAKE, 1 << 40),
                            stream=0)
     assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_mfma_probe_arguments():
+    # Rejected before any launch: unsupported dtype, empty grid, missing sink.
+    for args, what in [((moe.MOE_FP8, 1, 1, FAKE), "dtype"), ((moe.MOE_BF16, 0, 1, FAKE), "blocks"),
+                       ((moe.MOE_F32, 1, 0, FAKE), "iters"), ((moe.MOE_BF16, 1, 1, None), "sink")]:
+        with pytest.raises(moe.MoEError) as ei:
+            moe.moe_probe_mfma(*args, stream=0)
+        assert ei.value.status == moe.MOE_ERR_INVALID_ARG and what in str(ei.value), args
+
+
+def test_hbm_read_probe_arguments():
+    for args, what in [((FAKE, 1024, 0, FAKE), "blocks"), ((FAKE, 8, 1, FAKE), "bytes"),
+                       ((None, 1024, 1, FAKE), "buf"), ((FAKE, 1024, 1, None), "sink")]:
+        with pytest.raises(moe.MoEError) as ei:
+            moe.moe_probe_hbm_read(*args, stream=0)
+        assert ei.value.status == moe.MOE_ERR_INVALID_ARG and what in str(ei.value), args

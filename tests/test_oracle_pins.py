@@ -716,3 +716,29 @@ def test_fp8_expert_single_expert_numpy():
     y = oracle.expert_ffn(x, q1, q2, bf16=True)
     hid = oracle.bf16_round(np.maximum(oracle.bf16_round(x) @ q1.T, 0))
     np.testing.assert_allclose(y, hid @ q2.T, rtol=1e-12, atol=1e-12)
+
+
+def test_results_do_not_depend_on_thread_count():
+    # The CPU baseline is timed on one core and on all cores; both runs must
+    # compute the same numbers bit for bit (disjoint per-element outputs,
+    # serial sums over tokens).
+    r = rng(31)
+    T, d, n, k, h = 300, 16, 12, 3, 8
+    x = r.standard_normal((T, d))
+    wg = r.standard_normal((n, d))
+    wn = r.standard_normal((n, d))
+    z = r.standard_normal((T, n))
+    w1 = r.standard_normal((n, h, d))
+    w2 = r.standard_normal((n, d, h))
+    threads = oracle.num_threads()
+    try:
+        oracle.set_num_threads(1)
+        assert oracle.num_threads() == 1
+        one = oracle.forward(x, wg, k, w1, w2, w_noise=wn, noise=z, capacity_factor=1.0)
+        oracle.set_num_threads(max(2, threads))
+        many = oracle.forward(x, wg, k, w1, w2, w_noise=wn, noise=z, capacity_factor=1.0)
+    finally:
+        oracle.set_num_threads(threads)
+    np.testing.assert_array_equal(one["y"], many["y"])
+    np.testing.assert_array_equal(one["losses"], many["losses"])
+    np.testing.assert_array_equal(one["gate"].topk_idx, many["gate"].topk_idx)
