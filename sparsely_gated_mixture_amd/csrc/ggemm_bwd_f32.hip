@@ -142,7 +142,10 @@ __global__ __launch_bounds__(kThreads) void ggemm_bwd_f32_kernel(GemmBwdArgs p) 
 #pragma unroll
       for (int u = 0; u < 4; ++u) v[u] = h[u] > 0.f ? v[u] : 0.f;
     }
-    *(f32x4*)out = v;
+    if constexpr (MODE == BWD_WGRAD)
+      __builtin_nontemporal_store(v, (f32x4*)out);  // written once, not read again here
+    else
+      *(f32x4*)out = v;
   }
 }
 
