@@ -222,8 +222,19 @@ __global__ __launch_bounds__(256) void wgrad_reduce_kernel(const float* __restri
   const long long i4 = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
   const long long total = (long long)M * d;
   if (i4 >= total) return;
+  // The splits are added in order; their loads go out four at a time.
   f32x4 s = *(const f32x4*)(partial + i4);
-  for (int sp = 1; sp < splits; ++sp) {
+  int sp = 1;
+  for (; sp + 4 <= splits; sp += 4) {
+    f32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = *(const f32x4*)(partial + (long long)(sp + u) * total + i4);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) s[q] += v[u][q];
+  }
+  for (; sp < splits; ++sp) {
     const f32x4 v = *(const f32x4*)(partial + (long long)sp * total + i4);
 #pragma unroll
     for (int q = 0; q < 4; ++q) s[q] += v[q];
@@ -275,6 +286,11 @@ __global__ __launch_bounds__(256) void seg_colsum_kernel(const void* __restrict_
   out[(long long)e * N + c] = (float)s;
 }
 
+// dx[t] = the gate's dx + the shared expert's + the two-level secondary
+// gates' rows of the token + its kept slots' rows of dinput, added in that
+// order (slot order within each), one wavefront per token.  Lane s holds the
+// token's slot s; each pass covers 512 columns with two 16-byte vectors per
+// lane, so every source row's loads of the pass are independent.
 __global__ __launch_bounds__(256) void dx_gather_kernel(const float* __restrict__ dx_gate,
                                                         const float* __restrict__ dx_shared,
                                                         const float* __restrict__ du_perm,
@@ -283,31 +299,57 @@ __global__ __launch_bounds__(256) void dx_gather_kernel(const float* __restrict_
                                                         const float* __restrict__ du2,
                                                         const int32_t* __restrict__ slot2, int k2,
                                                         float* __restrict__ dx) {
+  constexpr int V = 2;  // 16-byte vectors per lane per pass: a 512-wide row in one pass
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const int32_t* sp = slot_pos + (long long)t * k;
-  for (int c = lane * 4; c < d; c += 256) {
-    f32x4 acc = *(const f32x4*)(dx_gate + (long long)t * d + c);
-    if (dx_shared) {
-      const f32x4 v = *(const f32x4*)(dx_shared + (long long)t * d + c);
+  // Lane s holds the token's slot s (k, k2 <= 64), broadcast with readlane.
+  const int my = lane < k ? slot_pos[(long long)t * k + lane] : -1;
+  const int my2 = lane < k2 ? slot2[(long long)t * k2 + lane] : -1;
+  for (int c0 = 0; c0 < d; c0 += 64 * 4 * V) {
+    bool ok[V];
+    long long off[V];
+    f32x4 acc[V];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] += v[q];
+    for (int v = 0; v < V; ++v) {
+      const int c = c0 + (v * 64 + lane) * 4;
+      ok[v] = c < d;
+      off[v] = c;
+      acc[v] = ok[v] ? *(const f32x4*)(dx_gate + (long long)t * d + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (dx_shared) {
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        if (ok[v]) {
+          const f32x4 x = *(const f32x4*)(dx_shared + (long long)t * d + off[v]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[v][q] += x[q];
+        }
     }
     for (int s = 0; s < k2; ++s) {  // the two-level secondary gates' rows
-      const int pos = slot2[(long long)t * k2 + s];
-      const f32x4 v = *(const f32x4*)(du2 + (long long)pos * d + c);
+      const long long pos = __builtin_amdgcn_readlane(my2, s);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] += v[q];
+      for (int v = 0; v < V; ++v)
+        if (ok[v]) {
+          const f32x4 x = *(const f32x4*)(du2 + pos * d + off[v]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[v][q] += x[q];
+        }
     }
     for (int s = 0; s < k; ++s) {
-      const int pos = sp[s];
+      const int pos = __builtin_amdgcn_readlane(my, s);
       if (pos < 0) continue;
-      const f32x4 v = *(const f32x4*)(du_perm + (long long)pos * d + c);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] += v[q];
+      for (int v = 0; v < V; ++v)
+        if (ok[v]) {
+          const f32x4 x = *(const f32x4*)(du_perm + (long long)pos * d + off[v]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[v][q] += x[q];
+        }
     }
-    *(f32x4*)(dx + (long long)t * d + c) = acc;
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      if (ok[v]) *(f32x4*)(dx + (long long)t * d + off[v]) = acc[v];
   }
 }
 
