@@ -14,7 +14,7 @@
 //  * gate_wgrad (fp32 MFMA, split over tokens) + wgrad_reduce: the gate's
 //    weight gradients dlogits^T x, partial products summed in a fixed order;
 //  * transpose_gate: [W_g; W_noise]^T for the input gradient through the
-//    gate (then the forward's fp32 GEMM);
+//    gate (then the forward's split-bf16 gate GEMM, gemm_gate.hip);
 //  * seg_colsum: per-expert column sums of bf16 rows (expert bias gradients);
 //  * dx_gather: per token, the gate's input gradient plus its kept rows'
 //    input gradients in slot order (plus the shared expert's);
