@@ -138,18 +138,24 @@ __global__ __launch_bounds__(64) void permute_kernel(const int32_t* __restrict__
   }
   for (int e = lane; e < n; e += 64) fill[e] = chunk_base[c * n + e];
   __syncthreads();
+  // Bits of an expert id (n <= 2^nbits).
+  int nbits = 0;
+  while ((1 << nbits) < n) ++nbits;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const long long a = a0 + g * 64 + lane;
     const bool ok = a < A;
     const int e = ev[g];
-    int before = 0, same = 0;
-    for (int j = 0; j < 64; ++j) {
-      const int ej = __builtin_amdgcn_readlane(e, j);
-      const int m = (ej == e) ? 1 : 0;
-      same += m;
-      before += (j < lane) ? m : 0;
+    // Lanes holding the same expert: the valid lanes, narrowed by one ballot
+    // per bit of the id; `before` counts those below this lane.
+    unsigned long long same_mask = __ballot(ok);
+    for (int b = 0; b < nbits; ++b) {
+      const unsigned long long ones = __ballot((e >> b) & 1);
+      same_mask &= ((e >> b) & 1) ? ones : ~ones;
     }
+    const int same = __popcll(same_mask);
+    const int before = (int)__builtin_amdgcn_mbcnt_hi(
+        (unsigned)(same_mask >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)same_mask, 0u));
     int base = 0;
     if (ok) base = fill[e];
     __syncthreads();  // every lane has read fill[] before the leaders update it
