@@ -209,3 +209,54 @@ def test_hbm_read_probe_arguments():
         with pytest.raises(moe.MoEError) as ei:
             moe.moe_probe_hbm_read(*args, stream=0)
         assert ei.value.status == moe.MOE_ERR_INVALID_ARG and what in str(ei.value), args
+
+
+def test_training_entry_points_validate_before_launch():
+    # moe_backward, moe_forward_train and moe_backward_saved check every
+    # pointer and the workspace before anything is enqueued.
+    c = base_cfg(d_model=64, d_hidden=64)
+    cc = _lib.make_config(c)
+    L = moe.load_library()
+    size = moe.moe_backward_workspace_size(c)
+    assert size > moe.moe_workspace_size(c)
+    # unsupported configurations report a zero backward workspace
+    assert moe.moe_backward_workspace_size(base_cfg(d_model=64, d_hidden=128, expert_dtype=2)) == 0
+    assert moe.moe_backward_workspace_size(base_cfg(d_model=96, d_hidden=64)) == 0
+    w = moe.make_weights(FAKE, w_noise=FAKE, w1=FAKE, w2=FAKE)
+    full = moe.make_grads(dx=FAKE, dw_gate=FAKE, dw_noise=FAKE, dw1=FAKE, dw2=FAKE)
+    ws = (FAKE, size)
+    # grads NULL
+    st = L.moe_backward(ctypes.byref(cc), ctypes.byref(w), FAKE, FAKE, None, FAKE, FAKE, None,
+                        FAKE, size, None)
+    assert st == moe.MOE_ERR_INVALID_ARG and "grads" in moe.moe_last_error()
+    st = L.moe_backward_saved(ctypes.byref(cc), ctypes.byref(w), FAKE, FAKE, None, FAKE, FAKE,
+                              None, FAKE, size, None)
+    assert st == moe.MOE_ERR_INVALID_ARG and "grads" in moe.moe_last_error()
+    # a required gradient missing
+    for call in (moe.moe_backward, moe.moe_backward_saved):
+        with pytest.raises(moe.MoEError) as ei:
+            call(c, w, FAKE, FAKE, None, FAKE, FAKE,
+                 moe.make_grads(dx=FAKE, dw_gate=FAKE, dw_noise=FAKE, dw2=FAKE), ws, stream=0)
+        assert ei.value.status == moe.MOE_ERR_INVALID_ARG and "dw1" in str(ei.value)
+        with pytest.raises(moe.MoEError) as ei:   # noisy gate without its noise tensor
+            call(c, w, FAKE, None, None, FAKE, FAKE, full, ws, stream=0)
+        assert ei.value.status == moe.MOE_ERR_INVALID_ARG and "noise" in str(ei.value)
+        with pytest.raises(moe.MoEError) as ei:   # workspace one byte short
+            call(c, w, FAKE, FAKE, None, FAKE, FAKE, full, (FAKE, size - 1), stream=0)
+        assert ei.value.status == moe.MOE_ERR_WORKSPACE
+    # forward_train: y and losses are required; the backward workspace, not the forward's
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_forward_train(c, w, FAKE, FAKE, None, None, FAKE, ws, stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG and "y" in str(ei.value)
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_forward_train(c, w, FAKE, FAKE, None, FAKE, None, ws, stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG and "losses" in str(ei.value)
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_forward_train(c, w, FAKE, FAKE, None, FAKE, FAKE,
+                              (FAKE, moe.moe_workspace_size(c)), stream=0)
+    assert ei.value.status == moe.MOE_ERR_WORKSPACE
+    # FP8 experts have no backward
+    c8 = base_cfg(d_model=64, d_hidden=128, expert_dtype=2)
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_forward_train(c8, w, FAKE, FAKE, None, FAKE, FAKE, ws, stream=0)
+    assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
