@@ -18,28 +18,48 @@
 namespace moe {
 namespace {
 
+// One wavefront per token.  Lane s holds the token's slot s (position and
+// weight, k <= 64), broadcast with readlane; each pass covers 512 columns
+// with two 16-byte vectors per lane, so the loads of every kept row of the
+// pass are independent.  Per element: acc = base, then acc = fma(w_s, row_s,
+// acc) in slot order.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_perm,
                                                       const int32_t* __restrict__ slot_pos,
                                                       const float* __restrict__ topk_w,
                                                       const float* __restrict__ y_base, int T,
                                                       int k, int d, float* __restrict__ y) {
+  constexpr int V = 2;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const int32_t* sp = slot_pos + (long long)t * k;
-  const float* w = topk_w + (long long)t * k;
-  for (int c = lane * 4; c < d; c += 64 * 4) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (y_base) acc = *(const f32x4*)(y_base + (long long)t * d + c);
-    for (int s = 0; s < k; ++s) {
-      const int pos = sp[s];
-      if (pos < 0) continue;
-      const float ws = w[s];
-      const f32x4 v = *(const f32x4*)(y_perm + (long long)pos * d + c);
+  const int my_pos = lane < k ? slot_pos[(long long)t * k + lane] : -1;
+  const float my_w = lane < k ? topk_w[(long long)t * k + lane] : 0.f;
+  for (int c0 = 0; c0 < d; c0 += 64 * 4 * V) {
+    bool ok[V];
+    int cc[V];
+    f32x4 acc[V];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] = fmaf(ws, v[q], acc[q]);
+    for (int v = 0; v < V; ++v) {
+      cc[v] = c0 + (v * 64 + lane) * 4;
+      ok[v] = cc[v] < d;
+      acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (y_base && ok[v]) acc[v] = *(const f32x4*)(y_base + (long long)t * d + cc[v]);
     }
-    *(f32x4*)(y + (long long)t * d + c) = acc;
+    for (int s = 0; s < k; ++s) {
+      const int pos = __builtin_amdgcn_readlane(my_pos, s);
+      if (pos < 0) continue;
+      const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), s));
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        if (ok[v]) {
+          const f32x4 x = *(const f32x4*)(y_perm + (long long)pos * d + cc[v]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[v][q] = fmaf(ws, x[q], acc[v][q]);
+        }
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      if (ok[v]) *(f32x4*)(y + (long long)t * d + cc[v]) = acc[v];
   }
 }
 
