@@ -54,6 +54,30 @@ __device__ __forceinline__ float softplus_f(float z) {
   return fmaxf(z, 0.f) + l;
 }
 
+// Phi(z) = erfc(-z / sqrt 2) / 2, branch-free.  erfc(y) for y >= 0 is the
+// Chebyshev-fitted form t exp(-y^2 + P(t)), t = 1 / (1 + y/2), of Press,
+// Teukolsky, Vetterling and Flannery, "Numerical Recipes" (2nd ed., section
+// 6.2, erfcc), fractional error below 1.2e-7; then Phi(z) = erfc(y)/2 for
+// z < 0 and 1 - erfc(y)/2 for z >= 0, y = |z| / sqrt 2.  Evaluated in fp32
+// with the hardware exp2 and reciprocal: within 2.2e-7 of Phi absolutely
+// (checked against a double-precision normal CDF over [-12, 12]).
+__device__ __forceinline__ float std_normal_cdf(float z) {
+  const float y = fabsf(z) * 0.70710678118654752f;
+  const float t = hw_rcp(fmaf(0.5f, y, 1.f));
+  float p = 0.17087277f;
+  p = fmaf(p, t, -0.82215223f);
+  p = fmaf(p, t, 1.48851587f);
+  p = fmaf(p, t, -1.13520398f);
+  p = fmaf(p, t, 0.27886807f);
+  p = fmaf(p, t, -0.18628806f);
+  p = fmaf(p, t, 0.09678418f);
+  p = fmaf(p, t, 0.37409196f);
+  p = fmaf(p, t, 1.00002368f);
+  p = fmaf(p, t, -1.26551223f);
+  const float e = t * hw_exp(fmaf(-y, y, p));  // erfc(y)
+  return z >= 0.f ? fmaf(-0.5f, e, 1.f) : 0.5f * e;
+}
+
 __device__ __forceinline__ int readlane_i(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
 __device__ __forceinline__ float readlane_f(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
@@ -268,7 +292,7 @@ __global__ __launch_bounds__(NW * 64) void topk_kernel(const TopkArgs p) {
         if (lane + 64 * q < n) {
           const float thr = ((selmask >> q) & 1u) ? v_k : v_km1;
           const float zz = (cl[q] - thr) * hw_rcp(sp[q]);
-          ld[q] += 0.5f * erfcf(-zz * 0.70710678118654752f);
+          ld[q] += std_normal_cdf(zz);
         }
       }
     }
