@@ -84,16 +84,25 @@ def sorted_gaps_near_tie(H_row, k):
     return False
 
 
-def routing_mismatches(gpu_idx, orc_idx, H, k):
-    """Tokens whose slots differ; asserts each is a near-tie and that their
-    count is within the budget.  Returns the mismatching token ids."""
+def routing_mismatches(gpu_idx, orc_idx, H, k, budget=MISMATCH_BUDGET):
+    """Tokens whose slots differ; asserts each is a near-tie, that every slot
+    the GPU chose holds a value within the near-tie distance of the oracle's
+    value of that rank (so the GPU's selection is a valid top-k), and that
+    their count is within the budget.  Returns the mismatching token ids."""
     bad = np.nonzero(np.any(gpu_idx != orc_idx, axis=1))[0]
     T = gpu_idx.shape[0]
     for t in bad:
         assert sorted_gaps_near_tie(H[t], k), (
             f"token {t} routes differently without a near-tie: gpu {gpu_idx[t]} "
             f"oracle {orc_idx[t]}")
-    assert len(bad) <= MISMATCH_BUDGET * T, f"{len(bad)} near-tie mismatches of {T} tokens"
+        ranked = np.sort(H[t])[::-1][:k]
+        chosen = H[t][gpu_idx[t]]
+        assert len(set(gpu_idx[t].tolist())) == k, f"token {t}: repeated expert"
+        assert np.all(np.abs(chosen - ranked) <=
+                      NEAR_TIE * np.maximum(np.abs(chosen), np.abs(ranked))), (
+            f"token {t}: the GPU's slots {gpu_idx[t]} are not a top-{k} within the near-tie "
+            f"distance")
+    assert len(bad) <= budget * T, f"{len(bad)} near-tie mismatches of {T} tokens"
     if len(bad):
         log(f"  near-tie routing mismatches: {len(bad)} of {T}")
     return bad
@@ -263,9 +272,11 @@ def full_size_sampled(cfg, n_sample=48, seed=0):
     return gpu
 
 
-def full_parity(cfg, T=None, aux=True):
+def full_parity(cfg, T=None, aux=True, tie_budget=MISMATCH_BUDGET):
     """End-to-end forward of `cfg` (T tokens) against the oracle, element by
-    element."""
+    element.  tie_budget: the fraction of tokens that may route differently
+    at a near-tie (the workloads' bar is 0.01 %; edge-case layouts whose
+    top-(k+1) values crowd together pass 1)."""
     T = cfg.T if T is None else T
     c = cfg.replace(T=T)
     log(f"[parity] {cfg.name} T={T} d={c.d_model} h={c.d_hidden} n={c.n_experts} k={c.k}")
@@ -275,7 +286,7 @@ def full_parity(cfg, T=None, aux=True):
     ew = expert_weights_host(inp, range(c.n_experts))
     ref = oracle_flat(c, h, ew)
     g = ref["gate"]
-    bad = routing_mismatches(gpu["topk_idx"], g.topk_idx, g.H, c.k)
+    bad = routing_mismatches(gpu["topk_idx"], g.topk_idx, g.H, c.k, tie_budget)
     ok = np.setdiff1d(np.arange(T), bad)
     np.testing.assert_allclose(gpu["topk_w"][ok], g.topk_w[ok], rtol=TOL_W_REL, atol=TOL_W)
     d = check_dispatch_exact(c, gpu, T)

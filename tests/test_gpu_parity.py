@@ -68,6 +68,18 @@ def test_forward_k_equals_n_dense():
     np.testing.assert_allclose(gpu["load"], np.full(8, 200.0), rtol=1e-6)
 
 
+@pytest.mark.parametrize("n,k", [(512, 2), (1024, 16), (2048, 64), (128, 64)])
+def test_forward_widest_gate_rows_and_largest_k(n, k):
+    # The gate epilogue's widest row layouts (8, 16 and 32 experts per lane)
+    # and the largest k (one slot per lane), noisy with a logit bias and
+    # capacity drops.  Their top-(k+1) values crowd together, so near-tie
+    # tokens may route either way (each such token's choice must still be a
+    # valid top-k); everything else is compared as in the other cases.
+    cfg = MoEConfig(f"wide{n}_k{k}", T=300, d_model=64, d_hidden=64, n_experts=n, k=k,
+                    capacity_factor=1.0, logit_bias="normal0.5", seed=90 + k)
+    full_parity(cfg, tie_budget=1.0)
+
+
 def test_forward_single_expert():
     cfg = MoEConfig("single", T=129, d_model=32, d_hidden=48, n_experts=1, k=1, noisy=False,
                     seed=79)
