@@ -65,11 +65,14 @@ def test_forward_fp8_swiglu_reduced_width():
     full_parity(PRESETS["fine_swiglu_fp8"].replace(d_model=256, d_hidden=128), T=512)
 
 
-def test_forward_fp8_odd_with_bias():
-    # n not a multiple of 8, a ragged last N tile (h = 192), zero biases
-    # through the bias epilogue.
+@pytest.mark.parametrize("bias", ["zero", "normal"])
+def test_forward_fp8_odd_with_bias(bias):
+    # n not a multiple of 8, a ragged last N tile (h = 192), expert biases
+    # (all zero, or N(0, 0.1^2) so that a misplaced bias shows) through the
+    # bias epilogue.
+    kw = dict(zero_expert_bias=True) if bias == "zero" else dict(expert_bias_std=0.1)
     cfg = MoEConfig("fp8_odd", T=300, d_model=128, d_hidden=192, n_experts=37, k=3,
-                    expert_dtype=DTYPE_FP8, zero_expert_bias=True, seed=83)
+                    expert_dtype=DTYPE_FP8, seed=83, **kw)
     full_parity(cfg)
 
 

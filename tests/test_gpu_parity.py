@@ -60,6 +60,13 @@ def test_forward_noisy_odd_shapes():
     full_parity(cfg.replace(expert_dtype=DTYPE_F32, name="odd_f32"))
 
 
+def test_forward_expert_biases_bf16():
+    # bf16 ReLU experts with nonzero biases b1, b2 ~ N(0, 0.1^2), capacity drops.
+    cfg = MoEConfig("bias_bf16", T=700, d_model=128, d_hidden=192, n_experts=24, k=2,
+                    capacity_factor=1.0, logit_bias="normal0.5", expert_bias_std=0.1, seed=84)
+    full_parity(cfg)
+
+
 def test_forward_k_equals_n_dense():
     # k = n: every expert on every token (soft routing); load is T per expert.
     cfg = MoEConfig("dense", T=200, d_model=64, d_hidden=64, n_experts=8, k=8,
