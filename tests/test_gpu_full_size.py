@@ -65,6 +65,32 @@ def test_hierarchical_element_wise():
     assert_close_rel(gpu["losses"], ref["losses"], TOL_AUX, 1e-7, "losses")
 
 
+@pytest.mark.parametrize("a,b", [(4, 128), (2, 256)])
+def test_two_level_wide_groups_element_wise(a, b):
+    # Secondary gates over 128 and 256 experts per group (two and four per
+    # lane in the grouped top-k), every output element against the oracle.
+    c = MoEConfig(f"hier_b{b}", T=192, d_model=64, d_hidden=64, n_experts=a * b, k=4,
+                  n_groups=a, k_groups=2, seed=300)
+    log(f"[parity] two-level a={a} b={b} T={c.T}")
+    inp = dev_inputs(c, c.T)
+    gpu = gpu_forward(c, inp)
+    h = host(inp)
+    ew = expert_weights_host(inp, range(c.n_experts))
+    ref = oracle.forward_hier(h["x"], h["w_gate"], h["w_noise"], h["noise"], c.k_groups,
+                              h["w_gate2"], h["w_noise2"], h["noise2"], c.k2, ew["w1"], ew["w2"],
+                              bf16=True, w_importance=c.w_importance, w_load=c.w_load,
+                              alpha=c.alpha_switch)
+    gh = ref["gate"]
+    assert not np.any(gh["near_tie"]), "the case's inputs hold a near-tie: pick another seed"
+    np.testing.assert_array_equal(gpu["topk_idx"], gh["topk_idx"])
+    np.testing.assert_allclose(gpu["topk_w"], gh["topk_w"], rtol=1e-4, atol=1e-6)
+    check_dispatch_exact(c, gpu, c.T)
+    assert max_abs_norm(gpu["y"], ref["y"]) <= y_tolerance(c)
+    assert_close_rel(gpu["importance"], gh["importance"], 1e-5, 1e-5, "importance")
+    assert_close_rel(gpu["load"], gh["load"], 1e-5, 1e-5, "load")
+    assert_close_rel(gpu["losses"], ref["losses"], TOL_AUX, 1e-7, "losses")
+
+
 def test_stage_gate_hier():
     cfg = PRESETS["hierarchical"]
     T = 2048
