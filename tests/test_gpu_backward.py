@@ -65,6 +65,10 @@ CASES = {
     "two_level_clean_f32": MoEConfig("bwd_two_level_clean", T=200, d_model=64, d_hidden=64,
                                      n_experts=64, k=4, n_groups=4, k_groups=2, noisy=False,
                                      expert_dtype=DTYPE_F32, seed=2109),
+    # a two-level layer with 128 experts per group (two per lane in the
+    # secondary gates' backward)
+    "two_level_wide": MoEConfig("bwd_two_level_wide", T=192, d_model=64, d_hidden=64,
+                                n_experts=512, k=4, n_groups=4, k_groups=2, seed=300),
     # the gate backward's wide row layouts: 16 and 32 experts per lane
     "wide_gate": MoEConfig("bwd_wide_gate", T=256, d_model=64, d_hidden=64, n_experts=1024,
                            k=4, logit_bias="normal0.5", seed=2110),
