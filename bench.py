@@ -78,10 +78,12 @@ def kernel_work(name, cfg, rows, nonempty, T):
     ng = cfg.n_groups if cfg.hierarchical else n  # the flat or primary gate's width
     ncols = 2 * ng if noisy else ng
     if cfg.hierarchical:
-        # the two-level secondary gate: T*k1 rows of 2b logits (grouped fp32 GEMM)
+        # the two-level secondary gate: T*k1 rows of 2b logits (grouped split-bf16
+        # GEMM: six bf16 products per term)
         r2, c2 = T * cfg.k_groups, (2 if noisy else 1) * cfg.b
-        if name.startswith("gemm_f32"):
-            return (r2 * d * 4 + cfg.n_groups * c2 * d * 4 + r2 * c2 * 4, 2.0 * r2 * c2 * d, "f32")
+        if name == "gate2_gemm_bf16x6":
+            return (r2 * d * 4 + cfg.n_groups * c2 * d * 4 + r2 * c2 * 4,
+                    6 * 2.0 * r2 * c2 * d, "bf16")
         if name == "gate_topk_grouped":
             return (r2 * c2 * 4 + (r2 * cfg.b * 4 if noisy else 0) + T * k * 8, 0.0, "f32")
     if name == "ggemm_bf16_relu":

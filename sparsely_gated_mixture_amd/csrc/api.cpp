@@ -460,7 +460,8 @@ moe_status run_gate_hier(const moe_config& c, const Plan& p, const float* x, con
     g.offsets = g_offsets;
     g.tile_count = t2c;
     g.max_mtiles = p.max_tiles2;
-    HIP_TRY(launch_gemm_f32(g, kSecondaryBM, s));
+    g.prof_name = "gate2_gemm_bf16x6";
+    HIP_TRY(launch_gemm_gate(g, kSecondaryBM, s));
   }
   // 4. secondary top-k per (token, primary slot) row
   TopkArgs u{};

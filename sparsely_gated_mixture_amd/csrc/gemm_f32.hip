@@ -1,9 +1,8 @@
 // fp32 GEMM on the gfx950 matrix cores (v_mfma_f32_32x32x2_f32).
 //
-// Used where the layer computes with fp32 operands on the fp32 matrix
-// instruction: the two-level layer's secondary gates (grouped rows, each
-// group's own weights) and fp32 experts.  (The flat and primary gate logits
-// use gemm_gate.hip, which reaches fp32 accuracy on the bf16 instruction.)  C = A . B^T with both operands
+// Used for fp32 experts (grouped rows, ReLU and bias fused).  The gate
+// logits (flat, primary and secondary) use gemm_gate.hip, which reaches fp32
+// accuracy on the bf16 instruction.  C = A . B^T with both operands
 // K-contiguous; tiles 64x64 (4 waves in a 2x2 grid) or 128x128 (8 waves in
 // a 2x4 grid: half the operand re-reads of 64x64 tiles, two waves per SIMD),
 // BK = 32, double-buffered LDS with register prefetch, one barrier per K

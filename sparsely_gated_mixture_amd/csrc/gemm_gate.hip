@@ -71,12 +71,26 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_gate_kernel(const GemmF32
   static_assert(CH >= 1 && FM >= 1 && FN >= 1, "bad tile shape");
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
 
-  // D rows: gate columns (W rows); D columns: tokens.
+  // D rows: gate columns (W rows); D columns: tokens.  Flat mode: tokens
+  // [mt*BN, M).  Grouped mode (a device tile map of BN-row tiles): rows
+  // [tile_row0, min(+BN, offsets[g+1])) of group g, whose weights are
+  // B1 + g*strideB1 | B2 + g*strideB2, token rows read through rowmap.
+  const bool grouped = p.tile_expert != nullptr;
   const int nW = (p.N + BM - 1) / BM;
-  const int L = xcd_tile(p.mtiles * nW);
+  const int L = xcd_tile((grouped ? *p.tile_count : p.mtiles) * nW);
   if (L < 0) return;
   const int mt = L / nW, wt = L % nW;
-  const int tok0 = mt * BN, col0 = wt * BM;
+  const int col0 = wt * BM;
+  int tok0 = mt * BN, tok_end = p.M;
+  const float* B1 = p.B1;
+  const float* B2 = p.B2;
+  if (grouped) {
+    const int g = p.tile_expert[mt];
+    tok0 = p.tile_row0[mt];
+    tok_end = min(tok0 + BN, p.offsets[g + 1]);
+    B1 += (long long)g * p.strideB1;
+    if (B2) B2 += (long long)g * p.strideB2;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
   const int K = p.K;
@@ -94,11 +108,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_gate_kernel(const GemmF32
     const int gc = col0 + rr[i];
     wok[i] = gc < p.N;
     const float* wrow =
-        gc < p.n1 ? p.B1 + (long long)gc * K : p.B2 + (long long)(gc - p.n1) * K;
-    wsrc[i] = (wok[i] ? wrow : p.B1) + kc[i];
+        gc < p.n1 ? B1 + (long long)gc * K : B2 + (long long)(gc - p.n1) * K;
+    wsrc[i] = (wok[i] ? wrow : B1) + kc[i];
     const int gt = tok0 + rr[i];
-    xok[i] = gt < p.M;
-    xsrc[i] = p.A + (long long)(xok[i] ? gt : 0) * p.lda + kc[i];
+    xok[i] = gt < tok_end;
+    const long long arow = !xok[i] ? 0 : p.rowmap ? (long long)p.rowmap[gt] : (long long)gt;
+    xsrc[i] = p.A + arow * p.lda + kc[i];
   }
   // Two register buffers: step s's fp32 chunks live in buffer s % 2, are
   // loaded two steps ahead and split into LDS one step ahead.
@@ -204,7 +219,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_gate_kernel(const GemmF32
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     const int tok = tok0 + wn * WN + j * 32 + lr;
-    if (tok >= p.M) continue;
+    if (tok >= tok_end) continue;
     float* crow = p.C + (long long)tok * p.ldc;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -226,8 +241,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_gate_kernel(const GemmF32
 }  // namespace
 
 hipError_t launch_gemm_gate(const GemmF32Args& a, int bm, hipStream_t s) {
+  if (a.bias || a.relu) return hipErrorInvalidValue;  // not an epilogue of this kernel
   const int nW = (a.N + bm - 1) / bm;
-  const long long total = (long long)a.mtiles * nW;
+  const long long total = (long long)(a.tile_expert ? a.max_mtiles : a.mtiles) * nW;
   if (total <= 0) return hipSuccess;
   const long long grid = (total + kXcds - 1) / kXcds * kXcds;
   ProfScope ps(a.prof_name ? a.prof_name : "gate_gemm_bf16x6", s);

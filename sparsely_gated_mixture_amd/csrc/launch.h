@@ -50,9 +50,10 @@ struct GemmF32Args {
 };
 // bm: 64 or 128 (BN = bm).
 hipError_t launch_gemm_f32(const GemmF32Args& a, int bm, hipStream_t s);
-// The same product in flat mode (no row map, bias or ReLU; a.mtiles M-tiles of
-// bm rows) on the bf16 matrix cores, each fp32 operand split into three bf16
-// parts (fp32 accuracy).  K % 4 == 0.
+// The same product without bias or ReLU on the bf16 matrix cores, each fp32
+// operand split into three bf16 parts (fp32 accuracy), in flat mode (a.mtiles
+// M-tiles of bm rows) or grouped mode (a tile map of bm-row tiles, row map,
+// per-group weights).  K % 4 == 0.
 hipError_t launch_gemm_gate(const GemmF32Args& a, int bm, hipStream_t s);
 // Matrix-unit peak probe (probe.hip): `blocks` blocks of 4 waves, `iters`
 // iterations of 4 MFMAs each; sink receives blocks * 256 floats.
