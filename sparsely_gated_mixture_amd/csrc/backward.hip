@@ -449,7 +449,7 @@ hipError_t launch_loss_grad(const float* importance, const float* load,
 
 int gate_wgrad_splits(int T, int d, int M) {
   const int tiles = ((d + kGwTile - 1) / kGwTile) * ((M + kGwTile - 1) / kGwTile);
-  int splits = (512 + tiles - 1) / tiles;        // about two tiles per CU
+  int splits = (256 + tiles - 1) / tiles;        // about one tile per CU
   const int max_splits = (T + 255) / 256;        // at least 256 tokens per split
   if (splits > max_splits) splits = max_splits;
   return splits < 1 ? 1 : splits;
