@@ -213,11 +213,13 @@ __global__ __launch_bounds__(kThreads, MODE == BWD_WGRAD ? 4 : 2) void ggemm_bwd
   }
 
   // --- epilogue: lane holds D[m .. m+3][c] for m = base + 8 q + 4 (lane/32)
-  if constexpr (EPI == BEPI_F32) {
-    // fp32 output: the tile goes through LDS in two halves of 64 rows c (the
-    // rows of the waves with wn == half; 16-byte chunk j of row c at
-    // j ^ (c % 32)), then each wave stores two whole 512-byte row segments per
-    // instruction.  The ring is free: the K loop ended with a barrier.
+  {
+    // The tile goes through LDS as fp32 in two halves of 64 rows c (the rows
+    // of the waves with wn == half; 16-byte chunk j of row c at j ^ (c % 32)).
+    // Then 32 lanes take one row c, four consecutive columns m each, so every
+    // instruction covers two whole row segments: 512 bytes of fp32 output, or
+    // the bf16 output with its mask / pre-activation reads, contiguous.  The
+    // ring is free: the K loop ended with a barrier.
     float* st = (float*)smem;
     const int ch = lane & 31;
     const int m = m0 + ch * 4;
@@ -257,27 +259,9 @@ __global__ __launch_bounds__(kThreads, MODE == BWD_WGRAD ? 4 : 2) void ggemm_bwd
                            ? p.C + (long long)e * p.strideC + (long long)c * p.ldc + m
                            : p.C2 + (long long)e * p.strideC + (long long)(c - p.c_split) * p.ldc + m;
           __builtin_nontemporal_store(v, (f32x4*)out);
-        } else {
+        } else if constexpr (EPI == BEPI_F32) {
           *(f32x4*)(p.C + (long long)c * p.ldc + m) = v;
-        }
-      }
-      __syncthreads();
-    }
-    return;
-  }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int c = c0 + wn * 64 + j * 32 + (lane & 31);
-    if (c >= c_end) continue;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int m = m0 + wm * 64 + i * 32 + 8 * q + 4 * (lane >> 5);
-        if (m >= p.M) continue;
-        const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                         acc[i][j][4 * q + 3]};
-        if constexpr (EPI == BEPI_RELU_MASK) {
+        } else if constexpr (EPI == BEPI_RELU_MASK) {
           const uint2 hv = *(const uint2*)(p.aux_h + (long long)c * p.ldaux + m);
           const uint32_t hw[2] = {hv.x, hv.y};
           float f[4];
@@ -304,6 +288,8 @@ __global__ __launch_bounds__(kThreads, MODE == BWD_WGRAD ? 4 : 2) void ggemm_bwd
               make_uint2(bf16x2_bits(db[0], db[1]), bf16x2_bits(db[2], db[3]));
         }
       }
+      __syncthreads();
+    }
   }
 }
 
