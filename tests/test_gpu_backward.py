@@ -168,6 +168,26 @@ def test_backward_parity(case):
         assert (ref["fwd"]["dispatch"]["slot_pos"] < 0).any(), "the case should drop slots"
 
 
+def test_backward_one_hot_many_tiles():
+    """All gate weights zero: every logit ties, the lowest-index rule sends
+    every token to experts 0 and 1, so those two experts' weight gradients
+    run over all T rows (many K-steps) and every other expert's are zero."""
+    cfg = MoEConfig("bwd_hot", T=700, d_model=64, d_hidden=128, n_experts=6, k=2, noisy=False,
+                    expert_bias_std=0.1, seed=81)
+    log("[backward] one-hot route T=700")
+    inp = make_inputs(cfg, device="cuda")
+    inp["w_gate"].zero_()
+    dy, dl = make_grad_inputs(cfg, device="cuda")
+    layer = MoELayer(cfg, inp)
+    torch.cuda.synchronize()
+    g = layer.backward(inp["x"], dy, dl)
+    torch.cuda.synchronize()
+    got = {k: v.cpu().double().numpy() for k, v in g.items()}
+    for name in ("dw1", "dw2", "db1", "db2"):
+        assert got[name][:2].any() and not got[name][2:].any(), name
+    _compare(cfg, inp, dy, dl, got)
+
+
 def test_backward_deterministic():
     cfg = CASES["lm_small"]
     _, _, _, _, a = _run(cfg)
