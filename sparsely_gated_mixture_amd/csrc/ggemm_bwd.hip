@@ -23,7 +23,8 @@
 //    and B is stored K-major like A.  Used for the weight gradients.
 // Epilogues: ReLU mask (dpre = dhid where the forward's hidden value is
 // positive) to bf16; SwiGLU (da, db from the saved pre-activations) to
-// bf16; plain fp32.
+// bf16; plain fp32.  Each one stages the finished tile through LDS, so its
+// global reads and writes cover whole row segments.
 // Operands go to LDS by direct global->LDS copies: ROWS mode keeps a ring of
 // two 32 KB stages (the next K-step's copies are issued before the current
 // step's MFMAs); WGRAD mode one stage, with four workgroups per CU.
