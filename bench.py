@@ -123,11 +123,13 @@ def kernel_work(name, cfg, rows, nonempty, T):
         return (rows * d * 4 + T * d * 4 + T * k * 8 + (T * d * 4 if hs else 0), 0.0, "f32")
     if name == "dispatch_permute":
         return (T * k * 4 * 2 + rows * 4, 0.0, "i32")
-    if name == "dispatch_hist":
-        return (T * k * 4 + ((T * k + 255) // 256) * n * 4, 0.0, "i32")
     w = 16 if (cfg.n_groups or n) <= 512 else 8
     rpb = max(2 * w, -(-((T + 255) // 256) // w) * w)
     nparts = (T + rpb - 1) // rpb
+    if name == "dispatch_hist":
+        # the flat layer's launch also sums the gate's Importance / Load partials
+        sums = 0 if cfg.n_groups else (nparts * n * 4 + n * 4) * (2 if noisy else 1)
+        return (T * k * 4 + ((T * k + 255) // 256) * n * 4 + sums, 0.0, "i32")
     if name == "gate_colsum":
         return (nparts * n * 4 + n * 4, 0.0, "f32")
     if name == "dispatch_colscan":

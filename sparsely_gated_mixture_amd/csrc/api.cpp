@@ -319,7 +319,7 @@ moe_status check_ws(void* ws, size_t ws_bytes, size_t need_bytes, const char* wh
 moe_status run_gate(const moe_config& c, const Plan& p, const float* x, const float* w_gate,
                     const float* b_gate, const float* w_noise, const float* noise,
                     int32_t* topk_idx, float* topk_w, float* importance, float* load,
-                    float* gate_stats, void* ws, hipStream_t s) {
+                    float* gate_stats, void* ws, hipStream_t s, ColsumVec* defer = nullptr) {
   const int n = c.n_experts;
   const bool noisy = w_noise != nullptr;
   float* logits = at<float>(ws, p.logits);
@@ -357,9 +357,13 @@ moe_status run_gate(const moe_config& c, const Plan& p, const float* x, const fl
   t.part_stats = gate_stats ? at<float>(ws, p.part_stats) : nullptr;
   t.rows_per_block = p.rows_per_block;
   HIP_TRY(launch_topk(t, s));
-  HIP_TRY(launch_colsum(p.nparts, ColsumVec{t.part_imp, n, importance},
-                        ColsumVec{t.part_load, n, load}, ColsumVec{t.part_stats, 2, gate_stats},
-                        s));
+  const ColsumVec sums[3] = {ColsumVec{t.part_imp, n, importance}, ColsumVec{t.part_load, n, load},
+                             ColsumVec{t.part_stats, 2, gate_stats}};
+  if (defer) {  // the caller's dispatch runs them inside its histogram launch
+    for (int i = 0; i < 3; ++i) defer[i] = sums[i];
+    return MOE_OK;
+  }
+  HIP_TRY(launch_colsum(p.nparts, sums[0], sums[1], sums[2], s));
   return MOE_OK;
 }
 
@@ -508,6 +512,10 @@ struct ForwardExtras {
   const float* load = nullptr;
   const float* gate_stats = nullptr;
   uint16_t* x_bf16 = nullptr;  // the shared expert's input, written by the gather
+  // The gate's column sums, deferred into the histogram launch (run_gate's
+  // `defer`), when colsum_fused.
+  ColsumVec colsum[3] = {};
+  bool colsum_fused = false;
 };
 
 moe_status run_dispatch(const moe_config& c, const Plan& p, const int32_t* topk_idx,
@@ -541,6 +549,11 @@ moe_status run_dispatch(const moe_config& c, const Plan& p, const int32_t* topk_
     da.alpha = c.alpha_switch;
     da.w_z = c.w_z;
     da.w_ent = c.w_entropy;
+    if (fx->colsum_fused) {
+      for (int i = 0; i < 3; ++i) da.colsum[i] = fx->colsum[i];
+      da.colsum_nparts = p.nparts;
+      da.colsum_fused = 1;
+    }
   }
   HIP_TRY(launch_dispatch(da, s));
   HIP_TRY(launch_gather(x, slot_pos, c.T, c.k, c.d_model, c.expert_dtype != MOE_F32, x_perm,
@@ -1048,7 +1061,8 @@ moe_status train_run(const moe_config& c, const moe_weights* wt, const float* x,
                         wt->w_noise2, noise2, idx, w, imp, ld, stats, ws, s, logits2, load_g));
   } else {
     CHECK(run_gate(c, p, x, wt->w_gate, wt->b_gate, wt->w_noise, noise, idx, w, imp, ld, stats,
-                   ws, s));
+                   ws, s, fx.colsum));
+    fx.colsum_fused = true;
   }
   CHECK(run_dispatch(c, p, idx, x, counts_pre, counts, offsets, perm, slot, xperm, ws, s, &fx));
   if (f32) {
@@ -1594,15 +1608,16 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const float
   float* yperm = at<float>(ws, p.f_yperm);
   const bool has_load = hier ? (wt->w_noise && wt->w_noise2) : (wt->w_noise != nullptr);
   float* stats = at<float>(ws, p.f_stats);
+  ForwardExtras fx;
   if (hier) {
     CHECK(run_gate_hier(c, p, x, wt->w_gate, wt->b_gate, wt->w_noise, noise, wt->w_gate2,
                         wt->w_noise2, noise2, idx, w, imp, ld, stats, ws, s));
   } else {
     CHECK(run_gate(c, p, x, wt->w_gate, wt->b_gate, wt->w_noise, noise, idx, w, imp, ld, stats,
-                   ws, s));
+                   ws, s, fx.colsum));
+    fx.colsum_fused = true;
   }
   const bool shared = c.d_hidden_shared > 0;
-  ForwardExtras fx;
   fx.tile_expert = at<int32_t>(ws, p.f_tile_expert);
   fx.tile_row0 = at<int32_t>(ws, p.f_tile_row0);
   fx.tile_count = at<int32_t>(ws, p.f_tile_count);

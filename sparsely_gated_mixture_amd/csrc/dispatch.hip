@@ -5,7 +5,10 @@
 //
 // The T*k (token, slot) assignments are cut into chunks of kDispatchChunk.
 //   1. chunk_hist_kernel: per-chunk expert histogram (integer LDS atomics,
-//      whose result does not depend on their order).
+//      whose result does not depend on their order).  In the layer forward
+//      the gate's fixed-order column sums ride in the same launch
+//      (hist_colsum_kernel: the first blocks histogram, the rest sum
+//      columns), which saves a launch on the path.
 //   2. column_scan_kernel: per expert, exclusive prefix over chunks, and the
 //      total count (counts_pre); four threads per expert each walk a quarter
 //      of the chunks, and the quarters are joined in order.
@@ -21,26 +24,47 @@
 //      it to each kept slot's row, converted to bf16 (RNE) or copied as fp32.
 #include <algorithm>
 
+#include "colsum.h"
 #include "common.h"
 #include "launch.h"
 
 namespace moe {
 namespace {
 
-__global__ __launch_bounds__(256) void chunk_hist_kernel(const int32_t* __restrict__ idx,
-                                                         long long A, int n,
-                                                         int32_t* __restrict__ chunk_hist) {
-  extern __shared__ int32_t hist[];
-  for (int e = threadIdx.x; e < n; e += 256) hist[e] = 0;
+// Histogram of chunk `c` into chunk_hist[c]; any block size.
+__device__ inline void chunk_hist_block(const int32_t* __restrict__ idx, long long A, int n,
+                                        int32_t* __restrict__ chunk_hist, int c, int32_t* hist) {
+  const int nt = (int)blockDim.x;
+  for (int e = threadIdx.x; e < n; e += nt) hist[e] = 0;
   __syncthreads();
-  const long long a0 = (long long)blockIdx.x * kDispatchChunk;
-  for (int i = threadIdx.x; i < kDispatchChunk; i += 256) {
+  const long long a0 = (long long)c * kDispatchChunk;
+  for (int i = threadIdx.x; i < kDispatchChunk; i += nt) {
     const long long a = a0 + i;
     if (a < A) atomicAdd(&hist[idx[a]], 1);
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < n; e += 256)
-    chunk_hist[(long long)blockIdx.x * n + e] = hist[e];
+  for (int e = threadIdx.x; e < n; e += nt) chunk_hist[(long long)c * n + e] = hist[e];
+}
+
+__global__ __launch_bounds__(256) void chunk_hist_kernel(const int32_t* __restrict__ idx,
+                                                         long long A, int n,
+                                                         int32_t* __restrict__ chunk_hist) {
+  extern __shared__ int32_t hist[];
+  chunk_hist_block(idx, A, n, chunk_hist, (int)blockIdx.x, hist);
+}
+
+// Blocks [0, nchunks) histogram their chunk; block nchunks + b sums columns
+// (b % cx) of the gate's vector b / cx (kColThreads threads either way).
+__global__ __launch_bounds__(kColThreads) void hist_colsum_kernel(
+    const int32_t* __restrict__ idx, long long A, int n, int32_t* __restrict__ chunk_hist,
+    int nchunks, const ColsumArgs cs, int nparts, int cx) {
+  extern __shared__ int32_t hist[];
+  const int b = (int)blockIdx.x;
+  if (b < nchunks) {
+    chunk_hist_block(idx, A, n, chunk_hist, b, hist);
+    return;
+  }
+  colsum_block(cs, nparts, (b - nchunks) % cx, (b - nchunks) / cx);
 }
 
 // 64 experts per block; thread (e, q) covers chunks [q*G, (q+1)*G).
@@ -297,7 +321,20 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   const int n = a.n;
   const int nchunks = (int)((A + kDispatchChunk - 1) / kDispatchChunk);
   const size_t shm = (size_t)n * sizeof(int32_t);
-  if (nchunks > 0) {
+  if (a.colsum_fused) {
+    ColsumArgs cs;
+    int nmax;
+    const int nv = colsum_pack(a.colsum, cs, nmax);
+    const int cx = (nmax + 63) / 64;
+    const int blocks = nchunks + cx * nv;
+    if (blocks > 0) {
+      ProfScope ps("dispatch_hist", s);
+      hist_colsum_kernel<<<dim3(blocks), dim3(kColThreads), shm, s>>>(
+          a.topk_idx, A, n, a.chunk_hist, nchunks, cs, a.colsum_nparts, cx > 0 ? cx : 1);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  } else if (nchunks > 0) {
     ProfScope ps("dispatch_hist", s);
     chunk_hist_kernel<<<dim3(nchunks), dim3(256), shm, s>>>(a.topk_idx, A, n, a.chunk_hist);
     hipError_t e = hipGetLastError();

@@ -25,6 +25,7 @@
 // blocks write partial vectors that a second kernel adds in block order.
 #include <math.h>
 
+#include "colsum.h"
 #include "common.h"
 #include "launch.h"
 
@@ -601,34 +602,9 @@ __global__ __launch_bounds__(NW * 64) void gate_bwd_kernel(const GateBwdArgs p) 
   }
 }
 
-// out[j] = sum of part[p][j] over p.  64 columns per block; 16 part-lanes per
-// column each add every 16th partial in ascending order (coalesced rows,
-// many loads in flight), then lane sums are added in lane order: the same
-// order on every call.
-constexpr int kColLanes = 16;
-// blockIdx.y selects the vector.
-struct ColsumArgs {
-  ColsumVec v[3];
-};
-__global__ __launch_bounds__(1024) void colsum_kernel(const ColsumArgs a, int nparts) {
-  __shared__ double sh[kColLanes][64];
-  const float* part = a.v[blockIdx.y].part;
-  float* out = a.v[blockIdx.y].out;
-  const int n = a.v[blockIdx.y].n;
-  const int c = threadIdx.x & 63, q = threadIdx.x >> 6;
-  const int j = blockIdx.x * 64 + c;
-  double s = 0.0;
-  if (j < n) {
-#pragma unroll 8
-    for (int p = q; p < nparts; p += kColLanes) s += (double)part[(long long)p * n + j];
-  }
-  sh[q][c] = s;
-  __syncthreads();
-  if (q == 0 && j < n) {
-    double t = 0.0;
-    for (int r = 0; r < kColLanes; ++r) t += sh[r][c];
-    out[j] = (float)t;
-  }
+// The gate's column sums in their own launch; blockIdx.y selects the vector.
+__global__ __launch_bounds__(kColThreads) void colsum_kernel(const ColsumArgs a, int nparts) {
+  colsum_block(a, nparts, (int)blockIdx.x, (int)blockIdx.y);
 }
 
 // One block: the secondary tiles' statistics in tile order, plus the
@@ -732,16 +708,13 @@ hipError_t launch_gate_bwd(const GateBwdArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_colsum(int nparts, ColsumVec v0, ColsumVec v1, ColsumVec v2, hipStream_t s) {
-  ColsumArgs a{};
-  int nv = 0, nmax = 0;
-  for (const ColsumVec& v : {v0, v1, v2})
-    if (v.part && v.n > 0) {
-      a.v[nv++] = v;
-      nmax = v.n > nmax ? v.n : nmax;
-    }
+  const ColsumVec v[3] = {v0, v1, v2};
+  ColsumArgs a;
+  int nmax;
+  const int nv = colsum_pack(v, a, nmax);
   if (nv == 0) return hipSuccess;
   ProfScope ps("gate_colsum", s);
-  colsum_kernel<<<dim3((nmax + 63) / 64, nv), dim3(64 * kColLanes), 0, s>>>(a, nparts);
+  colsum_kernel<<<dim3((nmax + 63) / 64, nv), dim3(kColThreads), 0, s>>>(a, nparts);
   return hipGetLastError();
 }
 

@@ -287,6 +287,12 @@ struct DispatchArgs {
   const float* load;
   const float* gate_stats;  // [2] or null: z-loss and entropy sums
   float w_imp, w_load, alpha, w_z, w_ent;
+  // Optional: the gate's column sums (its per-block Importance / Load /
+  // statistics partials over colsum_nparts parts) run inside the histogram
+  // launch instead of a launch of their own (colsum_fused != 0).
+  ColsumVec colsum[3];
+  int colsum_nparts;
+  int colsum_fused;
 };
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
 // Scatter each token's row to its kept slots: x_perm[slot_pos[t, s]] =
