@@ -224,7 +224,8 @@ moe_status moe_gate_hier(const moe_config* cfg, const float* x, const float* w_g
  *      first served in (token, slot) order),
  *      x_perm [T*k, d] = x[perm[row]] converted to expert_dtype (bf16 round
  *      to nearest even).
- * topk_idx entries must lie in [0, n). */
+ * topk_idx entries should lie in [0, n); an entry outside it is treated like a
+ * slot dropped for capacity (slot_pos -1, counted in no expert). */
 moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, const float* x,
                         int32_t* counts_pre, int32_t* counts, int32_t* offsets, int32_t* perm,
                         int32_t* slot_pos, void* x_perm, void* ws, size_t ws_bytes,

@@ -40,7 +40,10 @@ __device__ inline void chunk_hist_block(const int32_t* __restrict__ idx, long lo
   const long long a0 = (long long)c * kDispatchChunk;
   for (int i = threadIdx.x; i < kDispatchChunk; i += nt) {
     const long long a = a0 + i;
-    if (a < A) atomicAdd(&hist[idx[a]], 1);
+    if (a < A) {
+      const int e = idx[a];
+      if ((unsigned)e < (unsigned)n) atomicAdd(&hist[e], 1);  // ids outside [0, n): no expert
+    }
   }
   __syncthreads();
   for (int e = threadIdx.x; e < n; e += nt) chunk_hist[(long long)c * n + e] = hist[e];
@@ -168,8 +171,8 @@ __global__ __launch_bounds__(64) void permute_kernel(const int32_t* __restrict__
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const long long a = a0 + g * 64 + lane;
-    const bool ok = a < A;
     const int e = ev[g];
+    const bool ok = a < A && (unsigned)e < (unsigned)n;  // ids outside [0, n): dropped
     // Lanes holding the same expert: the valid lanes, narrowed by one ballot
     // per bit of the id; `before` counts those below this lane.
     unsigned long long same_mask = __ballot(ok);
@@ -194,6 +197,8 @@ __global__ __launch_bounds__(64) void permute_kernel(const int32_t* __restrict__
       } else {
         slot_pos[a] = -1;
       }
+    } else if (a < A) {
+      slot_pos[a] = -1;
     }
   }
 }

@@ -173,6 +173,56 @@ def _ws(cfg):
     return torch.empty(moe.moe_workspace_size(cfg), dtype=torch.uint8, device="cuda")
 
 
+@pytest.mark.parametrize("cf", [0.0, 1.0])
+def test_dispatch_out_of_range_ids_dropped(cf):
+    """Expert ids outside [0, n) handed to moe_dispatch are dropped like
+    over-capacity slots (slot_pos -1) and counted in no expert; the valid
+    ids are dispatched exactly as the definition orders them."""
+    c = MoEConfig("oob", T=300, d_model=64, d_hidden=64, n_experts=16, k=2, capacity_factor=cf,
+                  seed=90)
+    T, n, k, d = c.T, c.n_experts, c.k, c.d_model
+    rng = np.random.default_rng(90)
+    idx = rng.integers(0, n, size=(T, k)).astype(np.int32)
+    bad = rng.random((T, k)) < 0.1
+    idx[bad] = np.where(rng.random(int(bad.sum())) < 0.5, n, -1).astype(np.int32)
+    log(f"[dispatch] out-of-range ids: {int(bad.sum())} of {T * k}, cf={cf}")
+    x = torch.randn((T, d), generator=torch.Generator().manual_seed(90)).to("cuda")
+    i32 = dict(dtype=torch.int32, device="cuda")
+    cp, cn, off = (torch.empty(n, **i32), torch.empty(n, **i32), torch.empty(n + 1, **i32))
+    perm = torch.empty(T * k, **i32)
+    slot = torch.empty((T, k), **i32)
+    xp = torch.empty((T * k, d), dtype=torch.bfloat16, device="cuda")
+    moe.moe_dispatch(c, torch.from_numpy(idx).to("cuda"), x, cp, cn, off, perm, slot, xp, _ws(c))
+    torch.cuda.synchronize()
+    # the definition, slot by slot in (token, slot) order
+    valid = (idx >= 0) & (idx < n)
+    counts_pre = np.bincount(idx[valid], minlength=n)
+    cap = math.floor(cf * T * k / n) if cf > 0 else T * k
+    counts = np.minimum(counts_pre, cap)
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    fill = np.zeros(n, dtype=np.int64)
+    slot_ref = np.full((T, k), -1, dtype=np.int64)
+    perm_ref = np.zeros(int(offsets[-1]), dtype=np.int64)
+    for t in range(T):
+        for s in range(k):
+            e = idx[t, s]
+            if not valid[t, s]:
+                continue
+            r = fill[e]
+            fill[e] += 1
+            if r < cap:
+                slot_ref[t, s] = offsets[e] + r
+                perm_ref[offsets[e] + r] = t
+    np.testing.assert_array_equal(cp.cpu().numpy(), counts_pre)
+    np.testing.assert_array_equal(cn.cpu().numpy(), counts)
+    np.testing.assert_array_equal(off.cpu().numpy(), offsets)
+    np.testing.assert_array_equal(slot.cpu().numpy(), slot_ref)
+    rows = int(offsets[-1])
+    np.testing.assert_array_equal(perm.cpu().numpy()[:rows], perm_ref)
+    xb = oracle.bf16_round(x.cpu().double().numpy()[perm_ref])
+    np.testing.assert_array_equal(xp[:rows].float().cpu().numpy().astype(np.float64), xb)
+
+
 @pytest.mark.parametrize("name", ["tiny_f32", "lm_layer", "switch_cf", "fine_swiglu",
                                   "sigmoid_shared"])
 def test_stage_gate(name):
