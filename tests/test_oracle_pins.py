@@ -333,7 +333,7 @@ def _dispatch_brute(idx, n, cf):
     return lists, dropped, cap
 
 
-@pytest.mark.parametrize("cf", [0.0, 0.5, 1.0, 1.25, 3.0])
+@pytest.mark.parametrize("cf", [0.0, 0.5, 1.0, 1.25, 3.0, 1e30, 1e300])
 def test_dispatch_brute_force(cf):
     r = rng(4)
     for (T, n, k) in [(1, 1, 1), (9, 4, 2), (33, 7, 3), (64, 5, 1), (40, 16, 4)]:
@@ -621,6 +621,80 @@ def test_hierarchical_one_group_reduces_to_flat():
     prim = hier["gate"]["primary"].H
     np.testing.assert_allclose(hier["losses"][3], flat["losses"][3] + float(np.sum(prim * prim)) / T,
                                rtol=1e-12)
+
+
+def _two_level_golden():
+    with open(os.path.join(GOLDEN, "two_level_layer.json")) as f:
+        g = json.load(f)
+    ns = {"L": math.log(2.0), "Phi": lambda z: float(ndtr(z)),
+          "p": math.exp(0.5) / (1 + math.exp(0.5)), "q": 1 / (1 + math.exp(0.5))}
+
+    def ev(v):
+        if isinstance(v, list):
+            return [ev(u) for u in v]
+        if isinstance(v, str):
+            return float(eval(v, {"__builtins__": {}}, ns))
+        return v
+    return g, ev
+
+
+def two_level_golden_inputs():
+    """The hand-worked two-level case of tests/golden/two_level_layer.json as
+    arrays (noise weights and draws all zero)."""
+    g, ev = _two_level_golden()
+    inp = g["inputs"]
+    T, d, a, b, k1 = inp["T"], inp["d"], inp["a"], inp["b"], inp["k1"]
+    return dict(x=np.array(inp["x"], float), w_gate=np.array(inp["w_gate"], float),
+                w_noise=np.zeros((a, d)), noise=np.zeros((T, a)),
+                w_gate2=np.array(inp["w_gate2"], float), w_noise2=np.zeros((a, b, d)),
+                noise2=np.zeros((T, k1, b)), k1=k1, k2=inp["k2"]), g, ev
+
+
+def test_golden_two_level_load():
+    """The two-level Importance and Load against the hand-worked case: four
+    groups reached by 3, 2, 1 and 0 (token, slot) pairs, so Load_primary[g],
+    |X_g| and T all differ and one group is empty.  Reading of [NOTES]
+    "分层 MoE" with [PAPER] "負載平衡損失": Load_H[g*b+e] =
+    Load_primary[g] * Load_g[e] / |X_g|, 0 for an unreached group."""
+    inp, g, ev = two_level_golden_inputs()
+    exp = g["expected"]
+    out = oracle.gate_hier(inp["x"], inp["w_gate"], inp["w_noise"], inp["noise"], inp["k1"],
+                           inp["w_gate2"], inp["w_noise2"], inp["noise2"], inp["k2"])
+    pg = out["primary"]
+    np.testing.assert_array_equal(pg.topk_idx, exp["primary_topk_idx"])
+    np.testing.assert_allclose(pg.topk_w, ev(exp["primary_topk_w"]), rtol=1e-15)
+    lp = np.array(ev(exp["load_primary"]))
+    np.testing.assert_allclose(pg.load, lp, rtol=1e-14)
+    np.testing.assert_array_equal(out["group_tokens"], exp["group_tokens"])
+    ls = np.array(ev(exp["load_secondary"]))
+    np.testing.assert_allclose(out["load_secondary"], ls, rtol=1e-14, atol=0)
+    np.testing.assert_array_equal(out["topk_idx"], exp["topk_idx"])
+    np.testing.assert_allclose(out["topk_w"], ev(exp["topk_w"]), rtol=1e-15)
+    np.testing.assert_allclose(out["importance"], ev(exp["importance"]), rtol=1e-15, atol=0)
+    want = np.array(ev(exp["load"]))
+    np.testing.assert_allclose(out["load"], want, rtol=1e-14, atol=0)
+    assert np.all(out["load"][9:] == 0.0)  # the unreached group
+
+    # The case separates the reading from its plausible misreadings: each of
+    # these differs from the hand values by far more than the tolerance.
+    a, b = ls.shape
+    T = inp["x"].shape[0]
+    gt = np.array(exp["group_tokens"], float)
+    reached = gt > 0
+    no_primary = np.where(reached[:, None], ls, 0.0).ravel()
+    over_T = np.where(reached[:, None], lp[:, None] * ls / T, 0.0).ravel()
+    counts_for_load = np.where(reached[:, None], gt[:, None] * ls / np.maximum(gt, 1)[:, None],
+                               0.0).ravel()
+    transposed = np.where(reached[:, None], lp[:, None] * ls / np.maximum(gt, 1)[:, None],
+                          0.0).T.ravel()
+    for wrong in (no_primary, over_T, counts_for_load, transposed):
+        assert np.max(np.abs(wrong - want)) > 1e-3
+
+    # The two-level loss is w_load * CV^2 over all a*b entries.
+    losses = oracle.aux(T, 2, out["importance"], out["load"],
+                        oracle.dispatch(out["topk_idx"], a * b)["counts_pre"], 0.1, 0.1, 1.0)
+    cv2 = np.mean((want - want.mean()) ** 2) / want.mean() ** 2
+    assert losses[1] == pytest.approx(0.1 * cv2, rel=1e-13)
 
 
 def test_hierarchical_matches_dense_two_level_sum():
