@@ -90,7 +90,7 @@ typedef struct {
                              MOE_FP8 needs d_model and d_hidden multiples of 64 */
   int32_t n_groups;       /* two-level layer: a groups of b = n/a experts; 0 = flat */
   int32_t k_groups;       /* two-level layer: k1 groups per token, k = k1*k2 */
-  float capacity_factor;  /* > 0: expert capacity floor(cf*T*k/n); <= 0: none */
+  float capacity_factor;  /* > 0: expert capacity min(floor(cf*T*k/n), T*k); <= 0: none */
   float w_importance;     /* weight of CV(Importance)^2 */
   float w_load;           /* weight of CV(Load)^2 */
   float alpha_switch;     /* weight of n * sum_i f_i P_i */

@@ -395,7 +395,10 @@ void oracle_load(int T, int n, int k, const double* clean, const double* sp,
 int oracle_dispatch(int T, int k, int n, double cf, const int32_t* topk_idx, int32_t* counts_pre,
                     int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* slot_pos) {
   int64_t cap = INT64_MAX;
-  if (cf > 0.0) cap = (int64_t)floor(cf * (double)T * (double)k / (double)n);
+  /* An expert receives at most T*k pairs, so any capacity above that is no
+   * limit; clamping before the conversion keeps it defined for every finite
+   * cf. */
+  if (cf > 0.0) cap = (int64_t)fmin(floor(cf * (double)T * (double)k / (double)n), (double)T * k);
   for (int e = 0; e < n; ++e) counts_pre[e] = 0;
   for (int64_t a = 0; a < (int64_t)T * k; ++a) counts_pre[topk_idx[a]] += 1;
   for (int e = 0; e < n; ++e) counts[e] = (int32_t)(counts_pre[e] < cap ? counts_pre[e] : cap);

@@ -3,6 +3,7 @@
 // so a failing call enqueues nothing.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -120,8 +121,12 @@ moe_status validate(const moe_config* c) {
 
 long long capacity(const moe_config& c) {
   if (!(c.capacity_factor > 0.f)) return (long long)1 << 62;
-  return (long long)std::floor((double)c.capacity_factor * (double)c.T * (double)c.k /
-                               (double)c.n_experts);
+  // No expert can receive more than T*k slots, so a larger capacity is the
+  // same as T*k; clamping first keeps the conversion defined for any finite
+  // factor.
+  const double all = (double)c.T * (double)c.k;
+  const double cap = std::floor((double)c.capacity_factor * all / (double)c.n_experts);
+  return (long long)std::min(cap, all);
 }
 
 long long round_up(long long v, long long m) { return (v + m - 1) / m * m; }

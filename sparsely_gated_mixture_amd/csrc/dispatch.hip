@@ -17,9 +17,9 @@
 //      map and the auxiliary losses (all single-block work, one launch).
 //   4. permute_kernel: one wavefront walks its chunk in order, 64 slots at a
 //      time; a slot's rank inside its group of 64 is the number of earlier
-//      lanes with the same expert (found with wave-uniform readlanes), so
-//      the resulting order is exactly (token, slot) order -- stable, and
-//      independent of scheduling.
+//      lanes with the same expert (the lanes holding the same id are found
+//      with one ballot per bit of the expert id), so the resulting order is
+//      exactly (token, slot) order -- stable, and independent of scheduling.
 //   5. gather_kernel: one wavefront per token reads its row once and writes
 //      it to each kept slot's row, converted to bf16 (RNE) or copied as fp32.
 #include <algorithm>

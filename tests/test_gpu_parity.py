@@ -150,6 +150,15 @@ def test_capacity_boundaries():
     assert gpu["slot_pos"][10, 0] == -1 and np.all(gpu["slot_pos"][:10, 0] >= 0)
     np.testing.assert_array_equal(gpu["y"][10], 0.0)
     check_dispatch_exact(cfg, gpu, T)
+    # A capacity factor far above any count (finite, but floor(cf*T*k/n)
+    # exceeds every integer type) drops nothing: the same layer as no limit.
+    log("[parity] capacity factor 1e30")
+    big = gpu_forward(cfg.replace(capacity_factor=1e30), inp)
+    free = gpu_forward(cfg.replace(capacity_factor=0.0), inp)
+    for key in ("counts_pre", "counts", "offsets", "perm", "slot_pos", "y"):
+        np.testing.assert_array_equal(big[key], free[key], err_msg=key)
+    np.testing.assert_array_equal(big["counts"], [11, 10, 9, 10])
+    check_dispatch_exact(cfg.replace(capacity_factor=1e30), big, T)
 
 
 def test_determinism_bitwise():
