@@ -1,19 +1,26 @@
 """Benchmark of the MoE layer forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload lm_layer]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload fine_swiglu]
 
 One step is one moe_forward call over one batch: gate GEMM + gate epilogue
 (noise, top-k, softmax, importance/load), dispatch (histogram, scan,
 permutation, gather), the two grouped expert GEMMs, combine and the aux
-losses.  Inputs and weights are seeded synthetic tensors already resident in
-HBM.  Prints one JSON line:
+losses.  The default workload is the largest single-GPU one, the
+fine-grained layer (T=4096, d=7168, 256 SwiGLU experts of hidden 2048,
+top-8, Zipf-skewed routing); --workload picks another preset.  Inputs and
+weights are seeded synthetic tensors already resident in HBM.  Prints one
+JSON line:
   value        tokens/s over K back-to-back steps (host clock around the
-               synchronised loop);
+               synchronised loop); the per-step HIP-event medians with and
+               without a cache flush before each step are in `timing`;
   roofline     the dominant kernel's algorithmic bytes (or flops) per launch
                over its average duration, measured with HIP events recorded
                on the library's stream (moe_profile_*) around every launch of
                the timed eager steps, against the MI355X
                peak (HBM 8 TB/s, bf16 MFMA 2.5 PFLOP/s, fp32 157.3 TFLOP/s);
+               `traffic` is the kernel's HBM bytes per launch from the
+               rocprofv3 counter summary under profiles/, reported only while
+               the kernel's source is the one the counters were taken on;
   kernels      the same figures for every kernel of the step;
   timing       also per-step HIP-event medians, p10 and p90, warm (back to
                back) and cold (a 512 MiB write before each step evicts L2
@@ -23,8 +30,9 @@ HBM.  Prints one JSON line:
                every roofline entry also carries its fraction of these
                (frac_measured: HBM-bound kernels against the read stream);
   cpu_baseline the CPU oracle timed on a bounded sample of the same workload
-               (its first tokens, run repeatedly for about --cpu-seconds) on
-               this host's cores, and on one core (single_core);
+               (its first tokens: gate, dispatch, every expert they reach,
+               combine, losses; each expert's weights are copied to the host
+               outside the timed parts) on this host's cores;
   check        the GPU output on that sample against the oracle.
 
     python bench.py --backward [--steps K] [--warmup W] [--workload lm_layer]
@@ -42,8 +50,10 @@ line shape, same cpu_baseline (the oracle's backward includes its forward).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -56,12 +66,34 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer fwd tokens/sec at 1 GPU; expert-GEMM % MFMA peak; routing % HBM BW"
 PEAK_HBM_GBS = 8000.0
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
-# HBM bytes per launch of a kernel at a workload: rocprofv3 --pmc FETCH_SIZE
-# and WRITE_SIZE (separate runs, KiB per dispatch), each scaled by what the
-# same counter reads for a plain copy of known size (FETCH_SIZE x 2.0,
-# WRITE_SIZE x 1.0).  An entry is removed whenever its kernel changes; a
-# missing entry reports null.
-TRAFFIC_BYTES = {("lm_layer", "ggemm_bf16_out"): 422259896}
+DEFAULT_WORKLOAD = "fine_swiglu"
+# Gate GEMMs computed as fp32 contractions from six bf16 products per term.
+SPLIT_GATE_KERNELS = ("gate_gemm_bf16x6", "gate2_gemm_bf16x6", "bwd_gate_dx")
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` at `workload` from the committed
+    rocprofv3 summary profiles/<workload>_ggemm_traffic.txt: FETCH_SIZE and
+    WRITE_SIZE (separate --pmc runs, KiB per dispatch), each scaled by what
+    the same counter reads for a plain copy of known size.  A summary line
+      # traffic_bytes <kernel> <bytes> source <file> sha256 <hex>
+    carries the hash of the kernel's source file when the counters were
+    taken; a different source today (the kernel changed) gives None."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_ggemm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    pat = re.compile(r"^# traffic_bytes (\S+) (\d+) source (\S+) sha256 ([0-9a-f]+)$")
+    for line in open(path):
+        m = pat.match(line.strip())
+        if not m or m.group(1) != kernel:
+            continue
+        src = os.path.join(ROOT, m.group(3))
+        if not os.path.exists(src):
+            return None
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != m.group(4):
+            return None
+        return int(m.group(2))
+    return None
 
 
 def log(*a):
@@ -83,7 +115,7 @@ def kernel_work(name, cfg, rows, nonempty, T):
         r2, c2 = T * cfg.k_groups, (2 if noisy else 1) * cfg.b
         if name == "gate2_gemm_bf16x6":
             return (r2 * d * 4 + cfg.n_groups * c2 * d * 4 + r2 * c2 * 4,
-                    6 * 2.0 * r2 * c2 * d, "bf16")
+                    2.0 * r2 * c2 * d, "f32")
         if name == "gate_topk_grouped":
             return (r2 * c2 * 4 + (r2 * cfg.b * 4 if noisy else 0) + T * k * 8, 0.0, "f32")
     if name == "ggemm_bf16_relu":
@@ -111,8 +143,10 @@ def kernel_work(name, cfg, rows, nonempty, T):
     if name == "shared_bf16_out":
         return (d * hs * 2 + T * hs * 2 + T * d * 4, 2.0 * T * d * hs, "bf16")
     if name == "gate_gemm_bf16x6":
-        # fp32 operands split into three bf16 parts, six bf16 products per term
-        return (T * d * 4 + ncols * d * 4 + T * ncols * 4, 6 * 2.0 * T * ncols * d, "bf16")
+        # The method's work is one fp32 contraction (2*T*d*ncols flops, graded
+        # against the fp32 peak); the kernel reaches fp32 accuracy with six
+        # bf16 products per term (their rate is reported beside it).
+        return (T * d * 4 + ncols * d * 4 + T * ncols * 4, 2.0 * T * ncols * d, "f32")
     if name.startswith("gemm_f32"):
         return (T * d * 4 + ncols * d * 4 + T * ncols * 4, 2.0 * T * ncols * d, "f32")
     if name == "gate_topk":
@@ -175,8 +209,8 @@ def bwd_kernel_work(name, cfg, rows, nonempty, T):
         return (T * d * 2 + T * hws * 2 + hws * d * 4, 2.0 * T * hws * d, "bf16")
     if name == "bwd_gate_wgrad":
         return (T * d * 4 + T * M * 4 + M * d * 4, 2.0 * T * M * d, "f32")
-    if name == "bwd_gate_dx":  # split-bf16 GEMM: six bf16 products per term
-        return (T * M * 4 + M * d * 4 + T * d * 4, 6 * 2.0 * T * M * d, "bf16")
+    if name == "bwd_gate_dx":  # an fp32 contraction (split-bf16 GEMM: six bf16 products per term)
+        return (T * M * 4 + M * d * 4 + T * d * 4, 2.0 * T * M * d, "f32")
     if name == "bwd_combine":
         return (T * d * 4 + rows * d * 4 + rows * d * 2 + T * k * 12, 0.0, "f32")
     if name == "bwd_gate":
@@ -267,60 +301,120 @@ def measure_peaks():
 
 
 def cpu_baseline(cfg, inp, y_gpu, idx_gpu, sample_tokens, seconds):
-    """Time the CPU oracle on the first `sample_tokens` tokens (their gate,
-    dispatch, experts, combine and losses) and check the GPU output there."""
+    """The CPU oracle on the first S tokens of the batch, stage by stage: the
+    gate (flat or two-level), dispatch, every expert those tokens reach (and
+    the shared expert), combine and the losses, all in float64.  Each
+    expert's weights are copied to the host outside the timed parts, so the
+    figure is the oracle's own compute.  Without `sample_tokens`, S doubles
+    from 16 until a pass takes a quarter of `seconds`, then grows so that one
+    pass takes about half of it.  Where the
+    weights fit on the host (at most 16 GiB in float64) they are kept and the
+    pass repeats until `seconds` have passed; the same oracle also runs on
+    one core on a smaller sample.  The GPU's y on the sample is checked
+    against the oracle's on every token the two route alike."""
     import oracle
     from sparsely_gated_mixture_amd.workloads import to_numpy64
-    S = min(sample_tokens, cfg.T)
-    x = to_numpy64(inp["x"][:S])
-    g = {k: to_numpy64(inp[k]) for k in ("w_gate", "b_gate", "w_noise")}
-    noise = to_numpy64(inp["noise"][:S]) if inp.get("noise") is not None else None
-    w1 = to_numpy64(inp["w1"])
-    w2 = to_numpy64(inp["w2"])
-    w3 = to_numpy64(inp["w3"]) if inp.get("w3") is not None else None
     oracle.lib()
-    # The same sample is run back to back until about `seconds` of wall time
-    # have passed, so that the rate is not a one-second figure.
-    reps, dt = 0, 0.0
-    while reps == 0 or dt < seconds:
+    T, d, n, k = cfg.T, cfg.d_model, cfg.n_experts, cfg.k
+    bf = cfg.expert_dtype != 0
+    hk = {key: to_numpy64(inp.get(key)) for key in ("w_gate", "b_gate", "w_noise", "w_gate2",
+                                                    "w_noise2", "ws1", "ws3", "ws2")}
+    names = [nm for nm in ("w1", "w3", "w2", "b1", "b2") if inp.get(nm) is not None]
+    per_expert = sum(inp[nm][0].numel() * 8 for nm in names)
+    keep = n * per_expert <= (16 << 30)
+    cache = {}
+
+    def weights(e):
+        if e in cache:
+            return cache[e]
+        w = {nm: (inp[nm][e].to(torch.float64).cpu().numpy() if nm in names else None)
+             for nm in ("w1", "w3", "w2", "b1", "b2")}
+        if cfg.expert_dtype == 2:  # FP8: the values the codes stand for
+            for nm in ("w1", "w3", "w2"):
+                if w[nm] is not None:
+                    w[nm] = oracle.dequantize_fp8_rows(*oracle.quantize_fp8_rows(w[nm]))
+        if keep:
+            cache[e] = w
+        return w
+
+    def one_pass(S):
+        """(seconds of oracle compute, topk_idx, y) for the first S tokens."""
+        x = to_numpy64(inp["x"][:S])
+        noise = to_numpy64(inp["noise"][:S]) if inp.get("noise") is not None else None
+        spent = 0.0
         t0 = time.perf_counter()
-        ref = oracle.forward(x, g["w_gate"], cfg.k, w1, w2, b_gate=g["b_gate"],
-                             w_noise=g["w_noise"], noise=noise, w3=w3, mode=cfg.gate,
-                             act=cfg.act, bf16=cfg.expert_dtype == 1,
-                             capacity_factor=cfg.capacity_factor,
-                             w_importance=cfg.w_importance, w_load=cfg.w_load,
-                             alpha=cfg.alpha_switch)
-        dt += time.perf_counter() - t0
+        if cfg.hierarchical:
+            noise2 = to_numpy64(inp["noise2"][:S]) if inp.get("noise2") is not None else None
+            gh = oracle.gate_hier(x, hk["w_gate"], hk["w_noise"], noise, cfg.k_groups,
+                                  hk["w_gate2"], hk["w_noise2"], noise2, cfg.k2,
+                                  b_gate=hk["b_gate"])
+            idx, w, imp, ld = gh["topk_idx"], gh["topk_w"], gh["importance"], gh["load"]
+            zsum, entsum = gh["zsum"], gh["entsum"]
+        else:
+            gr = oracle.gate(x, hk["w_gate"], k, hk["b_gate"], hk["w_noise"], noise, cfg.gate)
+            idx, w, imp, ld, zsum, entsum = (gr.topk_idx, gr.topk_w, gr.importance, gr.load,
+                                             gr.zsum, gr.entsum)
+        disp = oracle.dispatch(idx, n, cfg.capacity_factor)
+        spent += time.perf_counter() - t0
+        off, perm = disp["offsets"], disp["perm"]
+        y_perm = np.zeros((disp["rows"], d))
+        for e in range(n):
+            lo, hi = int(off[e]), int(off[e + 1])
+            if hi == lo:
+                continue
+            we = weights(e)
+            t0 = time.perf_counter()
+            y_perm[lo:hi] = oracle.expert_ffn(x[perm[lo:hi]], we["w1"], we["w2"], b1=we["b1"],
+                                              w3=we["w3"], b2=we["b2"], act=cfg.act, bf16=bf)
+            spent += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        y = oracle.combine(y_perm, disp["slot_pos"], w, d)
+        if cfg.d_hidden_shared:
+            y = y + oracle.expert_ffn(x, hk["ws1"], hk["ws2"], w3=hk["ws3"], act=cfg.act,
+                                      bf16=bf)
+        oracle.aux(S, k, imp, ld, disp["counts_pre"], cfg.w_importance, cfg.w_load,
+                   cfg.alpha_switch, zsum, entsum, cfg.w_z, cfg.w_entropy)
+        spent += time.perf_counter() - t0
+        return spent, idx, y
+
+    sized = sample_tokens is None
+    S = min(T, 16 if sized else sample_tokens)
+    dt, idx, y = one_pass(S)
+    while sized and S < T and dt < seconds / 4:   # more rows per expert: more threads busy
+        S = min(T, 2 * S)
+        dt, idx, y = one_pass(S)
+    if sized and S < T and dt < seconds / 2:
+        S = int(min(T, S * seconds / 2 / max(dt, 1e-3)))
+        dt, idx, y = one_pass(S)
+    reps = 1
+    while keep and dt < seconds:
+        d1, _, _ = one_pass(S)
+        dt += d1
         reps += 1
     cores = oracle.num_threads()
-    # The same oracle on one core, on a smaller sample (its results do not
-    # depend on the thread count).
-    S1 = min(512, S)
-    oracle.set_num_threads(1)
-    try:
-        reps1, dt1 = 0, 0.0
-        while reps1 == 0 or dt1 < seconds / 2:
-            t0 = time.perf_counter()
-            oracle.forward(x[:S1], g["w_gate"], cfg.k, w1, w2, b_gate=g["b_gate"],
-                           w_noise=g["w_noise"], noise=None if noise is None else noise[:S1],
-                           w3=w3, mode=cfg.gate, act=cfg.act, bf16=cfg.expert_dtype == 1,
-                           capacity_factor=cfg.capacity_factor, w_importance=cfg.w_importance,
-                           w_load=cfg.w_load, alpha=cfg.alpha_switch)
-            dt1 += time.perf_counter() - t0
-            reps1 += 1
-    finally:
-        oracle.set_num_threads(cores)
-    same = np.all(idx_gpu[:S] == ref["gate"].topk_idx, axis=1)
-    scale = np.max(np.abs(ref["y"][same])) if same.any() else 1.0
-    err = float(np.max(np.abs(y_gpu[:S][same] - ref["y"][same])) / scale) if same.any() else None
     base = {"value": S * reps / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {S} of {cfg.T} tokens of the {cfg.name} workload "
-                      f"(gate, dispatch, experts, combine, losses in float64), "
-                      f"{reps} runs in {dt:.2f} s",
-            "single_core": {"value": S1 * reps1 / dt1, "unit": "tokens/s", "cores": 1,
-                            "sample": f"first {S1} tokens, {reps1} runs in {dt1:.2f} s"}}
+            "sample": f"first {S} of {T} tokens of the {cfg.name} workload (gate, dispatch, "
+                      f"the experts they reach, combine, losses in float64; expert weights "
+                      f"copied to the host outside the timed parts), {reps} pass(es), "
+                      f"{dt:.2f} s of oracle compute on {cores} OpenMP threads"}
+    if keep:
+        S1 = min(512, S)
+        oracle.set_num_threads(1)
+        try:
+            reps1, dt1 = 0, 0.0
+            while reps1 == 0 or dt1 < seconds / 2:
+                d1, _, _ = one_pass(S1)
+                dt1 += d1
+                reps1 += 1
+        finally:
+            oracle.set_num_threads(cores)
+        base["single_core"] = {"value": S1 * reps1 / dt1, "unit": "tokens/s", "cores": 1,
+                               "sample": f"first {S1} tokens, {reps1} passes, {dt1:.2f} s"}
+    same = np.all(idx_gpu[:S] == idx, axis=1)
+    scale = np.max(np.abs(y[same])) if same.any() else 1.0
+    err = float(np.max(np.abs(y_gpu[:S][same] - y[same])) / scale) if same.any() else None
     check = {"tokens": S, "routing_match": float(same.mean()), "y_max_abs_norm_err": err,
-             "tolerance": 2e-2 if cfg.expert_dtype == 1 else 1e-4}
+             "tolerance": 2e-2 if bf else 1e-4}
     return base, check
 
 
@@ -344,10 +438,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="lm_layer")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="run the oracle sample repeatedly for about this long")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=None,
+                    help="tokens of the CPU oracle's sample (default: the workload's first "
+                         "tokens, as many as about --cpu-seconds of oracle work takes)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target oracle compute time of the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches only (default: also replay a HIP graph)")
@@ -469,6 +565,10 @@ def main():
             if f:
                 entry.update({"flops": f, "TFLOP_s": tfs, "mfma_frac": tfs / PEAK_TFLOPS[dt],
                               "ai_flop_per_byte": f / b})
+                if name in SPLIT_GATE_KERNELS:
+                    entry["split_bf16_products"] = {
+                        "TFLOP_s": 6 * tfs, "frac_of_bf16_peak": 6 * tfs / PEAK_TFLOPS["bf16"],
+                        "note": "the six bf16 products per fp32 term the kernel issues"}
             entry["roofline"] = rl
         kernels[name] = entry
         if dominant is None or total_ms > dominant[1]:
@@ -504,7 +604,7 @@ def main():
     dk = kernels[dname]
     roofline = dict(dk["roofline"])
     roofline["kernel"] = dname
-    roofline["traffic"] = TRAFFIC_BYTES.get((cfg.name, dname))
+    roofline["traffic"] = measured_traffic(cfg.name, dname)
     roofline["algo_bytes_per_launch"] = dk["algo_bytes"]
     roofline["avg_us"] = dk["avg_us"]
 
@@ -523,14 +623,17 @@ def main():
                    "rows": rows, "nonempty_experts": nonempty, "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "kernels": kernels,
-        "timing": {"mode": mode, "eager_us_per_step": eager_elapsed / args.steps * 1e6,
+        "timing": {"value_basis": "K back-to-back steps, host clock around the synchronised "
+                                  "loop (the next step may find data of the previous one in "
+                                  "the 256 MB Infinity Cache); cold_events flushes it first",
+                   "mode": mode, "eager_us_per_step": eager_elapsed / args.steps * 1e6,
                    "eager_with_events_us_per_step": prof_elapsed / args.steps * 1e6,
                    "graph_us_per_step": (graph_elapsed / args.steps * 1e6) if graph else None,
                    "warm_events": warm, "cold_events": cold},
         "peaks_measured": peaks,
     }
     if not args.no_cpu_baseline:
-        log(f"[bench] CPU oracle on the first {args.cpu_sample_tokens} tokens")
+        log("[bench] CPU oracle on a sample of the first tokens")
         yh = y.cpu().double().numpy()
         ih = diag["topk_idx"].cpu().numpy()
         base, check = cpu_baseline(cfg, inp, yh, ih, args.cpu_sample_tokens, args.cpu_seconds)
@@ -629,8 +732,8 @@ def bench_backward(args, cfg, train=False):
             + (f"  {e['TFLOP_s']:7.1f} TFLOP/s" if "TFLOP_s" in e else ""))
     dname = dominant[0]
     roofline = dict(kernels[dname]["roofline"])
-    roofline.update(kernel=dname, traffic=TRAFFIC_BYTES.get((cfg.name + ":bwd", dname))
-                    if not train else TRAFFIC_BYTES.get((cfg.name + ":train", dname)),
+    roofline.update(kernel=dname, traffic=measured_traffic(
+                        cfg.name + ("_train" if train else "_bwd"), dname),
                     algo_bytes_per_launch=kernels[dname]["algo_bytes"],
                     avg_us=kernels[dname]["avg_us"])
     metric = ("MoE-layer training step (forward + all gradients) tokens/sec at 1 GPU" if train
@@ -664,7 +767,13 @@ def cpu_baseline_backward(cfg, inp, dy, dl, sample_tokens, seconds):
     tokens of the batch, repeated for about `seconds`."""
     import oracle
     from sparsely_gated_mixture_amd.workloads import to_numpy64
-    S = min(sample_tokens, cfg.T)
+    wbytes = sum(v.numel() * 8 for key, v in inp.items()
+                 if v is not None and key in ("w1", "w3", "w2"))
+    if wbytes > (16 << 30):
+        return {"value": None, "unit": "tokens/s", "cores": None, "kind": "oracle",
+                "sample": f"not run: the oracle's backward holds every expert weight in "
+                          f"float64 ({wbytes / 2**30:.0f} GiB) on the host"}
+    S = min(sample_tokens or 8192, cfg.T)
     h = {k: to_numpy64(v) for k, v in inp.items() if v is not None}
     x = h["x"][:S]
     noise = h["noise"][:S] if "noise" in h else None

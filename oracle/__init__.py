@@ -374,24 +374,37 @@ class GateResult:
     entsum: float = 0.0     # sum over tokens of the gate distribution's entropy
 
 
-def gate(x, w_gate, k, b_gate=None, w_noise=None, noise=None, mode=GATE_TOPK_SOFTMAX):
+def gate(x, w_gate, k, b_gate=None, w_noise=None, noise=None, mode=GATE_TOPK_SOFTMAX,
+         route=None):
     """[PAPER] Noisy Top-K gating plus its Importance / Load vectors, the
     z-loss and entropy statistics ([WIKI] part 2).
     GATE_SIGMOID_BIAS ([SURVEY] 6.2, 6.3): selection on h + b, weights from
     Sigmoid(h) normalised over the kept experts; no noise, no Load; the
-    z-loss statistic is taken over h (the bias is not a network output)."""
+    z-loss statistic is taken over h (the bias is not a network output).
+    route: optional [T, k] selection used in place of KeepTopK's (tests
+    compare against another implementation's choice at near-ties); the
+    weights, Importance and Load then follow from these logits with that
+    selection held fixed, H_(k) and H_(k+1) still being the k-th and
+    (k+1)-th largest values."""
+    def select(H):
+        idx, hk, hk1 = keep_topk(H, k)
+        if route is not None:
+            idx = _i(route)
+            assert idx.shape == (H.shape[0], k)
+        return idx, hk, hk1
+
     if mode == GATE_SIGMOID_BIAS:
         if w_noise is not None:
             raise ValueError("the sigmoid gate takes no noise")
         h, _, _ = gate_logits(x, w_gate)
         H = h + (_d(b_gate) if b_gate is not None else 0.0)
-        idx, hk, hk1 = keep_topk(H, k)
+        idx, hk, hk1 = select(H)
         w, probs = sigmoid_gate_weights(h, idx)
         imp = importance(probs)
         return GateResult(H, None, H, idx, w, probs, hk, hk1, imp, None, None,
                           near_ties(hk, hk1), zloss_sum(h), entropy_sum(probs))
     clean, sp, H = gate_logits(x, w_gate, b_gate, w_noise, noise)
-    idx, hk, hk1 = keep_topk(H, k)
+    idx, hk, hk1 = select(H)
     w, probs = gate_weights(H, idx, mode)
     imp = importance(probs)
     ld, P = (None, None)
@@ -443,18 +456,22 @@ def forward(x, w_gate, k, w1, w2, *, b_gate=None, w_noise=None, noise=None, b1=N
 
 
 def gate_hier(x, w_gate, w_noise, noise, k1, w_gate2, w_noise2, noise2, k2, b_gate=None,
-              b_gate2=None):
+              b_gate2=None, route=None):
     """O10 gating.  [NOTES] "分层 MoE": a primary gate picks k1 of a groups; in
     each chosen group a secondary gate (that group's own parameters) picks k2
     of its b experts.  Slot s*k2 + s2 of a token is expert g_s*b + e with
     weight w1_s * w2_{s,s2}.  Aux vectors: Importance over the product
     weights; Load in the factorised form of ``hier_load``.
-    Shapes: w_gate2/w_noise2 [a, b, d], noise2 [T, k1, b]."""
+    Shapes: w_gate2/w_noise2 [a, b, d], noise2 [T, k1, b].
+    route: optional [T, k1*k2] combined selection held fixed in place of
+    both levels' KeepTopK (see ``gate``)."""
     x = _d(x)
     T, d = x.shape
     w_gate2 = _d(w_gate2)
     a, b, _ = w_gate2.shape
-    pg = gate(x, w_gate, k1, b_gate, w_noise, noise)
+    route = None if route is None else _i(route)
+    pg = gate(x, w_gate, k1, b_gate, w_noise, noise,
+              route=None if route is None else route[:, ::k2] // b)
     idx = np.empty((T, k1 * k2), np.int32)
     wts = np.empty((T, k1 * k2))
     near = pg.near_tie.copy()
@@ -471,8 +488,11 @@ def gate_hier(x, w_gate, w_noise, noise, k1, w_gate2, w_noise2, noise2, k2, b_ga
         if len(toks) == 0:
             continue
         z2 = noise2[toks, slots] if noise2 is not None else None
+        r2 = None
+        if route is not None:
+            r2 = np.stack([route[t, s * k2:(s + 1) * k2] % b for t, s in zip(toks, slots)])
         sg = gate(x[toks], w_gate2[g], k2, None if b_gate2 is None else b_gate2[g],
-                  None if w_noise2 is None else w_noise2[g], z2)
+                  None if w_noise2 is None else w_noise2[g], z2, route=r2)
         secondary.append((g, toks, slots, sg))
         zsum += sg.zsum
         for r, (t, s) in enumerate(zip(toks, slots)):

@@ -200,43 +200,119 @@ def check_routing_any(cfg, gpu_idx, orc_idx, H, near_tie):
     return bad
 
 
-def sampled_y_reference(cfg, inp, x64, idx, w, slot_pos, tokens):
-    """y rows of `tokens` from the oracle's expert FFNs, given a routing
-    (idx, w, slot_pos); only the experts these tokens use are copied."""
-    experts = sorted({int(idx[t, s]) for t in tokens for s in range(idx.shape[1])
-                      if slot_pos[t, s] >= 0})
-    bf = cfg.expert_dtype != DTYPE_F32
-
-    def host32(name, e):
+def expert_weights_f64(cfg, inp, e):
+    """float64 host copies of expert e's weights (converted on the device,
+    one expert at a time); FP8 experts as the values their codes stand for."""
+    out = {}
+    for name in ("w1", "w3", "w2", "b1", "b2"):
         t = inp.get(name)
         if t is None:
-            return None
-        m = t[e].detach().float().cpu().numpy()
-        return fp8_dequant(m) if cfg.expert_dtype == DTYPE_FP8 and name != "b1" and name != "b2" \
-            else m
-
-    ys = np.zeros((len(tokens), cfg.d_model))
-    if cfg.d_hidden_shared:
-        ws = {k: (None if inp.get(k) is None else inp[k].detach().float().cpu().numpy())
-              for k in ("ws1", "ws3", "ws2")}
-        ys += oracle.expert_ffn(x64[tokens], ws["ws1"], ws["ws2"], w3=ws["ws3"], act=cfg.act,
-                                bf16=bf)
-    for e in experts:
-        w1, w2, w3 = host32("w1", e), host32("w2", e), host32("w3", e)
-        b1, b2 = host32("b1", e), host32("b2", e)
-        for r, t in enumerate(tokens):
-            for s in range(idx.shape[1]):
-                if int(idx[t, s]) != e or slot_pos[t, s] < 0:
-                    continue
-                out = oracle.expert_ffn(x64[t:t + 1], w1, w2, b1=b1, w3=w3, b2=b2,
-                                        act=cfg.act, bf16=bf)
-                ys[r] += w[t, s] * out[0]
-    return ys
+            out[name] = None
+            continue
+        m = t[e].to(torch.float64).cpu().numpy()
+        if cfg.expert_dtype == DTYPE_FP8 and name in ("w1", "w3", "w2"):
+            m = fp8_dequant(m)
+        out[name] = m
+    return out
 
 
-def full_size_sampled(cfg, n_sample=48, seed=0):
-    """Full-size forward of `cfg`: routing for every token against the
-    oracle gate, dispatch bit-exact, aux losses, and y on sampled tokens."""
+def expert_rows_reference(cfg, inp, x64, perm, offsets, rows_by_expert):
+    """The oracle's expert output rows y_perm[r] for the requested rows of
+    each expert (rows_by_expert: expert -> global rows of the merged batch),
+    computed expert by expert from the device's weights."""
+    bf = cfg.expert_dtype != DTYPE_F32
+    out = {}
+    for e in sorted(rows_by_expert):
+        rows = np.asarray(sorted(rows_by_expert[e]), np.int64)
+        if len(rows) == 0:
+            continue
+        assert np.all((rows >= offsets[e]) & (rows < offsets[e + 1]))
+        w = expert_weights_f64(cfg, inp, e)
+        ys = oracle.expert_ffn(x64[perm[rows]], w["w1"], w["w2"], b1=w["b1"], w3=w["w3"],
+                               b2=w["b2"], act=cfg.act, bf16=bf)
+        for r, v in zip(rows, ys):
+            out[int(r)] = v
+    return out
+
+
+def shared_reference(cfg, inp, x64, tokens):
+    """The shared expert's output on `tokens` (zeros without one)."""
+    if not cfg.d_hidden_shared:
+        return np.zeros((len(tokens), cfg.d_model))
+    ws = {k: (None if inp.get(k) is None else inp[k].to(torch.float64).cpu().numpy())
+          for k in ("ws1", "ws3", "ws2")}
+    return oracle.expert_ffn(x64[tokens], ws["ws1"], ws["ws2"], w3=ws["ws3"], act=cfg.act,
+                             bf16=cfg.expert_dtype != DTYPE_F32)
+
+
+def covering_tokens(gpu, disp, T, n_random=16, seed=0):
+    """Tokens whose outputs, checked together, exercise every non-empty
+    expert: the ends of the batch; the rows of the hottest expert's last
+    128-row tile (its first, second and last rows); every single-row expert;
+    then, experts in ascending order of rows, the token of one row of each
+    expert not yet covered; plus a few random tokens."""
+    counts, offsets, perm = disp["counts"], disp["offsets"], disp["perm"]
+    idx, slot_pos = gpu["topk_idx"], gpu["slot_pos"]
+    r = np.random.default_rng(seed)
+    chosen = [0, 1, T - 2, T - 1] if T >= 4 else list(range(T))
+    hot = int(np.argmax(counts))
+    lo, hi = int(offsets[hot]), int(offsets[hot + 1])
+    tile0 = lo + (hi - lo - 1) // 128 * 128
+    chosen += [int(perm[q]) for q in (tile0, min(tile0 + 1, hi - 1), hi - 2, hi - 1) if q >= lo]
+    chosen += [int(perm[offsets[e]]) for e in np.nonzero(counts == 1)[0]]
+    covered = set()
+
+    def cover(t):
+        covered.update(int(e) for e, p in zip(idx[t], slot_pos[t]) if p >= 0)
+    for t in chosen:
+        cover(t)
+    for e in np.argsort(counts, kind="stable"):
+        if counts[e] == 0 or int(e) in covered:
+            continue
+        q = int(offsets[e]) + int(r.integers(counts[e]))
+        chosen.append(int(perm[q]))
+        cover(int(perm[q]))
+    chosen += [int(t) for t in r.choice(T, size=min(T, n_random), replace=False)]
+    assert covered >= {int(e) for e in np.nonzero(counts)[0]}
+    return np.unique(np.asarray(chosen, np.int64))
+
+
+def oracle_gate_on_routing(cfg, h, idx):
+    """The oracle's Importance, Load and losses with the gate's selection
+    held at `idx` (the GPU's routing): the weights and load terms come from
+    the oracle's own logits, so tokens that route differently at a near-tie
+    count the way the GPU routed them instead of being left out."""
+    T, k, n = idx.shape[0], cfg.k, cfg.n_experts
+    if cfg.hierarchical:
+        gh = oracle.gate_hier(h["x"], h["w_gate"], h.get("w_noise"), h.get("noise"),
+                              cfg.k_groups, h["w_gate2"], h.get("w_noise2"), h.get("noise2"),
+                              cfg.k2, b_gate=h.get("b_gate"), route=idx)
+        imp, ld, zsum, entsum = gh["importance"], gh["load"], gh["zsum"], gh["entsum"]
+    else:
+        g = oracle.gate(h["x"], h["w_gate"], k, h.get("b_gate"), h.get("w_noise"),
+                        h.get("noise"), cfg.gate, route=idx)
+        imp, ld, zsum, entsum = g.importance, g.load, g.zsum, g.entsum
+    counts_pre = oracle.dispatch(idx, n, cfg.capacity_factor)["counts_pre"]
+    losses = oracle.aux(T, k, imp, ld, counts_pre, cfg.w_importance, cfg.w_load,
+                        cfg.alpha_switch, zsum, entsum, cfg.w_z, cfg.w_entropy)
+    return imp, ld, losses, zsum, entsum
+
+
+def check_aux(cfg, h, gpu):
+    imp, ld, losses, _, _ = oracle_gate_on_routing(cfg, h, gpu["topk_idx"])
+    assert_close_rel(gpu["importance"], imp, 1e-5, 1e-5, "importance")
+    if ld is not None:
+        assert_close_rel(gpu["load"], ld, 1e-5, 1e-5, "load")
+    assert_close_rel(gpu["losses"], losses, TOL_AUX, 1e-7, "losses")
+
+
+def full_size_check(cfg, every_token=False, n_random=16, seed=0):
+    """Full-size forward of `cfg` through moe_forward against the oracle:
+    routing of every token (bit-exact up to near ties), gate weights,
+    dispatch bit-exact, Importance / Load / losses (the oracle held at the
+    GPU's routing), and y element-wise -- on every token, or on tokens that
+    cover every non-empty expert (covering_tokens) -- from the oracle's
+    experts evaluated expert by expert."""
     log(f"[full-size] {cfg.name} T={cfg.T} d={cfg.d_model} h={cfg.d_hidden} "
         f"n={cfg.n_experts} k={cfg.k}")
     inp = dev_inputs(cfg)
@@ -247,27 +323,29 @@ def full_size_sampled(cfg, n_sample=48, seed=0):
     ok = np.setdiff1d(np.arange(cfg.T), bad)
     np.testing.assert_allclose(gpu["topk_w"][ok], ow[ok], rtol=TOL_W_REL, atol=TOL_W)
     d = check_dispatch_exact(cfg, gpu, cfg.T)
-    if len(bad) == 0:
-        assert_close_rel(gpu["importance"], oimp, 1e-5, 1e-5, "importance")
-        if oload is not None:
-            assert_close_rel(gpu["load"], oload, 1e-5, 1e-5, "load")
-        losses = oracle.aux(cfg.T, cfg.k, oimp, oload, d["counts_pre"], cfg.w_importance,
-                            cfg.w_load, cfg.alpha_switch, zsum, entsum, cfg.w_z, cfg.w_entropy)
-        assert_close_rel(gpu["losses"], losses, TOL_AUX, 1e-7, "losses")
-    # sampled outputs: ends of the batch, random tokens, and tokens routed to
-    # the most loaded expert
-    r = np.random.default_rng(seed)
-    hot = int(np.argmax(d["counts"]))
-    hot_tokens = np.nonzero(np.any(gpu["topk_idx"] == hot, axis=1))[0][:4]
-    pool = np.setdiff1d(ok, np.concatenate([[0, 1, cfg.T - 2, cfg.T - 1], hot_tokens]))
-    tokens = np.unique(np.concatenate([
-        [0, 1, cfg.T - 2, cfg.T - 1], hot_tokens,
-        r.choice(pool, size=min(len(pool), max(0, n_sample - 8)), replace=False)]))
-    tokens = np.intersect1d(tokens, ok)
-    ys = sampled_y_reference(cfg, inp, h["x"], gpu["topk_idx"], ow, gpu["slot_pos"], tokens)
+    check_aux(cfg, h, gpu)
+    if every_token:
+        tokens = ok
+    else:
+        tokens = np.intersect1d(covering_tokens(gpu, d, cfg.T, n_random, seed), ok)
+    rows_by_expert = {}
+    for t in tokens:
+        for e, p in zip(gpu["topk_idx"][t], gpu["slot_pos"][t]):
+            if p >= 0:
+                rows_by_expert.setdefault(int(e), []).append(int(p))
+    yp = expert_rows_reference(cfg, inp, h["x"], d["perm"], d["offsets"], rows_by_expert)
+    ys = shared_reference(cfg, inp, h["x"], tokens)
+    for i, t in enumerate(tokens):
+        for s in range(cfg.k):
+            p = gpu["slot_pos"][t, s]
+            if p >= 0:
+                ys[i] += ow[t, s] * yp[int(p)]
     err = max_abs_norm(gpu["y"][tokens], ys)
-    log(f"  routing mismatches {len(bad)}, kept rows {d['rows']}, sampled tokens {len(tokens)}, "
+    experts = len(rows_by_expert)
+    log(f"  routing mismatches {len(bad)}, kept rows {d['rows']}, checked tokens {len(tokens)} "
+        f"covering {experts} of {int(np.count_nonzero(d['counts']))} non-empty experts, "
         f"y error {err:.3e}")
+    assert experts == int(np.count_nonzero(d["counts"]))
     assert err <= y_tolerance(cfg)
     return gpu
 
@@ -300,4 +378,6 @@ def full_parity(cfg, T=None, aux=True, tie_budget=MISMATCH_BUDGET):
         if g.load is not None:
             assert_close_rel(gpu["load"], g.load, 1e-5, 1e-5, "load")
         assert_close_rel(gpu["losses"], ref["losses"], TOL_AUX, 1e-7, "losses")
+    elif aux:
+        check_aux(c, h, gpu)
     return gpu, ref

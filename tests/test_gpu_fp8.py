@@ -8,7 +8,7 @@ import torch
 import oracle
 import sparsely_gated_mixture_amd as moe
 from sparsely_gated_mixture_amd.workloads import DTYPE_FP8, PRESETS, MoEConfig
-from _support import (dev_inputs, full_parity, full_size_sampled, gpu_forward, log, max_abs_norm)
+from _support import (dev_inputs, full_parity, full_size_check, gpu_forward, log, max_abs_norm)
 
 pytestmark = pytest.mark.gpu
 
@@ -77,7 +77,7 @@ def test_forward_fp8_odd_with_bias(bias):
 
 
 def test_full_size_fp8_lm_layer():
-    full_size_sampled(PRESETS["lm_layer_fp8"])
+    full_size_check(PRESETS["lm_layer_fp8"], every_token=True)
 
 
 def test_fp8_layer_close_to_bf16_layer():

@@ -87,6 +87,16 @@ def test_forward_widest_gate_rows_and_largest_k(n, k):
     full_parity(cfg, tie_budget=1.0)
 
 
+@pytest.mark.parametrize("n", [512, 1024, 2048])
+def test_forward_wide_gate_mismatch_budget(n):
+    # The wide row layouts (8, 16 and 32 experts per lane) on lm_layer-like
+    # inputs (d = 512, noisy, logit bias, T = 8192), held to the workloads'
+    # bar: at most 0.01 % of tokens may route differently, each at a near tie.
+    cfg = MoEConfig(f"wide{n}_k8", T=8192, d_model=512, d_hidden=64, n_experts=n, k=8,
+                    logit_bias="normal0.5", seed=95)
+    full_parity(cfg)
+
+
 def test_forward_single_expert():
     cfg = MoEConfig("single", T=129, d_model=32, d_hidden=48, n_experts=1, k=1, noisy=False,
                     seed=79)

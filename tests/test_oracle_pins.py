@@ -623,6 +623,44 @@ def test_hierarchical_one_group_reduces_to_flat():
                                rtol=1e-12)
 
 
+def test_gate_route_held_fixed():
+    """gate(route=...) holds a given selection: with the oracle's own
+    selection every output is unchanged; with a near-tie swapped the weights
+    are the softmax over the chosen values, Importance still sums to T, and
+    Load changes only for the swapped experts."""
+    r = rng(21)
+    T, d, n, k = 40, 8, 9, 3
+    x = r.standard_normal((T, d))
+    wg, wn = r.standard_normal((n, d)), r.standard_normal((n, d))
+    z = r.standard_normal((T, n))
+    g = oracle.gate(x, wg, k, None, wn, z)
+    same = oracle.gate(x, wg, k, None, wn, z, route=g.topk_idx)
+    for f in ("topk_idx", "topk_w", "importance", "load", "probs"):
+        np.testing.assert_array_equal(getattr(same, f), getattr(g, f), err_msg=f)
+    t = 5
+    order = np.argsort(-g.H[t], kind="stable")
+    route = g.topk_idx.copy()
+    route[t, k - 1] = order[k]          # the (k+1)-th expert in place of the k-th
+    h = oracle.gate(x, wg, k, None, wn, z, route=route)
+    np.testing.assert_array_equal(h.topk_idx, route)
+    vals = g.H[t, route[t]]
+    np.testing.assert_allclose(h.topk_w[t], np.exp(vals - vals.max()) / np.exp(vals - vals.max()).sum(),
+                               rtol=1e-14)
+    assert h.importance.sum() == pytest.approx(T, rel=1e-14)
+    other = np.setdiff1d(np.arange(n), [order[k - 1], order[k]])
+    np.testing.assert_allclose(h.load[other], g.load[other], rtol=1e-14)
+    assert not np.allclose(h.load[order[k - 1]], g.load[order[k - 1]], rtol=1e-9)
+    # the two-level gate's own routing held fixed changes nothing
+    a, b = 3, 4
+    wg2, wn2 = r.standard_normal((a, b, d)), r.standard_normal((a, b, d))
+    z1, z2 = r.standard_normal((T, a)), r.standard_normal((T, 2, b))
+    gh = oracle.gate_hier(x, wg[:a], wn[:a], z1, 2, wg2, wn2, z2, 1)
+    gh2 = oracle.gate_hier(x, wg[:a], wn[:a], z1, 2, wg2, wn2, z2, 1, route=gh["topk_idx"])
+    for f in ("topk_idx", "topk_w", "importance", "load"):
+        np.testing.assert_array_equal(gh2[f], gh[f], err_msg=f)
+    assert gh2["zsum"] == gh["zsum"] and gh2["entsum"] == gh["entsum"]
+
+
 def _two_level_golden():
     with open(os.path.join(GOLDEN, "two_level_layer.json")) as f:
         g = json.load(f)
