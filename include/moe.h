@@ -186,6 +186,24 @@ moe_status moe_gate(const moe_config* cfg, const float* x, const float* w_gate,
                     int32_t* topk_idx, float* topk_w, float* importance, float* load,
                     float* gate_stats, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_gate without a workspace argument, for callers that cannot allocate
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments (minus ws, ws_bytes), same kernels, same
+ * results as moe_gate.
+ * Scratch: a static device array of 32 MiB inside the library, one copy per
+ * GPU, held from the first call on that GPU until the process ends; the call
+ * itself allocates nothing.  A config whose gate needs more scratch than
+ * that (moe_gate's workspace: the logits [T, 2n] fp32 plus per-block partial
+ * sums) returns MOE_ERR_WORKSPACE before any launch.
+ * Calls that overlap on one GPU (other streams, other threads) share that
+ * GPU's array and race: the caller must order them.  Consecutive calls need
+ * no clearing between them (every scratch byte read is written earlier in
+ * the same call). */
+moe_status moe_gate_static(const moe_config* cfg, const float* x, const float* w_gate,
+                           const float* b_gate, const float* w_noise, const float* noise,
+                           int32_t* topk_idx, float* topk_w, float* importance, float* load,
+                           float* gate_stats, void* stream);
+
 /* Two-level gate: a primary gate picks k1 of a groups, then each chosen
  * group's own secondary gate picks k2 of its b experts.
  *   Definition: chenshi221.pages.dev notes, section "Hierarchical MoE"; the

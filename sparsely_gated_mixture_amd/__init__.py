@@ -16,7 +16,7 @@ from ._lib import (EXPORTS, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTE
                    moe_combine, moe_dispatch, moe_expert_ffn,
                    moe_backward_saved, moe_fp8_weight_bytes, moe_forward,
                    moe_forward_train, moe_pack_fp8_weights,
-                   moe_gate, moe_gate_hier, moe_last_error, moe_profile_collect,
+                   moe_gate, moe_gate_hier, moe_gate_static, moe_last_error, moe_profile_collect,
                    moe_probe_hbm_read, moe_probe_mfma, moe_profile_enable,
                    moe_profile_entry,
                    moe_router_bias_update,

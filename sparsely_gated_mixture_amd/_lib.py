@@ -21,7 +21,7 @@ MOE_ERR_WORKSPACE = 3
 MOE_ERR_HIP = 4
 
 EXPORTS = ["moe_workspace_size", "moe_fp8_weight_bytes", "moe_pack_fp8_weights", "moe_gate",
-           "moe_gate_hier", "moe_dispatch", "moe_expert_ffn", "moe_shared_ffn", "moe_combine",
+           "moe_gate_static", "moe_gate_hier", "moe_dispatch", "moe_expert_ffn", "moe_shared_ffn", "moe_combine",
            "moe_aux_loss", "moe_router_bias_update", "moe_forward",
            "moe_backward_workspace_size", "moe_backward", "moe_forward_train",
            "moe_backward_saved", "moe_status_string",
@@ -92,6 +92,7 @@ def load_library():
     L.moe_pack_fp8_weights.argtypes = [i32, i32, i32, i32, P, P, P]
     L.moe_pack_fp8_weights.restype = ctypes.c_int
     L.moe_gate.argtypes = [cfgp] + [P] * 10 + [P, S, P]
+    L.moe_gate_static.argtypes = [cfgp] + [P] * 10 + [P]
     L.moe_gate_hier.argtypes = [cfgp] + [P] * 13 + [P, S, P]
     L.moe_dispatch.argtypes = [cfgp] + [P] * 8 + [P, S, P]
     L.moe_expert_ffn.argtypes = [cfgp] + [P] * 8 + [P, S, P]
@@ -124,7 +125,7 @@ def load_library():
                                     ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(ctypes.c_longlong)]
     L.moe_profile_entry.restype = ctypes.c_int
-    for name in ("moe_gate", "moe_gate_hier", "moe_dispatch", "moe_expert_ffn", "moe_shared_ffn",
+    for name in ("moe_gate", "moe_gate_static", "moe_gate_hier", "moe_dispatch", "moe_expert_ffn", "moe_shared_ffn",
                  "moe_combine", "moe_aux_loss", "moe_router_bias_update", "moe_forward",
                  "moe_backward", "moe_forward_train", "moe_backward_saved"):
         getattr(L, name).restype = ctypes.c_int
@@ -206,6 +207,15 @@ def moe_gate(cfg, x, w_gate, b_gate, w_noise, noise, topk_idx, topk_w, importanc
                                    _ptr(w_noise), _ptr(noise), _ptr(topk_idx), _ptr(topk_w),
                                    _ptr(importance), _ptr(load), _ptr(gate_stats), wp, wb,
                                    _stream(stream)))
+
+
+def moe_gate_static(cfg, x, w_gate, b_gate, w_noise, noise, topk_idx, topk_w, importance, load,
+                    gate_stats, stream=None):
+    c = make_config(cfg)
+    _check(load_library().moe_gate_static(ctypes.byref(c), _ptr(x), _ptr(w_gate), _ptr(b_gate),
+                                          _ptr(w_noise), _ptr(noise), _ptr(topk_idx),
+                                          _ptr(topk_w), _ptr(importance), _ptr(load),
+                                          _ptr(gate_stats), _stream(stream)))
 
 
 def moe_gate_hier(cfg, x, w_gate, b_gate, w_noise, noise, w_gate2, w_noise2, noise2, topk_idx,

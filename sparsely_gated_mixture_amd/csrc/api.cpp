@@ -133,6 +133,8 @@ long long round_up(long long v, long long m) { return (v + m - 1) / m * m; }
 
 }  // namespace
 
+moe_status moe::report_error(moe_status st, const char* msg) { return fail(st, "%s", msg); }
+
 int moe::device_cus() {
   static int cache[64] = {0};
   int dev = 0;
@@ -1404,6 +1406,15 @@ size_t moe_workspace_size(const moe_config* cfg) {
   if (validate(cfg) != MOE_OK) return 0;
   return make_plan(*cfg).total;
 }
+
+}  // extern "C"
+
+size_t moe::gate_workspace_bytes(const moe_config* cfg) {
+  if (validate(cfg) != MOE_OK) return 0;
+  return make_plan(*cfg).gate_bytes;
+}
+
+extern "C" {
 
 moe_status moe_gate(const moe_config* cfg, const float* x, const float* w_gate,
                     const float* b_gate, const float* w_noise, const float* noise,

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/moe.h"
+
 namespace moe {
 
 // Brackets one kernel launch with HIP events while kernel timing is on
@@ -98,6 +100,10 @@ hipError_t launch_pack_fp8(int n_experts, int N, int K, int src_bf16, const void
 
 // Compute units of the current device (queried once per device).
 int device_cus();
+// Sets the thread's last-error message (moe_last_error) and returns st.
+moe_status report_error(moe_status st, const char* msg);
+// Workspace bytes moe_gate needs for *cfg (0 when cfg is invalid).
+size_t gate_workspace_bytes(const moe_config* cfg);
 hipError_t launch_gemm_bf16(const GemmBf16Args& a, int epi, hipStream_t s);
 
 // ---------------------------------------------------------------------------

@@ -1,0 +1,46 @@
+"""moe_gate_static (the flat gate on the library's own static scratch, for
+callers that cannot allocate) against moe_gate with a workspace: two calls
+in a row on one device, the second on a smaller batch, each bit for bit
+equal to moe_gate on the same inputs."""
+import numpy as np
+import pytest
+import torch
+
+import sparsely_gated_mixture_amd as moe
+from sparsely_gated_mixture_amd.workloads import PRESETS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _outputs(cfg):
+    T, n, k = cfg.T, cfg.n_experts, cfg.k
+    dev = "cuda"
+    return dict(idx=torch.full((T, k), -3, dtype=torch.int32, device=dev),
+                w=torch.full((T, k), -3.0, device=dev), imp=torch.full((n,), -3.0, device=dev),
+                load=torch.full((n,), -3.0, device=dev), stats=torch.full((2,), -3.0, device=dev))
+
+
+def _gate(cfg, inp, out, static):
+    args = (cfg, inp["x"], inp["w_gate"], inp["b_gate"], inp["w_noise"], inp["noise"],
+            out["idx"], out["w"], out["imp"], out["load"], out["stats"])
+    if static:
+        moe.moe_gate_static(*args)
+    else:
+        ws = torch.empty(moe.moe_workspace_size(cfg), dtype=torch.uint8, device="cuda")
+        moe.moe_gate(*args, ws)
+    torch.cuda.synchronize()
+    return {key: v.cpu().numpy() for key, v in out.items()}
+
+
+def test_gate_static_matches_gate_on_consecutive_calls():
+    torch.cuda.set_device(0)
+    base = PRESETS["lm_layer"].replace(d_hidden=8)  # the lm_layer gate; tiny experts unused
+    for T in (8192, 1000):  # the second call is smaller and reuses the scratch
+        cfg = base.replace(T=T)
+        print(f"[no-alloc] moe_gate_static vs moe_gate, lm_layer gate T={T}", flush=True)
+        inp = make_inputs(cfg, device="cuda")
+        ref = _gate(cfg, inp, _outputs(cfg), static=False)
+        got = _gate(cfg, inp, _outputs(cfg), static=True)
+        for key in ref:
+            np.testing.assert_array_equal(got[key], ref[key], err_msg=f"T={T} {key}")
+        assert np.all(ref["idx"] >= 0) and np.all(ref["idx"] < cfg.n_experts)
