@@ -100,9 +100,25 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def launch_experts(name, cfg, counts):
+    """(rows, non-empty experts) one launch of a routed-expert GEMM covers:
+    all of them, or -- where the library splits the experts by size
+    (moe_expert_split_rows) -- those below the split for the 128-row kernel
+    (ggemm_bf16_*, ggemm_fp8_*) and the rest for the 256 x 256 one
+    (ggemm_big_*)."""
+    import sparsely_gated_mixture_amd as moe
+    c = np.asarray(counts)
+    c = c[c > 0]
+    split = moe.moe_expert_split_rows(cfg) if name.startswith("ggemm_") else 0
+    if split > 0:
+        c = c[c >= split] if name.startswith("ggemm_big_") else c[c < split]
+    return int(c.sum()), int(len(c))
+
+
 def kernel_work(name, cfg, rows, nonempty, T):
     """(algorithmic bytes, flops, dtype) of one launch of kernel `name` for
-    this step's realised routing."""
+    this step's realised routing (rows and non-empty experts of the
+    launch)."""
     d, h, n, k = cfg.d_model, cfg.d_hidden, cfg.n_experts, cfg.k
     bf = cfg.expert_dtype != 0
     wsz = 2 if bf else 4
@@ -118,12 +134,12 @@ def kernel_work(name, cfg, rows, nonempty, T):
                     2.0 * r2 * c2 * d, "f32")
         if name == "gate_topk_grouped":
             return (r2 * c2 * 4 + (r2 * cfg.b * 4 if noisy else 0) + T * k * 8, 0.0, "f32")
-    if name == "ggemm_bf16_relu":
+    if name in ("ggemm_bf16_relu", "ggemm_big_relu"):
         return (nonempty * h * d * 2 + rows * d * 2 + rows * h * 2, 2.0 * rows * h * d, "bf16")
-    if name == "ggemm_bf16_swiglu":
+    if name in ("ggemm_bf16_swiglu", "ggemm_big_swiglu"):
         return (nonempty * 2 * h * d * 2 + rows * d * 2 + rows * h * 2, 4.0 * rows * h * d,
                 "bf16")
-    if name == "ggemm_bf16_out":
+    if name in ("ggemm_bf16_out", "ggemm_big_out"):
         return (nonempty * d * h * 2 + rows * h * 2 + rows * d * 4, 2.0 * rows * d * h, "bf16")
     # FP8 experts: one byte per weight plus one fp32 scale per weight row
     if name == "ggemm_fp8_relu":
@@ -136,11 +152,11 @@ def kernel_work(name, cfg, rows, nonempty, T):
         return (nonempty * (d * h + 4 * d) + rows * h * 2 + rows * d * 4, 2.0 * rows * d * h,
                 "bf16")
     hs = cfg.d_hidden_shared
-    if name == "shared_bf16_relu":
+    if name in ("shared_bf16_relu", "shared_big_relu"):
         return (hs * d * 2 + T * d * 2 + T * hs * 2, 2.0 * T * hs * d, "bf16")
-    if name == "shared_bf16_swiglu":
+    if name in ("shared_bf16_swiglu", "shared_big_swiglu"):
         return (2 * hs * d * 2 + T * d * 2 + T * hs * 2, 4.0 * T * hs * d, "bf16")
-    if name == "shared_bf16_out":
+    if name in ("shared_bf16_out", "shared_big_out"):
         return (d * hs * 2 + T * hs * 2 + T * d * 4, 2.0 * T * d * hs, "bf16")
     if name == "gate_gemm_bf16x6":
         # The method's work is one fp32 contraction (2*T*d*ncols flops, graded
@@ -557,7 +573,7 @@ def main():
     dominant = None
     for name, total_ms, launches in stats:
         avg_s = total_ms / launches / 1e3
-        b, f, dt = kernel_work(name, cfg, rows, nonempty, T)
+        b, f, dt = kernel_work(name, cfg, *launch_experts(name, cfg, counts), T)
         entry = {"avg_us": avg_s * 1e6, "launches_per_step": launches / args.steps}
         if b:
             rl, gbs, tfs = roofline_entry(b, f, dt, avg_s)

@@ -155,6 +155,13 @@ moe_status moe_pack_fp8_weights(int32_t n_experts, int32_t N, int32_t K, int32_t
  * forward's need; each stage needs at most this).  0 on an invalid config. */
 size_t moe_workspace_size(const moe_config* cfg);
 
+/* How moe_expert_ffn / moe_forward split the experts between their two
+ * grouped GEMMs: experts keeping at least this many rows run on 256 x 256
+ * tiles, the others on 128-row tiles (0: every expert on 128-row tiles).
+ * Depends on the config only (bf16 weights with d_model and d_hidden both
+ * >= 2048 split); the results do not depend on it.  0 on an invalid config. */
+int32_t moe_expert_split_rows(const moe_config* cfg);
+
 /* Flat gating network: logits, noise, KeepTopK, softmax, and the two
  * auxiliary-loss vectors.
  *   Definition: xyznot.com summary, "Method and key formulas", Noisy Top-K

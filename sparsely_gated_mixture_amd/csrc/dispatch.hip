@@ -139,6 +139,35 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(const DispatchArg
       off += kept;
     }
     if (threadIdx.x == kFinThreads - 1) *a.tile_count = tc.y;
+    if (a.big_rows > 0) {
+      int ns = 0, nb = 0;
+      for (int e = b; e < e1; ++e) {
+        const int kept = a.counts[e];
+        if (kept >= a.big_rows) nb += (kept + kBigBM - 1) / kBigBM;
+        else ns += (kept + a.tile_bm - 1) / a.tile_bm;
+      }
+      const int2 cs = block_exscan<kFinThreads>(ns, si);
+      const int2 cb = block_exscan<kFinThreads>(nb, si);
+      int ts = cs.x, tb = cb.x;
+      off = sc.x;
+      for (int e = b; e < e1; ++e) {
+        const int kept = a.counts[e];
+        const bool big = kept >= a.big_rows;
+        const int bm = big ? kBigBM : a.tile_bm;
+        const TileMap& tm = big ? a.big_map : a.small_map;
+        int& t2 = big ? tb : ts;
+        for (int m = 0; m < kept; m += bm) {
+          tm.expert[t2] = e;
+          tm.row0[t2] = off + m;
+          ++t2;
+        }
+        off += kept;
+      }
+      if (threadIdx.x == kFinThreads - 1) {
+        *a.small_map.count = cs.y;
+        *a.big_map.count = cb.y;
+      }
+    }
   }
   if (a.losses)
     block_aux_losses<kFinThreads>(a.importance, a.load, a.counts_pre, a.gate_stats, a.T, a.k, n,
@@ -285,6 +314,52 @@ __global__ __launch_bounds__(256) void bias_update_kernel(const int32_t* __restr
   else if (c < tk) bias[i] = bias[i] + gamma;
 }
 
+// Single block: the segments split by size into a small-tile and a
+// big-tile map (see launch_tilemap_split).
+__global__ __launch_bounds__(1024) void tilemap_split_kernel(const int32_t* __restrict__ offsets,
+                                                             int n, int bm, int big_rows,
+                                                             TileMap sm, TileMap bg) {
+  __shared__ int32_t tsum[2][1024];
+  const int per = (n + 1023) / 1024;
+  const int b = threadIdx.x * per;
+  int ns = 0, nb = 0;
+  for (int i = 0; i < per && b + i < n; ++i) {
+    const int rows = offsets[b + i + 1] - offsets[b + i];
+    if (rows >= big_rows) nb += (rows + kBigBM - 1) / kBigBM;
+    else ns += (rows + bm - 1) / bm;
+  }
+  tsum[0][threadIdx.x] = ns;
+  tsum[1][threadIdx.x] = nb;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v0 = threadIdx.x >= off ? tsum[0][threadIdx.x - off] : 0;
+    const int v1 = threadIdx.x >= off ? tsum[1][threadIdx.x - off] : 0;
+    __syncthreads();
+    tsum[0][threadIdx.x] += v0;
+    tsum[1][threadIdx.x] += v1;
+    __syncthreads();
+  }
+  int ts = threadIdx.x ? tsum[0][threadIdx.x - 1] : 0;
+  int tb = threadIdx.x ? tsum[1][threadIdx.x - 1] : 0;
+  for (int i = 0; i < per && b + i < n; ++i) {
+    const int e = b + i;
+    const int r0 = offsets[e], rows = offsets[e + 1] - r0;
+    const bool big = rows >= big_rows;
+    const int tbm = big ? kBigBM : bm;
+    const TileMap& tm = big ? bg : sm;
+    int& t = big ? tb : ts;
+    for (int m = 0; m < rows; m += tbm) {
+      tm.expert[t] = e;
+      tm.row0[t] = r0 + m;
+      ++t;
+    }
+  }
+  if (threadIdx.x == 1023) {
+    *sm.count = tsum[0][1023];
+    *bg.count = tsum[1][1023];
+  }
+}
+
 // Single block: M-tiles of every expert segment, in expert order.
 __global__ __launch_bounds__(1024) void tilemap_kernel(const int32_t* __restrict__ offsets, int n,
                                                        int bm, int32_t* __restrict__ tile_expert,
@@ -400,6 +475,13 @@ hipError_t launch_bias_update(const int32_t* counts_pre, int n, int T, int k, fl
   ProfScope ps("bias_update", s);
   bias_update_kernel<<<dim3((n + 255) / 256), dim3(256), 0, s>>>(counts_pre, n,
                                                                  (long long)T * k, gamma, bias);
+  return hipGetLastError();
+}
+
+hipError_t launch_tilemap_split(const int32_t* offsets, int n, int bm, int big_rows,
+                                TileMap small, TileMap big, hipStream_t s) {
+  ProfScope ps("ffn_tilemap", s);
+  tilemap_split_kernel<<<dim3(1), dim3(1024), 0, s>>>(offsets, n, bm, big_rows, small, big);
   return hipGetLastError();
 }
 

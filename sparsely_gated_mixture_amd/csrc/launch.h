@@ -9,6 +9,14 @@
 
 namespace moe {
 
+// A grouped GEMM's tile map: tile t covers rows [row0[t], min(row0[t] + bm,
+// offsets[expert[t] + 1])) of expert[t]; *count tiles.
+struct TileMap {
+  int32_t* expert;
+  int32_t* row0;
+  int32_t* count;
+};
+
 // Brackets one kernel launch with HIP events while kernel timing is on
 // (moe_profile_enable); a no-op otherwise.
 struct ProfScope {
@@ -91,6 +99,10 @@ struct GemmBf16Args {
 };
 constexpr int kBf16BM = 128;
 constexpr int kMaxTilesPerWG = 512;  // tiles one persistent workgroup can hold
+// The 256 x 256-tile grouped GEMM (ggemm_big.hip): same arguments, a tile map
+// of kBigBM-row M-tiles, bf16 weights only (no FP8).
+constexpr int kBigBM = 256;
+hipError_t launch_gemm_big(const GemmBf16Args& a, int epi, hipStream_t s);
 
 // Pack n_experts [N, K] weight matrices (fp32, or bf16 when src_bf16) into
 // the FP8 E4M3 layout the grouped GEMM reads (codes by row pair and 64-wide
@@ -160,6 +172,10 @@ hipError_t launch_gemm_bwd_f32(const GemmBwdArgs& a, int mode, int epi, const ch
 // [offsets[e], offsets[e+1]), ceil(rows/bm) M-tiles in expert order.
 hipError_t launch_tilemap(const int32_t* offsets, int n, int bm, int32_t* tile_expert,
                           int32_t* tile_row0, int32_t* tile_count, hipStream_t s);
+// The same segments split by size: experts with fewer than big_rows rows in
+// bm-row tiles (small), the others in kBigBM-row tiles (big).
+hipError_t launch_tilemap_split(const int32_t* offsets, int n, int bm, int big_rows,
+                                TileMap small, TileMap big, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Gate epilogue: noise, KeepTopK, softmax / Switch, importance/load partials.
@@ -286,6 +302,11 @@ struct DispatchArgs {
   int32_t* tile_expert;
   int32_t* tile_row0;
   int32_t* tile_count;
+  // Optional (big_rows > 0, with tile_bm): the same segments split in two
+  // maps by size -- experts keeping fewer than big_rows rows in tile_bm-row
+  // tiles (small map), the others in kBigBM-row tiles (big map).
+  int big_rows;
+  TileMap small_map, big_map;
   // Optional: auxiliary losses from importance / load (load may be null) and
   // the pre-capacity counts (losses == null: none).
   float* losses;

@@ -1,0 +1,82 @@
+"""Expert GEMMs split by size (bf16 experts with d_model and d_hidden both
+>= 2048): experts that keep at least moe_expert_split_rows(cfg) rows run on
+256 x 256 tiles, the rest on 128-row tiles.  Element-wise parity against the
+oracle on shapes that reach both kernels, with an odd count of K-steps and
+a K tail (chunks past K), N tails (a last N-tile of 8 or 40 columns), expert
+biases through the big kernel's ReLU and identity epilogues, segments of one
+to several 256-row tiles, the shared expert on 256-row tiles, and the
+standalone moe_expert_ffn (which builds the two tile maps itself)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparsely_gated_mixture_amd as moe
+from sparsely_gated_mixture_amd.workloads import (ACT_SWIGLU, GATE_SIGMOID_BIAS, MoEConfig,
+                                                  make_inputs)
+from _support import (dev_inputs, expert_weights_host, full_parity, host, log, max_abs_norm)
+
+pytestmark = pytest.mark.gpu
+
+
+def _classes(cfg, counts):
+    split = moe.moe_expert_split_rows(cfg)
+    assert split > 0, "the case must reach the size split"
+    small = int(np.sum((counts > 0) & (counts < split)))
+    big = int(np.sum(counts >= split))
+    log(f"  split at {split} rows: {small} experts on 128-row tiles, {big} on 256 x 256 "
+        f"(largest {int(counts.max())} rows)")
+    return split, small, big
+
+
+def test_split_swiglu_sigmoid_shared():
+    # d = 2112: 33 K-steps of 64 (an odd count: the big kernel runs one step
+    # on zeros); h = 2056: the last 128-column N-tile of the SwiGLU GEMM holds
+    # 8 columns.  Shared expert of width 2048 on 256-row tiles.
+    cfg = MoEConfig("split_swiglu", T=400, d_model=2112, d_hidden=2056, n_experts=6, k=2,
+                    act=ACT_SWIGLU, gate=GATE_SIGMOID_BIAS, noisy=False, logit_bias="zipf1.1",
+                    d_hidden_shared=2048, seed=501)
+    gpu, ref = full_parity(cfg)
+    split, small, big = _classes(cfg, gpu["counts"])
+    assert small >= 1 and big >= 1
+    assert np.any(gpu["counts"] > 256)  # a segment of two 256-row tiles
+
+
+def test_split_relu_biases_k_tail():
+    # d = 2088: the last K-step holds 40 of 64 columns (chunks past K read as
+    # zeros); the output GEMM's N = 2088 ends in a 40-column tile; expert
+    # biases N(0, 0.1^2) through both kernels' epilogues.
+    cfg = MoEConfig("split_relu", T=360, d_model=2088, d_hidden=2048, n_experts=5, k=2,
+                    logit_bias="zipf1.1", expert_bias_std=0.1, seed=502)
+    gpu, ref = full_parity(cfg)
+    split, small, big = _classes(cfg, gpu["counts"])
+    assert small >= 1 and big >= 1
+
+
+def test_split_stage_expert_ffn():
+    # moe_expert_ffn on its own: the tile maps are built inside the call.
+    cfg = MoEConfig("split_stage", T=300, d_model=2048, d_hidden=2048, n_experts=4, k=2,
+                    logit_bias="zipf1.1", seed=503)
+    T, n, k, d = cfg.T, cfg.n_experts, cfg.k, cfg.d_model
+    log(f"[stage expert_ffn, split] T={T} d={d} h={cfg.d_hidden} n={n}")
+    inp = dev_inputs(cfg)
+    h = host(inp, ["x", "w_gate", "b_gate", "w_noise", "noise"])
+    g = oracle.gate(h["x"], h["w_gate"], k, h["b_gate"], h["w_noise"], h["noise"])
+    disp = oracle.dispatch(g.topk_idx, n, 0.0)
+    rows = disp["rows"]
+    xp = torch.from_numpy(oracle.bf16_round(h["x"][disp["perm"]])).to(torch.bfloat16).to("cuda")
+    xp = torch.cat([xp, torch.zeros((T * k - rows, d), dtype=torch.bfloat16, device="cuda")])
+    off = torch.from_numpy(disp["offsets"]).to("cuda")
+    yp = torch.full((T * k, d), 7.0, dtype=torch.float32, device="cuda")
+    ws = torch.empty(moe.moe_workspace_size(cfg), dtype=torch.uint8, device="cuda")
+    moe.moe_expert_ffn(cfg, xp, off, inp["w1"], None, None, inp["w2"], None, yp, ws)
+    torch.cuda.synchronize()
+    _classes(cfg, disp["counts"])
+    ew = expert_weights_host(inp, range(n))
+    y_ref = oracle.experts_apply(h["x"], disp["perm"], disp["offsets"],
+                                 np.stack([ew["w1"][e] for e in range(n)]),
+                                 np.stack([ew["w2"][e] for e in range(n)]), bf16=True)
+    err = max_abs_norm(yp[:rows].cpu().double().numpy(), y_ref)
+    log(f"  y_perm error {err:.3e}")
+    assert err <= 2e-2
+    assert torch.all(yp[rows:] == 7.0)  # rows past offsets[n] untouched
