@@ -82,9 +82,14 @@ def set_num_threads(n: int) -> None:
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-            build(force=True)
-        L = ctypes.CDLL(_LIB_PATH)
+        # ORACLE_LIBRARY_PATH: another build of oracle.c (the sanitizer test
+        # loads an AddressSanitizer / UBSan build this way)
+        path = os.environ.get("ORACLE_LIBRARY_PATH")
+        if not path:
+            path = _LIB_PATH
+            if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+                build(force=True)
+        L = ctypes.CDLL(path)
         c_int, c_dbl, c_i64 = ctypes.c_int, ctypes.c_double, ctypes.c_int64
         odp, oip = _opt(_dp), _opt(_ip)
         L.oracle_num_threads.argtypes = []

@@ -77,10 +77,13 @@ def load_library():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with "
+    # MOE_LIBRARY_PATH: another build of the same sources (the sanitizer test
+    # loads one whose host code carries AddressSanitizer / UBSan this way)
+    path = os.environ.get("MOE_LIBRARY_PATH") or LIB_PATH
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
                           "`python sparsely_gated_mixture_amd/build.py`")
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     P = ctypes.c_void_p
     S = ctypes.c_size_t
     cfgp = ctypes.POINTER(MoeConfig)
