@@ -162,6 +162,13 @@ size_t moe_workspace_size(const moe_config* cfg);
  * >= 2048 split); the results do not depend on it.  0 on an invalid config. */
 int32_t moe_expert_split_rows(const moe_config* cfg);
 
+/* Into how many K ranges moe_gate, moe_gate_hier (its primary gate) and
+ * moe_forward split the gate's logit GEMM: 1 (none) unless its tiles number
+ * fewer than three per CU and d_model >= 2048.  Each range's fp32 partial
+ * logits take [T, 2 * n_gate] of the workspace; the gate adds them in range
+ * order.  Depends on the config only; 0 on an invalid config. */
+int32_t moe_gate_k_splits(const moe_config* cfg);
+
 /* Flat gating network: logits, noise, KeepTopK, softmax, and the two
  * auxiliary-loss vectors.
  *   Definition: xyznot.com summary, "Method and key formulas", Noisy Top-K

@@ -163,6 +163,7 @@ struct Region {
 struct Plan {
   // gate (flat or primary)
   int n_gate = 0, ldl = 0, gemm_bm = 128, rows_per_block = 16, nparts = 0;
+  int gate_splits = 1;  // K-split of the flat / primary gate GEMM
   Region logits, part_imp, part_load, part_stats, prim_stats;
   // two-level extras
   int a = 0, b = 0, k1 = 0, k2 = 0, ldl2 = 0, max_tiles2 = 0;
@@ -212,6 +213,22 @@ int split_rows(const moe_config& c) {
   return (c.d_model >= 2048 && c.d_hidden >= 2048) ? kSplitRows : 0;
 }
 
+// K-split of the flat (or primary) gate GEMM.  While its tiles number fewer
+// than three per CU (the 64 x 64 kernel's occupancy on 256 CUs), K is split
+// into up to ceil(768 / tiles) ranges of at least 1024, every range
+// non-empty, with the partial logits (one [T, ldl] copy per range) within
+// 24 MiB.
+int gate_splits(long long T, long long d, int n_gate, int bm, int ldl) {
+  const long long tiles = ((T + bm - 1) / bm) * ((n_gate + bm - 1) / bm);
+  if (tiles <= 0 || tiles >= 768) return 1;
+  long long s = (768 + tiles - 1) / tiles;
+  s = std::min(s, d / 1024);
+  s = std::min(s, std::max(1LL, (24LL << 20) / (T * ldl * 4)));
+  s = std::max(1LL, std::min(s, 8LL));
+  while (s > 1 && (long long)gate_split_len((int)d, (int)s) * (s - 1) >= d) --s;
+  return (int)s;
+}
+
 Plan make_plan(const moe_config& c) {
   Plan p;
   const long long T = c.T, d = c.d_model, h = c.d_hidden, n = c.n_experts, k = c.k;
@@ -224,6 +241,7 @@ Plan make_plan(const moe_config& c) {
     // 128x128 tiles (8 waves) once they give every CU a tile; 64x64 below.
     const long long t128 = ((T + 127) / 128) * ((ncols + 127) / 128);
     p.gemm_bm = t128 >= 256 ? 128 : 64;
+    p.gate_splits = gate_splits(T, d, p.n_gate, p.gemm_bm, p.ldl);
   }
   {
     // one partial vector per block; at most 256 blocks (one per CU) once T
@@ -242,7 +260,7 @@ Plan make_plan(const moe_config& c) {
     p.k2 = c.k / c.k_groups;
     p.ldl2 = (int)round_up(2 * p.b, 4);
     p.max_tiles2 = (int)((T * p.k1 + kSecondaryBM - 1) / kSecondaryBM + p.a);
-    const long long logit_elems = std::max(T * p.ldl, T * p.k1 * p.ldl2);
+    const long long logit_elems = std::max(p.gate_splits * T * p.ldl, T * p.k1 * p.ldl2);
     p.logits = g.take(logit_elems * 4);
     p.part_imp = g.take((size_t)p.nparts * p.a * 4);
     p.part_load = g.take((size_t)p.nparts * p.a * 4);
@@ -267,7 +285,7 @@ Plan make_plan(const moe_config& c) {
     p.part2_load = g.take((size_t)p.max_tiles2 * p.b * 4);
     p.part2_stats = g.take((size_t)p.max_tiles2 * 2 * 4);
   } else {
-    p.logits = g.take(T * p.ldl * 4);
+    p.logits = g.take(p.gate_splits * T * p.ldl * 4);
     p.part_imp = g.take((size_t)p.nparts * n * 4);
     p.part_load = g.take((size_t)p.nparts * n * 4);
     p.part_stats = g.take((size_t)p.nparts * 2 * 4);
@@ -380,6 +398,8 @@ moe_status run_gate(const moe_config& c, const Plan& p, const float* x, const fl
     g.M = c.T;
     g.mtiles = (c.T + p.gemm_bm - 1) / p.gemm_bm;
     g.max_mtiles = g.mtiles;
+    g.ksplit = p.gate_splits;
+    g.split_stride = (long long)c.T * p.ldl;
     HIP_TRY(launch_gemm_gate(g, p.gemm_bm, s));
   }
   TopkArgs t{};
@@ -399,6 +419,8 @@ moe_status run_gate(const moe_config& c, const Plan& p, const float* x, const fl
   t.part_load = noisy ? at<float>(ws, p.part_load) : nullptr;
   t.part_stats = gate_stats ? at<float>(ws, p.part_stats) : nullptr;
   t.rows_per_block = p.rows_per_block;
+  t.nsplit = p.gate_splits;
+  t.split_stride = (long long)c.T * p.ldl;
   HIP_TRY(launch_topk(t, s));
   const ColsumVec sums[3] = {ColsumVec{t.part_imp, n, importance}, ColsumVec{t.part_load, n, load},
                              ColsumVec{t.part_stats, 2, gate_stats}};
@@ -439,6 +461,8 @@ moe_status run_gate_hier(const moe_config& c, const Plan& p, const float* x, con
     g.M = c.T;
     g.mtiles = (c.T + p.gemm_bm - 1) / p.gemm_bm;
     g.max_mtiles = g.mtiles;
+    g.ksplit = p.gate_splits;
+    g.split_stride = (long long)c.T * p.ldl;
     HIP_TRY(launch_gemm_gate(g, p.gemm_bm, s));
   }
   TopkArgs t{};
@@ -456,6 +480,8 @@ moe_status run_gate_hier(const moe_config& c, const Plan& p, const float* x, con
   t.part_load = noisy ? at<float>(ws, p.part_load) : nullptr;
   t.part_stats = gate_stats ? at<float>(ws, p.part_stats) : nullptr;
   t.rows_per_block = p.rows_per_block;
+  t.nsplit = p.gate_splits;
+  t.split_stride = (long long)c.T * p.ldl;
   HIP_TRY(launch_topk(t, s));
   HIP_TRY(launch_colsum(p.nparts, ColsumVec{t.part_imp, a, at<float>(ws, p.prim_imp)},
                         ColsumVec{t.part_load, a, at<float>(ws, p.prim_load)},
@@ -853,7 +879,7 @@ BwdPlan make_bwd_plan(const moe_config& c) {
   const bool swiglu = c.act == MOE_ACT_SWIGLU;
   Cursor w{b.f.total};
   const long long esz = c.expert_dtype == MOE_F32 ? 4 : 2;  // activations and their gradients
-  b.f.logits = w.take(T1 * b.f.ldl * 4);
+  b.f.logits = w.take(b.f.gate_splits * T1 * b.f.ldl * 4);
   b.f.hidden = w.take(A1 * h * esz);
   b.losses = w.take(8 * 4);
   b.dG = w.take(A1 * 4);
@@ -1519,6 +1545,11 @@ size_t moe_workspace_size(const moe_config* cfg) {
 int32_t moe_expert_split_rows(const moe_config* cfg) {
   if (validate(cfg) != MOE_OK) return 0;
   return split_rows(*cfg);
+}
+
+int32_t moe_gate_k_splits(const moe_config* cfg) {
+  if (validate(cfg) != MOE_OK) return 0;
+  return make_plan(*cfg).gate_splits;
 }
 
 }  // extern "C"

@@ -3,7 +3,9 @@
 // the current one, so every row of a block is in flight at once for the usual
 // row counts.
 //
-// Reads the fp32 logits written by the gate GEMM and computes, per row,
+// Reads the fp32 logits written by the gate GEMM (the sum of its K-split
+// partials, added in split order and written back for the backward) and
+// computes, per row,
 //   H_j = clean_j (+ bias_j) + z_j * Softplus(raw_j)      (noisy gate)
 // then KeepTopK by k+1 rounds of a wave-wide arg-max (DPP max of the ordered
 // float keys, then a ballot for the lowest index holding the maximum: larger
@@ -132,7 +134,7 @@ __global__ __launch_bounds__(NW * 64) void topk_kernel(const TopkArgs p) {
     long long nrow, ob;
     float wp;
     locate(r, nrow, ob, wp);
-    const float* lg = p.logits + (long long)r * p.ldl;
+    float* lg = p.logits + (long long)r * p.ldl;
 #pragma unroll
     for (int q = 0; q < NPL; ++q) {
       const int j = lane + 64 * q;
@@ -140,6 +142,27 @@ __global__ __launch_bounds__(NW * 64) void topk_kernel(const TopkArgs p) {
       in.c[q] = ok ? lg[j] : 0.f;
       in.r[q] = (ok && p.noisy) ? lg[n + j] : 0.f;
       in.z[q] = (ok && p.noisy) ? p.noise[nrow + j] : 0.f;
+    }
+    if (p.nsplit > 1) {  // the gate GEMM's K-split partials, added in split order
+      for (int sp = 1; sp < p.nsplit; ++sp) {
+        const float* part = lg + sp * p.split_stride;
+#pragma unroll
+        for (int q = 0; q < NPL; ++q) {
+          const int j = lane + 64 * q;
+          if (j < n) {
+            in.c[q] += part[j];
+            if (p.noisy) in.r[q] += part[n + j];
+          }
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < NPL; ++q) {
+        const int j = lane + 64 * q;
+        if (j < n) {
+          lg[j] = in.c[q];
+          if (p.noisy) lg[n + j] = in.r[q];
+        }
+      }
     }
   };
 

@@ -28,6 +28,15 @@
 // so each lane ends with four consecutive logit columns of one token.
 // Tiles 128 x 128 on 8 waves (4 across the columns) or 64 x 64 on 4 waves,
 // K steps of 32, two LDS stages, fp32 loads two steps ahead in registers.
+//
+// K-split (flat mode): with few tiles and a long K (T = 4096 tokens, 256
+// experts and d = 7168 make 256 tiles of 64 x 64, one per CU, each 7168 deep)
+// a CU would hold one workgroup's two steps of loads in flight and wait on
+// them; split into ranges of K, the items fill every CU three times over.
+// Each range starts on a 256-element chunk boundary and writes its own fp32
+// partial; the gate epilogue adds the partials in split order (a fixed
+// order, so the logits do not depend on scheduling), one more level of the
+// chunked accumulation above.
 #include "common.h"
 #include "launch.h"
 
@@ -75,11 +84,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_gate_kernel(const GemmF32
   // [mt*BN, M).  Grouped mode (a device tile map of BN-row tiles): rows
   // [tile_row0, min(+BN, offsets[g+1])) of group g, whose weights are
   // B1 + g*strideB1 | B2 + g*strideB2, token rows read through rowmap.
+  // K-split (flat mode): work item L is (split, M-tile, column tile) with the
+  // column tile fastest, so an XCD's neighbouring items share token rows.
   const bool grouped = p.tile_expert != nullptr;
   const int nW = (p.N + BM - 1) / BM;
-  const int L = xcd_tile((grouped ? *p.tile_count : p.mtiles) * nW);
+  const int nsplit = grouped ? 1 : max(1, p.ksplit);
+  const int tiles = (grouped ? *p.tile_count : p.mtiles) * nW;
+  const int L = xcd_tile(tiles * nsplit);
   if (L < 0) return;
-  const int mt = L / nW, wt = L % nW;
+  const int ks = L / tiles, mt = (L % tiles) / nW, wt = L % nW;
   const int col0 = wt * BM;
   int tok0 = mt * BN, tok_end = p.M;
   const float* B1 = p.B1;
@@ -93,7 +106,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_gate_kernel(const GemmF32
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
-  const int K = p.K;
+  // This item's K range [kb, K); the ranges start at multiples of 256, so
+  // the accumulation chunks below stay aligned to K = 0.
+  const int klen = nsplit > 1 ? gate_split_len(p.K, nsplit) : p.K;
+  const int kb = ks * klen;
+  const int K = min(p.K, kb + klen);
+  float* const C = p.C + (long long)ks * p.split_stride;
 
   // Global sources of this thread's chunks (row r, k offset kc).
   const float* wsrc[CH];
@@ -108,12 +126,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_gate_kernel(const GemmF32
     const int gc = col0 + rr[i];
     wok[i] = gc < p.N;
     const float* wrow =
-        gc < p.n1 ? B1 + (long long)gc * K : B2 + (long long)(gc - p.n1) * K;
-    wsrc[i] = (wok[i] ? wrow : B1) + kc[i];
+        gc < p.n1 ? B1 + (long long)gc * p.K : B2 + (long long)(gc - p.n1) * p.K;
+    wsrc[i] = (wok[i] ? wrow : B1) + kb + kc[i];
     const int gt = tok0 + rr[i];
     xok[i] = gt < tok_end;
     const long long arow = !xok[i] ? 0 : p.rowmap ? (long long)p.rowmap[gt] : (long long)gt;
-    xsrc[i] = p.A + arow * p.lda + kc[i];
+    xsrc[i] = p.A + arow * p.lda + kb + kc[i];
   }
   // Two register buffers: step s's fp32 chunks live in buffer s % 2, are
   // loaded two steps ahead and split into LDS one step ahead.
@@ -121,7 +139,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_gate_kernel(const GemmF32
   auto load = [&](int k0, int rb) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const bool kin = k0 + kc[i] < K;
+      const bool kin = kb + k0 + kc[i] < K;
       rw[rb][i] = (wok[i] && kin) ? *(const f32x4*)(wsrc[i] + k0) : f32x4{0.f, 0.f, 0.f, 0.f};
       rx[rb][i] = (xok[i] && kin) ? *(const f32x4*)(xsrc[i] + k0) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -152,7 +170,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_gate_kernel(const GemmF32
       for (int v = 0; v < 16; ++v) acc[i][j][v] = chunk[i][j][v] = small[i][j][v] = 0.f;
   constexpr int kChunkSteps = 256 / kBK;
 
-  const int nk = (K + kBK - 1) / kBK;
+  const int nk = (K - kb + kBK - 1) / kBK;
   const int lr = lane & 31, lh = lane >> 5;
   // Step kt (register buffer and LDS stage rb = kt % 2): load step kt+2,
   // compute step kt, split step kt+1 into the other stage.
@@ -220,7 +238,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_gate_kernel(const GemmF32
   for (int j = 0; j < FN; ++j) {
     const int tok = tok0 + wn * WN + j * 32 + lr;
     if (tok >= tok_end) continue;
-    float* crow = p.C + (long long)tok * p.ldc;
+    float* crow = C + (long long)tok * p.ldc;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -242,8 +260,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_gate_kernel(const GemmF32
 
 hipError_t launch_gemm_gate(const GemmF32Args& a, int bm, hipStream_t s) {
   if (a.bias || a.relu) return hipErrorInvalidValue;  // not an epilogue of this kernel
+  if (a.ksplit > 1 && (a.tile_expert || gate_split_len(a.K, a.ksplit) * (a.ksplit - 1) >= a.K))
+    return hipErrorInvalidValue;  // flat mode only, and every split non-empty
   const int nW = (a.N + bm - 1) / bm;
-  const long long total = (long long)(a.tile_expert ? a.max_mtiles : a.mtiles) * nW;
+  const long long total = (long long)(a.tile_expert ? a.max_mtiles : a.mtiles) * nW *
+                          (a.ksplit > 1 ? a.ksplit : 1);
   if (total <= 0) return hipSuccess;
   const long long grid = (total + kXcds - 1) / kXcds * kXcds;
   ProfScope ps(a.prof_name ? a.prof_name : "gate_gemm_bf16x6", s);

@@ -57,7 +57,18 @@ struct GemmF32Args {
   const int32_t* tile_count;  // device total of M-tiles (grouped mode)
   int max_mtiles;             // upper bound of M-tiles (grid sizing)
   const char* prof_name;      // profiler name of this launch (null: by tile size)
+  // K-split (gate GEMM, flat mode only): ksplit > 1 splits K into ksplit
+  // ranges of gate_split_len(K, ksplit) (a multiple of 256); split s writes
+  // its partial product to C + s * split_stride.  0 or 1: one product to C.
+  int ksplit;
+  long long split_stride;
 };
+// Length of each K range of a ksplit-way gate GEMM: ceil(K / ksplit) rounded
+// up to the kernel's 256-wide accumulation chunks.
+__host__ __device__ inline int gate_split_len(int K, int ksplit) {
+  const int per = (K + ksplit - 1) / ksplit;
+  return (per + 255) / 256 * 256;
+}
 // bm: 64 or 128 (BN = bm).
 hipError_t launch_gemm_f32(const GemmF32Args& a, int bm, hipStream_t s);
 // The same product without bias or ReLU on the bf16 matrix cores, each fp32
@@ -190,7 +201,7 @@ hipError_t launch_tilemap_split(const int32_t* offsets, int n, int bm, int big_r
 struct TopkArgs {
   int rows, n, k, switch_mode, noisy;
   int sigmoid_mode;         // selection on logit + bias, weights Sigmoid(logit) renormalised
-  const float* logits;
+  float* logits;
   long long ldl;
   const float* bias;
   const float* noise;       // flat: [rows, n]; grouped: [T, k1, n] indexed by (token, slot)
@@ -212,6 +223,12 @@ struct TopkArgs {
   const int32_t* tile_count;
   int max_tiles;
   int tile_rows;
+  // Flat mode: the gate GEMM's K-split partials.  nsplit > 1: row r's logits
+  // are the sum, in split order, of logits[r] + s * split_stride over s <
+  // nsplit; the kernel writes the sums back to logits[r] (split 0), where the
+  // backward reads them.  0 or 1: logits[r] as is.
+  int nsplit;
+  long long split_stride;
 };
 // Wavefronts (rows in flight) per gate-epilogue block: 16 while a row fits in
 // at most 8 registers per lane (n <= 512), else 8 (larger rows need the

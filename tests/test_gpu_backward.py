@@ -22,7 +22,7 @@ import torch
 
 import oracle
 from _support import TOL_BF16, TOL_F32, log, max_abs_norm
-from sparsely_gated_mixture_amd import MoELayer
+from sparsely_gated_mixture_amd import MoELayer, moe_gate_k_splits
 from sparsely_gated_mixture_amd.workloads import (ACT_SWIGLU, DTYPE_F32, GATE_SIGMOID_BIAS,
                                                   GATE_SWITCH_TOP1, PRESETS, MoEConfig,
                                                   make_grad_inputs, make_inputs, to_numpy64)
@@ -74,6 +74,13 @@ CASES = {
                            k=4, logit_bias="normal0.5", seed=2110),
     "widest_gate": MoEConfig("bwd_widest_gate", T=256, d_model=64, d_hidden=64,
                              n_experts=2048, k=8, logit_bias="normal0.5", seed=2110),
+    # d_model >= 2048 with few gate tiles: the gate GEMM splits K in two
+    # ([0, 1280) and [1280, 2112)), and the backward reads the logits the gate
+    # epilogue summed from the partials
+    "ksplit_noisy": MoEConfig("bwd_ksplit_noisy", T=256, d_model=2112, d_hidden=64,
+                              n_experts=16, k=2, seed=2111),
+    "ksplit_two_level": MoEConfig("bwd_ksplit_two_level", T=192, d_model=2048, d_hidden=64,
+                                  n_experts=32, k=4, n_groups=4, k_groups=2, seed=2112),
 }
 
 GRAD_OF = dict(dw_gate="w_gate", db_gate="b_gate", dw_noise="w_noise", dw1="w1", db1="b1",
@@ -155,6 +162,7 @@ def test_backward_parity(case):
     cfg = CASES[case]
     log(f"[backward] {case}: T={cfg.T} d={cfg.d_model} h={cfg.d_hidden} n={cfg.n_experts} "
         f"k={cfg.k}")
+    assert moe_gate_k_splits(cfg) == (2 if case.startswith("ksplit") else 1)
     inp, dy, dl, layer, got = _run(cfg)
     # the recomputed routing is the forward's: compare with the oracle's
     n, k, T = cfg.n_experts, cfg.k, cfg.T

@@ -75,6 +75,20 @@ def test_two_level_wide_groups_element_wise(a, b):
     c = MoEConfig(f"hier_b{b}", T=192, d_model=64, d_hidden=64, n_experts=a * b, k=4,
                   n_groups=a, k_groups=2, seed=300)
     log(f"[parity] two-level a={a} b={b} T={c.T}")
+    _two_level_check(c)
+
+
+def test_two_level_gate_k_split_element_wise():
+    # d_model = 2048 with 4 primary tiles: the primary gate's logit GEMM
+    # splits K in two; every output element against the oracle.
+    c = MoEConfig("hier_ksplit", T=256, d_model=2048, d_hidden=64, n_experts=32, k=4,
+                  n_groups=4, k_groups=2, seed=812)
+    assert moe.moe_gate_k_splits(c) == 2
+    log(f"[parity] two-level, gate K-split: T={c.T} d={c.d_model}")
+    _two_level_check(c)
+
+
+def _two_level_check(c):
     inp = dev_inputs(c, c.T)
     gpu = gpu_forward(c, inp)
     h = host(inp)

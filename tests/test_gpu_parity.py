@@ -274,6 +274,34 @@ def test_stage_gate(name):
         assert_close_rel(st.cpu().numpy(), [g.zsum, g.entsum], TOL_AUX, 1e-7, "gate stats")
 
 
+def test_stage_gate_k_split():
+    # d = 3000 with 22 gate tiles of 64 x 64: the logit GEMM splits K in two,
+    # [0, 1536) and [1536, 3000) (1464 deep, ending mid K-step), noisy gate
+    # over 96 experts (two column tiles, the raw half included).
+    cfg = MoEConfig("gate_ksplit", T=700, d_model=3000, d_hidden=8, n_experts=96, k=4,
+                    logit_bias="normal0.5", seed=811)
+    assert moe.moe_gate_k_splits(cfg) == 2
+    T, n, k = cfg.T, cfg.n_experts, cfg.k
+    log(f"[stage gate, K-split] T={T} d={cfg.d_model} n={n} k={k}")
+    inp = make_inputs(cfg, device="cuda")
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    imp = torch.empty(n, dtype=torch.float32, device="cuda")
+    ld = torch.empty(n, dtype=torch.float32, device="cuda")
+    st = torch.empty(2, dtype=torch.float32, device="cuda")
+    moe.moe_gate(cfg, inp["x"], inp["w_gate"], inp["b_gate"], inp["w_noise"], inp["noise"], idx,
+                 w, imp, ld, st, _ws(cfg))
+    torch.cuda.synchronize()
+    h = host(inp, ["x", "w_gate", "b_gate", "w_noise", "noise"])
+    g = oracle.gate(h["x"], h["w_gate"], k, h["b_gate"], h["w_noise"], h["noise"], cfg.gate)
+    bad = routing_mismatches(idx.cpu().numpy(), g.topk_idx, g.H, k)
+    assert len(bad) == 0, bad
+    np.testing.assert_allclose(w.cpu().numpy(), g.topk_w, rtol=TOL_W_REL, atol=TOL_W)
+    assert_close_rel(imp.cpu().numpy(), g.importance, 1e-5, 1e-5, "importance")
+    assert_close_rel(ld.cpu().numpy(), g.load, 1e-5, 1e-5, "load")
+    assert_close_rel(st.cpu().numpy(), [g.zsum, g.entsum], TOL_AUX, 1e-7, "gate stats")
+
+
 def _gate_only_inputs(cfg):
     small = cfg.replace(d_hidden=8, n_experts=cfg.n_experts, d_hidden_shared=0)
     # Same seeds for x / gate / noise as the full preset; tiny experts.
