@@ -14,20 +14,31 @@
 //    accumulation registers: per 16-wide K slice a wave reads 8 LDS
 //    fragments for 16 MFMAs (half a fragment per MFMA), and the tile reuses
 //    each weight row over 256 token rows;
-//  * the operands reach LDS through registers: each K-step of 64 (32 KB per
-//    operand) is loaded two steps ahead into one of two register sets (buffer
-//    loads, 16 per thread), then written to one of two LDS stages, so two
-//    steps' loads (128 KB per CU) are in flight while a step computes;
-//  * the load cursor runs across tile boundaries, so the next tile's first
-//    steps load while this tile finishes and stores;
-//  * loads never leave their operand: each buffer descriptor spans the
+//  * the operands go from memory straight into LDS (buffer loads with the
+//    LDS destination bit, no registers in between): two LDS stages of one
+//    64-wide K-step (32 KB per operand); while a step computes from one
+//    stage, its 16 copies per wave fill the other with the next step.  The
+//    copies are issued four at a time between the step's first 16 MFMAs, so
+//    the matrix unit keeps busy while the copy instructions issue; each step
+//    ends with the wave's copies landed and one workgroup barrier;
+//  * the copy cursor runs across tile boundaries, so the next tile's first
+//    step loads while this tile finishes and stores;
+//  * copies never leave their operand: each buffer descriptor spans the
 //    tile's rows only (the segment's live rows, the weight rows below N), and
 //    an out-of-range offset returns zeros without a memory access -- rows
-//    past a segment's end, columns past N, chunks past K and the extra step
-//    of an odd step count all read as zeros;
+//    past a segment's end, columns past N and chunks past K all read as
+//    zeros; past the last tile the descriptors span nothing;
 //  * LDS rows are 128 bytes (8 chunks of 16 bytes), chunk c of row r at
 //    position c ^ ((r >> 1) & 7), so the fragment reads of 16 consecutive
-//    rows hit 16 distinct bank groups.
+//    rows hit 16 distinct bank groups.  A copy moves 8 rows x 128 bytes into
+//    1 KB of LDS, lane i to bytes 16 i; lane i therefore reads the logical
+//    chunk that belongs at physical chunk i % 8 of its row;
+//  * work order: items in groups of kGroupM M-tiles (M fastest), cut into
+//    chunks of one XCD's workgroup count and dealt to the 8 XCDs in turn, so
+//    the XCDs work on neighbouring chunks -- mostly the same expert -- at the
+//    same time and its weights are fetched from HBM once for all of them
+//    (the repeats hit the Infinity Cache), while within an XCD the chunk's
+//    ~4 M-tiles x 8 N-tiles share their K-slices in the XCD's L2.
 // The MFMA computes D = W . X^T (weights as the A operand), so each lane ends
 // with 4 consecutive output columns of each of its rows.
 // SwiGLU: a tile's 256 weight rows are 128 columns of W1 and the same 128
@@ -52,9 +63,7 @@ constexpr int kGroupM = 4;           // M-tiles per group of the work order
 // returns zeros.
 constexpr int kOutOfRange = 0x40000000;
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ int swz(int r, int c) { return (c ^ ((r >> 1) & 7)) << 4; }
+typedef __attribute__((address_space(3))) void* lds_ptr;
 
 // A buffer descriptor over `bytes` bytes from `base` (raw, 32-bit data
 // format: plain byte addressing with a range check).
@@ -63,23 +72,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, long lo
                                            (int)min(bytes, (long long)kOutOfRange), 0x00020000);
 }
 
-// The loads of one step: thread t moves chunk (t & 7) of tile rows
-// (t >> 3) + 32 i, i < 8, of each operand.  Activation row r of the tile is
-// row row0 + r of X; weight row r is a column of W1 or W3 (see col_of).
-struct Cursor {
-  __amdgpu_buffer_rsrc_t xr, wr1, wr3;
-  int tile;  // tile the cursor is in (index into this workgroup's list)
-  int k;     // K-step within it
-};
-
 template <int EPI>
 struct Shape {
   static constexpr bool kSwiglu = EPI == EPI_SWIGLU_BF16;
   // Output columns per tile (SwiGLU: 128 columns of W1 and of W3).
   static constexpr int kCols = kSwiglu ? 128 : 256;
-  // Tile weight row r = lr + 32 i: its matrix (0: W1, 1: W3) and its column
-  // offset from the tile's first column.  SwiGLU: rows [128 w, 128 w + 64)
-  // are W1 columns 64 w + (r % 64), the next 64 rows the same W3 columns.
+  // Tile weight rows [32 i, 32 i + 32): their matrix (0: W1, 1: W3) and
+  // column offset from the tile's first column.  SwiGLU: rows [128 w, 128 w
+  // + 64) are W1 columns 64 w + (r % 64), the next 64 rows the same W3
+  // columns.
   static __device__ __forceinline__ int matrix(int i) { return kSwiglu ? (i >> 1) & 1 : 0; }
   static __device__ __forceinline__ int col(int i) {
     return kSwiglu ? (i >> 2) * 64 + (i & 1) * 32 : i * 32;
@@ -96,25 +97,25 @@ ggemm_big_kernel(const GemmBf16Args p) {
   // the compiler that it uses them keeps every MFMA in that form.
   asm volatile("" ::: "a0");
 
-  // This workgroup's tiles: XCD x owns tiles [x*per, (x+1)*per); its
-  // workgroups take every wpx-th of them.
+  // This workgroup's items: chunks of wpx consecutive items (wpx = the
+  // workgroups per XCD) go to the XCDs in turn, chunk c to XCD c % 8; slot s
+  // of an XCD takes item s of each of its chunks.
   const int nN = (p.N + S::kCols - 1) / S::kCols;
   const int total = *p.tile_count * nN;
-  const int per = (total + kXcds - 1) / kXcds;
   const int xcd = (int)(blockIdx.x % kXcds), slot = (int)(blockIdx.x / kXcds);
   const int wpx = (int)(gridDim.x / kXcds);
-  const int first = xcd * per + slot;
-  const int last = min(total, (xcd + 1) * per);
-  const int ntiles = first < last ? (last - first + wpx - 1) / wpx : 0;
+  const int nchunks = (total + wpx - 1) / wpx;
+  int ntiles = xcd < nchunks ? (nchunks - xcd + kXcds - 1) / kXcds : 0;
+  if (ntiles > 0 && xcd + kXcds * (ntiles - 1) == nchunks - 1 &&
+      (nchunks - 1) * wpx + slot >= total)
+    --ntiles;  // this slot is past the end of the last, partial chunk
   if (ntiles == 0) return;
   const int tid = threadIdx.x;
-  // Item L -> (M-tile, N-tile) in groups of kGroupM consecutive M-tiles:
-  // within a group the M-tile varies fastest, so the 32 workgroups of an XCD
-  // work on about 4 M-tiles x 8 N-tiles at a time (their activation and
-  // weight slices of a K-step fit the XCD's L2 many steps over).
+  // Item L -> (M-tile, N-tile) in groups of kGroupM consecutive M-tiles,
+  // the M-tile varying fastest within a group.
   const int mtiles = *p.tile_count;
   for (int t = tid; t < ntiles; t += kThreads) {
-    const int L = first + t * wpx;
+    const int L = (t * kXcds + xcd) * wpx + slot;
     const int grp = L / (kGroupM * nN), r = L % (kGroupM * nN);
     const int gsz = min(kGroupM, mtiles - grp * kGroupM);
     const int mt = grp * kGroupM + r % gsz, nt = r / gsz;
@@ -125,87 +126,74 @@ ggemm_big_kernel(const GemmBf16Args p) {
 
   const int K = p.K;
   const int nk = (K + kBK - 1) / kBK;
-  const int nk2 = (nk + 1) & ~1;  // steps per tile: an odd count runs one on zeros
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int lc = tid & 7, lr = tid >> 3;
   const int lr32 = lane & 31, lh = lane >> 5;
-  const long long xrow = p.lda * 2, wrow = (long long)K * 2;  // bytes per row
-  const int vx = lr * (int)xrow + lc * 16, vw = lr * (int)wrow + lc * 16;
 
-  // ---- load cursor ------------------------------------------------------
-  Cursor cur;
+  // ---- copy cursor ------------------------------------------------------
+  // Copy j (0..7) of an operand moves tile rows 32 j + 8 wave + lane / 8
+  // into LDS bytes [(4 j + wave) * 1024, +1024) of that operand's half of a
+  // stage: physical chunk lane % 8 of its row, which holds logical chunk
+  // (lane % 8) ^ ((row >> 1) & 7) -- the same for every j, since 32 j leaves
+  // bits 1..3 of the row alone.
+  const int lchunk = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
+  const int lrow = 8 * wave + (lane >> 3);  // row within each 32-row block
+  const long long xrowb = p.lda * 2, wrow = (long long)K * 2;
+  const int xoff0 = lrow * (int)xrowb + lchunk * 16;
+  const int woff0 = lrow * (int)wrow + lchunk * 16;
+  __amdgpu_buffer_rsrc_t xr, wr1, wr3;
+  int ct = 0, ck = 0;  // the cursor: tile, K-step
   auto set_tile = [&](int ti) {
     const int4 m = meta[ti];
     const int e = __builtin_amdgcn_readfirstlane(m.x);
     const int row0 = __builtin_amdgcn_readfirstlane(m.y);
     const int end = __builtin_amdgcn_readfirstlane(m.z);
     const int col0 = __builtin_amdgcn_readfirstlane(m.w);
-    const int live = min(kBM, end - row0);
-    cur.xr = rsrc(p.A + (long long)row0 * p.lda, (long long)live * xrow);
+    xr = rsrc(p.A + (long long)row0 * p.lda, (long long)min(kBM, end - row0) * xrowb);
+    const int wlive = min(S::kCols, p.N - col0);
     const uint8_t* w1 = (const uint8_t*)p.B1 + (long long)e * p.strideB;
-    const int wlive = min(S::kSwiglu ? 128 : 256, p.N - col0);
-    cur.wr1 = rsrc(w1 + (long long)col0 * wrow, (long long)wlive * wrow);
+    wr1 = rsrc(w1 + (long long)col0 * wrow, (long long)wlive * wrow);
     if constexpr (S::kSwiglu) {
       const uint8_t* w3 = (const uint8_t*)p.B3 + (long long)e * p.strideB;
-      cur.wr3 = rsrc(w3 + (long long)col0 * wrow, (long long)wlive * wrow);
+      wr3 = rsrc(w3 + (long long)col0 * wrow, (long long)wlive * wrow);
+    } else {
+      wr3 = wr1;
     }
   };
-  cur.tile = 0;
-  cur.k = 0;
   set_tile(0);
-  // Quarter q of the loads of step (cur.tile, cur.k) into R: activation rows
-  // (q < 2) or weight rows (q >= 2) 32 i + lr for i = 4 (q % 2) .. + 3.  Past
-  // the last tile, and at steps past K, the offsets leave the descriptors'
-  // ranges and the loads return zeros.  advance() moves the cursor on.
-  int oor = 0, so = 0;
-  auto gload_q = [&](u32x4 (&R)[16], int q) {
-    if (q == 0) {
-      const int k = cur.k;
-      const bool live = cur.tile < ntiles && k < nk;
-      // chunks past K in the last step read as zeros (K is a multiple of 8)
-      const bool kin = k * kBK + lc * 8 < K;
-      oor = (live && kin) ? 0 : kOutOfRange;
-      so = k * 128;
-    }
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int i = (q & 1) * 4 + ii;
-      if (q < 2) {
-        R[i] = __builtin_amdgcn_raw_buffer_load_b128(cur.xr, vx + i * 32 * (int)xrow + oor, so, 0);
-      } else {
-        const int vo = vw + S::col(i) * (int)wrow + oor;
-        R[8 + i] =
-            __builtin_amdgcn_raw_buffer_load_b128(S::matrix(i) ? cur.wr3 : cur.wr1, vo, so, 0);
+  auto advance = [&]() {
+    if (++ck == nk) {
+      ck = 0;
+      if (++ct < ntiles) {
+        set_tile(ct);
+      } else {  // past the last tile: descriptors that span nothing
+        xr = rsrc(p.A, 0);
+        wr1 = rsrc(p.B1, 0);
+        wr3 = wr1;
       }
     }
   };
-  auto advance = [&]() {
-    if (++cur.k == nk2) {
-      cur.k = 0;
-      if (++cur.tile < ntiles) set_tile(cur.tile);
+  // Copy q of the cursor's step into stage st: q < 8 the activation rows of
+  // block q, else the weight rows of block q - 8.  The descriptor is picked
+  // in a statement of its own: the copy builtin takes it as a plain variable.
+  auto copy = [&](int st, int q) {
+    uint8_t* sb = smem + st * kStage + wave * 1024;
+    const int koff = ck * 128;
+    const int oor = ck * kBK + lchunk * 8 < K ? 0 : kOutOfRange;
+    if (q < 8) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr)(sb + q * 4096), 16,
+                                               xoff0 + q * 32 * (int)xrowb + oor, koff, 0, 0);
+    } else {
+      const int j = q - 8;
+      const int wo = woff0 + S::col(j) * (int)wrow + oor;
+      if (S::matrix(j))
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr3, (lds_ptr)(sb + kTileB + j * 4096), 16, wo,
+                                                 koff, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr1, (lds_ptr)(sb + kTileB + j * 4096), 16, wo,
+                                                 koff, 0, 0);
     }
-  };
-  auto gload = [&](u32x4 (&R)[16]) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) gload_q(R, q);
-    advance();
-  };
-  const int wofs = lr * kRowB + swz(lr, lc);  // rows lr + 32 i share lr's swizzle
-  // Rows 32 i + lr, i = 4 h .. 4 h + 3, of both operands into `stage`.
-  auto swrite_h = [&](int stage, const u32x4 (&R)[16], int h) {
-    uint8_t* base = smem + stage * kStage + wofs;
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int i = h * 4 + ii;
-      *(u32x4*)(base + i * 32 * kRowB) = R[i];
-      *(u32x4*)(base + kTileB + i * 32 * kRowB) = R[8 + i];
-    }
-  };
-  auto swrite = [&](int stage, const u32x4 (&R)[16]) {
-    swrite_h(stage, R, 0);
-    swrite_h(stage, R, 1);
   };
 
   // ---- compute ------------------------------------------------------------
@@ -214,71 +202,72 @@ ggemm_big_kernel(const GemmBf16Args p) {
   // activation rows wm*128 + j*32 + lr32 (all sharing lr32's swizzle), chunk
   // 2 kk + lh.
   const int fs = (lr32 >> 1) & 7, fo = lr32 * kRowB;
+  auto frag_off = [&](int kk) { return fo + (((2 * kk + lh) ^ fs) << 4); };
   auto rdfrag = [&](const uint8_t* st, int kk, bf16x8 (&wf)[4], bf16x8 (&xf)[4]) {
-    const int o = fo + (((2 * kk + lh) ^ fs) << 4);
+    const int o = frag_off(kk);
 #pragma unroll
     for (int b = 0; b < 4; ++b)
       wf[b] = *(const bf16x8*)(st + kTileB + (wn * 128 + b * 32) * kRowB + o);
 #pragma unroll
     for (int j = 0; j < 4; ++j) xf[j] = *(const bf16x8*)(st + (wm * 128 + j * 32) * kRowB + o);
   };
+  auto mfma_row = [&](int b, const bf16x8 (&wf)[4], const bf16x8 (&xf)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[b][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[b], xf[j], acc[b][j], 0, 0, 0);
+  };
   auto mfmas = [&](const bf16x8 (&wf)[4], const bf16x8 (&xf)[4]) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[b][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[b], xf[j], acc[b][j], 0, 0, 0);
+    for (int b = 0; b < 4; ++b) mfma_row(b, wf, xf);
   };
-  // One K-step from LDS stage `stage`: load the step two ahead into Rl,
-  // compute, write Rw (the next step, loaded a step ago) into the other
-  // stage, barrier.
-  // One K-step from LDS stage `stage`, four 16-wide K slices.  Spread among
-  // each slice's 16 MFMAs: a quarter of the loads of the step two ahead
-  // (into Rl), the next slice's 8 fragment reads, and in slices 2 and 3 half
-  // of the LDS writes of the next step (Rw, loaded a step ago) into the other
-  // stage -- every wave finished reading that stage before the previous
-  // barrier.  Issued back to back, the loads would hold up the MFMAs behind
-  // them (in-order issue); spread out, the copies and the MFMAs overlap.
-  auto group = [&](bool writes, bool reads) {
+  // Spread among a slice's 16 MFMAs: the next slice's 8 fragment reads.
+  auto group = [&](bool reads) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);             // a load
-      if (writes) __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);  // two LDS writes
-      if (reads) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two LDS reads
+      if (reads) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);             // four MFMAs
     }
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto step = [&](int stage, u32x4 (&Rl)[16], const u32x4 (&Rw)[16]) {
+  // One K-step from stage `stage`, four 16-wide K slices.  Slice 0 runs in
+  // four rounds of four copies of the next step (into the other stage, which
+  // every wave finished reading before the previous barrier), two fragment
+  // reads of slice 1 and four MFMAs, pinned in that order; the later slices
+  // interleave their MFMAs with the next slice's reads.  The step ends when
+  // this wave's copies have landed (the compiler waits for them before the
+  // barrier) and all waves reach the barrier.
+  auto step = [&](int stage) {
     const uint8_t* st = smem + stage * kStage;
     bf16x8 wa[4], xa[4], wb[4], xb[4];
     rdfrag(st, 0, wa, xa);
-    gload_q(Rl, 0);
-    rdfrag(st, 1, wb, xb);
-    mfmas(wa, xa);
-    group(false, true);
-    gload_q(Rl, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const int o1 = frag_off(1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) copy(stage ^ 1, 4 * q + u);
+      wb[q] = *(const bf16x8*)(st + kTileB + (wn * 128 + q * 32) * kRowB + o1);
+      xb[q] = *(const bf16x8*)(st + (wm * 128 + q * 32) * kRowB + o1);
+      mfma_row(q, wa, xa);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    advance();
     rdfrag(st, 2, wa, xa);
     mfmas(wb, xb);
-    group(false, true);
-    gload_q(Rl, 2);
-    swrite_h(stage ^ 1, Rw, 0);
+    group(true);
     rdfrag(st, 3, wb, xb);
     mfmas(wa, xa);
-    group(true, true);
-    gload_q(Rl, 3);
-    advance();
-    swrite_h(stage ^ 1, Rw, 1);
+    group(true);
     mfmas(wb, xb);
-    group(true, false);
+    group(false);
     __syncthreads();
   };
-  u32x4 R0[16], R1[16];
-  gload(R0);
-  gload(R1);
-  swrite(0, R0);
+#pragma unroll
+  for (int q = 0; q < 16; ++q) copy(0, q);
+  advance();
   __syncthreads();
 
+  int stage = 0;
   for (int t = 0; t < ntiles; ++t) {
     const int4 m = meta[t];
     const int e = __builtin_amdgcn_readfirstlane(m.x);
@@ -291,9 +280,9 @@ ggemm_big_kernel(const GemmBf16Args p) {
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[b][j][v] = 0.f;
-    for (int g = 0; g < nk2; g += 2) {
-      step(0, R0, R1);
-      step(1, R1, R0);
+    for (int g = 0; g < nk; ++g) {
+      step(stage);
+      stage ^= 1;
     }
 
     // Epilogue.  D[n][m]: lane holds token row m = lr32 of each 32 x 32
