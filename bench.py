@@ -323,7 +323,8 @@ def cpu_baseline(cfg, inp, y_gpu, idx_gpu, sample_tokens, seconds):
     expert's weights are copied to the host outside the timed parts, so the
     figure is the oracle's own compute.  Without `sample_tokens`, S doubles
     from 16 until a pass takes a quarter of `seconds`, then grows so that one
-    pass takes about half of it.  Where the
+    pass takes about half of it (all of it where the weights do not fit on
+    the host and the pass does not repeat).  Where the
     weights fit on the host (at most 16 GiB in float64) they are kept and the
     pass repeats until `seconds` have passed; the same oracle also runs on
     one core on a smaller sample.  The GPU's y on the sample is checked
@@ -399,8 +400,10 @@ def cpu_baseline(cfg, inp, y_gpu, idx_gpu, sample_tokens, seconds):
     while sized and S < T and dt < seconds / 4:   # more rows per expert: more threads busy
         S = min(T, 2 * S)
         dt, idx, y = one_pass(S)
-    if sized and S < T and dt < seconds / 2:
-        S = int(min(T, S * seconds / 2 / max(dt, 1e-3)))
+    # one pass of about half of `seconds` when it repeats, else one of about `seconds`
+    target = seconds / 2 if keep else seconds
+    if sized and S < T and dt < target:
+        S = int(min(T, S * target / max(dt, 1e-3)))
         dt, idx, y = one_pass(S)
     reps = 1
     while keep and dt < seconds:
@@ -823,5 +826,19 @@ def cpu_baseline_backward(cfg, inp, dy, dl, sample_tokens, seconds):
                       f"recompute and every gradient in float64), {reps} runs in {dt:.2f} s"}
 
 
+def report_children():
+    """The run starts no process of its own (the oracle and the library are
+    loaded in-process); list any child process still alive at exit on
+    stderr, so a leftover would show in the log."""
+    try:
+        import psutil
+    except ImportError:
+        return
+    kids = psutil.Process().children(recursive=True)
+    log(f"[bench] child processes at exit: {len(kids)}"
+        + "".join(f"\n[bench]   pid {k.pid}: {' '.join(k.cmdline()[:4])}" for k in kids))
+
+
 if __name__ == "__main__":
     main()
+    report_children()
