@@ -142,13 +142,13 @@ def kernel_work(name, cfg, rows, nonempty, T):
     if name in ("ggemm_bf16_out", "ggemm_big_out"):
         return (nonempty * d * h * 2 + rows * h * 2 + rows * d * 4, 2.0 * rows * d * h, "bf16")
     # FP8 experts: one byte per weight plus one fp32 scale per weight row
-    if name == "ggemm_fp8_relu":
+    if name in ("ggemm_fp8_relu", "ggemm_big_fp8_relu"):
         return (nonempty * (h * d + 4 * h) + rows * d * 2 + rows * h * 2, 2.0 * rows * h * d,
                 "bf16")
-    if name == "ggemm_fp8_swiglu":
+    if name in ("ggemm_fp8_swiglu", "ggemm_big_fp8_swiglu"):
         return (nonempty * 2 * (h * d + 4 * h) + rows * d * 2 + rows * h * 2,
                 4.0 * rows * h * d, "bf16")
-    if name == "ggemm_fp8_out":
+    if name in ("ggemm_fp8_out", "ggemm_big_fp8_out"):
         return (nonempty * (d * h + 4 * d) + rows * h * 2 + rows * d * 4, 2.0 * rows * d * h,
                 "bf16")
     hs = cfg.d_hidden_shared

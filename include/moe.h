@@ -158,8 +158,9 @@ size_t moe_workspace_size(const moe_config* cfg);
 /* How moe_expert_ffn / moe_forward split the experts between their two
  * grouped GEMMs: experts keeping at least this many rows run on 256 x 256
  * tiles, the others on 128-row tiles (0: every expert on 128-row tiles).
- * Depends on the config only (bf16 weights with d_model and d_hidden both
- * >= 2048 split); the results do not depend on it.  0 on an invalid config. */
+ * Depends on the config only (bf16 or FP8 weights with d_model and d_hidden
+ * both >= 2048 split); the results do not depend on it.  0 on an invalid
+ * config. */
 int32_t moe_expert_split_rows(const moe_config* cfg);
 
 /* Into how many K ranges moe_gate, moe_gate_hier (its primary gate) and

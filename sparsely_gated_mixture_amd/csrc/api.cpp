@@ -206,10 +206,10 @@ struct Cursor {
 // the others on the 128-row one; 0: every expert on the 128-row GEMM.  The
 // split pays where both products are long (K >= 2048 each: the fine-grained
 // layer measured 17 % faster, 4.9 against 5.9 ms for the two GEMMs); with
-// short K (d = 512, h = 1024) every split measured slower.  bf16 weights
-// only.
+// short K (d = 512, h = 1024) every split measured slower.  bf16 and FP8
+// weights (fp32 experts run on their own GEMM).
 int split_rows(const moe_config& c) {
-  if (c.expert_dtype != MOE_BF16) return 0;
+  if (c.expert_dtype != MOE_BF16 && c.expert_dtype != MOE_FP8) return 0;
   return (c.d_model >= 2048 && c.d_hidden >= 2048) ? kSplitRows : 0;
 }
 
@@ -659,12 +659,14 @@ moe_status run_ffn(const moe_config& c, const Plan& p, const void* x_perm,
     } else {
       HIP_TRY(launch_tilemap_split(offsets, n, kBf16BM, p.big_rows, sm, bg, s));
     }
+    const bool fp8 = c.expert_dtype == MOE_FP8;
     GemmBf16Args g{};
     g.A = (const uint16_t*)x_perm;
     g.lda = d;
     g.B1 = w1;
     g.B3 = w3;
-    g.strideB = (long long)h * d * 2;
+    g.strideB = fp8 ? (long long)h * d + 4LL * h : (long long)h * d * 2;
+    g.fp8 = fp8;
     g.N = h;
     g.K = d;
     g.C = hidden;
@@ -677,7 +679,7 @@ moe_status run_ffn(const moe_config& c, const Plan& p, const void* x_perm,
     g2.lda = h;
     g2.B1 = w2;
     g2.B3 = nullptr;
-    g2.strideB = (long long)d * h * 2;
+    g2.strideB = fp8 ? (long long)d * h + 4LL * d : (long long)d * h * 2;
     g2.N = d;
     g2.K = h;
     g2.C = y_perm;

@@ -32,6 +32,18 @@ __device__ __forceinline__ uint32_t bf16x2_bits(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Eight E4M3 codes (bytes of `raw`, lowest first) as eight bf16 values, with
+// the gfx950 conversion instruction (v_cvt_scalef32_pk_bf16_fp8, scale 1).
+// Every E4M3 value is exact in bf16, so the widening loses nothing.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint2 raw) {
+  typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+  const bf2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.x, 1.0f, false);
+  const bf2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.x, 1.0f, true);
+  const bf2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.y, 1.0f, false);
+  const bf2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.y, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float((uint32_t)h << 16);
 }

@@ -53,18 +53,6 @@ constexpr int kThreads = kWaves * 64;
 
 __device__ __forceinline__ int swz(int r, int c) { return (c ^ ((r >> 1) & 7)) << 4; }
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// Eight E4M3 codes (bytes of `raw`, lowest first) as eight bf16 values.
-// Every E4M3 value is exact in bf16, so the widening loses nothing.
-__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint2 raw) {
-  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.x, 1.0f, false);
-  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.x, 1.0f, true);
-  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.y, 1.0f, false);
-  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.y, 1.0f, true);
-  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
 // HAS_BIAS is a template parameter so that the usual bias-free kernels have
 // no global loads in the epilogue (the compiler would otherwise wait there
 // for every copy in flight).

@@ -15,12 +15,13 @@
 //    fragments for 16 MFMAs (half a fragment per MFMA), and the tile reuses
 //    each weight row over 256 token rows;
 //  * the operands go from memory straight into LDS (buffer loads with the
-//    LDS destination bit, no registers in between): two LDS stages of one
-//    64-wide K-step (32 KB per operand); while a step computes from one
-//    stage, its 16 copies per wave fill the other with the next step.  The
-//    copies are issued four at a time between the step's first 16 MFMAs, so
-//    the matrix unit keeps busy while the copy instructions issue; each step
-//    ends with the wave's copies landed and one workgroup barrier;
+//    LDS destination bit, no registers in between, issued by the copy
+//    helper of lds_dma.h): two LDS stages of one 64-wide K-step (32 KB per
+//    operand); while a step computes from one stage, its 16 copies per wave
+//    fill the other with the next step.  The copies are issued a quarter at
+//    a time between the step's first 16 MFMAs, so the matrix unit keeps busy
+//    while the copy instructions issue; each step ends with the wave's
+//    copies landed (an explicit vmcnt wait) and one workgroup barrier;
 //  * the copy cursor runs across tile boundaries, so the next tile's first
 //    step loads while this tile finishes and stores;
 //  * copies never leave their operand: each buffer descriptor spans the
@@ -44,10 +45,18 @@
 // SwiGLU: a tile's 256 weight rows are 128 columns of W1 and the same 128
 // columns of W3, ordered so that each wave holds 64 columns of both and each
 // lane the matching pairs: the epilogue forms silu(g) * u in registers.
+// FP8 weights (E4M3 codes in the packed layout of moe_pack_fp8_weights: row
+// pairs, 128 bytes per pair and 64-wide K block, then one fp32 scale per
+// row): a weight row takes 64 bytes of LDS per step (16 codes = one 16-wide
+// K slice per 16-byte chunk, chunk c at c ^ ((row >> 1) & 3)), so a step's
+// weights are 16 KB in 4 copies per wave; each lane reads its 8 codes of a
+// slice and widens them to bf16 in registers, and the epilogue multiplies
+// each output column by its row scale.
 #include <math.h>
 
 #include "common.h"
 #include "launch.h"
+#include "lds_dma.h"
 
 namespace moe {
 namespace {
@@ -55,22 +64,22 @@ namespace {
 constexpr int kBM = kBigBM;    // rows per M-tile (the big tile map's granularity)
 constexpr int kBK = 64;        // K per step
 constexpr int kRowB = 128;     // LDS bytes per row and step (kBK bf16)
-constexpr int kTileB = 256 * kRowB;  // one operand's 32 KB per step
-constexpr int kStage = 2 * kTileB;   // 64 KB per LDS stage
+constexpr int kTileB = 256 * kRowB;  // the activations' 32 KB per step
 constexpr int kThreads = 256;
 constexpr int kGroupM = 4;           // M-tiles per group of the work order
 // A buffer offset this large lies beyond every descriptor's range: the load
 // returns zeros.
 constexpr int kOutOfRange = 0x40000000;
 
-typedef __attribute__((address_space(3))) void* lds_ptr;
 
-// A buffer descriptor over `bytes` bytes from `base` (raw, 32-bit data
-// format: plain byte addressing with a range check).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, long long bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
-                                           (int)min(bytes, (long long)kOutOfRange), 0x00020000);
-}
+// Weight rows in LDS: bf16 128 bytes per row and step, FP8 64.
+template <bool FP8>
+struct WRows {
+  static constexpr int kRowB = FP8 ? 64 : 128;
+  static constexpr int kTileB = 256 * kRowB;      // a step's weights
+  static constexpr int kStage = ::moe::kTileB + kTileB;  // activations + weights
+  static constexpr int kCopies = FP8 ? 4 : 8;     // weight copies per wave and step
+};
 
 template <int EPI>
 struct Shape {
@@ -87,10 +96,11 @@ struct Shape {
   }
 };
 
-template <int EPI, bool HAS_BIAS>
+template <int EPI, bool HAS_BIAS, bool FP8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 ggemm_big_kernel(const GemmBf16Args p) {
   using S = Shape<EPI>;
+  using W = WRows<FP8>;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   __shared__ int4 meta[kMaxTilesPerWG];  // per tile: expert, first row, end row, first column
   // The kernel keeps its accumulators in the accumulation registers; telling
@@ -132,17 +142,30 @@ ggemm_big_kernel(const GemmBf16Args p) {
   const int lr32 = lane & 31, lh = lane >> 5;
 
   // ---- copy cursor ------------------------------------------------------
-  // Copy j (0..7) of an operand moves tile rows 32 j + 8 wave + lane / 8
-  // into LDS bytes [(4 j + wave) * 1024, +1024) of that operand's half of a
-  // stage: physical chunk lane % 8 of its row, which holds logical chunk
-  // (lane % 8) ^ ((row >> 1) & 7) -- the same for every j, since 32 j leaves
-  // bits 1..3 of the row alone.
+  // Activations (and bf16 weights): copy j (0..7) moves tile rows 32 j + 8
+  // wave + lane / 8 into LDS bytes [(4 j + wave) * 1024, +1024) of the
+  // operand's part of a stage: physical chunk lane % 8 of its row, which
+  // holds logical chunk (lane % 8) ^ ((row >> 1) & 7) -- the same for every
+  // j, since 32 j leaves bits 1..3 of the row alone.
+  // FP8 weights: copy j (0..3) moves tile rows 64 j + 16 wave + lane / 4
+  // (64-byte LDS rows): physical chunk lane % 4, logical chunk (lane % 4) ^
+  // ((row >> 1) & 3) = (lane % 4) ^ ((lane / 8) % 4); those rows are rows 16
+  // (wave % 2) + lane / 4 of the 32-row weight blocks 2 j + wave / 2.
   const int lchunk = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
   const int lrow = 8 * wave + (lane >> 3);  // row within each 32-row block
-  const long long xrowb = p.lda * 2, wrow = (long long)K * 2;
+  const long long xrowb = p.lda * 2;
+  const long long wrow = (long long)K * 2;  // bf16 weight row; FP8: bytes per row pair
   const int xoff0 = lrow * (int)xrowb + lchunk * 16;
-  const int woff0 = lrow * (int)wrow + lchunk * 16;
-  __amdgpu_buffer_rsrc_t xr, wr1, wr3;
+  int woff0;
+  if constexpr (FP8) {
+    const int rin = 16 * (wave & 1) + (lane >> 2);
+    const int lc8 = (lane & 3) ^ ((lane >> 3) & 3);
+    woff0 = (rin >> 1) * (int)wrow + (rin & 1) * 64 + lc8 * 16;
+  } else {
+    woff0 = lrow * (int)wrow + lchunk * 16;
+  }
+  rsrc_t xr, wr1, wr3;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   int ct = 0, ck = 0;  // the cursor: tile, K-step
   auto set_tile = [&](int ti) {
     const int4 m = meta[ti];
@@ -150,13 +173,16 @@ ggemm_big_kernel(const GemmBf16Args p) {
     const int row0 = __builtin_amdgcn_readfirstlane(m.y);
     const int end = __builtin_amdgcn_readfirstlane(m.z);
     const int col0 = __builtin_amdgcn_readfirstlane(m.w);
-    xr = rsrc(p.A + (long long)row0 * p.lda, (long long)min(kBM, end - row0) * xrowb);
+    xr = buffer_rsrc(p.A + (long long)row0 * p.lda, (long long)min(kBM, end - row0) * xrowb);
     const int wlive = min(S::kCols, p.N - col0);
+    // bf16: rows [col0, col0 + wlive); FP8: the row pairs holding them (col0 is even)
+    const long long wbase = FP8 ? (long long)(col0 >> 1) * wrow : (long long)col0 * wrow;
+    const long long wbytes = FP8 ? (long long)((wlive + 1) >> 1) * wrow : (long long)wlive * wrow;
     const uint8_t* w1 = (const uint8_t*)p.B1 + (long long)e * p.strideB;
-    wr1 = rsrc(w1 + (long long)col0 * wrow, (long long)wlive * wrow);
+    wr1 = buffer_rsrc(w1 + wbase, wbytes);
     if constexpr (S::kSwiglu) {
       const uint8_t* w3 = (const uint8_t*)p.B3 + (long long)e * p.strideB;
-      wr3 = rsrc(w3 + (long long)col0 * wrow, (long long)wlive * wrow);
+      wr3 = buffer_rsrc(w3 + wbase, wbytes);
     } else {
       wr3 = wr1;
     }
@@ -168,48 +194,58 @@ ggemm_big_kernel(const GemmBf16Args p) {
       if (++ct < ntiles) {
         set_tile(ct);
       } else {  // past the last tile: descriptors that span nothing
-        xr = rsrc(p.A, 0);
-        wr1 = rsrc(p.B1, 0);
+        xr = buffer_rsrc(p.A, 0);
+        wr1 = buffer_rsrc(p.B1, 0);
         wr3 = wr1;
       }
     }
   };
   // Copy q of the cursor's step into stage st: q < 8 the activation rows of
-  // block q, else the weight rows of block q - 8.  The descriptor is picked
-  // in a statement of its own: the copy builtin takes it as a plain variable.
+  // block q, else weight copy q - 8.  FP8 weights need K % 64 == 0 (no tail).
   auto copy = [&](int st, int q) {
-    uint8_t* sb = smem + st * kStage + wave * 1024;
+    const uint32_t sb = lds0 + st * W::kStage + wave * 1024;
     const int koff = ck * 128;
     const int oor = ck * kBK + lchunk * 8 < K ? 0 : kOutOfRange;
     if (q < 8) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr)(sb + q * 4096), 16,
-                                               xoff0 + q * 32 * (int)xrowb + oor, koff, 0, 0);
+      bdma16(xr, xoff0 + q * 32 * (int)xrowb + oor, koff, sb + q * 4096);
     } else {
       const int j = q - 8;
-      const int wo = woff0 + S::col(j) * (int)wrow + oor;
-      if (S::matrix(j))
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr3, (lds_ptr)(sb + kTileB + j * 4096), 16, wo,
-                                                 koff, 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr1, (lds_ptr)(sb + kTileB + j * 4096), 16, wo,
-                                                 koff, 0, 0);
+      const int blk = FP8 ? 2 * j + (wave >> 1) : j;  // 32-row weight block
+      const int wo = FP8 ? woff0 + (S::col(blk) >> 1) * (int)wrow
+                         : woff0 + S::col(blk) * (int)wrow + oor;
+      bdma16(S::matrix(blk) ? wr3 : wr1, wo, koff, sb + kTileB + j * 4096);
     }
   };
+  constexpr int kCopies = 8 + W::kCopies;     // per wave and step
+  constexpr int kPerRound = kCopies / 4;      // issued with each row of slice 0's MFMAs
 
   // ---- compute ------------------------------------------------------------
   f32x16 acc[4][4];
   // Fragments of one 16-wide K slice: weight rows wn*128 + b*32 + lr32 and
   // activation rows wm*128 + j*32 + lr32 (all sharing lr32's swizzle), chunk
-  // 2 kk + lh.
+  // 2 kk + lh (FP8 weights: the lh half of 16-byte chunk kk).
   const int fs = (lr32 >> 1) & 7, fo = lr32 * kRowB;
   auto frag_off = [&](int kk) { return fo + (((2 * kk + lh) ^ fs) << 4); };
+  // FP8: this lane's 8 codes of weight block b in slice kk.
+  auto wraw = [&](const uint8_t* st, int kk, int b) -> uint2 {
+    const int r = wn * 128 + b * 32 + lr32;
+    return *(const uint2*)(st + kTileB + r * W::kRowB + ((kk ^ ((lr32 >> 1) & 3)) << 4) +
+                           lh * 8);
+  };
+  auto wfrag = [&](const uint8_t* st, int kk, int b) -> bf16x8 {
+    if constexpr (FP8)
+      return e4m3x8_to_bf16(wraw(st, kk, b));
+    else
+      return *(const bf16x8*)(st + kTileB + (wn * 128 + b * 32) * kRowB + frag_off(kk));
+  };
+  auto xfrag = [&](const uint8_t* st, int kk, int j) -> bf16x8 {
+    return *(const bf16x8*)(st + (wm * 128 + j * 32) * kRowB + frag_off(kk));
+  };
   auto rdfrag = [&](const uint8_t* st, int kk, bf16x8 (&wf)[4], bf16x8 (&xf)[4]) {
-    const int o = frag_off(kk);
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
-      wf[b] = *(const bf16x8*)(st + kTileB + (wn * 128 + b * 32) * kRowB + o);
+    for (int b = 0; b < 4; ++b) wf[b] = wfrag(st, kk, b);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xf[j] = *(const bf16x8*)(st + (wm * 128 + j * 32) * kRowB + o);
+    for (int j = 0; j < 4; ++j) xf[j] = xfrag(st, kk, j);
   };
   auto mfma_row = [&](int b, const bf16x8 (&wf)[4], const bf16x8 (&xf)[4]) {
 #pragma unroll
@@ -220,36 +256,59 @@ ggemm_big_kernel(const GemmBf16Args p) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) mfma_row(b, wf, xf);
   };
-  // Spread among a slice's 16 MFMAs: the next slice's 8 fragment reads.
+  // Spread among a slice's 16 MFMAs: the next slice's 8 fragment reads
+  // (FP8: the reads in the first half, then the 16 widening instructions of
+  // the codes they brought, so the widening waits on reads issued 8 MFMAs
+  // earlier).
   auto group = [&](bool reads) {
+    if (FP8 && reads) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (reads) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);             // four MFMAs
+      for (int q = 0; q < 2; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // four LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // four MFMAs
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // eight VALU (widening)
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // four MFMAs
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (reads) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);             // four MFMAs
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   };
   // One K-step from stage `stage`, four 16-wide K slices.  Slice 0 runs in
-  // four rounds of four copies of the next step (into the other stage, which
-  // every wave finished reading before the previous barrier), two fragment
-  // reads of slice 1 and four MFMAs, pinned in that order; the later slices
-  // interleave their MFMAs with the next slice's reads.  The step ends when
-  // this wave's copies have landed (the compiler waits for them before the
-  // barrier) and all waves reach the barrier.
+  // four rounds of a quarter of the next step's copies (into the other
+  // stage, which every wave finished reading before the previous barrier),
+  // two fragment reads of slice 1 and four MFMAs, pinned in that order; the
+  // later slices interleave their MFMAs with the next slice's reads.  The
+  // step ends when this wave's copies have landed and all waves reach the
+  // barrier.
   auto step = [&](int stage) {
-    const uint8_t* st = smem + stage * kStage;
+    const uint8_t* st = smem + stage * W::kStage;
     bf16x8 wa[4], xa[4], wb[4], xb[4];
     rdfrag(st, 0, wa, xa);
     __builtin_amdgcn_sched_barrier(0);
-    const int o1 = frag_off(1);
+    uint2 rb[4];  // FP8: slice 1's codes, widened after the rounds
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) copy(stage ^ 1, 4 * q + u);
-      wb[q] = *(const bf16x8*)(st + kTileB + (wn * 128 + q * 32) * kRowB + o1);
-      xb[q] = *(const bf16x8*)(st + (wm * 128 + q * 32) * kRowB + o1);
+      for (int u = 0; u < kPerRound; ++u) copy(stage ^ 1, kPerRound * q + u);
+      if constexpr (FP8)
+        rb[q] = wraw(st, 1, q);
+      else
+        wb[q] = wfrag(st, 1, q);
+      xb[q] = xfrag(st, 1, q);
       mfma_row(q, wa, xa);
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (FP8) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) wb[q] = e4m3x8_to_bf16(rb[q]);
     }
     advance();
     rdfrag(st, 2, wa, xa);
@@ -260,11 +319,13 @@ ggemm_big_kernel(const GemmBf16Args p) {
     group(true);
     mfmas(wb, xb);
     group(false);
+    wait_vm<0>();
     __syncthreads();
   };
 #pragma unroll
-  for (int q = 0; q < 16; ++q) copy(0, q);
+  for (int q = 0; q < kCopies; ++q) copy(0, q);
   advance();
+  wait_vm<0>();
   __syncthreads();
 
   int stage = 0;
@@ -286,8 +347,16 @@ ggemm_big_kernel(const GemmBf16Args p) {
     }
 
     // Epilogue.  D[n][m]: lane holds token row m = lr32 of each 32 x 32
-    // block and weight rows n = 8 (v / 4) + 4 lh + v % 4.
+    // block and weight rows n = 8 (v / 4) + 4 lh + v % 4.  FP8: the row
+    // scales follow each expert's codes.
     const float* bias = HAS_BIAS ? p.bias + (long long)e * p.N : nullptr;
+    const float* sc1 = nullptr;
+    const float* sc3 = nullptr;
+    if constexpr (FP8) {
+      sc1 = (const float*)((const uint8_t*)p.B1 + (long long)e * p.strideB + (long long)p.N * K);
+      if constexpr (S::kSwiglu)
+        sc3 = (const float*)((const uint8_t*)p.B3 + (long long)e * p.strideB + (long long)p.N * K);
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int gr = row0 + wm * 128 + j * 32 + lr32;
@@ -299,10 +368,15 @@ ggemm_big_kernel(const GemmBf16Args p) {
           for (int q = 0; q < 4; ++q) {
             const int gc = col0 + wn * 64 + b * 32 + 8 * q + 4 * lh;
             if (gc >= p.N) continue;
+            f32x4 s1 = {1.f, 1.f, 1.f, 1.f}, s3 = {1.f, 1.f, 1.f, 1.f};
+            if constexpr (FP8) {
+              s1 = *(const f32x4*)(sc1 + gc);
+              s3 = *(const f32x4*)(sc3 + gc);
+            }
             float f[4];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-              const float gv = acc[b][j][4 * q + v], uv = acc[b + 2][j][4 * q + v];
+              const float gv = acc[b][j][4 * q + v] * s1[v], uv = acc[b + 2][j][4 * q + v] * s3[v];
               f[v] = gv / (1.f + expf(-gv)) * uv;
             }
             *(uint2*)((uint16_t*)p.C + (long long)gr * p.ldc + gc) =
@@ -315,10 +389,12 @@ ggemm_big_kernel(const GemmBf16Args p) {
           for (int q = 0; q < 4; ++q) {
             const int gc = col0 + wn * 128 + b * 32 + 8 * q + 4 * lh;
             if (gc >= p.N) continue;
+            f32x4 s1 = {1.f, 1.f, 1.f, 1.f};
+            if constexpr (FP8) s1 = *(const f32x4*)(sc1 + gc);
             float f[4];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-              f[v] = acc[b][j][4 * q + v];
+              f[v] = acc[b][j][4 * q + v] * s1[v];
               if constexpr (HAS_BIAS) f[v] += bias[gc + v];
               if constexpr (EPI == EPI_RELU_BF16) f[v] = fmaxf(f[v], 0.f);
             }
@@ -333,9 +409,11 @@ ggemm_big_kernel(const GemmBf16Args p) {
   }
 }
 
-template <int EPI, bool HAS_BIAS>
+template <int EPI, bool HAS_BIAS, bool FP8>
 hipError_t launch_t(const GemmBf16Args& a, hipStream_t s) {
   using S = Shape<EPI>;
+  using W = WRows<FP8>;
+  if (FP8 && a.K % kBK) return hipErrorInvalidValue;  // FP8 codes come in 64-wide K blocks
   const int nN = (a.N + S::kCols - 1) / S::kCols;
   const long long max_total = (long long)a.max_mtiles * nN;
   if (max_total <= 0) return hipSuccess;
@@ -343,27 +421,38 @@ hipError_t launch_t(const GemmBf16Args& a, hipStream_t s) {
   if (grid < kXcds) grid = kXcds;
   const long long per = (max_total + kXcds - 1) / kXcds;
   while ((per + grid / kXcds - 1) / (grid / kXcds) > kMaxTilesPerWG) grid += kXcds;
-  static const char* const kNames[3] = {"ggemm_big_relu", "ggemm_big_swiglu", "ggemm_big_out"};
-  ProfScope ps(a.prof_name ? a.prof_name : kNames[EPI], s);
-  const void* fn = (const void*)ggemm_big_kernel<EPI, HAS_BIAS>;
-  hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kStage);
+  static const char* const kNames[2][3] = {
+      {"ggemm_big_relu", "ggemm_big_swiglu", "ggemm_big_out"},
+      {"ggemm_big_fp8_relu", "ggemm_big_fp8_swiglu", "ggemm_big_fp8_out"}};
+  ProfScope ps(a.prof_name ? a.prof_name : kNames[FP8 ? 1 : 0][EPI], s);
+  const void* fn = (const void*)ggemm_big_kernel<EPI, HAS_BIAS, FP8>;
+  hipError_t err =
+      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * W::kStage);
   if (err != hipSuccess) return err;
-  ggemm_big_kernel<EPI, HAS_BIAS><<<dim3((unsigned)grid), dim3(kThreads), 2 * kStage, s>>>(a);
+  ggemm_big_kernel<EPI, HAS_BIAS, FP8>
+      <<<dim3((unsigned)grid), dim3(kThreads), 2 * W::kStage, s>>>(a);
   return hipGetLastError();
+}
+
+template <bool FP8>
+hipError_t launch_typed(const GemmBf16Args& a, int epi, hipStream_t s) {
+  const bool bias = a.bias != nullptr;
+  switch (epi) {
+    case EPI_RELU_BF16:
+      return bias ? launch_t<EPI_RELU_BF16, true, FP8>(a, s)
+                  : launch_t<EPI_RELU_BF16, false, FP8>(a, s);
+    case EPI_SWIGLU_BF16:
+      return launch_t<EPI_SWIGLU_BF16, false, FP8>(a, s);
+    default:
+      return bias ? launch_t<EPI_IDENT_F32, true, FP8>(a, s)
+                  : launch_t<EPI_IDENT_F32, false, FP8>(a, s);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_gemm_big(const GemmBf16Args& a, int epi, hipStream_t s) {
-  const bool bias = a.bias != nullptr;
-  switch (epi) {
-    case EPI_RELU_BF16:
-      return bias ? launch_t<EPI_RELU_BF16, true>(a, s) : launch_t<EPI_RELU_BF16, false>(a, s);
-    case EPI_SWIGLU_BF16:
-      return launch_t<EPI_SWIGLU_BF16, false>(a, s);
-    default:
-      return bias ? launch_t<EPI_IDENT_F32, true>(a, s) : launch_t<EPI_IDENT_F32, false>(a, s);
-  }
+  return a.fp8 ? launch_typed<true>(a, epi, s) : launch_typed<false>(a, epi, s);
 }
 
 }  // namespace moe

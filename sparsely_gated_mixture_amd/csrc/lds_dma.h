@@ -38,6 +38,40 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
 #pragma clang diagnostic pop
 }
 
+// 16-byte buffer -> LDS copy through a buffer descriptor (raw addressing
+// with the descriptor's range check: an offset past its range copies zeros
+// and touches no memory).  voff is the lane's byte offset, soff a
+// wave-uniform one added to it; lane i writes LDS bytes [lds + 16 i, +16).
+// Same m0 handling and the same reason for not using the compiler builtin
+// as dma16; in addition, after such builtin copies the compiler inserts full
+// vmcnt waits before LDS reads it cannot prove disjoint from the copies'
+// destination, which would serialise a copy stream with the reads of the
+// other LDS stage.
+typedef uint32_t rsrc_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void bdma16(rsrc_t rsrc, int voff, int soff, uint32_t lds) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds),
+      "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+// A raw buffer descriptor (byte addressing, range check) over `bytes` bytes
+// from `base`, in scalar registers; `bytes` above 2^30 are clamped to 2^30.
+__device__ __forceinline__ rsrc_t buffer_rsrc(const void* base, long long bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  rsrc_t r;
+  r.x = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  r.y = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xffffu);
+  r.z = __builtin_amdgcn_readfirstlane((uint32_t)(bytes < (1LL << 30) ? bytes : (1LL << 30)));
+  r.w = 0x00020000u;
+  return r;
+}
+
 // Wait until at most N vector memory operations of this wave are in flight.
 // Loads complete in order, so this covers every copy issued more than N
 // loads ago.

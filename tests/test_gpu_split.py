@@ -5,15 +5,16 @@ oracle on shapes that reach both kernels, with an odd count of K-steps and
 a K tail (chunks past K), N tails (a last N-tile of 8 or 40 columns), expert
 biases through the big kernel's ReLU and identity epilogues, segments of one
 to several 256-row tiles, the shared expert on 256-row tiles, and the
-standalone moe_expert_ffn (which builds the two tile maps itself)."""
+standalone moe_expert_ffn (which builds the two tile maps itself), and FP8
+weights on both kernels (the oracle runs on the dequantized weights)."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import sparsely_gated_mixture_amd as moe
-from sparsely_gated_mixture_amd.workloads import (ACT_SWIGLU, GATE_SIGMOID_BIAS, MoEConfig,
-                                                  make_inputs)
+from sparsely_gated_mixture_amd.workloads import (ACT_SWIGLU, DTYPE_FP8, GATE_SIGMOID_BIAS,
+                                                  MoEConfig, make_inputs)
 from _support import (dev_inputs, expert_weights_host, full_parity, host, log, max_abs_norm)
 
 pytestmark = pytest.mark.gpu
@@ -80,3 +81,24 @@ def test_split_stage_expert_ffn():
     log(f"  y_perm error {err:.3e}")
     assert err <= 2e-2
     assert torch.all(yp[rows:] == 7.0)  # rows past offsets[n] untouched
+
+
+def test_split_fp8_swiglu():
+    # FP8 E4M3 weights on both kernels: h = 2112 ends the SwiGLU GEMM's last
+    # 128-column N-tile with 64 columns (half the row pairs of the tile).
+    cfg = MoEConfig("split_fp8_swiglu", T=400, d_model=2048, d_hidden=2112, n_experts=6, k=2,
+                    act=ACT_SWIGLU, expert_dtype=DTYPE_FP8, noisy=False, logit_bias="zipf1.1",
+                    seed=504)
+    gpu, ref = full_parity(cfg)
+    split, small, big = _classes(cfg, gpu["counts"])
+    assert small >= 1 and big >= 1
+
+
+def test_split_fp8_relu_biases():
+    # FP8 weights with ReLU, expert biases N(0, 0.1^2) and the row scales in
+    # the same epilogue; the output GEMM's N = 2112 ends in a 64-column tile.
+    cfg = MoEConfig("split_fp8_relu", T=360, d_model=2112, d_hidden=2048, n_experts=5, k=2,
+                    expert_dtype=DTYPE_FP8, logit_bias="zipf1.1", expert_bias_std=0.1, seed=505)
+    gpu, ref = full_parity(cfg)
+    split, small, big = _classes(cfg, gpu["counts"])
+    assert small >= 1 and big >= 1

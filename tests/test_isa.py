@@ -1,7 +1,8 @@
 """Checks of the compiled gfx950 code (CPU only: hipcc cross-compiles).
 
-The grouped GEMMs copy operands global -> LDS with an inline-asm
-global_load_lds_dwordx4 whose LDS address the asm writes into m0 itself.
+The grouped GEMMs copy operands global -> LDS with inline-asm
+global_load_lds_dwordx4 / buffer_load_dwordx4 ... lds instructions whose LDS
+address the asm writes into m0 itself.
 That is sound only while no compiler-generated instruction of those kernels
 reads m0 (the compiler would not know the asm changed it).  This test
 compiles every source that includes the copy helper and checks the code:
@@ -19,7 +20,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "sparsely_gated_mixture_amd", "csrc")
 
-# Instructions that read m0 without naming it.
+# Instructions that read m0 without naming it (besides buffer loads carrying
+# the lds modifier, matched on the whole line below).
 IMPLICIT_M0 = re.compile(r"^(s_movrel|v_movrel|s_sendmsg|ds_gws|ds_append|ds_consume|"
                          r"ds_ordered_count|s_set_gpr_idx|v_interp|ds_param|ds_direct|"
                          r"buffer_load_\w*lds|global_load_lds|scratch_load_lds|"
@@ -57,10 +59,15 @@ def test_m0_is_written_only_by_the_copy_helper(src, tmp_path):
         if re.search(r"\bm0\b", ins):
             assert op == "s_mov_b32" and ins.split()[1].rstrip(",") == "m0", (
                 f"{src}: compiler-generated use of m0: {ins}")
-            assert code[i + 1] == "s_nop 0" and code[i + 2].startswith(
-                "global_load_lds_dwordx4"), f"{src}: m0 write not followed by its copy: {ins}"
-        elif IMPLICIT_M0.match(op):
-            assert op == "global_load_lds_dwordx4" and code[i - 2].startswith("s_mov_b32 m0"), (
+            nxt = code[i + 2]
+            assert code[i + 1] == "s_nop 0" and (
+                nxt.startswith("global_load_lds_dwordx4") or
+                (nxt.startswith("buffer_load_dwordx4") and nxt.endswith(" lds"))), (
+                f"{src}: m0 write not followed by its copy: {ins}")
+        elif IMPLICIT_M0.match(op) or (op.startswith("buffer_load") and ins.endswith(" lds")):
+            is_copy = op == "global_load_lds_dwordx4" or (op == "buffer_load_dwordx4" and
+                                                          ins.endswith(" lds"))
+            assert is_copy and code[i - 2].startswith("s_mov_b32 m0"), (
                 f"{src}: instruction reading m0 outside the copy helper: {ins}")
             copies += 1
     assert copies > 0, f"{src}: no global->LDS copies found"
