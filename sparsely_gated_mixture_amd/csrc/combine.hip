@@ -18,23 +18,33 @@
 namespace moe {
 namespace {
 
-// One wavefront per token.  Lane s holds the token's slot s (position and
-// weight, k <= 64), broadcast with readlane; each pass covers 512 columns
-// with two 16-byte vectors per lane, so the loads of every kept row of the
-// pass are independent.  Per element: acc = base, then acc = fma(w_s, row_s,
-// acc) in slot order.
+// wpt wavefronts per token (1 while the batch fills the chip, else up to 8,
+// each taking every wpt-th pass of the row).  Lane s holds the token's slot s
+// (position and weight, k <= 64), broadcast with readlane; each pass covers
+// 512 columns with two 16-byte vectors per lane.  The slots go in groups of eight: the
+// loads of a group's rows are all issued before its multiply-adds, so a wave
+// keeps 16 KB of y_perm in flight.  Each slot's row is read through a
+// buffer descriptor over that row (scalar registers: the row is the same for
+// the whole wave); a dropped slot's descriptor spans nothing, so its loads
+// return zeros without a memory access and no branch breaks the group.
+// Per element: acc = base, then acc = fma(w_s, row_s, acc) in slot order (a
+// dropped slot adds w_s * 0).
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_perm,
                                                       const int32_t* __restrict__ slot_pos,
                                                       const float* __restrict__ topk_w,
                                                       const float* __restrict__ y_base, int T,
-                                                      int k, int d, float* __restrict__ y) {
+                                                      int k, int d, int wpt,
+                                                      float* __restrict__ y) {
   constexpr int V = 2;
+  constexpr int G = 8;  // slots per group of loads
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = gw / wpt, part = gw % wpt;
   if (t >= T) return;
   const int my_pos = lane < k ? slot_pos[(long long)t * k + lane] : -1;
   const float my_w = lane < k ? topk_w[(long long)t * k + lane] : 0.f;
-  for (int c0 = 0; c0 < d; c0 += 64 * 4 * V) {
+  constexpr int kOutOfRange = 0x40000000;  // past every row's descriptor
+  for (int c0 = part * 64 * 4 * V; c0 < d; c0 += 64 * 4 * V * wpt) {
     bool ok[V];
     int cc[V];
     f32x4 acc[V];
@@ -45,17 +55,29 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (y_base && ok[v]) acc[v] = *(const f32x4*)(y_base + (long long)t * d + cc[v]);
     }
-    for (int s = 0; s < k; ++s) {
-      const int pos = __builtin_amdgcn_readlane(my_pos, s);
-      if (pos < 0) continue;
-      const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), s));
+    for (int s0 = 0; s0 < k; s0 += G) {
+      f32x4 x[G][V];
+      float ws[G];
 #pragma unroll
-      for (int v = 0; v < V; ++v)
-        if (ok[v]) {
-          const f32x4 x = *(const f32x4*)(y_perm + (long long)pos * d + cc[v]);
+      for (int g = 0; g < G; ++g) {
+        const int s = s0 + g;  // s < 64 always; lanes past k hold pos -1 and weight 0
+        const int pos = __builtin_amdgcn_readlane(my_pos, s & 63);
+        ws[g] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), s & 63));
+        const bool live = pos >= 0 && s < k;
+        const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(y_perm) + (long long)(live ? pos : 0) * d, (short)0,
+            live ? d * 4 : 0, 0x00020000);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) acc[v][q] = fmaf(ws, x[q], acc[v][q]);
-        }
+        for (int v = 0; v < V; ++v)
+          x[g][v] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  yr, ok[v] ? cc[v] * 4 : kOutOfRange, 0, 0));
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[v][q] = fmaf(ws[g], x[g][v][q], acc[v][q]);
     }
 #pragma unroll
     for (int v = 0; v < V; ++v)
@@ -80,9 +102,16 @@ __global__ __launch_bounds__(256) void aux_kernel(const float* __restrict__ impo
 hipError_t launch_combine(const float* y_perm, const int32_t* slot_pos, const float* topk_w,
                           const float* y_base, int T, int k, int d, float* y, hipStream_t s) {
   if (T <= 0) return hipSuccess;
+  // Waves per token: enough for about 8192 waves (32 per CU), at most one
+  // per 512-column pass and at most 8.
+  const int passes = (d + 511) / 512;
+  int wpt = (8192 + T - 1) / T;
+  wpt = wpt < 1 ? 1 : wpt > 8 ? 8 : wpt;
+  if (wpt > passes) wpt = passes;
+  const long long waves = (long long)T * wpt;
   ProfScope ps("combine", s);
-  combine_kernel<<<dim3((T + 3) / 4), dim3(256), 0, s>>>(y_perm, slot_pos, topk_w, y_base, T, k,
-                                                         d, y);
+  combine_kernel<<<dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s>>>(
+      y_perm, slot_pos, topk_w, y_base, T, k, d, wpt, y);
   return hipGetLastError();
 }
 
