@@ -18,8 +18,8 @@
 //    LDS destination bit, no registers in between, issued by the copy
 //    helper of lds_dma.h): two LDS stages of one 64-wide K-step (32 KB per
 //    operand); while a step computes from one stage, its 16 copies per wave
-//    fill the other with the next step.  The copies are issued a quarter at
-//    a time between the step's first 16 MFMAs, so the matrix unit keeps busy
+//    fill the other with the next step.  The copies are issued an eighth at
+//    a time between the step's first 32 MFMAs, so the matrix unit keeps busy
 //    while the copy instructions issue; each step ends with the wave's
 //    copies landed (an explicit vmcnt wait) and one workgroup barrier;
 //  * the copy cursor runs across tile boundaries, so the next tile's first
@@ -217,7 +217,6 @@ ggemm_big_kernel(const GemmBf16Args p) {
     }
   };
   constexpr int kCopies = 8 + W::kCopies;     // per wave and step
-  constexpr int kPerRound = kCopies / 4;      // issued with each row of slice 0's MFMAs
 
   // ---- compute ------------------------------------------------------------
   f32x16 acc[4][4];
@@ -281,39 +280,46 @@ ggemm_big_kernel(const GemmBf16Args p) {
     }
     __builtin_amdgcn_sched_barrier(0);
   };
-  // One K-step from stage `stage`, four 16-wide K slices.  Slice 0 runs in
-  // four rounds of a quarter of the next step's copies (into the other
-  // stage, which every wave finished reading before the previous barrier),
-  // two fragment reads of slice 1 and four MFMAs, pinned in that order; the
-  // later slices interleave their MFMAs with the next slice's reads.  The
-  // step ends when this wave's copies have landed and all waves reach the
-  // barrier.
+  // One K-step from stage `stage`, four 16-wide K slices.  Slices 0 and 1
+  // run in four rounds each: an eighth of the next step's copies (into the
+  // other stage, which every wave finished reading before the previous
+  // barrier), the next slice's four weight and four activation fragment
+  // reads, and one row of four MFMAs, pinned in that order.  Spread this way
+  // the copies keep the LDS command queue from filling (issued four at a
+  // time in slice 0 alone they measured 6-10 % slower, all over the four
+  // slices slower still: the last copies land too late).  Slices 2 and 3
+  // interleave their MFMAs with the next slice's reads.  The step ends when
+  // this wave's copies have landed and all waves reach the barrier.  FP8:
+  // the codes read in a slice's rounds are widened right after them.
   auto step = [&](int stage) {
     const uint8_t* st = smem + stage * W::kStage;
     bf16x8 wa[4], xa[4], wb[4], xb[4];
+    uint2 rw[4];  // FP8: codes of the slice read in the rounds
     rdfrag(st, 0, wa, xa);
     __builtin_amdgcn_sched_barrier(0);
-    uint2 rb[4];  // FP8: slice 1's codes, widened after the rounds
+    auto rounds = [&](int r0, int kk, const bf16x8(&wc)[4], const bf16x8(&xc)[4],
+                      bf16x8(&wn)[4], bf16x8(&xn)[4]) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < 4; ++q) {
 #pragma unroll
-      for (int u = 0; u < kPerRound; ++u) copy(stage ^ 1, kPerRound * q + u);
-      if constexpr (FP8)
-        rb[q] = wraw(st, 1, q);
-      else
-        wb[q] = wfrag(st, 1, q);
-      xb[q] = xfrag(st, 1, q);
-      mfma_row(q, wa, xa);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if constexpr (FP8) {
+        for (int c = (r0 + q) * kCopies / 8; c < (r0 + q + 1) * kCopies / 8; ++c)
+          copy(stage ^ 1, c);
+        if constexpr (FP8)
+          rw[q] = wraw(st, kk, q);
+        else
+          wn[q] = wfrag(st, kk, q);
+        xn[q] = xfrag(st, kk, q);
+        mfma_row(q, wc, xc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (FP8) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) wb[q] = e4m3x8_to_bf16(rb[q]);
-    }
+        for (int q = 0; q < 4; ++q) wn[q] = e4m3x8_to_bf16(rw[q]);
+      }
+    };
+    rounds(0, 1, wa, xa, wb, xb);  // slice 0; reads slice 1
+    rounds(4, 2, wb, xb, wa, xa);  // slice 1; reads slice 2
     advance();
-    rdfrag(st, 2, wa, xa);
-    mfmas(wb, xb);
-    group(true);
     rdfrag(st, 3, wb, xb);
     mfmas(wa, xa);
     group(true);
