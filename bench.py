@@ -21,6 +21,12 @@ JSON line:
                `traffic` is the kernel's HBM bytes per launch from the
                rocprofv3 counter summary under profiles/, reported only while
                the kernel's source is the one the counters were taken on;
+  side_by_side where the bf16 experts split by size run their two grouped
+               GEMMs side by side on shares of the CUs: the shares, and per
+               phase (first GEMM, second GEMM) both kernels' algorithmic
+               bytes and flops over the longer duration; the 256 x 256
+               kernels' entries also carry their rate against their share of
+               the matrix-unit peak (frac_cu_share);
   kernels      the same figures for every kernel of the step;
   timing       also per-step HIP-event medians, p10 and p90, warm (back to
                back) and cold (a 512 MiB write before each step evicts L2
@@ -113,6 +119,44 @@ def launch_experts(name, cfg, counts):
     if split > 0:
         c = c[c >= split] if name.startswith("ggemm_big_") else c[c < split]
     return int(c.sum()), int(len(c))
+
+
+def side_by_side(cfg, counts, kernels):
+    """The two expert GEMM classes run side by side on shares of the CUs
+    (moe_expert_cu_split): each such kernel entry gets its CU count, the
+    256 x 256 kernels their rate against their share of the matrix-unit
+    peak, and the result describes each phase (first GEMM, second GEMM) as a
+    whole: both kernels' algorithmic bytes and flops over the longer of the
+    two durations (they start together).  None when they run one after the
+    other."""
+    import sparsely_gated_mixture_amd as moe
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    share = moe.moe_expert_cu_split(cfg, np.asarray(counts, np.int32), cus)
+    if not 0 < share < cus:
+        return None
+    out = {"cus_total": cus, "cus_big": share, "cus_small": cus - share, "phases": []}
+    for big_name, small_name in (("ggemm_big_swiglu", "ggemm_bf16_swiglu"),
+                                 ("ggemm_big_relu", "ggemm_bf16_relu"),
+                                 ("ggemm_big_out", "ggemm_bf16_out")):
+        b, sm = kernels.get(big_name), kernels.get(small_name)
+        if not b or not sm:
+            continue
+        b["cus"], sm["cus"] = share, cus - share
+        rl = b.get("roofline")
+        if rl and rl["bound"] == "mfma":
+            rl["peak_cu_share"] = rl["peak"] * share / cus
+            rl["frac_cu_share"] = rl["achieved"] / rl["peak_cu_share"]
+        t = max(b["avg_us"], sm["avg_us"]) * 1e-6
+        byt = b["algo_bytes"] + sm["algo_bytes"]
+        fl = b.get("flops", 0) + sm.get("flops", 0)
+        ph = {"kernels": [big_name, small_name], "us": t * 1e6, "algo_bytes": byt, "flops": fl,
+              "GB_s": byt / t / 1e9, "TFLOP_s": fl / t / 1e12}
+        if byt / PEAK_HBM_GBS / 1e9 >= fl / PEAK_TFLOPS["bf16"] / 1e12:
+            ph.update(bound="hbm", frac=ph["GB_s"] / PEAK_HBM_GBS)
+        else:
+            ph.update(bound="mfma", frac=ph["TFLOP_s"] / PEAK_TFLOPS["bf16"])
+        out["phases"].append(ph)
+    return out
 
 
 def kernel_work(name, cfg, rows, nonempty, T):
@@ -619,6 +663,7 @@ def main():
                   peaks["mfma_f32_TFLOP_s"])
             rl["peak_measured"] = mp
             rl["frac_measured"] = rl["achieved"] / mp
+    side = side_by_side(cfg, counts, kernels)
     dname = dominant[0]
     dk = kernels[dname]
     roofline = dict(dk["roofline"])
@@ -626,6 +671,9 @@ def main():
     roofline["traffic"] = measured_traffic(cfg.name, dname)
     roofline["algo_bytes_per_launch"] = dk["algo_bytes"]
     roofline["avg_us"] = dk["avg_us"]
+    if side:
+        roofline["cus"] = dk.get("cus")
+        roofline["side_by_side"] = side
 
     result = {
         "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
@@ -641,6 +689,7 @@ def main():
                    + (f", shared expert h={cfg.d_hidden_shared}" if cfg.d_hidden_shared else ""),
                    "rows": rows, "nonempty_experts": nonempty, "parallelism": "none (1 GPU)"},
         "roofline": roofline,
+        "side_by_side": side,
         "kernels": kernels,
         "timing": {"value_basis": "K back-to-back steps, host clock around the synchronised "
                                   "loop (the next step may find data of the previous one in "

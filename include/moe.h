@@ -170,6 +170,25 @@ int32_t moe_expert_split_rows(const moe_config* cfg);
  * order.  Depends on the config only; 0 on an invalid config. */
 int32_t moe_gate_k_splits(const moe_config* cfg);
 
+/* When experts are split by size (moe_expert_split_rows > 0) and the
+ * weights are bf16, the two grouped GEMMs run side by side: the small
+ * experts' 128-row GEMM, which streams their weights from HBM, on a second
+ * stream of the library's own, beside the big experts' 256 x 256-tile GEMM
+ * on the caller's stream, each on its own share of the compute units; the
+ * caller's stream waits for both before the combine.  (FP8 weights: one
+ * after the other.)  The share is computed on the device from the routing;
+ * this call computes the same share on the host.
+ *   counts: host array [n_experts] of the rows each expert keeps (the
+ *           dispatch's counts); cus: compute units of the GPU (0: the
+ *           current device's).
+ * Returns the compute units of the 256 x 256-tile GEMM (the other GEMM
+ * gets the rest): 0 without experts of at least moe_expert_split_rows rows,
+ * without the split or with FP8 weights, every CU without smaller non-empty
+ * experts, else a
+ * multiple of 8 (the XCD count) in [8, cus - 8].  -1 on an invalid config,
+ * null counts or cus < 0.  The results of the layer do not depend on it. */
+int32_t moe_expert_cu_split(const moe_config* cfg, const int32_t* counts, int32_t cus);
+
 /* Flat gating network: logits, noise, KeepTopK, softmax, and the two
  * auxiliary-loss vectors.
  *   Definition: xyznot.com summary, "Method and key formulas", Noisy Top-K

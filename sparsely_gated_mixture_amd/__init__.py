@@ -13,7 +13,8 @@ from ._lib import (EXPORTS, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTE
                    MOE_ERR_WORKSPACE, MOE_OK, N_LOSSES, MoeConfig, MoeDiag, MoEError,
                    MoeGrads, MoeWeights, load_library, make_config, make_diag, make_grads,
                    make_weights, moe_aux_loss, moe_backward, moe_backward_workspace_size,
-                   moe_combine, moe_dispatch, moe_expert_ffn, moe_expert_split_rows, moe_gate_k_splits,
+                   moe_combine, moe_dispatch, moe_expert_ffn, moe_expert_split_rows,
+                   moe_gate_k_splits, moe_expert_cu_split,
                    moe_backward_saved, moe_fp8_weight_bytes, moe_forward,
                    moe_forward_train, moe_pack_fp8_weights,
                    moe_gate, moe_gate_hier, moe_gate_static, moe_last_error, moe_profile_collect,

@@ -20,7 +20,7 @@ MOE_ERR_UNSUPPORTED = 2
 MOE_ERR_WORKSPACE = 3
 MOE_ERR_HIP = 4
 
-EXPORTS = ["moe_workspace_size", "moe_expert_split_rows", "moe_gate_k_splits", "moe_fp8_weight_bytes", "moe_pack_fp8_weights", "moe_gate",
+EXPORTS = ["moe_workspace_size", "moe_expert_split_rows", "moe_gate_k_splits", "moe_expert_cu_split", "moe_fp8_weight_bytes", "moe_pack_fp8_weights", "moe_gate",
            "moe_gate_static", "moe_gate_hier", "moe_dispatch", "moe_expert_ffn", "moe_shared_ffn", "moe_combine",
            "moe_aux_loss", "moe_router_bias_update", "moe_forward",
            "moe_backward_workspace_size", "moe_backward", "moe_forward_train",
@@ -94,6 +94,8 @@ def load_library():
     L.moe_expert_split_rows.restype = ctypes.c_int32
     L.moe_gate_k_splits.argtypes = [cfgp]
     L.moe_gate_k_splits.restype = ctypes.c_int32
+    L.moe_expert_cu_split.argtypes = [cfgp, P, i32]
+    L.moe_expert_cu_split.restype = ctypes.c_int32
     L.moe_fp8_weight_bytes.argtypes = [i32, i32, i32]
     L.moe_fp8_weight_bytes.restype = S
     L.moe_pack_fp8_weights.argtypes = [i32, i32, i32, i32, P, P, P]
@@ -209,6 +211,14 @@ def moe_expert_split_rows(cfg) -> int:
 def moe_gate_k_splits(cfg) -> int:
     c = make_config(cfg)
     return int(load_library().moe_gate_k_splits(ctypes.byref(c)))
+
+
+def moe_expert_cu_split(cfg, counts, cus: int = 0) -> int:
+    """counts: host int32 array (numpy or CPU tensor) of n_experts kept rows."""
+    import numpy as np
+    c = make_config(cfg)
+    a = np.ascontiguousarray(np.asarray(counts, dtype=np.int32))
+    return int(load_library().moe_expert_cu_split(ctypes.byref(c), a.ctypes.data, int(cus)))
 
 
 def moe_pack_fp8_weights(n_experts, N, K, src_dtype, src, dst, stream=None):

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <cstdlib>
 
 #include "../../include/moe.h"
 #include "launch.h"
@@ -152,6 +153,41 @@ int moe::device_cus() {
 
 namespace {
 
+// A second stream per device and the two events that fork work onto it from
+// the caller's stream and join it back (created on first use, kept until the
+// process ends; default priority).
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+SideStream* side_stream() {
+  static SideStream cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  SideStream& ss = cache[dev];
+  if (!ss.s) {
+    hipStream_t st = nullptr;
+    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
+      return nullptr;
+    ss.s = st;
+  }
+  return &ss;
+}
+
+// The side-by-side share's inputs for config c, written to `out` (device);
+// out stays null (no side-by-side run) unless the weights are bf16.
+CuSplit cu_split_of(const moe_config& c, int32_t* out) {
+  CuSplit sp{};
+  sp.out = c.expert_dtype == MOE_BF16 ? out : nullptr;
+  sp.cus = device_cus();
+  sp.d = c.d_model;
+  sp.h = c.d_hidden;
+  sp.swiglu = c.act == MOE_ACT_SWIGLU;
+  return sp;
+}
+
 // ---------------------------------------------------------------------------
 // Workspace layout.  [stage scratch: max over gate / dispatch / ffn]
 // [forward intermediates].  Stage calls use only the first part.
@@ -179,12 +215,12 @@ struct Plan {
   // experts split by size (big_rows > 0): fewer rows -> 128-row tiles of the
   // streaming GEMM (small map), more -> 256 x 256 tiles (big map)
   int big_rows = 0, max_mtiles_s = 0, max_mtiles_b = 0;
-  Region ts_expert, ts_row0, ts_count, tb_expert, tb_row0, tb_count;
+  Region ts_expert, ts_row0, ts_count, tb_expert, tb_row0, tb_count, t_split;
   size_t gate_bytes = 0, dispatch_bytes = 0, ffn_bytes = 0, stage_bytes = 0;
   // forward intermediates
   Region f_idx, f_w, f_imp, f_load, f_counts_pre, f_counts, f_offsets, f_perm, f_slot, f_xperm,
       f_yperm, f_tile_expert, f_tile_row0, f_tile_count, f_stats, f_ts_expert, f_ts_row0,
-      f_ts_count, f_tb_expert, f_tb_row0, f_tb_count;
+      f_ts_count, f_tb_expert, f_tb_row0, f_tb_count, f_split;
   // shared expert (d_hidden_shared > 0): bf16 copy of x, hidden, output, tile map
   int sh_tiles = 0;
   Region sh_xb, sh_hidden, sh_y, sh_te, sh_tr, sh_tc, sh_off;
@@ -314,6 +350,7 @@ Plan make_plan(const moe_config& c) {
     p.tb_expert = f.take((size_t)p.max_mtiles_b * 4);
     p.tb_row0 = f.take((size_t)p.max_mtiles_b * 4);
     p.tb_count = f.take(4);
+    p.t_split = f.take(4);
   }
   p.hidden = f.take(std::max(1LL, A) * h * (c.expert_dtype != MOE_F32 ? 2 : 4));
   p.ffn_bytes = f.at;
@@ -343,6 +380,7 @@ Plan make_plan(const moe_config& c) {
     p.f_tb_expert = w.take((size_t)p.max_mtiles_b * 4);
     p.f_tb_row0 = w.take((size_t)p.max_mtiles_b * 4);
     p.f_tb_count = w.take(4);
+    p.f_split = w.take(4);
   }
   if (c.d_hidden_shared > 0) {
     const long long hs = c.d_hidden_shared;
@@ -578,6 +616,7 @@ struct ForwardExtras {
   int32_t* tile_count = nullptr;
   int big_rows = 0;  // > 0: the dispatch also writes the size-split maps
   TileMap small_map{}, big_map{};
+  int32_t* cu_split = nullptr;  // with big_rows: where the dispatch writes the CU share
   float* losses = nullptr;
   const float* importance = nullptr;
   const float* load = nullptr;
@@ -614,6 +653,7 @@ moe_status run_dispatch(const moe_config& c, const Plan& p, const int32_t* topk_
     da.big_rows = fx->big_rows;
     da.small_map = fx->small_map;
     da.big_map = fx->big_map;
+    if (fx->big_rows > 0) da.split = cu_split_of(c, fx->cu_split);
     da.losses = fx->losses;
     da.importance = fx->importance;
     da.load = fx->load;
@@ -653,11 +693,14 @@ moe_status run_ffn(const moe_config& c, const Plan& p, const void* x_perm,
                at<int32_t>(ws, p.ts_count)};
     TileMap bg{at<int32_t>(ws, p.tb_expert), at<int32_t>(ws, p.tb_row0),
                at<int32_t>(ws, p.tb_count)};
+    int32_t* share = at<int32_t>(ws, p.t_split);
     if (fx && fx->big_rows > 0) {
       sm = fx->small_map;
       bg = fx->big_map;
+      share = fx->cu_split;
     } else {
-      HIP_TRY(launch_tilemap_split(offsets, n, kBf16BM, p.big_rows, sm, bg, s));
+      HIP_TRY(launch_tilemap_split(offsets, n, kBf16BM, p.big_rows, sm, bg,
+                                   cu_split_of(c, share), s));
     }
     const bool fp8 = c.expert_dtype == MOE_FP8;
     GemmBf16Args g{};
@@ -686,6 +729,15 @@ moe_status run_ffn(const moe_config& c, const Plan& p, const void* x_perm,
     g2.ldc = d;
     g2.bias = b2;
     const int epi1 = c.act == MOE_ACT_SWIGLU ? EPI_SWIGLU_BF16 : EPI_RELU_BF16;
+    // bf16 weights: the small experts' chain runs on the side stream beside
+    // the big experts' chain on `s`, each kernel on its share of the CUs.
+    // FP8 weights (or no side stream): one after the other, each on the
+    // whole grid.
+    SideStream* ss = c.expert_dtype == MOE_BF16 ? side_stream() : nullptr;
+    if (ss) {
+      HIP_TRY(hipEventRecord(ss->fork, s));
+      HIP_TRY(hipStreamWaitEvent(ss->s, ss->fork, 0));
+    }
     for (GemmBf16Args* a : {&g, &g2}) {
       GemmBf16Args as = *a, ab = *a;
       as.tile_expert = sm.expert;
@@ -696,9 +748,18 @@ moe_status run_ffn(const moe_config& c, const Plan& p, const void* x_perm,
       ab.tile_row0 = bg.row0;
       ab.tile_count = bg.count;
       ab.max_mtiles = p.max_mtiles_b;
+      if (ss) {
+        as.cu_split = ab.cu_split = share;
+        as.cu_big = 0;
+        ab.cu_big = 1;
+      }
       const int epi = a == &g ? epi1 : EPI_IDENT_F32;
-      HIP_TRY(launch_gemm_bf16(as, epi, s));
+      HIP_TRY(launch_gemm_bf16(as, epi, ss ? ss->s : s));
       HIP_TRY(launch_gemm_big(ab, epi, s));
+    }
+    if (ss) {
+      HIP_TRY(hipEventRecord(ss->join, ss->s));
+      HIP_TRY(hipStreamWaitEvent(s, ss->join, 0));
     }
     return MOE_OK;
   }
@@ -1554,6 +1615,21 @@ int32_t moe_gate_k_splits(const moe_config* cfg) {
   return make_plan(*cfg).gate_splits;
 }
 
+int32_t moe_expert_cu_split(const moe_config* cfg, const int32_t* counts, int32_t cus) {
+  if (validate(cfg) != MOE_OK || !counts || cus < 0) return -1;
+  const int big_rows = split_rows(*cfg);
+  if (big_rows <= 0) return 0;
+  long long br = 0, se = 0, sr = 0;
+  for (int e = 0; e < cfg->n_experts; ++e) {
+    const int kept = counts[e];
+    if (kept >= big_rows) br += kept;
+    else if (kept > 0) ++se, sr += kept;
+  }
+  if (cfg->expert_dtype != MOE_BF16) return 0;
+  const CuSplit sp = cu_split_of(*cfg, nullptr);
+  return expert_cu_split(cus > 0 ? cus : sp.cus, br, se, sr, sp.d, sp.h, sp.swiglu);
+}
+
 }  // extern "C"
 
 size_t moe::gate_workspace_bytes(const moe_config* cfg) {
@@ -1790,6 +1866,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const float
                            at<int32_t>(ws, p.f_ts_count)};
     fx.big_map = TileMap{at<int32_t>(ws, p.f_tb_expert), at<int32_t>(ws, p.f_tb_row0),
                          at<int32_t>(ws, p.f_tb_count)};
+    fx.cu_split = at<int32_t>(ws, p.f_split);
   }
   fx.losses = losses;
   fx.importance = imp;

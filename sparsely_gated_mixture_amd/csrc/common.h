@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.h"
+
 namespace moe {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -11,7 +13,21 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;   // CDNA wavefront width
-constexpr int kXcds = 8;    // MI355X: 8 accelerator complex dies, one L2 each
+
+// Workgroups a persistent grouped GEMM puts to work on `total` items: the
+// whole grid, or its share of a side-by-side run (cu_split), raised until no
+// workgroup holds more than kMaxTilesPerWG items (one holds at most
+// ceil(total / used) + 1 of them), never above the grid.  A multiple of kXcds.
+__device__ inline int gemm_used_grid(const GemmBf16Args& p, int total) {
+  const int grid = (int)gridDim.x;
+  if (!p.cu_split) return grid;
+  const int big = *p.cu_split;
+  int want = (p.cu_big ? big : p.num_cus - big) / kXcds * kXcds;
+  const int need =
+      ((total + kMaxTilesPerWG - 2) / (kMaxTilesPerWG - 1) + kXcds - 1) / kXcds * kXcds;
+  want = want > need ? want : need;
+  return want < grid ? want : grid;
+}
 
 // fp32 -> bf16 bit pattern, round to nearest, ties to even; NaN stays NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {

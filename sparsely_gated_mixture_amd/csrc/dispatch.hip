@@ -167,6 +167,20 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(const DispatchArg
         *a.small_map.count = cs.y;
         *a.big_map.count = cb.y;
       }
+      if (a.split.out) {
+        int big_r = 0, small_e = 0, small_r = 0;
+        for (int e = b; e < e1; ++e) {
+          const int kept = a.counts[e];
+          if (kept >= a.big_rows) big_r += kept;
+          else if (kept > 0) ++small_e, small_r += kept;
+        }
+        const int tb_rows = block_exscan<kFinThreads>(big_r, si).y;
+        const int ts_exp = block_exscan<kFinThreads>(small_e, si).y;
+        const int ts_rows = block_exscan<kFinThreads>(small_r, si).y;
+        if (threadIdx.x == 0)
+          *a.split.out = expert_cu_split(a.split.cus, tb_rows, ts_exp, ts_rows, a.split.d,
+                                         a.split.h, a.split.swiglu);
+      }
     }
   }
   if (a.losses)
@@ -318,7 +332,8 @@ __global__ __launch_bounds__(256) void bias_update_kernel(const int32_t* __restr
 // big-tile map (see launch_tilemap_split).
 __global__ __launch_bounds__(1024) void tilemap_split_kernel(const int32_t* __restrict__ offsets,
                                                              int n, int bm, int big_rows,
-                                                             TileMap sm, TileMap bg) {
+                                                             TileMap sm, TileMap bg,
+                                                             CuSplit split) {
   __shared__ int32_t tsum[2][1024];
   const int per = (n + 1023) / 1024;
   const int b = threadIdx.x * per;
@@ -357,6 +372,30 @@ __global__ __launch_bounds__(1024) void tilemap_split_kernel(const int32_t* __re
   if (threadIdx.x == 1023) {
     *sm.count = tsum[0][1023];
     *bg.count = tsum[1][1023];
+  }
+  if (split.out) {
+    // Rows of the big experts, count and rows of the small ones, summed in
+    // the same shared arrays (every thread has read its prefix above).
+    int v[3] = {0, 0, 0};
+    for (int i = 0; i < per && b + i < n; ++i) {
+      const int rows = offsets[b + i + 1] - offsets[b + i];
+      if (rows >= big_rows) v[0] += rows;
+      else if (rows > 0) v[1] += 1, v[2] += rows;
+    }
+    int tot[3];
+    for (int q = 0; q < 3; ++q) {
+      __syncthreads();
+      tsum[0][threadIdx.x] = v[q];
+      __syncthreads();
+      for (int off = 512; off > 0; off >>= 1) {
+        if ((int)threadIdx.x < off) tsum[0][threadIdx.x] += tsum[0][threadIdx.x + off];
+        __syncthreads();
+      }
+      tot[q] = tsum[0][0];
+    }
+    if (threadIdx.x == 0)
+      *split.out = expert_cu_split(split.cus, tot[0], tot[1], tot[2], split.d, split.h,
+                                   split.swiglu);
   }
 }
 
@@ -479,9 +518,10 @@ hipError_t launch_bias_update(const int32_t* counts_pre, int n, int T, int k, fl
 }
 
 hipError_t launch_tilemap_split(const int32_t* offsets, int n, int bm, int big_rows,
-                                TileMap small, TileMap big, hipStream_t s) {
+                                TileMap small, TileMap big, CuSplit split, hipStream_t s) {
   ProfScope ps("ffn_tilemap", s);
-  tilemap_split_kernel<<<dim3(1), dim3(1024), 0, s>>>(offsets, n, bm, big_rows, small, big);
+  tilemap_split_kernel<<<dim3(1), dim3(1024), 0, s>>>(offsets, n, bm, big_rows, small, big,
+                                                      split);
   return hipGetLastError();
 }
 

@@ -135,25 +135,43 @@ __global__ __launch_bounds__(NW * 64) void topk_kernel(const TopkArgs p) {
     float wp;
     locate(r, nrow, ob, wp);
     float* lg = p.logits + (long long)r * p.ldl;
+    // Lanes past n load entry 0 (every load stays unconditional, so a row's
+    // loads are all in flight together) and keep 0.
+    int jc[NPL];
+#pragma unroll
+    for (int q = 0; q < NPL; ++q) jc[q] = lane + 64 * q < n ? lane + 64 * q : 0;
 #pragma unroll
     for (int q = 0; q < NPL; ++q) {
-      const int j = lane + 64 * q;
-      const bool ok = j < n;
-      in.c[q] = ok ? lg[j] : 0.f;
-      in.r[q] = (ok && p.noisy) ? lg[n + j] : 0.f;
-      in.z[q] = (ok && p.noisy) ? p.noise[nrow + j] : 0.f;
+      const bool ok = lane + 64 * q < n;
+      const float c = lg[jc[q]];
+      in.c[q] = ok ? c : 0.f;
+      in.r[q] = 0.f;
+      in.z[q] = 0.f;
+    }
+    if (p.noisy) {
+#pragma unroll
+      for (int q = 0; q < NPL; ++q) {
+        const bool ok = lane + 64 * q < n;
+        const float rv = lg[n + jc[q]];
+        const float zv = p.noise[nrow + jc[q]];
+        in.r[q] = ok ? rv : 0.f;
+        in.z[q] = ok ? zv : 0.f;
+      }
     }
     if (p.nsplit > 1) {  // the gate GEMM's K-split partials, added in split order
       for (int sp = 1; sp < p.nsplit; ++sp) {
         const float* part = lg + sp * p.split_stride;
+        float pc[NPL], pr[NPL];
 #pragma unroll
-        for (int q = 0; q < NPL; ++q) {
-          const int j = lane + 64 * q;
-          if (j < n) {
-            in.c[q] += part[j];
-            if (p.noisy) in.r[q] += part[n + j];
-          }
+        for (int q = 0; q < NPL; ++q) pc[q] = part[jc[q]];
+        if (p.noisy) {
+#pragma unroll
+          for (int q = 0; q < NPL; ++q) pr[q] = part[n + jc[q]];
+#pragma unroll
+          for (int q = 0; q < NPL; ++q) in.r[q] += pr[q];
         }
+#pragma unroll
+        for (int q = 0; q < NPL; ++q) in.c[q] += pc[q];
       }
 #pragma unroll
       for (int q = 0; q < NPL; ++q) {

@@ -86,9 +86,14 @@ ggemm_bf16_kernel(const GemmBf16Args p) {
   // workgroups take every wpx-th of them.
   const int nN = (p.N + BN - 1) / BN;
   const int total = *p.tile_count * nN;
+  // Side by side with the 256 x 256-tile GEMM (this kernel on the side
+  // stream): workgroups numbered `used` and up return at once.
+  const int used = gemm_used_grid(p, total);
+  const int bid = (int)blockIdx.x;
+  if (bid >= used) return;
   const int per = (total + kXcds - 1) / kXcds;
-  const int xcd = (int)(blockIdx.x % kXcds), slot = (int)(blockIdx.x / kXcds);
-  const int wpx = (int)(gridDim.x / kXcds);
+  const int xcd = bid % kXcds, slot = bid / kXcds;
+  const int wpx = used / kXcds;
   const int first = xcd * per + slot;
   const int last = min(total, (xcd + 1) * per);
   const int ntiles = first < last ? (last - first + wpx - 1) / wpx : 0;

@@ -101,7 +101,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 ggemm_big_kernel(const GemmBf16Args p) {
   using S = Shape<EPI>;
   using W = WRows<FP8>;
-  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * W::kStage];
   __shared__ int4 meta[kMaxTilesPerWG];  // per tile: expert, first row, end row, first column
   // The kernel keeps its accumulators in the accumulation registers; telling
   // the compiler that it uses them keeps every MFMA in that form.
@@ -112,8 +112,19 @@ ggemm_big_kernel(const GemmBf16Args p) {
   // of an XCD takes item s of each of its chunks.
   const int nN = (p.N + S::kCols - 1) / S::kCols;
   const int total = *p.tile_count * nN;
-  const int xcd = (int)(blockIdx.x % kXcds), slot = (int)(blockIdx.x / kXcds);
-  const int wpx = (int)(gridDim.x / kXcds);
+  // Side by side with the 128-row GEMM (this kernel on the caller's stream,
+  // the other on a side stream): the lowest-numbered workgroups return at
+  // once and the top `used` ones work, renumbered from 0 (on the XCD their
+  // hardware number gives: grid and used are multiples of kXcds).  Measured
+  // on MI355X: with the returning workgroups numbered after the working ones
+  // instead, the kernel on the side stream did not start until this one
+  // ended; the side kernel's own returning workgroups numbered last are
+  // harmless, numbered first they held it back the same way.
+  const int used = gemm_used_grid(p, total);
+  const int bid = (int)blockIdx.x - ((int)gridDim.x - used);
+  if (bid < 0) return;
+  const int xcd = bid % kXcds, slot = bid / kXcds;
+  const int wpx = used / kXcds;
   const int nchunks = (total + wpx - 1) / wpx;
   int ntiles = xcd < nchunks ? (nchunks - xcd + kXcds - 1) / kXcds : 0;
   if (ntiles > 0 && xcd + kXcds * (ntiles - 1) == nchunks - 1 &&
@@ -431,12 +442,7 @@ hipError_t launch_t(const GemmBf16Args& a, hipStream_t s) {
       {"ggemm_big_relu", "ggemm_big_swiglu", "ggemm_big_out"},
       {"ggemm_big_fp8_relu", "ggemm_big_fp8_swiglu", "ggemm_big_fp8_out"}};
   ProfScope ps(a.prof_name ? a.prof_name : kNames[FP8 ? 1 : 0][EPI], s);
-  const void* fn = (const void*)ggemm_big_kernel<EPI, HAS_BIAS, FP8>;
-  hipError_t err =
-      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * W::kStage);
-  if (err != hipSuccess) return err;
-  ggemm_big_kernel<EPI, HAS_BIAS, FP8>
-      <<<dim3((unsigned)grid), dim3(kThreads), 2 * W::kStage, s>>>(a);
+  ggemm_big_kernel<EPI, HAS_BIAS, FP8><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -9,12 +9,56 @@
 
 namespace moe {
 
+constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, one L2 each
+
 // A grouped GEMM's tile map: tile t covers rows [row0[t], min(row0[t] + bm,
 // offsets[expert[t] + 1])) of expert[t]; *count tiles.
 struct TileMap {
   int32_t* expert;
   int32_t* row0;
   int32_t* count;
+};
+
+// The experts split by size run their two grouped GEMMs side by side when
+// the weights are bf16, each on its own share of the compute units: the
+// 256 x 256-tile GEMM of the big experts is bound by the matrix units of the
+// CUs it holds, while the 128-row GEMM of the small ones streams their
+// weights and is bound by HBM on the whole chip, so on fewer CUs it moves
+// more bytes per CU (about 31 against 22 GB/s) and the two overlap.  (With
+// FP8 weights the 128-row GEMM is bound inside the CU -- the same weights
+// per CU-second as bf16 -- and gains nothing; those run one after the
+// other.)  The share is set from the routing on the device, by the kernel
+// that writes the two tile maps, so that both chains take about as long:
+// from the big experts' flops, the small experts' weight and activation
+// bytes, and the rate one CU sustains on each while the other kernel runs
+// (measured on MI355X at d = 7168, h = 2048: 3.86 TFLOP/s and 30.5 GB/s per
+// CU).  A multiple of kXcds in [kXcds, cus - kXcds]; 0 without big experts,
+// every CU without small ones.
+constexpr double kBigFlopsPerCu = 3.86e12;
+constexpr double kSmallBytesPerCu = 30.5e9;
+__host__ __device__ inline int expert_cu_split(int cus, long long big_rows, long long small_experts,
+                                               long long small_rows, int d, int h, int swiglu) {
+  if (big_rows <= 0) return 0;
+  if (small_experts <= 0) return cus;
+  const double mats = swiglu ? 3.0 : 2.0;
+  const double t_big = 2.0 * mats * d * h * (double)big_rows / kBigFlopsPerCu;
+  const double t_small = (mats * d * h * 2.0 * (double)small_experts +
+                          (6.0 * d + 4.0 * h) * (double)small_rows) /
+                         kSmallBytesPerCu;
+  const int units = cus / kXcds;
+  if (units < 2) return cus;
+  int u = (int)(units * t_big / (t_big + t_small) + 0.5);
+  u = u < 1 ? 1 : (u > units - 1 ? units - 1 : u);
+  return u * kXcds;
+}
+
+// Where the tile-map kernels write that share (out == null: no side-by-side
+// run) and what it is computed from.
+struct CuSplit {
+  int32_t* out;  // device int: CUs of the 256 x 256-tile GEMM
+  int cus;       // compute units of the device
+  int d, h;      // model and hidden widths
+  int swiglu;    // 1: W1, W3 and W2 per expert; 0: W1 and W2
 };
 
 // Brackets one kernel launch with HIP events while kernel timing is on
@@ -107,6 +151,12 @@ struct GemmBf16Args {
   int shared;            // 1: the shared expert (only the profiler name differs)
   int fp8;               // 1: B1/B3 are packed E4M3 weights with per-row scales
   const char* prof_name; // profiler name of this launch (null: by epilogue and kind)
+  // Side-by-side run (expert_cu_split): cu_split (device) holds the CUs of
+  // the 256 x 256-tile GEMM; this launch keeps that many workgroups
+  // (cu_big = 1) or num_cus minus that many (cu_big = 0), at least enough
+  // for kMaxTilesPerWG, and the others return at once.  Null: the whole grid.
+  const int32_t* cu_split;
+  int cu_big;
 };
 constexpr int kBf16BM = 128;
 constexpr int kMaxTilesPerWG = 512;  // tiles one persistent workgroup can hold
@@ -186,7 +236,7 @@ hipError_t launch_tilemap(const int32_t* offsets, int n, int bm, int32_t* tile_e
 // The same segments split by size: experts with fewer than big_rows rows in
 // bm-row tiles (small), the others in kBigBM-row tiles (big).
 hipError_t launch_tilemap_split(const int32_t* offsets, int n, int bm, int big_rows,
-                                TileMap small, TileMap big, hipStream_t s);
+                                TileMap small, TileMap big, CuSplit split, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Gate epilogue: noise, KeepTopK, softmax / Switch, importance/load partials.
@@ -324,6 +374,7 @@ struct DispatchArgs {
   // tiles (small map), the others in kBigBM-row tiles (big map).
   int big_rows;
   TileMap small_map, big_map;
+  CuSplit split;  // with big_rows > 0: the side-by-side CU share (split.out may be null)
   // Optional: auxiliary losses from importance / load (load may be null) and
   // the pre-capacity counts (losses == null: none).
   float* losses;

@@ -5,6 +5,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 import sparsely_gated_mixture_amd as moe
@@ -58,6 +59,39 @@ def test_workspace_size_of_presets(name):
     rows = cfg.T * cfg.k
     per = 4 if cfg.expert_dtype == 0 else 2  # x_perm is bf16 for bf16 and FP8 experts
     assert size >= rows * cfg.d_model * (per + 4)
+
+
+def test_expert_cu_split():
+    # The CU share of the 256 x 256-tile GEMM when the experts split by size
+    # run side by side (a scheduling choice; results do not depend on it).
+    fine = PRESETS["fine_swiglu"]
+    n = fine.n_experts
+    counts = np.zeros(n, np.int32)
+    counts[:31] = 30808 // 31          # big experts (>= 128 rows)
+    counts[31:161] = 2000 // 130       # small ones, 15 rows each
+    share = moe.moe_expert_cu_split(fine, counts, 256)
+    assert share == 168                # the balance measured best at this shape
+    assert share % 8 == 0 and 8 <= share <= 248
+    # no big expert: the small-expert GEMM keeps every CU; no small expert:
+    # the big-expert GEMM does
+    assert moe.moe_expert_cu_split(fine, np.full(n, 100, np.int32), 256) == 0
+    assert moe.moe_expert_cu_split(fine, np.where(np.arange(n) < 8, 4096, 0).astype(np.int32),
+                                   256) == 256
+    # more rows on the big experts -> a larger share, never past 248
+    prev = 0
+    for rows in (200, 1000, 4000, 20000, 200000):
+        c = counts.copy()
+        c[:31] = rows
+        cur = moe.moe_expert_cu_split(fine, c, 256)
+        assert prev <= cur <= 248 and cur % 8 == 0
+        prev = cur
+    assert moe.moe_expert_cu_split(fine, np.where(np.arange(n) < 31, 10 ** 6, 1).astype(
+        np.int32), 256) == 248
+    # configs without the size split, FP8 weights (the two GEMMs run one
+    # after the other), and bad arguments
+    assert moe.moe_expert_cu_split(PRESETS["lm_layer"], np.full(256, 128, np.int32), 256) == 0
+    assert moe.moe_expert_cu_split(PRESETS["fine_swiglu_fp8"], counts, 256) == 0
+    assert moe.moe_expert_cu_split(fine, counts, -1) == -1
 
 
 def test_gate_k_splits():

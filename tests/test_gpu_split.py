@@ -25,8 +25,12 @@ def _classes(cfg, counts):
     assert split > 0, "the case must reach the size split"
     small = int(np.sum((counts > 0) & (counts < split)))
     big = int(np.sum(counts >= split))
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    share = moe.moe_expert_cu_split(cfg, np.asarray(counts, np.int32), cus)
     log(f"  split at {split} rows: {small} experts on 128-row tiles, {big} on 256 x 256 "
-        f"(largest {int(counts.max())} rows)")
+        f"(largest {int(counts.max())} rows); side by side on {share} + {cus - share} CUs")
+    if small and big and cfg.expert_dtype != DTYPE_FP8:
+        assert 0 < share < cus
     return split, small, big
 
 
@@ -102,3 +106,89 @@ def test_split_fp8_relu_biases():
     gpu, ref = full_parity(cfg)
     split, small, big = _classes(cfg, gpu["counts"])
     assert small >= 1 and big >= 1
+
+
+@pytest.mark.parametrize("case,counts", [
+    # one big expert beside 31 small ones: the 256 x 256 GEMM gets the least share
+    ("one_big", [130] + [3] * 31),
+    # only big experts: the 128-row GEMM has no tiles, the other every CU
+    ("all_big", [200, 150, 130, 140] + [0] * 28),
+    # only small experts: the 256 x 256 GEMM has no tiles
+    ("all_small", [5] * 20 + [0] * 12),
+    # in between, with empty experts among the small ones
+    ("mixed", [260, 140] + [10, 0] * 15),
+])
+def test_split_side_by_side_shares(case, counts):
+    # moe_expert_ffn on hand-made segments whose CU shares span the range
+    # (8 CUs to every CU for the big-expert GEMM); each expert's rows are
+    # checked against the oracle's expert FFN.
+    cfg = MoEConfig("split_shares", T=1024, d_model=2048, d_hidden=2048, n_experts=32, k=1,
+                    seed=506)
+    counts = np.asarray(counts, np.int32)
+    n, d = cfg.n_experts, cfg.d_model
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    rows = int(offsets[-1])
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    share = moe.moe_expert_cu_split(cfg, counts, cus)
+    log(f"[split shares] {case}: {rows} rows, 256 x 256 GEMM on {share} of {cus} CUs")
+    want = {"one_big": 8, "all_big": cus, "all_small": 0}
+    if case in want:
+        assert share == want[case]
+    else:
+        assert 0 < share < cus
+    inp = dev_inputs(cfg)
+    r = np.random.default_rng(506)
+    x = oracle.bf16_round(r.standard_normal((rows, d)))
+    xp = torch.zeros((cfg.T * cfg.k, d), dtype=torch.bfloat16, device="cuda")
+    xp[:rows] = torch.from_numpy(x).to(torch.bfloat16).to("cuda")
+    yp = torch.full((cfg.T * cfg.k, d), 7.0, dtype=torch.float32, device="cuda")
+    ws = torch.empty(moe.moe_workspace_size(cfg), dtype=torch.uint8, device="cuda")
+    moe.moe_expert_ffn(cfg, xp, torch.from_numpy(offsets).to("cuda"), inp["w1"], None, None,
+                       inp["w2"], None, yp, ws)
+    torch.cuda.synchronize()
+    live = [e for e in range(n) if counts[e] > 0]
+    ew = expert_weights_host(inp, live)
+    w1 = np.zeros((n, cfg.d_hidden, d))
+    w2 = np.zeros((n, d, cfg.d_hidden))
+    for e in live:
+        w1[e], w2[e] = ew["w1"][e], ew["w2"][e]
+    y_ref = oracle.experts_apply(x, np.arange(rows), offsets, w1, w2, bf16=True, experts=live)
+    err = max_abs_norm(yp[:rows].cpu().double().numpy(), y_ref)
+    log(f"  y_perm error {err:.3e}")
+    assert err <= 2e-2
+    assert torch.all(yp[rows:] == 7.0)
+
+
+def test_split_graph_replay_matches_eager():
+    # The forward with the two size classes side by side (a second stream
+    # forked from the caller's and joined back) captured into a HIP graph:
+    # every replay, with eager work and synchronisations in between, equals
+    # the eager result bit for bit.
+    cfg = MoEConfig("split_graph", T=400, d_model=2048, d_hidden=2048, n_experts=6, k=2,
+                    act=ACT_SWIGLU, noisy=False, logit_bias="zipf1.1", seed=507)
+    inp = dev_inputs(cfg)
+    layer = moe.MoELayer(cfg, inp)
+    log("[split] graph replay, T=400, d=h=2048, 6 experts")
+    y_ref, l_ref = layer.forward(inp["x"], inp["noise"])
+    torch.cuda.synchronize()
+    y_ref, l_ref = y_ref.clone(), l_ref.clone()
+    y = torch.empty_like(y_ref)
+    losses = torch.empty_like(l_ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer.forward(inp["x"], inp["noise"], y=y, losses=losses)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward(inp["x"], inp["noise"], y=y, losses=losses)
+    for rep in range(4):
+        y.fill_(float("nan"))
+        losses.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), f"replay {rep}"
+        assert torch.equal(losses, l_ref), f"replay {rep}"
+        y2, _ = layer.forward(inp["x"], inp["noise"])
+        torch.cuda.synchronize()
+        assert torch.equal(y2, y_ref)
