@@ -228,6 +228,8 @@ def kernel_work(name, cfg, rows, nonempty, T):
         return (nparts * n * 4 + n * 4, 0.0, "f32")
     if name == "dispatch_colscan":
         return (((T * k + 255) // 256) * n * 8 + n * 4, 0.0, "i32")
+    if name == "dispatch_scan_finalize":  # the column scan, then the finalize in its last block
+        return (((T * k + 255) // 256) * n * 8 + n * 4 + n * 12, 0.0, "i32")
     if name in ("dispatch_finalize", "dispatch_offsets", "ffn_tilemap", "aux_loss"):
         return (n * 12, 0.0, "i32")
     return (0.0, 0.0, "")

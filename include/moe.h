@@ -176,7 +176,10 @@ int32_t moe_gate_k_splits(const moe_config* cfg);
  * stream of the library's own, beside the big experts' 256 x 256-tile GEMM
  * on the caller's stream, each on its own share of the compute units; the
  * caller's stream waits for both before the combine.  (FP8 weights: one
- * after the other.)  The share is computed on the device from the routing;
+ * after the other.)  Calls on one device from several host threads take
+ * turns on that second stream; a call captured into a graph before any
+ * uncaptured call on its device has created the stream runs the two one
+ * after the other.  The share is computed on the device from the routing;
  * this call computes the same share on the host.
  *   counts: host array [n_experts] of the rows each expert keeps (the
  *           dispatch's counts); cus: compute units of the GPU (0: the

@@ -7,8 +7,9 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
-#include <cstring>
 #include <cstdlib>
+#include <cstring>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "launch.h"
@@ -159,13 +160,25 @@ namespace {
 struct SideStream {
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
+  // Held from the fork to the join, so that calls from several host threads
+  // on one device do not interleave their uses of the shared events (their
+  // side-stream work runs one call after the other).
+  std::mutex m;
 };
-SideStream* side_stream() {
+// The current device's side stream, or null: it is created on first use,
+// but not while `caller` is being captured into a graph (that call then runs
+// the two classes one after the other).
+SideStream* side_stream(hipStream_t caller) {
   static SideStream cache[64];
+  static std::mutex init;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
   SideStream& ss = cache[dev];
+  std::lock_guard<std::mutex> lock(init);
   if (!ss.s) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(caller, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone)
+      return nullptr;
     hipStream_t st = nullptr;
     if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
     if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
@@ -313,7 +326,7 @@ Plan make_plan(const moe_config& c) {
     p.g_slot = g.take(std::max(1LL, T * p.k1) * 4);
     const long long gchunks = (T * p.k1 + kDispatchChunk - 1) / kDispatchChunk;
     p.g_chunk_hist = g.take(std::max(1LL, gchunks) * p.a * 4);
-    p.g_chunk_base = g.take(std::max(1LL, gchunks) * p.a * 4);
+    p.g_chunk_base = g.take((std::max(1LL, gchunks) * p.a + 1) * 4);  // + the scan's ticket
     p.t2_expert = g.take((size_t)p.max_tiles2 * 4);
     p.t2_row0 = g.take((size_t)p.max_tiles2 * 4);
     p.t2_count = g.take(4);
@@ -331,7 +344,7 @@ Plan make_plan(const moe_config& c) {
   Cursor dsp{0};
   p.nchunks = (int)((A + kDispatchChunk - 1) / kDispatchChunk);
   p.chunk_hist = dsp.take(std::max(1LL, (long long)p.nchunks) * n * 4);
-  p.chunk_base = dsp.take(std::max(1LL, (long long)p.nchunks) * n * 4);
+  p.chunk_base = dsp.take((std::max(1LL, (long long)p.nchunks) * n + 1) * 4);  // + the ticket
   p.dispatch_bytes = dsp.at;
   // ffn scratch
   Cursor f{0};
@@ -733,8 +746,10 @@ moe_status run_ffn(const moe_config& c, const Plan& p, const void* x_perm,
     // the big experts' chain on `s`, each kernel on its share of the CUs.
     // FP8 weights (or no side stream): one after the other, each on the
     // whole grid.
-    SideStream* ss = c.expert_dtype == MOE_BF16 ? side_stream() : nullptr;
+    SideStream* ss = c.expert_dtype == MOE_BF16 ? side_stream(s) : nullptr;
+    std::unique_lock<std::mutex> side_lock;
     if (ss) {
+      side_lock = std::unique_lock<std::mutex>(ss->m);
       HIP_TRY(hipEventRecord(ss->fork, s));
       HIP_TRY(hipStreamWaitEvent(ss->s, ss->fork, 0));
     }

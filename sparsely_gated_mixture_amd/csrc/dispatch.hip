@@ -9,12 +9,14 @@
 //      the gate's fixed-order column sums ride in the same launch
 //      (hist_colsum_kernel: the first blocks histogram, the rest sum
 //      columns), which saves a launch on the path.
-//   2. column_scan_kernel: per expert, exclusive prefix over chunks, and the
-//      total count (counts_pre); four threads per expert each walk a quarter
-//      of the chunks, and the quarters are joined in order.
-//   3. finalize_kernel: counts = min(counts_pre, C), exclusive scan ->
-//      offsets; in the layer forward it also writes the grouped GEMM's tile
-//      map and the auxiliary losses (all single-block work, one launch).
+//   2. scan_finalize_kernel, column scan: per expert, exclusive prefix over
+//      chunks, and the total count (counts_pre); four threads per expert
+//      each walk a quarter of the chunks, and the quarters are joined in
+//      order.
+//   3. in the same launch, the finalize, run by the scan block that finishes
+//      last: counts = min(counts_pre, C), exclusive scan -> offsets; in the
+//      layer forward it also writes the grouped GEMMs' tile maps (and the
+//      side-by-side CU share) and the auxiliary losses.
 //   4. permute_kernel: one wavefront walks its chunk in order, 64 slots at a
 //      time; a slot's rank inside its group of 64 is the number of earlier
 //      lanes with the same expert (the lanes holding the same id are found
@@ -49,10 +51,13 @@ __device__ inline void chunk_hist_block(const int32_t* __restrict__ idx, long lo
   for (int e = threadIdx.x; e < n; e += nt) chunk_hist[(long long)c * n + e] = hist[e];
 }
 
+// `done`: the ticket of the scan + finalize launch that follows, set to 0.
 __global__ __launch_bounds__(256) void chunk_hist_kernel(const int32_t* __restrict__ idx,
                                                          long long A, int n,
-                                                         int32_t* __restrict__ chunk_hist) {
+                                                         int32_t* __restrict__ chunk_hist,
+                                                         int32_t* __restrict__ done) {
   extern __shared__ int32_t hist[];
+  if (blockIdx.x == 0 && threadIdx.x == 0) *done = 0;
   chunk_hist_block(idx, A, n, chunk_hist, (int)blockIdx.x, hist);
 }
 
@@ -60,9 +65,10 @@ __global__ __launch_bounds__(256) void chunk_hist_kernel(const int32_t* __restri
 // (b % cx) of the gate's vector b / cx (kColThreads threads either way).
 __global__ __launch_bounds__(kColThreads) void hist_colsum_kernel(
     const int32_t* __restrict__ idx, long long A, int n, int32_t* __restrict__ chunk_hist,
-    int nchunks, const ColsumArgs cs, int nparts, int cx) {
+    int nchunks, const ColsumArgs cs, int nparts, int cx, int32_t* __restrict__ done) {
   extern __shared__ int32_t hist[];
   const int b = (int)blockIdx.x;
+  if (b == 0 && threadIdx.x == 0) *done = 0;
   if (b < nchunks) {
     chunk_hist_block(idx, A, n, chunk_hist, b, hist);
     return;
@@ -70,11 +76,11 @@ __global__ __launch_bounds__(kColThreads) void hist_colsum_kernel(
   colsum_block(cs, nparts, (b - nchunks) % cx, (b - nchunks) / cx);
 }
 
-// 64 experts per block; thread (e, q) covers chunks [q*G, (q+1)*G).
-__global__ __launch_bounds__(256) void column_scan_kernel(const int32_t* __restrict__ chunk_hist,
-                                                          int nchunks, int n,
-                                                          int32_t* __restrict__ chunk_base,
-                                                          int32_t* __restrict__ counts_pre) {
+// 64 experts per block (256 threads); thread (e, q) covers chunks
+// [q*G, (q+1)*G).
+__device__ inline void column_scan_block(const int32_t* __restrict__ chunk_hist, int nchunks,
+                                         int n, int32_t* __restrict__ chunk_base,
+                                         int32_t* __restrict__ counts_pre) {
   __shared__ int32_t qs[4][64];
   const int el = threadIdx.x & 63, q = threadIdx.x >> 6;
   const int e = blockIdx.x * 64 + el;
@@ -100,10 +106,10 @@ __global__ __launch_bounds__(256) void column_scan_kernel(const int32_t* __restr
   }
 }
 
-// Single block of kFinThreads threads; thread t owns the contiguous experts
+// One block of kFinThreads threads; thread t owns the contiguous experts
 // [t*per, t*per + per).
 constexpr int kFinThreads = 256;
-__global__ __launch_bounds__(kFinThreads) void finalize_kernel(const DispatchArgs a) {
+__device__ inline void finalize_block(const DispatchArgs& a) {
   __shared__ int32_t si[kFinThreads / 64];
   __shared__ double sd[kFinThreads / 64];
   const int n = a.n;
@@ -186,6 +192,28 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(const DispatchArg
   if (a.losses)
     block_aux_losses<kFinThreads>(a.importance, a.load, a.counts_pre, a.gate_stats, a.T, a.k, n,
                                   a.w_imp, a.w_load, a.alpha, a.w_z, a.w_ent, a.losses, sd);
+}
+
+// The column scan in blocks of 64 experts; the last block to finish then
+// runs the finalize, so the two take one launch.  "Last" is a ticket on
+// `done` (set to 0 by the histogram launch before): each block makes its
+// counts visible device-wide (a device-scope fence: writeback across the
+// XCDs' L2s), then takes a ticket; the block that draws the last one fences
+// again (invalidating stale lines) and reads every block's counts.  No block
+// waits for another.
+static_assert(kFinThreads == 256, "the scan and the finalize share the 256-thread block");
+__global__ void zero_int_kernel(int32_t* __restrict__ p) { *p = 0; }
+__global__ __launch_bounds__(256) void scan_finalize_kernel(const DispatchArgs a, int nchunks,
+                                                            int32_t* __restrict__ done) {
+  column_scan_block(a.chunk_hist, nchunks, a.n, a.chunk_base, a.counts_pre);
+  __shared__ int last;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) last = atomicAdd(done, 1) == (int)gridDim.x - 1;
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  finalize_block(a);
 }
 
 // One wavefront per chunk.
@@ -440,6 +468,11 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   const int n = a.n;
   const int nchunks = (int)((A + kDispatchChunk - 1) / kDispatchChunk);
   const size_t shm = (size_t)n * sizeof(int32_t);
+  // The scan + finalize launch's ticket: the int after the chunk bases,
+  // zeroed by the histogram launch (or by a one-thread launch when there is
+  // no histogram to take: no assignments and no column sums).
+  int32_t* done = a.chunk_base + (long long)(nchunks > 0 ? nchunks : 1) * n;
+  bool zeroed = false;
   if (a.colsum_fused) {
     ColsumArgs cs;
     int nmax;
@@ -449,28 +482,29 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
     if (blocks > 0) {
       ProfScope ps("dispatch_hist", s);
       hist_colsum_kernel<<<dim3(blocks), dim3(kColThreads), shm, s>>>(
-          a.topk_idx, A, n, a.chunk_hist, nchunks, cs, a.colsum_nparts, cx > 0 ? cx : 1);
+          a.topk_idx, A, n, a.chunk_hist, nchunks, cs, a.colsum_nparts, cx > 0 ? cx : 1, done);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
+      zeroed = true;
     }
   } else if (nchunks > 0) {
     ProfScope ps("dispatch_hist", s);
-    chunk_hist_kernel<<<dim3(nchunks), dim3(256), shm, s>>>(a.topk_idx, A, n, a.chunk_hist);
+    chunk_hist_kernel<<<dim3(nchunks), dim3(256), shm, s>>>(a.topk_idx, A, n, a.chunk_hist,
+                                                             done);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    zeroed = true;
+  }
+  if (!zeroed) {
+    zero_int_kernel<<<dim3(1), dim3(1), 0, s>>>(done);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   {
-    ProfScope ps("dispatch_colscan", s);
-    column_scan_kernel<<<dim3((n + 63) / 64), dim3(256), 0, s>>>(a.chunk_hist, nchunks, n,
-                                                                  a.chunk_base, a.counts_pre);
+    ProfScope ps("dispatch_scan_finalize", s);
+    scan_finalize_kernel<<<dim3((n + 63) / 64), dim3(256), 0, s>>>(a, nchunks, done);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  {
-    ProfScope ps("dispatch_finalize", s);
-    finalize_kernel<<<dim3(1), dim3(kFinThreads), 0, s>>>(a);
-  }
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (nchunks > 0) {
     ProfScope ps("dispatch_permute", s);

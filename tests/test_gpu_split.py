@@ -192,3 +192,42 @@ def test_split_graph_replay_matches_eager():
         y2, _ = layer.forward(inp["x"], inp["noise"])
         torch.cuda.synchronize()
         assert torch.equal(y2, y_ref)
+
+
+def test_split_two_host_threads():
+    # Two host threads, each with its own layer, workspace and stream, run
+    # side-by-side forwards at once (the library's second stream is shared
+    # per device): every result equals the single-threaded one bit for bit.
+    import threading
+    cfg = MoEConfig("split_threads", T=400, d_model=2048, d_hidden=2048, n_experts=6, k=2,
+                    act=ACT_SWIGLU, noisy=False, logit_bias="zipf1.1", seed=508)
+    inp = dev_inputs(cfg)
+    layers = [moe.MoELayer(cfg, inp) for _ in range(2)]
+    log("[split] two host threads, T=400, d=h=2048, 6 experts")
+    y_ref, l_ref = layers[0].forward(inp["x"], inp["noise"])
+    torch.cuda.synchronize()
+    y_ref, l_ref = y_ref.clone(), l_ref.clone()
+    results, errors = [[], []], []
+
+    def run(i):
+        try:
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                for _ in range(6):
+                    y, l = layers[i].forward(inp["x"], inp["noise"])
+                    results[i].append((y.clone(), l.clone()))
+            st.synchronize()
+        except Exception as exc:  # reported below
+            errors.append(exc)
+
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(2):
+        assert len(results[i]) == 6
+        for y, l in results[i]:
+            assert torch.equal(y, y_ref) and torch.equal(l, l_ref)
