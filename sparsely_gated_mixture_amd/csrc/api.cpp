@@ -1637,7 +1637,7 @@ int32_t moe_expert_cu_split(const moe_config* cfg, const int32_t* counts, int32_
   long long br = 0, se = 0, sr = 0;
   for (int e = 0; e < cfg->n_experts; ++e) {
     const int kept = counts[e];
-    if (kept >= big_rows) br += kept;
+    if (kept >= big_rows) br += (kept + kBigBM - 1) / kBigBM * kBigBM;
     else if (kept > 0) ++se, sr += kept;
   }
   if (cfg->expert_dtype != MOE_BF16) return 0;

@@ -177,7 +177,7 @@ __device__ inline void finalize_block(const DispatchArgs& a) {
         int big_r = 0, small_e = 0, small_r = 0;
         for (int e = b; e < e1; ++e) {
           const int kept = a.counts[e];
-          if (kept >= a.big_rows) big_r += kept;
+          if (kept >= a.big_rows) big_r += (kept + kBigBM - 1) / kBigBM * kBigBM;
           else if (kept > 0) ++small_e, small_r += kept;
         }
         const int tb_rows = block_exscan<kFinThreads>(big_r, si).y;
@@ -402,12 +402,12 @@ __global__ __launch_bounds__(1024) void tilemap_split_kernel(const int32_t* __re
     *bg.count = tsum[1][1023];
   }
   if (split.out) {
-    // Rows of the big experts, count and rows of the small ones, summed in
+    // Padded rows of the big experts, count and rows of the small ones, summed in
     // the same shared arrays (every thread has read its prefix above).
     int v[3] = {0, 0, 0};
     for (int i = 0; i < per && b + i < n; ++i) {
       const int rows = offsets[b + i + 1] - offsets[b + i];
-      if (rows >= big_rows) v[0] += rows;
+      if (rows >= big_rows) v[0] += (rows + kBigBM - 1) / kBigBM * kBigBM;
       else if (rows > 0) v[1] += 1, v[2] += rows;
     }
     int tot[3];

@@ -29,19 +29,24 @@ struct TileMap {
 // per CU-second as bf16 -- and gains nothing; those run one after the
 // other.)  The share is set from the routing on the device, by the kernel
 // that writes the two tile maps, so that both chains take about as long:
-// from the big experts' flops, the small experts' weight and activation
-// bytes, and the rate one CU sustains on each while the other kernel runs
-// (measured on MI355X at d = 7168, h = 2048: 3.86 TFLOP/s and 30.5 GB/s per
-// CU).  A multiple of kXcds in [kXcds, cus - kXcds]; 0 without big experts,
-// every CU without small ones.
-constexpr double kBigFlopsPerCu = 3.86e12;
-constexpr double kSmallBytesPerCu = 30.5e9;
-__host__ __device__ inline int expert_cu_split(int cus, long long big_rows, long long small_experts,
-                                               long long small_rows, int d, int h, int swiglu) {
-  if (big_rows <= 0) return 0;
+// from the big experts' flops over their rows padded to whole 256-row tiles
+// (the 256 x 256 kernel's unit of work: an expert of 130 rows costs a whole
+// tile), the small experts' weight and activation bytes, and the rate one CU
+// sustains on each while the other kernel runs (measured on MI355X at d =
+// 7168, h = 2048: 4.1-4.3 TFLOP/s of padded tile work and 27-30 GB/s per CU,
+// over routings with 31 and 77 big experts).  A multiple of kXcds in
+// [kXcds, cus - kXcds]; 0 without big experts, every CU without small ones.
+constexpr double kBigFlopsPerCu = 4.2e12;
+constexpr double kSmallBytesPerCu = 29e9;
+// big_padded_rows: the big experts' rows, each expert's rounded up to a
+// multiple of kBigBM.
+__host__ __device__ inline int expert_cu_split(int cus, long long big_padded_rows,
+                                               long long small_experts, long long small_rows,
+                                               int d, int h, int swiglu) {
+  if (big_padded_rows <= 0) return 0;
   if (small_experts <= 0) return cus;
   const double mats = swiglu ? 3.0 : 2.0;
-  const double t_big = 2.0 * mats * d * h * (double)big_rows / kBigFlopsPerCu;
+  const double t_big = 2.0 * mats * d * h * (double)big_padded_rows / kBigFlopsPerCu;
   const double t_small = (mats * d * h * 2.0 * (double)small_experts +
                           (6.0 * d + 4.0 * h) * (double)small_rows) /
                          kSmallBytesPerCu;
