@@ -211,6 +211,8 @@ def kernel_work(name, cfg, rows, nonempty, T):
         return (T * d * 4 + ncols * d * 4 + T * ncols * 4, 2.0 * T * ncols * d, "f32")
     if name == "gate_topk":
         return (T * ncols * 4 + (T * ng * 4 if noisy else 0) + T * k * 8, 0.0, "f32")
+    if name == "dispatch_gather_bf16":  # x once in token order (experts read rows via perm)
+        return (T * d * 4 + T * d * 2, 0.0, "f32")
     if name == "dispatch_gather":
         return (T * d * 4 + rows * d * wsz + rows * 4 + (T * d * 2 if hs else 0), 0.0, "f32")
     if name == "combine":

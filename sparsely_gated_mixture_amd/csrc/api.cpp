@@ -634,7 +634,10 @@ struct ForwardExtras {
   const float* importance = nullptr;
   const float* load = nullptr;
   const float* gate_stats = nullptr;
-  uint16_t* x_bf16 = nullptr;  // the shared expert's input, written by the gather
+  uint16_t* x_bf16 = nullptr;  // x in bf16, token order, written by the gather
+  // Non-null: GEMM 1 reads merged row r as row row_token[r] (= perm) of the
+  // token-order x_bf16, and the gather writes no x_perm.
+  const int32_t* row_token = nullptr;
   // The gate's column sums, deferred into the histogram launch (run_gate's
   // `defer`), when colsum_fused.
   ColsumVec colsum[3] = {};
@@ -688,6 +691,15 @@ moe_status run_dispatch(const moe_config& c, const Plan& p, const int32_t* topk_
   return MOE_OK;
 }
 
+// GEMM 1 of the layer forward reading its rows through perm (`x_perm` is then
+// the token-order bf16 x).
+void set_row_token(GemmBf16Args& g, const moe_config& c, const ForwardExtras* fx) {
+  if (!fx || !fx->row_token) return;
+  g.row_token = fx->row_token;
+  g.row_token_n = (int)((long long)c.T * c.k);
+  g.a_rows = c.T;
+}
+
 // `fx` (layer forward) carries a tile map the dispatch already wrote;
 // otherwise the tile map is built here from `offsets`.
 moe_status run_ffn(const moe_config& c, const Plan& p, const void* x_perm,
@@ -730,7 +742,9 @@ moe_status run_ffn(const moe_config& c, const Plan& p, const void* x_perm,
     g.bias = b1;
     g.offsets = offsets;
     g.num_cus = device_cus();
+    set_row_token(g, c, fx);
     GemmBf16Args g2 = g;
+    g2.row_token = nullptr;
     g2.A = (const uint16_t*)hidden;
     g2.lda = h;
     g2.B1 = w2;
@@ -799,8 +813,10 @@ moe_status run_ffn(const moe_config& c, const Plan& p, const void* x_perm,
     g.tile_count = tc;
     g.max_mtiles = p.max_mtiles;
     g.num_cus = device_cus();
+    set_row_token(g, c, fx);
     HIP_TRY(launch_gemm_bf16(g, c.act == MOE_ACT_SWIGLU ? EPI_SWIGLU_BF16 : EPI_RELU_BF16, s));
     GemmBf16Args g2 = g;
+    g2.row_token = nullptr;
     g2.A = (const uint16_t*)hidden;
     g2.lda = h;
     g2.B1 = w2;
@@ -1888,8 +1904,19 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const float
   fx.load = has_load ? ld : nullptr;
   fx.gate_stats = stats;
   fx.x_bf16 = shared ? at<uint16_t>(ws, p.sh_xb) : nullptr;
-  CHECK(run_dispatch(c, p, idx, x, counts_pre, counts, offsets, perm, slot, xperm, ws, s, &fx));
-  CHECK(run_ffn(c, p, xperm, offsets, wt->w1, wt->b1, wt->w3, wt->w2, wt->b2, yperm, ws, s, &fx));
+  // bf16 and FP8 experts: the gather writes x once in token order as bf16
+  // (into the x_perm region unless the shared expert's copy exists) and GEMM 1
+  // reads each merged row through perm, instead of k copies of every row.
+  const bool via_perm =
+      c.expert_dtype != MOE_F32 && (long long)c.T * c.d_model * 2 <= (1LL << 30);
+  if (via_perm) {
+    fx.row_token = perm;
+    if (!fx.x_bf16) fx.x_bf16 = (uint16_t*)xperm;
+  }
+  CHECK(run_dispatch(c, p, idx, x, counts_pre, counts, offsets, perm, slot,
+                     via_perm ? nullptr : xperm, ws, s, &fx));
+  CHECK(run_ffn(c, p, via_perm ? (const void*)fx.x_bf16 : xperm, offsets, wt->w1, wt->b1, wt->w3,
+                wt->w2, wt->b2, yperm, ws, s, &fx));
   float* ysh = shared ? at<float>(ws, p.sh_y) : nullptr;
   if (shared) CHECK(run_shared_ffn(c, p, fx.x_bf16, wt->ws1, wt->ws3, wt->ws2, ysh, ws, s));
   HIP_TRY(launch_combine(yperm, slot, w, ysh, c.T, c.k, c.d_model, y, s));

@@ -14,6 +14,26 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;   // CDNA wavefront width
 
+// Token of merged rows base .. base + 7 for the lane's group of 8 (lane / 8),
+// base wave-uniform: eight scalar loads (through the constant address space,
+// so they count on lgkmcnt and leave the vector-memory count of the copies
+// alone), each index clamped to [0, n - 1], then the lane's pick.
+__device__ __forceinline__ int row_token8(const int32_t* perm, int base, int n, int lane) {
+  typedef __attribute__((address_space(4))) const int32_t cint;
+  cint* q = (cint*)perm;
+  int v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = base + i;
+    v[i] = q[r < n ? r : n - 1];
+  }
+  const int g = lane >> 3;
+  int t = v[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) t = g == i ? v[i] : t;
+  return t;
+}
+
 // Workgroups a persistent grouped GEMM puts to work on `total` items: the
 // whole grid, or its share of a side-by-side run (cu_split), raised until no
 // workgroup holds more than kMaxTilesPerWG items (one holds at most

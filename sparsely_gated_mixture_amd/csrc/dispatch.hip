@@ -23,7 +23,9 @@
 //      with one ballot per bit of the expert id), so the resulting order is
 //      exactly (token, slot) order -- stable, and independent of scheduling.
 //   5. gather_kernel: one wavefront per token reads its row once and writes
-//      it to each kept slot's row, converted to bf16 (RNE) or copied as fp32.
+//      it to each kept slot's row, converted to bf16 (RNE) or copied as fp32,
+//      and/or once in token order as bf16 (the layer forward's bf16 experts
+//      then read their rows through perm and no slot rows are written).
 #include <algorithm>
 
 #include "colsum.h"
@@ -296,7 +298,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const float* __restrict__ x
       pk.w = bf16x2_bits(v1[2], v1[3]);
     }
     if (x_bf16) *(uint4*)(x_bf16 + (long long)t * d + c) = pk;
-    for (int s = 0; s < k; ++s) {
+    for (int s = 0; out && s < k; ++s) {
       const int row = sp[s];
       if (row < 0) continue;
       if (bf16_out) {
@@ -519,7 +521,7 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
 hipError_t launch_gather(const float* x, const int32_t* slot_pos, int T, int k, int d,
                          int bf16_out, void* x_perm, uint16_t* x_bf16, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  ProfScope ps("dispatch_gather", s);
+  ProfScope ps(x_perm ? "dispatch_gather" : "dispatch_gather_bf16", s);
   gather_kernel<<<dim3((T + 3) / 4), dim3(256), 0, s>>>(x, slot_pos, T, k, d, bf16_out, x_perm,
                                                         x_bf16);
   return hipGetLastError();

@@ -131,12 +131,18 @@ ggemm_bf16_kernel(const GemmBf16Args p) {
     // Row groups (8 rows per copy) past the segment's end are not copied:
     // their LDS rows only ever feed output columns that are not stored.
     a_live = 0;
+    const int ty = __builtin_amdgcn_readfirstlane(m.y), tz = __builtin_amdgcn_readfirstlane(m.z);
 #pragma unroll
     for (int j = 0; j < ADMA; ++j) {
       const int r = (wave + kWaves * j) * 8 + (lane >> 3);
       a_live += m.y + (wave + kWaves * j) * 8 < m.z ? 1 : 0;
       a_chunk[j] = ((lane & 7) ^ ((r >> 1) & 7)) * 8;
-      a_src[j] = (const uint8_t*)(p.A + (long long)min(m.y + r, m.z - 1) * p.lda + a_chunk[j]);
+      // the merged row (rows past the segment repeat its last one), or its token
+      long long arow = min(m.y + r, m.z - 1);
+      if (p.row_token)
+        arow = row_token8(p.row_token, ty + (wave + kWaves * j) * 8,
+                          min(tz, p.row_token_n), lane);
+      a_src[j] = (const uint8_t*)(p.A + arow * p.lda + a_chunk[j]);
     }
 #pragma unroll
     for (int j = 0; j < BDMA; ++j) {

@@ -176,6 +176,10 @@ ggemm_big_kernel(const GemmBf16Args p) {
     woff0 = lrow * (int)wrow + lchunk * 16;
   }
   rsrc_t xr, wr1, wr3;
+  // Byte offset of this lane's row in activation copy q: its row within the
+  // tile's descriptor, or (rows through the permutation) its token's row in
+  // the whole of A, past the descriptor for rows past the segment.
+  int xo[8];
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   int ct = 0, ck = 0;  // the cursor: tile, K-step
   auto set_tile = [&](int ti) {
@@ -184,7 +188,20 @@ ggemm_big_kernel(const GemmBf16Args p) {
     const int row0 = __builtin_amdgcn_readfirstlane(m.y);
     const int end = __builtin_amdgcn_readfirstlane(m.z);
     const int col0 = __builtin_amdgcn_readfirstlane(m.w);
-    xr = buffer_rsrc(p.A + (long long)row0 * p.lda, (long long)min(kBM, end - row0) * xrowb);
+    if (p.row_token) {
+      xr = buffer_rsrc(p.A, (long long)p.a_rows * xrowb);
+      const int n = min(end, p.row_token_n);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int base = row0 + 32 * q + 8 * wave;
+        const int tok = row_token8(p.row_token, base, n, lane);
+        xo[q] = base + (lane >> 3) < end ? tok * (int)xrowb + lchunk * 16 : kOutOfRange;
+      }
+    } else {
+      xr = buffer_rsrc(p.A + (long long)row0 * p.lda, (long long)min(kBM, end - row0) * xrowb);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) xo[q] = xoff0 + q * 32 * (int)xrowb;
+    }
     const int wlive = min(S::kCols, p.N - col0);
     // bf16: rows [col0, col0 + wlive); FP8: the row pairs holding them (col0 is even)
     const long long wbase = FP8 ? (long long)(col0 >> 1) * wrow : (long long)col0 * wrow;
@@ -218,7 +235,7 @@ ggemm_big_kernel(const GemmBf16Args p) {
     const int koff = ck * 128;
     const int oor = ck * kBK + lchunk * 8 < K ? 0 : kOutOfRange;
     if (q < 8) {
-      bdma16(xr, xoff0 + q * 32 * (int)xrowb + oor, koff, sb + q * 4096);
+      bdma16(xr, (int)((uint32_t)xo[q] + (uint32_t)oor), koff, sb + q * 4096);
     } else {
       const int j = q - 8;
       const int blk = FP8 ? 2 * j + (wave >> 1) : j;  // 32-row weight block
@@ -431,6 +448,8 @@ hipError_t launch_t(const GemmBf16Args& a, hipStream_t s) {
   using S = Shape<EPI>;
   using W = WRows<FP8>;
   if (FP8 && a.K % kBK) return hipErrorInvalidValue;  // FP8 codes come in 64-wide K blocks
+  // rows through the permutation: 32-bit byte offsets into the whole of A
+  if (a.row_token && (long long)a.a_rows * a.lda * 2 > (1LL << 30)) return hipErrorInvalidValue;
   const int nN = (a.N + S::kCols - 1) / S::kCols;
   const long long max_total = (long long)a.max_mtiles * nN;
   if (max_total <= 0) return hipSuccess;

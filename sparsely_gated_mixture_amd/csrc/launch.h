@@ -162,6 +162,14 @@ struct GemmBf16Args {
   // for kMaxTilesPerWG, and the others return at once.  Null: the whole grid.
   const int32_t* cu_split;
   int cu_big;
+  // Activation rows through the permutation (null: A holds the merged rows
+  // themselves): merged row r is row row_token[r] of A = [a_rows, K] bf16,
+  // for r < row_token_n (the layer forward's token-order bf16 copy of x and
+  // its perm); the copies look each row up with scalar loads when a tile
+  // starts.
+  const int32_t* row_token;
+  int row_token_n;
+  int a_rows;
 };
 constexpr int kBf16BM = 128;
 constexpr int kMaxTilesPerWG = 512;  // tiles one persistent workgroup can hold
