@@ -123,7 +123,8 @@ def launch_experts(name, cfg, counts):
 
 def side_by_side(cfg, counts, kernels):
     """The two expert GEMM classes run side by side on shares of the CUs
-    (moe_expert_cu_split): each such kernel entry gets its CU count, the
+    (moe_expert_cu_split, one share per product): each such kernel entry
+    gets its CU count, the
     256 x 256 kernels their rate against their share of the matrix-unit
     peak, and the result describes each phase (first GEMM, second GEMM) as a
     whole: both kernels' algorithmic bytes and flops over the longer of the
@@ -131,16 +132,19 @@ def side_by_side(cfg, counts, kernels):
     other."""
     import sparsely_gated_mixture_amd as moe
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    share = moe.moe_expert_cu_split(cfg, np.asarray(counts, np.int32), cus)
-    if not 0 < share < cus:
+    shares = [moe.moe_expert_cu_split(cfg, np.asarray(counts, np.int32), cus, prod)
+              for prod in (0, 1)]
+    if not all(0 < s < cus for s in shares):
         return None
-    out = {"cus_total": cus, "cus_big": share, "cus_small": cus - share, "phases": []}
-    for big_name, small_name in (("ggemm_big_swiglu", "ggemm_bf16_swiglu"),
-                                 ("ggemm_big_relu", "ggemm_bf16_relu"),
-                                 ("ggemm_big_out", "ggemm_bf16_out")):
+    out = {"cus_total": cus, "cus_big": shares, "cus_small": [cus - s for s in shares],
+           "phases": []}
+    for big_name, small_name, prod in (("ggemm_big_swiglu", "ggemm_bf16_swiglu", 0),
+                                       ("ggemm_big_relu", "ggemm_bf16_relu", 0),
+                                       ("ggemm_big_out", "ggemm_bf16_out", 1)):
         b, sm = kernels.get(big_name), kernels.get(small_name)
         if not b or not sm:
             continue
+        share = shares[prod]
         b["cus"], sm["cus"] = share, cus - share
         rl = b.get("roofline")
         if rl and rl["bound"] == "mfma":

@@ -179,8 +179,8 @@ int32_t moe_gate_k_splits(const moe_config* cfg);
  * after the other.)  Calls on one device from several host threads take
  * turns on that second stream; a call captured into a graph before any
  * uncaptured call on its device has created the stream runs the two one
- * after the other.  The share is computed on the device from the routing;
- * this call computes the same share on the host.
+ * after the other.  The shares are computed on the device from the
+ * routing; this call computes the same share on the host.
  *   counts: host array [n_experts] of the rows each expert keeps (the
  *           dispatch's counts); cus: compute units of the GPU (0: the
  *           current device's).
@@ -188,9 +188,13 @@ int32_t moe_gate_k_splits(const moe_config* cfg);
  * gets the rest): 0 without experts of at least moe_expert_split_rows rows,
  * without the split or with FP8 weights, every CU without smaller non-empty
  * experts, else a
- * multiple of 8 (the XCD count) in [8, cus - 8].  -1 on an invalid config,
- * null counts or cus < 0.  The results of the layer do not depend on it. */
-int32_t moe_expert_cu_split(const moe_config* cfg, const int32_t* counts, int32_t cus);
+ * multiple of 8 (the XCD count) in [8, cus - 8].  Each product has its own
+ * share (product 0: x W1^T, with x W3^T for SwiGLU; 1: hidden W2^T): the
+ * 256 x 256 GEMM runs at another rate per CU on K = d_model than on K =
+ * d_hidden.  -1 on an invalid config, null counts, cus < 0 or a product
+ * other than 0 and 1.  The results of the layer do not depend on it. */
+int32_t moe_expert_cu_split(const moe_config* cfg, const int32_t* counts, int32_t cus,
+                            int32_t product);
 
 /* Flat gating network: logits, noise, KeepTopK, softmax, and the two
  * auxiliary-loss vectors.

@@ -94,7 +94,7 @@ def load_library():
     L.moe_expert_split_rows.restype = ctypes.c_int32
     L.moe_gate_k_splits.argtypes = [cfgp]
     L.moe_gate_k_splits.restype = ctypes.c_int32
-    L.moe_expert_cu_split.argtypes = [cfgp, P, i32]
+    L.moe_expert_cu_split.argtypes = [cfgp, P, i32, i32]
     L.moe_expert_cu_split.restype = ctypes.c_int32
     L.moe_fp8_weight_bytes.argtypes = [i32, i32, i32]
     L.moe_fp8_weight_bytes.restype = S
@@ -213,12 +213,14 @@ def moe_gate_k_splits(cfg) -> int:
     return int(load_library().moe_gate_k_splits(ctypes.byref(c)))
 
 
-def moe_expert_cu_split(cfg, counts, cus: int = 0) -> int:
-    """counts: host int32 array (numpy or CPU tensor) of n_experts kept rows."""
+def moe_expert_cu_split(cfg, counts, cus: int = 0, product: int = 0) -> int:
+    """counts: host int32 array (numpy or CPU tensor) of n_experts kept rows;
+    product: 0 the first expert product, 1 the second."""
     import numpy as np
     c = make_config(cfg)
     a = np.ascontiguousarray(np.asarray(counts, dtype=np.int32))
-    return int(load_library().moe_expert_cu_split(ctypes.byref(c), a.ctypes.data, int(cus)))
+    return int(load_library().moe_expert_cu_split(ctypes.byref(c), a.ctypes.data, int(cus),
+                                                  int(product)))
 
 
 def moe_pack_fp8_weights(n_experts, N, K, src_dtype, src, dst, stream=None):

@@ -363,7 +363,7 @@ Plan make_plan(const moe_config& c) {
     p.tb_expert = f.take((size_t)p.max_mtiles_b * 4);
     p.tb_row0 = f.take((size_t)p.max_mtiles_b * 4);
     p.tb_count = f.take(4);
-    p.t_split = f.take(4);
+    p.t_split = f.take(2 * 4);  // one share per product
   }
   p.hidden = f.take(std::max(1LL, A) * h * (c.expert_dtype != MOE_F32 ? 2 : 4));
   p.ffn_bytes = f.at;
@@ -393,7 +393,7 @@ Plan make_plan(const moe_config& c) {
     p.f_tb_expert = w.take((size_t)p.max_mtiles_b * 4);
     p.f_tb_row0 = w.take((size_t)p.max_mtiles_b * 4);
     p.f_tb_count = w.take(4);
-    p.f_split = w.take(4);
+    p.f_split = w.take(2 * 4);
   }
   if (c.d_hidden_shared > 0) {
     const long long hs = c.d_hidden_shared;
@@ -767,22 +767,24 @@ moe_status run_ffn(const moe_config& c, const Plan& p, const void* x_perm,
       HIP_TRY(hipEventRecord(ss->fork, s));
       HIP_TRY(hipStreamWaitEvent(ss->s, ss->fork, 0));
     }
-    for (GemmBf16Args* a : {&g, &g2}) {
+    for (int prod = 0; prod < 2; ++prod) {
+      const GemmBf16Args* a = prod == 0 ? &g : &g2;
       GemmBf16Args as = *a, ab = *a;
       as.tile_expert = sm.expert;
       as.tile_row0 = sm.row0;
       as.tile_count = sm.count;
       as.max_mtiles = p.max_mtiles_s;
+      as.b_stream = 1;  // the small map's experts hold fewer rows than one M-tile
       ab.tile_expert = bg.expert;
       ab.tile_row0 = bg.row0;
       ab.tile_count = bg.count;
       ab.max_mtiles = p.max_mtiles_b;
       if (ss) {
-        as.cu_split = ab.cu_split = share;
+        as.cu_split = ab.cu_split = share + prod;
         as.cu_big = 0;
         ab.cu_big = 1;
       }
-      const int epi = a == &g ? epi1 : EPI_IDENT_F32;
+      const int epi = prod == 0 ? epi1 : EPI_IDENT_F32;
       HIP_TRY(launch_gemm_bf16(as, epi, ss ? ss->s : s));
       HIP_TRY(launch_gemm_big(ab, epi, s));
     }
@@ -1646,8 +1648,9 @@ int32_t moe_gate_k_splits(const moe_config* cfg) {
   return make_plan(*cfg).gate_splits;
 }
 
-int32_t moe_expert_cu_split(const moe_config* cfg, const int32_t* counts, int32_t cus) {
-  if (validate(cfg) != MOE_OK || !counts || cus < 0) return -1;
+int32_t moe_expert_cu_split(const moe_config* cfg, const int32_t* counts, int32_t cus,
+                            int32_t product) {
+  if (validate(cfg) != MOE_OK || !counts || cus < 0 || (product != 0 && product != 1)) return -1;
   const int big_rows = split_rows(*cfg);
   if (big_rows <= 0) return 0;
   long long br = 0, se = 0, sr = 0;
@@ -1658,7 +1661,7 @@ int32_t moe_expert_cu_split(const moe_config* cfg, const int32_t* counts, int32_
   }
   if (cfg->expert_dtype != MOE_BF16) return 0;
   const CuSplit sp = cu_split_of(*cfg, nullptr);
-  return expert_cu_split(cus > 0 ? cus : sp.cus, br, se, sr, sp.d, sp.h, sp.swiglu);
+  return expert_cu_split(cus > 0 ? cus : sp.cus, br, se, sr, sp.d, sp.h, sp.swiglu, product);
 }
 
 }  // extern "C"

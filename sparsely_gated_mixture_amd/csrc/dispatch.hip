@@ -185,9 +185,10 @@ __device__ inline void finalize_block(const DispatchArgs& a) {
         const int tb_rows = block_exscan<kFinThreads>(big_r, si).y;
         const int ts_exp = block_exscan<kFinThreads>(small_e, si).y;
         const int ts_rows = block_exscan<kFinThreads>(small_r, si).y;
-        if (threadIdx.x == 0)
-          *a.split.out = expert_cu_split(a.split.cus, tb_rows, ts_exp, ts_rows, a.split.d,
-                                         a.split.h, a.split.swiglu);
+        if (threadIdx.x < 2)
+          a.split.out[threadIdx.x] = expert_cu_split(a.split.cus, tb_rows, ts_exp, ts_rows,
+                                                     a.split.d, a.split.h, a.split.swiglu,
+                                                     (int)threadIdx.x);
       }
     }
   }
@@ -423,9 +424,9 @@ __global__ __launch_bounds__(1024) void tilemap_split_kernel(const int32_t* __re
       }
       tot[q] = tsum[0][0];
     }
-    if (threadIdx.x == 0)
-      *split.out = expert_cu_split(split.cus, tot[0], tot[1], tot[2], split.d, split.h,
-                                   split.swiglu);
+    if (threadIdx.x < 2)
+      split.out[threadIdx.x] = expert_cu_split(split.cus, tot[0], tot[1], tot[2], split.d,
+                                               split.h, split.swiglu, (int)threadIdx.x);
   }
 }
 

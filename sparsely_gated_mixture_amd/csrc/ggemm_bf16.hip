@@ -174,9 +174,15 @@ ggemm_bf16_kernel(const GemmBf16Args p) {
 #pragma unroll
       for (int j = 0; j < ADMA; ++j)
         if (j < a_live) dma16(a_src[j] + adv, sb + (wave + kWaves * j) * 1024);
+      if (p.b_stream) {
 #pragma unroll
-      for (int j = 0; j < BDMA; ++j)
-        dma16(b_src[j] + adv, sb + A_BYTES + (wave + kWaves * j) * 1024);
+        for (int j = 0; j < BDMA; ++j)
+          dma16_stream(b_src[j] + adv, sb + A_BYTES + (wave + kWaves * j) * 1024);
+      } else {
+#pragma unroll
+        for (int j = 0; j < BDMA; ++j)
+          dma16(b_src[j] + adv, sb + A_BYTES + (wave + kWaves * j) * 1024);
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < ADMA; ++j)
@@ -184,9 +190,14 @@ ggemm_bf16_kernel(const GemmBf16Args p) {
           dma16(k0 + a_chunk[j] < K ? (const void*)(a_src[j] + adv) : (const void*)kZeroChunk,
                 sb + (wave + kWaves * j) * 1024);
 #pragma unroll
-      for (int j = 0; j < BDMA; ++j)
-        dma16(k0 + b_chunk[j] < K ? (const void*)(b_src[j] + adv) : (const void*)kZeroChunk,
-              sb + A_BYTES + (wave + kWaves * j) * 1024);
+      for (int j = 0; j < BDMA; ++j) {
+        const void* src =
+            k0 + b_chunk[j] < K ? (const void*)(b_src[j] + adv) : (const void*)kZeroChunk;
+        if (p.b_stream)
+          dma16_stream(src, sb + A_BYTES + (wave + kWaves * j) * 1024);
+        else
+          dma16(src, sb + A_BYTES + (wave + kWaves * j) * 1024);
+      }
     }
     cnt_prev = cnt_last;
     cnt_last = a_live + BDMA;

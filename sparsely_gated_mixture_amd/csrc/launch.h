@@ -24,32 +24,38 @@ struct TileMap {
 // 256 x 256-tile GEMM of the big experts is bound by the matrix units of the
 // CUs it holds, while the 128-row GEMM of the small ones streams their
 // weights and is bound by HBM on the whole chip, so on fewer CUs it moves
-// more bytes per CU (about 31 against 22 GB/s) and the two overlap.  (With
+// more bytes per CU (about 30 against 22 GB/s) and the two overlap.  (With
 // FP8 weights the 128-row GEMM is bound inside the CU -- the same weights
 // per CU-second as bf16 -- and gains nothing; those run one after the
-// other.)  The share is set from the routing on the device, by the kernel
-// that writes the two tile maps, so that both chains take about as long:
-// from the big experts' flops over their rows padded to whole 256-row tiles
-// (the 256 x 256 kernel's unit of work: an expert of 130 rows costs a whole
-// tile), the small experts' weight and activation bytes, and the rate one CU
-// sustains on each while the other kernel runs (measured on MI355X at d =
-// 7168, h = 2048: 4.1-4.3 TFLOP/s of padded tile work and 27-30 GB/s per CU,
-// over routings with 31 and 77 big experts).  A multiple of kXcds in
-// [kXcds, cus - kXcds]; 0 without big experts, every CU without small ones.
-constexpr double kBigFlopsPerCu = 4.2e12;
-constexpr double kSmallBytesPerCu = 29e9;
+// other.)  The shares are set from the routing on the device, by the kernel
+// that writes the two tile maps, one for each product (first: x W1^T and
+// x W3^T; second: hidden W2^T), so that both chains of a product take about
+// as long: from the big experts' flops over their rows padded to whole
+// 256-row tiles (the 256 x 256 kernel's unit of work: an expert of 130 rows
+// costs a whole tile), the small experts' weight and activation bytes, and
+// the rate one CU sustains on each while the other kernel runs (measured on
+// MI355X at d = 7168, h = 2048: 4.9 and 4.35 TFLOP/s of padded tile work in
+// the first and second product -- K = 7168 against 2048 per tile -- and 30
+// GB/s per CU).  A multiple of kXcds in [kXcds, cus - kXcds]; 0 without big
+// experts, every CU without small ones.
+constexpr double kBigFlopsPerCu0 = 4.9e12;   // first product
+constexpr double kBigFlopsPerCu1 = 4.35e12;  // second product
+constexpr double kSmallBytesPerCu = 30e9;
 // big_padded_rows: the big experts' rows, each expert's rounded up to a
-// multiple of kBigBM.
+// multiple of kBigBM.  product: 0 first, 1 second.
 __host__ __device__ inline int expert_cu_split(int cus, long long big_padded_rows,
                                                long long small_experts, long long small_rows,
-                                               int d, int h, int swiglu) {
+                                               int d, int h, int swiglu, int product) {
   if (big_padded_rows <= 0) return 0;
   if (small_experts <= 0) return cus;
-  const double mats = swiglu ? 3.0 : 2.0;
-  const double t_big = 2.0 * mats * d * h * (double)big_padded_rows / kBigFlopsPerCu;
-  const double t_small = (mats * d * h * 2.0 * (double)small_experts +
-                          (6.0 * d + 4.0 * h) * (double)small_rows) /
-                         kSmallBytesPerCu;
+  // weight matrices of the product (each d x h) and activation bytes per row
+  const double mats = product == 0 && swiglu ? 2.0 : 1.0;
+  const double row_bytes = product == 0 ? 2.0 * d + 2.0 * h : 2.0 * h + 4.0 * d;
+  const double t_big = 2.0 * mats * d * h * (double)big_padded_rows /
+                       (product == 0 ? kBigFlopsPerCu0 : kBigFlopsPerCu1);
+  const double t_small =
+      (mats * d * h * 2.0 * (double)small_experts + row_bytes * (double)small_rows) /
+      kSmallBytesPerCu;
   const int units = cus / kXcds;
   if (units < 2) return cus;
   int u = (int)(units * t_big / (t_big + t_small) + 0.5);
@@ -60,7 +66,7 @@ __host__ __device__ inline int expert_cu_split(int cus, long long big_padded_row
 // Where the tile-map kernels write that share (out == null: no side-by-side
 // run) and what it is computed from.
 struct CuSplit {
-  int32_t* out;  // device int: CUs of the 256 x 256-tile GEMM
+  int32_t* out;  // device int[2]: CUs of the 256 x 256-tile GEMM in each product
   int cus;       // compute units of the device
   int d, h;      // model and hidden widths
   int swiglu;    // 1: W1, W3 and W2 per expert; 0: W1 and W2
@@ -157,7 +163,7 @@ struct GemmBf16Args {
   int fp8;               // 1: B1/B3 are packed E4M3 weights with per-row scales
   const char* prof_name; // profiler name of this launch (null: by epilogue and kind)
   // Side-by-side run (expert_cu_split): cu_split (device) holds the CUs of
-  // the 256 x 256-tile GEMM; this launch keeps that many workgroups
+  // the 256 x 256-tile GEMM in this product; this launch keeps that many workgroups
   // (cu_big = 1) or num_cus minus that many (cu_big = 0), at least enough
   // for kMaxTilesPerWG, and the others return at once.  Null: the whole grid.
   const int32_t* cu_split;
@@ -170,6 +176,10 @@ struct GemmBf16Args {
   const int32_t* row_token;
   int row_token_n;
   int a_rows;
+  // Nonzero: each weight tile is read by one work item only (every expert
+  // holds one M-tile), so the 128-row kernel copies weights with the
+  // non-temporal hint.
+  int b_stream;
 };
 constexpr int kBf16BM = 128;
 constexpr int kMaxTilesPerWG = 512;  // tiles one persistent workgroup can hold

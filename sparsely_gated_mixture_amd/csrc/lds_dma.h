@@ -38,6 +38,21 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
 #pragma clang diagnostic pop
 }
 
+// dma16 with the non-temporal hint, for lines that no other copy will ask
+// for again (a small expert's weight tile): they then do not push reusable
+// lines out of L2.
+__device__ __forceinline__ void dma16_stream(const void* g, uint32_t lds) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off nt" ::"v"(g),
+      "s"(lds)
+      : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
 // 16-byte buffer -> LDS copy through a buffer descriptor (raw addressing
 // with the descriptor's range check: an offset past its range copies zeros
 // and touches no memory).  voff is the lane's byte offset, soff a

@@ -70,14 +70,22 @@ def test_expert_cu_split():
     counts[:31] = 30808 // 31          # big experts (>= 128 rows)
     counts[31:161] = 2000 // 130       # small ones, 15 rows each
     share = moe.moe_expert_cu_split(fine, counts, 256)
-    # 31 x 1024 padded rows of 2.2e10 flops each at 4.2 TFLOP/s per CU against
-    # 130 x 88 MB of weights at 29 GB/s per CU: 20 of 32 XCD rows
-    assert share == 160
+    # First product: 31 x 1024 padded rows of 5.9e10 flops each (x W1^T and
+    # x W3^T) at 4.9 TFLOP/s per CU against 130 x 58.7 MB of W1 | W3 at 30
+    # GB/s per CU: 19 of 32 XCD rows.  Second product: 2.9e10 flops per row
+    # at 4.35 TFLOP/s against 130 x 29.4 MB of W2: 20 of 32.
+    assert share == 152
+    assert moe.moe_expert_cu_split(fine, counts, 256, 1) == 160
     assert share % 8 == 0 and 8 <= share <= 248
+    # product 0 or 1 only
+    assert moe.moe_expert_cu_split(fine, counts, 256, 2) == -1
+    assert moe.moe_expert_cu_split(fine, counts, 256, -1) == -1
     # the big experts count by whole 256-row tiles: 129 rows cost what 256 do
     c129, c256 = counts.copy(), counts.copy()
     c129[:31], c256[:31] = 129, 256
-    assert moe.moe_expert_cu_split(fine, c129, 256) == moe.moe_expert_cu_split(fine, c256, 256)
+    for prod in (0, 1):
+        assert (moe.moe_expert_cu_split(fine, c129, 256, prod) ==
+                moe.moe_expert_cu_split(fine, c256, 256, prod))
     # no big expert: the small-expert GEMM keeps every CU; no small expert:
     # the big-expert GEMM does
     assert moe.moe_expert_cu_split(fine, np.full(n, 100, np.int32), 256) == 0

@@ -26,11 +26,13 @@ def _classes(cfg, counts):
     small = int(np.sum((counts > 0) & (counts < split)))
     big = int(np.sum(counts >= split))
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    share = moe.moe_expert_cu_split(cfg, np.asarray(counts, np.int32), cus)
+    shares = [moe.moe_expert_cu_split(cfg, np.asarray(counts, np.int32), cus, prod)
+              for prod in (0, 1)]
     log(f"  split at {split} rows: {small} experts on 128-row tiles, {big} on 256 x 256 "
-        f"(largest {int(counts.max())} rows); side by side on {share} + {cus - share} CUs")
+        f"(largest {int(counts.max())} rows); side by side, 256 x 256 GEMM on {shares} of "
+        f"{cus} CUs (first, second product)")
     if small and big and cfg.expert_dtype != DTYPE_FP8:
-        assert 0 < share < cus
+        assert all(0 < share < cus for share in shares)
     return split, small, big
 
 
@@ -129,15 +131,17 @@ def test_split_side_by_side_shares(case, counts):
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     rows = int(offsets[-1])
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    share = moe.moe_expert_cu_split(cfg, counts, cus)
-    log(f"[split shares] {case}: {rows} rows, 256 x 256 GEMM on {share} of {cus} CUs")
+    shares = [moe.moe_expert_cu_split(cfg, counts, cus, prod) for prod in (0, 1)]
+    log(f"[split shares] {case}: {rows} rows, 256 x 256 GEMM on {shares} of {cus} CUs "
+        f"(first, second product)")
     want = {"all_big": cus, "all_small": 0}
-    if case in want:
-        assert share == want[case]
-    elif case == "one_big":
-        assert 8 <= share <= 24  # a small share: the big-expert GEMM on a few CUs per XCD
-    else:
-        assert 0 < share < cus
+    for share in shares:
+        if case in want:
+            assert share == want[case]
+        elif case == "one_big":
+            assert 8 <= share <= 24  # a small share: the big-expert GEMM on a few CUs per XCD
+        else:
+            assert 0 < share < cus
     inp = dev_inputs(cfg)
     r = np.random.default_rng(506)
     x = oracle.bf16_round(r.standard_normal((rows, d)))
