@@ -263,16 +263,17 @@ int split_rows(const moe_config& c) {
 }
 
 // K-split of the flat (or primary) gate GEMM.  While its tiles number fewer
-// than three per CU (the 64 x 64 kernel's occupancy on 256 CUs), K is split
-// into up to ceil(768 / tiles) ranges of at least 1024, every range
-// non-empty, with the partial logits (one [T, ldl] copy per range) within
-// 24 MiB.
+// than three per CU (the 64 x 64 kernel's occupancy on 256 CUs; one per CU
+// for the 128 x 128 kernel), K is split into up to ceil(768 / tiles) (256 /
+// tiles) ranges of at least 1024, every range non-empty, with the partial
+// logits (one [T, ldl] copy per range) within 32 MiB.
 int gate_splits(long long T, long long d, int n_gate, int bm, int ldl) {
   const long long tiles = ((T + bm - 1) / bm) * ((n_gate + bm - 1) / bm);
-  if (tiles <= 0 || tiles >= 768) return 1;
-  long long s = (768 + tiles - 1) / tiles;
+  const long long target = bm == 128 ? 256 : 768;
+  if (tiles <= 0 || tiles >= target) return 1;
+  long long s = (target + tiles - 1) / tiles;
   s = std::min(s, d / 1024);
-  s = std::min(s, std::max(1LL, (24LL << 20) / (T * ldl * 4)));
+  s = std::min(s, std::max(1LL, (32LL << 20) / (T * ldl * 4)));
   s = std::max(1LL, std::min(s, 8LL));
   while (s > 1 && (long long)gate_split_len((int)d, (int)s) * (s - 1) >= d) --s;
   return (int)s;
@@ -287,9 +288,11 @@ Plan make_plan(const moe_config& c) {
   const int ncols = 2 * p.n_gate;  // clean | raw (the raw half is unused when noiseless)
   p.ldl = (int)round_up(ncols, 4);
   {
-    // 128x128 tiles (8 waves) once they give every CU a tile; 64x64 below.
+    // 128x128 tiles (8 waves) once they give every CU a tile, or at d >= 2048
+    // where the K-split makes up the count (fewer re-reads of x and fewer
+    // fragment reads per MFMA than 64x64); 64x64 otherwise.
     const long long t128 = ((T + 127) / 128) * ((ncols + 127) / 128);
-    p.gemm_bm = t128 >= 256 ? 128 : 64;
+    p.gemm_bm = t128 >= 256 || d >= 2048 ? 128 : 64;
     p.gate_splits = gate_splits(T, d, p.n_gate, p.gemm_bm, p.ldl);
   }
   {

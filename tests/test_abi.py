@@ -109,17 +109,18 @@ def test_expert_cu_split():
 
 
 def test_gate_k_splits():
-    # The gate GEMM's K-split: none while the tiles fill the CUs three times or
-    # d_model < 2048; else up to ceil(768 / tiles) ranges of >= 1024, every
-    # range non-empty, the partial logits within 24 MiB.
+    # The gate GEMM's K-split: none while the tiles fill the CUs (three 64 x 64
+    # or one 128 x 128 tile per CU; d_model >= 2048 takes 128 x 128) or
+    # d_model < 2048; else up to ceil(768 / tiles) (256 / tiles for 128 x 128)
+    # ranges of >= 1024, every range non-empty, the partial logits within 32 MiB.
     assert moe.moe_gate_k_splits(PRESETS["lm_layer"]) == 1          # d = 512
-    assert moe.moe_gate_k_splits(PRESETS["fine_swiglu"]) == 3       # 256 tiles, 3 x 8 MiB
-    assert moe.moe_gate_k_splits(PRESETS["sigmoid_shared"]) == 3
+    assert moe.moe_gate_k_splits(PRESETS["fine_swiglu"]) == 4       # 64 tiles, 4 x 8 MiB
+    assert moe.moe_gate_k_splits(PRESETS["sigmoid_shared"]) == 4
     assert moe.moe_gate_k_splits(base_cfg(T=700, d_model=3000, n_experts=96, k=4)) == 2
     assert moe.moe_gate_k_splits(base_cfg(T=64, d_model=8192, n_experts=8, k=2)) == 8
     # 768 tiles of 128 x 128 (T = 24576, 512 experts): no split
     assert moe.moe_gate_k_splits(base_cfg(T=24576, d_model=4096, n_experts=512, k=2)) == 1
-    # T = 6144, d = 7168, 256 experts: 2 x 12 MiB of partials
+    # T = 6144, d = 7168, 256 experts: 96 tiles, 2 x 12 MiB of partials
     assert moe.moe_gate_k_splits(base_cfg(T=6144, d_model=7168, n_experts=256, k=2)) == 2
     # a whole workspace per extra range: the size grows with the split
     one = moe.moe_workspace_size(base_cfg(T=64, d_model=1024, n_experts=8, k=2))
