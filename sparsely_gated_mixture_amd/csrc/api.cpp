@@ -1656,15 +1656,20 @@ int32_t moe_expert_cu_split(const moe_config* cfg, const int32_t* counts, int32_
   if (validate(cfg) != MOE_OK || !counts || cus < 0 || (product != 0 && product != 1)) return -1;
   const int big_rows = split_rows(*cfg);
   if (big_rows <= 0) return 0;
-  long long br = 0, se = 0, sr = 0;
+  long long br = 0, bg = 0, se = 0, sr = 0;
   for (int e = 0; e < cfg->n_experts; ++e) {
     const int kept = counts[e];
-    if (kept >= big_rows) br += (kept + kBigBM - 1) / kBigBM * kBigBM;
-    else if (kept > 0) ++se, sr += kept;
+    if (kept >= big_rows) {
+      const long long mt = (kept + kBigBM - 1) / kBigBM;
+      br += mt * kBigBM;
+      bg += (mt + kBigGroupM - 1) / kBigGroupM;
+    } else if (kept > 0) {
+      ++se, sr += kept;
+    }
   }
   if (cfg->expert_dtype != MOE_BF16) return 0;
   const CuSplit sp = cu_split_of(*cfg, nullptr);
-  return expert_cu_split(cus > 0 ? cus : sp.cus, br, se, sr, sp.d, sp.h, sp.swiglu, product);
+  return expert_cu_split(cus > 0 ? cus : sp.cus, br, bg, se, sr, sp.d, sp.h, sp.swiglu, product);
 }
 
 }  // extern "C"

@@ -176,19 +176,25 @@ __device__ inline void finalize_block(const DispatchArgs& a) {
         *a.big_map.count = cb.y;
       }
       if (a.split.out) {
-        int big_r = 0, small_e = 0, small_r = 0;
+        int big_r = 0, big_g = 0, small_e = 0, small_r = 0;
         for (int e = b; e < e1; ++e) {
           const int kept = a.counts[e];
-          if (kept >= a.big_rows) big_r += (kept + kBigBM - 1) / kBigBM * kBigBM;
-          else if (kept > 0) ++small_e, small_r += kept;
+          if (kept >= a.big_rows) {
+            const int mt = (kept + kBigBM - 1) / kBigBM;
+            big_r += mt * kBigBM;
+            big_g += (mt + kBigGroupM - 1) / kBigGroupM;
+          } else if (kept > 0) {
+            ++small_e, small_r += kept;
+          }
         }
         const int tb_rows = block_exscan<kFinThreads>(big_r, si).y;
+        const int tb_groups = block_exscan<kFinThreads>(big_g, si).y;
         const int ts_exp = block_exscan<kFinThreads>(small_e, si).y;
         const int ts_rows = block_exscan<kFinThreads>(small_r, si).y;
         if (threadIdx.x < 2)
-          a.split.out[threadIdx.x] = expert_cu_split(a.split.cus, tb_rows, ts_exp, ts_rows,
-                                                     a.split.d, a.split.h, a.split.swiglu,
-                                                     (int)threadIdx.x);
+          a.split.out[threadIdx.x] =
+              expert_cu_split(a.split.cus, tb_rows, tb_groups, ts_exp, ts_rows, a.split.d,
+                              a.split.h, a.split.swiglu, (int)threadIdx.x);
       }
     }
   }
@@ -405,16 +411,22 @@ __global__ __launch_bounds__(1024) void tilemap_split_kernel(const int32_t* __re
     *bg.count = tsum[1][1023];
   }
   if (split.out) {
-    // Padded rows of the big experts, count and rows of the small ones, summed in
-    // the same shared arrays (every thread has read its prefix above).
-    int v[3] = {0, 0, 0};
+    // Padded rows and M-tile groups of the big experts, count and rows of the
+    // small ones, summed in the same shared arrays (every thread has read its
+    // prefix above).
+    int v[4] = {0, 0, 0, 0};
     for (int i = 0; i < per && b + i < n; ++i) {
       const int rows = offsets[b + i + 1] - offsets[b + i];
-      if (rows >= big_rows) v[0] += (rows + kBigBM - 1) / kBigBM * kBigBM;
-      else if (rows > 0) v[1] += 1, v[2] += rows;
+      if (rows >= big_rows) {
+        const int mt = (rows + kBigBM - 1) / kBigBM;
+        v[0] += mt * kBigBM;
+        v[3] += (mt + kBigGroupM - 1) / kBigGroupM;
+      } else if (rows > 0) {
+        v[1] += 1, v[2] += rows;
+      }
     }
-    int tot[3];
-    for (int q = 0; q < 3; ++q) {
+    int tot[4];
+    for (int q = 0; q < 4; ++q) {
       __syncthreads();
       tsum[0][threadIdx.x] = v[q];
       __syncthreads();
@@ -425,8 +437,8 @@ __global__ __launch_bounds__(1024) void tilemap_split_kernel(const int32_t* __re
       tot[q] = tsum[0][0];
     }
     if (threadIdx.x < 2)
-      split.out[threadIdx.x] = expert_cu_split(split.cus, tot[0], tot[1], tot[2], split.d,
-                                               split.h, split.swiglu, (int)threadIdx.x);
+      split.out[threadIdx.x] = expert_cu_split(split.cus, tot[0], tot[3], tot[1], tot[2],
+                                               split.d, split.h, split.swiglu, (int)threadIdx.x);
   }
 }
 

@@ -34,7 +34,7 @@
 //    rows hit 16 distinct bank groups.  A copy moves 8 rows x 128 bytes into
 //    1 KB of LDS, lane i to bytes 16 i; lane i therefore reads the logical
 //    chunk that belongs at physical chunk i % 8 of its row;
-//  * work order: items in groups of kGroupM M-tiles (M fastest), cut into
+//  * work order: items in groups of kBigGroupM M-tiles (M fastest), cut into
 //    chunks of one XCD's workgroup count and dealt to the 8 XCDs in turn, so
 //    the XCDs work on neighbouring chunks -- mostly the same expert -- at the
 //    same time and its weights are fetched from HBM once for all of them
@@ -66,7 +66,6 @@ constexpr int kBK = 64;        // K per step
 constexpr int kRowB = 128;     // LDS bytes per row and step (kBK bf16)
 constexpr int kTileB = 256 * kRowB;  // the activations' 32 KB per step
 constexpr int kThreads = 256;
-constexpr int kGroupM = 4;           // M-tiles per group of the work order
 // A buffer offset this large lies beyond every descriptor's range: the load
 // returns zeros.
 constexpr int kOutOfRange = 0x40000000;
@@ -132,14 +131,14 @@ ggemm_big_kernel(const GemmBf16Args p) {
     --ntiles;  // this slot is past the end of the last, partial chunk
   if (ntiles == 0) return;
   const int tid = threadIdx.x;
-  // Item L -> (M-tile, N-tile) in groups of kGroupM consecutive M-tiles,
+  // Item L -> (M-tile, N-tile) in groups of kBigGroupM consecutive M-tiles,
   // the M-tile varying fastest within a group.
   const int mtiles = *p.tile_count;
   for (int t = tid; t < ntiles; t += kThreads) {
     const int L = (t * kXcds + xcd) * wpx + slot;
-    const int grp = L / (kGroupM * nN), r = L % (kGroupM * nN);
-    const int gsz = min(kGroupM, mtiles - grp * kGroupM);
-    const int mt = grp * kGroupM + r % gsz, nt = r / gsz;
+    const int grp = L / (kBigGroupM * nN), r = L % (kBigGroupM * nN);
+    const int gsz = min(kBigGroupM, mtiles - grp * kBigGroupM);
+    const int mt = grp * kBigGroupM + r % gsz, nt = r / gsz;
     const int e = p.tile_expert[mt];
     meta[t] = make_int4(e, p.tile_row0[mt], p.offsets[e + 1], nt * S::kCols);
   }

@@ -30,29 +30,42 @@ struct TileMap {
 // other.)  The shares are set from the routing on the device, by the kernel
 // that writes the two tile maps, one for each product (first: x W1^T and
 // x W3^T; second: hidden W2^T), so that both chains of a product take about
-// as long: from the big experts' flops over their rows padded to whole
-// 256-row tiles (the 256 x 256 kernel's unit of work: an expert of 130 rows
-// costs a whole tile), the small experts' weight and activation bytes, and
-// the rate one CU sustains on each while the other kernel runs (measured on
-// MI355X at d = 7168, h = 2048: 4.9 and 4.35 TFLOP/s of padded tile work in
-// the first and second product -- K = 7168 against 2048 per tile -- and 30
-// GB/s per CU).  A multiple of kXcds in [kXcds, cus - kXcds]; 0 without big
-// experts, every CU without small ones.
-constexpr double kBigFlopsPerCu0 = 4.9e12;   // first product
-constexpr double kBigFlopsPerCu1 = 4.35e12;  // second product
+// as long.  Each chain's cost in CU-seconds:
+//   big, first product:  flops over the big experts' rows padded to whole
+//     256-row tiles (the 256 x 256 kernel's unit of work: an expert of 130
+//     rows costs a whole tile) / kBigFlopsPerCu0, plus the weight bytes of
+//     its M-tile groups (each group of kBigGroupM M-tiles of an expert reads
+//     the expert's weights once) / kBigWeightBytesPerCu0;
+//   big, second product: padded-tile flops / kBigFlopsPerCu1;
+//   small: the product's weight and activation bytes / kSmallBytesPerCu.
+// The rates were fitted on MI355X to the measured balance points of two
+// routings at d = 7168, h = 2048 (31 big experts of up to 16 M-tiles, and 73
+// of mostly one or two), each kernel running beside the other.  The share is
+// a multiple of kXcds in [kXcds, cus - kXcds] (each XCD then holds as many
+// workgroups of each kernel as every other XCD); 0 without big experts,
+// every CU without small ones.
+constexpr double kBigFlopsPerCu0 = 5.13e12;
+constexpr double kBigWeightBytesPerCu0 = 59e9;
+constexpr double kBigFlopsPerCu1 = 4.4e12;
 constexpr double kSmallBytesPerCu = 30e9;
+constexpr int kBigGroupM = 4;  // M-tiles per group of the 256 x 256 kernel's work order
 // big_padded_rows: the big experts' rows, each expert's rounded up to a
-// multiple of kBigBM.  product: 0 first, 1 second.
+// multiple of kBigBM; big_groups: sum over the big experts of
+// ceil(M-tiles / kBigGroupM).  product: 0 first, 1 second.
 __host__ __device__ inline int expert_cu_split(int cus, long long big_padded_rows,
-                                               long long small_experts, long long small_rows,
-                                               int d, int h, int swiglu, int product) {
+                                               long long big_groups, long long small_experts,
+                                               long long small_rows, int d, int h, int swiglu,
+                                               int product) {
   if (big_padded_rows <= 0) return 0;
   if (small_experts <= 0) return cus;
   // weight matrices of the product (each d x h) and activation bytes per row
   const double mats = product == 0 && swiglu ? 2.0 : 1.0;
   const double row_bytes = product == 0 ? 2.0 * d + 2.0 * h : 2.0 * h + 4.0 * d;
-  const double t_big = 2.0 * mats * d * h * (double)big_padded_rows /
-                       (product == 0 ? kBigFlopsPerCu0 : kBigFlopsPerCu1);
+  const double flops = 2.0 * mats * d * h * (double)big_padded_rows;
+  const double t_big =
+      product == 0
+          ? flops / kBigFlopsPerCu0 + mats * d * h * 2.0 * (double)big_groups / kBigWeightBytesPerCu0
+          : flops / kBigFlopsPerCu1;
   const double t_small =
       (mats * d * h * 2.0 * (double)small_experts + row_bytes * (double)small_rows) /
       kSmallBytesPerCu;

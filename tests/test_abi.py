@@ -71,9 +71,11 @@ def test_expert_cu_split():
     counts[31:161] = 2000 // 130       # small ones, 15 rows each
     share = moe.moe_expert_cu_split(fine, counts, 256)
     # First product: 31 x 1024 padded rows of 5.9e10 flops each (x W1^T and
-    # x W3^T) at 4.9 TFLOP/s per CU against 130 x 58.7 MB of W1 | W3 at 30
-    # GB/s per CU: 19 of 32 XCD rows.  Second product: 2.9e10 flops per row
-    # at 4.35 TFLOP/s against 130 x 29.4 MB of W2: 20 of 32.
+    # x W3^T) at 5.13 TFLOP/s per CU, plus 31 M-tile groups of 58.7 MB of
+    # W1 | W3 at 59 GB/s per CU, against 130 x 58.7 MB of small experts'
+    # W1 | W3 at 30 GB/s per CU: 19.4 of 32 XCD rows, rounded to 19.  Second
+    # product: 2.9e10 flops per row at 4.4 TFLOP/s against 130 x 29.4 MB of
+    # W2: 20 of 32.
     assert share == 152
     assert moe.moe_expert_cu_split(fine, counts, 256, 1) == 160
     assert share % 8 == 0 and 8 <= share <= 248
