@@ -209,8 +209,10 @@ def kernel_work(name, cfg, rows, nonempty, T):
     if name == "gate_gemm_bf16x6":
         # The method's work is one fp32 contraction (2*T*d*ncols flops, graded
         # against the fp32 peak); the kernel reaches fp32 accuracy with six
-        # bf16 products per term (their rate is reported beside it).
-        return (T * d * 4 + ncols * d * 4 + T * ncols * 4, 2.0 * T * ncols * d, "f32")
+        # bf16 products per term (their rate is reported beside it).  In the
+        # flat layer with bf16 or FP8 experts it also writes x in bf16.
+        xb = T * d * 2 if bf and not cfg.hierarchical and T * d * 2 <= 1 << 30 else 0
+        return (T * d * 4 + ncols * d * 4 + T * ncols * 4 + xb, 2.0 * T * ncols * d, "f32")
     if name.startswith("gemm_f32"):
         return (T * d * 4 + ncols * d * 4 + T * ncols * 4, 2.0 * T * ncols * d, "f32")
     if name == "gate_topk":

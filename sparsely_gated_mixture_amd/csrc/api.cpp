@@ -434,13 +434,15 @@ moe_status check_ws(void* ws, size_t ws_bytes, size_t need_bytes, const char* wh
 moe_status run_gate(const moe_config& c, const Plan& p, const float* x, const float* w_gate,
                     const float* b_gate, const float* w_noise, const float* noise,
                     int32_t* topk_idx, float* topk_w, float* importance, float* load,
-                    float* gate_stats, void* ws, hipStream_t s, ColsumVec* defer = nullptr) {
+                    float* gate_stats, void* ws, hipStream_t s, ColsumVec* defer = nullptr,
+                    uint16_t* x_bf16 = nullptr) {
   const int n = c.n_experts;
   const bool noisy = w_noise != nullptr;
   float* logits = at<float>(ws, p.logits);
   if (c.T > 0) {
     GemmF32Args g{};
     g.A = x;
+    g.a_bf16 = x_bf16;  // optional: x in bf16, token order, as a by-product
     g.lda = c.d_model;
     g.B1 = w_gate;
     g.B2 = w_noise;
@@ -638,6 +640,7 @@ struct ForwardExtras {
   const float* load = nullptr;
   const float* gate_stats = nullptr;
   uint16_t* x_bf16 = nullptr;  // x in bf16, token order, written by the gather
+  bool x_bf16_written = false;  // ... or already by the gate GEMM
   // Non-null: GEMM 1 reads merged row r as row row_token[r] (= perm) of the
   // token-order x_bf16, and the gather writes no x_perm.
   const int32_t* row_token = nullptr;
@@ -689,8 +692,10 @@ moe_status run_dispatch(const moe_config& c, const Plan& p, const int32_t* topk_
     }
   }
   HIP_TRY(launch_dispatch(da, s));
-  HIP_TRY(launch_gather(x, slot_pos, c.T, c.k, c.d_model, c.expert_dtype != MOE_F32, x_perm,
-                        fx ? fx->x_bf16 : nullptr, s));
+  uint16_t* xb = fx && !fx->x_bf16_written ? fx->x_bf16 : nullptr;
+  if (x_perm || xb)
+    HIP_TRY(launch_gather(x, slot_pos, c.T, c.k, c.d_model, c.expert_dtype != MOE_F32, x_perm, xb,
+                          s));
   return MOE_OK;
 }
 
@@ -1890,15 +1895,28 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const float
   const bool has_load = hier ? (wt->w_noise && wt->w_noise2) : (wt->w_noise != nullptr);
   float* stats = at<float>(ws, p.f_stats);
   ForwardExtras fx;
+  const bool shared = c.d_hidden_shared > 0;
+  fx.x_bf16 = shared ? at<uint16_t>(ws, p.sh_xb) : nullptr;
+  // bf16 and FP8 experts: x is rounded to bf16 once, in token order (into the
+  // x_perm region unless the shared expert's copy exists), and GEMM 1 reads
+  // each merged row through perm, instead of k copies of every row.  The flat
+  // gate GEMM writes that copy as a by-product of splitting x (the two-level
+  // layer's gather writes it).
+  const bool via_perm =
+      c.expert_dtype != MOE_F32 && (long long)c.T * c.d_model * 2 <= (1LL << 30);
+  if (via_perm) {
+    fx.row_token = perm;
+    if (!fx.x_bf16) fx.x_bf16 = (uint16_t*)xperm;
+  }
   if (hier) {
     CHECK(run_gate_hier(c, p, x, wt->w_gate, wt->b_gate, wt->w_noise, noise, wt->w_gate2,
                         wt->w_noise2, noise2, idx, w, imp, ld, stats, ws, s));
   } else {
     CHECK(run_gate(c, p, x, wt->w_gate, wt->b_gate, wt->w_noise, noise, idx, w, imp, ld, stats,
-                   ws, s, fx.colsum));
+                   ws, s, fx.colsum, fx.x_bf16));
     fx.colsum_fused = true;
+    fx.x_bf16_written = fx.x_bf16 != nullptr;
   }
-  const bool shared = c.d_hidden_shared > 0;
   fx.tile_expert = at<int32_t>(ws, p.f_tile_expert);
   fx.tile_row0 = at<int32_t>(ws, p.f_tile_row0);
   fx.tile_count = at<int32_t>(ws, p.f_tile_count);
@@ -1914,16 +1932,6 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const float
   fx.importance = imp;
   fx.load = has_load ? ld : nullptr;
   fx.gate_stats = stats;
-  fx.x_bf16 = shared ? at<uint16_t>(ws, p.sh_xb) : nullptr;
-  // bf16 and FP8 experts: the gather writes x once in token order as bf16
-  // (into the x_perm region unless the shared expert's copy exists) and GEMM 1
-  // reads each merged row through perm, instead of k copies of every row.
-  const bool via_perm =
-      c.expert_dtype != MOE_F32 && (long long)c.T * c.d_model * 2 <= (1LL << 30);
-  if (via_perm) {
-    fx.row_token = perm;
-    if (!fx.x_bf16) fx.x_bf16 = (uint16_t*)xperm;
-  }
   CHECK(run_dispatch(c, p, idx, x, counts_pre, counts, offsets, perm, slot,
                      via_perm ? nullptr : xperm, ws, s, &fx));
   CHECK(run_ffn(c, p, via_perm ? (const void*)fx.x_bf16 : xperm, offsets, wt->w1, wt->b1, wt->w3,

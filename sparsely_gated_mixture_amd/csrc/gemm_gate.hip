@@ -113,9 +113,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_gate_kernel(const GemmF32
   const int K = min(p.K, kb + klen);
   float* const C = p.C + (long long)ks * p.split_stride;
 
-  // Global sources of this thread's chunks (row r, k offset kc).
+  // Global sources of this thread's chunks (row r, k offset kc), and where
+  // the x chunks' bf16 copy goes (first column tile of a flat launch with
+  // a_bf16).
+  const bool xcopy = p.a_bf16 && !grouped && wt == 0;
   const float* wsrc[CH];
   const float* xsrc[CH];
+  uint16_t* xdst[CH];
   bool wok[CH], xok[CH];
   int rr[CH], kc[CH];
 #pragma unroll
@@ -132,6 +136,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_gate_kernel(const GemmF32
     xok[i] = gt < tok_end;
     const long long arow = !xok[i] ? 0 : p.rowmap ? (long long)p.rowmap[gt] : (long long)gt;
     xsrc[i] = p.A + arow * p.lda + kb + kc[i];
+    xdst[i] = xcopy ? p.a_bf16 + (long long)gt * p.K + kb + kc[i] : nullptr;
   }
   // Two register buffers: step s's fp32 chunks live in buffer s % 2, are
   // loaded two steps ahead and split into LDS one step ahead.
@@ -144,7 +149,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_gate_kernel(const GemmF32
       rx[rb][i] = (xok[i] && kin) ? *(const f32x4*)(xsrc[i] + k0) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   };
-  auto store = [&](int buf, int rb) {
+  // Split register buffer rb (the step at K offset k0 of this range) into
+  // LDS stage buf.
+  auto store = [&](int buf, int rb, int k0) {
     uint8_t* st = smem + buf * STAGE;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
@@ -155,6 +162,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_gate_kernel(const GemmF32
       *(uint2*)(st + 1 * COMP + off) = m;
       *(uint2*)(st + 2 * COMP + off) = l;
       split3(rx[rb][i], h, m, l);
+      if (xcopy && xok[i] && kb + k0 + kc[i] < K) *(uint2*)(xdst[i] + k0) = h;
       *(uint2*)(st + 3 * COMP + off) = h;
       *(uint2*)(st + 4 * COMP + off) = m;
       *(uint2*)(st + 5 * COMP + off) = l;
@@ -215,12 +223,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_gate_kernel(const GemmF32
             chunk[i][j][v] = 0.f;
           }
     }
-    if (kt + 1 < nk) store(rb ^ 1, rb ^ 1);
+    if (kt + 1 < nk) store(rb ^ 1, rb ^ 1, (kt + 1) * kBK);
     __syncthreads();
   };
   load(0, 0);
   if (nk > 1) load(kBK, 1);
-  store(0, 0);
+  store(0, 0, 0);
   __syncthreads();
   for (int kt = 0; kt < nk; kt += 2) {
     step(kt, 0);

@@ -130,6 +130,10 @@ struct GemmF32Args {
   // its partial product to C + s * split_stride.  0 or 1: one product to C.
   int ksplit;
   long long split_stride;
+  // Flat mode, optional: the items of the first column tile also write A
+  // rounded to bf16 (to nearest even: the operand split's high part) to
+  // a_bf16 = [M, K] -- the layer forward's token-order bf16 copy of x.
+  uint16_t* a_bf16;
 };
 // Length of each K range of a ksplit-way gate GEMM: ceil(K / ksplit) rounded
 // up to the kernel's 256-wide accumulation chunks.
