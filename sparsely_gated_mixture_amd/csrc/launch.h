@@ -52,28 +52,50 @@ constexpr int kBigGroupM = 4;  // M-tiles per group of the 256 x 256 kernel's wo
 // big_padded_rows: the big experts' rows, each expert's rounded up to a
 // multiple of kBigBM; big_groups: sum over the big experts of
 // ceil(M-tiles / kBigGroupM).  product: 0 first, 1 second.
+//
+// The two chains run independently (each kernel waits only for the previous
+// one on its own stream), so the step ends with the longer chain.  The first
+// product's share balances that product.  The second product's share then
+// balances the chains' totals, on the side the first product frees first:
+// if the small experts' chain finishes its first product first, the big
+// experts' second product may take more CUs than its first (they are free
+// by the time it starts), never fewer than the first's, and the other way
+// round, so neither kernel's workgroups wait for CUs the other chain holds.
 __host__ __device__ inline int expert_cu_split(int cus, long long big_padded_rows,
                                                long long big_groups, long long small_experts,
                                                long long small_rows, int d, int h, int swiglu,
                                                int product) {
   if (big_padded_rows <= 0) return 0;
   if (small_experts <= 0) return cus;
-  // weight matrices of the product (each d x h) and activation bytes per row
-  const double mats = product == 0 && swiglu ? 2.0 : 1.0;
-  const double row_bytes = product == 0 ? 2.0 * d + 2.0 * h : 2.0 * h + 4.0 * d;
-  const double flops = 2.0 * mats * d * h * (double)big_padded_rows;
-  const double t_big =
-      product == 0
-          ? flops / kBigFlopsPerCu0 + mats * d * h * 2.0 * (double)big_groups / kBigWeightBytesPerCu0
-          : flops / kBigFlopsPerCu1;
-  const double t_small =
-      (mats * d * h * 2.0 * (double)small_experts + row_bytes * (double)small_rows) /
-      kSmallBytesPerCu;
   const int units = cus / kXcds;
   if (units < 2) return cus;
-  int u = (int)(units * t_big / (t_big + t_small) + 0.5);
-  u = u < 1 ? 1 : (u > units - 1 ? units - 1 : u);
-  return u * kXcds;
+  // Each product's cost in CU-seconds: weight matrices (each d x h) and
+  // activation bytes per row.
+  double t_big[2], t_small[2];
+  for (int q = 0; q < 2; ++q) {
+    const double mats = q == 0 && swiglu ? 2.0 : 1.0;
+    const double row_bytes = q == 0 ? 2.0 * d + 2.0 * h : 2.0 * h + 4.0 * d;
+    const double flops = 2.0 * mats * d * h * (double)big_padded_rows;
+    t_big[q] = q == 0 ? flops / kBigFlopsPerCu0 +
+                            mats * d * h * 2.0 * (double)big_groups / kBigWeightBytesPerCu0
+                      : flops / kBigFlopsPerCu1;
+    t_small[q] = (mats * d * h * 2.0 * (double)small_experts + row_bytes * (double)small_rows) /
+                 kSmallBytesPerCu;
+  }
+  int u0 = (int)(units * t_big[0] / (t_big[0] + t_small[0]) + 0.5);
+  u0 = u0 < 1 ? 1 : (u0 > units - 1 ? units - 1 : u0);
+  if (product == 0) return u0 * kXcds;
+  // chain times in units of CU-seconds per XCD row of CUs
+  const double b0 = t_big[0] / u0, s0 = t_small[0] / (units - u0);
+  const int lo = s0 <= b0 ? u0 : 1, hi = s0 <= b0 ? units - 1 : u0;
+  int best = u0;
+  double best_t = 1e300;
+  for (int u = lo; u <= hi; ++u) {
+    const double tb = b0 + t_big[1] / u, ts = s0 + t_small[1] / (units - u);
+    const double t = tb > ts ? tb : ts;
+    if (t < best_t) best_t = t, best = u;
+  }
+  return best * kXcds;
 }
 
 // Where the tile-map kernels write that share (out == null: no side-by-side
