@@ -226,7 +226,7 @@ def kernel_work(name, cfg, rows, nonempty, T):
     if name == "dispatch_permute":
         return (T * k * 4 * 2 + rows * 4, 0.0, "i32")
     w = 16 if (cfg.n_groups or n) <= 512 else 8
-    rpb = max(2 * w, -(-((T + 255) // 256) // w) * w)
+    rpb = max(w, -(-((T + 255) // 256) // w) * w)
     nparts = (T + rpb - 1) // rpb
     if name == "dispatch_hist":
         # the flat layer's launch also sums the gate's Importance / Load partials
