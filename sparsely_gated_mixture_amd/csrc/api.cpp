@@ -1930,7 +1930,9 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const float
                          at<int32_t>(ws, p.f_tb_count)};
     fx.cu_split = at<int32_t>(ws, p.f_split);
   }
-  fx.losses = losses;
+  // The losses are not needed before the combine: one extra block of the
+  // combine launch computes them, off the dispatch's serial finalize.
+  fx.losses = nullptr;
   fx.importance = imp;
   fx.load = has_load ? ld : nullptr;
   fx.gate_stats = stats;
@@ -1940,7 +1942,10 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const float
                 wt->w2, wt->b2, yperm, ws, s, &fx));
   float* ysh = shared ? at<float>(ws, p.sh_y) : nullptr;
   if (shared) CHECK(run_shared_ffn(c, p, fx.x_bf16, wt->ws1, wt->ws3, wt->ws2, ysh, ws, s));
-  HIP_TRY(launch_combine(yperm, slot, w, ysh, c.T, c.k, c.d_model, y, s));
+  const AuxArgs aux{imp,       fx.load,   counts_pre,     stats,       c.T,
+                    c.k,       c.n_experts, c.w_importance, c.w_load, c.alpha_switch,
+                    c.w_z,     c.w_entropy, losses};
+  HIP_TRY(launch_combine(yperm, slot, w, ysh, c.T, c.k, c.d_model, y, s, &aux));
   return MOE_OK;
 }
 

@@ -8,7 +8,8 @@
 // E_i(x)) starts the sum.
 //
 // Aux losses (same page, load-balancing losses; MoE survey, tufusi.com 3.2;
-// wkbse.com MoE introduction, part 2): one block computes, in double
+// wkbse.com MoE introduction, part 2), as an extra block of the layer
+// forward's combine launch or a launch of their own: one block computes, in double
 // precision with fixed-order tree reductions, w_imp*CV(Importance)^2,
 // w_load*CV(Load)^2 (population variance, two passes), alpha*n*sum_i f_i P_i,
 // the mean router z statistic and minus the mean gate entropy.
@@ -34,11 +35,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       const float* __restrict__ topk_w,
                                                       const float* __restrict__ y_base, int T,
                                                       int k, int d, int wpt,
-                                                      float* __restrict__ y) {
+                                                      float* __restrict__ y, const AuxArgs aux) {
+  // Block 0 of a launch with losses computes them, beside the token blocks
+  // (dispatched first, it does not extend the launch's tail).
+  if (aux.losses && blockIdx.x == 0) {
+    __shared__ double sh[256];
+    block_aux_losses<256>(aux.importance, aux.load, aux.counts_pre, aux.gate_stats, aux.T, aux.k,
+                          aux.n, aux.w_imp, aux.w_load, aux.alpha, aux.w_z, aux.w_ent,
+                          aux.losses, sh);
+    return;
+  }
   constexpr int V = 2;
   constexpr int G = 8;  // slots per group of loads
   const int lane = threadIdx.x & 63;
-  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int gw = ((int)blockIdx.x - (aux.losses ? 1 : 0)) * 4 + (threadIdx.x >> 6);
   const int t = gw / wpt, part = gw % wpt;
   if (t >= T) return;
   const int my_pos = lane < k ? slot_pos[(long long)t * k + lane] : -1;
@@ -100,8 +110,15 @@ __global__ __launch_bounds__(256) void aux_kernel(const float* __restrict__ impo
 }  // namespace
 
 hipError_t launch_combine(const float* y_perm, const int32_t* slot_pos, const float* topk_w,
-                          const float* y_base, int T, int k, int d, float* y, hipStream_t s) {
-  if (T <= 0) return hipSuccess;
+                          const float* y_base, int T, int k, int d, float* y, hipStream_t s,
+                          const AuxArgs* aux) {
+  if (T <= 0) {
+    if (aux && aux->losses)
+      return launch_aux(aux->importance, aux->load, aux->counts_pre, aux->gate_stats, aux->T,
+                        aux->k, aux->n, aux->w_imp, aux->w_load, aux->alpha, aux->w_z,
+                        aux->w_ent, aux->losses, s);
+    return hipSuccess;
+  }
   // Waves per token: enough for about 8192 waves (32 per CU), at most one
   // per 512-column pass and at most 8.
   const int passes = (d + 511) / 512;
@@ -109,9 +126,11 @@ hipError_t launch_combine(const float* y_perm, const int32_t* slot_pos, const fl
   wpt = wpt < 1 ? 1 : wpt > 8 ? 8 : wpt;
   if (wpt > passes) wpt = passes;
   const long long waves = (long long)T * wpt;
+  const AuxArgs ax = aux ? *aux : AuxArgs{};
+  const long long blocks = (waves + 3) / 4 + (ax.losses ? 1 : 0);
   ProfScope ps("combine", s);
-  combine_kernel<<<dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s>>>(
-      y_perm, slot_pos, topk_w, y_base, T, k, d, wpt, y);
+  combine_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(y_perm, slot_pos, topk_w, y_base,
+                                                              T, k, d, wpt, y, ax);
   return hipGetLastError();
 }
 

@@ -470,9 +470,22 @@ hipError_t launch_bias_update(const int32_t* counts_pre, int n, int T, int k, fl
 // ---------------------------------------------------------------------------
 // Combine and aux.
 // ---------------------------------------------------------------------------
-// y[t] = y_base[t] (when given) + sum over kept slots, in slot order.
+// The auxiliary losses' inputs (block_aux_losses); losses == null: none.
+struct AuxArgs {
+  const float* importance;
+  const float* load;  // may be null (no Load term)
+  const int32_t* counts_pre;
+  const float* gate_stats;  // may be null
+  int T, k, n;
+  float w_imp, w_load, alpha, w_z, w_ent;
+  float* losses;
+};
+// y[t] = y_base[t] (when given) + sum over kept slots, in slot order.  With
+// aux (losses non-null) one more block of the launch (its first) computes the
+// losses.
 hipError_t launch_combine(const float* y_perm, const int32_t* slot_pos, const float* topk_w,
-                          const float* y_base, int T, int k, int d, float* y, hipStream_t s);
+                          const float* y_base, int T, int k, int d, float* y, hipStream_t s,
+                          const AuxArgs* aux = nullptr);
 hipError_t launch_aux(const float* importance, const float* load, const int32_t* counts_pre,
                       const float* gate_stats, int T, int k, int n, float w_imp, float w_load,
                       float alpha, float w_z, float w_ent, float* losses, hipStream_t s);
