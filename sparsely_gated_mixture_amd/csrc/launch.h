@@ -29,8 +29,8 @@ struct TileMap {
 // per CU-second as bf16 -- and gains nothing; those run one after the
 // other.)  The shares are set from the routing on the device, by the kernel
 // that writes the two tile maps, one for each product (first: x W1^T and
-// x W3^T; second: hidden W2^T), so that both chains of a product take about
-// as long.  Each chain's cost in CU-seconds:
+// x W3^T; second: hidden W2^T), so that the two kernels' chains take about
+// as long (below).  Each kernel's cost in CU-seconds:
 //   big, first product:  flops over the big experts' rows padded to whole
 //     256-row tiles (the 256 x 256 kernel's unit of work: an expert of 130
 //     rows costs a whole tile) / kBigFlopsPerCu0, plus the weight bytes of
