@@ -231,7 +231,7 @@ moe_status moe_gate(const moe_config* cfg, const float* x, const float* w_gate,
  * memory: code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc.  Same arguments (minus ws, ws_bytes), same kernels, same
  * results as moe_gate.
- * Scratch: a static device array of 32 MiB inside the library, one copy per
+ * Scratch: a static device array of 48 MiB inside the library, one copy per
  * GPU, held from the first call on that GPU until the process ends; the call
  * itself allocates nothing.  A config whose gate needs more scratch than
  * that (moe_gate's workspace: the logits [T, 2n] fp32 plus per-block partial

@@ -28,9 +28,11 @@
 namespace moe {
 namespace {
 
-// 32 MiB: the gate's logits [T, 2n] fp32 and its partial sums -- e.g.
-// T = 8192 tokens with a noisy gate over 256 experts needs 16.8 MB.
-constexpr size_t kScratchBytes = (size_t)32 << 20;
+// 48 MiB: the gate's logits [T, 2n] fp32 (one copy per K range when K is
+// split) and its partial sums -- e.g. T = 8192 tokens with a noisy gate over
+// 256 experts needs 16.8 MB; T = 4096 at d = 7168 over 256 experts (K in
+// four ranges) 34 MB.
+constexpr size_t kScratchBytes = (size_t)48 << 20;
 constexpr int kMaxDevices = 64;
 
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];

@@ -44,3 +44,22 @@ def test_gate_static_matches_gate_on_consecutive_calls():
         for key in ref:
             np.testing.assert_array_equal(got[key], ref[key], err_msg=f"T={T} {key}")
         assert np.all(ref["idx"] >= 0) and np.all(ref["idx"] < cfg.n_experts)
+
+
+def test_gate_static_fine_grained_gate_with_k_split():
+    # The fine-grained layer's gate (d = 7168, 256 experts, no noise): 128 x
+    # 128 tiles with K split four ways, whose partial logits take most of the
+    # static scratch; then a smaller batch (seven ranges of its own split).
+    torch.cuda.set_device(0)
+    base = PRESETS["fine_swiglu"].replace(d_hidden=8)  # tiny experts, unused by the gate
+    assert moe.moe_gate_k_splits(base) == 4
+    for T in (4096, 1000):
+        cfg = base.replace(T=T)
+        print(f"[no-alloc] moe_gate_static vs moe_gate, fine-grained gate T={T}, "
+              f"K split {moe.moe_gate_k_splits(cfg)}", flush=True)
+        inp = make_inputs(cfg, device="cuda")
+        ref = _gate(cfg, inp, _outputs(cfg), static=False)
+        got = _gate(cfg, inp, _outputs(cfg), static=True)
+        for key in ("idx", "w", "imp", "stats"):
+            np.testing.assert_array_equal(got[key], ref[key], err_msg=f"T={T} {key}")
+        assert np.all(ref["idx"] >= 0) and np.all(ref["idx"] < cfg.n_experts)
