@@ -163,13 +163,15 @@ def side_by_side(cfg, counts, kernels):
     return out
 
 
-def kernel_work(name, cfg, rows, nonempty, T):
+def kernel_work(name, cfg, rows, nonempty, T, fwd=True):
     """(algorithmic bytes, flops, dtype) of one launch of kernel `name` for
     this step's realised routing (rows and non-empty experts of the
-    launch)."""
+    launch).  fwd: the layer forward, whose bf16 / FP8 experts write their
+    output rows in bf16 (the training forward keeps them in fp32)."""
     d, h, n, k = cfg.d_model, cfg.d_hidden, cfg.n_experts, cfg.k
     bf = cfg.expert_dtype != 0
     wsz = 2 if bf else 4
+    ysz = 2 if bf and fwd else 4  # bytes per element of the expert output rows
     noisy = cfg.noisy
     ng = cfg.n_groups if cfg.hierarchical else n  # the flat or primary gate's width
     ncols = 2 * ng if noisy else ng
@@ -188,7 +190,7 @@ def kernel_work(name, cfg, rows, nonempty, T):
         return (nonempty * 2 * h * d * 2 + rows * d * 2 + rows * h * 2, 4.0 * rows * h * d,
                 "bf16")
     if name in ("ggemm_bf16_out", "ggemm_big_out"):
-        return (nonempty * d * h * 2 + rows * h * 2 + rows * d * 4, 2.0 * rows * d * h, "bf16")
+        return (nonempty * d * h * 2 + rows * h * 2 + rows * d * ysz, 2.0 * rows * d * h, "bf16")
     # FP8 experts: one byte per weight plus one fp32 scale per weight row
     if name in ("ggemm_fp8_relu", "ggemm_big_fp8_relu"):
         return (nonempty * (h * d + 4 * h) + rows * d * 2 + rows * h * 2, 2.0 * rows * h * d,
@@ -197,7 +199,7 @@ def kernel_work(name, cfg, rows, nonempty, T):
         return (nonempty * 2 * (h * d + 4 * h) + rows * d * 2 + rows * h * 2,
                 4.0 * rows * h * d, "bf16")
     if name in ("ggemm_fp8_out", "ggemm_big_fp8_out"):
-        return (nonempty * (d * h + 4 * d) + rows * h * 2 + rows * d * 4, 2.0 * rows * d * h,
+        return (nonempty * (d * h + 4 * d) + rows * h * 2 + rows * d * ysz, 2.0 * rows * d * h,
                 "bf16")
     hs = cfg.d_hidden_shared
     if name in ("shared_bf16_relu", "shared_big_relu"):
@@ -222,7 +224,7 @@ def kernel_work(name, cfg, rows, nonempty, T):
     if name == "dispatch_gather":
         return (T * d * 4 + rows * d * wsz + rows * 4 + (T * d * 2 if hs else 0), 0.0, "f32")
     if name == "combine":
-        return (rows * d * 4 + T * d * 4 + T * k * 8 + (T * d * 4 if hs else 0), 0.0, "f32")
+        return (rows * d * ysz + T * d * 4 + T * k * 8 + (T * d * 4 if hs else 0), 0.0, "f32")
     if name == "dispatch_permute":
         return (T * k * 4 * 2 + rows * 4, 0.0, "i32")
     w = 16 if (cfg.n_groups or n) <= 512 else 8
@@ -294,7 +296,7 @@ def bwd_kernel_work(name, cfg, rows, nonempty, T):
         return (r2 * d * 4 + r2 * c2 * 4 + wbytes, 2.0 * r2 * c2 * d, "f32")
     if name == "bwd_dx_gather":
         return (T * d * 4 + rows * d * 4 + (T * d * 4 if hs else 0) + T * d * 4, 0.0, "f32")
-    return kernel_work(name, cfg, rows, nonempty, T)
+    return kernel_work(name, cfg, rows, nonempty, T, fwd=False)
 
 
 def gate_text(cfg):

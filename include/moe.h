@@ -360,7 +360,10 @@ moe_status moe_router_bias_update(const moe_config* cfg, const int32_t* counts_p
  * In:  weights (see moe_weights), x [T, d], noise [T, n_gate] (required iff
  *      weights->w_noise), noise2 [T, k1, b] (two-level, iff w_noise2).
  * Out: y [T, d] fp32 (no residual added), losses [5] fp32 (as moe_aux_loss),
- *      diag: optional intermediates (may be NULL). */
+ *      diag: optional intermediates (may be NULL).
+ * Precision: with bf16 or FP8 experts each expert's output row is rounded to
+ * bf16 before the combine weights and sums it in fp32 (moe_expert_ffn and
+ * the training forward keep those rows in fp32). */
 moe_status moe_forward(const moe_config* cfg, const moe_weights* weights, const float* x,
                        const float* noise, const float* noise2, float* y, float* losses,
                        const moe_diag* diag, void* ws, size_t ws_bytes, void* stream);

@@ -715,7 +715,7 @@ void set_row_token(GemmBf16Args& g, const moe_config& c, const ForwardExtras* fx
 moe_status run_ffn(const moe_config& c, const Plan& p, const void* x_perm,
                    const int32_t* offsets, const void* w1, const float* b1, const void* w3,
                    const void* w2, const float* b2, float* y_perm, void* ws, hipStream_t s,
-                   const ForwardExtras* fx = nullptr) {
+                   const ForwardExtras* fx = nullptr, bool y_bf16 = false) {
   const int n = c.n_experts, d = c.d_model, h = c.d_hidden;
   int32_t* te = fx ? fx->tile_expert : at<int32_t>(ws, p.t_expert);
   int32_t* tr = fx ? fx->tile_row0 : at<int32_t>(ws, p.t_row0);
@@ -766,6 +766,7 @@ moe_status run_ffn(const moe_config& c, const Plan& p, const void* x_perm,
     g2.ldc = d;
     g2.bias = b2;
     const int epi1 = c.act == MOE_ACT_SWIGLU ? EPI_SWIGLU_BF16 : EPI_RELU_BF16;
+    const int epi2 = y_bf16 ? EPI_IDENT_BF16 : EPI_IDENT_F32;
     // bf16 weights: the small experts' chain runs on the side stream beside
     // the big experts' chain on `s`, each kernel on its share of the CUs.
     // FP8 weights (or no side stream): one after the other, each on the
@@ -794,7 +795,7 @@ moe_status run_ffn(const moe_config& c, const Plan& p, const void* x_perm,
         as.cu_big = 0;
         ab.cu_big = 1;
       }
-      const int epi = prod == 0 ? epi1 : EPI_IDENT_F32;
+      const int epi = prod == 0 ? epi1 : epi2;
       HIP_TRY(launch_gemm_bf16(as, epi, ss ? ss->s : s));
       HIP_TRY(launch_gemm_big(ab, epi, s));
     }
@@ -839,7 +840,7 @@ moe_status run_ffn(const moe_config& c, const Plan& p, const void* x_perm,
     g2.C = y_perm;
     g2.ldc = d;
     g2.bias = b2;
-    HIP_TRY(launch_gemm_bf16(g2, EPI_IDENT_F32, s));
+    HIP_TRY(launch_gemm_bf16(g2, y_bf16 ? EPI_IDENT_BF16 : EPI_IDENT_F32, s));
   } else {
     GemmF32Args g{};
     g.A = (const float*)x_perm;
@@ -1938,14 +1939,17 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const float
   fx.gate_stats = stats;
   CHECK(run_dispatch(c, p, idx, x, counts_pre, counts, offsets, perm, slot,
                      via_perm ? nullptr : xperm, ws, s, &fx));
+  // bf16 / FP8 experts: their output rows are rounded to bf16 (only the
+  // combine reads them); fp32 experts keep fp32 rows.
+  const bool y_bf16 = c.expert_dtype != MOE_F32;
   CHECK(run_ffn(c, p, via_perm ? (const void*)fx.x_bf16 : xperm, offsets, wt->w1, wt->b1, wt->w3,
-                wt->w2, wt->b2, yperm, ws, s, &fx));
+                wt->w2, wt->b2, yperm, ws, s, &fx, y_bf16));
   float* ysh = shared ? at<float>(ws, p.sh_y) : nullptr;
   if (shared) CHECK(run_shared_ffn(c, p, fx.x_bf16, wt->ws1, wt->ws3, wt->ws2, ysh, ws, s));
   const AuxArgs aux{imp,       fx.load,   counts_pre,     stats,       c.T,
                     c.k,       c.n_experts, c.w_importance, c.w_load, c.alpha_switch,
                     c.w_z,     c.w_entropy, losses};
-  HIP_TRY(launch_combine(yperm, slot, w, ysh, c.T, c.k, c.d_model, y, s, &aux));
+  HIP_TRY(launch_combine(yperm, slot, w, ysh, c.T, c.k, c.d_model, y, s, &aux, y_bf16));
   return MOE_OK;
 }
 

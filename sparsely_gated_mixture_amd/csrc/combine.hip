@@ -19,6 +19,8 @@
 namespace moe {
 namespace {
 
+typedef unsigned int v2u32 __attribute__((ext_vector_type(2)));
+
 // wpt wavefronts per token (1 while the batch fills the chip, else up to 8,
 // each taking every wpt-th pass of the row).  Lane s holds the token's slot s
 // (position and weight, k <= 64), broadcast with readlane; each pass covers
@@ -29,8 +31,10 @@ namespace {
 // the whole wave); a dropped slot's descriptor spans nothing, so its loads
 // return zeros without a memory access and no branch breaks the group.
 // Per element: acc = base, then acc = fma(w_s, row_s, acc) in slot order (a
-// dropped slot adds w_s * 0).
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_perm,
+// dropped slot adds w_s * 0).  TY: the element type of y_perm (float, or
+// uint16_t for bf16 rows, widened exactly to fp32 before the multiply-add).
+template <typename TY>
+__global__ __launch_bounds__(256) void combine_kernel(const TY* __restrict__ y_perm,
                                                       const int32_t* __restrict__ slot_pos,
                                                       const float* __restrict__ topk_w,
                                                       const float* __restrict__ y_base, int T,
@@ -74,13 +78,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         const int pos = __builtin_amdgcn_readlane(my_pos, s & 63);
         ws[g] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), s & 63));
         const bool live = pos >= 0 && s < k;
+        constexpr int ES = (int)sizeof(TY);
         const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<float*>(y_perm) + (long long)(live ? pos : 0) * d, (short)0,
-            live ? d * 4 : 0, 0x00020000);
+            const_cast<TY*>(y_perm) + (long long)(live ? pos : 0) * d, (short)0,
+            live ? d * ES : 0, 0x00020000);
 #pragma unroll
-        for (int v = 0; v < V; ++v)
-          x[g][v] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                  yr, ok[v] ? cc[v] * 4 : kOutOfRange, 0, 0));
+        for (int v = 0; v < V; ++v) {
+          if constexpr (ES == 4) {
+            x[g][v] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    yr, ok[v] ? cc[v] * 4 : kOutOfRange, 0, 0));
+          } else {
+            // 4 bf16 values; each widens to fp32 by a 16-bit shift
+            const v2u32 r = __builtin_amdgcn_raw_buffer_load_b64(
+                yr, ok[v] ? cc[v] * 2 : kOutOfRange, 0, 0);
+            x[g][v] = f32x4{__uint_as_float(r[0] << 16), __uint_as_float(r[0] & 0xffff0000u),
+                            __uint_as_float(r[1] << 16), __uint_as_float(r[1] & 0xffff0000u)};
+          }
+        }
       }
 #pragma unroll
       for (int g = 0; g < G; ++g)
@@ -109,9 +123,9 @@ __global__ __launch_bounds__(256) void aux_kernel(const float* __restrict__ impo
 
 }  // namespace
 
-hipError_t launch_combine(const float* y_perm, const int32_t* slot_pos, const float* topk_w,
+hipError_t launch_combine(const void* y_perm, const int32_t* slot_pos, const float* topk_w,
                           const float* y_base, int T, int k, int d, float* y, hipStream_t s,
-                          const AuxArgs* aux) {
+                          const AuxArgs* aux, bool y_bf16) {
   if (T <= 0) {
     if (aux && aux->losses)
       return launch_aux(aux->importance, aux->load, aux->counts_pre, aux->gate_stats, aux->T,
@@ -129,8 +143,12 @@ hipError_t launch_combine(const float* y_perm, const int32_t* slot_pos, const fl
   const AuxArgs ax = aux ? *aux : AuxArgs{};
   const long long blocks = (waves + 3) / 4 + (ax.losses ? 1 : 0);
   ProfScope ps("combine", s);
-  combine_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(y_perm, slot_pos, topk_w, y_base,
-                                                              T, k, d, wpt, y, ax);
+  if (y_bf16)
+    combine_kernel<uint16_t><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
+        (const uint16_t*)y_perm, slot_pos, topk_w, y_base, T, k, d, wpt, y, ax);
+  else
+    combine_kernel<float><<<dim3((unsigned)blocks), dim3(256), 0, s>>>((const float*)y_perm, slot_pos, topk_w,
+                                                                       y_base, T, k, d, wpt, y, ax);
   return hipGetLastError();
 }
 

@@ -33,7 +33,7 @@
 // The MFMA computes D = W . X^T (weights as the A operand), so each lane ends
 // with 4 consecutive output columns of one row and stores them directly.
 // Epilogues: ReLU(+bias) -> bf16 hidden; silu(x.W1^T) * (x.W3^T) -> bf16
-// hidden; identity(+bias) -> fp32 expert output.
+// hidden; identity(+bias) -> fp32 or bf16 expert output.
 // Rows past a segment's end and columns past N copy clamped (valid) rows and
 // are never stored; K-tail chunks copy a 16-byte zero constant.
 #include <math.h>
@@ -451,6 +451,9 @@ hipError_t launch_typed(const GemmBf16Args& a, int epi, hipStream_t s) {
                   : launch_t<256, EPI_RELU_BF16, 2, false, FP8>(a, s);
     case EPI_SWIGLU_BF16:
       return launch_t<128, EPI_SWIGLU_BF16, 2, false, FP8>(a, s);
+    case EPI_IDENT_BF16:
+      return bias ? launch_t<256, EPI_IDENT_BF16, 2, true, FP8>(a, s)
+                  : launch_t<256, EPI_IDENT_BF16, 2, false, FP8>(a, s);
     default:
       return bias ? launch_t<256, EPI_IDENT_F32, 2, true, FP8>(a, s)
                   : launch_t<256, EPI_IDENT_F32, 2, false, FP8>(a, s);

@@ -6,7 +6,7 @@
 // lists M-tiles -- here 256 rows of one expert's merged batch -- and the work
 // items are (M-tile, N-tile) pairs; W[e] = [N, K] (out x in) and X = [rows,
 // K], both streaming along K; epilogues ReLU(+bias) -> bf16, SwiGLU -> bf16,
-// identity(+bias) -> fp32.
+// identity(+bias) -> fp32 or bf16.
 //
 // What differs is the shape of the work per compute unit:
 //  * one 4-wave workgroup per CU (one wave per SIMD), each wave a 128 x 128
@@ -456,9 +456,9 @@ hipError_t launch_t(const GemmBf16Args& a, hipStream_t s) {
   if (grid < kXcds) grid = kXcds;
   const long long per = (max_total + kXcds - 1) / kXcds;
   while ((per + grid / kXcds - 1) / (grid / kXcds) > kMaxTilesPerWG) grid += kXcds;
-  static const char* const kNames[2][3] = {
-      {"ggemm_big_relu", "ggemm_big_swiglu", "ggemm_big_out"},
-      {"ggemm_big_fp8_relu", "ggemm_big_fp8_swiglu", "ggemm_big_fp8_out"}};
+  static const char* const kNames[2][4] = {
+      {"ggemm_big_relu", "ggemm_big_swiglu", "ggemm_big_out", "ggemm_big_out"},
+      {"ggemm_big_fp8_relu", "ggemm_big_fp8_swiglu", "ggemm_big_fp8_out", "ggemm_big_fp8_out"}};
   ProfScope ps(a.prof_name ? a.prof_name : kNames[FP8 ? 1 : 0][EPI], s);
   ggemm_big_kernel<EPI, HAS_BIAS, FP8><<<dim3((unsigned)grid), dim3(kThreads), 0, s>>>(a);
   return hipGetLastError();
@@ -473,6 +473,9 @@ hipError_t launch_typed(const GemmBf16Args& a, int epi, hipStream_t s) {
                   : launch_t<EPI_RELU_BF16, false, FP8>(a, s);
     case EPI_SWIGLU_BF16:
       return launch_t<EPI_SWIGLU_BF16, false, FP8>(a, s);
+    case EPI_IDENT_BF16:
+      return bias ? launch_t<EPI_IDENT_BF16, true, FP8>(a, s)
+                  : launch_t<EPI_IDENT_BF16, false, FP8>(a, s);
     default:
       return bias ? launch_t<EPI_IDENT_F32, true, FP8>(a, s)
                   : launch_t<EPI_IDENT_F32, false, FP8>(a, s);

@@ -181,7 +181,9 @@ hipError_t launch_hbm_read_probe(const void* buf, long long bytes, int blocks, f
 // ---------------------------------------------------------------------------
 // bf16 MFMA grouped GEMM for the expert FFNs.
 // ---------------------------------------------------------------------------
-enum GemmEpi { EPI_RELU_BF16 = 0, EPI_SWIGLU_BF16 = 1, EPI_IDENT_F32 = 2 };
+// EPI_IDENT_BF16: identity(+bias) rounded to bf16 (the layer forward's expert
+// outputs, which only the combine reads).
+enum GemmEpi { EPI_RELU_BF16 = 0, EPI_SWIGLU_BF16 = 1, EPI_IDENT_F32 = 2, EPI_IDENT_BF16 = 3 };
 struct GemmBf16Args {
   const uint16_t* A;     // [rows, K] bf16, rows contiguous
   long long lda;
@@ -482,10 +484,10 @@ struct AuxArgs {
 };
 // y[t] = y_base[t] (when given) + sum over kept slots, in slot order.  With
 // aux (losses non-null) one more block of the launch (its first) computes the
-// losses.
-hipError_t launch_combine(const float* y_perm, const int32_t* slot_pos, const float* topk_w,
+// losses.  y_perm holds fp32 rows, or bf16 rows when y_bf16 is set.
+hipError_t launch_combine(const void* y_perm, const int32_t* slot_pos, const float* topk_w,
                           const float* y_base, int T, int k, int d, float* y, hipStream_t s,
-                          const AuxArgs* aux = nullptr);
+                          const AuxArgs* aux = nullptr, bool y_bf16 = false);
 hipError_t launch_aux(const float* importance, const float* load, const int32_t* counts_pre,
                       const float* gate_stats, int T, int k, int n, float w_imp, float w_load,
                       float alpha, float w_z, float w_ent, float* losses, hipStream_t s);

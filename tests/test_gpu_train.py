@@ -47,11 +47,13 @@ def _check_step(cfg, T=None):
     torch.cuda.synchronize()
     y, losses = _np(y), _np(losses)
     np.testing.assert_array_equal(losses, l_ref)
-    swiglu_bf16 = cfg.act == ACT_SWIGLU and cfg.expert_dtype != DTYPE_F32
-    if swiglu_bf16:
+    if cfg.expert_dtype != DTYPE_F32:
+        # moe_forward rounds bf16 experts' output rows to bf16 before the
+        # combine (one rounding, 2^-9 relative, per kept slot); the training
+        # forward keeps them in fp32 for the backward.
         err = max_abs_norm(y, y_ref) if y.size else 0.0
         log(f"  y vs moe_forward: {err:.2e} max-abs-normalised")
-        assert err <= 1e-3, err
+        assert err <= 4e-3, err
     else:
         np.testing.assert_array_equal(y, y_ref)
     assert g.keys() == g_ref.keys()
